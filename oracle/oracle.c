@@ -1,0 +1,282 @@
+/*
+ * CPU ORACLE for the ternary group-scaled matmul — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library. The GPU library never links, includes or calls it, and
+ * this file includes nothing from the GPU library: the two share no code.
+ *
+ * What it computes, in fp64, plainly and slowly:
+ *
+ *   y[m][n] = sum_k  s[n][k/128] * t[n][k] * xr[m][k]
+ *
+ * where t[n][k] in {-1, 0, +1} are the ternary codes, s[n][g] is the fp16
+ * scale shared by the 128 weights of group g along K, and xr is the
+ * activation x, or R x when the weights are stored in the rotated basis.
+ *   - The weight definition w = s_g * t with one fp16 scale per 128 weights:
+ *     "Ternary Bonsai 2 27B, 5.93GB ... (feat. PrismML)" (discuss.pytorch.kr),
+ *     section "Ternary weights and the rotated basis", subsection
+ *     "Group-scaled ternary format", the equation for w_i; the same formula in
+ *     "Bonsai 27B and how 1-bit survives" (velog.io), section "What the format is".
+ *   - The rotation R = (1/sqrt(n)) H_n S with S a fixed +-1 diagonal, and the
+ *     layer computing f(x) = W(Rx): same P3 page, subsection "Block-wise
+ *     Hadamard rotation". Here n = 128 (one block per scale group) and H is
+ *     the natural-order Sylvester matrix H[i][j] = (-1)^popcount(i & j), the
+ *     normalised Sylvester transform the WebGPU loader insists on (P3 page,
+ *     section "Running in the browser with WebGPU").
+ *
+ * Every step is done the obvious way: each row is unpacked from its packed
+ * bytes by a bit-by-bit loop, dequantised to doubles (fp16/bf16 -> double is
+ * exact), and multiplied; the rotation is a dense 128x128 matrix-vector
+ * product per block, not a fast transform. Threads split rows only; the
+ * arithmetic for each output is a plain sequential sum over k.
+ *
+ * Packed layouts (the pages fix the cost per weight, not the bit order; these
+ * are the readings this oracle fixes):
+ *   slot2: code q = t + 1 in {0, 1, 2} (3 is invalid); element k of a row sits
+ *          in bits 2*(k%4) .. 2*(k%4)+1 of byte k/4; rows are K/4 bytes apart.
+ *          With the fp16 scale per 128 weights this is 34 bytes per 128
+ *          weights, the figure the P3 page gives for scale plus 2-bit codes in
+ *          "Two packings: PTQ1_0 and PQ2_0".
+ *   base3: five trits per byte, byte b of a row = sum_{j<5} (t[5b+j]+1) * 3^j;
+ *          trits past K are 0 (digit 1); a row holds ceil(K/5) such bytes,
+ *          then pad bytes of value 121 (five zero trits) up to a multiple of 16.
+ *   scales: a separate fp16 array [n][K/128], row-major.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_BAD_CODE -1
+#define ORC_BAD_SHAPE -2
+#define ORC_BAD_LAYOUT -3
+
+#define ORC_SLOT2 1
+#define ORC_BASE3 2
+
+#define ORC_X_F16 1
+#define ORC_X_BF16 2
+
+/* ---- storage dtypes -> double (exact), from the IEEE 754 bit layouts ---- */
+
+double orc_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);            /* subnormal: m * 2^-24 */
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + m), e - 25);       /* (1 + m/1024) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
+double orc_bf16_to_f64(uint16_t b) {
+  int sign = (b >> 15) & 1, e = (b >> 7) & 255, m = b & 127;
+  double v;
+  if (e == 0) v = ldexp((double)m, -133);           /* subnormal: m * 2^-133 */
+  else if (e == 255) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(128 + m), e - 134);       /* (1 + m/128) * 2^(e-127) */
+  return sign ? -v : v;
+}
+
+/* ---- layout sizes ---- */
+
+int64_t orc_row_bytes(int32_t layout, int64_t k) {
+  if (k <= 0 || k % 128 != 0) return 0;
+  if (layout == ORC_SLOT2) return k / 4;
+  if (layout == ORC_BASE3) {
+    int64_t used = (k + 4) / 5;
+    return (used + 15) / 16 * 16;
+  }
+  return 0;
+}
+
+/* ---- slot2 ---- */
+
+int orc_pack_slot2(const int8_t* t, int64_t n, int64_t k, uint8_t* codes) {
+  if (k % 128 != 0 || n < 0) return ORC_BAD_SHAPE;
+  int64_t rb = k / 4;
+  memset(codes, 0, (size_t)(n * rb));
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t c = 0; c < k; ++c) {
+      int v = t[r * k + c];
+      if (v < -1 || v > 1) return ORC_BAD_CODE;
+      int q = v + 1;
+      int64_t byte = c / 4;
+      int bit = 2 * (int)(c % 4);
+      codes[r * rb + byte] |= (uint8_t)(q << bit);
+    }
+  }
+  return ORC_OK;
+}
+
+int orc_unpack_slot2(const uint8_t* codes, int64_t n, int64_t k, int8_t* t) {
+  if (k % 128 != 0 || n < 0) return ORC_BAD_SHAPE;
+  int64_t rb = k / 4;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t c = 0; c < k; ++c) {
+      int q = (codes[r * rb + c / 4] >> (2 * (c % 4))) & 3;
+      if (q == 3) return ORC_BAD_CODE;
+      t[r * k + c] = (int8_t)(q - 1);
+    }
+  }
+  return ORC_OK;
+}
+
+/* ---- base3 ---- */
+
+int orc_pack_base3(const int8_t* t, int64_t n, int64_t k, uint8_t* codes) {
+  if (k % 128 != 0 || n < 0) return ORC_BAD_SHAPE;
+  int64_t rb = orc_row_bytes(ORC_BASE3, k);
+  int64_t used = (k + 4) / 5;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t b = 0; b < rb; ++b) {
+      int value = 0, power = 1;
+      for (int j = 0; j < 5; ++j) {
+        int64_t c = 5 * b + j;
+        int digit = 1; /* trit 0 for positions past K and for pad bytes */
+        if (b < used && c < k) {
+          int v = t[r * k + c];
+          if (v < -1 || v > 1) return ORC_BAD_CODE;
+          digit = v + 1;
+        }
+        value += digit * power;
+        power *= 3;
+      }
+      codes[r * rb + b] = (uint8_t)value;
+    }
+  }
+  return ORC_OK;
+}
+
+int orc_unpack_base3(const uint8_t* codes, int64_t n, int64_t k, int8_t* t) {
+  if (k % 128 != 0 || n < 0) return ORC_BAD_SHAPE;
+  int64_t rb = orc_row_bytes(ORC_BASE3, k);
+  int64_t used = (k + 4) / 5;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t b = 0; b < rb; ++b) {
+      int value = codes[r * rb + b];
+      if (value > 242) return ORC_BAD_CODE;
+      if (b >= used) {
+        if (value != 121) return ORC_BAD_CODE;
+        continue;
+      }
+      for (int j = 0; j < 5; ++j) {
+        int digit = value % 3;
+        value /= 3;
+        int64_t c = 5 * b + j;
+        if (c < k) t[r * k + c] = (int8_t)(digit - 1);
+        else if (digit != 1) return ORC_BAD_CODE; /* positions past K hold trit 0 */
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ---- one row of codes -> trits (used by the product; same loops as above) ---- */
+
+static int unpack_row(int32_t layout, const uint8_t* row, int64_t k, int8_t* t) {
+  if (layout == ORC_SLOT2) return orc_unpack_slot2(row, 1, k, t);
+  if (layout == ORC_BASE3) return orc_unpack_base3(row, 1, k, t);
+  return ORC_BAD_LAYOUT;
+}
+
+/* ---- Sylvester Hadamard and the block rotation ---- */
+
+static int popcount32(uint32_t v) {
+  int c = 0;
+  while (v) { c += (int)(v & 1u); v >>= 1; }
+  return c;
+}
+
+/* H[i][j] = (-1)^popcount(i & j), natural (Sylvester) order; n must be a power of 2 */
+void orc_hadamard(int32_t n, int8_t* h) {
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < n; ++j)
+      h[(int64_t)i * n + j] = (int8_t)((popcount32((uint32_t)(i & j)) & 1) ? -1 : 1);
+}
+
+/* xr[m][k] = sum_j H[i][j] * sign[b*128+j] * x[m][b*128+j] / sqrt(128), k = b*128 + i */
+void orc_rotate_f64(const double* x, const int8_t* sign, int64_t m, int64_t k, double* xr) {
+  int8_t h[128 * 128];
+  orc_hadamard(128, h);
+  const double norm = sqrt(128.0);
+  for (int64_t r = 0; r < m; ++r) {
+    for (int64_t b = 0; b < k / 128; ++b) {
+      const double* xb = x + r * k + b * 128;
+      const int8_t* sb = sign + b * 128;
+      for (int i = 0; i < 128; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < 128; ++j) acc += (double)h[i * 128 + j] * ((double)sb[j] * xb[j]);
+        xr[r * k + b * 128 + i] = acc / norm;
+      }
+    }
+  }
+}
+
+/* activation bits -> doubles */
+int orc_load_x(const uint16_t* x, int32_t x_dtype, int64_t count, double* out) {
+  for (int64_t i = 0; i < count; ++i) {
+    if (x_dtype == ORC_X_F16) out[i] = orc_f16_to_f64(x[i]);
+    else if (x_dtype == ORC_X_BF16) out[i] = orc_bf16_to_f64(x[i]);
+    else return ORC_BAD_LAYOUT;
+  }
+  return ORC_OK;
+}
+
+/*
+ * y[m][j] and bound[m][j] for the selected rows n = rows[j] (all rows if rows == NULL,
+ * then n_sel must equal n).
+ *   y     = sum_k s * t * xr
+ *   bound = 1e-3 * sum_k |s * t * xr| + 1e-6   (per-element tolerance on the result)
+ * codes: [n][row_stride] bytes, scales: [n][k/128] fp16 bits, x: [m][k] fp16/bf16 bits,
+ * sign: [k] (+-1) or NULL for the unrotated basis.
+ */
+int orc_matmul_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
+                   const uint16_t* scales, int64_t n, int64_t k,
+                   const uint16_t* x, int32_t x_dtype, int64_t m,
+                   const int8_t* sign, const int64_t* rows, int64_t n_sel,
+                   double* y, double* bound) {
+  if (k <= 0 || k % 128 != 0 || m < 1 || n < 0) return ORC_BAD_SHAPE;
+  if (orc_row_bytes(layout, k) == 0) return ORC_BAD_LAYOUT;
+  if (row_stride < orc_row_bytes(layout, k)) return ORC_BAD_SHAPE;
+  if (rows == NULL && n_sel != n) return ORC_BAD_SHAPE;
+
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(m * k));
+  double* xr = (double*)malloc(sizeof(double) * (size_t)(m * k));
+  if (!xd || !xr) { free(xd); free(xr); return ORC_BAD_SHAPE; }
+  int rc = orc_load_x(x, x_dtype, m * k, xd);
+  if (rc == ORC_OK) {
+    if (sign) orc_rotate_f64(xd, sign, m, k, xr);
+    else memcpy(xr, xd, sizeof(double) * (size_t)(m * k));
+  }
+  free(xd);
+  if (rc != ORC_OK) { free(xr); return rc; }
+
+  int status = ORC_OK;
+#pragma omp parallel
+  {
+    int8_t* t = (int8_t*)malloc((size_t)k);
+    double* w = (double*)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t j = 0; j < n_sel; ++j) {
+      int64_t r = rows ? rows[j] : j;
+      if (r < 0 || r >= n) { status = ORC_BAD_SHAPE; continue; }
+      if (unpack_row(layout, codes + r * row_stride, k, t) != ORC_OK) { status = ORC_BAD_CODE; continue; }
+      for (int64_t c = 0; c < k; ++c) w[c] = orc_f16_to_f64(scales[r * (k / 128) + c / 128]) * (double)t[c];
+      for (int64_t i = 0; i < m; ++i) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t c = 0; c < k; ++c) {
+          double p = w[c] * xr[i * k + c];
+          acc += p;
+          mag += fabs(p);
+        }
+        y[i * n_sel + j] = acc;
+        bound[i * n_sel + j] = 1e-3 * mag + 1e-6;
+      }
+    }
+    free(t);
+    free(w);
+  }
+  free(xr);
+  return status;
+}

@@ -1,0 +1,424 @@
+"""Pins for the CPU oracle, independent of the oracle's own code.
+
+Each check ties the oracle to something it does not compute itself: hand-worked bytes
+(tests/golden), numpy/scipy library routines (IEEE decoding, Sylvester Hadamard, dense
+matmul), closed forms of the group-scaled product, exhaustive enumeration and brute force
+on tiny shapes. Citations name the page and section whose definition each check follows:
+  P3 = "Ternary Bonsai 2 27B, 5.93GB ... (feat. PrismML)" (discuss.pytorch.kr)
+  P2 = "Bonsai 27B and how 1-bit survives" (velog.io)
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_fixture(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split(";")
+            rows.append(([int(v) for v in lhs.split()], rhs.strip()))
+    return rows
+
+
+# ---------------------------------------------------------------- storage dtypes
+
+def test_f16_decode_matches_numpy_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_bf16_decode_matches_float32_top_half_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    got = np.array([oracle.bf16_to_f64(int(b)) for b in bits])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+# ---------------------------------------------------------------- slot-2 bytes (P3, "Two packings")
+
+def _row_with_prefix(prefix, k=128):
+    t = np.zeros((1, k), dtype=np.int8)
+    t[0, :len(prefix)] = prefix
+    return t
+
+
+@pytest.mark.parametrize("trits,hexbyte", _read_fixture("slot2_bytes.txt"))
+def test_slot2_hand_bytes(trits, hexbyte):
+    codes = oracle.pack(oracle.SLOT2, _row_with_prefix(trits))
+    assert codes[0, 0] == int(hexbyte, 16)
+    assert (codes[0, 1:] == 0x55).all()  # zero trits elsewhere: q = 1 in every slot
+
+
+def test_slot2_all_zero_dword():
+    codes = oracle.pack(oracle.SLOT2, np.zeros((1, 128), dtype=np.int8))
+    assert codes[0, :4].view(np.uint32)[0] == 0x55555555
+
+
+def test_slot2_every_byte_round_trips_or_is_rejected():
+    valid = 0
+    for b in range(256):
+        slots = [(b >> (2 * i)) & 3 for i in range(4)]
+        codes = np.full((1, 32), 0x55, dtype=np.uint8)
+        codes[0, 0] = b
+        if 3 in slots:
+            with pytest.raises(oracle.OracleError):
+                oracle.unpack(oracle.SLOT2, codes, 128)
+            continue
+        valid += 1
+        t = oracle.unpack(oracle.SLOT2, codes, 128)
+        assert list(t[0, :4]) == [s - 1 for s in slots]
+        assert (oracle.pack(oracle.SLOT2, t) == codes).all()
+    assert valid == 81
+
+
+def test_slot2_random_round_trip_and_position():
+    t = synth.trits(0, 11, (5, 384), 0.4)
+    codes = oracle.pack(oracle.SLOT2, t)
+    assert codes.shape == (5, 96)
+    assert (oracle.unpack(oracle.SLOT2, codes, 384) == t).all()
+    # element k lives in byte k//4 at bit 2*(k%4): check directly with numpy bit arithmetic
+    for k in (0, 1, 2, 3, 4, 127, 128, 383):
+        q = (codes[:, k // 4] >> (2 * (k % 4))) & 3
+        assert (q.astype(np.int16) - 1 == t[:, k]).all()
+
+
+def test_pack_rejects_bad_trits():
+    t = np.zeros((1, 128), dtype=np.int8)
+    t[0, 5] = 2
+    for layout in (oracle.SLOT2, oracle.BASE3):
+        with pytest.raises(oracle.OracleError):
+            oracle.pack(layout, t)
+
+
+# ---------------------------------------------------------------- base-3 bytes
+
+@pytest.mark.parametrize("trits,value", _read_fixture("base3_bytes.txt"))
+def test_base3_hand_bytes(trits, value):
+    codes = oracle.pack(oracle.BASE3, _row_with_prefix(trits))
+    assert codes[0, 0] == int(value)
+    assert codes.shape == (1, 32)  # ceil(128/5) = 26 bytes, padded to 32
+    assert (codes[0, 1:26] == 121).all()
+    assert (codes[0, 26:] == 121).all()
+
+
+def test_base3_every_byte_round_trips_or_is_rejected():
+    for b in range(256):
+        codes = np.full((1, 32), 121, dtype=np.uint8)
+        codes[0, 0] = b
+        if b > 242:
+            with pytest.raises(oracle.OracleError):
+                oracle.unpack(oracle.BASE3, codes, 128)
+            continue
+        t = oracle.unpack(oracle.BASE3, codes, 128)
+        digits = [(b // 3 ** j) % 3 for j in range(5)]
+        assert list(t[0, :5]) == [d - 1 for d in digits]
+        assert (oracle.pack(oracle.BASE3, t) == codes).all()
+
+
+def test_base3_last_byte_of_k4096():
+    # K = 4096: byte 819 holds trit 4095 and four positions past K (trit 0, digit 1 each):
+    # value = (t_4095 + 1) + 3 + 9 + 27 + 81 = (t_4095 + 1) + 120
+    for last in (-1, 0, 1):
+        t = np.zeros((1, 4096), dtype=np.int8)
+        t[0, -1] = last
+        codes = oracle.pack(oracle.BASE3, t)
+        assert codes.shape == (1, 832)
+        assert codes[0, 819] == (last + 1) + 120
+        assert (codes[0, 820:] == 121).all()
+
+
+def test_base3_rejects_noncanonical_padding():
+    t = synth.trits(0, 12, (1, 4096), 0.5)
+    codes = oracle.pack(oracle.BASE3, t)
+    bad = codes.copy()
+    bad[0, 825] = 120  # pad byte must be 121
+    with pytest.raises(oracle.OracleError):
+        oracle.unpack(oracle.BASE3, bad, 4096)
+    bad = codes.copy()
+    bad[0, 819] = (t[0, -1] + 1) + 3 * 2  # a position past K carrying a nonzero trit
+    with pytest.raises(oracle.OracleError):
+        oracle.unpack(oracle.BASE3, bad, 4096)
+
+
+def test_base3_random_round_trip():
+    for k in (128, 1024, 4096, 5120, 12288):
+        t = synth.trits(3, k, (3, k), 0.5)
+        codes = oracle.pack(oracle.BASE3, t)
+        assert (oracle.unpack(oracle.BASE3, codes, k) == t).all()
+        # the digit rule written with numpy over the whole row
+        used = (k + 4) // 5
+        digits = np.ones((3, used * 5), dtype=np.int64)
+        digits[:, :k] = t.astype(np.int64) + 1
+        expect = (digits.reshape(3, used, 5) * (3 ** np.arange(5))).sum(axis=2)
+        assert (codes[:, :used] == expect).all()
+
+
+# ---------------------------------------------------------------- byte counts (P3 "Group-scaled ternary format",
+#                                                                   "Two packings")
+
+def _bits_per_weight(layout, n, k):
+    return (n * oracle.row_bytes(layout, k) + n * (k // 128) * 2) * 8 / (n * k)
+
+
+def test_slot2_costs_34_bytes_per_128_weights():
+    for k in (128, 1024, 4096, 5120, 12288, 17408):
+        assert oracle.row_bytes(oracle.SLOT2, k) / (k / 128) + 2 == 34
+        assert _bits_per_weight(oracle.SLOT2, 7, k) == 2.125
+
+
+def test_base3_density():
+    b_eff = math.log2(3) + 16 / 128  # the information bound plus the fp16 scale (P3, b_eff equation)
+    for k in (128, 1024, 4096, 5120, 12288, 17408):
+        for layout in (oracle.SLOT2, oracle.BASE3):
+            assert _bits_per_weight(layout, 3, k) >= b_eff
+    # exactly 8/5 + 16/128 = 1.725 where ceil(K/5) is already a multiple of 16
+    assert _bits_per_weight(oracle.BASE3, 1, 5120) == pytest.approx(1.725, abs=1e-15)
+    assert oracle.row_bytes(oracle.BASE3, 4096) == 832
+    assert oracle.row_bytes(oracle.BASE3, 12288) == 2464
+    assert oracle.row_bytes(oracle.BASE3, 17408) == 3488
+
+
+def test_config1_bytes():
+    assert 256 * oracle.row_bytes(oracle.SLOT2, 1024) + 256 * 8 * 2 == 69632
+
+
+def test_published_file_sizes_fit_34_bytes_per_group():
+    # P3 "Points to note when reading": the two released files are 7,206,168,928 B (2-bit slots)
+    # and 5,946,648,928 B (dense). With 34 B per 128-group for the slot layout and 28 B for a
+    # dense layout of ceil(128/5) = 26 code bytes + 2 scale bytes, the difference must be a whole
+    # number of groups times 6 B, and the implied weight count plus the 26,238,464 parameters kept
+    # in high precision (P3 table in "The 0.0976% left in high precision") must match the 53.80 GB
+    # FP16 size (P3 introduction) to within the rounding of that figure.
+    diff = 7_206_168_928 - 5_946_648_928
+    slot_bytes_per_group = oracle.row_bytes(oracle.SLOT2, 128) + 2
+    assert slot_bytes_per_group == 34
+    dense_bytes_per_group = math.ceil(128 / 5) + 2
+    groups, rem = divmod(diff, slot_bytes_per_group - dense_bytes_per_group)
+    assert rem == 0
+    assert abs((groups * 128 + 26_238_464) * 2 / 53.80e9 - 1) < 1e-3
+
+
+# ---------------------------------------------------------------- Hadamard and rotation (P3 "Block-wise Hadamard rotation")
+
+def test_hadamard_is_sylvester():
+    for n in (1, 2, 4, 8, 16, 32, 64, 128):
+        h = oracle.hadamard(n).astype(np.int64)
+        assert (h == scipy.linalg.hadamard(n)).all()
+        assert (h @ h.T == n * np.eye(n, dtype=np.int64)).all()
+        assert (h == h.T).all()
+        if n >= 2:
+            half = oracle.hadamard(n // 2).astype(np.int64)
+            assert (h == np.block([[half, half], [half, -half]])).all()
+
+
+def _dense_rotation(signs):
+    k = signs.size
+    h = scipy.linalg.hadamard(128).astype(np.float64) / math.sqrt(128)
+    r = np.zeros((k, k))
+    for b in range(k // 128):
+        sl = slice(b * 128, (b + 1) * 128)
+        r[sl, sl] = h * signs[sl].astype(np.float64)[None, :]  # H S: sign on the input side
+    return r
+
+
+def test_rotation_matches_dense_block_matrix():
+    k = 512
+    sg = synth.signs(0, 1, k)
+    x = synth.normal(0, 2, (3, k))
+    got = oracle.rotate(x, sg)
+    ref = x @ _dense_rotation(sg).T
+    assert np.abs(got - ref).max() < 1e-13
+
+
+def test_rotation_is_orthogonal():
+    k = 256
+    sg = synth.signs(5, 1, k)
+    rcols = oracle.rotate(np.eye(k), sg)  # row i = R e_i = column i of R
+    r = rcols.T
+    assert np.abs(r.T @ r - np.eye(k)).max() < 1e-14
+    x = synth.normal(1, 3, (4, k))
+    assert np.allclose(np.linalg.norm(oracle.rotate(x, sg), axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+
+
+def test_rotation_of_one_hot():
+    k = 128
+    sg = synth.signs(7, 1, k)
+    h = scipy.linalg.hadamard(128)
+    for j in (0, 1, 77, 127):
+        e = np.zeros(k)
+        e[j] = 1.0
+        assert np.allclose(oracle.rotate(e, sg), sg[j] * h[:, j] / math.sqrt(128), atol=1e-15)
+
+
+def test_rotation_identities():
+    # (W H)(H^T x) / 128 = W x  and  (W R^T)(R x) = W x, on dense fp64 W
+    k = 256
+    w = synth.normal(2, 1, (5, k))
+    x = synth.normal(2, 2, (k,))
+    h = np.kron(np.eye(k // 128), scipy.linalg.hadamard(128).astype(np.float64))
+    assert np.allclose((w @ h) @ (h.T @ x) / 128, w @ x, atol=1e-12)
+    sg = synth.signs(2, 3, k)
+    rt = _dense_rotation(sg).T
+    assert np.allclose((w @ rt) @ oracle.rotate(x, sg), w @ x, atol=1e-12)
+
+
+# ---------------------------------------------------------------- the product (P3 "Group-scaled ternary format")
+
+def _dense_weights(trits, scales_f16):
+    s = np.asarray(scales_f16, dtype=np.float16).astype(np.float64)
+    return trits.astype(np.float64) * np.repeat(s, 128, axis=1)
+
+
+@pytest.mark.parametrize("layout", [oracle.SLOT2, oracle.BASE3])
+def test_closed_forms(layout):
+    k = 256
+    x16 = synth.x_f16(0, 1, (k,))
+    xs = x16.astype(np.float64)
+    t = np.zeros((4, k), dtype=np.int8)
+    t[0, :128] = 1          # all +1 in group 0, zero in group 1
+    t[1, 128:] = -1         # all -1 in group 1
+    t[3, 200] = -1          # one-hot
+    s = np.array([[0.5, 3.0], [0.25, 2.0], [1.0, 1.0], [7.0, 0.125]], dtype=np.float16)
+    codes = oracle.pack(layout, t)
+    y, bound = oracle.matmul(layout, codes, s, k, x16.view(np.uint16), oracle.X_F16)
+    assert y[0, 0] == pytest.approx(0.5 * xs[:128].sum(), rel=1e-15, abs=1e-15)
+    assert y[0, 1] == pytest.approx(-2.0 * xs[128:].sum(), rel=1e-15, abs=1e-15)
+    assert y[0, 2] == 0.0
+    assert y[0, 3] == -0.125 * xs[200]
+    assert bound[0, 2] == 1e-6
+
+
+@pytest.mark.parametrize("layout", [oracle.SLOT2, oracle.BASE3])
+def test_integer_inputs_give_exact_integers(layout):
+    k = 512
+    t = synth.trits(4, 1, (6, k), 0.4)
+    x = (synth.trits(4, 2, (2, k), 0.0).astype(np.int64) * 3 + synth.trits(4, 3, (2, k), 0.2)).astype(np.int64)
+    expo = synth.trits(4, 4, (6, k // 128), 0.0).astype(np.int64)  # scales 2^-1 or 2^+1
+    s = np.ldexp(1.0, expo).astype(np.float16)
+    codes = oracle.pack(layout, t)
+    y, _ = oracle.matmul(layout, codes, s, k, x.astype(np.float16).view(np.uint16), oracle.X_F16)
+    ref = x.astype(np.float64) @ _dense_weights(t, s).T
+    assert (y == ref).all()
+
+
+@pytest.mark.parametrize("layout", [oracle.SLOT2, oracle.BASE3])
+@pytest.mark.parametrize("k", [128, 256])
+@pytest.mark.parametrize("m", [1, 3])
+def test_brute_force_tiny(layout, k, m):
+    n = 4
+    t = synth.trits(k + m, layout, (n, k), 0.4)
+    s = synth.scales_f16(k + m, 9, (n, k // 128))
+    x16 = synth.x_f16(k + m, 10, (m, k))
+    codes = oracle.pack(layout, t)
+    y, bound = oracle.matmul(layout, codes, s, k, x16.view(np.uint16), oracle.X_F16)
+    terms = x16.astype(np.float64)[:, None, :] * _dense_weights(t, s)[None, :, :]
+    assert np.allclose(y, terms.sum(axis=2), rtol=1e-13, atol=1e-16)
+    assert np.allclose(bound, 1e-3 * np.abs(terms).sum(axis=2) + 1e-6, rtol=1e-13)
+
+
+def test_bf16_activations():
+    k = 256
+    t = synth.trits(1, 1, (3, k), 0.4)
+    s = synth.scales_f16(1, 2, (3, 2))
+    xb = synth.x_bf16_bits(1, 3, (2, k))
+    xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    y, _ = oracle.matmul(oracle.SLOT2, oracle.pack(oracle.SLOT2, t), s, k, xb, oracle.X_BF16)
+    assert np.allclose(y, xf @ _dense_weights(t, s).T, rtol=1e-13, atol=1e-16)
+
+
+@pytest.mark.parametrize("layout", [oracle.SLOT2, oracle.BASE3])
+def test_rotated_product_brute_force(layout):
+    k, m = 256, 2
+    t = synth.trits(8, 1, (3, k), 0.5)
+    s = synth.scales_f16(8, 2, (3, 2))
+    x16 = synth.x_f16(8, 3, (m, k))
+    sg = synth.signs(8, 4, k)
+    y, bound = oracle.matmul(layout, oracle.pack(layout, t), s, k, x16.view(np.uint16), oracle.X_F16, signs=sg)
+    xr = x16.astype(np.float64) @ _dense_rotation(sg).T
+    terms = xr[:, None, :] * _dense_weights(t, s)[None, :, :]
+    assert np.allclose(y, terms.sum(axis=2), rtol=1e-12, atol=1e-15)
+    assert np.allclose(bound, 1e-3 * np.abs(terms).sum(axis=2) + 1e-6, rtol=1e-12)
+
+
+def test_rotated_hand_example():
+    # sigma = +1 everywhere, x = e_0: R x = H[:, 0] / sqrt(128) = (1, ..., 1) / sqrt(128).
+    # Row of all +1 codes at scale 1 gives 128 / sqrt(128) = sqrt(128); a row equal to any other
+    # Hadamard row gives 0 (rows of H are orthogonal to the all-ones row 0).
+    # sigma_3 = -1, x = e_3: R x = -H[:, 3] / sqrt(128); the row t = H[3] then gives -sqrt(128).
+    k = 128
+    h = scipy.linalg.hadamard(128).astype(np.int8)
+    t = np.stack([np.ones(k, dtype=np.int8), h[5], h[3]])
+    s = np.ones((3, 1), dtype=np.float16)
+    sg = np.ones(k, dtype=np.int8)
+    x = np.zeros((2, k), dtype=np.float16)
+    x[0, 0] = 1
+    x[1, 3] = 1
+    sg[3] = -1
+    y, _ = oracle.matmul(oracle.SLOT2, oracle.pack(oracle.SLOT2, t), s, k, x.view(np.uint16), oracle.X_F16, signs=sg)
+    assert y[0, 0] == pytest.approx(math.sqrt(128), rel=1e-15)
+    assert y[0, 1] == pytest.approx(0.0, abs=1e-15)
+    assert y[1, 2] == pytest.approx(-math.sqrt(128), rel=1e-15)
+
+
+def test_row_sampling_matches_full():
+    k = 384
+    t = synth.trits(2, 5, (50, k), 0.4)
+    s = synth.scales_f16(2, 6, (50, 3))
+    x16 = synth.x_f16(2, 7, (2, k))
+    codes = oracle.pack(oracle.BASE3, t)
+    full, _ = oracle.matmul(oracle.BASE3, codes, s, k, x16.view(np.uint16), oracle.X_F16)
+    rows = np.array([49, 0, 17, 17, 3])
+    part, _ = oracle.matmul(oracle.BASE3, codes, s, k, x16.view(np.uint16), oracle.X_F16, rows=rows)
+    assert (part == full[:, rows]).all()
+
+
+def test_golden_small_product():
+    # tests/golden/small_product.txt: a K = 128 example worked by hand.
+    path = os.path.join(GOLDEN, "small_product.txt")
+    spec = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if line:
+                key, val = line.split("=")
+                spec[key.strip()] = val.strip()
+    k = 128
+    x = np.array([int(v) for v in spec["x"].split()], dtype=np.float16)
+    assert x.size == k
+    rows = [r for r in spec if r.startswith("row")]
+    t = np.zeros((len(rows), k), dtype=np.int8)
+    s = np.zeros((len(rows), 1), dtype=np.float16)
+    expect = np.zeros(len(rows))
+    for i, name in enumerate(sorted(rows)):
+        kind, scale, want = spec[name].split()
+        if kind == "plus":
+            t[i] = 1
+        elif kind == "minus":
+            t[i] = -1
+        elif kind == "alternate":
+            t[i, 0::2] = 1
+            t[i, 1::2] = -1
+        elif kind.startswith("onehot"):
+            t[i, int(kind[len("onehot"):])] = -1
+        s[i, 0] = float(scale)
+        expect[i] = float(want)
+    for layout in (oracle.SLOT2, oracle.BASE3):
+        y, _ = oracle.matmul(layout, oracle.pack(layout, t), s, k, x.view(np.uint16), oracle.X_F16)
+        assert (y[0] == expect).all()
