@@ -1,0 +1,199 @@
+/*
+ * tgs.h — C ABI of the ternary group-scaled matmul library for AMD Instinct MI355X (gfx950).
+ *
+ * The library multiplies activations by weights w = s_g * t, where each code t is -1, 0 or +1
+ * and every group of 128 consecutive weights along K shares one fp16 scale s_g. The weights stay
+ * packed in device memory and are decoded inside the kernels; no fp16 copy of W is ever made.
+ *
+ * Page references (titles as given by the sites):
+ *   [P3] "Ternary Bonsai 2 27B, 5.93GB ... (feat. PrismML)", discuss.pytorch.kr
+ *   [P2] "Bonsai 27B and how 1-bit survives", velog.io
+ *   [P1] "Fine-tuning the ternary Bonsai-8B on Metal", molayo1419.me
+ *
+ * Conventions for every entry point:
+ *   - Every call returns a tgs_status. Nothing is thrown across the ABI. After a failure,
+ *     tgs_last_error() returns a message for the calling thread.
+ *   - The caller owns every buffer it passes in. Pointers documented as "device" must be
+ *     device memory of the current HIP device; "host" pointers must be host memory.
+ *   - Arguments are checked on the host before any device work is queued. A rejected call
+ *     queues nothing and leaves every output untouched.
+ *   - Device calls run asynchronously on the given HIP stream (NULL = the default stream).
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - All calls are thread-safe. The library allocates no device memory and keeps no state
+ *     between calls.
+ */
+#ifndef TGS_H
+#define TGS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TGS_MAGIC 0x31534754u /* "TGS1" */
+#define TGS_VERSION 1u
+#define TGS_GROUP 128          /* weights per fp16 scale, along K */
+#define TGS_MAX_M_GEMV 8       /* activation rows accepted by ternary_gemv */
+#define TGS_MAX_BATCH 32       /* matrices per ternary_gemv_batched call */
+
+typedef enum {
+  TGS_OK = 0,
+  TGS_E_NULL = 1,     /* a required pointer is NULL */
+  TGS_E_SHAPE = 2,    /* K % 128 != 0, N < 1, M out of range, row stride too small ... */
+  TGS_E_ALIGN = 3,    /* a buffer is not aligned as documented */
+  TGS_E_CODE = 4,     /* invalid code: trit outside {-1,0,1}, slot value 3, base-3 byte > 242,
+                         non-canonical padding, sign outside {-1,+1} */
+  TGS_E_LAYOUT = 5,   /* bad descriptor magic/version or unknown layout */
+  TGS_E_BASIS = 6,    /* weights in the rotated basis without signs, or signs for plain weights */
+  TGS_E_SIZE = 7,     /* an output buffer is too small */
+  TGS_E_DTYPE = 8,    /* unsupported activation/output dtype for this call */
+  TGS_E_DEVICE = 9    /* a HIP runtime call failed */
+} tgs_status;
+
+/*
+ * Packed layouts. [P3] section "Two packings: PTQ1_0 and PQ2_0" describes one layout with each
+ * ternary value in its own 2-bit slot (scale plus codes = 34 bytes per 128 weights) and one that
+ * packs ternary values densely. The pages fix neither bit order; these are the library's:
+ *
+ * TGS_LAYOUT_SLOT2: code q = t + 1 (0 -> -1, 1 -> 0, 2 -> +1; 3 is invalid). Element k of a row is
+ *   held in bits 2*(k%4) and 2*(k%4)+1 of byte k/4, so a little-endian 32-bit word holds 16
+ *   consecutive codes, element j in bits 2j..2j+1. Minimum row length K/4 bytes.
+ * TGS_LAYOUT_BASE3: five trits per byte: byte b of a row = sum_{j<5} (t[5b+j] + 1) * 3^j, so
+ *   valid bytes are 0..242. Positions past K in the last used byte hold t = 0. A row holds
+ *   ceil(K/5) bytes followed by pad bytes of value 121 (five zero trits) up to a multiple of
+ *   16 bytes: minimum row length round_up(ceil(K/5), 16) bytes.
+ *
+ * Both layouts keep the scales in a separate fp16 array [N][K/128], row-major, one per group of
+ * 128 consecutive weights of a row ([P3] "Group-scaled ternary format": w_i = s_g * t_i with one
+ * FP16 scale per 128 weights; [P2] "What the format is").
+ */
+typedef enum { TGS_LAYOUT_SLOT2 = 1, TGS_LAYOUT_BASE3 = 2 } tgs_layout;
+
+/* Activation / output element types (IEEE binary16, bfloat16, binary32). */
+typedef enum { TGS_F16 = 1, TGS_BF16 = 2, TGS_F32 = 3 } tgs_dtype;
+
+/*
+ * A packed weight matrix W [n][k] (n output features, k input features).
+ *   magic, version  TGS_MAGIC, TGS_VERSION (tgs_matrix_init fills them)
+ *   layout          a tgs_layout
+ *   rotated         0: plain basis. 1: the codes are weights of the rotated basis, so the layer
+ *                   computes y = W (R x), R = blockdiag_128((1/sqrt(128)) H_128 S) with H_128 the
+ *                   natural-order Sylvester Hadamard matrix and S = diag(signs) ([P3] section
+ *                   "Block-wise Hadamard rotation": R = H_n S / sqrt(n), f(x) = W(Rx); here n = 128,
+ *                   one rotation block per scale group). The packed model declares its basis and
+ *                   the runtime must either apply the transform or refuse ([P3], same section):
+ *                   calls on rotated weights require signs, calls on plain weights reject them.
+ *   n, k            n >= 1, k >= 128, k % 128 == 0
+ *   code_row_stride bytes between consecutive rows of codes: a multiple of 16 and at least
+ *                   tgs_code_row_bytes(layout, k)
+ *   codes           [n][code_row_stride] bytes, 16-byte aligned
+ *   scales          [n][k/128] fp16 bit patterns, 2-byte aligned. Any fp16 value is accepted;
+ *                   NaN and Inf propagate.
+ */
+typedef struct tgs_matrix {
+  uint32_t magic;
+  uint32_t version;
+  int32_t layout;
+  int32_t rotated;
+  int64_t n;
+  int64_t k;
+  int64_t code_row_stride;
+  const void* codes;
+  const uint16_t* scales;
+} tgs_matrix;
+
+/* Minimum bytes per row of codes for the layout, or 0 if layout/k is invalid. */
+size_t tgs_code_row_bytes(int32_t layout, int64_t k);
+
+/* Fill a descriptor with magic/version and the minimum row stride. Returns TGS_E_SHAPE or
+ * TGS_E_LAYOUT for invalid shapes/layouts (the descriptor is then left zeroed). */
+tgs_status tgs_matrix_init(tgs_matrix* w, int32_t layout, int32_t rotated, int64_t n, int64_t k,
+                           const void* codes, const uint16_t* scales);
+
+/*
+ * pack_ternary (host): encode trits into the packed layout.
+ *   trits      host [n][k] int8 in {-1, 0, +1}
+ *   scales     host [n][k/128] fp16 bits, copied to scales_out (both may be NULL to skip)
+ *   codes_out  host buffer of codes_bytes >= n * tgs_code_row_bytes(layout, k); rows are
+ *              written at the minimum stride
+ * A native-ternary checkpoint is exactly scale x {-1, 0, +1}, so this re-encoding is lossless
+ * ([P1] opening section on what these models are); unpack_ternary inverts it bit-exactly.
+ * Returns TGS_E_CODE for a trit outside {-1, 0, +1}; codes_out may then be partly written.
+ */
+tgs_status pack_ternary(int32_t layout, const int8_t* trits, const uint16_t* scales, int64_t n,
+                        int64_t k, void* codes_out, size_t codes_bytes, uint16_t* scales_out);
+
+/*
+ * unpack_ternary (host): decode a host-resident packed matrix back to trits (and copy its
+ * scales). Every byte is checked: slot value 3, base-3 bytes above 242, nonzero trits past K and
+ * pad bytes other than 121 give TGS_E_CODE. trits_out is [n][k] int8; scales_out may be NULL.
+ */
+tgs_status unpack_ternary(const tgs_matrix* w, int8_t* trits_out, uint16_t* scales_out);
+
+/*
+ * ternary_gemv (device): y[i][j] = sum_k s[j][k/128] * t[j][k] * xr[i][k] for i < m, j < n,
+ * with xr = x, or xr = R x when w->rotated (the rotation is computed inside the kernel).
+ *   w       descriptor (host memory) of device-resident codes and scales
+ *   x       device [m][k] activations of x_dtype; only TGS_F16 is accepted; 16-byte aligned
+ *   m       1 .. TGS_MAX_M_GEMV (decode, or a small verify batch)
+ *   signs   device [k] int8 in {-1, +1} when w->rotated, else NULL. Values are not checked on
+ *           the device: any other value gives an unspecified result.
+ *   y       device [m][n] fp32, 4-byte aligned
+ *   stream  hipStream_t or NULL
+ * Arithmetic: codes are decoded in registers; each 128-group is accumulated in fp32 and scaled
+ * by its fp16 scale in fp32. Rotated activations are rounded once to fp16 after the transform,
+ * so |R x| must stay below 65504. Results are deterministic run to run (no float atomics).
+ */
+tgs_status ternary_gemv(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m,
+                        const int8_t* signs, float* y, void* stream);
+
+/*
+ * ternary_gemv_batched (device): count independent ternary_gemv calls (1..TGS_MAX_BATCH) that
+ * share m and x_dtype, issued as few kernel launches as possible. ws is a host array of count
+ * descriptors; xs, signs and ys are host arrays of count device pointers (signs may be NULL if
+ * no matrix is rotated). Matrices may share an input (e.g. the q/k/v projections of one token).
+ * Same rules and errors as ternary_gemv; all descriptors are checked before anything is queued.
+ */
+tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void* const* xs,
+                                int32_t x_dtype, int64_t m, const int8_t* const* signs,
+                                float* const* ys, void* stream);
+
+/*
+ * ternary_gemm (device): the same product for m >= 1 rows of activations (prefill). The codes
+ * are decoded tile by tile into LDS as bf16 and multiplied on the matrix cores (MFMA) with fp32
+ * accumulation; each 128-group's partial product is scaled by its fp16 scale in fp32 ([P3]
+ * section "Low-bit kernels for hybrid attention": unpack and group scale fused into the GEMM).
+ *   x       device [m][k], TGS_BF16 only, 16-byte aligned
+ *   signs   must be NULL: this product is provided for plain-basis weights only, and rotated
+ *           weights are refused with TGS_E_BASIS rather than multiplied in the wrong basis
+ *   y       device [m][n] fp32, 4-byte aligned
+ */
+tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m,
+                        const int8_t* signs, float* y, void* stream);
+
+/*
+ * hadamard_rotate_g128 (device): y[i][b*128 + r] = (1/sqrt(128)) * sum_c H[r][c] * signs[b*128+c]
+ * * x[i][b*128+c] for every row i < m and 128-block b: the block rotation R of [P3] "Block-wise
+ * Hadamard rotation" with n = 128 and H the natural-order Sylvester matrix, signs applied first.
+ *   x        device [m][k], x_dtype TGS_F16, TGS_BF16 or TGS_F32; 16-byte aligned
+ *   k        multiple of 128
+ *   signs    device [k] int8 in {-1, +1}
+ *   y        device [m][k], y_dtype TGS_F16 or TGS_F32; 16-byte aligned; must not overlap x
+ * Computed in fp32 with a fast Walsh-Hadamard butterfly; fp16 output is rounded once.
+ */
+tgs_status hadamard_rotate_g128(const void* x, int32_t x_dtype, int64_t m, int64_t k,
+                                const int8_t* signs, void* y, int32_t y_dtype, void* stream);
+
+/* Static text for a status code. */
+const char* tgs_status_string(tgs_status status);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* tgs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGS_H */

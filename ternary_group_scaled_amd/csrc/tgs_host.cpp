@@ -1,0 +1,356 @@
+// Host side of the C ABI declared in include/tgs.h: packing, unpacking, argument checks and
+// kernel dispatch. Everything here runs on the CPU; device work is only queued by the launch
+// helpers of the .hip files, after every argument has been checked.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "tgs.h"
+#include "tgs_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tgs_status fail(tgs_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tgs_status ok() {
+  g_last_error.clear();
+  return TGS_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t row_bytes(int32_t layout, int64_t k) {
+  if (k < 128 || k % 128 != 0) return 0;
+  if (layout == TGS_LAYOUT_SLOT2) return (size_t)(k / 4);
+  if (layout == TGS_LAYOUT_BASE3) return (size_t)(((k + 4) / 5 + 15) / 16 * 16);
+  return 0;
+}
+
+// Run fn(row_begin, row_end) over [0, n) on up to 16 host threads.
+template <class F>
+void parallel_rows(int64_t n, int64_t work_per_row, F fn) {
+  int64_t threads = (int64_t)std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  if (n * work_per_row < (1 << 20)) threads = 1;
+  threads = std::min(threads, std::max<int64_t>(n, 1));
+  if (threads <= 1) {
+    fn((int64_t)0, n);
+    return;
+  }
+  std::vector<std::thread> pool;
+  const int64_t per = (n + threads - 1) / threads;
+  for (int64_t t = 0; t < threads; ++t) {
+    const int64_t b = t * per, e = std::min(n, b + per);
+    if (b >= e) break;
+    pool.emplace_back([=] { fn(b, e); });
+  }
+  for (auto& th : pool) th.join();
+}
+
+// ---- slot-2: 16 codes per 32-bit word, element j in bits 2j..2j+1, code q = t + 1 --------
+
+bool pack_row_slot2(const int8_t* t, int64_t k, uint8_t* out) {
+  for (int64_t c = 0; c < k; c += 16) {
+    uint32_t word = 0;
+    for (int j = 0; j < 16; ++j) {
+      const int v = t[c + j];
+      if (v < -1 || v > 1) return false;
+      word |= (uint32_t)(v + 1) << (2 * j);
+    }
+    std::memcpy(out + c / 4, &word, 4);
+  }
+  return true;
+}
+
+bool unpack_row_slot2(const uint8_t* in, int64_t k, int8_t* t) {
+  for (int64_t c = 0; c < k; c += 16) {
+    uint32_t word;
+    std::memcpy(&word, in + c / 4, 4);
+    // a slot holding 3 has both bits set
+    if (word & (word >> 1) & 0x55555555u) return false;
+    for (int j = 0; j < 16; ++j) t[c + j] = (int8_t)((int)((word >> (2 * j)) & 3u) - 1);
+  }
+  return true;
+}
+
+// ---- base-3: byte b = sum_{j<5} (t[5b+j] + 1) * 3^j, pad bytes 121 -------------------------
+
+bool pack_row_base3(const int8_t* t, int64_t k, size_t rb, uint8_t* out) {
+  const int64_t used = (k + 4) / 5;
+  for (int64_t b = 0; b < used; ++b) {
+    int value = 0;
+    for (int j = 4; j >= 0; --j) {
+      const int64_t c = 5 * b + j;
+      int digit = 1;
+      if (c < k) {
+        const int v = t[c];
+        if (v < -1 || v > 1) return false;
+        digit = v + 1;
+      }
+      value = value * 3 + digit;
+    }
+    out[b] = (uint8_t)value;
+  }
+  std::memset(out + used, 121, rb - (size_t)used);
+  return true;
+}
+
+bool unpack_row_base3(const uint8_t* in, int64_t k, size_t rb, int8_t* t) {
+  const int64_t used = (k + 4) / 5;
+  for (int64_t b = 0; b < used; ++b) {
+    int value = in[b];
+    if (value > 242) return false;
+    for (int j = 0; j < 5; ++j) {
+      const int digit = value % 3;
+      value /= 3;
+      const int64_t c = 5 * b + j;
+      if (c < k)
+        t[c] = (int8_t)(digit - 1);
+      else if (digit != 1)
+        return false;
+    }
+  }
+  for (size_t b = (size_t)used; b < rb; ++b)
+    if (in[b] != 121) return false;
+  return true;
+}
+
+// ---- descriptor checks -------------------------------------------------------------------
+
+tgs_status check_matrix(const tgs_matrix* w, bool device) {
+  if (!w) return fail(TGS_E_NULL, "matrix descriptor is NULL");
+  if (w->magic != TGS_MAGIC || w->version != TGS_VERSION)
+    return fail(TGS_E_LAYOUT, "bad descriptor magic/version (0x%08x, %u); use tgs_matrix_init", w->magic, w->version);
+  if (w->layout != TGS_LAYOUT_SLOT2 && w->layout != TGS_LAYOUT_BASE3)
+    return fail(TGS_E_LAYOUT, "unknown layout %d", w->layout);
+  if (w->rotated != 0 && w->rotated != 1) return fail(TGS_E_LAYOUT, "rotated flag must be 0 or 1, got %d", w->rotated);
+  if (w->n < 1 || w->k < 128 || w->k % 128 != 0)
+    return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128 (n=%lld, k=%lld)", (long long)w->n,
+                (long long)w->k);
+  if (device && (w->n > INT32_MAX || w->k > (1LL << 30)))
+    return fail(TGS_E_SHAPE, "n or k too large for the device kernels (n=%lld, k=%lld)", (long long)w->n,
+                (long long)w->k);
+  const size_t rb = row_bytes(w->layout, w->k);
+  if (w->code_row_stride < (int64_t)rb || w->code_row_stride % 16 != 0)
+    return fail(TGS_E_SHAPE, "code_row_stride %lld must be a multiple of 16 and >= %zu", (long long)w->code_row_stride,
+                rb);
+  if (!w->codes || !w->scales) return fail(TGS_E_NULL, "codes or scales pointer is NULL");
+  if (!aligned(w->codes, 16)) return fail(TGS_E_ALIGN, "codes must be 16-byte aligned");
+  if (!aligned(w->scales, 2)) return fail(TGS_E_ALIGN, "scales must be 2-byte aligned");
+  return TGS_OK;
+}
+
+tgs_status check_basis(const tgs_matrix* w, const int8_t* signs) {
+  if (w->rotated && !signs)
+    return fail(TGS_E_BASIS, "weights are in the rotated basis: the sign vector of the rotation is required");
+  if (!w->rotated && signs)
+    return fail(TGS_E_BASIS, "signs given for weights in the plain basis; refusing to rotate the activations");
+  return TGS_OK;
+}
+
+tgs_status device_error(hipError_t e, const char* what) {
+  return fail(TGS_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tgs_code_row_bytes(int32_t layout, int64_t k) { return row_bytes(layout, k); }
+
+tgs_status tgs_matrix_init(tgs_matrix* w, int32_t layout, int32_t rotated, int64_t n, int64_t k, const void* codes,
+                           const uint16_t* scales) {
+  if (!w) return fail(TGS_E_NULL, "matrix descriptor is NULL");
+  std::memset(w, 0, sizeof(*w));
+  if (layout != TGS_LAYOUT_SLOT2 && layout != TGS_LAYOUT_BASE3) return fail(TGS_E_LAYOUT, "unknown layout %d", layout);
+  if (n < 1 || k < 128 || k % 128 != 0) return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128");
+  w->magic = TGS_MAGIC;
+  w->version = TGS_VERSION;
+  w->layout = layout;
+  w->rotated = rotated ? 1 : 0;
+  w->n = n;
+  w->k = k;
+  w->code_row_stride = (int64_t)row_bytes(layout, k);
+  w->codes = codes;
+  w->scales = scales;
+  return ok();
+}
+
+tgs_status pack_ternary(int32_t layout, const int8_t* trits, const uint16_t* scales, int64_t n, int64_t k,
+                        void* codes_out, size_t codes_bytes, uint16_t* scales_out) {
+  if (layout != TGS_LAYOUT_SLOT2 && layout != TGS_LAYOUT_BASE3) return fail(TGS_E_LAYOUT, "unknown layout %d", layout);
+  if (n < 1 || k < 128 || k % 128 != 0) return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128");
+  if (!trits || !codes_out) return fail(TGS_E_NULL, "trits or codes_out is NULL");
+  if ((scales == nullptr) != (scales_out == nullptr))
+    return fail(TGS_E_NULL, "scales and scales_out must both be given or both be NULL");
+  const size_t rb = row_bytes(layout, k);
+  if (codes_bytes < rb * (size_t)n)
+    return fail(TGS_E_SIZE, "codes_out holds %zu bytes, %zu needed", codes_bytes, rb * (size_t)n);
+  uint8_t* out = static_cast<uint8_t*>(codes_out);
+  std::vector<char> bad((size_t)n, 0);
+  parallel_rows(n, k, [&](int64_t b, int64_t e) {
+    for (int64_t r = b; r < e; ++r) {
+      const int8_t* t = trits + r * k;
+      uint8_t* o = out + (size_t)r * rb;
+      bool good = layout == TGS_LAYOUT_SLOT2 ? pack_row_slot2(t, k, o) : pack_row_base3(t, k, rb, o);
+      if (!good) bad[(size_t)r] = 1;
+    }
+  });
+  for (int64_t r = 0; r < n; ++r)
+    if (bad[(size_t)r]) return fail(TGS_E_CODE, "row %lld holds a trit outside {-1, 0, +1}", (long long)r);
+  if (scales) std::memcpy(scales_out, scales, sizeof(uint16_t) * (size_t)n * (size_t)(k / 128));
+  return ok();
+}
+
+tgs_status unpack_ternary(const tgs_matrix* w, int8_t* trits_out, uint16_t* scales_out) {
+  tgs_status st = check_matrix(w, false);
+  if (st != TGS_OK) return st;
+  if (!trits_out) return fail(TGS_E_NULL, "trits_out is NULL");
+  const size_t rb = row_bytes(w->layout, w->k);
+  const uint8_t* in = static_cast<const uint8_t*>(w->codes);
+  std::vector<char> bad((size_t)w->n, 0);
+  parallel_rows(w->n, w->k, [&](int64_t b, int64_t e) {
+    for (int64_t r = b; r < e; ++r) {
+      const uint8_t* row = in + (size_t)r * (size_t)w->code_row_stride;
+      int8_t* t = trits_out + r * w->k;
+      bool good = w->layout == TGS_LAYOUT_SLOT2 ? unpack_row_slot2(row, w->k, t) : unpack_row_base3(row, w->k, rb, t);
+      if (!good) bad[(size_t)r] = 1;
+    }
+  });
+  for (int64_t r = 0; r < w->n; ++r)
+    if (bad[(size_t)r])
+      return fail(TGS_E_CODE, "row %lld holds an invalid code (%s)", (long long)r,
+                  w->layout == TGS_LAYOUT_SLOT2 ? "a 2-bit slot of value 3"
+                                                : "a byte above 242, a nonzero trit past K or a pad byte other than 121");
+  if (scales_out) std::memcpy(scales_out, w->scales, sizeof(uint16_t) * (size_t)w->n * (size_t)(w->k / 128));
+  return ok();
+}
+
+tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void* const* xs, int32_t x_dtype,
+                                int64_t m, const int8_t* const* signs, float* const* ys, void* stream) {
+  if (!ws || !xs || !ys) return fail(TGS_E_NULL, "descriptor, input or output array is NULL");
+  if (count < 1 || count > TGS_MAX_BATCH) return fail(TGS_E_SHAPE, "count must be 1..%d, got %d", TGS_MAX_BATCH, count);
+  if (x_dtype != TGS_F16) return fail(TGS_E_DTYPE, "ternary_gemv takes fp16 activations (TGS_F16)");
+  if (m < 1 || m > TGS_MAX_M_GEMV) return fail(TGS_E_SHAPE, "m must be 1..%d, got %lld", TGS_MAX_M_GEMV, (long long)m);
+  for (int32_t i = 0; i < count; ++i) {
+    tgs_status st = check_matrix(&ws[i], true);
+    if (st != TGS_OK) return st;
+    st = check_basis(&ws[i], signs ? signs[i] : nullptr);
+    if (st != TGS_OK) return st;
+    if (!xs[i] || !ys[i]) return fail(TGS_E_NULL, "input or output %d is NULL", i);
+    if (!aligned(xs[i], 16)) return fail(TGS_E_ALIGN, "x must be 16-byte aligned");
+    if (!aligned(ys[i], 4)) return fail(TGS_E_ALIGN, "y must be 4-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // one launch per distinct plan (layout, lanes per row, basis), in call order
+  std::vector<char> done((size_t)count, 0);
+  for (int32_t i = 0; i < count; ++i) {
+    if (done[(size_t)i]) continue;
+    const tgs::GemvPlan plan = tgs::gemv_plan(ws[i].layout, ws[i].k, m, ws[i].rotated);
+    tgs::GemvArgs args;
+    std::memset(&args, 0, sizeof(args));
+    args.m = (int32_t)m;
+    int32_t blocks = 0;
+    for (int32_t j = i; j < count; ++j) {
+      if (done[(size_t)j]) continue;
+      const tgs::GemvPlan pj = tgs::gemv_plan(ws[j].layout, ws[j].k, m, ws[j].rotated);
+      if (pj.layout != plan.layout || pj.lanes != plan.lanes || pj.rotated != plan.rotated) continue;
+      tgs::GemvJob& job = args.job[args.count++];
+      job.codes = static_cast<const uint8_t*>(ws[j].codes);
+      job.scales = ws[j].scales;
+      job.x = static_cast<const uint16_t*>(xs[j]);
+      job.signs = signs ? signs[j] : nullptr;
+      job.y = ys[j];
+      job.stride = ws[j].code_row_stride;
+      job.n = (int32_t)ws[j].n;
+      job.k = (int32_t)ws[j].k;
+      job.block0 = blocks;
+      job.row_blocks = (int32_t)((ws[j].n + plan.rows_per_block - 1) / plan.rows_per_block);
+      blocks += job.row_blocks;
+      done[(size_t)j] = 1;
+    }
+    hipError_t e = tgs::gemv_launch(plan, args, blocks, s);
+    if (e != hipSuccess) return device_error(e, "ternary_gemv launch");
+  }
+  return ok();
+}
+
+tgs_status ternary_gemv(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m, const int8_t* signs, float* y,
+                        void* stream) {
+  const void* xs[1] = {x};
+  const int8_t* ss[1] = {signs};
+  float* ys[1] = {y};
+  if (!w) return fail(TGS_E_NULL, "matrix descriptor is NULL");
+  return ternary_gemv_batched(w, 1, xs, x_dtype, m, ss, ys, stream);
+}
+
+tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m, const int8_t* signs, float* y,
+                        void* stream) {
+  tgs_status st = check_matrix(w, true);
+  if (st != TGS_OK) return st;
+  if (w->rotated)
+    return fail(TGS_E_BASIS, "ternary_gemm multiplies plain-basis weights only; these weights are rotated");
+  if (signs) return fail(TGS_E_BASIS, "signs given for weights in the plain basis");
+  if (x_dtype != TGS_BF16) return fail(TGS_E_DTYPE, "ternary_gemm takes bf16 activations (TGS_BF16)");
+  if (m < 1 || m > (1LL << 30)) return fail(TGS_E_SHAPE, "m must be >= 1, got %lld", (long long)m);
+  if (!x || !y) return fail(TGS_E_NULL, "x or y is NULL");
+  if (!aligned(x, 16)) return fail(TGS_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(y, 4)) return fail(TGS_E_ALIGN, "y must be 4-byte aligned");
+  hipError_t e = tgs::gemm_launch(w->layout, static_cast<const uint8_t*>(w->codes), w->code_row_stride, w->scales,
+                                  w->n, w->k, static_cast<const uint16_t*>(x), m, y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "ternary_gemm launch");
+  return ok();
+}
+
+tgs_status hadamard_rotate_g128(const void* x, int32_t x_dtype, int64_t m, int64_t k, const int8_t* signs, void* y,
+                                int32_t y_dtype, void* stream) {
+  if (!x || !signs || !y) return fail(TGS_E_NULL, "x, signs or y is NULL");
+  if (x_dtype != TGS_F16 && x_dtype != TGS_BF16 && x_dtype != TGS_F32)
+    return fail(TGS_E_DTYPE, "x_dtype must be TGS_F16, TGS_BF16 or TGS_F32");
+  if (y_dtype != TGS_F16 && y_dtype != TGS_F32) return fail(TGS_E_DTYPE, "y_dtype must be TGS_F16 or TGS_F32");
+  if (m < 1 || k < 128 || k % 128 != 0 || m * (k / 128) > (1LL << 40))
+    return fail(TGS_E_SHAPE, "need m >= 1 and k a positive multiple of 128");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(TGS_E_ALIGN, "x and y must be 16-byte aligned");
+  const size_t xe = x_dtype == TGS_F32 ? 4 : 2, ye = y_dtype == TGS_F32 ? 4 : 2;
+  const char *xb = static_cast<const char*>(x), *yb = static_cast<const char*>(y);
+  const size_t xn = (size_t)(m * k) * xe, yn = (size_t)(m * k) * ye;
+  if (xb < yb + yn && yb < xb + xn) return fail(TGS_E_SHAPE, "x and y overlap");
+  hipError_t e = tgs::hadamard_launch(x, x_dtype, m, k, signs, y, y_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "hadamard_rotate_g128 launch");
+  return ok();
+}
+
+const char* tgs_status_string(tgs_status status) {
+  switch (status) {
+    case TGS_OK: return "ok";
+    case TGS_E_NULL: return "null pointer";
+    case TGS_E_SHAPE: return "invalid shape";
+    case TGS_E_ALIGN: return "misaligned buffer";
+    case TGS_E_CODE: return "invalid code";
+    case TGS_E_LAYOUT: return "invalid descriptor or layout";
+    case TGS_E_BASIS: return "basis mismatch";
+    case TGS_E_SIZE: return "buffer too small";
+    case TGS_E_DTYPE: return "unsupported dtype";
+    case TGS_E_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* tgs_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

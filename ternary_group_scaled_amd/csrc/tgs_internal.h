@@ -1,0 +1,53 @@
+// Internal declarations shared by the host entry points (tgs_host.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tgs.h"
+
+namespace tgs {
+
+constexpr int kMaxJobs = TGS_MAX_BATCH;
+
+// One matrix of a batched GEMV launch. All pointers are device pointers.
+struct GemvJob {
+  const uint8_t* codes;    // [n][stride]
+  const uint16_t* scales;  // [n][k/128] fp16 bits
+  const uint16_t* x;       // [m][k] fp16 bits
+  const int8_t* signs;     // [k] or nullptr (plain basis)
+  float* y;                // [m][n]
+  int64_t stride;          // bytes between rows of codes
+  int32_t n;
+  int32_t k;
+  int32_t block0;          // first workgroup of this job in the launch
+  int32_t row_blocks;      // workgroups for this job
+};
+
+struct GemvArgs {
+  GemvJob job[kMaxJobs];
+  int32_t count;
+  int32_t m;
+};
+
+// Shape class of a GEMV launch: every job in one launch shares these.
+struct GemvPlan {
+  int32_t layout;     // TGS_LAYOUT_*
+  int32_t lanes;      // lanes per row (16, 32 or 64)
+  int32_t m;          // activation rows
+  int32_t rotated;    // 0 or 1
+  int32_t rows_per_block;
+};
+
+// Launch helpers implemented in the .hip files. They only queue work; all argument checks
+// happen in tgs_host.cpp before they are called.
+GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated);
+hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream);
+
+hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
+                       const uint16_t* x_bf16, int64_t m, float* y, hipStream_t stream);
+
+hipError_t hadamard_launch(const void* x, int32_t x_dtype, int64_t m, int64_t k, const int8_t* signs, void* y,
+                           int32_t y_dtype, hipStream_t stream);
+
+}  // namespace tgs

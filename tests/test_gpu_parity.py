@@ -1,0 +1,221 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Tolerance per element: |y - y_ref| <= 1e-3 * sum_k |s t xr| + 1e-6 (the oracle's `bound`), with xr the
+rotated activation for rotated weights. Packing must be bit-exact. Exact equalities hold where every
+partial sum is exactly representable in fp32 (integer activations, power-of-two scales).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (assert_within_bound, make_signs, make_weights, make_x_bf16_bits, make_x_f16,
+                      oracle_product)
+
+torch = pytest.importorskip("torch")
+import ternary_group_scaled_amd as tgs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+LAYOUTS = [tgs.SLOT2, tgs.BASE3]
+LNAME = {tgs.SLOT2: "slot2", tgs.BASE3: "base3"}
+
+
+def _packed(layout, t, s, rotated=False):
+    return tgs.PackedMatrix.from_trits(layout, t, s, device=DEV, rotated=rotated)
+
+
+def _x_dev(x16):
+    return torch.from_numpy(x16.view(np.int16).copy()).to(DEV).view(torch.float16)
+
+
+def _gemv(layout, t, s, x16, signs=None):
+    w = _packed(layout, t, s, rotated=signs is not None)
+    sg = torch.from_numpy(signs).to(DEV) if signs is not None else None
+    y = tgs.ternary_gemv(w, _x_dev(x16), signs=sg)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# ------------------------------------------------------------------------------ small configuration
+
+def test_config1_slot2_gemv():
+    """256 x 1024 GEMV, codes P(0)=0.4, scales |N(0,0.02)|+1e-4, x fp16 N(0,1), seed 0."""
+    t, s = make_weights(0, "config1", 256, 1024, 0.4)
+    x16 = make_x_f16(0, "config1", 1, 1024)
+    codes, _ = tgs.pack_ternary(tgs.SLOT2, t, s)
+    assert (codes == oracle.pack(tgs.SLOT2, t)).all()
+    back, _ = tgs.unpack_ternary(tgs.SLOT2, codes, s, 1024)
+    assert (back == t).all()
+    y = _gemv(tgs.SLOT2, t, s, x16)
+    y_ref, bound = oracle_product(tgs.SLOT2, t, s, x16.view(np.uint16), oracle.X_F16)
+    assert_within_bound(y, y_ref, bound, "config1")
+    y2 = _gemv(tgs.SLOT2, t, s, x16)
+    assert (y2.view(np.uint32) == y.view(np.uint32)).all()  # run-to-run bitwise determinism
+
+
+SHAPES = [(1, 128), (17, 256), (300, 1024), (129, 4096), (64, 5120), (33, 12288), (40, 17408), (70, 640)]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 8])
+def test_gemv_matches_oracle(layout, n, k, m):
+    t, s = make_weights(n + k, f"gemv{layout}", n, k, 0.4 if layout == tgs.SLOT2 else 0.5)
+    x16 = make_x_f16(m, f"gemv{n}x{k}", m, k)
+    y = _gemv(layout, t, s, x16)
+    y_ref, bound = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16)
+    assert_within_bound(y, y_ref, bound, f"{LNAME[layout]} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+@pytest.mark.parametrize("n,k", [(1, 128), (33, 640), (100, 5120), (20, 17408), (65, 4096)])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_rotated_gemv_matches_oracle(layout, n, k, m):
+    t, s = make_weights(n * 3 + k, f"rot{layout}", n, k, 0.5)
+    x16 = make_x_f16(m + 7, f"rot{n}x{k}", m, k)
+    sg = make_signs(k, "rot", k)
+    y = _gemv(layout, t, s, x16, signs=sg)
+    y_ref, bound = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg)
+    assert_within_bound(y, y_ref, bound, f"rotated {LNAME[layout]} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+def test_integer_inputs_are_exact(layout):
+    # integer x in [-4, 4] and power-of-two scales: every partial sum is an fp32-exact integer
+    # multiple of a power of two, so any summation order gives the oracle's value bit for bit
+    n, k, m = 200, 12288, 2
+    t, _ = make_weights(5, "exact", n, k, 0.4)
+    expo = synth.trits(5, 77, (n, k // 128), 0.0).astype(np.int64) - 3
+    s = np.ldexp(1.0, expo).astype(np.float16)
+    xi = synth.trits(6, 1, (m, k), 0.2).astype(np.int64) * 4 + synth.trits(6, 2, (m, k), 0.3)
+    x16 = xi.astype(np.float16)
+    y = _gemv(layout, t, s, x16)
+    y_ref, _ = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16)
+    assert (y.astype(np.float64) == y_ref).all()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+def test_special_rows(layout):
+    # all +1 rows give s * sum x, all -1 rows -s * sum x, all-zero rows 0, and one-hot rows s * t * x_j,
+    # each within the tolerance bound (the oracle's values are exact; see test_oracle_pins)
+    k = 1024
+    t = np.zeros((5, k), dtype=np.int8)
+    t[0] = 1
+    t[1] = -1
+    t[3, 517] = 1
+    t[4, 1023] = -1
+    s = synth.scales_f16(1, 2, (5, k // 128))
+    x16 = make_x_f16(3, "special", 1, k)
+    y = _gemv(layout, t, s, x16)
+    y_ref, bound = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16)
+    assert_within_bound(y, y_ref, bound, "special rows")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+def test_batched_equals_single_calls(layout):
+    shapes = [(300, 4096), (64, 4096), (96, 12288), (5, 1024)]
+    ws, xs, ys, singles = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        t, s = make_weights(i, f"batch{layout}", n, k, 0.4)
+        x16 = make_x_f16(i, "batch", 1, k)
+        ws.append(_packed(layout, t, s))
+        xs.append(_x_dev(x16))
+        ys.append(torch.empty((1, n), dtype=torch.float32, device=DEV))
+        singles.append(_gemv(layout, t, s, x16))
+    tgs.ternary_gemv_batched(ws, xs, ys)
+    torch.cuda.synchronize()
+    for y, ref in zip(ys, singles):
+        assert (y.cpu().numpy().view(np.uint32) == ref.view(np.uint32)).all()
+
+
+def test_batched_mixed_layouts_and_bases():
+    k = 1280
+    sg = make_signs(1, "mixed", k)
+    cases = [(tgs.SLOT2, False), (tgs.BASE3, True), (tgs.SLOT2, True), (tgs.BASE3, False)]
+    ws, xs, ys, signs, refs = [], [], [], [], []
+    for i, (layout, rot) in enumerate(cases):
+        t, s = make_weights(i, "mixed", 50 + i, k, 0.5)
+        x16 = make_x_f16(i, "mixed", 2, k)
+        ws.append(_packed(layout, t, s, rotated=rot))
+        xs.append(_x_dev(x16))
+        ys.append(torch.empty((2, 50 + i), dtype=torch.float32, device=DEV))
+        signs.append(torch.from_numpy(sg).to(DEV) if rot else None)
+        refs.append(oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg if rot else None))
+    tgs.ternary_gemv_batched(ws, xs, ys, signs=signs)
+    torch.cuda.synchronize()
+    for y, (y_ref, bound) in zip(ys, refs):
+        assert_within_bound(y.cpu().numpy(), y_ref, bound, "mixed batch")
+
+
+def test_wrong_basis_is_refused_on_the_device_path():
+    t, s = make_weights(1, "basis", 8, 256, 0.4)
+    w = _packed(tgs.SLOT2, t, s, rotated=True)
+    with pytest.raises(tgs.TgsError) as info:
+        tgs.ternary_gemv(w, _x_dev(make_x_f16(1, "basis", 1, 256)))
+    assert info.value.name == "TGS_E_BASIS"
+
+
+# ------------------------------------------------------------------------------ Hadamard
+
+@pytest.mark.parametrize("in_dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("out_dtype", ["f32", "f16"])
+def test_hadamard_rotate_matches_oracle(in_dtype, out_dtype):
+    m, k = 3, 1280
+    sg = make_signs(2, "had", k)
+    xd = synth.normal(2, 9, (m, k))
+    if in_dtype == "f16":
+        host = xd.astype(np.float16)
+        xt = torch.from_numpy(host.copy()).to(DEV)
+        xref = host.astype(np.float64)
+    elif in_dtype == "bf16":
+        bits = synth.bf16_bits(xd)
+        xt = torch.from_numpy(bits.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+        xref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        host = xd.astype(np.float32)
+        xt = torch.from_numpy(host.copy()).to(DEV)
+        xref = host.astype(np.float64)
+    od = torch.float32 if out_dtype == "f32" else torch.float16
+    y = tgs.hadamard_rotate_g128(xt, torch.from_numpy(sg).to(DEV), out_dtype=od)
+    torch.cuda.synchronize()
+    ref = oracle.rotate(xref, sg)
+    got = y.float().cpu().numpy().astype(np.float64)
+    blk_l1 = np.repeat(np.abs(xref).reshape(m, -1, 128).sum(axis=2), 128, axis=1) / np.sqrt(128)
+    if out_dtype == "f32":
+        assert (np.abs(got - ref) <= 1e-6 * blk_l1 + 1e-30).all()
+    else:
+        assert (np.abs(got - ref) <= 2.0 ** -11 * np.abs(ref) + 1e-6 * blk_l1 + 2.0 ** -25).all()
+
+
+# ------------------------------------------------------------------------------ GEMM
+
+def _gemm(layout, t, s, xbits):
+    w = _packed(layout, t, s)
+    xt = torch.from_numpy(xbits.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    y = tgs.ternary_gemm(w, xt)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+@pytest.mark.parametrize("n,k", [(128, 128), (300, 1024), (129, 2048), (64, 640)])
+@pytest.mark.parametrize("m", [1, 16, 50, 128, 200])
+def test_gemm_matches_oracle(layout, n, k, m):
+    t, s = make_weights(n + k + m, f"gemm{layout}", n, k, 0.4)
+    xb = make_x_bf16_bits(m, f"gemm{n}", m, k)
+    y = _gemm(layout, t, s, xb)
+    y_ref, bound = oracle_product(layout, t, s, xb, oracle.X_BF16)
+    assert_within_bound(y, y_ref, bound, f"gemm {LNAME[layout]} {n}x{k} m={m}")
+
+
+def test_gemm_integer_inputs_are_exact_and_match_gemv():
+    n, k, m = 160, 2048, 1
+    t, _ = make_weights(9, "gemmexact", n, k, 0.4)
+    s = np.ldexp(1.0, synth.trits(9, 5, (n, k // 128), 0.0).astype(np.int64)).astype(np.float16)
+    xi = (synth.trits(9, 6, (m, k), 0.2).astype(np.int64) * 3).astype(np.float32)
+    y_gemm = _gemm(tgs.SLOT2, t, s, synth.bf16_bits(xi))
+    y_gemv = _gemv(tgs.SLOT2, t, s, xi.astype(np.float16))
+    y_ref, _ = oracle_product(tgs.SLOT2, t, s, xi.astype(np.float16).view(np.uint16), oracle.X_F16)
+    assert (y_gemm.astype(np.float64) == y_ref).all()
+    assert (y_gemm.view(np.uint32) == y_gemv.view(np.uint32)).all()

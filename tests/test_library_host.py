@@ -1,0 +1,170 @@
+"""Host-side tests of the C-ABI library: load, exports, packing and argument checks.
+
+No device work is queued here: every call either runs on the host (pack/unpack) or is
+rejected by the host-side checks before any HIP call, so these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import ternary_group_scaled_amd as tgs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CONFIG_K = (128, 1024, 4096, 5120, 12288, 17408)
+
+
+def test_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "tgs.h")).read()
+    declared = set(re.findall(r"^\s*(?:tgs_status|size_t|const char\*)\s+(\w+)\s*\(", header, re.M))
+    assert {"pack_ternary", "unpack_ternary", "ternary_gemv", "ternary_gemm", "hadamard_rotate_g128"} <= declared
+    lib = ctypes.CDLL(tgs.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(tgs.EXPORTS)
+
+
+def test_status_strings():
+    for code in range(10):
+        assert tgs.status_string(code)
+    assert tgs.status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("k", CONFIG_K)
+def test_row_bytes_match_oracle(k):
+    for layout in (tgs.SLOT2, tgs.BASE3):
+        assert tgs.code_row_bytes(layout, k) == oracle.row_bytes(layout, k)
+    assert tgs.code_row_bytes(tgs.SLOT2, 100) == 0
+    assert tgs.code_row_bytes(7, 128) == 0
+
+
+@pytest.mark.parametrize("layout", [tgs.SLOT2, tgs.BASE3])
+@pytest.mark.parametrize("k", CONFIG_K)
+def test_pack_bit_exact_vs_oracle(layout, k):
+    n = 37
+    t = synth.trits(1, k * 10 + layout, (n, k), 0.4 if layout == tgs.SLOT2 else 0.5)
+    s = synth.scales_f16(1, k, (n, k // 128))
+    codes, s_out = tgs.pack_ternary(layout, t, s)
+    assert (codes == oracle.pack(layout, t)).all()
+    assert (s_out.view(np.uint16) == s.view(np.uint16)).all()
+    back, s_back = tgs.unpack_ternary(layout, codes, s, k)
+    assert (back == t).all()
+    assert (s_back.view(np.uint16) == s.view(np.uint16)).all()
+
+
+def test_pack_large_parallel_path_is_exact():
+    # big enough for the multi-threaded packer
+    t = synth.trits(2, 3, (300, 12288), 0.4)
+    for layout in (tgs.SLOT2, tgs.BASE3):
+        codes, _ = tgs.pack_ternary(layout, t)
+        assert (codes == oracle.pack(layout, t)).all()
+
+
+def test_unpack_reads_the_oracle_bytes():
+    t = synth.trits(3, 3, (5, 1024), 0.4)
+    for layout in (tgs.SLOT2, tgs.BASE3):
+        s = np.ones((5, 8), dtype=np.float16)
+        back, _ = tgs.unpack_ternary(layout, oracle.pack(layout, t), s, 1024)
+        assert (back == t).all()
+
+
+def _expect(status_name, fn, *args):
+    with pytest.raises(tgs.TgsError) as info:
+        fn(*args)
+    assert info.value.name == status_name, str(info.value)
+
+
+def test_pack_errors():
+    t = np.zeros((2, 128), dtype=np.int8)
+    t[1, 77] = 2
+    _expect("TGS_E_CODE", tgs.pack_ternary, tgs.SLOT2, t)
+    _expect("TGS_E_CODE", tgs.pack_ternary, tgs.BASE3, t)
+    _expect("TGS_E_SHAPE", tgs.pack_ternary, tgs.SLOT2, np.zeros((2, 100), dtype=np.int8))
+    _expect("TGS_E_LAYOUT", tgs.pack_ternary, 3, np.zeros((2, 128), dtype=np.int8))
+    lib = tgs.lib()
+    out = np.zeros(10, dtype=np.uint8)
+    good = np.zeros((2, 128), dtype=np.int8)
+    assert lib.pack_ternary(tgs.SLOT2, good.ctypes.data, None, 2, 128, out.ctypes.data, out.nbytes, None) == 7
+    assert lib.pack_ternary(tgs.SLOT2, None, None, 2, 128, out.ctypes.data, out.nbytes, None) == 1
+
+
+def test_unpack_errors():
+    s = np.ones((1, 1), dtype=np.float16)
+    slot = np.full((1, 32), 0x55, dtype=np.uint8)
+    slot[0, 9] = 0x7F  # slot value 3
+    _expect("TGS_E_CODE", tgs.unpack_ternary, tgs.SLOT2, slot, s, 128)
+    b3 = np.full((1, 32), 121, dtype=np.uint8)
+    b3[0, 3] = 243
+    _expect("TGS_E_CODE", tgs.unpack_ternary, tgs.BASE3, b3, s, 128)
+    b3 = np.full((1, 32), 121, dtype=np.uint8)
+    b3[0, 30] = 0  # pad byte must be 121
+    _expect("TGS_E_CODE", tgs.unpack_ternary, tgs.BASE3, b3, s, 128)
+    b3 = np.full((1, 32), 121, dtype=np.uint8)
+    b3[0, 25] = 121 + 2 * 27  # trit 128 (past K) set to +1
+    _expect("TGS_E_CODE", tgs.unpack_ternary, tgs.BASE3, b3, s, 128)
+
+
+def _fake_matrix(layout=tgs.SLOT2, rotated=0, n=4, k=256, codes=0x100000, scales=0x200000):
+    m = tgs.Matrix()
+    assert tgs.lib().tgs_matrix_init(ctypes.byref(m), layout, rotated, n, k, codes, scales) == 0
+    return m
+
+
+def _gemv(m, x=0x300000, x_dtype=tgs.F16, rows=1, signs=None, y=0x400000):
+    return tgs.lib().ternary_gemv(ctypes.byref(m), x, x_dtype, rows, signs, y, None)
+
+
+def test_device_call_argument_checks_happen_before_any_device_work():
+    lib = tgs.lib()
+    assert _gemv(_fake_matrix(rotated=1)) == 6            # rotated weights need signs
+    assert _gemv(_fake_matrix(rotated=0), signs=0x500000) == 6  # plain weights refuse signs
+    assert _gemv(_fake_matrix(), x_dtype=tgs.BF16) == 8
+    assert _gemv(_fake_matrix(), rows=0) == 2
+    assert _gemv(_fake_matrix(), rows=9) == 2
+    assert _gemv(_fake_matrix(), x=0x300004) == 3          # x must be 16-byte aligned
+    assert _gemv(_fake_matrix(), y=0x400002) == 3
+    assert _gemv(_fake_matrix(codes=0x100008)) == 3        # codes 16-byte aligned
+    assert _gemv(_fake_matrix(), x=None) == 1
+    bad = _fake_matrix()
+    bad.magic = 0
+    assert _gemv(bad) == 5
+    bad = _fake_matrix()
+    bad.layout = 9
+    assert _gemv(bad) == 5
+    bad = _fake_matrix()
+    bad.k = 200
+    assert _gemv(bad) == 2
+    bad = _fake_matrix()
+    bad.code_row_stride = 48  # < 64 bytes per row at k = 256
+    assert _gemv(bad) == 2
+    assert "rotated" in lib.tgs_last_error().decode() or lib.tgs_last_error()
+    # ternary_gemm
+    m = _fake_matrix()
+    assert lib.ternary_gemm(ctypes.byref(m), 0x300000, tgs.F16, 4, None, 0x400000, None) == 8
+    assert lib.ternary_gemm(ctypes.byref(_fake_matrix(rotated=1)), 0x300000, tgs.BF16, 4, 0x500000, 0x400000,
+                            None) == 6
+    assert lib.ternary_gemm(ctypes.byref(m), 0x300000, tgs.BF16, 0, None, 0x400000, None) == 2
+    # hadamard_rotate_g128
+    assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 200, 0x500000, 0x400000, tgs.F32, None) == 2
+    assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, 0x500000, 0x400000, tgs.BF16, None) == 8
+    assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, None, 0x400000, tgs.F32, None) == 1
+    assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, 0x500000, 0x300100, tgs.F32, None) == 2  # overlap
+    # batched
+    ms = (tgs.Matrix * 2)(_fake_matrix(), _fake_matrix(rotated=1))
+    xp = (ctypes.c_void_p * 2)(0x300000, 0x300000)
+    yp = (ctypes.c_void_p * 2)(0x400000, 0x410000)
+    assert lib.ternary_gemv_batched(ms, 2, xp, tgs.F16, 1, None, yp, None) == 6
+    assert lib.ternary_gemv_batched(ms, 0, xp, tgs.F16, 1, None, yp, None) == 2
+    assert lib.ternary_gemv_batched(ms, 33, xp, tgs.F16, 1, None, yp, None) == 2
+
+
+def test_matrix_init_rejects_bad_shapes():
+    m = tgs.Matrix()
+    assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 0, 0, 128, 1, 1) == 2
+    assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 0, 4, 129, 1, 1) == 2
+    assert tgs.lib().tgs_matrix_init(ctypes.byref(m), 5, 0, 4, 128, 1, 1) == 5
+    assert m.magic == 0
