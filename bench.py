@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the ternary group-scaled GEMV/GEMM library on one MI355X.
+
+Default workload: the 8B-class decode GEMV set at M = 1 in the 2-bit-slot layout: 36 layers,
+each with q 4096x4096, k 1024x4096, v 1024x4096, o 4096x4096, gate 12288x4096, up 12288x4096 and
+down 4096x12288 (N x K), every matrix its own buffer (1.845 GB of packed weights, far more than
+the 256 MB last-level cache). One step = one pass over all 252 matrices in layer order, where
+matrices that read the same input share a launch (q/k/v, gate/up): 144 launches, captured once
+in a HIP graph and replayed. Inputs are seeded synthetic data already resident in HBM.
+
+Prints one JSON line (rank 0). `value` is achieved algorithmic GB/s for the whole pass:
+packed codes + fp16 scales + fp16 activations read + fp32 outputs written, divided by the
+wall time of a step. `roofline` reports the same bytes over the GEMV kernel's own average
+duration (HIP events around each launch, on the launch stream), against the 8 TB/s HBM peak.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+
+Other workloads (`--workload base3|gemm|rotated|config1`) print lines of their own; they are
+measurements for the design notes, not the headline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "ternary GEMV achieved HBM GB/s (% of peak) + weight-tokens/s, 8B-class set, M=1"
+
+LAYER_8B = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
+            ("gate", 12288, 4096), ("up", 12288, 4096), ("down", 4096, 12288)]
+# launches of one layer, in order; matrices in a group read the same activation vector
+GROUPS_8B = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="8b", choices=["8b", "base3", "rotated", "gemm", "config1"])
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--mode", default="layer", choices=["layer", "fused-layer", "set"],
+                    help="launch grouping for the 8B set: same-input groups (144 launches), one launch per "
+                         "layer (36), or the whole set in as few launches as possible")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def build_matrix(torch, tgs, synth, layout, seed, tag, n, k, p_zero, rotated=False):
+    t = synth.trits(seed, synth.stream_id(tag, "codes"), (n, k), p_zero)
+    s = synth.scales_f16(seed, synth.stream_id(tag, "scales"), (n, k // 128))
+    codes, scales = tgs.pack_ternary(layout, t, s)
+    w = tgs.PackedMatrix(layout, torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda(), k,
+                         rotated=rotated)
+    return w, codes, scales
+
+
+def x_f16_dev(torch, synth, seed, tag, m, k):
+    x = synth.x_f16(seed, synth.stream_id(tag, "x"), (m, k))
+    return torch.from_numpy(x.view(np.int16).copy()).cuda().view(torch.float16), x
+
+
+# ----------------------------------------------------------------------------- timing helpers
+
+def time_graph(torch, fn, steps, warmup):
+    """Capture fn() once into a graph; replay warmup + steps times; ms per replay (event timing)."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        fn()  # eager run before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps, graph
+
+
+def time_launches(torch, launches, reps):
+    """Average duration of each launch (HIP events right around it on its stream), in ms."""
+    stream = torch.cuda.current_stream()
+    totals = np.zeros(len(launches))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+    for _ in range(reps):
+        for (a, b), fn in zip(evs, launches):
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        totals += np.array([a.elapsed_time(b) for a, b in evs])
+    return totals / reps
+
+
+# ----------------------------------------------------------------------------- 8B decode set
+
+def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_name=None):
+    layers = args.layers
+    log(f"[bench] building {layers} layers x {len(LAYER_8B)} matrices ({'slot-2' if layout == 1 else 'base-3'})")
+    t0 = time.time()
+    mats, host = [], []
+    for L in range(layers):
+        d = {}
+        for name, n, k in LAYER_8B:
+            w, codes, scales = build_matrix(torch, tgs, synth, layout, 0, f"{tag}/L{L}/{name}", n, k, p_zero)
+            d[name] = w
+            if L == 0:
+                host.append((name, codes, scales, n, k))
+        mats.append(d)
+    inputs, outputs = [], []
+    for L in range(layers):
+        xs = {}
+        for grp in GROUPS_8B:
+            k = mats[L][grp[0]].k
+            xs[grp] = x_f16_dev(torch, synth, 0, f"{tag}/L{L}/{grp[0]}", 1, k)
+        inputs.append(xs)
+        outputs.append({name: torch.empty((1, n), dtype=torch.float32, device="cuda") for name, n, _ in LAYER_8B})
+    torch.cuda.synchronize()
+    log(f"[bench] built in {time.time() - t0:.1f}s")
+
+    w_bytes = sum(mats[L][name].nbytes for L in range(layers) for name, _, _ in LAYER_8B)
+    x_bytes = sum(inputs[L][g][0].numel() * 2 for L in range(layers) for g in GROUPS_8B)
+    y_bytes = sum(outputs[L][name].numel() * 4 for L in range(layers) for name, _, _ in LAYER_8B)
+    total_bytes = w_bytes + x_bytes + y_bytes
+
+    # launch list for one pass
+    def group_launch(L, grp):
+        ws = [mats[L][nm] for nm in grp]
+        xs = [inputs[L][grp][0]] * len(grp)
+        ys = [outputs[L][nm] for nm in grp]
+        return lambda: tgs.ternary_gemv_batched(ws, xs, ys)
+
+    if args.mode == "layer":
+        launches = [group_launch(L, g) for L in range(layers) for g in GROUPS_8B]
+    else:
+        per = []
+        for L in range(layers):
+            for g in GROUPS_8B:
+                for nm in g:
+                    per.append((mats[L][nm], inputs[L][g][0], outputs[L][nm]))
+        chunk = len(LAYER_8B) if args.mode == "fused-layer" else tgs.MAX_BATCH
+        launches = []
+        for i in range(0, len(per), chunk):
+            part = per[i:i + chunk]
+            launches.append((lambda p: lambda: tgs.ternary_gemv_batched([a for a, _, _ in p], [b for _, b, _ in p],
+                                                                        [c for _, _, c in p]))(part))
+
+    def one_pass():
+        for fn in launches:
+            fn()
+
+    log(f"[bench] timing {args.steps} graph replays of {len(launches)} launches ({args.mode})")
+    ms, _graph = time_graph(torch, one_pass, args.steps, args.warmup)
+    per_launch_ms = time_launches(torch, launches, reps=max(3, args.steps // 4))
+    kernel_ms = float(per_launch_ms.sum())
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    kernel_gbs = total_bytes / (kernel_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms * 1e3:.1f} us -> {gbs:.0f} GB/s; sum of kernel times {kernel_ms * 1e3:.1f} us -> "
+        f"{kernel_gbs:.0f} GB/s")
+
+    # parity spot check of layer 0 against the oracle on sampled rows
+    check_layer0(torch, host, inputs[0], outputs[0], layout)
+
+    result = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": workload_name or "8B-class decode GEMV set, 2-bit-slot layout, M=1",
+                   "layers": layers, "matrices": layers * len(LAYER_8B), "launches_per_step": len(launches),
+                   "launch_mode": args.mode, "p_zero": p_zero, "algorithmic_bytes_per_step": int(total_bytes),
+                   "weight_bytes_per_step": int(w_bytes)},
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(1e3 / ms, 1),
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_kernel", "avg_launch_us": round(kernel_ms * 1e3 / len(launches), 3),
+                     "bytes_per_launch_avg": int(total_bytes / len(launches))},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_8b(host, layout, args.cpu_seconds, ms, total_bytes / layers)
+    return result
+
+
+def check_layer0(torch, host, xs, ys, layout):
+    import oracle
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for name, codes, scales, n, k in host:
+        grp = [g for g in GROUPS_8B if name in g][0]
+        x16 = xs[grp][1]
+        rows = np.sort(rng.choice(n, size=min(n, 64), replace=False))
+        y_ref, bound = oracle.matmul(layout, codes, scales, k, x16.view(np.uint16), oracle.X_F16, rows=rows)
+        y = ys[name].cpu().numpy()[:, rows].astype(np.float64)
+        ratio = float((np.abs(y - y_ref) / bound).max())
+        worst = max(worst, ratio)
+        if ratio > 1.0:
+            raise SystemExit(f"parity check failed for layer 0 {name}: max err/bound {ratio:.3g}")
+    log(f"[bench] layer-0 sampled parity ok (max err/bound {worst:.3g})")
+
+
+def cpu_baseline_8b(host, layout, seconds, gpu_ms, layer_bytes):
+    """The fp64 oracle on the host cores over layer-0's 7 matrices, repeated for ~`seconds`."""
+    import oracle
+    import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    xs = {name: synth.x_f16(1, synth.stream_id("cpu", name), (1, k)) for name, _, _, _, k in host}
+    t0 = time.time()
+    passes = 0
+    while True:
+        for name, codes, scales, n, k in host:
+            oracle.matmul(layout, codes, scales, k, xs[name].view(np.uint16), oracle.X_F16)
+        passes += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = (time.time() - t0) / passes
+    layer_gbs = layer_bytes / dt / 1e9
+    return {"value": round(layer_gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 of the set (7 matrices, {int(layer_bytes)} algorithmic bytes), {passes} passes in "
+                      f"{time.time() - t0:.1f}s; full-set equivalent {1.0 / (dt * 36):.3f} steps/s",
+            "gpu_speedup": round((dt * 36) / (gpu_ms * 1e-3), 1)}
+
+
+# ----------------------------------------------------------------------------- other workloads
+
+def bench_rotated(args, torch, tgs, synth):
+    """27B-class rotated-basis GEMV, base-3: gate/up 17408x5120 and down 5120x17408 per layer."""
+    layers = min(args.layers, 64)
+    shapes = [("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408)]
+    res = []
+    for m in (1, 8):
+        log(f"[bench] rotated base-3 set, {layers} layers, m={m}")
+        mats, xs, ys, sg = [], [], [], {}
+        for k in (5120, 17408):
+            sg[k] = torch.from_numpy(synth.signs(0, synth.stream_id("rot/signs", k), k)).cuda()
+        for L in range(layers):
+            for name, n, k in shapes:
+                w, _, _ = build_matrix(torch, tgs, synth, 2, 0, f"rot/L{L}/{name}", n, k, 0.5, rotated=True)
+                mats.append(w)
+                ys.append(torch.empty((m, n), dtype=torch.float32, device="cuda"))
+            xg = x_f16_dev(torch, synth, 0, f"rot/L{L}/in{m}", m, 5120)[0]
+            xd = x_f16_dev(torch, synth, 0, f"rot/L{L}/mid{m}", m, 17408)[0]
+            xs += [xg, xg, xd]
+        nb = sum(w.nbytes for w in mats) + sum(x.numel() * 2 for x in xs[::3]) + sum(
+            x.numel() * 2 for x in xs[2::3]) + sum(y.numel() * 4 for y in ys)
+        launches = []
+        for L in range(layers):
+            i = 3 * L
+            launches.append((lambda a, b, c, s: lambda: tgs.ternary_gemv_batched(a, b, c, signs=s))(
+                mats[i:i + 2], xs[i:i + 2], ys[i:i + 2], [sg[5120]] * 2))
+            launches.append((lambda a, b, c, s: lambda: tgs.ternary_gemv_batched(a, b, c, signs=s))(
+                mats[i + 2:i + 3], xs[i + 2:i + 3], ys[i + 2:i + 3], [sg[17408]]))
+
+        def one_pass():
+            for fn in launches:
+                fn()
+
+        ms, _ = time_graph(torch, one_pass, args.steps, args.warmup)
+        kms = float(time_launches(torch, launches, reps=3).sum())
+        res.append({"metric": "rotated ternary GEMV achieved GB/s, 27B-class set", "value": round(nb / ms / 1e6, 1),
+                    "unit": "GB/s", "m": m, "ms_per_step": round(ms, 4), "kernel_gbs": round(nb / kms / 1e6, 1),
+                    "config": {"workload": f"27B-class rotated GEMV set, base-3, {layers} layers, M={m}",
+                               "bytes_per_step": int(nb)}})
+        del mats, xs, ys
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_gemm(args, torch, tgs, synth):
+    """27B-class prefill GEMM, slot-2: gate/up 17408x5120 and down 5120x17408, M in {16, 128, 2048}."""
+    res = []
+    copies = 16
+    for n, k in ((17408, 5120), (5120, 17408)):
+        ws = [build_matrix(torch, tgs, synth, 1, 0, f"gemm/{n}x{k}/{i}", n, k, 0.4)[0] for i in range(copies)]
+        for m in (16, 128, 2048):
+            xb = synth.x_bf16_bits(0, synth.stream_id("gemm/x", m, k), (m, k))
+            x = torch.from_numpy(xb.view(np.int16).copy()).cuda().view(torch.bfloat16)
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            launches = [(lambda w: lambda: tgs.ternary_gemm(w, x, y))(w) for w in ws]
+
+            def one_pass():
+                for fn in launches:
+                    fn()
+
+            ms, _ = time_graph(torch, one_pass, max(2, args.steps // 4), 1)
+            per = ms / copies
+            flops = 2.0 * m * n * k
+            nb = ws[0].nbytes + m * k * 2 + m * n * 4
+            res.append({"metric": "ternary GEMM TFLOP/s", "value": round(flops / per / 1e9, 2), "unit": "TFLOP/s",
+                        "pct_of_bf16_peak": round(100 * flops / per / 1e9 / BF16_MFMA_PEAK_TFLOPS, 2),
+                        "gbs": round(nb / per / 1e6, 1), "us": round(per * 1e3, 2),
+                        "config": {"workload": f"27B-class prefill GEMM {n}x{k}, M={m}, slot-2"}})
+            log(f"[bench] gemm {n}x{k} m={m}: {per * 1e3:.1f} us, {flops / per / 1e9:.1f} TFLOP/s")
+        del ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the library's hot path is a single-GPU "
+                                   "kernel set; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    import ternary_group_scaled_amd as tgs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.workload == "8b":
+        out = [bench_8b(args, torch, tgs, synth)]
+    elif args.workload == "base3":
+        out = [bench_8b(args, torch, tgs, synth, layout=2, p_zero=0.5, tag="8b3",
+                        workload_name="8B-class decode GEMV set, base-3 layout, M=1")]
+    elif args.workload == "rotated":
+        out = bench_rotated(args, torch, tgs, synth)
+    elif args.workload == "gemm":
+        out = bench_gemm(args, torch, tgs, synth)
+    else:
+        args.layers = 1
+        out = [bench_8b(args, torch, tgs, synth)]
+    for line in out:
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

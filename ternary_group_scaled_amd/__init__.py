@@ -44,7 +44,7 @@ class Matrix(ctypes.Structure):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m ternary_group_scaled_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python ternary_group_scaled_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 _lib = ctypes.CDLL(LIB_PATH)
 

@@ -1,12 +1,13 @@
 """Build libtgs.so (the HIP library behind include/tgs.h) in-tree for gfx950.
 
 Each source compiles separately (in parallel) with hipcc, then one shared library is linked
-next to this file. Usage: python -m ternary_group_scaled_amd.build
+next to this file. Usage: python ternary_group_scaled_amd/build.py
 """
 from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -26,12 +27,27 @@ def _hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+def _check_no_scratch(src: str, remarks: str) -> None:
+    """Every kernel must keep its values in registers: a kernel that spills to scratch is a build error."""
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) != 0:
+            raise RuntimeError(f"{src}: kernel {name} uses {m.group(1)} bytes/lane of scratch (register spill)")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    remarks = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *remarks, "-c", os.path.join(CSRC, src), "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{proc.stdout}\n{proc.stderr}")
+    if remarks:
+        _check_no_scratch(src, proc.stderr)
     return obj
 
 

@@ -14,22 +14,28 @@
 // chunks of a row, so every load instruction is a fully used, contiguous span.
 //
 // Decode without unpacking (slot-2). Codes q = t + 1 sit in 2-bit slots; a 32-bit word holds 16
-// of them, element j in bits 2j..2j+1. ANDing the word with 0x00030003 << 2i keeps the codes of
-// elements i and i+8 in the low mantissa bits of the two fp16 halves: with a zero exponent
-// field those halves are the fp16 subnormals q * 4^i * 2^-24, exactly. v_dot2_f32_f16 then
-// multiplies them by the activation pair (x_i, x_{i+8}) and adds into an fp32 accumulator:
-// products of an 11-bit significand by q * 4^i are exact, so each position i (i < 5) keeps
-// its own accumulator, and positions 5..7 reuse the accumulators of 0..2 after one 10-bit shift
-// of the word. At the end of a chunk the five accumulators are rescaled by 2^24 / 4^i (exact
-// powers of two) and sum_k q x - sum_k x = sum_k t x. That is one AND and one dot2 per two
-// weights plus one shift per word, instead of a shift/mask/convert/FMA per weight.
+// of them, element j in bits 2j..2j+1. Masking the word (or the word shifted by 4 or 6 bits)
+// with 0x00300030, 0x00C000C0 or 0x03000300 keeps the codes of elements j and j+8 in mantissa
+// bits 4..9 of the two fp16 halves: with a zero exponent field those halves are the fp16
+// subnormals q * 2^(p-24), p in {4, 6, 8}, exactly. v_dot2_f32_f16 multiplies them by the
+// activation pair (x_j, x_{j+8}) and adds into an fp32 accumulator, one accumulator per bit
+// position p. Three shifted copies cover all 16 codes: two shifts, eight ANDs and eight dot2 per
+// 16 weights. (Positions below bit 4 are avoided: measured on gfx950, dot2 with an fp16
+// subnormal operand whose value is q * 2^-24 loses about 7 bits, while at bit 4 and above the
+// error stays below 4e-7 of the sum.) At the end of a chunk the accumulators are combined with
+// exact power-of-two factors into 2^-20 * sum_k q x.
+//
+// Since t = q - 1, sum_k t x = sum_k q x - sum_k x. The second sum is produced by running the
+// identical decode-and-dot sequence on the code word of an all-zero row (every slot q = 1), once
+// per slice: a row whose codes are all zero then cancels bit for bit and gives exactly 0.
 //
 // Base-3. Each byte holds five trits, byte = sum_j (t_j + 1) 3^j. A word is split into two
 // 16-bit lanes (bytes 0,2 and bytes 1,3); each digit is peeled off both lanes at once with
-// packed 16-bit integer ops (q = v * 171 >> 9 equals v / 3 for v < 256; digit = v - 3q). The
-// digit, 0..2, in a 16-bit lane is again an fp16 subnormal, fed to dot2 as above. A 16-byte
-// chunk (80 trits) can straddle a 128-trit scale group, so each lane keeps two accumulators and
-// masks its activation pairs by group once per slice.
+// packed 16-bit integer ops (q = v * 171 >> 9 equals v / 3 for v < 256; digit = v - 3q) and
+// shifted to bits 4..5 of its lane, where it is again an exact fp16 subnormal fed to dot2. A
+// 16-byte chunk (80 trits) can straddle a 128-trit scale group, so each lane keeps two
+// accumulators and masks its activation pairs by group once per slice. The same all-zero-row
+// trick (byte 121 = five zero trits) supplies sum_k x.
 //
 // Scales are applied in fp32 per chunk, partial sums are reduced across the S lanes of a row
 // with lane shuffles in a fixed order: results are identical run to run.
@@ -43,7 +49,8 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kIter = 4;  // rows per lane slot per workgroup
+// word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format, no swizzle)
+constexpr int kRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
@@ -54,13 +61,6 @@ template <int E1, int E2>
 __device__ __forceinline__ uint32_t xpair(const uint32_t* w) {
   constexpr uint32_t sel = ((E1 & 1) ? 0x0302u : 0x0100u) | (((E2 & 1) ? 0x0706u : 0x0504u) << 16);
   return __builtin_amdgcn_perm(w[E2 / 2], w[E1 / 2], sel);
-}
-
-__device__ __forceinline__ float half_lo(uint32_t w) {
-  return (float)__builtin_bit_cast(half2_t, w)[0];
-}
-__device__ __forceinline__ float half_hi(uint32_t w) {
-  return (float)__builtin_bit_cast(half2_t, w)[1];
 }
 
 template <int LAYOUT>
@@ -92,35 +92,23 @@ struct XRegs;
 template <int MT>
 struct XRegs<TGS_LAYOUT_SLOT2, MT> {
   uint32_t p[MT][32];  // pairs: [dword d][position i] -> (x_{16d+i}, x_{16d+i+8})
-  float sum[MT];       // sum of the chunk's 64 activations
 
   __device__ __forceinline__ void load(const uint16_t* lds_chunk, int token_stride, int /*boundary*/) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      uint32_t w[32];
       const uint4* src = reinterpret_cast<const uint4*>(lds_chunk + t * token_stride);
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        uint4 q = src[v];
-        w[4 * v + 0] = q.x;
-        w[4 * v + 1] = q.y;
-        w[4 * v + 2] = q.z;
-        w[4 * v + 3] = q.w;
-      }
-      float s = 0.f;
-#pragma unroll
-      for (int v = 0; v < 32; ++v) s += half_lo(w[v]) + half_hi(w[v]);
-      sum[t] = s;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        p[t][8 * d + 0] = xpair<0, 8>(w + 8 * d);
-        p[t][8 * d + 1] = xpair<1, 9>(w + 8 * d);
-        p[t][8 * d + 2] = xpair<2, 10>(w + 8 * d);
-        p[t][8 * d + 3] = xpair<3, 11>(w + 8 * d);
-        p[t][8 * d + 4] = xpair<4, 12>(w + 8 * d);
-        p[t][8 * d + 5] = xpair<5, 13>(w + 8 * d);
-        p[t][8 * d + 6] = xpair<6, 14>(w + 8 * d);
-        p[t][8 * d + 7] = xpair<7, 15>(w + 8 * d);
+      for (int d = 0; d < 4; ++d) {  // 16 activations per code word, built one word at a time
+        const uint4 a = src[2 * d], b = src[2 * d + 1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        p[t][8 * d + 0] = xpair<0, 8>(w);
+        p[t][8 * d + 1] = xpair<1, 9>(w);
+        p[t][8 * d + 2] = xpair<2, 10>(w);
+        p[t][8 * d + 3] = xpair<3, 11>(w);
+        p[t][8 * d + 4] = xpair<4, 12>(w);
+        p[t][8 * d + 5] = xpair<5, 13>(w);
+        p[t][8 * d + 6] = xpair<6, 14>(w);
+        p[t][8 * d + 7] = xpair<7, 15>(w);
       }
     }
   }
@@ -133,7 +121,6 @@ struct XRegs<TGS_LAYOUT_BASE3, MT> {
   // the chunk, [1] to the second.
   uint32_t e[2][MT][20];
   uint32_t o[2][MT][20];
-  float sum[2][MT];
 
   template <int D, int J>
   __device__ __forceinline__ void set(const uint32_t* w, int t, int boundary) {
@@ -170,15 +157,6 @@ struct XRegs<TGS_LAYOUT_BASE3, MT> {
         w[4 * v + 2] = q.z;
         w[4 * v + 3] = q.w;
       }
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int v = 0; v < 40; ++v) {
-        float a = half_lo(w[v]), b = half_hi(w[v]);
-        if (2 * v < boundary) s0 += a; else s1 += a;
-        if (2 * v + 1 < boundary) s0 += b; else s1 += b;
-      }
-      sum[0][t] = s0;
-      sum[1][t] = s1;
       set_dword<0>(w, t, boundary);
       set_dword<1>(w, t, boundary);
       set_dword<2>(w, t, boundary);
@@ -189,44 +167,39 @@ struct XRegs<TGS_LAYOUT_BASE3, MT> {
 
 // ---- per-row chunk products ------------------------------------------------------------
 
-// Slot-2: returns sum_k t_k x_k over the 64 weights of the chunk for each token.
+// Slot-2: 2^-20 * sum_k q_k x_k over the 64 weights of the chunk, per token.
 template <int MT>
 __device__ __forceinline__ void chunk_dot_slot2(const uint4& cw, const XRegs<TGS_LAYOUT_SLOT2, MT>& xr,
                                                 float (&out)[MT]) {
-  float a[MT][5];
+  float a2[MT], a3[MT], a4[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int i = 0; i < 5; ++i) a[t][i] = 0.f;
+  for (int t = 0; t < MT; ++t) a2[t] = a3[t] = a4[t] = 0.f;
   const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t u = words[d];
-    const uint32_t u10 = u >> 10;
-    const uint32_t m0 = u & 0x00030003u, m1 = u & 0x000C000Cu, m2 = u & 0x00300030u, m3 = u & 0x00C000C0u,
-                   m4 = u & 0x03000300u, m5 = u10 & 0x00030003u, m6 = u10 & 0x000C000Cu, m7 = u10 & 0x00300030u;
+    const uint32_t u = words[d], v = u << 4, w = u >> 6;
+    // codes of elements (j, j+8) at fp16 mantissa bits 4-5 (a2), 6-7 (a3) or 8-9 (a4)
+    const uint32_t c2 = u & 0x00300030u, c3 = u & 0x00C000C0u, c4 = u & 0x03000300u;  // j = 2, 3, 4
+    const uint32_t c0 = v & 0x00300030u, c1 = v & 0x00C000C0u;                          // j = 0, 1
+    const uint32_t c5 = w & 0x00300030u, c6 = w & 0x00C000C0u, c7 = w & 0x03000300u;  // j = 5, 6, 7
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const uint32_t* p = &xr.p[t][8 * d];
-      a[t][0] = dot2(m0, p[0], a[t][0]);
-      a[t][1] = dot2(m1, p[1], a[t][1]);
-      a[t][2] = dot2(m2, p[2], a[t][2]);
-      a[t][3] = dot2(m3, p[3], a[t][3]);
-      a[t][4] = dot2(m4, p[4], a[t][4]);
-      a[t][0] = dot2(m5, p[5], a[t][0]);
-      a[t][1] = dot2(m6, p[6], a[t][1]);
-      a[t][2] = dot2(m7, p[7], a[t][2]);
+      a2[t] = dot2(c2, p[2], a2[t]);
+      a3[t] = dot2(c3, p[3], a3[t]);
+      a4[t] = dot2(c4, p[4], a4[t]);
+      a2[t] = dot2(c0, p[0], a2[t]);
+      a3[t] = dot2(c1, p[1], a3[t]);
+      a2[t] = dot2(c5, p[5], a2[t]);
+      a3[t] = dot2(c6, p[6], a3[t]);
+      a4[t] = dot2(c7, p[7], a4[t]);
     }
   }
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    // sum q x = 2^24 * (a0 + a1/4 + a2/16 + a3/64 + a4/256); every factor is a power of two
-    float h = fmaf(fmaf(fmaf(fmaf(a[t][4], 0.25f, a[t][3]), 0.25f, a[t][2]), 0.25f, a[t][1]), 0.25f, a[t][0]);
-    out[t] = fmaf(h, 16777216.0f, -xr.sum[t]);
-  }
+  for (int t = 0; t < MT; ++t) out[t] = fmaf(fmaf(a4[t], 0.25f, a3[t]), 0.25f, a2[t]);
 }
 
-// Base-3: sums for the (up to) two scale groups of the chunk, per token.
+// Base-3: 2^-20 * sum_k (t_k + 1) x_k for the (up to) two scale groups of the chunk, per token.
 template <int MT>
 __device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const XRegs<TGS_LAYOUT_BASE3, MT>& xr,
                                                 float (&out0)[MT], float (&out1)[MT]) {
@@ -252,7 +225,9 @@ __device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const XRegs<TGS
         de = ve;
         dd = vo;
       }
-      const uint32_t be = __builtin_bit_cast(uint32_t, de), bo = __builtin_bit_cast(uint32_t, dd);
+      // digit at bits 4..5: the fp16 subnormal digit * 2^-20
+      const uint32_t be = __builtin_bit_cast(uint32_t, de << (u16x2)4);
+      const uint32_t bo = __builtin_bit_cast(uint32_t, dd << (u16x2)4);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         a0[t] = dot2(be, xr.e[0][t][5 * d + j], a0[t]);
@@ -264,8 +239,8 @@ __device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const XRegs<TGS
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    out0[t] = fmaf(a0[t], 16777216.0f, -xr.sum[0][t]);
-    out1[t] = fmaf(a1[t], 16777216.0f, -xr.sum[1][t]);
+    out0[t] = a0[t];
+    out1[t] = a1[t];
   }
 }
 
@@ -325,9 +300,18 @@ __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint
 
 // ---- the kernel ----------------------------------------------------------------------
 
-template <int LAYOUT, int S, int MT, bool ROT>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs args) {
+// Single-token slot-2 kernels must keep four waves per SIMD resident (at most 128 VGPRs; three for
+// the rotated variant) to have enough loads in flight; the build fails if that ever forces a spill.
+template <int LAYOUT, int MT, bool ROT>
+constexpr int min_waves_per_eu() {
+  return (LAYOUT == TGS_LAYOUT_SLOT2 && MT == 1) ? (ROT ? 3 : 4) : (MT == 1 ? 2 : 1);
+}
+
+template <int LAYOUT, int S, int MT, int ITER, bool ROT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8)))
+void gemv_kernel(const GemvArgs args) {
   using G = Geo<LAYOUT>;
+  constexpr int kIter = ITER;
   constexpr int kRowsPerInstr = 64 / S;
   constexpr int kRowsPerWave = kIter * kRowsPerInstr;
   constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
@@ -349,6 +333,39 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs args) {
   const int rslot = lane / S;   // row slot within an instruction
   const int row0 = ((int)blockIdx.x - job.block0) * kRowsPerBlock + wave * kRowsPerWave + rslot;
 
+  constexpr int kBatch = kIter >= 2 ? 2 : 1;
+  constexpr int kBatches = kIter / kBatch;
+  constexpr int kRing = kBatches >= 4 ? 4 : 3;
+  struct Batch {
+    uint4 cw[kBatch];
+    uint32_t s0[kBatch], s1[kBatch];  // raw fp16 scale bits: converted only when used, so a
+                                      // prefetch never waits for its own loads
+  };
+  // Buffer resources: loads past the end of the codes or scales return 0 instead of faulting,
+  // so rows past n need no branch and every load is issued unconditionally (which keeps the
+  // wait counts exact and the prefetch pipelined). The host limits both arrays to < 2^31 bytes.
+  const __amdgpu_buffer_rsrc_t code_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.codes, 0, (int)((int64_t)n * job.stride), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t scale_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
+  // codes and the (up to two) group scales of rows b*kBatch .. b*kBatch+kBatch-1 of this lane
+  // slot. A lane whose chunk lies past the row (last slice) reads some other in-bounds bytes; its
+  // activations are zero and its scales are forced to zero when used, so it adds nothing.
+  auto load_batch = [&](Batch& bt, int b, int c, bool chunk_ok, int g0, bool has_g1) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int row = row0 + (b * kBatch + i) * kRowsPerInstr;
+      // unsigned arithmetic: an offset past the buffer simply reads as zero
+      const uint32_t code_off = (uint32_t)row * (uint32_t)job.stride + (uint32_t)c * 16u;
+      const uint32_t scale_off = ((uint32_t)row * (uint32_t)groups + (uint32_t)g0) * 2u;
+      bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)code_off, 0, 0));
+      bt.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)scale_off, 0, 0);
+      bt.s1[i] = 0;
+      if (LAYOUT == TGS_LAYOUT_BASE3)
+        bt.s1[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)(scale_off + 2u), 0, 0);
+    }
+  };
+
   for (int m0 = 0; m0 < m; m0 += MT) {
     float part[kIter][MT];
 #pragma unroll
@@ -358,6 +375,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs args) {
 
     for (int ks = 0; ks < slices; ++ks) {
       const int k_begin = ks * kSliceElems;
+      const int c = ks * S + cl;  // this lane's chunk
+      const bool chunk_ok = c < chunks;
+      // first trit of the second scale group, relative to the chunk (base-3 only)
+      const int t0 = c * G::kElems;
+      const int boundary = (LAYOUT == TGS_LAYOUT_BASE3) ? ((t0 / 128 + 1) * 128 - t0) : 1 << 20;
+      const int g0 = (LAYOUT == TGS_LAYOUT_SLOT2) ? c / 2 : t0 / 128;
+      const bool has_g1 = LAYOUT == TGS_LAYOUT_BASE3 && boundary < G::kElems && g0 + 1 < groups;
+
+      // Codes and scales do not depend on the activations: start loading the first batches of
+      // rows before the activation slice is staged, so the two latencies overlap.
+      Batch ring[kRing];
+#pragma unroll
+      for (int b = 0; b < kRing - 1 && b < kBatches; ++b) load_batch(ring[b], b, c, chunk_ok, g0, has_g1);
+
       __syncthreads();  // the previous slice's activations are no longer read
       if constexpr (ROT)
         stage_rotated<MT>(xs, kSliceElems, job.x, job.signs, k, m, m0, k_begin);
@@ -365,127 +396,142 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs args) {
         stage_plain<MT>(xs, kSliceElems, job.x, k, m, m0, k_begin);
       __syncthreads();
 
-      const int c = ks * S + cl;  // this lane's chunk
-      const bool chunk_ok = c < chunks;
-      // first trit of the second scale group, relative to the chunk (base-3 only)
-      const int t0 = c * G::kElems;
-      const int boundary = (LAYOUT == TGS_LAYOUT_BASE3) ? ((t0 / 128 + 1) * 128 - t0) : 1 << 20;
-
       XRegs<LAYOUT, MT> xr;
       xr.load(xs + cl * G::kElems, kSliceElems, boundary);
-
-      uint4 cw[kIter];
-#pragma unroll
-      for (int it = 0; it < kIter; ++it) {
-        const int row = row0 + it * kRowsPerInstr;
-        cw[it] = make_uint4(0, 0, 0, 0);
-        if (chunk_ok && row < n)
-          cw[it] = *reinterpret_cast<const uint4*>(job.codes + (int64_t)row * job.stride + (int64_t)c * 16);
-      }
+      // chunk products of an all-zero row: the same decode-and-dot on its code word
+      float ref0[MT], ref1[MT];
       if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
-        float sc[kIter];
-#pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-          const int row = row0 + it * kRowsPerInstr;
-          sc[it] = (chunk_ok && row < n) ? f16_to_f32(job.scales[(int64_t)row * groups + c / 2]) : 0.f;
-        }
-#pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-          float tx[MT];
-          chunk_dot_slot2<MT>(cw[it], xr, tx);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) part[it][t] = fmaf(sc[it], tx[t], part[it][t]);
-        }
+        chunk_dot_slot2<MT>(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), xr, ref0);
       } else {
-        const int g0 = t0 / 128;
-        const bool has_g1 = boundary < G::kElems && g0 + 1 < groups;
-        float sc0[kIter], sc1[kIter];
+        chunk_dot_base3<MT>(make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u), xr, ref0, ref1);
+      }
+
+      // rows in batches; kRing - 1 batches are in flight while one is computed (a ring of register
+      // sets, fully unrolled, so no copies)
 #pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-          const int row = row0 + it * kRowsPerInstr;
-          const bool ok = chunk_ok && row < n;
-          sc0[it] = ok ? f16_to_f32(job.scales[(int64_t)row * groups + g0]) : 0.f;
-          sc1[it] = (ok && has_g1) ? f16_to_f32(job.scales[(int64_t)row * groups + g0 + 1]) : 0.f;
-        }
+      for (int b = 0; b < kBatches; ++b) {
+        if (b + kRing - 1 < kBatches) load_batch(ring[(b + kRing - 1) % kRing], b + kRing - 1, c, chunk_ok, g0, has_g1);
+        // keep the scheduler from hoisting later batches' loads: the ring bounds the registers
+        __builtin_amdgcn_sched_barrier(0);
+        const Batch& cur = ring[b % kRing];
 #pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-          float tx0[MT], tx1[MT];
-          chunk_dot_base3<MT>(cw[it], xr, tx0, tx1);
+        for (int i = 0; i < kBatch; ++i) {
+          const int it = b * kBatch + i;
+          const float sc0 = chunk_ok ? f16_to_f32((uint16_t)cur.s0[i]) : 0.f;
+          if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
+            float qx[MT];
+            chunk_dot_slot2<MT>(cur.cw[i], xr, qx);
 #pragma unroll
-          for (int t = 0; t < MT; ++t) part[it][t] = fmaf(sc1[it], tx1[t], fmaf(sc0[it], tx0[t], part[it][t]));
+            for (int t = 0; t < MT; ++t) part[it][t] = fmaf(sc0, (qx[t] - ref0[t]) * 1048576.0f, part[it][t]);
+          } else {
+            const float sc1 = (chunk_ok && has_g1) ? f16_to_f32((uint16_t)cur.s1[i]) : 0.f;
+            float q0[MT], q1[MT];
+            chunk_dot_base3<MT>(cur.cw[i], xr, q0, q1);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+              part[it][t] = fmaf(sc1, (q1[t] - ref1[t]) * 1048576.0f,
+                                 fmaf(sc0, (q0[t] - ref0[t]) * 1048576.0f, part[it][t]));
+          }
         }
       }
     }
 
-    // reduce across the S lanes of each row, fixed order
+    // Reduce across the S lanes of each row, in a fixed order. Transposed: at each exchange step
+    // a lane keeps half of its values and sends the other half to its partner, so the number of
+    // values per lane halves until one is left; the remaining steps are plain butterflies. The
+    // sum of row slot `it` ends in the lanes whose bits (within the S-lane group) match `it`.
 #pragma unroll
-    for (int it = 0; it < kIter; ++it) {
+    for (int t = 0; t < MT; ++t) {
+      float v[kIter];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        float v = part[it][t];
+      for (int it = 0; it < kIter; ++it) v[it] = part[it][t];
+      int count = kIter;
 #pragma unroll
-        for (int off = S / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        part[it][t] = v;
-      }
-    }
-    if (cl == 0) {
+      for (int off = S / 2; off >= 1; off >>= 1) {
+        const bool upper = (lane & off) != 0;
+        if (count > 1) {
 #pragma unroll
-      for (int it = 0; it < kIter; ++it) {
-        const int row = row0 + it * kRowsPerInstr;
-        if (row < n) {
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-            if (m0 + t < m) job.y[(int64_t)(m0 + t) * n + row] = part[it][t];
+          for (int i = 0; i < kIter / 2; ++i) {
+            if (2 * i + 1 < count) {
+              const float keep = upper ? v[2 * i + 1] : v[2 * i];
+              const float send = upper ? v[2 * i] : v[2 * i + 1];
+              v[i] = keep + __shfl_xor(send, off);
+            }
+          }
+          count /= 2;
+        } else {
+          v[0] += __shfl_xor(v[0], off);
         }
       }
+      // after the exchanges, lane bit pattern (within its S-lane group) selects the row slot:
+      // each exchange step with offset `off` (taken while count > 1) routes odd slots to the
+      // lanes with that bit set
+      int it_sel = 0, bit = 0;
+#pragma unroll
+      for (int off = S / 2, cnt = kIter; off >= 1 && cnt > 1; off >>= 1, cnt /= 2, ++bit)
+        if (lane & off) it_sel |= 1 << bit;
+      const int row = row0 + it_sel * kRowsPerInstr;
+      // one lane per (row slot): the lowest lane whose exchange bits equal it_sel
+      int low_bits = 0;
+#pragma unroll
+      for (int off = S / 2, cnt = kIter; off >= 1; off >>= 1, cnt = cnt > 1 ? cnt / 2 : 1)
+        if (cnt <= 1) low_bits |= off;
+      if ((cl & low_bits) == 0 && row < n && m0 + t < m) job.y[(int64_t)(m0 + t) * n + row] = v[0];
     }
   }
 }
 
-template <int LAYOUT, int S, int MT, bool ROT>
+template <int LAYOUT, int S, int MT, int ITER, bool ROT>
 hipError_t launch_one(GemvArgs& args, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_kernel<LAYOUT, S, MT, ROT>), dim3(blocks), dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((gemv_kernel<LAYOUT, S, MT, ITER, ROT>), dim3(blocks), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
+// rows per lane slot: 8 for large single-token launches (more work per workgroup), else 4;
+// fewer when several tokens share the registers
 template <int LAYOUT, int S, int MT>
-hipError_t launch_rot(bool rot, GemvArgs& args, int blocks, hipStream_t stream) {
-  return rot ? launch_one<LAYOUT, S, MT, true>(args, blocks, stream)
-             : launch_one<LAYOUT, S, MT, false>(args, blocks, stream);
+hipError_t launch_rot(bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
+  if constexpr (MT == 1 && LAYOUT == TGS_LAYOUT_SLOT2) {
+    if (iter == 8)
+      return rot ? launch_one<LAYOUT, S, MT, 8, true>(args, blocks, stream)
+                 : launch_one<LAYOUT, S, MT, 8, false>(args, blocks, stream);
+    return rot ? launch_one<LAYOUT, S, MT, 4, true>(args, blocks, stream)
+               : launch_one<LAYOUT, S, MT, 4, false>(args, blocks, stream);
+  } else {
+    constexpr int it = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
+    return rot ? launch_one<LAYOUT, S, MT, it, true>(args, blocks, stream)
+               : launch_one<LAYOUT, S, MT, it, false>(args, blocks, stream);
+  }
 }
 
 template <int LAYOUT, int S>
-hipError_t launch_mt(int mt, bool rot, GemvArgs& args, int blocks, hipStream_t stream) {
+hipError_t launch_mt(int mt, bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
     switch (mt) {
-      case 1: return launch_rot<LAYOUT, S, 1>(rot, args, blocks, stream);
-      case 2: return launch_rot<LAYOUT, S, 2>(rot, args, blocks, stream);
-      case 4: return launch_rot<LAYOUT, S, 4>(rot, args, blocks, stream);
-      default: return launch_rot<LAYOUT, S, 8>(rot, args, blocks, stream);
+      case 1: return launch_rot<LAYOUT, S, 1>(rot, iter, args, blocks, stream);
+      case 2: return launch_rot<LAYOUT, S, 2>(rot, iter, args, blocks, stream);
+      default: return launch_rot<LAYOUT, S, 4>(rot, iter, args, blocks, stream);
     }
   } else {
-    return mt == 1 ? launch_rot<LAYOUT, S, 1>(rot, args, blocks, stream)
-                   : launch_rot<LAYOUT, S, 2>(rot, args, blocks, stream);
+    return launch_rot<LAYOUT, S, 1>(rot, iter, args, blocks, stream);
   }
 }
 
 template <int LAYOUT>
-hipError_t launch_s(int s, int mt, bool rot, GemvArgs& args, int blocks, hipStream_t stream) {
+hipError_t launch_s(int s, int mt, bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   switch (s) {
-    case 16: return launch_mt<LAYOUT, 16>(mt, rot, args, blocks, stream);
-    case 32: return launch_mt<LAYOUT, 32>(mt, rot, args, blocks, stream);
-    default: return launch_mt<LAYOUT, 64>(mt, rot, args, blocks, stream);
+    case 16: return launch_mt<LAYOUT, 16>(mt, rot, iter, args, blocks, stream);
+    case 32: return launch_mt<LAYOUT, 32>(mt, rot, iter, args, blocks, stream);
+    default: return launch_mt<LAYOUT, 64>(mt, rot, iter, args, blocks, stream);
   }
 }
 
 }  // namespace
 
-// Tokens per pass (compile-time width of the activation registers).
+// Tokens per pass (compile-time width of the activation registers); larger m loops over passes.
 static int tokens_per_pass(int32_t layout, int64_t m) {
-  if (layout == TGS_LAYOUT_BASE3) return m >= 2 ? 2 : 1;
-  int mt = 1;
-  while (mt < m) mt *= 2;
-  return mt;
+  if (layout == TGS_LAYOUT_BASE3) return 1;
+  return m >= 4 ? 4 : (m >= 2 ? 2 : 1);
 }
 
 GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
@@ -504,16 +550,29 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
     }
   }
   p.lanes = best;
-  p.rows_per_block = kWaves * kIter * (64 / best);
+  const int mt = tokens_per_pass(layout, m);
+  p.iter = mt == 1 ? 4 : (mt == 2 ? 2 : 1);
+  p.rows_per_block = kWaves * p.iter * (64 / best);
   return p;
+}
+
+void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
+  // single-token slot-2 launches with plenty of rows: 2x more rows per workgroup, still >= 2048
+  // workgroups
+  if (p.layout != TGS_LAYOUT_SLOT2 || tokens_per_pass(p.layout, p.m) != 1) return;
+  const int64_t big_rows = (int64_t)kWaves * 8 * (64 / p.lanes);
+  if ((total_rows + big_rows - 1) / big_rows >= 2048) {
+    p.iter = 8;
+    p.rows_per_block = (int32_t)big_rows;
+  }
 }
 
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream) {
   const int mt = tokens_per_pass(plan.layout, plan.m);
   const bool rot = plan.rotated != 0;
   if (plan.layout == TGS_LAYOUT_SLOT2)
-    return launch_s<TGS_LAYOUT_SLOT2>(plan.lanes, mt, rot, args, blocks, stream);
-  return launch_s<TGS_LAYOUT_BASE3>(plan.lanes, mt, rot, args, blocks, stream);
+    return launch_s<TGS_LAYOUT_SLOT2>(plan.lanes, mt, rot, plan.iter, args, blocks, stream);
+  return launch_s<TGS_LAYOUT_BASE3>(plan.lanes, mt, rot, plan.iter, args, blocks, stream);
 }
 
 }  // namespace tgs

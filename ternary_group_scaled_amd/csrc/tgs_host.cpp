@@ -149,6 +149,9 @@ tgs_status check_matrix(const tgs_matrix* w, bool device) {
   if (w->code_row_stride < (int64_t)rb || w->code_row_stride % 16 != 0)
     return fail(TGS_E_SHAPE, "code_row_stride %lld must be a multiple of 16 and >= %zu", (long long)w->code_row_stride,
                 rb);
+  if (device && w->n * w->code_row_stride >= (1LL << 31))
+    return fail(TGS_E_SHAPE, "codes of one matrix must stay below 2 GiB (n * code_row_stride = %lld)",
+                (long long)(w->n * w->code_row_stride));
   if (!w->codes || !w->scales) return fail(TGS_E_NULL, "codes or scales pointer is NULL");
   if (!aligned(w->codes, 16)) return fail(TGS_E_ALIGN, "codes must be 16-byte aligned");
   if (!aligned(w->scales, 2)) return fail(TGS_E_ALIGN, "scales must be 2-byte aligned");
@@ -261,15 +264,24 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
   std::vector<char> done((size_t)count, 0);
   for (int32_t i = 0; i < count; ++i) {
     if (done[(size_t)i]) continue;
-    const tgs::GemvPlan plan = tgs::gemv_plan(ws[i].layout, ws[i].k, m, ws[i].rotated);
-    tgs::GemvArgs args;
-    std::memset(&args, 0, sizeof(args));
-    args.m = (int32_t)m;
-    int32_t blocks = 0;
+    tgs::GemvPlan plan = tgs::gemv_plan(ws[i].layout, ws[i].k, m, ws[i].rotated);
+    // the jobs of this launch: every remaining matrix with the same plan, in call order
+    std::vector<int32_t> members;
+    int64_t total_rows = 0;
     for (int32_t j = i; j < count; ++j) {
       if (done[(size_t)j]) continue;
       const tgs::GemvPlan pj = tgs::gemv_plan(ws[j].layout, ws[j].k, m, ws[j].rotated);
       if (pj.layout != plan.layout || pj.lanes != plan.lanes || pj.rotated != plan.rotated) continue;
+      members.push_back(j);
+      total_rows += ws[j].n;
+      done[(size_t)j] = 1;
+    }
+    tgs::gemv_plan_set_rows(plan, total_rows);
+    tgs::GemvArgs args;
+    std::memset(&args, 0, sizeof(args));
+    args.m = (int32_t)m;
+    int32_t blocks = 0;
+    for (int32_t j : members) {
       tgs::GemvJob& job = args.job[args.count++];
       job.codes = static_cast<const uint8_t*>(ws[j].codes);
       job.scales = ws[j].scales;
@@ -282,7 +294,6 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
       job.block0 = blocks;
       job.row_blocks = (int32_t)((ws[j].n + plan.rows_per_block - 1) / plan.rows_per_block);
       blocks += job.row_blocks;
-      done[(size_t)j] = 1;
     }
     hipError_t e = tgs::gemv_launch(plan, args, blocks, s);
     if (e != hipSuccess) return device_error(e, "ternary_gemv launch");

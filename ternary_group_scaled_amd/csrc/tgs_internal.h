@@ -36,12 +36,15 @@ struct GemvPlan {
   int32_t lanes;      // lanes per row (16, 32 or 64)
   int32_t m;          // activation rows
   int32_t rotated;    // 0 or 1
+  int32_t iter;       // rows per lane slot
   int32_t rows_per_block;
 };
 
 // Launch helpers implemented in the .hip files. They only queue work; all argument checks
 // happen in tgs_host.cpp before they are called.
 GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated);
+// after the jobs of a launch are known: pick rows per workgroup from their total row count
+void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows);
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream);
 
 hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
