@@ -56,6 +56,9 @@ def parse():
                          "layer (36), or the whole set in as few launches as possible")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (a known-size kernel that calibrates "
+                         "the FETCH_SIZE/WRITE_SIZE counters in a profile of this command)")
     return ap.parse_args()
 
 
@@ -147,40 +150,42 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
     y_bytes = sum(outputs[L][name].numel() * 4 for L in range(layers) for name, _, _ in LAYER_8B)
     total_bytes = w_bytes + x_bytes + y_bytes
 
-    # launch list for one pass
+    # launch lists for one pass, per launch mode
     def group_launch(L, grp):
         ws = [mats[L][nm] for nm in grp]
         xs = [inputs[L][grp][0]] * len(grp)
         ys = [outputs[L][nm] for nm in grp]
         return lambda: tgs.ternary_gemv_batched(ws, xs, ys)
 
-    if args.mode == "layer":
-        launches = [group_launch(L, g) for L in range(layers) for g in GROUPS_8B]
-    else:
-        per = []
-        for L in range(layers):
-            for g in GROUPS_8B:
-                for nm in g:
-                    per.append((mats[L][nm], inputs[L][g][0], outputs[L][nm]))
-        chunk = len(LAYER_8B) if args.mode == "fused-layer" else tgs.MAX_BATCH
-        launches = []
+    def batched_launches(chunk):
+        per = [(mats[L][nm], inputs[L][g][0], outputs[L][nm]) for L in range(layers) for g in GROUPS_8B for nm in g]
+        out = []
         for i in range(0, len(per), chunk):
             part = per[i:i + chunk]
-            launches.append((lambda p: lambda: tgs.ternary_gemv_batched([a for a, _, _ in p], [b for _, b, _ in p],
-                                                                        [c for _, _, c in p]))(part))
+            out.append((lambda p: lambda: tgs.ternary_gemv_batched([a for a, _, _ in p], [b for _, b, _ in p],
+                                                                   [c for _, _, c in p]))(part))
+        return out
 
-    def one_pass():
-        for fn in launches:
-            fn()
+    modes = {"layer": [group_launch(L, g) for L in range(layers) for g in GROUPS_8B],
+             "fused-layer": batched_launches(len(LAYER_8B)),
+             "set": batched_launches(tgs.MAX_BATCH)}
+    timings = {}
+    for mode in ["layer", "fused-layer", "set"]:
+        launches = modes[mode]
 
-    log(f"[bench] timing {args.steps} graph replays of {len(launches)} launches ({args.mode})")
-    ms, _graph = time_graph(torch, one_pass, args.steps, args.warmup)
-    per_launch_ms = time_launches(torch, launches, reps=max(3, args.steps // 4))
-    kernel_ms = float(per_launch_ms.sum())
+        def one_pass(launches=launches):
+            for fn in launches:
+                fn()
+
+        log(f"[bench] timing {args.steps} graph replays of {len(launches)} launches ({mode})")
+        ms_m, _graph = time_graph(torch, one_pass, args.steps, args.warmup)
+        per_launch_ms = time_launches(torch, launches, reps=max(3, args.steps // 4))
+        timings[mode] = (ms_m, float(per_launch_ms.sum()), len(launches))
+        log(f"[bench]   {mode}: step {ms_m * 1e3:.1f} us -> {total_bytes / ms_m / 1e6:.0f} GB/s; sum of kernel times "
+            f"{per_launch_ms.sum() * 1e3:.1f} us -> {total_bytes / per_launch_ms.sum() / 1e6:.0f} GB/s")
+    ms, kernel_ms, n_launches = timings[args.mode]
     gbs = total_bytes / (ms * 1e-3) / 1e9
     kernel_gbs = total_bytes / (kernel_ms * 1e-3) / 1e9
-    log(f"[bench] step {ms * 1e3:.1f} us -> {gbs:.0f} GB/s; sum of kernel times {kernel_ms * 1e3:.1f} us -> "
-        f"{kernel_gbs:.0f} GB/s")
 
     # parity spot check of layer 0 against the oracle on sampled rows
     check_layer0(torch, host, inputs[0], outputs[0], layout)
@@ -190,15 +195,17 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": workload_name or "8B-class decode GEMV set, 2-bit-slot layout, M=1",
-                   "layers": layers, "matrices": layers * len(LAYER_8B), "launches_per_step": len(launches),
+                   "layers": layers, "matrices": layers * len(LAYER_8B), "launches_per_step": n_launches,
                    "launch_mode": args.mode, "p_zero": p_zero, "algorithmic_bytes_per_step": int(total_bytes),
                    "weight_bytes_per_step": int(w_bytes)},
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(1e3 / ms, 1),
+        "launch_modes": {m: {"launches": t[2], "ms_per_step": round(t[0], 5), "gbs": round(total_bytes / t[0] / 1e6, 1),
+                             "kernel_gbs": round(total_bytes / t[1] / 1e6, 1)} for m, t in timings.items()},
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_kernel", "avg_launch_us": round(kernel_ms * 1e3 / len(launches), 3),
-                     "bytes_per_launch_avg": int(total_bytes / len(launches))},
+                     "kernel": "gemv_kernel", "avg_launch_us": round(kernel_ms * 1e3 / n_launches, 3),
+                     "bytes_per_launch_avg": int(total_bytes / n_launches)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_8b(host, layout, args.cpu_seconds, ms, total_bytes / layers)
@@ -333,6 +340,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload == "8b":
         out = [bench_8b(args, torch, tgs, synth)]
     elif args.workload == "base3":

@@ -6,12 +6,13 @@
 // "Group-scaled ternary format"; xr = R x for rotated-basis weights per the same page,
 // subsection "Block-wise Hadamard rotation" (block n = 128 here).
 //
-// Work split. A workgroup (4 waves) owns a block of rows and walks K in slices. In a slice
-// each lane owns one 16-byte chunk of codes (64 slot-2 weights or 80 base-3 trits) at a fixed
-// K position and keeps the matching activations in registers while it walks its rows, so x is
-// read from LDS once per slice and reused for every row. `S` lanes share a row (16, 32 or 64);
-// a wave covers 64/S rows per load instruction, and consecutive lanes read consecutive 16-byte
-// chunks of a row, so every load instruction is a fully used, contiguous span.
+// Work split. A workgroup (4 waves) owns a block of rows and walks K in slices. In a slice each
+// lane owns one 16-byte chunk of codes (64 slot-2 weights or 80 base-3 trits) at a fixed K
+// position and keeps the matching activations in registers while it walks its rows. `S` lanes
+// share a row (16, 32 or 64); a wave covers 64/S rows per load instruction, and consecutive lanes
+// read consecutive 16-byte chunks of a row, so every load instruction is a fully used,
+// contiguous span. Codes and scales are read through buffer resources (reads past the end return
+// zero), issued before the activation slice is staged and pipelined in a ring of register sets.
 //
 // Decode without unpacking (slot-2). Codes q = t + 1 sit in 2-bit slots; a 32-bit word holds 16
 // of them, element j in bits 2j..2j+1. Masking the word (or the word shifted by 4 or 6 bits)
@@ -22,23 +23,28 @@
 // position p. Three shifted copies cover all 16 codes: two shifts, eight ANDs and eight dot2 per
 // 16 weights. (Positions below bit 4 are avoided: measured on gfx950, dot2 with an fp16
 // subnormal operand whose value is q * 2^-24 loses about 7 bits, while at bit 4 and above the
-// error stays below 4e-7 of the sum.) At the end of a chunk the accumulators are combined with
-// exact power-of-two factors into 2^-20 * sum_k q x.
+// error stays below 4e-7 of the sum.) The accumulators are combined with exact power-of-two
+// factors into 2^-20 * sum_k q x.
 //
 // Since t = q - 1, sum_k t x = sum_k q x - sum_k x. The second sum is produced by running the
-// identical decode-and-dot sequence on the code word of an all-zero row (every slot q = 1), once
-// per slice: a row whose codes are all zero then cancels bit for bit and gives exactly 0.
+// identical decode-and-dot sequence on the code word of an all-zero row (every slot q = 1): a
+// row whose codes are all zero then cancels bit for bit and gives exactly 0.
 //
 // Base-3. Each byte holds five trits, byte = sum_j (t_j + 1) 3^j. A word is split into two
 // 16-bit lanes (bytes 0,2 and bytes 1,3); each digit is peeled off both lanes at once with
 // packed 16-bit integer ops (q = v * 171 >> 9 equals v / 3 for v < 256; digit = v - 3q) and
 // shifted to bits 4..5 of its lane, where it is again an exact fp16 subnormal fed to dot2. A
 // 16-byte chunk (80 trits) can straddle a 128-trit scale group, so each lane keeps two
-// accumulators and masks its activation pairs by group once per slice. The same all-zero-row
-// trick (byte 121 = five zero trits) supplies sum_k x.
+// accumulators with activation pairs masked by group. The all-zero row (byte 121 = five zero
+// trits) again supplies sum_k x.
 //
-// Scales are applied in fp32 per chunk, partial sums are reduced across the S lanes of a row
-// with lane shuffles in a fixed order: results are identical run to run.
+// Shared per-slice work. The activation pairs of a chunk and its all-zero-row product depend on
+// the chunk only, not on the wave, so one thread per chunk builds them once per workgroup and
+// stores them in LDS, laid out [16-byte granule][chunk] so that the waves' reads are
+// conflict-free 16-byte accesses by consecutive lanes.
+//
+// Scales are applied in fp32 per chunk; partial sums are reduced across the S lanes of a row in
+// a fixed order: results are identical run to run.
 #include "tgs_internal.h"
 
 namespace tgs {
@@ -47,13 +53,23 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+// waves per workgroup: 4 for every variant (8 waves per workgroup measured slower on the large
+// single-token launches, and 4 gives small matrices more workgroups)
+template <int ITER>
+constexpr int waves_for() {
+  return 4;
+}
+// cache policy of the weight stream: non-temporal (read once, no reuse)
+constexpr int kStreamAux = 2;
 // word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format, no swizzle)
 constexpr int kRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
 }
 
 // Activation pair (element e1 in the low half, e2 in the high half) from fp16 words w[e/2].
@@ -67,15 +83,13 @@ template <int LAYOUT>
 struct Geo;
 template <>
 struct Geo<TGS_LAYOUT_SLOT2> {
-  static constexpr int kElems = 64;  // weights per 16-byte chunk
-  static constexpr int kPairs = 32;  // activation pairs per chunk
-  static constexpr int kAccs = 1;    // scale groups a chunk can touch
+  static constexpr int kElems = 64;   // weights per 16-byte chunk
+  static constexpr int kPairDw = 32;  // pair words per chunk and token
 };
 template <>
 struct Geo<TGS_LAYOUT_BASE3> {
   static constexpr int kElems = 80;
-  static constexpr int kPairs = 40;
-  static constexpr int kAccs = 2;
+  static constexpr int kPairDw = 80;  // 40 pairs, each masked to the chunk's first and second group
 };
 
 __host__ __device__ inline int chunks_per_row(int layout, int k) {
@@ -84,128 +98,81 @@ __host__ __device__ inline int chunks_per_row(int layout, int k) {
   return (used + 15) / 16;
 }
 
-// ---- per-lane activation registers for one slice --------------------------------------
+// ---- building the activation pairs of one chunk ------------------------------------------
 
-template <int LAYOUT, int MT>
-struct XRegs;
-
-template <int MT>
-struct XRegs<TGS_LAYOUT_SLOT2, MT> {
-  uint32_t p[MT][32];  // pairs: [dword d][position i] -> (x_{16d+i}, x_{16d+i+8})
-
-  __device__ __forceinline__ void load(const uint16_t* lds_chunk, int token_stride, int /*boundary*/) {
+// slot-2: p[8d + i] = (x_{16d+i}, x_{16d+i+8}) from the chunk's 64 fp16 activations (32 words)
+__device__ __forceinline__ void build_pairs_slot2(const uint32_t* w, uint32_t* p) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint4* src = reinterpret_cast<const uint4*>(lds_chunk + t * token_stride);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {  // 16 activations per code word, built one word at a time
-        const uint4 a = src[2 * d], b = src[2 * d + 1];
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        p[t][8 * d + 0] = xpair<0, 8>(w);
-        p[t][8 * d + 1] = xpair<1, 9>(w);
-        p[t][8 * d + 2] = xpair<2, 10>(w);
-        p[t][8 * d + 3] = xpair<3, 11>(w);
-        p[t][8 * d + 4] = xpair<4, 12>(w);
-        p[t][8 * d + 5] = xpair<5, 13>(w);
-        p[t][8 * d + 6] = xpair<6, 14>(w);
-        p[t][8 * d + 7] = xpair<7, 15>(w);
-      }
-    }
+  for (int d = 0; d < 4; ++d) {
+    p[8 * d + 0] = xpair<0, 8>(w + 8 * d);
+    p[8 * d + 1] = xpair<1, 9>(w + 8 * d);
+    p[8 * d + 2] = xpair<2, 10>(w + 8 * d);
+    p[8 * d + 3] = xpair<3, 11>(w + 8 * d);
+    p[8 * d + 4] = xpair<4, 12>(w + 8 * d);
+    p[8 * d + 5] = xpair<5, 13>(w + 8 * d);
+    p[8 * d + 6] = xpair<6, 14>(w + 8 * d);
+    p[8 * d + 7] = xpair<7, 15>(w + 8 * d);
   }
-};
+}
 
-template <int MT>
-struct XRegs<TGS_LAYOUT_BASE3, MT> {
-  // pairs for each dword d and digit j: e = bytes (0,2) -> trits (20d+j, 20d+10+j),
-  // o = bytes (1,3) -> trits (20d+5+j, 20d+15+j); [0] masked to the first scale group of
-  // the chunk, [1] to the second.
-  uint32_t e[2][MT][20];
-  uint32_t o[2][MT][20];
+// base-3: for dword d and digit j, bytes (0,2) carry trits (20d+j, 20d+10+j) and bytes (1,3)
+// trits (20d+5+j, 20d+15+j). Layout of p: [0,20) e-pairs of the first group, [20,40) e-pairs of
+// the second group, [40,60) and [60,80) the same for the o-pairs; index 5d + j within each.
+template <int D, int J>
+__device__ __forceinline__ void base3_pair(const uint32_t* w, int boundary, uint32_t* p) {
+  constexpr int e1 = 20 * D + J, e2 = 20 * D + 10 + J, o1 = 20 * D + 5 + J, o2 = 20 * D + 15 + J;
+  const uint32_t pe = xpair<e1, e2>(w), po = xpair<o1, o2>(w);
+  const uint32_t me = (e1 < boundary ? 0xFFFFu : 0u) | (e2 < boundary ? 0xFFFF0000u : 0u);
+  const uint32_t mo = (o1 < boundary ? 0xFFFFu : 0u) | (o2 < boundary ? 0xFFFF0000u : 0u);
+  p[5 * D + J] = pe & me;
+  p[20 + 5 * D + J] = pe & ~me;
+  p[40 + 5 * D + J] = po & mo;
+  p[60 + 5 * D + J] = po & ~mo;
+}
 
-  template <int D, int J>
-  __device__ __forceinline__ void set(const uint32_t* w, int t, int boundary) {
-    constexpr int e1 = 20 * D + J, e2 = 20 * D + 10 + J, o1 = 20 * D + 5 + J, o2 = 20 * D + 15 + J;
-    uint32_t pe = xpair<e1, e2>(w), po = xpair<o1, o2>(w);
-    uint32_t me = (e1 < boundary ? 0xFFFFu : 0u) | (e2 < boundary ? 0xFFFF0000u : 0u);
-    uint32_t mo = (o1 < boundary ? 0xFFFFu : 0u) | (o2 < boundary ? 0xFFFF0000u : 0u);
-    e[0][t][5 * D + J] = pe & me;
-    e[1][t][5 * D + J] = pe & ~me;
-    o[0][t][5 * D + J] = po & mo;
-    o[1][t][5 * D + J] = po & ~mo;
-  }
+template <int D>
+__device__ __forceinline__ void base3_pairs_dword(const uint32_t* w, int boundary, uint32_t* p) {
+  base3_pair<D, 0>(w, boundary, p);
+  base3_pair<D, 1>(w, boundary, p);
+  base3_pair<D, 2>(w, boundary, p);
+  base3_pair<D, 3>(w, boundary, p);
+  base3_pair<D, 4>(w, boundary, p);
+}
 
-  template <int D>
-  __device__ __forceinline__ void set_dword(const uint32_t* w, int t, int boundary) {
-    set<D, 0>(w, t, boundary);
-    set<D, 1>(w, t, boundary);
-    set<D, 2>(w, t, boundary);
-    set<D, 3>(w, t, boundary);
-    set<D, 4>(w, t, boundary);
-  }
+// boundary: index within the chunk of the first trit of the second scale group (>= 80: none)
+__device__ __forceinline__ void build_pairs_base3(const uint32_t* w, int boundary, uint32_t* p) {
+  base3_pairs_dword<0>(w, boundary, p);
+  base3_pairs_dword<1>(w, boundary, p);
+  base3_pairs_dword<2>(w, boundary, p);
+  base3_pairs_dword<3>(w, boundary, p);
+}
 
-  // boundary: index within the chunk of the first trit of the second scale group (>= 80: none)
-  __device__ __forceinline__ void load(const uint16_t* lds_chunk, int token_stride, int boundary) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      uint32_t w[40];
-      const uint4* src = reinterpret_cast<const uint4*>(lds_chunk + t * token_stride);
-#pragma unroll
-      for (int v = 0; v < 10; ++v) {
-        uint4 q = src[v];
-        w[4 * v + 0] = q.x;
-        w[4 * v + 1] = q.y;
-        w[4 * v + 2] = q.z;
-        w[4 * v + 3] = q.w;
-      }
-      set_dword<0>(w, t, boundary);
-      set_dword<1>(w, t, boundary);
-      set_dword<2>(w, t, boundary);
-      set_dword<3>(w, t, boundary);
-    }
-  }
-};
+// ---- chunk products -------------------------------------------------------------------------
 
-// ---- per-row chunk products ------------------------------------------------------------
-
-// Slot-2: 2^-20 * sum_k q_k x_k over the 64 weights of the chunk, per token.
-template <int MT>
-__device__ __forceinline__ void chunk_dot_slot2(const uint4& cw, const XRegs<TGS_LAYOUT_SLOT2, MT>& xr,
-                                                float (&out)[MT]) {
-  float a2[MT], a3[MT], a4[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) a2[t] = a3[t] = a4[t] = 0.f;
+// slot-2: 2^-20 * sum_k q_k x_k over the 64 weights of a chunk
+__device__ __forceinline__ float chunk_dot_slot2(const uint4& cw, const uint32_t* p) {
+  float a2 = 0.f, a3 = 0.f, a4 = 0.f;
   const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t u = words[d], v = u << 4, w = u >> 6;
+    const uint32_t* q = p + 8 * d;
     // codes of elements (j, j+8) at fp16 mantissa bits 4-5 (a2), 6-7 (a3) or 8-9 (a4)
-    const uint32_t c2 = u & 0x00300030u, c3 = u & 0x00C000C0u, c4 = u & 0x03000300u;  // j = 2, 3, 4
-    const uint32_t c0 = v & 0x00300030u, c1 = v & 0x00C000C0u;                          // j = 0, 1
-    const uint32_t c5 = w & 0x00300030u, c6 = w & 0x00C000C0u, c7 = w & 0x03000300u;  // j = 5, 6, 7
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint32_t* p = &xr.p[t][8 * d];
-      a2[t] = dot2(c2, p[2], a2[t]);
-      a3[t] = dot2(c3, p[3], a3[t]);
-      a4[t] = dot2(c4, p[4], a4[t]);
-      a2[t] = dot2(c0, p[0], a2[t]);
-      a3[t] = dot2(c1, p[1], a3[t]);
-      a2[t] = dot2(c5, p[5], a2[t]);
-      a3[t] = dot2(c6, p[6], a3[t]);
-      a4[t] = dot2(c7, p[7], a4[t]);
-    }
+    a2 = dot2(u & 0x00300030u, q[2], a2);  // j = 2
+    a3 = dot2(u & 0x00C000C0u, q[3], a3);  // j = 3
+    a4 = dot2(u & 0x03000300u, q[4], a4);  // j = 4
+    a2 = dot2(v & 0x00300030u, q[0], a2);  // j = 0
+    a3 = dot2(v & 0x00C000C0u, q[1], a3);  // j = 1
+    a2 = dot2(w & 0x00300030u, q[5], a2);  // j = 5
+    a3 = dot2(w & 0x00C000C0u, q[6], a3);  // j = 6
+    a4 = dot2(w & 0x03000300u, q[7], a4);  // j = 7
   }
-#pragma unroll
-  for (int t = 0; t < MT; ++t) out[t] = fmaf(fmaf(a4[t], 0.25f, a3[t]), 0.25f, a2[t]);
+  return fmaf(fmaf(a4, 0.25f, a3), 0.25f, a2);
 }
 
-// Base-3: 2^-20 * sum_k (t_k + 1) x_k for the (up to) two scale groups of the chunk, per token.
-template <int MT>
-__device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const XRegs<TGS_LAYOUT_BASE3, MT>& xr,
-                                                float (&out0)[MT], float (&out1)[MT]) {
-  float a0[MT], a1[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) a0[t] = a1[t] = 0.f;
+// base-3: 2^-20 * sum_k (t_k + 1) x_k for the (up to) two scale groups of a chunk
+__device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const uint32_t* p, float& out0, float& out1) {
+  float a0 = 0.f, a1 = 0.f;
   const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -228,51 +195,27 @@ __device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const XRegs<TGS
       // digit at bits 4..5: the fp16 subnormal digit * 2^-20
       const uint32_t be = __builtin_bit_cast(uint32_t, de << (u16x2)4);
       const uint32_t bo = __builtin_bit_cast(uint32_t, dd << (u16x2)4);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        a0[t] = dot2(be, xr.e[0][t][5 * d + j], a0[t]);
-        a1[t] = dot2(be, xr.e[1][t][5 * d + j], a1[t]);
-        a0[t] = dot2(bo, xr.o[0][t][5 * d + j], a0[t]);
-        a1[t] = dot2(bo, xr.o[1][t][5 * d + j], a1[t]);
-      }
+      a0 = dot2(be, p[5 * d + j], a0);
+      a1 = dot2(be, p[20 + 5 * d + j], a1);
+      a0 = dot2(bo, p[40 + 5 * d + j], a0);
+      a1 = dot2(bo, p[60 + 5 * d + j], a1);
     }
   }
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    out0[t] = a0[t];
-    out1[t] = a1[t];
-  }
+  out0 = a0;
+  out1 = a1;
 }
 
-__device__ __forceinline__ float f16_to_f32(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
-}
+// ---- staging one slice of activations ----------------------------------------------------
 
-// ---- staging one slice of activations into LDS -------------------------------------------
-
-// Plain basis: copy x[m0 + t][k_begin .. k_begin + len) to lds[t][...], zero past K or M.
-template <int MT>
-__device__ __forceinline__ void stage_plain(uint16_t* lds, int len, const uint16_t* x, int k, int m, int m0,
-                                            int k_begin) {
-  const int vecs = len / 8;  // 8 halves per 16-byte vector; len and K are multiples of 8
-  for (int idx = threadIdx.x; idx < MT * vecs; idx += kThreads) {
-    const int t = idx / vecs, v = idx - t * vecs;
-    const int kk = k_begin + 8 * v;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (m0 + t < m && kk < k) val = *reinterpret_cast<const uint4*>(x + (int64_t)(m0 + t) * k + kk);
-    *reinterpret_cast<uint4*>(lds + t * len + 8 * v) = val;
-  }
-}
-
-// Rotated basis: each wave rotates whole 128-blocks: x -> (1/sqrt(128)) H_128 diag(sign) x,
-// H in natural Sylvester order, computed in fp32 with an in-register butterfly (lane l holds
-// elements l and l + 64), then rounded once to fp16.
-template <int MT>
+// Rotated basis: each wave rotates whole 128-blocks into lds_x (fp16):
+// x -> (1/sqrt(128)) H_128 diag(sign) x, H in natural Sylvester order, computed in fp32 with an
+// in-register butterfly (lane l holds elements l and l + 64), then rounded once to fp16.
+template <int MT, int WAVES>
 __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint16_t* x, const int8_t* sign,
                                               int k, int m, int m0, int k_begin) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int blocks = len / 128;
-  for (int idx = wave; idx < MT * blocks; idx += kWaves) {
+  for (int idx = wave; idx < MT * blocks; idx += WAVES) {
     const int t = idx / blocks, b = idx - t * blocks;
     const int kb = k_begin + 128 * b;
     float v0 = 0.f, v1 = 0.f;
@@ -308,16 +251,22 @@ constexpr int min_waves_per_eu() {
 }
 
 template <int LAYOUT, int S, int MT, int ITER, bool ROT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8)))
-void gemv_kernel(const GemvArgs args) {
+__global__ __launch_bounds__(64 * waves_for<ITER>())
+__attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) void gemv_kernel(const GemvArgs args) {
   using G = Geo<LAYOUT>;
+  constexpr int kWaves = waves_for<ITER>();
+  constexpr int kThreads = 64 * kWaves;
   constexpr int kIter = ITER;
   constexpr int kRowsPerInstr = 64 / S;
   constexpr int kRowsPerWave = kIter * kRowsPerInstr;
   constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
   constexpr int kSliceElems = S * G::kElems;
+  constexpr int kGran = G::kPairDw / 4;  // 16-byte granules of pair words per chunk and token
+  constexpr int kAcc = LAYOUT == TGS_LAYOUT_BASE3 ? 2 : 1;
 
-  __shared__ __attribute__((aligned(16))) uint16_t xs[MT * kSliceElems];
+  __shared__ uint4 lds_pairs[MT * kGran * S];                                          // [t][granule][chunk]
+  __shared__ float lds_ref[MT * kAcc * S];                                             // [t][group][chunk]
+  __shared__ __attribute__((aligned(16))) uint16_t lds_x[ROT ? MT * kSliceElems : 8];  // rotated staging
 
   // find this workgroup's job (uniform; the table lives in the kernel arguments)
   int j = 0;
@@ -328,9 +277,9 @@ void gemv_kernel(const GemvArgs args) {
   const int chunks = chunks_per_row(LAYOUT, k);
   const int slices = (chunks + S - 1) / S;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cl = lane % S;      // chunk lane within a row
-  const int rslot = lane / S;   // row slot within an instruction
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cl = lane % S;     // chunk lane within a row
+  const int rslot = lane / S;  // row slot within an instruction
   const int row0 = ((int)blockIdx.x - job.block0) * kRowsPerBlock + wave * kRowsPerWave + rslot;
 
   constexpr int kBatch = kIter >= 2 ? 2 : 1;
@@ -351,14 +300,16 @@ void gemv_kernel(const GemvArgs args) {
   // codes and the (up to two) group scales of rows b*kBatch .. b*kBatch+kBatch-1 of this lane
   // slot. A lane whose chunk lies past the row (last slice) reads some other in-bounds bytes; its
   // activations are zero and its scales are forced to zero when used, so it adds nothing.
-  auto load_batch = [&](Batch& bt, int b, int c, bool chunk_ok, int g0, bool has_g1) {
+  auto load_batch = [&](Batch& bt, int b, int c, int g0) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int row = row0 + (b * kBatch + i) * kRowsPerInstr;
-      // unsigned arithmetic: an offset past the buffer simply reads as zero
-      const uint32_t code_off = (uint32_t)row * (uint32_t)job.stride + (uint32_t)c * 16u;
-      const uint32_t scale_off = ((uint32_t)row * (uint32_t)groups + (uint32_t)g0) * 2u;
-      bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)code_off, 0, 0));
+      // unsigned arithmetic: an offset past the buffer simply reads as zero. Rows, row strides
+      // and group counts are below 2^24 (checked on the host), so the full-rate 24-bit multiply
+      // gives the exact low 32 bits.
+      const uint32_t code_off = __umul24((uint32_t)row, (uint32_t)job.stride) + (uint32_t)c * 16u;
+      const uint32_t scale_off = (__umul24((uint32_t)row, (uint32_t)groups) + (uint32_t)g0) * 2u;
+      bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)code_off, 0, kStreamAux));
       bt.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)scale_off, 0, 0);
       bt.s1[i] = 0;
       if (LAYOUT == TGS_LAYOUT_BASE3)
@@ -377,7 +328,6 @@ void gemv_kernel(const GemvArgs args) {
       const int k_begin = ks * kSliceElems;
       const int c = ks * S + cl;  // this lane's chunk
       const bool chunk_ok = c < chunks;
-      // first trit of the second scale group, relative to the chunk (base-3 only)
       const int t0 = c * G::kElems;
       const int boundary = (LAYOUT == TGS_LAYOUT_BASE3) ? ((t0 / 128 + 1) * 128 - t0) : 1 << 20;
       const int g0 = (LAYOUT == TGS_LAYOUT_SLOT2) ? c / 2 : t0 / 128;
@@ -387,30 +337,72 @@ void gemv_kernel(const GemvArgs args) {
       // rows before the activation slice is staged, so the two latencies overlap.
       Batch ring[kRing];
 #pragma unroll
-      for (int b = 0; b < kRing - 1 && b < kBatches; ++b) load_batch(ring[b], b, c, chunk_ok, g0, has_g1);
+      for (int b = 0; b < kRing - 1 && b < kBatches; ++b) load_batch(ring[b], b, c, g0);
 
-      __syncthreads();  // the previous slice's activations are no longer read
-      if constexpr (ROT)
-        stage_rotated<MT>(xs, kSliceElems, job.x, job.signs, k, m, m0, k_begin);
-      else
-        stage_plain<MT>(xs, kSliceElems, job.x, k, m, m0, k_begin);
+      // ---- stage: pairs and all-zero-row products of the slice's chunks, once per workgroup
+      __syncthreads();  // the previous slice's pairs are no longer read
+      if constexpr (ROT) {
+        stage_rotated<MT, kWaves>(lds_x, kSliceElems, job.x, job.signs, k, m, m0, k_begin);
+        __syncthreads();
+      }
+      for (int u = tid; u < MT * S; u += kThreads) {
+        const int t = u / S, bc = u - t * S;  // token, chunk within the slice
+        const int bt0 = (ks * S + bc) * G::kElems;
+        const int bbound = (LAYOUT == TGS_LAYOUT_BASE3) ? ((bt0 / 128 + 1) * 128 - bt0) : 1 << 20;
+        uint32_t w[G::kElems / 2];
+#pragma unroll
+        for (int v = 0; v < G::kElems / 8; ++v) {
+          uint4 q = make_uint4(0, 0, 0, 0);
+          const int kk = bt0 + 8 * v;  // K and chunk starts are multiples of 8
+          if constexpr (ROT) {
+            q = *reinterpret_cast<const uint4*>(lds_x + t * kSliceElems + bc * G::kElems + 8 * v);
+          } else {
+            if (m0 + t < m && kk < k) q = *reinterpret_cast<const uint4*>(job.x + (int64_t)(m0 + t) * k + kk);
+          }
+          w[4 * v + 0] = q.x;
+          w[4 * v + 1] = q.y;
+          w[4 * v + 2] = q.z;
+          w[4 * v + 3] = q.w;
+        }
+        uint32_t p[G::kPairDw];
+        if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
+          build_pairs_slot2(w, p);
+          lds_ref[t * S + bc] = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
+        } else {
+          build_pairs_base3(w, bbound, p);
+          float r0, r1;
+          chunk_dot_base3(make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u), p, r0, r1);
+          lds_ref[(t * 2 + 0) * S + bc] = r0;
+          lds_ref[(t * 2 + 1) * S + bc] = r1;
+        }
+#pragma unroll
+        for (int g = 0; g < kGran; ++g)
+          lds_pairs[(t * kGran + g) * S + bc] = make_uint4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
+      }
       __syncthreads();
 
-      XRegs<LAYOUT, MT> xr;
-      xr.load(xs + cl * G::kElems, kSliceElems, boundary);
-      // chunk products of an all-zero row: the same decode-and-dot on its code word
+      // ---- this lane's pairs and reference products
+      uint32_t xp[MT][G::kPairDw];
       float ref0[MT], ref1[MT];
-      if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
-        chunk_dot_slot2<MT>(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), xr, ref0);
-      } else {
-        chunk_dot_base3<MT>(make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u), xr, ref0, ref1);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int g = 0; g < kGran; ++g) {
+          const uint4 q = lds_pairs[(t * kGran + g) * S + cl];
+          xp[t][4 * g + 0] = q.x;
+          xp[t][4 * g + 1] = q.y;
+          xp[t][4 * g + 2] = q.z;
+          xp[t][4 * g + 3] = q.w;
+        }
+        ref0[t] = lds_ref[(t * kAcc) * S + cl];
+        ref1[t] = kAcc == 2 ? lds_ref[(t * kAcc + kAcc - 1) * S + cl] : 0.f;
       }
 
       // rows in batches; kRing - 1 batches are in flight while one is computed (a ring of register
       // sets, fully unrolled, so no copies)
 #pragma unroll
       for (int b = 0; b < kBatches; ++b) {
-        if (b + kRing - 1 < kBatches) load_batch(ring[(b + kRing - 1) % kRing], b + kRing - 1, c, chunk_ok, g0, has_g1);
+        if (b + kRing - 1 < kBatches) load_batch(ring[(b + kRing - 1) % kRing], b + kRing - 1, c, g0);
         // keep the scheduler from hoisting later batches' loads: the ring bounds the registers
         __builtin_amdgcn_sched_barrier(0);
         const Batch& cur = ring[b % kRing];
@@ -419,18 +411,17 @@ void gemv_kernel(const GemvArgs args) {
           const int it = b * kBatch + i;
           const float sc0 = chunk_ok ? f16_to_f32((uint16_t)cur.s0[i]) : 0.f;
           if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
-            float qx[MT];
-            chunk_dot_slot2<MT>(cur.cw[i], xr, qx);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) part[it][t] = fmaf(sc0, (qx[t] - ref0[t]) * 1048576.0f, part[it][t]);
-          } else {
-            const float sc1 = (chunk_ok && has_g1) ? f16_to_f32((uint16_t)cur.s1[i]) : 0.f;
-            float q0[MT], q1[MT];
-            chunk_dot_base3<MT>(cur.cw[i], xr, q0, q1);
 #pragma unroll
             for (int t = 0; t < MT; ++t)
-              part[it][t] = fmaf(sc1, (q1[t] - ref1[t]) * 1048576.0f,
-                                 fmaf(sc0, (q0[t] - ref0[t]) * 1048576.0f, part[it][t]));
+              part[it][t] = fmaf(sc0, chunk_dot_slot2(cur.cw[i], xp[t]) - ref0[t], part[it][t]);
+          } else {
+            const float sc1 = (chunk_ok && has_g1) ? f16_to_f32((uint16_t)cur.s1[i]) : 0.f;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+              float q0, q1;
+              chunk_dot_base3(cur.cw[i], xp[t], q0, q1);
+              part[it][t] = fmaf(sc1, q1 - ref1[t], fmaf(sc0, q0 - ref0[t], part[it][t]));
+            }
           }
         }
       }
@@ -438,8 +429,7 @@ void gemv_kernel(const GemvArgs args) {
 
     // Reduce across the S lanes of each row, in a fixed order. Transposed: at each exchange step
     // a lane keeps half of its values and sends the other half to its partner, so the number of
-    // values per lane halves until one is left; the remaining steps are plain butterflies. The
-    // sum of row slot `it` ends in the lanes whose bits (within the S-lane group) match `it`.
+    // values per lane halves until one is left; the remaining steps are plain butterflies.
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       float v[kIter];
@@ -463,31 +453,251 @@ void gemv_kernel(const GemvArgs args) {
           v[0] += __shfl_xor(v[0], off);
         }
       }
-      // after the exchanges, lane bit pattern (within its S-lane group) selects the row slot:
-      // each exchange step with offset `off` (taken while count > 1) routes odd slots to the
-      // lanes with that bit set
+      // Each exchange step with offset `off` routes odd row slots to the lanes with that bit set,
+      // so those bits of the lane index name the row slot it now holds.
       int it_sel = 0, bit = 0;
 #pragma unroll
       for (int off = S / 2, cnt = kIter; off >= 1 && cnt > 1; off >>= 1, cnt /= 2, ++bit)
         if (lane & off) it_sel |= 1 << bit;
       const int row = row0 + it_sel * kRowsPerInstr;
-      // one lane per (row slot): the lowest lane whose exchange bits equal it_sel
+      // one writer per row slot: the lane whose butterfly-step bits are zero
       int low_bits = 0;
 #pragma unroll
       for (int off = S / 2, cnt = kIter; off >= 1; off >>= 1, cnt = cnt > 1 ? cnt / 2 : 1)
         if (cnt <= 1) low_bits |= off;
-      if ((cl & low_bits) == 0 && row < n && m0 + t < m) job.y[(int64_t)(m0 + t) * n + row] = v[0];
+      // the chunk products carry a factor 2^-20, undone here (an exact power of two)
+      if ((cl & low_bits) == 0 && row < n && m0 + t < m) job.y[(int64_t)(m0 + t) * n + row] = v[0] * 1048576.0f;
     }
   }
 }
 
-template <int LAYOUT, int S, int MT, int ITER, bool ROT>
-hipError_t launch_one(GemvArgs& args, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_kernel<LAYOUT, S, MT, ITER, ROT>), dim3(blocks), dim3(kThreads), 0, stream, args);
+// ---- streaming kernel: slot-2 codes, one activation row, plain basis ------------------------
+//
+// The decode case that carries most of the traffic. Differences from gemv_kernel:
+//   - the activation pairs and all-zero-row products of the whole row length are staged once per
+//     workgroup (at most 132 bytes per 64 weights of K in LDS), so the row stream never stops for
+//     a barrier;
+//   - each wave walks a long run of rows (a runtime count) with a ring of four 2-row batches in
+//     flight, continuing across K slices: codes never wait for activations;
+//   - each 2-row batch is reduced across its lanes right away (permlane swaps and DPP row
+//     rotations: about four VALU operations per row and no LDS traffic); rows that span several
+//     K slices add their slice sums into a per-row LDS accumulator owned by one lane.
+
+// 32-bit lane moves within 16-lane rows (DPP): rotate right by N, or fixed quad/half patterns
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppRor1 = 0x121, kDppRor2 = 0x122, kDppRor4 = 0x124, kDppRor8 = 0x128;
+constexpr int kDppHalfMirror = 0x141, kDppQuadSwap2 = 0x4E, kDppQuadSwap1 = 0xB1;
+
+// Sum of v0 over the S lanes of each row group goes to the group's lanes holding slot 0, and of
+// v1 to those holding slot 1. Returns the sum this lane holds and sets `slot` to which one it is.
+// Lane-half swaps of gfx950, as inline asm: with the swap builtins, an expression that uses both
+// results reads the first one twice (seen in the assembly of this file), so the operands are
+// passed read-write here. Each s_nop 1 gives the two wait states a VALU write needs before a
+// swap reads the register, and the same after, before the next VALU reads the result.
+__device__ __forceinline__ void swap_halves32(float& a, float& b) {  // a's lanes 32..63 <-> b's 0..31
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows16(float& a, float& b) {  // a's odd 16-lane rows <-> b's even
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+template <int S>
+__device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& slot) {
+  if constexpr (S == 64) {
+    // lanes 0..31 end with v0[l] + v0[l + 32], lanes 32..63 with v1[l - 32] + v1[l]
+    swap_halves32(v0, v1);
+    float s = v0 + v1;
+    // each lane adds the lane 16 away in its 32-lane half
+    float t = s;
+    swap_rows16(s, t);
+    s += t;
+    s += dpp<kDppRor8>(s);
+    s += dpp<kDppRor4>(s);
+    s += dpp<kDppRor2>(s);
+    s += dpp<kDppRor1>(s);
+    slot = lane >> 5;
+    return s;
+  } else if constexpr (S == 32) {
+    // within each 32-lane half: lanes 0..15 end with v0 of rows 0 and 1, lanes 16..31 with v1
+    swap_rows16(v0, v1);
+    float s = v0 + v1;
+    s += dpp<kDppRor8>(s);
+    s += dpp<kDppRor4>(s);
+    s += dpp<kDppRor2>(s);
+    s += dpp<kDppRor1>(s);
+    slot = (lane >> 4) & 1;
+    return s;
+  } else {
+    static_assert(S == 16, "lanes per row must be 16, 32 or 64");
+    // within each 16-lane group: lanes 0..7 keep slot 0, lanes 8..15 slot 1
+    const bool upper = (lane & 8) != 0;
+    const float keep = upper ? v1 : v0, send = upper ? v0 : v1;
+    float s = keep + dpp<kDppRor8>(send);
+    s += dpp<kDppHalfMirror>(s);  // lane i with lane 7 - i of its 8-lane half
+    s += dpp<kDppQuadSwap2>(s);
+    s += dpp<kDppQuadSwap1>(s);
+    slot = (lane >> 3) & 1;
+    return s;
+  }
+}
+
+template <int S>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void gemv_stream_kernel(const GemvArgs args, int rows_per_wave, int log2_batches_per_slice) {
+  constexpr int kRowsPerInstr = 64 / S;
+  constexpr int kRing = 4;
+  extern __shared__ uint4 smem[];  // pairs [8 granules][chunks] | refs [chunks] | row sums [rows]
+
+  int j = 0;
+  while (j + 1 < args.count && (int)blockIdx.x >= args.job[j + 1].block0) ++j;
+  const GemvJob& job = args.job[j];
+  const int n = job.n, k = job.k;
+  const int groups = k / 128;
+  const int chunks = k / 64;
+  const int slices = (chunks + S - 1) / S;
+  const int cpad = slices * S;  // chunk slots staged (the tail of the last slice is zero)
+  const int R = rows_per_wave;  // row slots per wave; a multiple of 8
+  const int batches_per_slice = R / 2;
+  const int total_batches = slices * batches_per_slice;
+
+  uint4* lds_pairs = smem;
+  float* lds_ref = reinterpret_cast<float*>(smem + 8 * cpad);
+  float* lds_acc = lds_ref + cpad;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cl = lane % S, rslot = lane / S;
+  const int block_row0 = ((int)blockIdx.x - job.block0) * 4 * R * kRowsPerInstr;
+  const int wave_row0 = block_row0 + wave * R * kRowsPerInstr;  // row of slot 0 of row group 0
+  const int row0 = wave_row0 + rslot;
+
+  const __amdgpu_buffer_rsrc_t code_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.codes, 0, (int)((int64_t)n * job.stride), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t scale_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
+
+  struct Batch {
+    uint4 cw[2];
+    uint32_t s[2];
+  };
+  // batch index -> (slice, rows); loads past the matrix read as zero
+  auto load_batch = [&](Batch& bt, int idx) {
+    const int ks = idx >> log2_batches_per_slice, b = idx & (batches_per_slice - 1);
+    const int c = ks * S + cl;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = row0 + (2 * b + i) * kRowsPerInstr;
+      const uint32_t code_off = __umul24((uint32_t)row, (uint32_t)job.stride) + (uint32_t)c * 16u;
+      const uint32_t scale_off = (__umul24((uint32_t)row, (uint32_t)groups) + (uint32_t)(c >> 1)) * 2u;
+      bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)code_off, 0, kStreamAux));
+      bt.s[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)scale_off, 0, 0);
+    }
+  };
+
+  // the weight stream starts before anything else
+  Batch ring[kRing];
+#pragma unroll
+  for (int b = 0; b < kRing - 1; ++b)
+    if (b < total_batches) load_batch(ring[b], b);
+
+  // stage the pairs and all-zero-row products of every chunk of the row, once
+  for (int c = tid; c < cpad; c += 256) {
+    uint32_t w[32];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      uint4 q = make_uint4(0, 0, 0, 0);
+      if (c < chunks) q = *reinterpret_cast<const uint4*>(job.x + (int64_t)c * 64 + 8 * v);
+      w[4 * v + 0] = q.x;
+      w[4 * v + 1] = q.y;
+      w[4 * v + 2] = q.z;
+      w[4 * v + 3] = q.w;
+    }
+    uint32_t p[32];
+    build_pairs_slot2(w, p);
+    lds_ref[c] = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) lds_pairs[g * cpad + c] = make_uint4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
+  }
+  if (slices > 1)
+    for (int r = tid; r < 4 * R * kRowsPerInstr; r += 256) lds_acc[r] = 0.f;
+  __syncthreads();
+
+  uint32_t xp[32];
+  float ref = 0.f;
+  bool chunk_ok = false;
+  for (int base = 0; base < total_batches; base += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int idx = base + u;
+      if (idx < total_batches) {
+        if (idx + kRing - 1 < total_batches) load_batch(ring[(u + kRing - 1) % kRing], idx + kRing - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int b = idx & (batches_per_slice - 1);
+        if (b == 0) {  // a new K slice: this lane's pairs (conflict-free 16-byte LDS reads)
+          const int c = (idx >> log2_batches_per_slice) * S + cl;
+#pragma unroll
+          for (int g = 0; g < 8; ++g) {
+            const uint4 q = lds_pairs[g * cpad + c];
+            xp[4 * g + 0] = q.x;
+            xp[4 * g + 1] = q.y;
+            xp[4 * g + 2] = q.z;
+            xp[4 * g + 3] = q.w;
+          }
+          ref = lds_ref[c];
+          chunk_ok = c < chunks;
+        }
+        const Batch& cur = ring[u];
+        const float s0 = chunk_ok ? f16_to_f32((uint16_t)cur.s[0]) : 0.f;
+        const float s1 = chunk_ok ? f16_to_f32((uint16_t)cur.s[1]) : 0.f;
+        const float v0 = s0 * (chunk_dot_slot2(cur.cw[0], xp) - ref);
+        const float v1 = s1 * (chunk_dot_slot2(cur.cw[1], xp) - ref);
+        int slot;
+        const float sum = reduce_pair<S>(v0, v1, lane, slot);
+        // one writer per row: the first lane of each (row group, slot)
+        constexpr int kSlotLanes = S == 64 ? 32 : (S == 32 ? 16 : 8);
+        if ((lane & (kSlotLanes - 1)) == 0) {
+          const int local = wave * R * kRowsPerInstr + (2 * b + slot) * kRowsPerInstr + rslot;
+          const int row = block_row0 + local;
+          if (slices == 1) {
+            if (row < n) job.y[row] = sum * 1048576.0f;
+          } else {
+            lds_acc[local] += sum;
+          }
+        }
+      }
+    }
+  }
+  if (slices > 1) {
+    // each row's slice sums were added by one lane of this wave; LDS ops of a wave are in order
+    for (int r = lane; r < R * kRowsPerInstr; r += 64) {
+      const int local = wave * R * kRowsPerInstr + r;
+      const int row = block_row0 + local;
+      if (row < n) job.y[row] = lds_acc[local] * 1048576.0f;
+    }
+  }
+}
+
+template <int S>
+hipError_t launch_stream(GemvArgs& args, int blocks, int rows_per_wave, int k_max, hipStream_t stream) {
+  int lbb = 0;
+  while ((1 << lbb) < rows_per_wave / 2) ++lbb;
+  const int chunks = k_max / 64;
+  const int cpad = (chunks + S - 1) / S * S;
+  const size_t lds = (size_t)cpad * (8 * 16 + 4) + (size_t)4 * rows_per_wave * (64 / S) * 4;
+  hipLaunchKernelGGL((gemv_stream_kernel<S>), dim3(blocks), dim3(256), lds, stream, args, rows_per_wave, lbb);
   return hipGetLastError();
 }
 
-// rows per lane slot: 8 for large single-token launches (more work per workgroup), else 4;
+template <int LAYOUT, int S, int MT, int ITER, bool ROT>
+hipError_t launch_one(GemvArgs& args, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_kernel<LAYOUT, S, MT, ITER, ROT>), dim3(blocks), dim3(64 * waves_for<ITER>()), 0, stream,
+                     args);
+  return hipGetLastError();
+}
+
+// rows per lane slot: 8 for large single-token slot-2 launches (more work per workgroup), else 4;
 // fewer when several tokens share the registers
 template <int LAYOUT, int S, int MT>
 hipError_t launch_rot(bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
@@ -550,17 +760,29 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
     }
   }
   p.lanes = best;
+  // the streaming kernel stages activation pairs for the whole row in LDS (132 bytes per 64
+  // weights of K): used up to K = 28672, which keeps it under 64 KB per workgroup
+  p.stream = (layout == TGS_LAYOUT_SLOT2 && m == 1 && !rotated && k <= 28672) ? 1 : 0;
   const int mt = tokens_per_pass(layout, m);
   p.iter = mt == 1 ? 4 : (mt == 2 ? 2 : 1);
-  p.rows_per_block = kWaves * p.iter * (64 / best);
+  p.rows_per_block = 4 * p.iter * (64 / best);  // 4 waves per workgroup at these sizes
   return p;
 }
 
 void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
-  // single-token slot-2 launches with plenty of rows: 2x more rows per workgroup, still >= 2048
-  // workgroups
+  if (p.stream) {
+    // rows per wave: as many as keep >= 1024 workgroups (4 per CU), between 8 and 64
+    const int64_t rows_per_instr = 64 / p.lanes;
+    int r = 64;
+    while (r > 8 && (total_rows + 4 * r * rows_per_instr - 1) / (4 * r * rows_per_instr) < 1024) r /= 2;
+    p.iter = r;
+    p.rows_per_block = (int32_t)(4 * r * rows_per_instr);
+    return;
+  }
+  // single-token slot-2 launches with plenty of rows: twice the rows per workgroup (8 rows per lane
+  // slot) while that still leaves >= 2048 workgroups
   if (p.layout != TGS_LAYOUT_SLOT2 || tokens_per_pass(p.layout, p.m) != 1) return;
-  const int64_t big_rows = (int64_t)kWaves * 8 * (64 / p.lanes);
+  const int64_t big_rows = (int64_t)waves_for<8>() * 8 * (64 / p.lanes);
   if ((total_rows + big_rows - 1) / big_rows >= 2048) {
     p.iter = 8;
     p.rows_per_block = (int32_t)big_rows;
@@ -568,6 +790,15 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
 }
 
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream) {
+  if (plan.stream) {
+    int k_max = 0;
+    for (int i = 0; i < args.count; ++i) k_max = args.job[i].k > k_max ? args.job[i].k : k_max;
+    switch (plan.lanes) {
+      case 16: return launch_stream<16>(args, blocks, plan.iter, k_max, stream);
+      case 32: return launch_stream<32>(args, blocks, plan.iter, k_max, stream);
+      default: return launch_stream<64>(args, blocks, plan.iter, k_max, stream);
+    }
+  }
   const int mt = tokens_per_pass(plan.layout, plan.m);
   const bool rot = plan.rotated != 0;
   if (plan.layout == TGS_LAYOUT_SLOT2)

@@ -142,9 +142,9 @@ tgs_status check_matrix(const tgs_matrix* w, bool device) {
   if (w->n < 1 || w->k < 128 || w->k % 128 != 0)
     return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128 (n=%lld, k=%lld)", (long long)w->n,
                 (long long)w->k);
-  if (device && (w->n > INT32_MAX || w->k > (1LL << 30)))
-    return fail(TGS_E_SHAPE, "n or k too large for the device kernels (n=%lld, k=%lld)", (long long)w->n,
-                (long long)w->k);
+  if (device && (w->n >= (1LL << 24) || w->k >= (1LL << 24) || w->code_row_stride >= (1LL << 24)))
+    return fail(TGS_E_SHAPE, "n, k and the row stride must stay below 2^24 for the device kernels (n=%lld, k=%lld)",
+                (long long)w->n, (long long)w->k);
   const size_t rb = row_bytes(w->layout, w->k);
   if (w->code_row_stride < (int64_t)rb || w->code_row_stride % 16 != 0)
     return fail(TGS_E_SHAPE, "code_row_stride %lld must be a multiple of 16 and >= %zu", (long long)w->code_row_stride,
@@ -271,7 +271,8 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
     for (int32_t j = i; j < count; ++j) {
       if (done[(size_t)j]) continue;
       const tgs::GemvPlan pj = tgs::gemv_plan(ws[j].layout, ws[j].k, m, ws[j].rotated);
-      if (pj.layout != plan.layout || pj.lanes != plan.lanes || pj.rotated != plan.rotated) continue;
+      if (pj.layout != plan.layout || pj.lanes != plan.lanes || pj.rotated != plan.rotated || pj.stream != plan.stream)
+        continue;
       members.push_back(j);
       total_rows += ws[j].n;
       done[(size_t)j] = 1;

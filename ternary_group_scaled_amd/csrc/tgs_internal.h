@@ -36,6 +36,7 @@ struct GemvPlan {
   int32_t lanes;      // lanes per row (16, 32 or 64)
   int32_t m;          // activation rows
   int32_t rotated;    // 0 or 1
+  int32_t stream;     // 1: the streaming single-token kernel (slot-2, plain basis)
   int32_t iter;       // rows per lane slot
   int32_t rows_per_block;
 };

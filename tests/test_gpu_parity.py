@@ -54,7 +54,8 @@ def test_config1_slot2_gemv():
     assert (y2.view(np.uint32) == y.view(np.uint32)).all()  # run-to-run bitwise determinism
 
 
-SHAPES = [(1, 128), (17, 256), (300, 1024), (129, 4096), (64, 5120), (33, 12288), (40, 17408), (70, 640)]
+SHAPES = [(1, 128), (17, 256), (300, 1024), (129, 4096), (64, 5120), (33, 12288), (40, 17408), (70, 640),
+          (9, 30720), (130, 2048)]
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
