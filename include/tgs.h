@@ -145,6 +145,8 @@ tgs_status unpack_ternary(const tgs_matrix* w, int8_t* trits_out, uint16_t* scal
  * Arithmetic: codes are decoded in registers; each 128-group is accumulated in fp32 and scaled
  * by its fp16 scale in fp32. Rotated activations are rounded once to fp16 after the transform,
  * so |R x| must stay below 65504. Results are deterministic run to run (no float atomics).
+ * Device limits (all device calls): n, k and the row stride below 2^24, and n * row stride at
+ * most 2^31 - 2^20 bytes; larger matrices give TGS_E_SHAPE.
  */
 tgs_status ternary_gemv(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m,
                         const int8_t* signs, float* y, void* stream);

@@ -553,7 +553,7 @@ void gemv_stream_kernel(const GemvArgs args, int rows_per_wave, int log2_batches
 
   int j = 0;
   while (j + 1 < args.count && (int)blockIdx.x >= args.job[j + 1].block0) ++j;
-  const GemvJob& job = args.job[j];
+  const GemvJob job = args.job[j];  // a copy: the fields stay in scalar registers
   const int n = job.n, k = job.k;
   const int groups = k / 128;
   const int chunks = k / 64;
@@ -582,8 +582,11 @@ void gemv_stream_kernel(const GemvArgs args, int rows_per_wave, int log2_batches
     uint4 cw[2];
     uint32_t s[2];
   };
-  // batch index -> (slice, rows); loads past the matrix read as zero
+  // batch index -> (slice, rows). Loads past the matrix read as zero; batches past the last one are
+  // parked out of range, so every load is issued unconditionally and the compiler's wait counts
+  // stay exact (a load skipped on one path makes every later wait assume the worst case).
   auto load_batch = [&](Batch& bt, int idx) {
+    const bool live = idx < total_batches;
     const int ks = idx >> log2_batches_per_slice, b = idx & (batches_per_slice - 1);
     const int c = ks * S + cl;
 #pragma unroll
@@ -591,34 +594,46 @@ void gemv_stream_kernel(const GemvArgs args, int rows_per_wave, int log2_batches
       const int row = row0 + (2 * b + i) * kRowsPerInstr;
       const uint32_t code_off = __umul24((uint32_t)row, (uint32_t)job.stride) + (uint32_t)c * 16u;
       const uint32_t scale_off = (__umul24((uint32_t)row, (uint32_t)groups) + (uint32_t)(c >> 1)) * 2u;
-      bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)code_off, 0, kStreamAux));
-      bt.s[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)scale_off, 0, 0);
+      bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               code_rsrc, live ? (int)code_off : kOobOffset, 0, kStreamAux));
+      bt.s[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, live ? (int)scale_off : kOobOffset, 0, 0);
     }
   };
 
-  // the weight stream starts before anything else
-  Batch ring[kRing];
-#pragma unroll
-  for (int b = 0; b < kRing - 1; ++b)
-    if (b < total_batches) load_batch(ring[b], b);
-
-  // stage the pairs and all-zero-row products of every chunk of the row, once
-  for (int c = tid; c < cpad; c += 256) {
-    uint32_t w[32];
+  // Activation loads go out first: vector-memory waits retire in issue order, so staging them
+  // then waits only for these and overlaps the weight loads issued next. Reads past K return zero.
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)job.x, 0, k * 2, kRsrcWord3);
+  auto load_x = [&](uint32_t (&w)[32], int c) {
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      uint4 q = make_uint4(0, 0, 0, 0);
-      if (c < chunks) q = *reinterpret_cast<const uint4*>(job.x + (int64_t)c * 64 + 8 * v);
+      const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, c * 128 + 16 * v, 0, 0));
       w[4 * v + 0] = q.x;
       w[4 * v + 1] = q.y;
       w[4 * v + 2] = q.z;
       w[4 * v + 3] = q.w;
     }
+  };
+  // pairs and all-zero-row product of chunk c into LDS
+  auto stage = [&](const uint32_t (&w)[32], int c) {
     uint32_t p[32];
     build_pairs_slot2(w, p);
     lds_ref[c] = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
 #pragma unroll
     for (int g = 0; g < 8; ++g) lds_pairs[g * cpad + c] = make_uint4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
+  };
+  uint32_t xw[32];
+  load_x(xw, tid);
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+
+  Batch ring[kRing];
+#pragma unroll
+  for (int b = 0; b < kRing - 1; ++b) load_batch(ring[b], b);
+
+  // stage every chunk of the row once (one per thread up to K = 16384)
+  if (tid < cpad) stage(xw, tid);
+  for (int c = tid + 256; c < cpad; c += 256) {
+    load_x(xw, c);
+    stage(xw, c);
   }
   if (slices > 1)
     for (int r = tid; r < 4 * R * kRowsPerInstr; r += 256) lds_acc[r] = 0.f;
@@ -631,40 +646,39 @@ void gemv_stream_kernel(const GemvArgs args, int rows_per_wave, int log2_batches
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int idx = base + u;
-      if (idx < total_batches) {
-        if (idx + kRing - 1 < total_batches) load_batch(ring[(u + kRing - 1) % kRing], idx + kRing - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        const int b = idx & (batches_per_slice - 1);
-        if (b == 0) {  // a new K slice: this lane's pairs (conflict-free 16-byte LDS reads)
-          const int c = (idx >> log2_batches_per_slice) * S + cl;
+      const bool live = idx < total_batches;
+      load_batch(ring[(u + kRing - 1) % kRing], idx + kRing - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int b = idx & (batches_per_slice - 1);
+      if (b == 0 && live) {  // a new K slice: this lane's pairs (conflict-free 16-byte LDS reads)
+        const int c = (idx >> log2_batches_per_slice) * S + cl;
 #pragma unroll
-          for (int g = 0; g < 8; ++g) {
-            const uint4 q = lds_pairs[g * cpad + c];
-            xp[4 * g + 0] = q.x;
-            xp[4 * g + 1] = q.y;
-            xp[4 * g + 2] = q.z;
-            xp[4 * g + 3] = q.w;
-          }
-          ref = lds_ref[c];
-          chunk_ok = c < chunks;
+        for (int g = 0; g < 8; ++g) {
+          const uint4 q = lds_pairs[g * cpad + c];
+          xp[4 * g + 0] = q.x;
+          xp[4 * g + 1] = q.y;
+          xp[4 * g + 2] = q.z;
+          xp[4 * g + 3] = q.w;
         }
-        const Batch& cur = ring[u];
-        const float s0 = chunk_ok ? f16_to_f32((uint16_t)cur.s[0]) : 0.f;
-        const float s1 = chunk_ok ? f16_to_f32((uint16_t)cur.s[1]) : 0.f;
-        const float v0 = s0 * (chunk_dot_slot2(cur.cw[0], xp) - ref);
-        const float v1 = s1 * (chunk_dot_slot2(cur.cw[1], xp) - ref);
-        int slot;
-        const float sum = reduce_pair<S>(v0, v1, lane, slot);
-        // one writer per row: the first lane of each (row group, slot)
-        constexpr int kSlotLanes = S == 64 ? 32 : (S == 32 ? 16 : 8);
-        if ((lane & (kSlotLanes - 1)) == 0) {
-          const int local = wave * R * kRowsPerInstr + (2 * b + slot) * kRowsPerInstr + rslot;
-          const int row = block_row0 + local;
-          if (slices == 1) {
-            if (row < n) job.y[row] = sum * 1048576.0f;
-          } else {
-            lds_acc[local] += sum;
-          }
+        ref = lds_ref[c];
+        chunk_ok = c < chunks;
+      }
+      const Batch& cur = ring[u];
+      const float s0 = chunk_ok ? f16_to_f32((uint16_t)cur.s[0]) : 0.f;
+      const float s1 = chunk_ok ? f16_to_f32((uint16_t)cur.s[1]) : 0.f;
+      const float v0 = s0 * (chunk_dot_slot2(cur.cw[0], xp) - ref);
+      const float v1 = s1 * (chunk_dot_slot2(cur.cw[1], xp) - ref);
+      int slot;
+      const float sum = reduce_pair<S>(v0, v1, lane, slot);
+      // one writer per row: the first lane of each (row group, slot)
+      constexpr int kSlotLanes = S == 64 ? 32 : (S == 32 ? 16 : 8);
+      if (live && (lane & (kSlotLanes - 1)) == 0) {
+        const int local = wave * R * kRowsPerInstr + (2 * b + slot) * kRowsPerInstr + rslot;
+        const int row = block_row0 + local;
+        if (slices == 1) {
+          if (row < n) job.y[row] = sum * 1048576.0f;
+        } else {
+          lds_acc[local] += sum;
         }
       }
     }
@@ -771,10 +785,11 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
 
 void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
   if (p.stream) {
-    // rows per wave: as many as keep >= 1024 workgroups (4 per CU), between 8 and 64
+    // rows per wave: as many as keep >= 2048 workgroups (8 per CU), between 8 and 64. Fewer than 8
+    // rows per wave measured slower: each workgroup stages the whole activation row first.
     const int64_t rows_per_instr = 64 / p.lanes;
     int r = 64;
-    while (r > 8 && (total_rows + 4 * r * rows_per_instr - 1) / (4 * r * rows_per_instr) < 1024) r /= 2;
+    while (r > 8 && (total_rows + 4 * r * rows_per_instr - 1) / (4 * r * rows_per_instr) < 2048) r /= 2;
     p.iter = r;
     p.rows_per_block = (int32_t)(4 * r * rows_per_instr);
     return;

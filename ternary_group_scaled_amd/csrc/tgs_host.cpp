@@ -149,8 +149,8 @@ tgs_status check_matrix(const tgs_matrix* w, bool device) {
   if (w->code_row_stride < (int64_t)rb || w->code_row_stride % 16 != 0)
     return fail(TGS_E_SHAPE, "code_row_stride %lld must be a multiple of 16 and >= %zu", (long long)w->code_row_stride,
                 rb);
-  if (device && w->n * w->code_row_stride >= (1LL << 31))
-    return fail(TGS_E_SHAPE, "codes of one matrix must stay below 2 GiB (n * code_row_stride = %lld)",
+  if (device && w->n * w->code_row_stride > tgs::kMaxDeviceCodeBytes)
+    return fail(TGS_E_SHAPE, "codes of one matrix must stay within 2 GiB - 1 MiB (n * code_row_stride = %lld)",
                 (long long)(w->n * w->code_row_stride));
   if (!w->codes || !w->scales) return fail(TGS_E_NULL, "codes or scales pointer is NULL");
   if (!aligned(w->codes, 16)) return fail(TGS_E_ALIGN, "codes must be 16-byte aligned");

@@ -9,6 +9,10 @@
 namespace tgs {
 
 constexpr int kMaxJobs = TGS_MAX_BATCH;
+// Largest code plane of one matrix on the device. Kernels read through 32-bit buffer offsets and
+// park loads they do not need at kOobOffset, which must lie past every valid range.
+constexpr int64_t kMaxDeviceCodeBytes = (1LL << 31) - (1LL << 20);
+constexpr int kOobOffset = 0x7FFFFFF0;
 
 // One matrix of a batched GEMV launch. All pointers are device pointers.
 struct GemvJob {
