@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="8b", choices=["8b", "base3", "rotated", "gemm", "config1"])
-    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers of the set (default: 36 for the 8B-class sets, 64 for the rotated 27B-class set)")
     ap.add_argument("--mode", default="layer", choices=["layer", "fused-layer", "set"],
                     help="launch grouping for the 8B set: same-input groups (144 launches), one launch per "
                          "layer (36), or the whole set in as few launches as possible")
@@ -144,7 +145,7 @@ def measured_traffic(profile_name):
 # ----------------------------------------------------------------------------- 8B decode set
 
 def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_name=None):
-    layers = args.layers
+    layers = args.layers or 36
     log(f"[bench] building {layers} layers x {len(LAYER_8B)} matrices ({'slot-2' if layout == 1 else 'base-3'})")
     t0 = time.time()
     mats, host = [], []
@@ -238,7 +239,7 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
                      "traffic_profile": profile if traffic is not None else None},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_8b(host, layout, args.cpu_seconds, ms, total_bytes / layers)
+        result["cpu_baseline"] = cpu_baseline_8b(host, layout, args.cpu_seconds, ms, total_bytes / layers, layers)
     return result
 
 
@@ -260,7 +261,7 @@ def check_layer0(torch, host, xs, ys, layout):
     log(f"[bench] layer-0 sampled parity ok (max err/bound {worst:.3g})")
 
 
-def cpu_baseline_8b(host, layout, seconds, gpu_ms, layer_bytes):
+def cpu_baseline_8b(host, layout, seconds, gpu_ms, layer_bytes, layers):
     """The fp64 oracle on the host cores over layer-0's 7 matrices, repeated for ~`seconds`."""
     import oracle
     import synth
@@ -278,15 +279,15 @@ def cpu_baseline_8b(host, layout, seconds, gpu_ms, layer_bytes):
     layer_gbs = layer_bytes / dt / 1e9
     return {"value": round(layer_gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"layer 0 of the set (7 matrices, {int(layer_bytes)} algorithmic bytes), {passes} passes in "
-                      f"{time.time() - t0:.1f}s; full-set equivalent {1.0 / (dt * 36):.3f} steps/s",
-            "gpu_speedup": round((dt * 36) / (gpu_ms * 1e-3), 1)}
+                      f"{time.time() - t0:.1f}s; full-set equivalent {1.0 / (dt * layers):.3f} steps/s",
+            "gpu_speedup": round((dt * layers) / (gpu_ms * 1e-3), 1)}
 
 
 # ----------------------------------------------------------------------------- other workloads
 
 def bench_rotated(args, torch, tgs, synth):
     """27B-class rotated-basis GEMV, base-3: gate/up 17408x5120 and down 5120x17408 per layer."""
-    layers = min(args.layers, 64)
+    layers = args.layers or 64
     shapes = [("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408)]
     res = []
     for m in (1, 8):
