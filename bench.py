@@ -212,7 +212,7 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
     per_launch_bytes = total_bytes / n_launches
     per_launch_s = ms * 1e-3 / n_launches
     kernel_gbs = per_launch_bytes / per_launch_s / 1e9
-    kernel = "gemv_stream_kernel" if layout == 1 else "gemv_kernel"
+    kernel = "gemv_wave_kernel" if layout == 1 else "gemv_kernel"
     profile = f"{kernel}.8b_{'slot2' if layout == 1 else 'base3'}_m1_{args.mode}.pmc.txt"
     traffic = measured_traffic(profile)
 

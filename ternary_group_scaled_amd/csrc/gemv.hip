@@ -471,18 +471,23 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
   }
 }
 
-// ---- streaming kernel: slot-2 codes, one activation row, plain basis ------------------------
+// ---- single-token kernel: slot-2 codes, one activation row, plain basis --------------------
 //
-// The decode case that carries most of the traffic. Differences from gemv_kernel:
-//   - the activation pairs and all-zero-row products of the whole row length are staged once per
-//     workgroup (at most 132 bytes per 64 weights of K in LDS), so the row stream never stops for
-//     a barrier;
-//   - each wave walks a long run of rows (a runtime count) with a ring of four 2-row batches in
-//     flight, continuing across K slices: codes never wait for activations;
-//   - each 2-row batch is reduced across its lanes right away (permlane swaps and DPP row
-//     rotations: about four VALU operations per row and no LDS traffic); rows that span several
-//     K slices add their slice sums into a per-row LDS accumulator owned by one lane.
-
+// The decode case that carries most of the traffic. A workgroup owns a block of rows and has one
+// wave per K slice of S chunks (64 weights each). Each lane owns one chunk of every row of its
+// wave, so the lane that turns its 64 activations into dot2 pairs (and their all-zero-row
+// product) is the only one that ever uses them: they stay in registers, with no LDS staging and
+// no barrier before the weight stream. Per wave:
+//   1. its activation loads (8 x 16 B per lane) go out first, then the first four 2-row batches
+//      of codes and scales, so for small matrices all of a wave's loads are in flight at once;
+//   2. the pairs are built while the weights are in flight (vector-memory waits retire in issue
+//      order, so this waits only for the activations);
+//   3. batches are consumed in groups of four; while a group is consumed, the next group's loads
+//      go out into the slots just freed. Every load of a group is issued unconditionally, so the
+//      compiler's wait counts are exact;
+//   4. each batch is reduced across its lanes right away (lane-half swaps and DPP rotations, no
+//      LDS). With one slice the sums go straight to y; otherwise each wave writes its slice sums
+//      to LDS and, after one barrier, every row adds its slices in a fixed order.
 // 32-bit lane moves within 16-lane rows (DPP): rotate right by N, or fixed quad/half patterns
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -545,11 +550,11 @@ __device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& 
 }
 
 template <int S>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void gemv_stream_kernel(const GemvArgs args, int rows_per_wave, int log2_batches_per_slice) {
+__global__ __launch_bounds__(1024)
+void gemv_wave_kernel(const GemvArgs args, int rows_per_wave) {
   constexpr int kRowsPerInstr = 64 / S;
   constexpr int kRing = 4;
-  extern __shared__ uint4 smem[];  // pairs [8 granules][chunks] | refs [chunks] | row sums [rows]
+  extern __shared__ float lds_acc[];  // [slices][rows of the workgroup], only when slices > 1
 
   int j = 0;
   while (j + 1 < args.count && (int)blockIdx.x >= args.job[j + 1].block0) ++j;
@@ -557,150 +562,109 @@ void gemv_stream_kernel(const GemvArgs args, int rows_per_wave, int log2_batches
   const int n = job.n, k = job.k;
   const int groups = k / 128;
   const int chunks = k / 64;
-  const int slices = (chunks + S - 1) / S;
-  const int cpad = slices * S;  // chunk slots staged (the tail of the last slice is zero)
-  const int R = rows_per_wave;  // row slots per wave; a multiple of 8
-  const int batches_per_slice = R / 2;
-  const int total_batches = slices * batches_per_slice;
+  const int slices = (chunks + S - 1) / S;  // == waves per workgroup
+  const int R = rows_per_wave;              // row slots per wave: 8, 16, 32 or 64
+  const int batches = R / 2;
+  const int rows_wg = R * kRowsPerInstr;
 
-  uint4* lds_pairs = smem;
-  float* lds_ref = reinterpret_cast<float*>(smem + 8 * cpad);
-  float* lds_acc = lds_ref + cpad;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;  // wave index == K slice
   const int cl = lane % S, rslot = lane / S;
-  const int block_row0 = ((int)blockIdx.x - job.block0) * 4 * R * kRowsPerInstr;
-  const int wave_row0 = block_row0 + wave * R * kRowsPerInstr;  // row of slot 0 of row group 0
-  const int row0 = wave_row0 + rslot;
+  const int c = ks * S + cl;  // this lane's chunk
+  const bool lane_live = c < chunks;
+  const int block_row0 = ((int)blockIdx.x - job.block0) * rows_wg;
+  const int row0 = block_row0 + rslot;
 
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)job.x, 0, k * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t code_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)job.codes, 0, (int)((int64_t)n * job.stride), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t scale_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)job.scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
 
+  // 1. activations of this lane's chunk (reads past K return zero)
+  uint32_t xw[32];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, c * 128 + 16 * v, 0, 0));
+    xw[4 * v + 0] = q.x;
+    xw[4 * v + 1] = q.y;
+    xw[4 * v + 2] = q.z;
+    xw[4 * v + 3] = q.w;
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order
+
   struct Batch {
     uint4 cw[2];
     uint32_t s[2];
   };
-  // batch index -> (slice, rows). Loads past the matrix read as zero; batches past the last one are
-  // parked out of range, so every load is issued unconditionally and the compiler's wait counts
-  // stay exact (a load skipped on one path makes every later wait assume the worst case).
-  auto load_batch = [&](Batch& bt, int idx) {
-    const bool live = idx < total_batches;
-    const int ks = idx >> log2_batches_per_slice, b = idx & (batches_per_slice - 1);
-    const int c = ks * S + cl;
+  // batch b -> rows row0 + (2b + i) * kRowsPerInstr. Rows past the matrix read as zero; a lane
+  // past the row's last chunk parks its loads out of range (no traffic, zero data).
+  const uint32_t code_col = (uint32_t)c * 16u, scale_col = (uint32_t)(c >> 1) * 2u;
+  auto load_batch = [&](Batch& bt, int b) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int row = row0 + (2 * b + i) * kRowsPerInstr;
-      const uint32_t code_off = __umul24((uint32_t)row, (uint32_t)job.stride) + (uint32_t)c * 16u;
-      const uint32_t scale_off = (__umul24((uint32_t)row, (uint32_t)groups) + (uint32_t)(c >> 1)) * 2u;
+      const uint32_t row = (uint32_t)(row0 + (2 * b + i) * kRowsPerInstr);
+      const uint32_t code_off = __umul24(row, (uint32_t)job.stride) + code_col;
+      const uint32_t scale_off = __umul24(row, (uint32_t)groups) * 2u + scale_col;
       bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               code_rsrc, live ? (int)code_off : kOobOffset, 0, kStreamAux));
-      bt.s[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, live ? (int)scale_off : kOobOffset, 0, 0);
+                                               code_rsrc, lane_live ? (int)code_off : kOobOffset, 0, kStreamAux));
+      bt.s[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, lane_live ? (int)scale_off : kOobOffset, 0, 0);
     }
   };
-
-  // Activation loads go out first: vector-memory waits retire in issue order, so staging them
-  // then waits only for these and overlaps the weight loads issued next. Reads past K return zero.
-  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)job.x, 0, k * 2, kRsrcWord3);
-  auto load_x = [&](uint32_t (&w)[32], int c) {
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, c * 128 + 16 * v, 0, 0));
-      w[4 * v + 0] = q.x;
-      w[4 * v + 1] = q.y;
-      w[4 * v + 2] = q.z;
-      w[4 * v + 3] = q.w;
-    }
-  };
-  // pairs and all-zero-row product of chunk c into LDS
-  auto stage = [&](const uint32_t (&w)[32], int c) {
-    uint32_t p[32];
-    build_pairs_slot2(w, p);
-    lds_ref[c] = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) lds_pairs[g * cpad + c] = make_uint4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
-  };
-  uint32_t xw[32];
-  load_x(xw, tid);
-  __builtin_amdgcn_sched_barrier(0);  // keep the issue order
-
   Batch ring[kRing];
 #pragma unroll
-  for (int b = 0; b < kRing - 1; ++b) load_batch(ring[b], b);
+  for (int u = 0; u < kRing; ++u) load_batch(ring[u], u);
+  __builtin_amdgcn_sched_barrier(0);  // every load is out before anything waits
 
-  // stage every chunk of the row once (one per thread up to K = 16384)
-  if (tid < cpad) stage(xw, tid);
-  for (int c = tid + 256; c < cpad; c += 256) {
-    load_x(xw, c);
-    stage(xw, c);
-  }
-  if (slices > 1)
-    for (int r = tid; r < 4 * R * kRowsPerInstr; r += 256) lds_acc[r] = 0.f;
-  __syncthreads();
-
+  // 2. dot2 pairs and the all-zero-row product of this lane's chunk
   uint32_t xp[32];
-  float ref = 0.f;
-  bool chunk_ok = false;
-  for (int base = 0; base < total_batches; base += kRing) {
-#pragma unroll
-    for (int u = 0; u < kRing; ++u) {
-      const int idx = base + u;
-      const bool live = idx < total_batches;
-      load_batch(ring[(u + kRing - 1) % kRing], idx + kRing - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      const int b = idx & (batches_per_slice - 1);
-      if (b == 0 && live) {  // a new K slice: this lane's pairs (conflict-free 16-byte LDS reads)
-        const int c = (idx >> log2_batches_per_slice) * S + cl;
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          const uint4 q = lds_pairs[g * cpad + c];
-          xp[4 * g + 0] = q.x;
-          xp[4 * g + 1] = q.y;
-          xp[4 * g + 2] = q.z;
-          xp[4 * g + 3] = q.w;
-        }
-        ref = lds_ref[c];
-        chunk_ok = c < chunks;
-      }
-      const Batch& cur = ring[u];
-      const float s0 = chunk_ok ? f16_to_f32((uint16_t)cur.s[0]) : 0.f;
-      const float s1 = chunk_ok ? f16_to_f32((uint16_t)cur.s[1]) : 0.f;
-      const float v0 = s0 * (chunk_dot_slot2(cur.cw[0], xp) - ref);
-      const float v1 = s1 * (chunk_dot_slot2(cur.cw[1], xp) - ref);
-      int slot;
-      const float sum = reduce_pair<S>(v0, v1, lane, slot);
-      // one writer per row: the first lane of each (row group, slot)
-      constexpr int kSlotLanes = S == 64 ? 32 : (S == 32 ? 16 : 8);
-      if (live && (lane & (kSlotLanes - 1)) == 0) {
-        const int local = wave * R * kRowsPerInstr + (2 * b + slot) * kRowsPerInstr + rslot;
+  build_pairs_slot2(xw, xp);
+  const float ref = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), xp);
+
+  constexpr int kSlotLanes = S == 64 ? 32 : (S == 32 ? 16 : 8);
+  const bool writer = (lane & (kSlotLanes - 1)) == 0;
+  auto consume = [&](const Batch& cur, int b) {
+    const float v0 = f16_to_f32((uint16_t)cur.s[0]) * (chunk_dot_slot2(cur.cw[0], xp) - ref);
+    const float v1 = f16_to_f32((uint16_t)cur.s[1]) * (chunk_dot_slot2(cur.cw[1], xp) - ref);
+    int slot;
+    const float sum = reduce_pair<S>(v0, v1, lane, slot);
+    if (writer) {
+      const int local = (2 * b + slot) * kRowsPerInstr + rslot;  // one writer per (row, slice)
+      if (slices == 1) {
         const int row = block_row0 + local;
-        if (slices == 1) {
-          if (row < n) job.y[row] = sum * 1048576.0f;
-        } else {
-          lds_acc[local] += sum;
-        }
+        if (row < n) job.y[row] = sum * 1048576.0f;
+      } else {
+        lds_acc[ks * rows_wg + local] = sum;
       }
     }
+  };
+  // 3. groups of four batches; the next group's loads reuse the slots as they are freed
+  const int groups_of_4 = batches >> 2;
+  for (int g = 0; g + 1 < groups_of_4; ++g) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      consume(ring[u], 4 * g + u);
+      load_batch(ring[u], 4 * (g + 1) + u);
+    }
   }
+#pragma unroll
+  for (int u = 0; u < kRing; ++u) consume(ring[u], 4 * (groups_of_4 - 1) + u);
+
+  // 4. rows spanning several slices: add the slice sums in slice order
   if (slices > 1) {
-    // each row's slice sums were added by one lane of this wave; LDS ops of a wave are in order
-    for (int r = lane; r < R * kRowsPerInstr; r += 64) {
-      const int local = wave * R * kRowsPerInstr + r;
-      const int row = block_row0 + local;
-      if (row < n) job.y[row] = lds_acc[local] * 1048576.0f;
+    __syncthreads();
+    for (int r = threadIdx.x; r < rows_wg; r += (int)blockDim.x) {
+      float acc = 0.f;
+      for (int q = 0; q < slices; ++q) acc += lds_acc[q * rows_wg + r];
+      const int row = block_row0 + r;
+      if (row < n) job.y[row] = acc * 1048576.0f;
     }
   }
 }
 
 template <int S>
-hipError_t launch_stream(GemvArgs& args, int blocks, int rows_per_wave, int k_max, hipStream_t stream) {
-  int lbb = 0;
-  while ((1 << lbb) < rows_per_wave / 2) ++lbb;
-  const int chunks = k_max / 64;
-  const int cpad = (chunks + S - 1) / S * S;
-  const size_t lds = (size_t)cpad * (8 * 16 + 4) + (size_t)4 * rows_per_wave * (64 / S) * 4;
-  hipLaunchKernelGGL((gemv_stream_kernel<S>), dim3(blocks), dim3(256), lds, stream, args, rows_per_wave, lbb);
+hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
+  const size_t lds = slices > 1 ? (size_t)slices * rows_per_wave * (64 / S) * sizeof(float) : 0;
+  hipLaunchKernelGGL((gemv_wave_kernel<S>), dim3(blocks), dim3(64 * slices), lds, stream, args, rows_per_wave);
   return hipGetLastError();
 }
 
@@ -763,8 +727,19 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
   p.layout = layout;
   p.m = (int32_t)m;
   p.rotated = rotated;
-  // lanes per row: the width in {16, 32, 64} that wastes the fewest chunk slots (ties: wider)
+  p.slices = 0;
   const int chunks = chunks_per_row(layout, (int)k);
+  // the single-token kernel: one wave per K slice of 64 chunks, up to 16 waves per workgroup
+  p.stream = (layout == TGS_LAYOUT_SLOT2 && m == 1 && !rotated && k <= kMaxWaveKernelK) ? 1 : 0;
+  if (p.stream) {
+    // rows shorter than one full slice: 32 or 16 lanes per row, several rows per instruction
+    p.lanes = chunks > 32 ? 64 : (chunks > 16 ? 32 : 16);
+    p.slices = (chunks + p.lanes - 1) / p.lanes;
+    p.iter = 8;
+    p.rows_per_block = 8 * (64 / p.lanes);
+    return p;
+  }
+  // lanes per row: the width in {16, 32, 64} that wastes the fewest chunk slots (ties: wider)
   int best = 64, best_waste = 1 << 30;
   for (int s : {64, 32, 16}) {
     int waste = (chunks + s - 1) / s * s - chunks;
@@ -774,9 +749,6 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
     }
   }
   p.lanes = best;
-  // the streaming kernel stages activation pairs for the whole row in LDS (132 bytes per 64
-  // weights of K): used up to K = 28672, which keeps it under 64 KB per workgroup
-  p.stream = (layout == TGS_LAYOUT_SLOT2 && m == 1 && !rotated && k <= 28672) ? 1 : 0;
   const int mt = tokens_per_pass(layout, m);
   p.iter = mt == 1 ? 4 : (mt == 2 ? 2 : 1);
   p.rows_per_block = 4 * p.iter * (64 / best);  // 4 waves per workgroup at these sizes
@@ -785,13 +757,14 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
 
 void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
   if (p.stream) {
-    // rows per wave: as many as keep >= 2048 workgroups (8 per CU), between 8 and 64. Fewer than 8
-    // rows per wave measured slower: each workgroup stages the whole activation row first.
+    // rows per wave: as many (8..64) as still give kWaveKernelTargetWaves waves in all. Small
+    // launches get 8 rows per wave, which puts every load of a wave in flight at once.
     const int64_t rows_per_instr = 64 / p.lanes;
     int r = 64;
-    while (r > 8 && (total_rows + 4 * r * rows_per_instr - 1) / (4 * r * rows_per_instr) < 2048) r /= 2;
+    while (r > 8 && (total_rows + r * rows_per_instr - 1) / (r * rows_per_instr) * p.slices < kWaveKernelTargetWaves)
+      r /= 2;
     p.iter = r;
-    p.rows_per_block = (int32_t)(4 * r * rows_per_instr);
+    p.rows_per_block = (int32_t)(r * rows_per_instr);
     return;
   }
   // single-token slot-2 launches with plenty of rows: twice the rows per workgroup (8 rows per lane
@@ -806,12 +779,10 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
 
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream) {
   if (plan.stream) {
-    int k_max = 0;
-    for (int i = 0; i < args.count; ++i) k_max = args.job[i].k > k_max ? args.job[i].k : k_max;
     switch (plan.lanes) {
-      case 16: return launch_stream<16>(args, blocks, plan.iter, k_max, stream);
-      case 32: return launch_stream<32>(args, blocks, plan.iter, k_max, stream);
-      default: return launch_stream<64>(args, blocks, plan.iter, k_max, stream);
+      case 16: return launch_wave<16>(args, blocks, plan.iter, plan.slices, stream);
+      case 32: return launch_wave<32>(args, blocks, plan.iter, plan.slices, stream);
+      default: return launch_wave<64>(args, blocks, plan.iter, plan.slices, stream);
     }
   }
   const int mt = tokens_per_pass(plan.layout, plan.m);

@@ -260,7 +260,7 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
     if (!aligned(ys[i], 4)) return fail(TGS_E_ALIGN, "y must be 4-byte aligned");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // one launch per distinct plan (layout, lanes per row, basis), in call order
+  // one launch per distinct plan (layout, lanes per row, basis, kernel, K slices), in call order
   std::vector<char> done((size_t)count, 0);
   for (int32_t i = 0; i < count; ++i) {
     if (done[(size_t)i]) continue;
@@ -271,7 +271,8 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
     for (int32_t j = i; j < count; ++j) {
       if (done[(size_t)j]) continue;
       const tgs::GemvPlan pj = tgs::gemv_plan(ws[j].layout, ws[j].k, m, ws[j].rotated);
-      if (pj.layout != plan.layout || pj.lanes != plan.lanes || pj.rotated != plan.rotated || pj.stream != plan.stream)
+      if (pj.layout != plan.layout || pj.lanes != plan.lanes || pj.rotated != plan.rotated ||
+          pj.stream != plan.stream || pj.slices != plan.slices)
         continue;
       members.push_back(j);
       total_rows += ws[j].n;

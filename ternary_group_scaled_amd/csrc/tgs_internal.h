@@ -13,6 +13,10 @@ constexpr int kMaxJobs = TGS_MAX_BATCH;
 // park loads they do not need at kOobOffset, which must lie past every valid range.
 constexpr int64_t kMaxDeviceCodeBytes = (1LL << 31) - (1LL << 20);
 constexpr int kOobOffset = 0x7FFFFFF0;
+// The single-token kernel runs one wave per 4096 weights of K, at most 16 per workgroup.
+constexpr int kMaxWaveKernelK = 16 * 4096;
+// and aims for at least this many waves per launch when choosing rows per wave
+constexpr int kWaveKernelTargetWaves = 4096;
 
 // One matrix of a batched GEMV launch. All pointers are device pointers.
 struct GemvJob {
@@ -40,7 +44,8 @@ struct GemvPlan {
   int32_t lanes;      // lanes per row (16, 32 or 64)
   int32_t m;          // activation rows
   int32_t rotated;    // 0 or 1
-  int32_t stream;     // 1: the streaming single-token kernel (slot-2, plain basis)
+  int32_t stream;     // 1: the single-token kernel (slot-2, plain basis, m = 1)
+  int32_t slices;     // single-token kernel: K slices of 64 chunks = waves per workgroup
   int32_t iter;       // rows per lane slot
   int32_t rows_per_block;
 };
