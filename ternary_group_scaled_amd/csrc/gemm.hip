@@ -201,9 +201,222 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
     }
 }
 
+// ---- skinny product: up to 32 activation rows, slot-2 codes ----------------------------------
+//
+// With few activation rows the tile kernel above has too few workgroups (n / 128) to fill the
+// chip, and its LDS round trips sit on the critical path. Here a workgroup of W waves owns
+// 16 * FB outputs and 16 * TB activation rows, and splits K across its waves: wave w takes
+// scale groups [w * G / W, (w + 1) * G / W). Every wave builds its MFMA operands in
+// registers: x fragments straight from memory, weights decoded from 8 bytes of codes per lane
+// per group. Within each 16 consecutive k, both operands use the order 0,8,1,9,...,7,15 of the
+// slot-2 decode, so the contraction is unchanged. Each group's partial is scaled in fp32; the W
+// per-wave results are added through LDS in wave order (deterministic, no atomics).
+// Every workgroup reads all of x for its outputs, so x traffic from L2 falls as FB grows: the
+// few-row case uses FB = 4 and keeps the kernel within 128 VGPRs (two stages), so that 16 waves
+// fit on a CU, rather than shrinking FB to get more workgroups.
+
+// pairs 4H..4H+3 of decode16_slot2(u): bf16(2t_i) in the low half, bf16(2t_{i+8}) in the high half
+template <int H>
+__device__ __forceinline__ uint4 decode4_slot2(uint32_t u) {
+  constexpr uint32_t kTable = 0x004000C0u;
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * H + j;  // shift left by 8 - 2i (negative: right)
+    const uint32_t v = i <= 4 ? (u << (8 - 2 * i)) : (u >> (2 * i - 8));
+    o[j] = __builtin_amdgcn_perm(0u, kTable, (v & 0x03000300u) | 0x000C000Cu);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// pairs 4H..4H+3 of interleave16 over 16 consecutive bf16 values in w[0..7]
+template <int H>
+__device__ __forceinline__ uint4 interleave4(const uint32_t* w) {
+  if constexpr (H == 0)
+    return make_uint4(pair16<0, 8>(w), pair16<1, 9>(w), pair16<2, 10>(w), pair16<3, 11>(w));
+  else
+    return make_uint4(pair16<4, 12>(w), pair16<5, 13>(w), pair16<6, 14>(w), pair16<7, 15>(w));
+}
+
+template <int TB, int kFB, int kWaves, int kStages>
+__global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t* __restrict__ codes, int64_t stride,
+                                                          const uint16_t* __restrict__ scales, int n, int k,
+                                                          const uint16_t* __restrict__ x, int m,
+                                                          float* __restrict__ y) {
+  // kFB: 16-output blocks per workgroup; kWaves: K slices (waves) per workgroup; kStages: groups
+  // of loads in flight per wave
+  __shared__ float red[kWaves][TB * kFB * 4][64];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fr = lane & 15, kq = lane >> 4;  // fragment row and k quarter
+  const int n_base = blockIdx.x * 16 * kFB, m_base = blockIdx.y * 16 * TB;
+  const int groups = k / 128;
+  const int g_begin = wave * groups / kWaves, g_end = (wave + 1) * groups / kWaves;
+
+  // reads past each buffer (rows >= n, activation rows >= m) return zero
+  const __amdgpu_buffer_rsrc_t code_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)codes, 0, (int)((int64_t)n * stride), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t scale_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)((int64_t)m * k * 2), kRsrcWord3);
+
+  // per lane: output row (feature) n_base + 16 fb + fr reads 8 bytes of codes per group at 8 * kq;
+  // activation row m_base + 16 tb + fr reads 32 values per group at 32 * kq
+  // Rows past n and activation rows past m land beyond their buffer and read as zero. The
+  // offsets are unsigned: n * stride <= 2^31 - 2^20 and 64 rows more add at most 2^30, and m <= 32,
+  // so none wraps around.
+  uint32_t code_off[kFB], scale_off[kFB], x_off[TB];
+#pragma unroll
+  for (int fb = 0; fb < kFB; ++fb) {
+    const uint32_t row = (uint32_t)(n_base + 16 * fb + fr);
+    code_off[fb] = row * (uint32_t)stride + 8u * (uint32_t)kq;
+    scale_off[fb] = row * (uint32_t)groups * 2u;
+  }
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const uint32_t row = (uint32_t)(m_base + 16 * tb + fr);
+    x_off[tb] = (row * (uint32_t)k + 32u * (uint32_t)kq) * 2u;
+  }
+
+  struct Stage {
+    uint32_t cw[kFB][2];
+    uint32_t sc[kFB];
+    uint32_t xv[TB][16];
+  };
+  // Every workgroup reads the same activations; if all started at the same group, hundreds of CUs
+  // would request the same few L2 lines at once. Each workgroup walks its waves' groups in a
+  // rotated order instead: its i-th group is g_begin + (i + rot) mod count.
+  const int count = g_end - g_begin;
+  const int rot = count > 0 ? (int)(blockIdx.x % (unsigned)count) : 0;
+  auto load = [&](Stage& st, int i) {
+    const bool live = i < count;
+    int g = g_begin + i + rot;
+    if (g >= g_end) g -= count;
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) {
+      const int off = live ? (int)(code_off[fb] + 32u * (uint32_t)g) : kOobOffset;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, off, 0, 0);
+      st.cw[fb][0] = v[0];
+      st.cw[fb][1] = v[1];
+      st.sc[fb] = __builtin_amdgcn_raw_buffer_load_b16(
+          scale_rsrc, live ? (int)(scale_off[fb] + 2u * (uint32_t)g) : kOobOffset, 0, 0);
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int off = live ? (int)(x_off[tb] + 256u * (uint32_t)g + 16u * (uint32_t)v) : kOobOffset;
+        const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, off, 0, 0));
+        st.xv[tb][4 * v + 0] = q.x;
+        st.xv[tb][4 * v + 1] = q.y;
+        st.xv[tb][4 * v + 2] = q.z;
+        st.xv[tb][4 * v + 3] = q.w;
+      }
+  };
+
+  f32x4 acc[TB][kFB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) acc[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage& st) {
+    f32x4 part[TB][kFB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int fb = 0; fb < kFB; ++fb) part[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {  // 32 k per step: this lane's k quarter holds 8 of them
+      bf16x8 a[TB], b[kFB];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        a[tb] = __builtin_bit_cast(bf16x8, (s & 1) ? interleave4<1>(st.xv[tb] + 8 * (s >> 1))
+                                                   : interleave4<0>(st.xv[tb] + 8 * (s >> 1)));
+#pragma unroll
+      for (int fb = 0; fb < kFB; ++fb)
+        b[fb] = __builtin_bit_cast(bf16x8, (s & 1) ? decode4_slot2<1>(st.cw[fb][s >> 1])
+                                                   : decode4_slot2<0>(st.cw[fb][s >> 1]));
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int fb = 0; fb < kFB; ++fb)
+          part[tb][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], b[fb], part[tb][fb], 0, 0, 0);
+    }
+    // D[i][j] (activation row i, output j) sits in lane 16 * (i / 4) + j, register i % 4
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) {
+      const float sc = 0.5f * f16_to_f32((uint16_t)st.sc[fb]);  // the weights were decoded as 2t
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[tb][fb][r] = fmaf(sc, part[tb][fb][r], acc[tb][fb][r]);
+    }
+  };
+
+  // kStages groups of loads in flight; a stage is reloaded as soon as it has been multiplied
+  // (loads past the wave's last group are parked out of range, so every load is unconditional
+  // and the compiler's wait counts stay exact)
+  Stage st[kStages];
+#pragma unroll
+  for (int u = 0; u < kStages; ++u) load(st[u], u);
+  for (int base = 0; base < count; base += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      if (base + u < count) compute(st[u]);
+      load(st[u], base + u + kStages);
+    }
+  }
+
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(tb * kFB + fb) * 4 + r][lane] = acc[tb][fb][r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < TB * kFB * 4 * 64; e += kWaves * 64) {
+    const int idx = e >> 6, ln = e & 63;
+    const int tb = idx / (kFB * 4), fb = (idx / 4) % kFB, r = idx % 4;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += red[w][idx][ln];
+    const int row = m_base + 16 * tb + 4 * (ln >> 4) + r, col = n_base + 16 * fb + (ln & 15);
+    if (row < m && col < n) y[(int64_t)row * n + col] = sum;
+  }
+}
+
 template <int LAYOUT>
 hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
                          const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
+  if (LAYOUT == TGS_LAYOUT_SLOT2 && m <= 32) {
+    const int ni = (int)n, ki = (int)k, mi = (int)m;
+    if (m <= 16) {
+      // 64 outputs per workgroup; 16 K slices when that gives too few workgroups to fill the chip
+      const dim3 grid((unsigned)((n + 63) / 64));
+      if ((n + 63) / 64 >= 256)
+        hipLaunchKernelGGL((gemm_skinny_kernel<1, 4, 8, 2>), grid, dim3(512), 0, stream, codes, stride, scales, ni,
+                           ki, x, mi, y);
+      else
+        hipLaunchKernelGGL((gemm_skinny_kernel<1, 4, 16, 2>), grid, dim3(1024), 0, stream, codes, stride, scales, ni,
+                           ki, x, mi, y);
+    } else {
+      // 16 outputs per block: the most (4, 2, 1) that still gives 512 workgroups
+      const int64_t fb = (n + 63) / 64 >= 512 ? 4 : ((n + 31) / 32 >= 512 ? 2 : 1);
+      const dim3 grid((unsigned)((n + 16 * fb - 1) / (16 * fb)), (unsigned)((m + 31) / 32));
+      if (fb == 4)
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 8, 3>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
+                           x, mi, y);
+      else if (fb == 2)
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, 2, 8, 3>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
+                           x, mi, y);
+      else
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, 1, 8, 3>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
+                           x, mi, y);
+    }
+    return hipGetLastError();
+  }
   const unsigned gx = (unsigned)((n + kBN - 1) / kBN);
   if (m <= 16) {
     hipLaunchKernelGGL((gemm_kernel<LAYOUT, 16>), dim3(gx, (unsigned)((m + 15) / 16)), dim3(kThreads), 0, stream,

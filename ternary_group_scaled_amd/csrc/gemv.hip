@@ -59,10 +59,6 @@ template <int ITER>
 constexpr int waves_for() {
   return 4;
 }
-// cache policy of the weight stream: non-temporal (read once, no reuse)
-constexpr int kStreamAux = 2;
-// word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format, no swizzle)
-constexpr int kRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
@@ -549,11 +545,11 @@ __device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& 
   }
 }
 
-template <int S>
+template <int S, int G>
 __global__ __launch_bounds__(1024)
 void gemv_wave_kernel(const GemvArgs args, int rows_per_wave) {
   constexpr int kRowsPerInstr = 64 / S;
-  constexpr int kRing = 4;
+  constexpr int kRing = G;  // batches per group: 4, or 1-2 for waves of 2-4 rows
   extern __shared__ float lds_acc[];  // [slices][rows of the workgroup], only when slices > 1
 
   int j = 0;
@@ -563,7 +559,7 @@ void gemv_wave_kernel(const GemvArgs args, int rows_per_wave) {
   const int groups = k / 128;
   const int chunks = k / 64;
   const int slices = (chunks + S - 1) / S;  // == waves per workgroup
-  const int R = rows_per_wave;              // row slots per wave: 8, 16, 32 or 64
+  const int R = rows_per_wave;              // row slots per wave: 2 * G * (number of groups)
   const int batches = R / 2;
   const int rows_wg = R * kRowsPerInstr;
 
@@ -637,17 +633,17 @@ void gemv_wave_kernel(const GemvArgs args, int rows_per_wave) {
       }
     }
   };
-  // 3. groups of four batches; the next group's loads reuse the slots as they are freed
-  const int groups_of_4 = batches >> 2;
-  for (int g = 0; g + 1 < groups_of_4; ++g) {
+  // 3. groups of G batches; the next group's loads reuse the slots as they are freed
+  const int n_groups = batches / kRing;
+  for (int g = 0; g + 1 < n_groups; ++g) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
-      consume(ring[u], 4 * g + u);
-      load_batch(ring[u], 4 * (g + 1) + u);
+      consume(ring[u], kRing * g + u);
+      load_batch(ring[u], kRing * (g + 1) + u);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kRing; ++u) consume(ring[u], 4 * (groups_of_4 - 1) + u);
+  for (int u = 0; u < kRing; ++u) consume(ring[u], kRing * (n_groups - 1) + u);
 
   // 4. rows spanning several slices: add the slice sums in slice order
   if (slices > 1) {
@@ -664,7 +660,12 @@ void gemv_wave_kernel(const GemvArgs args, int rows_per_wave) {
 template <int S>
 hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
   const size_t lds = slices > 1 ? (size_t)slices * rows_per_wave * (64 / S) * sizeof(float) : 0;
-  hipLaunchKernelGGL((gemv_wave_kernel<S>), dim3(blocks), dim3(64 * slices), lds, stream, args, rows_per_wave);
+  if (rows_per_wave >= 8)
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 4>), dim3(blocks), dim3(64 * slices), lds, stream, args, rows_per_wave);
+  else if (rows_per_wave == 4)
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 2>), dim3(blocks), dim3(64 * slices), lds, stream, args, rows_per_wave);
+  else
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 1>), dim3(blocks), dim3(64 * slices), lds, stream, args, rows_per_wave);
   return hipGetLastError();
 }
 

@@ -13,6 +13,11 @@ constexpr int kMaxJobs = TGS_MAX_BATCH;
 // park loads they do not need at kOobOffset, which must lie past every valid range.
 constexpr int64_t kMaxDeviceCodeBytes = (1LL << 31) - (1LL << 20);
 constexpr int kOobOffset = 0x7FFFFFF0;
+// cache policy of a weight stream read once: non-temporal
+constexpr int kStreamAux = 2;
+// word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format, no swizzle); reads
+// past the resource's size return zero
+constexpr int kRsrcWord3 = 0x00020000;
 // The single-token kernel runs one wave per 4096 weights of K, at most 16 per workgroup.
 constexpr int kMaxWaveKernelK = 16 * 4096;
 // and aims for at least this many waves per launch when choosing rows per wave

@@ -200,14 +200,39 @@ def _gemm(layout, t, s, xbits):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
-@pytest.mark.parametrize("n,k", [(128, 128), (300, 1024), (129, 2048), (64, 640)])
-@pytest.mark.parametrize("m", [1, 16, 50, 128, 200])
+@pytest.mark.parametrize("n,k", [(128, 128), (300, 1024), (129, 2048), (64, 640), (70, 4352)])
+@pytest.mark.parametrize("m", [1, 8, 16, 24, 32, 50, 128, 200])
 def test_gemm_matches_oracle(layout, n, k, m):
     t, s = make_weights(n + k + m, f"gemm{layout}", n, k, 0.4)
     xb = make_x_bf16_bits(m, f"gemm{n}", m, k)
     y = _gemm(layout, t, s, xb)
     y_ref, bound = oracle_product(layout, t, s, xb, oracle.X_BF16)
     assert_within_bound(y, y_ref, bound, f"gemm {LNAME[layout]} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("n", [17000, 33000])
+@pytest.mark.parametrize("m", [5, 20])
+def test_gemm_wide_matrices(n, m):
+    """Wide matrices take the few-row product with 2 or 4 output blocks per workgroup."""
+    k = 384
+    t, s = make_weights(n + m, "gemmwide", n, k, 0.4)
+    xb = make_x_bf16_bits(m, f"gemmwide{n}", m, k)
+    y = _gemm(tgs.SLOT2, t, s, xb)
+    y_ref, bound = oracle_product(tgs.SLOT2, t, s, xb, oracle.X_BF16)
+    assert_within_bound(y, y_ref, bound, f"gemm wide {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 20, 40])
+def test_gemm_integer_inputs_are_exact(m):
+    """Integer activations and power-of-two scales: every partial sum is exact in fp32, so each
+    GEMM path (skinny and tiled) must equal the oracle bit for bit."""
+    n, k = 200, 2304
+    t, _ = make_weights(11 + m, "gemmexactm", n, k, 0.4)
+    s = np.ldexp(1.0, synth.trits(11, 7, (n, k // 128), 0.0).astype(np.int64)).astype(np.float16)
+    xi = (synth.trits(11 + m, 8, (m, k), 0.2).astype(np.int64) * 3).astype(np.float32)
+    y_gemm = _gemm(tgs.SLOT2, t, s, synth.bf16_bits(xi))
+    y_ref, _ = oracle_product(tgs.SLOT2, t, s, synth.bf16_bits(xi), oracle.X_BF16)
+    assert (y_gemm.astype(np.float64) == y_ref).all()
 
 
 def test_gemm_integer_inputs_are_exact_and_match_gemv():
