@@ -6,16 +6,22 @@
 // processing (section "Low-bit kernels for hybrid attention"); the format is the page's
 // "Group-scaled ternary format" (w = s_g * t, one fp16 scale per 128 weights along K).
 //
-// Tiling. A workgroup computes a BM x 128 tile of y and walks K one scale group (128) at a time:
-//   1. the activation tile [BM][128] is copied into LDS;
-//   2. the weight tile [128][128] is decoded from packed codes straight into LDS as bf16 values
+// Tiled product (any number of activation rows). A workgroup of 4 waves (2 x 2) computes a
+// BM x BN tile of y and walks K one scale group (128) at a time, with the next group's data in
+// flight while the current one is multiplied:
+//   1. each thread's share of group g + 1 is loaded into registers: activation units of 16 k
+//      values, and 16 bytes (64 codes) of one weight row;
+//   2. meanwhile v_mfma_f32_16x16x32_bf16 runs over group g from LDS, and the group's partial is
+//      scaled by 0.5 * s[n][g] in fp32 and added to the running sum (the scale never enters a
+//      bf16 operand: rounding s to bf16 would cost 2^-9 relative);
+//   3. after a barrier the registers go to LDS: activations reordered, weights decoded to bf16
 //      2t in {-2, 0, +2} (exact; the factor 2 keeps the low byte of every bf16 zero, so one
-//      v_perm table lookup makes two weights);
-//   3. v_mfma_f32_16x16x32_bf16 accumulates the group's partial product in fp32;
-//   4. the partial is scaled by 0.5 * s[n][g] in fp32 and added to the running sum.
-// Step 4 keeps the scale out of the bf16 operands: rounding s to bf16 would cost 2^-9 relative.
+//      v_perm table lookup makes two weights).
 // Within every 16 consecutive k, both tiles are stored in the order 0,8,1,9,...,7,15 (the order
 // the slot-2 decode produces pairs in); the contraction over k does not depend on that order.
+// Up to 32 activation rows take the skinny kernel further below instead.
+#include <algorithm>
+
 #include "tgs_internal.h"
 
 namespace tgs {
@@ -25,7 +31,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kBN = 128;
 constexpr int kBK = 128;
 constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 elements (16 bytes of padding)
 
@@ -73,71 +78,79 @@ __device__ __forceinline__ uint16_t bf16_of_2t_digit(uint32_t digit) {
   return digit == 0 ? 0xC000u : (digit == 2 ? 0x4000u : 0u);
 }
 
-template <int LAYOUT, int BM>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restrict__ codes, int64_t stride,
-                                                        const uint16_t* __restrict__ scales, int n, int k,
-                                                        const uint16_t* __restrict__ x, int m,
-                                                        float* __restrict__ y) {
-  constexpr int kWavesN = (BM >= 64) ? 2 : 4;
-  constexpr int kWavesM = 4 / kWavesN;
-  constexpr int kWM = BM / kWavesM;       // rows of y per wave
-  constexpr int kWN = kBN / kWavesN;      // columns of y per wave
+template <int LAYOUT, int BM, int BN>
+__global__ __launch_bounds__(kThreads) void gemm_tile_kernel(const uint8_t* __restrict__ codes, int64_t stride,
+                                                             const uint16_t* __restrict__ scales, int n, int k,
+                                                             const uint16_t* __restrict__ x, int m,
+                                                             float* __restrict__ y) {
+  constexpr int kWM = BM / 2, kWN = BN / 2;  // tile of one wave
   constexpr int kBlkM = kWM / 16, kBlkN = kWN / 16;
+  constexpr int kXUnits = BM * 8 / kThreads;  // 16-value activation units per thread and group
+  constexpr int kCodeThreads = BN * 2;        // threads that each hold 64 codes of one row
 
   __shared__ __attribute__((aligned(16))) uint16_t xs[BM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[kBN * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[BN * kPitch];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / kWavesN, wn = wave % kWavesN;
-  const int n_base = blockIdx.x * kBN, m_base = blockIdx.y * BM;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_base = blockIdx.x * BN, m_base = blockIdx.y * BM;
   const int groups = k / 128;
 
-  f32x4 acc[kBlkM][kBlkN];
-#pragma unroll
-  for (int a = 0; a < kBlkM; ++a)
-#pragma unroll
-    for (int b = 0; b < kBlkN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Rows past m (activations) and past n (codes, scales) land beyond their buffers and read as
+  // zero; they only feed outputs that are never stored. Offsets are unsigned: the host keeps
+  // m * k * 2 and n * stride below 2^31, and one tile more stays below 2^32.
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, (int)((int64_t)m * k * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t code_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)codes, 0, (int)((int64_t)n * stride), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t scale_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
 
-  for (int g = 0; g < groups; ++g) {
-    const int k0 = g * 128;
-    __syncthreads();
-    // 1. activations [BM][128] -> LDS, 16 k values per unit
-    for (int u = tid; u < BM * 8; u += kThreads) {
-      const int r = u >> 3, c16 = (u & 7) * 16;
-      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (m_base + r < m) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)(m_base + r) * k + k0 + c16);
-        uint4 a = src[0], b = src[1];
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-      }
+  uint32_t xr[kXUnits][8];
+  uint4 cr = make_uint4(0, 0, 0, 0);
+  auto load_stage = [&](int g) {
+#pragma unroll
+    for (int u = 0; u < kXUnits; ++u) {
+      const int unit = tid + u * kThreads, r = unit >> 3, c16 = (unit & 7) * 16;
+      const uint32_t off = ((uint32_t)(m_base + r) * (uint32_t)k + (uint32_t)(g * 128 + c16)) * 2u;
+      const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (int)off, 0, 0));
+      const uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (int)off + 16, 0, 0));
+      xr[u][0] = a.x; xr[u][1] = a.y; xr[u][2] = a.z; xr[u][3] = a.w;
+      xr[u][4] = b.x; xr[u][5] = b.y; xr[u][6] = b.z; xr[u][7] = b.w;
+    }
+    if (LAYOUT == TGS_LAYOUT_SLOT2 && tid < kCodeThreads) {
+      const uint32_t off = (uint32_t)(n_base + (tid >> 1)) * (uint32_t)stride + (uint32_t)(g * 32 + 16 * (tid & 1));
+      cr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)off, 0, kStreamAux));
+    }
+  };
+  auto store_stage = [&](int g) {
+#pragma unroll
+    for (int u = 0; u < kXUnits; ++u) {
+      const int unit = tid + u * kThreads, r = unit >> 3, c16 = (unit & 7) * 16;
       uint32_t o[8];
-      interleave16(w, o);
+      interleave16(xr[u], o);
       uint4* dst = reinterpret_cast<uint4*>(xs + r * kPitch + c16);
       dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
       dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
-    // 2. weights [128][128] -> LDS as bf16(2t); each thread decodes 64 k values of one row
-    {
+    if (tid < kCodeThreads) {
       const int r = tid >> 1, h = tid & 1;
-      const int row = n_base + r;
       uint32_t out[32];
       if (LAYOUT == TGS_LAYOUT_SLOT2) {
-        uint4 cw = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);  // q = 1: t = 0
-        if (row < n) cw = *reinterpret_cast<const uint4*>(codes + (int64_t)row * stride + k0 / 4 + 16 * h);
-        decode16_slot2(cw.x, out + 0);
-        decode16_slot2(cw.y, out + 8);
-        decode16_slot2(cw.z, out + 16);
-        decode16_slot2(cw.w, out + 24);
+        decode16_slot2(cr.x, out + 0);
+        decode16_slot2(cr.y, out + 8);
+        decode16_slot2(cr.z, out + 16);
+        decode16_slot2(cr.w, out + 24);
       } else {
+        // base-3: digit by digit from the packed bytes (not on a measured path)
+        const int row = n_base + r;
         uint32_t w[32];
-        const int kk0 = k0 + 64 * h;
+        const int kk0 = g * 128 + 64 * h;
         for (int e = 0; e < 64; e += 2) {
           uint32_t lo = 0, hi = 0;
           if (row < n) {
             const uint8_t* rp = codes + (int64_t)row * stride;
-            uint32_t b0 = rp[(kk0 + e) / 5], b1 = rp[(kk0 + e + 1) / 5];
-            uint32_t d0 = b0, d1 = b1;
+            uint32_t d0 = rp[(kk0 + e) / 5], d1 = rp[(kk0 + e + 1) / 5];
             for (int j = 0; j < (kk0 + e) % 5; ++j) d0 /= 3;
             for (int j = 0; j < (kk0 + e + 1) % 5; ++j) d1 /= 3;
             lo = bf16_of_2t_digit(d0 % 3);
@@ -151,15 +164,33 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
 #pragma unroll
       for (int v = 0; v < 8; ++v) dst[v] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
     }
-    __syncthreads();
+  };
 
-    // 3. MFMA over the group, 4 steps of 32 k
+  f32x4 acc[kBlkM][kBlkN];
+#pragma unroll
+  for (int a = 0; a < kBlkM; ++a)
+#pragma unroll
+    for (int b = 0; b < kBlkN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int g = 0; g < groups; ++g) {
+    const bool more = g + 1 < groups;
+    if (more) load_stage(g + 1);
+    // this lane's output columns: their scales, loaded ahead of the MFMAs
+    uint32_t sraw[kBlkN];
+#pragma unroll
+    for (int b = 0; b < kBlkN; ++b) {
+      const uint32_t col = (uint32_t)(n_base + wn * kWN + 16 * b + fr);
+      sraw[b] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)((col * (uint32_t)groups + (uint32_t)g) * 2u), 0, 0);
+    }
     f32x4 part[kBlkM][kBlkN];
 #pragma unroll
     for (int a = 0; a < kBlkM; ++a)
 #pragma unroll
       for (int b = 0; b < kBlkN; ++b) part[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 af[kBlkM], bfr[kBlkN];
@@ -175,15 +206,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
         for (int b = 0; b < kBlkN; ++b)
           part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], part[a][b], 0, 0, 0);
     }
-    // 4. scale the group's partial by 0.5 * s[n][g] (the weights were decoded as 2t)
 #pragma unroll
     for (int b = 0; b < kBlkN; ++b) {
-      const int col = n_base + wn * kWN + 16 * b + fr;
-      const float sc = col < n ? 0.5f * f16_to_f32(scales[(int64_t)col * groups + g]) : 0.f;
+      const float sc = 0.5f * f16_to_f32((uint16_t)sraw[b]);  // the weights were decoded as 2t
 #pragma unroll
       for (int a = 0; a < kBlkM; ++a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[a][b][r] = fmaf(sc, part[a][b][r], acc[a][b][r]);
+    }
+    __syncthreads();
+    if (more) {
+      store_stage(g + 1);
+      __syncthreads();
     }
   }
 
@@ -417,17 +451,23 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
     }
     return hipGetLastError();
   }
-  const unsigned gx = (unsigned)((n + kBN - 1) / kBN);
-  if (m <= 16) {
-    hipLaunchKernelGGL((gemm_kernel<LAYOUT, 16>), dim3(gx, (unsigned)((m + 15) / 16)), dim3(kThreads), 0, stream,
-                       codes, stride, scales, (int)n, (int)k, x, (int)m, y);
-  } else if (m <= 64) {
-    hipLaunchKernelGGL((gemm_kernel<LAYOUT, 64>), dim3(gx, (unsigned)((m + 63) / 64)), dim3(kThreads), 0, stream,
-                       codes, stride, scales, (int)n, (int)k, x, (int)m, y);
-  } else {
-    hipLaunchKernelGGL((gemm_kernel<LAYOUT, 128>), dim3(gx, (unsigned)((m + 127) / 128)), dim3(kThreads), 0,
-                       stream, codes, stride, scales, (int)n, (int)k, x, (int)m, y);
-  }
+  // tiles: 128 x 128 for many activation rows, else 64 rows; 64 columns when 128 gives too few tiles
+  const int bm = m > 128 ? 128 : 64;
+  const int64_t m_tiles = (m + bm - 1) / bm;
+  const int bn = (n + 127) / 128 * m_tiles >= 512 ? 128 : 64;
+  const dim3 grid((unsigned)((n + bn - 1) / bn), (unsigned)m_tiles);
+  if (bm == 128 && bn == 128)
+    hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, 128, 128>), grid, dim3(kThreads), 0, stream, codes, stride, scales,
+                       (int)n, (int)k, x, (int)m, y);
+  else if (bm == 128)
+    hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, 128, 64>), grid, dim3(kThreads), 0, stream, codes, stride, scales,
+                       (int)n, (int)k, x, (int)m, y);
+  else if (bn == 128)
+    hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, 64, 128>), grid, dim3(kThreads), 0, stream, codes, stride, scales,
+                       (int)n, (int)k, x, (int)m, y);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, 64, 64>), grid, dim3(kThreads), 0, stream, codes, stride, scales,
+                       (int)n, (int)k, x, (int)m, y);
   return hipGetLastError();
 }
 
@@ -435,9 +475,17 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
 
 hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n,
                        int64_t k, const uint16_t* x_bf16, int64_t m, float* y, hipStream_t stream) {
-  if (layout == TGS_LAYOUT_SLOT2)
-    return launch_layout<TGS_LAYOUT_SLOT2>(codes, stride, scales, n, k, x_bf16, m, y, stream);
-  return launch_layout<TGS_LAYOUT_BASE3>(codes, stride, scales, n, k, x_bf16, m, y, stream);
+  // activation rows per launch: the kernels address x with 32-bit offsets (m * k * 2 < 2^31)
+  const int64_t max_rows = std::max<int64_t>(128, (kMaxDeviceCodeBytes / (2 * k)) / 128 * 128);
+  for (int64_t r0 = 0; r0 < m; r0 += max_rows) {
+    const int64_t mr = std::min(max_rows, m - r0);
+    const hipError_t e =
+        layout == TGS_LAYOUT_SLOT2
+            ? launch_layout<TGS_LAYOUT_SLOT2>(codes, stride, scales, n, k, x_bf16 + r0 * k, mr, y + r0 * n, stream)
+            : launch_layout<TGS_LAYOUT_BASE3>(codes, stride, scales, n, k, x_bf16 + r0 * k, mr, y + r0 * n, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tgs

@@ -222,6 +222,18 @@ def test_gemm_wide_matrices(n, m):
     assert_within_bound(y, y_ref, bound, f"gemm wide {n}x{k} m={m}")
 
 
+def test_gemm_large_tiles_sampled():
+    """Many rows and columns take 128 x 128 tiles; checked on sampled output columns."""
+    n, k, m = 8192, 256, 1040
+    t, s = make_weights(31, "gemmbig", n, k, 0.4)
+    xb = make_x_bf16_bits(31, "gemmbigx", m, k)
+    y = _gemm(tgs.SLOT2, t, s, xb)
+    cols = np.sort(np.random.default_rng(3).choice(n, size=96, replace=False))
+    cols[0], cols[-1] = 0, n - 1
+    y_ref, bound = oracle_product(tgs.SLOT2, t, s, xb, oracle.X_BF16, rows=cols)
+    assert_within_bound(y[:, cols], y_ref, bound, f"gemm {n}x{k} m={m} sampled")
+
+
 @pytest.mark.parametrize("m", [1, 20, 40])
 def test_gemm_integer_inputs_are_exact(m):
     """Integer activations and power-of-two scales: every partial sum is exact in fp32, so each
