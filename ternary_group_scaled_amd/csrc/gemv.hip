@@ -33,7 +33,9 @@
 // Base-3. Each byte holds five trits, byte = sum_j (t_j + 1) 3^j. A word is split into two
 // 16-bit lanes (bytes 0,2 and bytes 1,3); each digit is peeled off both lanes at once with
 // packed 16-bit integer ops (q = v * 171 >> 9 equals v / 3 for v < 256; digit = v - 3q) and
-// shifted to bits 4..5 of its lane, where it is again an exact fp16 subnormal fed to dot2. A
+// left in bits 0..1 of its lane, where it is again an exact fp16 subnormal fed to dot2 (at these
+// bits dot2 keeps fewer product bits, about 2^-17 relative: far inside the tolerance, and the
+// all-zero-row subtraction still cancels exactly, since it repeats the same operations). A
 // 16-byte chunk (80 trits) can straddle a 128-trit scale group, so each lane keeps two
 // accumulators with activation pairs masked by group. The all-zero row (byte 121 = five zero
 // trits) again supplies sum_k x.
@@ -166,7 +168,7 @@ __device__ __forceinline__ float chunk_dot_slot2(const uint4& cw, const uint32_t
   return fmaf(fmaf(a4, 0.25f, a3), 0.25f, a2);
 }
 
-// base-3: 2^-20 * sum_k (t_k + 1) x_k for the (up to) two scale groups of a chunk
+// base-3: 2^-24 * sum_k (t_k + 1) x_k for the (up to) two scale groups of a chunk
 __device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const uint32_t* p, float& out0, float& out1) {
   float a0 = 0.f, a1 = 0.f;
   const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
@@ -188,9 +190,9 @@ __device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const uint32_t*
         de = ve;
         dd = vo;
       }
-      // digit at bits 4..5: the fp16 subnormal digit * 2^-20
-      const uint32_t be = __builtin_bit_cast(uint32_t, de << (u16x2)4);
-      const uint32_t bo = __builtin_bit_cast(uint32_t, dd << (u16x2)4);
+      // digit at bits 0..1: the fp16 subnormal digit * 2^-24
+      const uint32_t be = __builtin_bit_cast(uint32_t, de);
+      const uint32_t bo = __builtin_bit_cast(uint32_t, dd);
       a0 = dot2(be, p[5 * d + j], a0);
       a1 = dot2(be, p[20 + 5 * d + j], a1);
       a0 = dot2(bo, p[40 + 5 * d + j], a0);
@@ -461,8 +463,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
 #pragma unroll
       for (int off = S / 2, cnt = kIter; off >= 1; off >>= 1, cnt = cnt > 1 ? cnt / 2 : 1)
         if (cnt <= 1) low_bits |= off;
-      // the chunk products carry a factor 2^-20, undone here (an exact power of two)
-      if ((cl & low_bits) == 0 && row < n && m0 + t < m) job.y[(int64_t)(m0 + t) * n + row] = v[0] * 1048576.0f;
+      // the chunk products carry a factor 2^-20 (slot-2) or 2^-24 (base-3), undone here exactly
+      constexpr float kUnscale = LAYOUT == TGS_LAYOUT_BASE3 ? 16777216.0f : 1048576.0f;
+      if ((cl & low_bits) == 0 && row < n && m0 + t < m) job.y[(int64_t)(m0 + t) * n + row] = v[0] * kUnscale;
     }
   }
 }
