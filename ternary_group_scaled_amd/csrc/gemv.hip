@@ -732,7 +732,17 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
   p.m = (int32_t)m;
   p.rotated = rotated;
   p.slices = 0;
+  p.mfma = 0;
   const int chunks = chunks_per_row(layout, (int)k);
+  // base-3 with several tokens: decode once, multiply all tokens on the matrix cores
+  if (layout == TGS_LAYOUT_BASE3 && m >= 2) {
+    p.mfma = 1;
+    p.stream = 0;
+    p.lanes = 64;
+    p.iter = 1;
+    p.rows_per_block = kMfmaGemvRows;
+    return p;
+  }
   // the single-token kernel: one wave per K slice of 64 chunks, up to 16 waves per workgroup
   p.stream = (layout == TGS_LAYOUT_SLOT2 && m == 1 && !rotated && k <= kMaxWaveKernelK) ? 1 : 0;
   if (p.stream) {
@@ -760,6 +770,7 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
 }
 
 void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
+  if (p.mfma) return;
   if (p.stream) {
     // rows per wave: as many (8..64) as still give kWaveKernelTargetWaves waves in all. Small
     // launches get 8 rows per wave, which puts every load of a wave in flight at once.
@@ -782,6 +793,7 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
 }
 
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream) {
+  if (plan.mfma) return gemv_b3_mfma_launch(args, blocks, plan.m, plan.rotated != 0, stream);
   if (plan.stream) {
     switch (plan.lanes) {
       case 16: return launch_wave<16>(args, blocks, plan.iter, plan.slices, stream);

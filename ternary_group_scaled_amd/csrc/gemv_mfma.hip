@@ -1,0 +1,261 @@
+// Base-3 GEMV for a few activation rows (2..8 tokens) on the matrix cores.
+//
+// y[i][j] = sum_k s[j][k/128] * t[j][k] * xr[i][k], with xr = x or, for weights stored in the
+// rotated basis, xr = R x, R = blockdiag((1/sqrt(128)) H_128 S) ("Ternary Bonsai 2 27B, 5.93GB ...
+// (feat. PrismML)" (discuss.pytorch.kr), subsections "Group-scaled ternary format" and
+// "Block-wise Hadamard rotation"). With several tokens the per-token dot2 decode repeats the
+// whole base-3 digit extraction for every token; here the codes are decoded once into fp16
+// weights t in {-1, 0, +1} and v_mfma_f32_16x16x32_f16 multiplies them by all tokens at once
+// (tokens are the 16 rows of the A operand, padded with zeros).
+//
+// Work split. A workgroup of 8 waves owns 64 output rows (4 blocks of 16) and splits the scale
+// groups of K across its waves; each wave walks its groups one at a time:
+//   - Codes. A group's 128 trits start in byte B0 = floor(128 g / 5) at digit off0 = 128 g - 5 B0
+//     and end within the 32 bytes from B0. Lane (r, q) of a row block (r = lane % 16, q = lane / 16)
+//     reads bytes B0 + 8q .. B0 + 8q + 7 of row r (three aligned dwords and a funnel shift) and
+//     peels their digits with packed 16-bit integer ops (q = v * 171 >> 9 equals v / 3 for
+//     v < 256; digit = v - 3q), five per byte, as the dot2 kernels do. MFMA step j (0..4) takes
+//     digit j of all eight bytes, paired (byte 0, byte 2), (1, 3), (4, 6), (5, 7); one v_perm table
+//     lookup turns a digit pair into two fp16 weights (t = digit - 1, exact).
+//   - Activations. The wave writes the group's activations (rotated when the weights are: sign
+//     flip, the natural-order Sylvester butterfly over the 128-block, 1/sqrt(128), one rounding to
+//     fp16) into a private LDS tile laid out [q][j][8] in exactly the order of the weight operand,
+//     so each MFMA step reads its A fragment with one 16-byte load. The 32 slots of the 160-trit
+//     window that lie outside the group hold zeros: the trits there (neighbouring groups, or
+//     bytes past the row) multiply zero, and every MFMA step stays within one scale group.
+//   - Each group's 16 x 16 partial is scaled by its fp16 scale in fp32 and added to the running
+//     sum; at the end the 8 waves' sums are added through LDS in wave order (deterministic).
+#include "tgs_internal.h"
+
+namespace tgs {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFB = 4;          // 16-row blocks of y per workgroup
+constexpr int kWaves = 8;       // K slices per workgroup
+constexpr int kRowPitch = 168;  // halves per token row of the activation tile: 160 slots + 8 (bank spread)
+
+// window position rel (0..159) of a group's trit -> its slot in the [q][j][8] tile
+__device__ __forceinline__ int tile_slot(int rel) {
+  const int b = (rel * 205) >> 10;  // rel / 5 for rel < 160
+  const int j = rel - 5 * b;
+  const int q = b >> 3, bl = b & 7;
+  const int pos = (bl & 4) | ((bl & 1) << 1) | ((bl >> 1) & 1);  // byte order 0,2,1,3,4,6,5,7
+  return (q * 5 + j) * 8 + pos;
+}
+
+// two fp16 weights 2 digits -> (t_lo, t_hi): the digit picks byte d of the table {0xBC, 0, 0x3C, 0}
+// as the high byte of each half (fp16 -1, 0, +1; the fourth entry only ever meets a zero activation)
+__device__ __forceinline__ uint32_t weights_of_digits(u16x2 d) {
+  constexpr uint32_t kTable = 0x003C00BCu;
+  return __builtin_amdgcn_perm(0u, kTable, (__builtin_bit_cast(uint32_t, d) << 8) | 0x000C000Cu);
+}
+
+__device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both halves
+  const u16x2 q = (v * (u16x2)171) >> (u16x2)9;
+  const u16x2 d = v - q * (u16x2)3;
+  v = q;
+  return d;
+}
+
+template <int MT, bool ROT>
+__global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
+  __shared__ __attribute__((aligned(16))) _Float16 tiles[kWaves][16 * kRowPitch];
+
+  int jb = 0;
+  while (jb + 1 < args.count && (int)blockIdx.x >= args.job[jb + 1].block0) ++jb;
+  const GemvJob job = args.job[jb];
+  const int n = job.n, k = job.k, m = args.m;
+  const int groups = k / 128;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fr = lane & 15, kq = lane >> 4;
+  const int n_base = ((int)blockIdx.x - job.block0) * 16 * kFB;
+  const int g_begin = wave * groups / kWaves, g_end = (wave + 1) * groups / kWaves;
+
+  _Float16* tile = tiles[wave];
+  // rows MT..15 of the A operand stay zero; rows < MT are rewritten for every group
+  for (int i = lane; i < 16 * kRowPitch / 8; i += 64) reinterpret_cast<uint4*>(tile)[i] = make_uint4(0, 0, 0, 0);
+
+  // reads past each buffer return zero: rows >= n, tokens >= m (their outputs are not stored)
+  const __amdgpu_buffer_rsrc_t code_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.codes, 0, (int)((int64_t)n * job.stride), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t scale_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.x, 0, (int)((int64_t)m * k * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t sign_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.signs, 0, ROT ? k : 0, kRsrcWord3);
+
+  // offsets are unsigned: n * stride < 2^31 and 64 rows more add less than 2^31
+  uint32_t row_off[kFB], scale_row[kFB];
+#pragma unroll
+  for (int fb = 0; fb < kFB; ++fb) {
+    const uint32_t row = (uint32_t)(n_base + 16 * fb + fr);
+    row_off[fb] = row * (uint32_t)job.stride;
+    scale_row[fb] = row * (uint32_t)groups * 2u;
+  }
+
+  struct Stage {
+    uint32_t c[kFB][3];  // three aligned dwords of codes per row block
+    uint32_t s[kFB];     // raw fp16 scale bits
+    uint32_t x[MT][2];   // raw fp16 activation bits: elements lane and lane + 64 of the block
+    uint32_t sg[2];      // sign bytes of those elements
+  };
+  auto load = [&](Stage& st, int g) {
+    const bool live = g < g_end;
+    const uint32_t byte0 = (uint32_t)((128 * g) / 5 + 8 * kq);
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) {
+      const int off = live ? (int)(row_off[fb] + (byte0 & ~3u)) : kOobOffset;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b96(code_rsrc, off, 0, 0);
+      st.c[fb][0] = v[0];
+      st.c[fb][1] = v[1];
+      st.c[fb][2] = v[2];
+      st.s[fb] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, live ? (int)(scale_row[fb] + 2u * g) : kOobOffset,
+                                                     0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = 128 * g + lane + 64 * h;
+        st.x[t][h] = __builtin_amdgcn_raw_buffer_load_b16(x_rsrc, live ? (int)((t * k + e) * 2) : kOobOffset, 0, 0);
+      }
+    if (ROT) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        st.sg[h] = __builtin_amdgcn_raw_buffer_load_b8(sign_rsrc, live ? 128 * g + lane + 64 * h : kOobOffset, 0, 0);
+    }
+  };
+
+  f32x4 acc[kFB];
+#pragma unroll
+  for (int fb = 0; fb < kFB; ++fb) acc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage& st, int g) {
+    const int off0 = 128 * g - 5 * ((128 * g) / 5);  // digit of byte B0 where the group starts
+    const uint32_t sh = (uint32_t)(((128 * g) / 5 + 8 * kq) & 3);
+    // activations of this group -> tile rows 0..MT-1, in the weight operand's slot order
+    const int slot_a = tile_slot(lane + off0), slot_b = tile_slot(lane + 64 + off0);
+    const int slot_z = tile_slot(lane < off0 ? lane : 128 + lane);  // lanes < 32: slots outside the group
+    float sgn0 = 1.f, sgn1 = 1.f;
+    if (ROT) {
+      sgn0 = (int8_t)(st.sg[0] & 0xFFu) < 0 ? -1.f : 1.f;
+      sgn1 = (int8_t)(st.sg[1] & 0xFFu) < 0 ? -1.f : 1.f;
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)st.x[t][0]);
+      float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)st.x[t][1]);
+      if (ROT) {
+        v0 *= sgn0;
+        v1 *= sgn1;
+        const float a = v0 + v1, b = v0 - v1;  // the stride-64 stage, inside the lane
+        v0 = a;
+        v1 = b;
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {
+          const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
+          const bool upper = (lane & s) != 0;
+          v0 = upper ? (p0 - v0) : (v0 + p0);
+          v1 = upper ? (p1 - v1) : (v1 + p1);
+        }
+        v0 *= 0.08838834764831845f;  // 1/sqrt(128)
+        v1 *= 0.08838834764831845f;
+      }
+      tile[t * kRowPitch + slot_a] = (_Float16)v0;
+      tile[t * kRowPitch + slot_b] = (_Float16)v1;
+      if (lane < 32) tile[t * kRowPitch + slot_z] = (_Float16)0.f;
+    }
+    __asm__ volatile("" ::: "memory");  // the tile writes precede the fragment reads (one wave, in order)
+
+    // this lane's 8 bytes of each row block, then 5 MFMA steps
+    u16x2 ve0[kFB], vo0[kFB], ve1[kFB], vo1[kFB];
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) {
+      const uint32_t w0 = __builtin_amdgcn_alignbyte(st.c[fb][1], st.c[fb][0], sh);
+      const uint32_t w1 = __builtin_amdgcn_alignbyte(st.c[fb][2], st.c[fb][1], sh);
+      ve0[fb] = __builtin_bit_cast(u16x2, w0 & 0x00FF00FFu);
+      vo0[fb] = __builtin_bit_cast(u16x2, (w0 >> 8) & 0x00FF00FFu);
+      ve1[fb] = __builtin_bit_cast(u16x2, w1 & 0x00FF00FFu);
+      vo1[fb] = __builtin_bit_cast(u16x2, (w1 >> 8) & 0x00FF00FFu);
+    }
+    f32x4 part[kFB];
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) part[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const half8 a = *reinterpret_cast<const half8*>(tile + fr * kRowPitch + (kq * 5 + j) * 8);
+#pragma unroll
+      for (int fb = 0; fb < kFB; ++fb) {
+        const u16x2 de0 = j < 4 ? peel(ve0[fb]) : ve0[fb];
+        const u16x2 do0 = j < 4 ? peel(vo0[fb]) : vo0[fb];
+        const u16x2 de1 = j < 4 ? peel(ve1[fb]) : ve1[fb];
+        const u16x2 do1 = j < 4 ? peel(vo1[fb]) : vo1[fb];
+        const uint4 b4 = make_uint4(weights_of_digits(de0), weights_of_digits(do0), weights_of_digits(de1),
+                                    weights_of_digits(do1));
+        part[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, b4), part[fb], 0, 0, 0);
+      }
+    }
+    __asm__ volatile("" ::: "memory");  // the fragment reads precede the next group's tile writes
+    // D[i][j] (token i, output j) sits in lane 16 * (i / 4) + j, register i % 4
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) {
+      const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)st.s[fb]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[fb][r] = fmaf(sc, part[fb][r], acc[fb][r]);
+    }
+  };
+
+  // two groups of loads in flight; loads past the wave's last group are parked out of range
+  Stage st0, st1;
+  load(st0, g_begin);
+  for (int g = g_begin; g < g_end; g += 2) {
+    load(st1, g + 1);
+    compute(st0, g);
+    if (g + 1 >= g_end) break;
+    load(st0, g + 2);
+    compute(st1, g + 1);
+  }
+
+  // add the waves' sums in wave order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&tiles[0][0]);  // [wave][fb * 4 + r][lane]
+#pragma unroll
+  for (int fb = 0; fb < kFB; ++fb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * kFB * 4 + fb * 4 + r) * 64 + lane] = acc[fb][r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < kFB * 4 * 64; e += kWaves * 64) {
+    const int idx = e >> 6, ln = e & 63;
+    const int fb = idx >> 2, r = idx & 3;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += red[(w * kFB * 4 + idx) * 64 + ln];
+    const int token = 4 * (ln >> 4) + r, row = n_base + 16 * fb + (ln & 15);
+    if (token < m && row < n) job.y[(int64_t)token * n + row] = sum;
+  }
+}
+
+template <int MT>
+hipError_t launch_mt(GemvArgs& args, int blocks, bool rotated, hipStream_t stream) {
+  if (rotated)
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, true>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+  else
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, false>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, bool rotated, hipStream_t stream) {
+  if (m <= 2) return launch_mt<2>(args, blocks, rotated, stream);
+  if (m <= 4) return launch_mt<4>(args, blocks, rotated, stream);
+  return launch_mt<8>(args, blocks, rotated, stream);
+}
+
+}  // namespace tgs

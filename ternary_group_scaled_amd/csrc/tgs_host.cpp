@@ -272,7 +272,7 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
       if (done[(size_t)j]) continue;
       const tgs::GemvPlan pj = tgs::gemv_plan(ws[j].layout, ws[j].k, m, ws[j].rotated);
       if (pj.layout != plan.layout || pj.lanes != plan.lanes || pj.rotated != plan.rotated ||
-          pj.stream != plan.stream || pj.slices != plan.slices)
+          pj.stream != plan.stream || pj.slices != plan.slices || pj.mfma != plan.mfma)
         continue;
       members.push_back(j);
       total_rows += ws[j].n;
