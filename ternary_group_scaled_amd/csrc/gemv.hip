@@ -1,4 +1,5 @@
-// Ternary group-scaled GEMV (M <= 8 activation rows) for gfx950.
+// Ternary group-scaled GEMV (M <= 8 activation rows), slot-2 codes, for gfx950. (Base-3 codes
+// take the matrix-core kernel in gemv_mfma.hip.)
 //
 // y[i][n] = sum_k s[n][k/128] * t[n][k] * xr[i][k], weights read once, in packed form.
 // The weight definition w = s_g * t with one fp16 scale per 128 weights is the one of
@@ -7,7 +8,7 @@
 // subsection "Block-wise Hadamard rotation" (block n = 128 here).
 //
 // Work split. A workgroup (4 waves) owns a block of rows and walks K in slices. In a slice each
-// lane owns one 16-byte chunk of codes (64 slot-2 weights or 80 base-3 trits) at a fixed K
+// lane owns one 16-byte chunk of codes (64 weights) at a fixed K
 // position and keeps the matching activations in registers while it walks its rows. `S` lanes
 // share a row (16, 32 or 64); a wave covers 64/S rows per load instruction, and consecutive lanes
 // read consecutive 16-byte chunks of a row, so every load instruction is a fully used,
@@ -30,16 +31,6 @@
 // identical decode-and-dot sequence on the code word of an all-zero row (every slot q = 1): a
 // row whose codes are all zero then cancels bit for bit and gives exactly 0.
 //
-// Base-3. Each byte holds five trits, byte = sum_j (t_j + 1) 3^j. A word is split into two
-// 16-bit lanes (bytes 0,2 and bytes 1,3); each digit is peeled off both lanes at once with
-// packed 16-bit integer ops (q = v * 171 >> 9 equals v / 3 for v < 256; digit = v - 3q) and
-// left in bits 0..1 of its lane, where it is again an exact fp16 subnormal fed to dot2 (at these
-// bits dot2 keeps fewer product bits, about 2^-17 relative: far inside the tolerance, and the
-// all-zero-row subtraction still cancels exactly, since it repeats the same operations). A
-// 16-byte chunk (80 trits) can straddle a 128-trit scale group, so each lane keeps two
-// accumulators with activation pairs masked by group. The all-zero row (byte 121 = five zero
-// trits) again supplies sum_k x.
-//
 // Shared per-slice work. The activation pairs of a chunk and its all-zero-row product depend on
 // the chunk only, not on the wave, so one thread per chunk builds them once per workgroup and
 // stores them in LDS, laid out [16-byte granule][chunk] so that the waves' reads are
@@ -53,7 +44,6 @@ namespace tgs {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // waves per workgroup: 4 for every variant (8 waves per workgroup measured slower on the large
 // single-token launches, and 4 gives small matrices more workgroups)
@@ -77,24 +67,8 @@ __device__ __forceinline__ uint32_t xpair(const uint32_t* w) {
   return __builtin_amdgcn_perm(w[E2 / 2], w[E1 / 2], sel);
 }
 
-template <int LAYOUT>
-struct Geo;
-template <>
-struct Geo<TGS_LAYOUT_SLOT2> {
-  static constexpr int kElems = 64;   // weights per 16-byte chunk
-  static constexpr int kPairDw = 32;  // pair words per chunk and token
-};
-template <>
-struct Geo<TGS_LAYOUT_BASE3> {
-  static constexpr int kElems = 80;
-  static constexpr int kPairDw = 80;  // 40 pairs, each masked to the chunk's first and second group
-};
-
-__host__ __device__ inline int chunks_per_row(int layout, int k) {
-  if (layout == TGS_LAYOUT_SLOT2) return k / 64;
-  int used = (k + 4) / 5;
-  return (used + 15) / 16;
-}
+constexpr int kChunkElems = 64;   // weights per 16-byte chunk
+constexpr int kChunkPairDw = 32;  // activation pair words per chunk and token
 
 // ---- building the activation pairs of one chunk ------------------------------------------
 
@@ -111,38 +85,6 @@ __device__ __forceinline__ void build_pairs_slot2(const uint32_t* w, uint32_t* p
     p[8 * d + 6] = xpair<6, 14>(w + 8 * d);
     p[8 * d + 7] = xpair<7, 15>(w + 8 * d);
   }
-}
-
-// base-3: for dword d and digit j, bytes (0,2) carry trits (20d+j, 20d+10+j) and bytes (1,3)
-// trits (20d+5+j, 20d+15+j). Layout of p: [0,20) e-pairs of the first group, [20,40) e-pairs of
-// the second group, [40,60) and [60,80) the same for the o-pairs; index 5d + j within each.
-template <int D, int J>
-__device__ __forceinline__ void base3_pair(const uint32_t* w, int boundary, uint32_t* p) {
-  constexpr int e1 = 20 * D + J, e2 = 20 * D + 10 + J, o1 = 20 * D + 5 + J, o2 = 20 * D + 15 + J;
-  const uint32_t pe = xpair<e1, e2>(w), po = xpair<o1, o2>(w);
-  const uint32_t me = (e1 < boundary ? 0xFFFFu : 0u) | (e2 < boundary ? 0xFFFF0000u : 0u);
-  const uint32_t mo = (o1 < boundary ? 0xFFFFu : 0u) | (o2 < boundary ? 0xFFFF0000u : 0u);
-  p[5 * D + J] = pe & me;
-  p[20 + 5 * D + J] = pe & ~me;
-  p[40 + 5 * D + J] = po & mo;
-  p[60 + 5 * D + J] = po & ~mo;
-}
-
-template <int D>
-__device__ __forceinline__ void base3_pairs_dword(const uint32_t* w, int boundary, uint32_t* p) {
-  base3_pair<D, 0>(w, boundary, p);
-  base3_pair<D, 1>(w, boundary, p);
-  base3_pair<D, 2>(w, boundary, p);
-  base3_pair<D, 3>(w, boundary, p);
-  base3_pair<D, 4>(w, boundary, p);
-}
-
-// boundary: index within the chunk of the first trit of the second scale group (>= 80: none)
-__device__ __forceinline__ void build_pairs_base3(const uint32_t* w, int boundary, uint32_t* p) {
-  base3_pairs_dword<0>(w, boundary, p);
-  base3_pairs_dword<1>(w, boundary, p);
-  base3_pairs_dword<2>(w, boundary, p);
-  base3_pairs_dword<3>(w, boundary, p);
 }
 
 // ---- chunk products -------------------------------------------------------------------------
@@ -166,41 +108,6 @@ __device__ __forceinline__ float chunk_dot_slot2(const uint4& cw, const uint32_t
     a4 = dot2(w & 0x03000300u, q[7], a4);  // j = 7
   }
   return fmaf(fmaf(a4, 0.25f, a3), 0.25f, a2);
-}
-
-// base-3: 2^-24 * sum_k (t_k + 1) x_k for the (up to) two scale groups of a chunk
-__device__ __forceinline__ void chunk_dot_base3(const uint4& cw, const uint32_t* p, float& out0, float& out1) {
-  float a0 = 0.f, a1 = 0.f;
-  const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    u16x2 ve = __builtin_bit_cast(u16x2, words[d] & 0x00FF00FFu);
-    u16x2 vo = __builtin_bit_cast(u16x2, (words[d] >> 8) & 0x00FF00FFu);
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      u16x2 de, dd;
-      if (j < 4) {
-        u16x2 qe = (ve * (u16x2)171) >> (u16x2)9;
-        u16x2 qo = (vo * (u16x2)171) >> (u16x2)9;
-        de = ve - qe * (u16x2)3;
-        dd = vo - qo * (u16x2)3;
-        ve = qe;
-        vo = qo;
-      } else {
-        de = ve;
-        dd = vo;
-      }
-      // digit at bits 0..1: the fp16 subnormal digit * 2^-24
-      const uint32_t be = __builtin_bit_cast(uint32_t, de);
-      const uint32_t bo = __builtin_bit_cast(uint32_t, dd);
-      a0 = dot2(be, p[5 * d + j], a0);
-      a1 = dot2(be, p[20 + 5 * d + j], a1);
-      a0 = dot2(bo, p[40 + 5 * d + j], a0);
-      a1 = dot2(bo, p[60 + 5 * d + j], a1);
-    }
-  }
-  out0 = a0;
-  out1 = a1;
 }
 
 // ---- staging one slice of activations ----------------------------------------------------
@@ -241,29 +148,27 @@ __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint
 
 // ---- the kernel ----------------------------------------------------------------------
 
-// Single-token slot-2 kernels must keep four waves per SIMD resident (at most 128 VGPRs; three for
-// the rotated variant) to have enough loads in flight; the build fails if that ever forces a spill.
-template <int LAYOUT, int MT, bool ROT>
+// Single-token kernels must keep four waves per SIMD resident (at most 128 VGPRs; three for the
+// rotated variant) to have enough loads in flight; the build fails if that ever forces a spill.
+template <int MT, bool ROT>
 constexpr int min_waves_per_eu() {
-  return (LAYOUT == TGS_LAYOUT_SLOT2 && MT == 1) ? (ROT ? 3 : 4) : (MT == 1 ? 2 : 1);
+  return MT == 1 ? (ROT ? 3 : 4) : 1;
 }
 
-template <int LAYOUT, int S, int MT, int ITER, bool ROT>
+template <int S, int MT, int ITER, bool ROT>
 __global__ __launch_bounds__(64 * waves_for<ITER>())
-__attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) void gemv_kernel(const GemvArgs args) {
-  using G = Geo<LAYOUT>;
+__attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_kernel(const GemvArgs args) {
   constexpr int kWaves = waves_for<ITER>();
   constexpr int kThreads = 64 * kWaves;
   constexpr int kIter = ITER;
   constexpr int kRowsPerInstr = 64 / S;
   constexpr int kRowsPerWave = kIter * kRowsPerInstr;
   constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
-  constexpr int kSliceElems = S * G::kElems;
-  constexpr int kGran = G::kPairDw / 4;  // 16-byte granules of pair words per chunk and token
-  constexpr int kAcc = LAYOUT == TGS_LAYOUT_BASE3 ? 2 : 1;
+  constexpr int kSliceElems = S * kChunkElems;
+  constexpr int kGran = kChunkPairDw / 4;  // 16-byte granules of pair words per chunk and token
 
   __shared__ uint4 lds_pairs[MT * kGran * S];                                          // [t][granule][chunk]
-  __shared__ float lds_ref[MT * kAcc * S];                                             // [t][group][chunk]
+  __shared__ float lds_ref[MT * S];                                                    // [t][chunk]
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[ROT ? MT * kSliceElems : 8];  // rotated staging
 
   // find this workgroup's job (uniform; the table lives in the kernel arguments)
@@ -272,7 +177,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
   const GemvJob& job = args.job[j];
   const int n = job.n, k = job.k, m = args.m;
   const int groups = k / 128;
-  const int chunks = chunks_per_row(LAYOUT, k);
+  const int chunks = k / kChunkElems;
   const int slices = (chunks + S - 1) / S;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -285,8 +190,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
   constexpr int kRing = kBatches >= 4 ? 4 : 3;
   struct Batch {
     uint4 cw[kBatch];
-    uint32_t s0[kBatch], s1[kBatch];  // raw fp16 scale bits: converted only when used, so a
-                                      // prefetch never waits for its own loads
+    uint32_t s0[kBatch];  // raw fp16 scale bits: converted only when used, so a prefetch never
+                          // waits for its own loads
   };
   // Buffer resources: loads past the end of the codes or scales return 0 instead of faulting,
   // so rows past n need no branch and every load is issued unconditionally (which keeps the
@@ -295,8 +200,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
       __builtin_amdgcn_make_buffer_rsrc((void*)job.codes, 0, (int)((int64_t)n * job.stride), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t scale_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)job.scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
-  // codes and the (up to two) group scales of rows b*kBatch .. b*kBatch+kBatch-1 of this lane
-  // slot. A lane whose chunk lies past the row (last slice) reads some other in-bounds bytes; its
+  // codes and the group scale of rows b*kBatch .. b*kBatch+kBatch-1 of this lane slot. A lane whose chunk lies past the row (last slice) reads some other in-bounds bytes; its
   // activations are zero and its scales are forced to zero when used, so it adds nothing.
   auto load_batch = [&](Batch& bt, int b, int c, int g0) {
 #pragma unroll
@@ -309,9 +213,6 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
       const uint32_t scale_off = (__umul24((uint32_t)row, (uint32_t)groups) + (uint32_t)g0) * 2u;
       bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)code_off, 0, kStreamAux));
       bt.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)scale_off, 0, 0);
-      bt.s1[i] = 0;
-      if (LAYOUT == TGS_LAYOUT_BASE3)
-        bt.s1[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)(scale_off + 2u), 0, 0);
     }
   };
 
@@ -326,10 +227,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
       const int k_begin = ks * kSliceElems;
       const int c = ks * S + cl;  // this lane's chunk
       const bool chunk_ok = c < chunks;
-      const int t0 = c * G::kElems;
-      const int boundary = (LAYOUT == TGS_LAYOUT_BASE3) ? ((t0 / 128 + 1) * 128 - t0) : 1 << 20;
-      const int g0 = (LAYOUT == TGS_LAYOUT_SLOT2) ? c / 2 : t0 / 128;
-      const bool has_g1 = LAYOUT == TGS_LAYOUT_BASE3 && boundary < G::kElems && g0 + 1 < groups;
+      const int g0 = c / 2;  // two chunks per scale group
 
       // Codes and scales do not depend on the activations: start loading the first batches of
       // rows before the activation slice is staged, so the two latencies overlap.
@@ -345,15 +243,14 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
       }
       for (int u = tid; u < MT * S; u += kThreads) {
         const int t = u / S, bc = u - t * S;  // token, chunk within the slice
-        const int bt0 = (ks * S + bc) * G::kElems;
-        const int bbound = (LAYOUT == TGS_LAYOUT_BASE3) ? ((bt0 / 128 + 1) * 128 - bt0) : 1 << 20;
-        uint32_t w[G::kElems / 2];
+        const int bt0 = (ks * S + bc) * kChunkElems;
+        uint32_t w[kChunkElems / 2];
 #pragma unroll
-        for (int v = 0; v < G::kElems / 8; ++v) {
+        for (int v = 0; v < kChunkElems / 8; ++v) {
           uint4 q = make_uint4(0, 0, 0, 0);
           const int kk = bt0 + 8 * v;  // K and chunk starts are multiples of 8
           if constexpr (ROT) {
-            q = *reinterpret_cast<const uint4*>(lds_x + t * kSliceElems + bc * G::kElems + 8 * v);
+            q = *reinterpret_cast<const uint4*>(lds_x + t * kSliceElems + bc * kChunkElems + 8 * v);
           } else {
             if (m0 + t < m && kk < k) q = *reinterpret_cast<const uint4*>(job.x + (int64_t)(m0 + t) * k + kk);
           }
@@ -362,17 +259,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
           w[4 * v + 2] = q.z;
           w[4 * v + 3] = q.w;
         }
-        uint32_t p[G::kPairDw];
-        if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
-          build_pairs_slot2(w, p);
-          lds_ref[t * S + bc] = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
-        } else {
-          build_pairs_base3(w, bbound, p);
-          float r0, r1;
-          chunk_dot_base3(make_uint4(0x79797979u, 0x79797979u, 0x79797979u, 0x79797979u), p, r0, r1);
-          lds_ref[(t * 2 + 0) * S + bc] = r0;
-          lds_ref[(t * 2 + 1) * S + bc] = r1;
-        }
+        uint32_t p[kChunkPairDw];
+        build_pairs_slot2(w, p);
+        lds_ref[t * S + bc] = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
 #pragma unroll
         for (int g = 0; g < kGran; ++g)
           lds_pairs[(t * kGran + g) * S + bc] = make_uint4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
@@ -380,8 +269,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
       __syncthreads();
 
       // ---- this lane's pairs and reference products
-      uint32_t xp[MT][G::kPairDw];
-      float ref0[MT], ref1[MT];
+      uint32_t xp[MT][kChunkPairDw];
+      float ref0[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -392,8 +281,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
           xp[t][4 * g + 2] = q.z;
           xp[t][4 * g + 3] = q.w;
         }
-        ref0[t] = lds_ref[(t * kAcc) * S + cl];
-        ref1[t] = kAcc == 2 ? lds_ref[(t * kAcc + kAcc - 1) * S + cl] : 0.f;
+        ref0[t] = lds_ref[t * S + cl];
       }
 
       // rows in batches; kRing - 1 batches are in flight while one is computed (a ring of register
@@ -408,19 +296,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
         for (int i = 0; i < kBatch; ++i) {
           const int it = b * kBatch + i;
           const float sc0 = chunk_ok ? f16_to_f32((uint16_t)cur.s0[i]) : 0.f;
-          if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-              part[it][t] = fmaf(sc0, chunk_dot_slot2(cur.cw[i], xp[t]) - ref0[t], part[it][t]);
-          } else {
-            const float sc1 = (chunk_ok && has_g1) ? f16_to_f32((uint16_t)cur.s1[i]) : 0.f;
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              float q0, q1;
-              chunk_dot_base3(cur.cw[i], xp[t], q0, q1);
-              part[it][t] = fmaf(sc1, q1 - ref1[t], fmaf(sc0, q0 - ref0[t], part[it][t]));
-            }
-          }
+          for (int t = 0; t < MT; ++t)
+            part[it][t] = fmaf(sc0, chunk_dot_slot2(cur.cw[i], xp[t]) - ref0[t], part[it][t]);
         }
       }
     }
@@ -463,9 +341,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<LAYOUT, MT, ROT>(), 8))) voi
 #pragma unroll
       for (int off = S / 2, cnt = kIter; off >= 1; off >>= 1, cnt = cnt > 1 ? cnt / 2 : 1)
         if (cnt <= 1) low_bits |= off;
-      // the chunk products carry a factor 2^-20 (slot-2) or 2^-24 (base-3), undone here exactly
-      constexpr float kUnscale = LAYOUT == TGS_LAYOUT_BASE3 ? 16777216.0f : 1048576.0f;
-      if ((cl & low_bits) == 0 && row < n && m0 + t < m) job.y[(int64_t)(m0 + t) * n + row] = v[0] * kUnscale;
+      // the chunk products carry a factor 2^-20, undone here (an exact power of two)
+      if ((cl & low_bits) == 0 && row < n && m0 + t < m) job.y[(int64_t)(m0 + t) * n + row] = v[0] * 1048576.0f;
     }
   }
 }
@@ -672,59 +549,47 @@ hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices
   return hipGetLastError();
 }
 
-template <int LAYOUT, int S, int MT, int ITER, bool ROT>
+template <int S, int MT, int ITER, bool ROT>
 hipError_t launch_one(GemvArgs& args, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_kernel<LAYOUT, S, MT, ITER, ROT>), dim3(blocks), dim3(64 * waves_for<ITER>()), 0, stream,
-                     args);
+  hipLaunchKernelGGL((gemv_kernel<S, MT, ITER, ROT>), dim3(blocks), dim3(64 * waves_for<ITER>()), 0, stream, args);
   return hipGetLastError();
 }
 
-// rows per lane slot: 8 for large single-token slot-2 launches (more work per workgroup), else 4;
+// rows per lane slot: 8 for large single-token launches (more work per workgroup), else 4;
 // fewer when several tokens share the registers
-template <int LAYOUT, int S, int MT>
+template <int S, int MT>
 hipError_t launch_rot(bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
-  if constexpr (MT == 1 && LAYOUT == TGS_LAYOUT_SLOT2) {
+  if constexpr (MT == 1) {
     if (iter == 8)
-      return rot ? launch_one<LAYOUT, S, MT, 8, true>(args, blocks, stream)
-                 : launch_one<LAYOUT, S, MT, 8, false>(args, blocks, stream);
-    return rot ? launch_one<LAYOUT, S, MT, 4, true>(args, blocks, stream)
-               : launch_one<LAYOUT, S, MT, 4, false>(args, blocks, stream);
+      return rot ? launch_one<S, MT, 8, true>(args, blocks, stream) : launch_one<S, MT, 8, false>(args, blocks, stream);
+    return rot ? launch_one<S, MT, 4, true>(args, blocks, stream) : launch_one<S, MT, 4, false>(args, blocks, stream);
   } else {
-    constexpr int it = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
-    return rot ? launch_one<LAYOUT, S, MT, it, true>(args, blocks, stream)
-               : launch_one<LAYOUT, S, MT, it, false>(args, blocks, stream);
+    constexpr int it = MT == 2 ? 2 : 1;
+    return rot ? launch_one<S, MT, it, true>(args, blocks, stream) : launch_one<S, MT, it, false>(args, blocks, stream);
   }
 }
 
-template <int LAYOUT, int S>
+template <int S>
 hipError_t launch_mt(int mt, bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
-  if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
-    switch (mt) {
-      case 1: return launch_rot<LAYOUT, S, 1>(rot, iter, args, blocks, stream);
-      case 2: return launch_rot<LAYOUT, S, 2>(rot, iter, args, blocks, stream);
-      default: return launch_rot<LAYOUT, S, 4>(rot, iter, args, blocks, stream);
-    }
-  } else {
-    return launch_rot<LAYOUT, S, 1>(rot, iter, args, blocks, stream);
+  switch (mt) {
+    case 1: return launch_rot<S, 1>(rot, iter, args, blocks, stream);
+    case 2: return launch_rot<S, 2>(rot, iter, args, blocks, stream);
+    default: return launch_rot<S, 4>(rot, iter, args, blocks, stream);
   }
 }
 
-template <int LAYOUT>
 hipError_t launch_s(int s, int mt, bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   switch (s) {
-    case 16: return launch_mt<LAYOUT, 16>(mt, rot, iter, args, blocks, stream);
-    case 32: return launch_mt<LAYOUT, 32>(mt, rot, iter, args, blocks, stream);
-    default: return launch_mt<LAYOUT, 64>(mt, rot, iter, args, blocks, stream);
+    case 16: return launch_mt<16>(mt, rot, iter, args, blocks, stream);
+    case 32: return launch_mt<32>(mt, rot, iter, args, blocks, stream);
+    default: return launch_mt<64>(mt, rot, iter, args, blocks, stream);
   }
 }
 
 }  // namespace
 
 // Tokens per pass (compile-time width of the activation registers); larger m loops over passes.
-static int tokens_per_pass(int32_t layout, int64_t m) {
-  if (layout == TGS_LAYOUT_BASE3) return 1;
-  return m >= 4 ? 4 : (m >= 2 ? 2 : 1);
-}
+static int tokens_per_pass(int64_t m) { return m >= 4 ? 4 : (m >= 2 ? 2 : 1); }
 
 GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
   GemvPlan p;
@@ -733,18 +598,19 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
   p.rotated = rotated;
   p.slices = 0;
   p.mfma = 0;
-  const int chunks = chunks_per_row(layout, (int)k);
-  // base-3 with several tokens: decode once, multiply all tokens on the matrix cores
-  if (layout == TGS_LAYOUT_BASE3 && m >= 2) {
+  // base-3: decode once, multiply all tokens on the matrix cores
+  if (layout == TGS_LAYOUT_BASE3) {
     p.mfma = 1;
     p.stream = 0;
     p.lanes = 64;
     p.iter = 1;
-    p.rows_per_block = kMfmaGemvRows;
+    p.rows_per_block = gemv_b3_mfma_rows((int32_t)m);
     return p;
   }
-  // the single-token kernel: one wave per K slice of 64 chunks, up to 16 waves per workgroup
-  p.stream = (layout == TGS_LAYOUT_SLOT2 && m == 1 && !rotated && k <= kMaxWaveKernelK) ? 1 : 0;
+  // slot-2 from here on. The single-token kernel: one wave per K slice of 64 chunks, up to 16
+  // waves per workgroup
+  const int chunks = (int)(k / kChunkElems);
+  p.stream = (m == 1 && !rotated && k <= kMaxWaveKernelK) ? 1 : 0;
   if (p.stream) {
     // rows shorter than one full slice: 32 or 16 lanes per row, several rows per instruction
     p.lanes = chunks > 32 ? 64 : (chunks > 16 ? 32 : 16);
@@ -763,7 +629,7 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
     }
   }
   p.lanes = best;
-  const int mt = tokens_per_pass(layout, m);
+  const int mt = tokens_per_pass(m);
   p.iter = mt == 1 ? 4 : (mt == 2 ? 2 : 1);
   p.rows_per_block = 4 * p.iter * (64 / best);  // 4 waves per workgroup at these sizes
   return p;
@@ -784,7 +650,7 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
   }
   // single-token slot-2 launches with plenty of rows: twice the rows per workgroup (8 rows per lane
   // slot) while that still leaves >= 2048 workgroups
-  if (p.layout != TGS_LAYOUT_SLOT2 || tokens_per_pass(p.layout, p.m) != 1) return;
+  if (tokens_per_pass(p.m) != 1) return;
   const int64_t big_rows = (int64_t)waves_for<8>() * 8 * (64 / p.lanes);
   if ((total_rows + big_rows - 1) / big_rows >= 2048) {
     p.iter = 8;
@@ -801,11 +667,7 @@ hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hip
       default: return launch_wave<64>(args, blocks, plan.iter, plan.slices, stream);
     }
   }
-  const int mt = tokens_per_pass(plan.layout, plan.m);
-  const bool rot = plan.rotated != 0;
-  if (plan.layout == TGS_LAYOUT_SLOT2)
-    return launch_s<TGS_LAYOUT_SLOT2>(plan.lanes, mt, rot, plan.iter, args, blocks, stream);
-  return launch_s<TGS_LAYOUT_BASE3>(plan.lanes, mt, rot, plan.iter, args, blocks, stream);
+  return launch_s(plan.lanes, tokens_per_pass(plan.m), plan.rotated != 0, plan.iter, args, blocks, stream);
 }
 
 }  // namespace tgs

@@ -1,14 +1,15 @@
-// Base-3 GEMV for a few activation rows (2..8 tokens) on the matrix cores.
+// Base-3 GEMV (1..8 tokens) on the matrix cores.
 //
 // y[i][j] = sum_k s[j][k/128] * t[j][k] * xr[i][k], with xr = x or, for weights stored in the
 // rotated basis, xr = R x, R = blockdiag((1/sqrt(128)) H_128 S) ("Ternary Bonsai 2 27B, 5.93GB ...
 // (feat. PrismML)" (discuss.pytorch.kr), subsections "Group-scaled ternary format" and
-// "Block-wise Hadamard rotation"). With several tokens the per-token dot2 decode repeats the
-// whole base-3 digit extraction for every token; here the codes are decoded once into fp16
-// weights t in {-1, 0, +1} and v_mfma_f32_16x16x32_f16 multiplies them by all tokens at once
-// (tokens are the 16 rows of the A operand, padded with zeros).
+// "Block-wise Hadamard rotation"). A dot2 decode would repeat the whole base-3 digit extraction
+// for every token; here the codes are decoded once into fp16 weights t in {-1, 0, +1} and
+// v_mfma_f32_16x16x32_f16 multiplies them by all tokens at once (tokens are the 16 rows of the A
+// operand, padded with zeros). Even for one token this measured faster than the dot2 decode: the
+// matrix cores take the multiply-adds and the decode is a few packed integer ops per digit.
 //
-// Work split. A workgroup of 8 waves owns 64 output rows (4 blocks of 16) and splits the scale
+// Work split. A workgroup of 8 waves owns 16 * FB output rows and splits the scale
 // groups of K across its waves; each wave walks its groups one at a time:
 //   - Codes. A group's 128 trits start in byte B0 = floor(128 g / 5) at digit off0 = 128 g - 5 B0
 //     and end within the 32 bytes from B0. Lane (r, q) of a row block (r = lane % 16, q = lane / 16)
@@ -34,8 +35,11 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kFB = 4;          // 16-row blocks of y per workgroup
 constexpr int kWaves = 8;       // K slices per workgroup
+// 16-row blocks per workgroup: 1 for a single token (more workgroups for the small launches of a
+// decode step; measured best), 4 for several tokens (the decode and rotation are shared by more
+// rows)
+constexpr int kMfmaFB1 = 1;
 constexpr int kRowPitch = 168;  // halves per token row of the activation tile: 160 slots + 8 (bank spread)
 
 // window position rel (0..159) of a group's trit -> its slot in the [q][j][8] tile
@@ -61,7 +65,7 @@ __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both 
   return d;
 }
 
-template <int MT, bool ROT>
+template <int MT, int kFB, bool ROT>
 __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
   __shared__ __attribute__((aligned(16))) _Float16 tiles[kWaves][16 * kRowPitch];
 
@@ -241,21 +245,24 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   }
 }
 
-template <int MT>
+template <int MT, int FB>
 hipError_t launch_mt(GemvArgs& args, int blocks, bool rotated, hipStream_t stream) {
   if (rotated)
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, true>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, true>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
   else
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, false>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, false>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int gemv_b3_mfma_rows(int32_t m) { return m == 1 ? 16 * kMfmaFB1 : 64; }
+
 hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, bool rotated, hipStream_t stream) {
-  if (m <= 2) return launch_mt<2>(args, blocks, rotated, stream);
-  if (m <= 4) return launch_mt<4>(args, blocks, rotated, stream);
-  return launch_mt<8>(args, blocks, rotated, stream);
+  if (m <= 1) return launch_mt<1, kMfmaFB1>(args, blocks, rotated, stream);
+  if (m <= 2) return launch_mt<2, 4>(args, blocks, rotated, stream);
+  if (m <= 4) return launch_mt<4, 4>(args, blocks, rotated, stream);
+  return launch_mt<8, 4>(args, blocks, rotated, stream);
 }
 
 }  // namespace tgs

@@ -51,7 +51,7 @@ struct GemvPlan {
   int32_t rotated;    // 0 or 1
   int32_t stream;     // 1: the single-token kernel (slot-2, plain basis, m = 1)
   int32_t slices;     // single-token kernel: K slices of 64 chunks = waves per workgroup
-  int32_t mfma;       // 1: base-3 with several tokens, on the matrix cores (gemv_mfma.hip)
+  int32_t mfma;       // 1: base-3, on the matrix cores (gemv_mfma.hip)
   int32_t iter;       // rows per lane slot
   int32_t rows_per_block;
 };
@@ -62,8 +62,8 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated);
 // after the jobs of a launch are known: pick rows per workgroup from their total row count
 void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows);
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream);
-// base-3, 2..8 tokens: 64 rows of y per workgroup
-constexpr int kMfmaGemvRows = 64;
+// base-3 on the matrix cores: rows of y per workgroup for m tokens
+int gemv_b3_mfma_rows(int32_t m);
 hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, bool rotated, hipStream_t stream);
 
 hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
