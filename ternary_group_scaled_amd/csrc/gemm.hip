@@ -78,23 +78,29 @@ __device__ __forceinline__ uint16_t bf16_of_2t_digit(uint32_t digit) {
   return digit == 0 ? 0xC000u : (digit == 2 ? 0x4000u : 0u);
 }
 
-// Two waves per SIMD (at most 256 registers), so that two workgroups share a CU and one's MFMAs
-// run while the other waits on its loads (measured +40% at 2048 rows over one workgroup per CU).
-template <int LAYOUT, int BM, int BN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void gemm_tile_kernel(const uint8_t* __restrict__ codes, int64_t stride,
-                                                             const uint16_t* __restrict__ scales, int n, int k,
-                                                             const uint16_t* __restrict__ x, int m,
-                                                             float* __restrict__ y) {
+// Two waves per SIMD (at most 256 registers; slot-2), so that two workgroups share a CU and one's
+// MFMAs run while the other waits on its loads (measured +40% at 2048 rows over one per CU).
+// KS = 2 splits K between two halves of the workgroup (4 waves each, groups taken alternately,
+// own LDS tiles); the second half's sums are added to the first's at the end, through LDS. It is
+// used when the tiles alone give too few workgroups.
+template <int LAYOUT, int BM, int BN, int KS>
+__global__ __launch_bounds__(kThreads * KS)
+__attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_SLOT2 ? 2 : 1, 8))) void gemm_tile_kernel(
+    const uint8_t* __restrict__ codes, int64_t stride, const uint16_t* __restrict__ scales, int n, int k,
+    const uint16_t* __restrict__ x, int m, float* __restrict__ y) {
   constexpr int kWM = BM / 2, kWN = BN / 2;  // tile of one wave
   constexpr int kBlkM = kWM / 16, kBlkN = kWN / 16;
   constexpr int kXUnits = BM * 8 / kThreads;  // 16-value activation units per thread and group
   constexpr int kCodeThreads = BN * 2;        // threads that each hold 64 codes of one row
 
-  __shared__ __attribute__((aligned(16))) uint16_t xs[BM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[BN * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t xs_all[KS][BM * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t ws_all[KS][BN * kPitch];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kh = (int)threadIdx.x / kThreads;  // K half
+  const int tid = (int)threadIdx.x % kThreads, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  uint16_t* xs = xs_all[kh];
+  uint16_t* ws = ws_all[kh];
   const int n_base = blockIdx.x * BN, m_base = blockIdx.y * BM;
   const int groups = k / 128;
 
@@ -175,12 +181,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     for (int b = 0; b < kBlkN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  load_stage(0);
-  store_stage(0);
+  // this half takes groups kh, kh + KS, ...; both halves run the same number of iterations (the
+  // barriers are shared), and a group index past the end is loaded harmlessly but not multiplied
+  const int iters = (groups + KS - 1) / KS;
+  load_stage(kh);
+  store_stage(kh);
   __syncthreads();
-  for (int g = 0; g < groups; ++g) {
-    const bool more = g + 1 < groups;
-    if (more) load_stage(g + 1);
+  for (int i = 0; i < iters; ++i) {
+    const int g = i * KS + kh;
+    const bool more = i + 1 < iters;
+    if (more) load_stage(g + KS);
     // this lane's output columns: their scales, loaded ahead of the MFMAs
     uint32_t sraw[kBlkN];
 #pragma unroll
@@ -208,19 +218,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
         for (int b = 0; b < kBlkN; ++b)
           part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], part[a][b], 0, 0, 0);
     }
+    if (KS == 1 || g < groups) {
 #pragma unroll
-    for (int b = 0; b < kBlkN; ++b) {
-      const float sc = 0.5f * f16_to_f32((uint16_t)sraw[b]);  // the weights were decoded as 2t
+      for (int b = 0; b < kBlkN; ++b) {
+        const float sc = 0.5f * f16_to_f32((uint16_t)sraw[b]);  // the weights were decoded as 2t
 #pragma unroll
-      for (int a = 0; a < kBlkM; ++a)
+        for (int a = 0; a < kBlkM; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[a][b][r] = fmaf(sc, part[a][b][r], acc[a][b][r]);
+          for (int r = 0; r < 4; ++r) acc[a][b][r] = fmaf(sc, part[a][b][r], acc[a][b][r]);
+      }
     }
     __syncthreads();
     if (more) {
-      store_stage(g + 1);
+      store_stage(g + KS);
       __syncthreads();
     }
+  }
+  if constexpr (KS == 2) {
+    // the second half hands its sums to the first (fixed order: first + second)
+    float* red = reinterpret_cast<float*>(xs_all[1]);  // 4 waves x 64 lanes x kBlkM*kBlkN*4 floats
+    static_assert(kBlkM * kBlkN * 4 * 256 * 4 <= BM * kPitch * 2, "reduction buffer fits the tile");
+    if (kh == 1) {
+#pragma unroll
+      for (int a = 0; a < kBlkM; ++a)
+#pragma unroll
+        for (int b = 0; b < kBlkN; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((a * kBlkN + b) * 4 + r) * 256 + tid] = acc[a][b][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int a = 0; a < kBlkM; ++a)
+#pragma unroll
+      for (int b = 0; b < kBlkN; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[a][b][r] += red[((a * kBlkN + b) * 4 + r) * 256 + tid];
   }
 
   // epilogue: D[i][j] of a 16x16 block sits in lane (i/4)*16 + j, register i%4
@@ -453,23 +486,29 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
     }
     return hipGetLastError();
   }
-  // tiles: 128 x 128 for many activation rows, else 64 rows; 64 columns when 128 gives too few tiles
+  // tiles: 128 x 128 for many activation rows, else 64 rows; 64 columns when 128 gives too few tiles;
+  // K split in two inside the workgroup when even then there are fewer than 512 tiles
   const int bm = m > 128 ? 128 : 64;
   const int64_t m_tiles = (m + bm - 1) / bm;
   const int bn = (n + 127) / 128 * m_tiles >= 512 ? 128 : 64;
+  const int64_t tiles = (n + bn - 1) / bn * m_tiles;
+  const bool ks2 = tiles < 512 && k / 128 >= 16;
   const dim3 grid((unsigned)((n + bn - 1) / bn), (unsigned)m_tiles);
-  if (bm == 128 && bn == 128)
-    hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, 128, 128>), grid, dim3(kThreads), 0, stream, codes, stride, scales,
-                       (int)n, (int)k, x, (int)m, y);
-  else if (bm == 128)
-    hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, 128, 64>), grid, dim3(kThreads), 0, stream, codes, stride, scales,
-                       (int)n, (int)k, x, (int)m, y);
-  else if (bn == 128)
-    hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, 64, 128>), grid, dim3(kThreads), 0, stream, codes, stride, scales,
-                       (int)n, (int)k, x, (int)m, y);
-  else
-    hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, 64, 64>), grid, dim3(kThreads), 0, stream, codes, stride, scales,
-                       (int)n, (int)k, x, (int)m, y);
+  const int ni = (int)n, ki = (int)k, mi = (int)m;
+#define TGS_TILE(BM_, BN_, KS_)                                                                           \
+  hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, BM_, BN_, KS_>), grid, dim3(kThreads * KS_), 0, stream, codes, \
+                     stride, scales, ni, ki, x, mi, y)
+  // (128-column tiles are only chosen with >= 512 tiles, so never with the K split)
+  if (bm == 128 && bn == 128) {
+    TGS_TILE(128, 128, 1);
+  } else if (bm == 128) {
+    if (ks2) TGS_TILE(128, 64, 2); else TGS_TILE(128, 64, 1);
+  } else if (bn == 128) {
+    TGS_TILE(64, 128, 1);
+  } else {
+    if (ks2) TGS_TILE(64, 64, 2); else TGS_TILE(64, 64, 1);
+  }
+#undef TGS_TILE
   return hipGetLastError();
 }
 

@@ -200,7 +200,7 @@ def _gemm(layout, t, s, xbits):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
-@pytest.mark.parametrize("n,k", [(128, 128), (300, 1024), (129, 2048), (64, 640), (70, 4352)])
+@pytest.mark.parametrize("n,k", [(128, 128), (300, 1024), (129, 2048), (64, 640), (70, 4352), (90, 2176)])
 @pytest.mark.parametrize("m", [1, 8, 16, 24, 32, 50, 128, 200])
 def test_gemm_matches_oracle(layout, n, k, m):
     t, s = make_weights(n + k + m, f"gemm{layout}", n, k, 0.4)
