@@ -171,10 +171,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
   __shared__ float lds_ref[MT * S];                                                    // [t][chunk]
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[ROT ? MT * kSliceElems : 8];  // rotated staging
 
-  // find this workgroup's job (uniform; the table lives in the kernel arguments)
-  int j = 0;
-  while (j + 1 < args.count && (int)blockIdx.x >= args.job[j + 1].block0) ++j;
-  const GemvJob& job = args.job[j];
+  const GemvJob job = gemv_job_of_block(args);  // uniform
   const int n = job.n, k = job.k, m = args.m;
   const int groups = k / 128;
   const int chunks = k / kChunkElems;
@@ -427,19 +424,17 @@ __device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& 
 
 template <int S, int G>
 __global__ __launch_bounds__(1024)
-void gemv_wave_kernel(const GemvArgs args, int rows_per_wave) {
+void gemv_wave_kernel(const GemvArgs args) {
   constexpr int kRowsPerInstr = 64 / S;
   constexpr int kRing = G;  // batches per group: 4, or 1-2 for waves of 2-4 rows
   extern __shared__ float lds_acc[];  // [slices][rows of the workgroup], only when slices > 1
 
-  int j = 0;
-  while (j + 1 < args.count && (int)blockIdx.x >= args.job[j + 1].block0) ++j;
-  const GemvJob job = args.job[j];  // a copy: the fields stay in scalar registers
+  const GemvJob job = gemv_job_of_block(args);  // a copy: the fields stay in scalar registers
   const int n = job.n, k = job.k;
   const int groups = k / 128;
   const int chunks = k / 64;
   const int slices = (chunks + S - 1) / S;  // == waves per workgroup
-  const int R = rows_per_wave;              // row slots per wave: 2 * G * (number of groups)
+  const int R = args.rows_per_wave;         // row slots per wave: 2 * G * (number of groups)
   const int batches = R / 2;
   const int rows_wg = R * kRowsPerInstr;
 
@@ -540,12 +535,13 @@ void gemv_wave_kernel(const GemvArgs args, int rows_per_wave) {
 template <int S>
 hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
   const size_t lds = slices > 1 ? (size_t)slices * rows_per_wave * (64 / S) * sizeof(float) : 0;
+  args.rows_per_wave = rows_per_wave;
   if (rows_per_wave >= 8)
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 4>), dim3(blocks), dim3(64 * slices), lds, stream, args, rows_per_wave);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 4>), dim3(blocks), dim3(64 * slices), lds, stream, args);
   else if (rows_per_wave == 4)
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 2>), dim3(blocks), dim3(64 * slices), lds, stream, args, rows_per_wave);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 2>), dim3(blocks), dim3(64 * slices), lds, stream, args);
   else
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 1>), dim3(blocks), dim3(64 * slices), lds, stream, args, rows_per_wave);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 1>), dim3(blocks), dim3(64 * slices), lds, stream, args);
   return hipGetLastError();
 }
 

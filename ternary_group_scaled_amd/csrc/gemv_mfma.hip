@@ -69,9 +69,7 @@ template <int MT, int kFB, bool ROT>
 __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
   __shared__ __attribute__((aligned(16))) _Float16 tiles[kWaves][16 * kRowPitch];
 
-  int jb = 0;
-  while (jb + 1 < args.count && (int)blockIdx.x >= args.job[jb + 1].block0) ++jb;
-  const GemvJob job = args.job[jb];
+  const GemvJob job = gemv_job_of_block(args);
   const int n = job.n, k = job.k, m = args.m;
   const int groups = k / 128;
 

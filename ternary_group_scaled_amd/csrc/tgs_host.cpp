@@ -282,6 +282,7 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
     tgs::GemvArgs args;
     std::memset(&args, 0, sizeof(args));
     args.m = (int32_t)m;
+    for (int32_t i = 0; i < tgs::kMaxJobs; ++i) args.start[i] = INT32_MAX;
     int32_t blocks = 0;
     for (int32_t j : members) {
       tgs::GemvJob& job = args.job[args.count++];
@@ -294,6 +295,7 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
       job.n = (int32_t)ws[j].n;
       job.k = (int32_t)ws[j].k;
       job.block0 = blocks;
+      args.start[args.count - 1] = blocks;
       job.row_blocks = (int32_t)((ws[j].n + plan.rows_per_block - 1) / plan.rows_per_block);
       blocks += job.row_blocks;
     }

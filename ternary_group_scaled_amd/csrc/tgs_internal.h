@@ -37,11 +37,42 @@ struct GemvJob {
   int32_t row_blocks;      // workgroups for this job
 };
 
+// Kernel argument block of a batched GEMV launch. The header comes first so that a wave can read
+// it, the start table and job 0 in one batch of scalar loads; only a workgroup of a later job
+// waits for a second load (its job's fields).
 struct GemvArgs {
-  GemvJob job[kMaxJobs];
   int32_t count;
   int32_t m;
+  int32_t rows_per_wave;     // single-token kernel only
+  int32_t reserved;
+  int32_t start[kMaxJobs];   // == job[i].block0 for i < count; INT32_MAX past the last job
+  GemvJob job[kMaxJobs];
 };
+
+// The job of this workgroup: the last one whose first workgroup is at or before blockIdx.x.
+__device__ __forceinline__ GemvJob gemv_job_of_block(const GemvArgs& a) {
+  const int b = (int)blockIdx.x;
+  GemvJob job = a.job[0];
+  // job 0 is read with the start table, before the search (not as a select of two addresses)
+  __asm__ volatile("" ::"s"(job.codes), "s"(job.scales), "s"(job.x), "s"(job.signs), "s"(job.y), "s"(job.stride),
+                   "s"(job.n), "s"(job.k), "s"(job.block0));
+  // starts increase and are >= 1 past job 0: start - 1 - b is negative exactly when b >= start
+  int32_t st[kMaxJobs];
+#pragma unroll
+  for (int i = 1; i < kMaxJobs; ++i) st[i] = a.start[i];
+  // the whole table, and the header, in the same batch of loads
+  __asm__ volatile("" ::"s"(a.m), "s"(a.rows_per_wave), "s"(st[1]), "s"(st[2]), "s"(st[3]), "s"(st[4]), "s"(st[5]),
+                   "s"(st[6]), "s"(st[7]), "s"(st[8]), "s"(st[9]), "s"(st[10]), "s"(st[11]), "s"(st[12]), "s"(st[13]),
+                   "s"(st[14]), "s"(st[15]), "s"(st[16]));
+  __asm__ volatile("" ::"s"(st[17]), "s"(st[18]), "s"(st[19]), "s"(st[20]), "s"(st[21]), "s"(st[22]), "s"(st[23]),
+                   "s"(st[24]), "s"(st[25]), "s"(st[26]), "s"(st[27]), "s"(st[28]), "s"(st[29]), "s"(st[30]),
+                   "s"(st[31]));
+  uint32_t j = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxJobs; ++i) j += (uint32_t)(st[i] - 1 - b) >> 31;
+  if (j != 0) job = a.job[j];
+  return job;
+}
 
 // Shape class of a GEMV launch: every job in one launch shares these.
 struct GemvPlan {
