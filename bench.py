@@ -109,8 +109,8 @@ def time_graph(torch, fn, steps, warmup):
     return start.elapsed_time(stop) / steps, graph
 
 
-KERNEL_SOURCES = ["ternary_group_scaled_amd/csrc/gemv.hip", "ternary_group_scaled_amd/csrc/tgs_internal.h",
-                  "ternary_group_scaled_amd/csrc/tgs_host.cpp"]
+KERNEL_SOURCES = ["ternary_group_scaled_amd/csrc/gemv.hip", "ternary_group_scaled_amd/csrc/lane_ops.h",
+                  "ternary_group_scaled_amd/csrc/tgs_internal.h", "ternary_group_scaled_amd/csrc/tgs_host.cpp"]
 
 
 def kernel_source_sha():

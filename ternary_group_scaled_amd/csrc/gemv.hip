@@ -38,6 +38,7 @@
 //
 // Scales are applied in fp32 per chunk; partial sums are reduced across the S lanes of a row in
 // a fixed order: results are identical run to run.
+#include "lane_ops.h"
 #include "tgs_internal.h"
 
 namespace tgs {
@@ -361,27 +362,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
 //   4. each batch is reduced across its lanes right away (lane-half swaps and DPP rotations, no
 //      LDS). With one slice the sums go straight to y; otherwise each wave writes its slice sums
 //      to LDS and, after one barrier, every row adds its slices in a fixed order.
-// 32-bit lane moves within 16-lane rows (DPP): rotate right by N, or fixed quad/half patterns
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-constexpr int kDppRor1 = 0x121, kDppRor2 = 0x122, kDppRor4 = 0x124, kDppRor8 = 0x128;
-constexpr int kDppHalfMirror = 0x141, kDppQuadSwap2 = 0x4E, kDppQuadSwap1 = 0xB1;
 
 // Sum of v0 over the S lanes of each row group goes to the group's lanes holding slot 0, and of
 // v1 to those holding slot 1. Returns the sum this lane holds and sets `slot` to which one it is.
-// Lane-half swaps of gfx950, as inline asm: with the swap builtins, an expression that uses both
-// results reads the first one twice (seen in the assembly of this file), so the operands are
-// passed read-write here. Each s_nop 1 gives the two wait states a VALU write needs before a
-// swap reads the register, and the same after, before the next VALU reads the result.
-__device__ __forceinline__ void swap_halves32(float& a, float& b) {  // a's lanes 32..63 <-> b's 0..31
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap_rows16(float& a, float& b) {  // a's odd 16-lane rows <-> b's even
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-
 template <int S>
 __device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& slot) {
   if constexpr (S == 64) {

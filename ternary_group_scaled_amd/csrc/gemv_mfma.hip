@@ -26,6 +26,9 @@
 //     bytes past the row) multiply zero, and every MFMA step stays within one scale group.
 //   - Each group's 16 x 16 partial is scaled by its fp16 scale in fp32 and added to the running
 //     sum; at the end the 8 waves' sums are added through LDS in wave order (deterministic).
+#include <type_traits>
+
+#include "lane_ops.h"
 #include "tgs_internal.h"
 
 namespace tgs {
@@ -68,6 +71,10 @@ __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both 
 template <int MT, int kFB, bool ROT>
 __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
   __shared__ __attribute__((aligned(16))) _Float16 tiles[kWaves][16 * kRowPitch];
+  // byte offsets of tile slots for each start digit off0 (0..4): the group's 128 activations in
+  // K order, then the 32 window positions outside the group
+  __shared__ __attribute__((aligned(16))) uint16_t slot_tab[5][128];
+  __shared__ __attribute__((aligned(16))) uint16_t zero_tab[5][32];
 
   const GemvJob job = gemv_job_of_block(args);
   const int n = job.n, k = job.k, m = args.m;
@@ -78,9 +85,21 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   const int n_base = ((int)blockIdx.x - job.block0) * 16 * kFB;
   const int g_begin = wave * groups / kWaves, g_end = (wave + 1) * groups / kWaves;
 
+  // activations: kL lanes per token, each with kE consecutive elements of the group
+  constexpr int kL = 64 / MT, kE = 2 * MT;
+  const int tok = lane / kL, p = lane % kL;
+
   _Float16* tile = tiles[wave];
   // rows MT..15 of the A operand stay zero; rows < MT are rewritten for every group
   for (int i = lane; i < 16 * kRowPitch / 8; i += 64) reinterpret_cast<uint4*>(tile)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < 5 * 160; i += kWaves * 64) {
+    const int o = i / 160, e = i - 160 * o;
+    if (e < 128)
+      slot_tab[o][e] = (uint16_t)(2 * tile_slot(o + e));
+    else  // rel in [0, o) and [o + 128, 160)
+      zero_tab[o][e - 128] = (uint16_t)(2 * tile_slot(e - 128 < o ? e - 128 : e));
+  }
+  __syncthreads();
 
   // reads past each buffer return zero: rows >= n, tokens >= m (their outputs are not stored)
   const __amdgpu_buffer_rsrc_t code_rsrc =
@@ -102,10 +121,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   }
 
   struct Stage {
-    uint32_t c[kFB][3];  // three aligned dwords of codes per row block
-    uint32_t s[kFB];     // raw fp16 scale bits
-    uint32_t x[MT][2];   // raw fp16 activation bits: elements lane and lane + 64 of the block
-    uint32_t sg[2];      // sign bytes of those elements
+    uint32_t c[kFB][3];          // three aligned dwords of codes per row block
+    uint32_t s[kFB];             // raw fp16 scale bits
+    uint32_t x[MT];              // this lane's kE fp16 activations, in pairs
+    uint32_t sg[(kE + 3) / 4];   // their sign bytes
   };
   auto load = [&](Stage& st, int g) {
     const bool live = g < g_end;
@@ -120,17 +139,41 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       st.s[fb] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, live ? (int)(scale_row[fb] + 2u * g) : kOobOffset,
                                                      0, 0);
     }
+    const int xo = live ? (tok * k + 128 * g + kE * p) * 2 : kOobOffset;
+    if constexpr (MT == 8) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo, 0, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo + 16, 0, 0);
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = 128 * g + lane + 64 * h;
-        st.x[t][h] = __builtin_amdgcn_raw_buffer_load_b16(x_rsrc, live ? (int)((t * k + e) * 2) : kOobOffset, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        st.x[i] = a[i];
+        st.x[4 + i] = b[i];
       }
-    if (ROT) {
+    } else if constexpr (MT == 4) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo, 0, 0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        st.sg[h] = __builtin_amdgcn_raw_buffer_load_b8(sign_rsrc, live ? 128 * g + lane + 64 * h : kOobOffset, 0, 0);
+      for (int i = 0; i < 4; ++i) st.x[i] = a[i];
+    } else if constexpr (MT == 2) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b64(x_rsrc, xo, 0, 0);
+      st.x[0] = a[0];
+      st.x[1] = a[1];
+    } else {
+      st.x[0] = __builtin_amdgcn_raw_buffer_load_b32(x_rsrc, xo, 0, 0);
+    }
+    if constexpr (ROT) {
+      const int so = live ? 128 * g + kE * p : kOobOffset;
+      if constexpr (MT == 8) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(sign_rsrc, so, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.sg[i] = a[i];
+      } else if constexpr (MT == 4) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b64(sign_rsrc, so, 0, 0);
+        st.sg[0] = a[0];
+        st.sg[1] = a[1];
+      } else if constexpr (MT == 2) {
+        st.sg[0] = __builtin_amdgcn_raw_buffer_load_b32(sign_rsrc, so, 0, 0);
+      } else {
+        st.sg[0] = __builtin_amdgcn_raw_buffer_load_b16(sign_rsrc, so, 0, 0);
+      }
     }
   };
 
@@ -138,40 +181,87 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
 #pragma unroll
   for (int fb = 0; fb < kFB; ++fb) acc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  char* row_bytes = reinterpret_cast<char*>(tile + tok * kRowPitch);
   auto compute = [&](const Stage& st, int g) {
     const int off0 = 128 * g - 5 * ((128 * g) / 5);  // digit of byte B0 where the group starts
     const uint32_t sh = (uint32_t)(((128 * g) / 5 + 8 * kq) & 3);
-    // activations of this group -> tile rows 0..MT-1, in the weight operand's slot order
-    const int slot_a = tile_slot(lane + off0), slot_b = tile_slot(lane + 64 + off0);
-    const int slot_z = tile_slot(lane < off0 ? lane : 128 + lane);  // lanes < 32: slots outside the group
-    float sgn0 = 1.f, sgn1 = 1.f;
-    if (ROT) {
-      sgn0 = (int8_t)(st.sg[0] & 0xFFu) < 0 ? -1.f : 1.f;
-      sgn1 = (int8_t)(st.sg[1] & 0xFFu) < 0 ? -1.f : 1.f;
+    // this lane's slots: kE consecutive entries of the table row for off0
+    uint16_t slot[kE];
+    {
+      const uint16_t* src = &slot_tab[off0][kE * p];
+      if constexpr (kE >= 8) {
+#pragma unroll
+        for (int h = 0; h < kE / 8; ++h) {
+          const uint4 q = reinterpret_cast<const uint4*>(src)[h];
+          const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            slot[8 * h + 2 * i] = (uint16_t)w[i];
+            slot[8 * h + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+          }
+        }
+      } else if constexpr (kE == 4) {
+        const uint2 q = *reinterpret_cast<const uint2*>(src);
+        slot[0] = (uint16_t)q.x;
+        slot[1] = (uint16_t)(q.x >> 16);
+        slot[2] = (uint16_t)q.y;
+        slot[3] = (uint16_t)(q.y >> 16);
+      } else {
+        const uint32_t q = *reinterpret_cast<const uint32_t*>(src);
+        slot[0] = (uint16_t)q;
+        slot[1] = (uint16_t)(q >> 16);
+      }
+    }
+    // activations of this group -> tile row tok, in the weight operand's slot order; for rotated
+    // weights: sign flip (on the fp16 sign bits), the natural-order Sylvester butterfly over the
+    // 128-block in fp32 (strides below kE inside the lane, the rest across lanes), 1/sqrt(128),
+    // one rounding to fp16
+    float v[kE];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      uint32_t xd = st.x[i];
+      if constexpr (ROT) {
+        // sign bytes of elements 2i and 2i + 1 -> bits 15 and 31
+        const uint32_t sel = (i & 1) ? 0x030C020Cu : 0x010C000Cu;
+        xd ^= __builtin_amdgcn_perm(0u, st.sg[i >> 1], sel) & 0x80008000u;
+      }
+      v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)xd);
+      v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(xd >> 16));
+    }
+    if constexpr (ROT) {
+#pragma unroll
+      for (int h = 1; h < kE; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < kE; ++i)
+          if ((i & h) == 0) {
+            const float a = v[i], b = v[i + h];
+            v[i] = a + b;
+            v[i + h] = a - b;
+          }
+      auto cross = [&](auto s_tag) {
+        constexpr int S = decltype(s_tag)::value;
+        const float sgn = (p & S) ? -1.f : 1.f;  // the upper lane of a pair keeps partner - own
+#pragma unroll
+        for (int i = 0; i < kE; ++i) v[i] = fmaf(v[i], sgn, xor_lane<S>(v[i], lane));
+      };
+      if constexpr (kL > 1) cross(std::integral_constant<int, 1>{});
+      if constexpr (kL > 2) cross(std::integral_constant<int, 2>{});
+      if constexpr (kL > 4) cross(std::integral_constant<int, 4>{});
+      if constexpr (kL > 8) cross(std::integral_constant<int, 8>{});
+      if constexpr (kL > 16) cross(std::integral_constant<int, 16>{});
+      if constexpr (kL > 32) cross(std::integral_constant<int, 32>{});
+#pragma unroll
+      for (int i = 0; i < kE; ++i) v[i] *= 0.08838834764831845f;  // 1/sqrt(128)
     }
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)st.x[t][0]);
-      float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)st.x[t][1]);
-      if (ROT) {
-        v0 *= sgn0;
-        v1 *= sgn1;
-        const float a = v0 + v1, b = v0 - v1;  // the stride-64 stage, inside the lane
-        v0 = a;
-        v1 = b;
+    for (int i = 0; i < kE; ++i) *reinterpret_cast<_Float16*>(row_bytes + slot[i]) = (_Float16)v[i];
+    // the 32 window slots outside the group meet zeros
+    if constexpr (kL <= 32) {
+      constexpr int kZ = 32 / kL;
 #pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) {
-          const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-          const bool upper = (lane & s) != 0;
-          v0 = upper ? (p0 - v0) : (v0 + p0);
-          v1 = upper ? (p1 - v1) : (v1 + p1);
-        }
-        v0 *= 0.08838834764831845f;  // 1/sqrt(128)
-        v1 *= 0.08838834764831845f;
-      }
-      tile[t * kRowPitch + slot_a] = (_Float16)v0;
-      tile[t * kRowPitch + slot_b] = (_Float16)v1;
-      if (lane < 32) tile[t * kRowPitch + slot_z] = (_Float16)0.f;
+      for (int z = 0; z < kZ; ++z) *reinterpret_cast<_Float16*>(row_bytes + zero_tab[off0][kZ * p + z]) = (_Float16)0.f;
+    } else {
+      if (p < 32) *reinterpret_cast<_Float16*>(row_bytes + zero_tab[off0][p]) = (_Float16)0.f;
     }
     __asm__ volatile("" ::: "memory");  // the tile writes precede the fragment reads (one wave, in order)
 
