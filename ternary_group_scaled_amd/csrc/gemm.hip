@@ -280,9 +280,9 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_SLOT2 ? 2 : 1, 8))) void
 // per group. Within each 16 consecutive k, both operands use the order 0,8,1,9,...,7,15 of the
 // slot-2 decode, so the contraction is unchanged. Each group's partial is scaled in fp32; the W
 // per-wave results are added through LDS in wave order (deterministic, no atomics).
-// Every workgroup reads all of x for its outputs, so x traffic from L2 falls as FB grows: the
-// few-row case uses FB = 4 and keeps the kernel within 128 VGPRs (two stages), so that 16 waves
-// fit on a CU, rather than shrinking FB to get more workgroups.
+// Every workgroup reads all of x for its outputs, so x traffic from L2 falls as FB grows. The
+// host picks FB so that a launch is about one workgroup per CU (one round of workgroups) rather
+// than shrinking FB to get more workgroups.
 
 // pairs 4H..4H+3 of decode16_slot2(u): bf16(2t_i) in the low half, bf16(2t_{i+8}) in the high half
 template <int H>
@@ -462,14 +462,23 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
   if (LAYOUT == TGS_LAYOUT_SLOT2 && m <= 32) {
     const int ni = (int)n, ki = (int)k, mi = (int)m;
     if (m <= 16) {
-      // 64 outputs per workgroup; 16 K slices when that gives too few workgroups to fill the chip
-      const dim3 grid((unsigned)((n + 63) / 64));
-      if ((n + 63) / 64 >= 256)
-        hipLaunchKernelGGL((gemm_skinny_kernel<1, 4, 8, 2>), grid, dim3(512), 0, stream, codes, stride, scales, ni,
-                           ki, x, mi, y);
-      else
-        hipLaunchKernelGGL((gemm_skinny_kernel<1, 4, 16, 2>), grid, dim3(1024), 0, stream, codes, stride, scales, ni,
-                           ki, x, mi, y);
+      // 16 * FB outputs per workgroup of 8 waves, FB = n / 4096 rounded up, within 2..6: about one
+      // workgroup per CU (the kernel's registers allow one), and every workgroup reads all of x,
+      // so its L2 traffic falls as FB grows. (Measured on 17408 x 5120 and 5120 x 17408: FB = 5
+      // and 2 beat both neighbours and the 16-wave variants.)
+      const int64_t fb = std::min<int64_t>(6, std::max<int64_t>(2, (n + 4095) / 4096));
+      const dim3 grid((unsigned)((n + 16 * fb - 1) / (16 * fb)));
+#define TGS_SKINNY(FB_)                                                                                          \
+  hipLaunchKernelGGL((gemm_skinny_kernel<1, FB_, 8, 2>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki, \
+                     x, mi, y)
+      switch (fb) {
+        case 2: TGS_SKINNY(2); break;
+        case 3: TGS_SKINNY(3); break;
+        case 4: TGS_SKINNY(4); break;
+        case 5: TGS_SKINNY(5); break;
+        default: TGS_SKINNY(6); break;
+      }
+#undef TGS_SKINNY
     } else {
       // 16 outputs per block: the most (4, 2, 1) that still gives 512 workgroups
       const int64_t fb = (n + 63) / 64 >= 512 ? 4 : ((n + 31) / 32 >= 512 ? 2 : 1);
