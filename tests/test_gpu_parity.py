@@ -210,10 +210,11 @@ def test_gemm_matches_oracle(layout, n, k, m):
     assert_within_bound(y, y_ref, bound, f"gemm {LNAME[layout]} {n}x{k} m={m}")
 
 
-@pytest.mark.parametrize("n", [17000, 33000])
-@pytest.mark.parametrize("m", [5, 20])
+@pytest.mark.parametrize("n", [4100, 9000, 13000, 17000, 33000])
+@pytest.mark.parametrize("m", [5, 16, 20])
 def test_gemm_wide_matrices(n, m):
-    """Wide matrices take the few-row product with 2 or 4 output blocks per workgroup."""
+    """Wide matrices take the few-row product: up to 16 rows with 2..6 output blocks per
+    workgroup (n / 4096 rounded up), 17..32 rows with 1, 2 or 4."""
     k = 384
     t, s = make_weights(n + m, "gemmwide", n, k, 0.4)
     xb = make_x_bf16_bits(m, f"gemmwide{n}", m, k)
