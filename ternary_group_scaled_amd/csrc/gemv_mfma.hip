@@ -39,10 +39,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;       // K slices per workgroup
-// 16-row blocks per workgroup: 1 for a single token (more workgroups for the small launches of a
-// decode step; measured best), 4 for several tokens (the decode and rotation are shared by more
-// rows)
+// 16-row blocks per workgroup, measured best: 1 for a single token (more workgroups for the small
+// launches of a decode step), 2 for several tokens (the 27B rotated set with 8 tokens: 618 GB/s,
+// against 477 with 1 and 490 with 4)
 constexpr int kMfmaFB1 = 1;
+constexpr int kMfmaFBMulti = 2;
 constexpr int kRowPitch = 168;  // halves per token row of the activation tile: 160 slots + 8 (bank spread)
 
 // window position rel (0..159) of a group's trit -> its slot in the [q][j][8] tile
@@ -317,6 +318,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   // add the waves' sums in wave order
   __syncthreads();
   float* red = reinterpret_cast<float*>(&tiles[0][0]);  // [wave][fb * 4 + r][lane]
+  static_assert(kWaves * kFB * 4 * 64 * sizeof(float) <= sizeof(tiles), "the wave sums fit in the tiles");
 #pragma unroll
   for (int fb = 0; fb < kFB; ++fb)
 #pragma unroll
@@ -344,13 +346,13 @@ hipError_t launch_mt(GemvArgs& args, int blocks, bool rotated, hipStream_t strea
 
 }  // namespace
 
-int gemv_b3_mfma_rows(int32_t m) { return m == 1 ? 16 * kMfmaFB1 : 64; }
+int gemv_b3_mfma_rows(int32_t m) { return 16 * (m == 1 ? kMfmaFB1 : kMfmaFBMulti); }
 
 hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, bool rotated, hipStream_t stream) {
   if (m <= 1) return launch_mt<1, kMfmaFB1>(args, blocks, rotated, stream);
-  if (m <= 2) return launch_mt<2, 4>(args, blocks, rotated, stream);
-  if (m <= 4) return launch_mt<4, 4>(args, blocks, rotated, stream);
-  return launch_mt<8, 4>(args, blocks, rotated, stream);
+  if (m <= 2) return launch_mt<2, kMfmaFBMulti>(args, blocks, rotated, stream);
+  if (m <= 4) return launch_mt<4, kMfmaFBMulti>(args, blocks, rotated, stream);
+  return launch_mt<8, kMfmaFBMulti>(args, blocks, rotated, stream);
 }
 
 }  // namespace tgs
