@@ -71,6 +71,8 @@ def _load():
         lib.orc_rotate_f64.restype = None
         lib.orc_matmul_f64.argtypes = [i32, vp, i64, vp, i64, i64, vp, i32, i64, vp, vp, i64, vp, vp]
         lib.orc_matmul_f64.restype = ctypes.c_int
+        lib.orc_code_flips.argtypes = [i32, vp, i64, vp, i64, i64, i64, vp]
+        lib.orc_code_flips.restype = i64
         _lib = lib
     return _lib
 
@@ -167,3 +169,20 @@ def matmul(layout: int, codes: np.ndarray, scales: np.ndarray, k: int, x_bits: n
                                 y.ctypes.data, bound.ctypes.data)
     _check(rc, "matmul")
     return y, bound
+
+
+def code_flips(layout: int, codes_a: np.ndarray, codes_b: np.ndarray, k: int):
+    """Code flips between two packed matrices: (total, per-row counts int64 [n]).
+
+    codes_a, codes_b: uint8 [n][stride_a], [n][stride_b] of the same layout and k.
+    """
+    a = np.ascontiguousarray(codes_a, dtype=np.uint8)
+    b = np.ascontiguousarray(codes_b, dtype=np.uint8)
+    n = a.shape[0]
+    assert b.shape[0] == n
+    counts = np.zeros(n, dtype=np.int64)
+    total = _load().orc_code_flips(layout, a.ctypes.data, a.shape[1], b.ctypes.data, b.shape[1], n, k,
+                                   counts.ctypes.data)
+    if total < 0:
+        raise OracleError(f"code_flips: oracle status {total}")
+    return int(total), counts

@@ -280,3 +280,46 @@ int orc_matmul_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
   free(xr);
   return status;
 }
+
+/* ---- code flips between two packed checkpoints ---- */
+
+/*
+ * A code flip is a weight whose ternary code changed between two checkpoints, for
+ * example 0 -> +1 or +1 -> -1; it is the only way training changes what the model
+ * computes, as opposed to nudging the shared scales ("Fine-tuning the ternary
+ * Bonsai-8B on Metal" (molayo1419.me), opening section on native-ternary models;
+ * the closing advice counts the flips per checkpoint).
+ *
+ * counts[r] = #{ c < k : t_a[r][c] != t_b[r][c] } for two matrices of the same
+ * layout and shape, each row unpacked with the bit-by-bit loops above. Rows are
+ * row_stride_a / row_stride_b bytes apart; bytes past the row's codes are not read
+ * as codes. Returns the total, or a negative status.
+ */
+int64_t orc_code_flips(int32_t layout, const uint8_t* a, int64_t row_stride_a, const uint8_t* b,
+                       int64_t row_stride_b, int64_t n, int64_t k, int64_t* counts) {
+  if (k <= 0 || k % 128 != 0 || n < 0) return ORC_BAD_SHAPE;
+  if (orc_row_bytes(layout, k) == 0) return ORC_BAD_LAYOUT;
+  if (row_stride_a < orc_row_bytes(layout, k) || row_stride_b < orc_row_bytes(layout, k)) return ORC_BAD_SHAPE;
+  int64_t total = 0;
+  int status = ORC_OK;
+#pragma omp parallel reduction(+ : total)
+  {
+    int8_t* ta = (int8_t*)malloc((size_t)k);
+    int8_t* tb = (int8_t*)malloc((size_t)k);
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t r = 0; r < n; ++r) {
+      if (unpack_row(layout, a + r * row_stride_a, k, ta) != ORC_OK ||
+          unpack_row(layout, b + r * row_stride_b, k, tb) != ORC_OK) {
+        status = ORC_BAD_CODE;
+        continue;
+      }
+      int64_t c = 0;
+      for (int64_t i = 0; i < k; ++i) c += ta[i] != tb[i];
+      if (counts) counts[r] = c;
+      total += c;
+    }
+    free(ta);
+    free(tb);
+  }
+  return status == ORC_OK ? total : status;
+}

@@ -28,6 +28,9 @@ MUTANTS = {
     "f16_exponent_bias": ("v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
     "f16_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     "bf16_mantissa_width": ("v = ldexp((double)(128 + m), e - 134);", "v = ldexp((double)(256 + m), e - 135);"),
+    "flips_dropped_last_trit": ("for (int64_t i = 0; i < k; ++i) c += ta[i] != tb[i];",
+                                "for (int64_t i = 0; i + 1 < k; ++i) c += ta[i] != tb[i];"),
+    "flips_row_stride": ("unpack_row(layout, b + r * row_stride_b, k, tb)", "unpack_row(layout, b + r * row_stride_a, k, tb)"),
 }
 
 

@@ -6,6 +6,7 @@ matmul), closed forms of the group-scaled product, exhaustive enumeration and br
 on tiny shapes. Citations name the page and section whose definition each check follows:
   P3 = "Ternary Bonsai 2 27B, 5.93GB ... (feat. PrismML)" (discuss.pytorch.kr)
   P2 = "Bonsai 27B and how 1-bit survives" (velog.io)
+  P1 = "Fine-tuning the ternary Bonsai-8B on Metal" (molayo1419.me)
 """
 import math
 import os
@@ -422,3 +423,63 @@ def test_golden_small_product():
     for layout in (oracle.SLOT2, oracle.BASE3):
         y, _ = oracle.matmul(layout, oracle.pack(layout, t), s, k, x.view(np.uint16), oracle.X_F16)
         assert (y[0] == expect).all()
+
+
+# ---------------------------------------------------------------- code flips (P1, opening section)
+# A code flip is a weight whose code changed between two checkpoints. The pins plant flips at
+# positions the test chooses and compare with that known count, so a count of changed bytes or
+# of changed words instead of changed trits, or a dropped position, fails.
+
+
+def _flipped(t, rng, frac):
+    """t with a random set of positions changed to another trit; returns (u, planted mask)."""
+    mask = rng.random(t.shape) < frac
+    step = rng.integers(1, 3, size=t.shape)  # +1 or +2 modulo 3: always a different trit
+    u = t.copy()
+    u[mask] = ((t[mask].astype(np.int64) + 1 + step[mask]) % 3 - 1).astype(np.int8)
+    return u, mask
+
+
+@pytest.mark.parametrize("layout", [oracle.SLOT2, oracle.BASE3])
+@pytest.mark.parametrize("k", [128, 640, 4096])
+def test_code_flips_count_the_planted_positions(layout, k):
+    rng = np.random.default_rng(k + layout)
+    n = 37
+    t = synth.trits(11, k, (n, k), 0.4)
+    u, mask = _flipped(t, rng, 0.03)
+    a, b = oracle.pack(layout, t), oracle.pack(layout, u)
+    total, rows = oracle.code_flips(layout, a, b, k)
+    assert total == int(mask.sum())
+    assert (rows == mask.sum(axis=1)).all()
+
+
+@pytest.mark.parametrize("layout", [oracle.SLOT2, oracle.BASE3])
+def test_code_flips_extremes_and_symmetry(layout):
+    k, n = 384, 9
+    t = synth.trits(12, 3, (n, k), 0.4)
+    a = oracle.pack(layout, t)
+    assert oracle.code_flips(layout, a, a, k)[0] == 0
+    every = ((t.astype(np.int64) + 2) % 3 - 1).astype(np.int8)  # each trit moved to another value
+    assert oracle.code_flips(layout, a, oracle.pack(layout, every), k)[0] == n * k
+    rng = np.random.default_rng(5)
+    u, _ = _flipped(t, rng, 0.1)
+    v, _ = _flipped(u, rng, 0.1)
+    b, c = oracle.pack(layout, u), oracle.pack(layout, v)
+    ab, ba = oracle.code_flips(layout, a, b, k)[0], oracle.code_flips(layout, b, a, k)[0]
+    assert ab == ba
+    assert oracle.code_flips(layout, a, c, k)[0] <= ab + oracle.code_flips(layout, b, c, k)[0]
+
+
+def test_code_flips_do_not_depend_on_the_layout_or_the_row_padding():
+    k, n = 1280, 21
+    t = synth.trits(13, 4, (n, k), 0.5)
+    u, mask = _flipped(t, np.random.default_rng(9), 0.02)
+    counts = []
+    for layout in (oracle.SLOT2, oracle.BASE3):
+        a, b = oracle.pack(layout, t), oracle.pack(layout, u)
+        # wider rows on one side, with bytes past the codes that differ from the other side
+        wide = np.full((n, a.shape[1] + 48), 0xFF, dtype=np.uint8)
+        wide[:, :a.shape[1]] = a
+        counts.append(oracle.code_flips(layout, wide, b, k))
+    assert counts[0][0] == counts[1][0] == int(mask.sum())
+    assert (counts[0][1] == counts[1][1]).all()
