@@ -17,7 +17,7 @@ to back). Its `traffic` is the HBM bytes per launch that rocprofv3 counters meas
 same command, read from profiles/ only while the kernel sources still match the ones profiled.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
 
-Other workloads (`--workload base3|gemm|rotated|config1`) print lines of their own; they are
+Other workloads (`--workload base3|gemm|rotated|flips|config1`) print lines of their own; they are
 measurements for the design notes, not the headline.
 """
 from __future__ import annotations
@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8b", choices=["8b", "base3", "rotated", "gemm", "config1"])
+    ap.add_argument("--workload", default="8b", choices=["8b", "base3", "rotated", "gemm", "flips", "config1"])
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the set (default: 36 for the 8B-class sets, 64 for the rotated 27B-class set)")
     ap.add_argument("--mode", default="layer", choices=["layer", "fused-layer", "set"],
@@ -212,12 +212,9 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
     per_launch_bytes = total_bytes / n_launches
     per_launch_s = ms * 1e-3 / n_launches
     kernel_gbs = per_launch_bytes / per_launch_s / 1e9
-    kernel = "gemv_wave_kernel" if layout == 1 else "gemv_kernel"
+    kernel = "gemv_wave_kernel" if layout == 1 else "gemv_b3_mfma_kernel"
     profile = f"{kernel}.8b_{'slot2' if layout == 1 else 'base3'}_m1_{args.mode}.pmc.txt"
     traffic = measured_traffic(profile)
-
-    # parity spot check of layer 0 against the oracle on sampled rows
-    check_layer0(torch, host, inputs[0], outputs[0], layout)
 
     result = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -239,43 +236,36 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
                      "traffic_profile": profile if traffic is not None else None},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_8b(host, layout, args.cpu_seconds, ms, total_bytes / layers, layers)
+        result["cpu_baseline"] = cpu_baseline_8b(torch, host, inputs[0], outputs[0], layout, args.cpu_seconds, ms,
+                                                 total_bytes / layers, layers)
     return result
 
 
-def check_layer0(torch, host, xs, ys, layout):
+def cpu_baseline_8b(torch, host, xs, ys, layout, seconds, gpu_ms, layer_bytes, layers):
+    """The fp64 oracle on the host cores over layer 0's 7 matrices, with the inputs the GPU pass
+    used, repeated for ~`seconds`. Its first pass is also compared with the GPU's layer-0 outputs
+    (every row, within the tolerance bound)."""
     import oracle
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    worst = 0.0
-    for name, codes, scales, n, k in host:
-        grp = [g for g in GROUPS_8B if name in g][0]
-        x16 = xs[grp][1]
-        rows = np.sort(rng.choice(n, size=min(n, 64), replace=False))
-        y_ref, bound = oracle.matmul(layout, codes, scales, k, x16.view(np.uint16), oracle.X_F16, rows=rows)
-        y = ys[name].cpu().numpy()[:, rows].astype(np.float64)
-        ratio = float((np.abs(y - y_ref) / bound).max())
-        worst = max(worst, ratio)
-        if not ratio <= 1.0:  # NaN fails too
-            raise SystemExit(f"parity check failed for layer 0 {name}: max err/bound {ratio:.3g}")
-    log(f"[bench] layer-0 sampled parity ok (max err/bound {worst:.3g})")
-
-
-def cpu_baseline_8b(host, layout, seconds, gpu_ms, layer_bytes, layers):
-    """The fp64 oracle on the host cores over layer-0's 7 matrices, repeated for ~`seconds`."""
-    import oracle
-    import synth
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    xs = {name: synth.x_f16(1, synth.stream_id("cpu", name), (1, k)) for name, _, _, _, k in host}
+    torch.cuda.synchronize()
+    y_gpu = {name: ys[name].cpu().numpy().astype(np.float64) for name, _, _, _, _ in host}
+    x_of = {name: xs[[g for g in GROUPS_8B if name in g][0]][1] for name, _, _, _, _ in host}
+    worst = 0.0
     t0 = time.time()
     passes = 0
     while True:
         for name, codes, scales, n, k in host:
-            oracle.matmul(layout, codes, scales, k, xs[name].view(np.uint16), oracle.X_F16)
+            y_ref, bound = oracle.matmul(layout, codes, scales, k, x_of[name].view(np.uint16), oracle.X_F16)
+            if passes == 0:
+                ratio = float((np.abs(y_gpu[name] - y_ref) / bound).max())
+                if not ratio <= 1.0:  # NaN fails too
+                    raise SystemExit(f"parity check failed for layer 0 {name}: max err/bound {ratio:.3g}")
+                worst = max(worst, ratio)
         passes += 1
         if time.time() - t0 >= seconds:
             break
     dt = (time.time() - t0) / passes
+    log(f"[bench] layer-0 parity against the oracle ok (max err/bound {worst:.3g})")
     layer_gbs = layer_bytes / dt / 1e9
     return {"value": round(layer_gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"layer 0 of the set (7 matrices, {int(layer_bytes)} algorithmic bytes), {passes} passes in "
@@ -358,6 +348,99 @@ def bench_gemm(args, torch, tgs, synth):
     return res
 
 
+def bench_flips(args, torch, tgs, synth):
+    """Code flips between two checkpoints of the 8B-class set (every matrix of 36 layers), one line
+    per layout: the second checkpoint is the first with 0.7% of its codes changed (the rate the
+    fine-tuning page reports for its best run). Up to 32 pairs per launch."""
+    res = []
+    layers = args.layers or 36
+    for layout, p_zero, lname in ((1, 0.4, "2-bit-slot"), (2, 0.5, "base-3")):
+        t0 = time.time()
+        pairs, host0, planted = [], [], 0
+        for L in range(layers):
+            for nm, n, k in LAYER_8B:
+                tag = f"flips{layout}/L{L}/{nm}"
+                t = synth.trits(0, synth.stream_id(tag, "codes"), (n, k), p_zero)
+                # positions to change: nonzero draws of a second stream, P = 0.007; each moves to
+                # the next trit value, so every drawn position is a flip
+                sel = synth.trits(0, synth.stream_id(tag, "flips"), (n, k), 0.993) != 0
+                u = np.where(sel, ((t.astype(np.int16) + 2) % 3 - 1).astype(np.int8), t)
+                planted += int(sel.sum())
+                s = synth.scales_f16(0, synth.stream_id(tag, "scales"), (n, k // 128))
+                ca, sc = tgs.pack_ternary(layout, t, s)
+                cb, _ = tgs.pack_ternary(layout, u, s)
+                sd = torch.from_numpy(sc.view(np.int16)).cuda()
+                a = tgs.PackedMatrix(layout, torch.from_numpy(ca).cuda(), sd, k)
+                b = tgs.PackedMatrix(layout, torch.from_numpy(cb).cuda(), sd, k)
+                pairs.append((a, b))
+                if L == 0:
+                    host0.append((nm, ca, cb, k))
+        totals = [torch.zeros(1, dtype=torch.int64, device="cuda") for _ in pairs]
+        rows = [torch.empty(a.n, dtype=torch.int32, device="cuda") for a, _ in pairs]
+        torch.cuda.synchronize()
+        log(f"[bench] flips ({lname}): built {len(pairs)} pairs in {time.time() - t0:.1f}s")
+        launches = []
+        for i in range(0, len(pairs), tgs.MAX_BATCH):
+            sl = slice(i, i + tgs.MAX_BATCH)
+            launches.append((lambda p, t, r: lambda: tgs.ternary_code_flips_batched(p, t, r))(pairs[sl], totals[sl],
+                                                                                          rows[sl]))
+
+        def one_pass():
+            for fn in launches:
+                fn()
+
+        ms, _graph = time_graph(torch, one_pass, args.steps, args.warmup)
+        del _graph
+        counted = sum(int(t.item()) for t in totals)
+        if counted != planted:
+            raise SystemExit(f"code flips: counted {counted}, planted {planted}")
+        code_bytes = sum(a.codes.numel() + b.codes.numel() for a, b in pairs)
+        out_bytes = sum(r.numel() * 4 for r in rows)
+        gbs = (code_bytes + out_bytes) / (ms * 1e-3) / 1e9
+        log(f"[bench] flips ({lname}): step {ms * 1e3:.1f} us -> {gbs:.0f} GB/s, {counted} flips "
+            f"({100.0 * counted / sum(a.n * a.k for a, _ in pairs):.3f}% of codes)")
+        line = {"metric": "ternary code flips between two checkpoints, achieved HBM GB/s", "value": round(gbs, 1),
+                "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+                "higher_is_better": True, "dtype": "u8", "data": "synthetic",
+                "config": {"workload": f"8B-class set, two checkpoints, {lname} layout, 0.7% of codes changed",
+                           "layers": layers, "pairs": len(pairs), "launches_per_step": len(launches),
+                           "bytes_per_step": int(code_bytes + out_bytes), "flips": counted},
+                "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                "roofline": {"bound": "hbm" if layout == 1 else "alu", "achieved": round(gbs, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "kernel": "code_flip_kernel"}}
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_flips(torch, host0, rows[:len(host0)], layout, args.cpu_seconds,
+                                                      ms, len(pairs))
+        res.append(line)
+        del pairs, totals, rows, launches
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_flips(torch, host0, rows0, layout, seconds, gpu_ms, n_pairs):
+    """The oracle's code-flip count over layer 0's 7 pairs, repeated for ~`seconds`; its first pass
+    is also compared with the GPU's per-row counts of those pairs."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    gpu_rows = [r.cpu().numpy().astype(np.int64) for r in rows0]
+    t0 = time.time()
+    passes, nbytes = 0, sum(ca.nbytes + cb.nbytes for _, ca, cb, _ in host0)
+    while True:
+        for i, (nm, ca, cb, k) in enumerate(host0):
+            _, ref_rows = oracle.code_flips(layout, ca, cb, k)
+            if passes == 0 and not (ref_rows == gpu_rows[i]).all():
+                raise SystemExit(f"code flips of layer 0 {nm} differ from the oracle")
+        passes += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = (time.time() - t0) / passes
+    log("[bench] layer-0 code flips equal the oracle's")
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 of the set (7 pairs, {nbytes} code bytes), {passes} passes in {time.time() - t0:.1f}s",
+            "gpu_speedup": round((dt * n_pairs / len(host0)) / (gpu_ms * 1e-3), 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -386,6 +469,8 @@ def main():
         out = bench_rotated(args, torch, tgs, synth)
     elif args.workload == "gemm":
         out = bench_gemm(args, torch, tgs, synth)
+    elif args.workload == "flips":
+        out = bench_flips(args, torch, tgs, synth)
     else:
         args.layers = 1
         out = [bench_8b(args, torch, tgs, synth)]

@@ -188,6 +188,33 @@ tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int
 tgs_status hadamard_rotate_g128(const void* x, int32_t x_dtype, int64_t m, int64_t k,
                                 const int8_t* signs, void* y, int32_t y_dtype, void* stream);
 
+/*
+ * ternary_code_flips (device): how many weights changed code between two packed matrices of the
+ * same layout, shape and basis, per row and in total. A code flip is a weight whose ternary code
+ * changes between checkpoints, e.g. 0 -> +1 or +1 -> -1: the only way training changes what a
+ * native-ternary model computes, as opposed to nudging the shared scales ([P1] opening section;
+ * its closing advice is to record the flips of every checkpoint).
+ *   a, b        descriptors (host memory) of device-resident codes: same layout, rotated, n and k;
+ *               the row strides may differ. Scales are not read.
+ *   row_counts  device [n] uint32, 4-byte aligned, or NULL: flips of each row
+ *   total       device uint64, 8-byte aligned, or NULL: flips of the whole matrix
+ *               (at least one of row_counts and total is required)
+ * The codes must be valid (unpack_ternary would accept them): pad trits and pad bytes are
+ * compared as stored, and are equal in valid matrices. Counts are exact integers, identical run
+ * to run. Both code planes are read once (the call is bound by HBM bandwidth for slot-2).
+ */
+tgs_status ternary_code_flips(const tgs_matrix* a, const tgs_matrix* b, uint32_t* row_counts, uint64_t* total,
+                              void* stream);
+
+/*
+ * ternary_code_flips_batched (device): count pairs (1..TGS_MAX_BATCH) of one layout in one
+ * launch (plus a small one that clears the totals). as and bs are host arrays of count
+ * descriptors; row_counts and totals are host arrays of count device pointers (either array,
+ * or entries of it, may be NULL as above, but every pair needs one of the two).
+ */
+tgs_status ternary_code_flips_batched(const tgs_matrix* as, const tgs_matrix* bs, int32_t count,
+                                      uint32_t* const* row_counts, uint64_t* const* totals, void* stream);
+
 /* Static text for a status code. */
 const char* tgs_status_string(tgs_status status);
 

@@ -59,8 +59,11 @@ _lib.ternary_gemv_batched.argtypes = [ctypes.POINTER(Matrix), _i32, ctypes.POINT
                                       ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]
 _lib.ternary_gemm.argtypes = [ctypes.POINTER(Matrix), _vp, _i32, _i64, _vp, _vp, _vp]
 _lib.hadamard_rotate_g128.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]
+_lib.ternary_code_flips.argtypes = [ctypes.POINTER(Matrix), ctypes.POINTER(Matrix), _vp, _vp, _vp]
+_lib.ternary_code_flips_batched.argtypes = [ctypes.POINTER(Matrix), ctypes.POINTER(Matrix), _i32,
+                                            ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]
 for _name in ("tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv", "ternary_gemv_batched",
-              "ternary_gemm", "hadamard_rotate_g128"):
+              "ternary_gemm", "hadamard_rotate_g128", "ternary_code_flips", "ternary_code_flips_batched"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.tgs_status_string.argtypes = [ctypes.c_int]
 _lib.tgs_status_string.restype = ctypes.c_char_p
@@ -68,7 +71,8 @@ _lib.tgs_last_error.argtypes = []
 _lib.tgs_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("tgs_code_row_bytes", "tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv",
-           "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "tgs_status_string", "tgs_last_error")
+           "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "ternary_code_flips",
+           "ternary_code_flips_batched", "tgs_status_string", "tgs_last_error")
 
 
 def _check(status: int):
@@ -214,3 +218,29 @@ def hadamard_rotate_g128(x, signs, y=None, out_dtype=None, stream=None):
     _check(_lib.hadamard_rotate_g128(x2.data_ptr(), dt[x2.dtype], x2.shape[0], k, signs.data_ptr(), y.data_ptr(),
                                      dt[y.dtype], _stream_handle(stream)))
     return y
+
+
+def ternary_code_flips(a: PackedMatrix, b: PackedMatrix, rows=True, total=True, stream=None):
+    """Code flips between two packed matrices on the GPU: (total uint64 [1] or None,
+    per-row counts int32 [n] holding uint32 values, or None)."""
+    torch = _torch()
+    dev = a.codes.device
+    r = torch.empty(a.n, dtype=torch.int32, device=dev) if rows else None
+    t = torch.empty(1, dtype=torch.int64, device=dev) if total else None
+    _check(_lib.ternary_code_flips(ctypes.byref(a.desc), ctypes.byref(b.desc), r.data_ptr() if r is not None else None,
+                                   t.data_ptr() if t is not None else None, _stream_handle(stream)))
+    return t, r
+
+
+def ternary_code_flips_batched(pairs, totals, rows=None, stream=None):
+    """Code flips of several pairs (a, b) of one layout in one launch. totals: int64 [1] tensors
+    (or None entries); rows: int32 [n] tensors (or None entries), or None."""
+    count = len(pairs)
+    da = (Matrix * count)(*[a.desc for a, _ in pairs])
+    db = (Matrix * count)(*[b.desc for _, b in pairs])
+    tp = (_vp * count)(*[t.data_ptr() if t is not None else None for t in totals])
+    rp = None
+    if rows is not None:
+        rp = (_vp * count)(*[r.data_ptr() if r is not None else None for r in rows])
+    _check(_lib.ternary_code_flips_batched(da, db, count, rp, tp, _stream_handle(stream)))
+    return totals, rows

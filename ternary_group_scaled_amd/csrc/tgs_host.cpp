@@ -305,6 +305,59 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
   return ok();
 }
 
+tgs_status ternary_code_flips_batched(const tgs_matrix* as, const tgs_matrix* bs, int32_t count,
+                                     uint32_t* const* row_counts, uint64_t* const* totals, void* stream) {
+  if (!as || !bs) return fail(TGS_E_NULL, "descriptor array is NULL");
+  if (!row_counts && !totals) return fail(TGS_E_NULL, "neither per-row counts nor totals requested");
+  if (count < 1 || count > TGS_MAX_BATCH) return fail(TGS_E_SHAPE, "count must be 1..%d, got %d", TGS_MAX_BATCH, count);
+  for (int32_t i = 0; i < count; ++i) {
+    tgs_status st = check_matrix(&as[i], true);
+    if (st != TGS_OK) return st;
+    st = check_matrix(&bs[i], true);
+    if (st != TGS_OK) return st;
+    if (as[i].layout != bs[i].layout || as[i].n != bs[i].n || as[i].k != bs[i].k)
+      return fail(TGS_E_SHAPE, "pair %d: the two matrices differ in layout or shape", i);
+    if (as[i].rotated != bs[i].rotated)
+      return fail(TGS_E_BASIS, "pair %d: one matrix is in the rotated basis and the other is not", i);
+    if (as[i].layout != as[0].layout) return fail(TGS_E_LAYOUT, "all pairs of one call must share a layout");
+    uint32_t* rc = row_counts ? row_counts[i] : nullptr;
+    uint64_t* tot = totals ? totals[i] : nullptr;
+    if (!rc && !tot) return fail(TGS_E_NULL, "pair %d: neither a per-row count nor a total requested", i);
+    if (rc && !aligned(rc, 4)) return fail(TGS_E_ALIGN, "row counts must be 4-byte aligned");
+    if (tot && !aligned(tot, 8)) return fail(TGS_E_ALIGN, "totals must be 8-byte aligned");
+  }
+  tgs::FlipArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.count = count;
+  args.layout = as[0].layout;
+  const int rows_per_block = tgs::code_flip_rows_per_block();
+  int32_t blocks = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    tgs::FlipJob& job = args.job[i];
+    job.a = static_cast<const uint8_t*>(as[i].codes);
+    job.b = static_cast<const uint8_t*>(bs[i].codes);
+    job.rows = row_counts ? row_counts[i] : nullptr;
+    job.total = totals ? totals[i] : nullptr;
+    job.stride_a = as[i].code_row_stride;
+    job.stride_b = bs[i].code_row_stride;
+    job.n = (int32_t)as[i].n;
+    job.row_bytes = (int32_t)row_bytes(as[i].layout, as[i].k);
+    job.block0 = blocks;
+    blocks += (int32_t)((as[i].n + rows_per_block - 1) / rows_per_block);
+  }
+  hipError_t e = tgs::code_flip_launch(args, blocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "ternary_code_flips launch");
+  return ok();
+}
+
+tgs_status ternary_code_flips(const tgs_matrix* a, const tgs_matrix* b, uint32_t* row_counts, uint64_t* total,
+                              void* stream) {
+  if (!a || !b) return fail(TGS_E_NULL, "matrix descriptor is NULL");
+  uint32_t* rcs[1] = {row_counts};
+  uint64_t* tots[1] = {total};
+  return ternary_code_flips_batched(a, b, 1, rcs, tots, stream);
+}
+
 tgs_status ternary_gemv(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m, const int8_t* signs, float* y,
                         void* stream) {
   const void* xs[1] = {x};

@@ -97,6 +97,29 @@ hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hip
 int gemv_b3_mfma_rows(int32_t m);
 hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, bool rotated, hipStream_t stream);
 
+// Code flips: one pair of matrices of a batched launch (device pointers).
+struct FlipJob {
+  const uint8_t* a;
+  const uint8_t* b;
+  uint32_t* rows;   // [n] or nullptr
+  uint64_t* total;  // one counter or nullptr
+  int64_t stride_a;
+  int64_t stride_b;
+  int32_t n;
+  int32_t row_bytes;  // minimum row length of the layout: the bytes compared
+  int32_t block0;     // first workgroup of this pair in the launch
+  int32_t reserved;
+};
+
+struct FlipArgs {
+  FlipJob job[kMaxJobs];
+  int32_t count;
+  int32_t layout;
+};
+
+int code_flip_rows_per_block();
+hipError_t code_flip_launch(FlipArgs& args, int32_t blocks, hipStream_t stream);
+
 hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
                        const uint16_t* x_bf16, int64_t m, float* y, hipStream_t stream);
 

@@ -258,3 +258,83 @@ def test_gemm_integer_inputs_are_exact_and_match_gemv():
     y_ref, _ = oracle_product(tgs.SLOT2, t, s, xi.astype(np.float16).view(np.uint16), oracle.X_F16)
     assert (y_gemm.astype(np.float64) == y_ref).all()
     assert (y_gemm.view(np.uint32) == y_gemv.view(np.uint32)).all()
+
+
+# ------------------------------------------------------------------------------ code flips
+
+def _flip_pair(layout, n, k, frac, seed, pad=0):
+    """Two packed checkpoints: t and t with a seeded fraction of trits changed. Returns
+    (PackedMatrix a, PackedMatrix b, codes_a, codes_b)."""
+    t = synth.trits(seed, n * 7 + k, (n, k), 0.4)
+    rng = np.random.default_rng(seed)
+    mask = rng.random((n, k)) < frac
+    step = rng.integers(1, 3, size=(n, k))
+    u = t.copy()
+    u[mask] = ((t[mask].astype(np.int64) + 1 + step[mask]) % 3 - 1).astype(np.int8)
+    s = synth.scales_f16(seed, 5, (n, k // 128))
+    ca, _ = tgs.pack_ternary(layout, t, s)
+    cb, _ = tgs.pack_ternary(layout, u, s)
+    if pad:  # a wider row stride for the first matrix, with garbage past its codes
+        wide = np.full((n, ca.shape[1] + pad), 0xEE, dtype=np.uint8)
+        wide[:, :ca.shape[1]] = ca
+        ca = wide
+    sd = torch.from_numpy(s.view(np.int16)).to(DEV)
+    a = tgs.PackedMatrix(layout, torch.from_numpy(ca).to(DEV), sd, k)
+    b = tgs.PackedMatrix(layout, torch.from_numpy(cb).to(DEV), sd, k)
+    return a, b, ca, cb
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+@pytest.mark.parametrize("n,k,frac", [(1, 128, 0.5), (17, 384, 0.05), (300, 1280, 0.007), (33, 4096, 0.1),
+                                      (129, 12288, 0.003), (5, 17408, 0.02)])
+def test_code_flips_match_oracle(layout, n, k, frac):
+    a, b, ca, cb = _flip_pair(layout, n, k, frac, seed=n + k)
+    total, rows = tgs.ternary_code_flips(a, b)
+    torch.cuda.synchronize()
+    ref_total, ref_rows = oracle.code_flips(layout, ca, cb, k)
+    assert int(total.item()) == ref_total
+    assert (rows.cpu().numpy().astype(np.int64) == ref_rows).all()
+    total2, rows2 = tgs.ternary_code_flips(a, b)
+    assert int(total2.item()) == ref_total and torch.equal(rows, rows2)  # identical run to run
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+def test_code_flips_extremes_strides_and_outputs(layout):
+    n, k = 70, 640
+    a, _, ca, _ = _flip_pair(layout, n, k, 0.0, seed=3, pad=48)
+    t = tgs.unpack_ternary(layout, ca[:, :tgs.code_row_bytes(layout, k)], np.zeros((n, k // 128), np.float16), k)[0]
+    every = ((t.astype(np.int64) + 2) % 3 - 1).astype(np.int8)
+    cb = tgs.pack_ternary(layout, every, None)[0]
+    b = tgs.PackedMatrix(layout, torch.from_numpy(cb).to(DEV), a.scales, k)
+    assert int(tgs.ternary_code_flips(a, a)[0].item()) == 0
+    total, rows = tgs.ternary_code_flips(a, b)
+    assert int(total.item()) == n * k and (rows.cpu().numpy() == k).all()
+    # only a total, only rows
+    t_only, none_rows = tgs.ternary_code_flips(a, b, rows=False)
+    none_total, r_only = tgs.ternary_code_flips(a, b, total=False)
+    assert none_rows is None and none_total is None
+    assert int(t_only.item()) == n * k and (r_only.cpu().numpy() == k).all()
+
+
+def test_code_flips_batched_equals_single_calls():
+    pairs, refs = [], []
+    for i, (n, k) in enumerate([(40, 1024), (300, 4096), (7, 12288)]):
+        a, b, ca, cb = _flip_pair(tgs.SLOT2, n, k, 0.01 * (i + 1), seed=20 + i)
+        pairs.append((a, b))
+        refs.append(oracle.code_flips(tgs.SLOT2, ca, cb, k))
+    totals = [torch.empty(1, dtype=torch.int64, device=DEV) for _ in pairs]
+    rows = [torch.empty(a.n, dtype=torch.int32, device=DEV) for a, _ in pairs]
+    tgs.ternary_code_flips_batched(pairs, totals, rows)
+    torch.cuda.synchronize()
+    for t, r, (ref_t, ref_r) in zip(totals, rows, refs):
+        assert int(t.item()) == ref_t
+        assert (r.cpu().numpy().astype(np.int64) == ref_r).all()
+
+
+def test_code_flips_full_size_matrix():
+    """A 12288 x 4096 gate/up-sized matrix at the 0.7% flip rate the fine-tuning page reports."""
+    a, b, ca, cb = _flip_pair(tgs.SLOT2, 12288, 4096, 0.007, seed=77)
+    total, rows = tgs.ternary_code_flips(a, b)
+    ref_total, ref_rows = oracle.code_flips(tgs.SLOT2, ca, cb, 4096)
+    assert int(total.item()) == ref_total
+    assert (rows.cpu().numpy().astype(np.int64) == ref_rows).all()

@@ -162,6 +162,35 @@ def test_device_call_argument_checks_happen_before_any_device_work():
     assert lib.ternary_gemv_batched(ms, 33, xp, tgs.F16, 1, None, yp, None) == 2
 
 
+def test_code_flip_argument_checks_happen_before_any_device_work():
+    lib = tgs.lib()
+    a, b = _fake_matrix(), _fake_matrix()
+    flips = lambda x, y, rows=0x600000, total=0x700000: lib.ternary_code_flips(ctypes.byref(x), ctypes.byref(y),
+                                                                                rows, total, None)
+    assert flips(a, b, rows=None, total=None) == 1         # nothing requested
+    assert flips(a, b, rows=0x600002) == 3                 # row counts 4-byte aligned
+    assert flips(a, b, total=0x700004) == 3                # total 8-byte aligned
+    other = _fake_matrix()
+    other.k = 384
+    other.code_row_stride = 96
+    assert flips(a, other) == 2                            # shapes differ
+    other = _fake_matrix()
+    other.layout = tgs.BASE3
+    other.code_row_stride = 64
+    assert flips(a, other) == 2                            # layouts differ
+    assert flips(a, _fake_matrix(rotated=1)) == 6          # bases differ
+    bad = _fake_matrix()
+    bad.magic = 0
+    assert flips(bad, b) == 5
+    ms = (tgs.Matrix * 2)(_fake_matrix(), _fake_matrix())
+    tp = (ctypes.c_void_p * 2)(0x700000, 0x700008)
+    assert lib.ternary_code_flips_batched(ms, ms, 0, None, tp, None) == 2
+    assert lib.ternary_code_flips_batched(ms, ms, 33, None, tp, None) == 2
+    assert lib.ternary_code_flips_batched(ms, ms, 2, None, None, None) == 1
+    tp_gap = (ctypes.c_void_p * 2)(0x700000, None)
+    assert lib.ternary_code_flips_batched(ms, ms, 2, None, tp_gap, None) == 1  # pair 1 requests nothing
+
+
 def test_matrix_init_rejects_bad_shapes():
     m = tgs.Matrix()
     assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 0, 0, 128, 1, 1) == 2
