@@ -67,9 +67,9 @@ def _load():
             f.restype = ctypes.c_int
         lib.orc_hadamard.argtypes = [i32, vp]
         lib.orc_hadamard.restype = None
-        lib.orc_rotate_f64.argtypes = [vp, vp, i64, i64, vp]
+        lib.orc_rotate_f64.argtypes = [vp, vp, i64, i64, i64, vp]
         lib.orc_rotate_f64.restype = None
-        lib.orc_matmul_f64.argtypes = [i32, vp, i64, vp, i64, i64, vp, i32, i64, vp, vp, i64, vp, vp]
+        lib.orc_matmul_f64.argtypes = [i32, vp, i64, vp, i64, i64, vp, i32, i64, vp, i64, vp, i64, vp, vp]
         lib.orc_matmul_f64.restype = ctypes.c_int
         lib.orc_code_flips.argtypes = [i32, vp, i64, vp, i64, i64, i64, vp]
         lib.orc_code_flips.restype = i64
@@ -125,26 +125,27 @@ def hadamard(n: int = 128) -> np.ndarray:
     return h
 
 
-def rotate(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
-    """x float64 [m][k] (or [k]) -> R x per 128-block, float64."""
+def rotate(x: np.ndarray, signs: np.ndarray, block: int = 128) -> np.ndarray:
+    """x float64 [m][k] (or [k]) -> R x per block of `block` (128 or 1024) elements, float64."""
     xd = np.ascontiguousarray(x, dtype=np.float64)
     shape = xd.shape
     xd = xd.reshape(-1, shape[-1])
     m, k = xd.shape
     s = np.ascontiguousarray(signs, dtype=np.int8)
-    assert s.shape == (k,) and k % 128 == 0
+    assert s.shape == (k,) and block in (128, 1024) and k % block == 0
     out = np.zeros_like(xd)
-    _load().orc_rotate_f64(xd.ctypes.data, s.ctypes.data, m, k, out.ctypes.data)
+    _load().orc_rotate_f64(xd.ctypes.data, s.ctypes.data, m, k, block, out.ctypes.data)
     return out.reshape(shape)
 
 
 def matmul(layout: int, codes: np.ndarray, scales: np.ndarray, k: int, x_bits: np.ndarray,
-           x_dtype: int, signs: np.ndarray | None = None, rows: np.ndarray | None = None):
+           x_dtype: int, signs: np.ndarray | None = None, rows: np.ndarray | None = None, block: int = 128):
     """Reference product. Returns (y, bound), both float64 [m][n_sel].
 
     codes uint8 [n][stride]; scales fp16 (float16 or uint16 bits) [n][k/128];
     x_bits uint16 bit patterns [m][k] (fp16 or bf16 per x_dtype); signs int8 [k] or None;
-    rows: int64 row indices to evaluate, or None for all rows.
+    rows: int64 row indices to evaluate, or None for all rows; block: rotation block (128 or
+    1024) when signs are given.
     """
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     n, stride = c.shape
@@ -165,7 +166,7 @@ def matmul(layout: int, codes: np.ndarray, scales: np.ndarray, k: int, x_bits: n
     y = np.zeros((m, n_sel), dtype=np.float64)
     bound = np.zeros((m, n_sel), dtype=np.float64)
     rc = _load().orc_matmul_f64(layout, c.ctypes.data, stride, s.ctypes.data, n, k, xb.ctypes.data,
-                                x_dtype, m, sg.ctypes.data if sg is not None else None, r_ptr, n_sel,
+                                x_dtype, m, sg.ctypes.data if sg is not None else None, block, r_ptr, n_sel,
                                 y.ctypes.data, bound.ctypes.data)
     _check(rc, "matmul")
     return y, bound

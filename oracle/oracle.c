@@ -19,14 +19,16 @@
  *     "Bonsai 27B and how 1-bit survives" (velog.io), section "What the format is".
  *   - The rotation R = (1/sqrt(n)) H_n S with S a fixed +-1 diagonal, and the
  *     layer computing f(x) = W(Rx): same P3 page, subsection "Block-wise
- *     Hadamard rotation". Here n = 128 (one block per scale group) and H is
- *     the natural-order Sylvester matrix H[i][j] = (-1)^popcount(i & j), the
- *     normalised Sylvester transform the WebGPU loader insists on (P3 page,
- *     section "Running in the browser with WebGPU").
+ *     Hadamard rotation". The block size n is 128 (one block per scale group)
+ *     or 1024 (the size that subsection names; a block then spans 8 groups),
+ *     and H is the natural-order Sylvester matrix H[i][j] =
+ *     (-1)^popcount(i & j), the normalised Sylvester transform the WebGPU
+ *     loader insists on (P3 page, section "Running in the browser with
+ *     WebGPU").
  *
  * Every step is done the obvious way: each row is unpacked from its packed
  * bytes by a bit-by-bit loop, dequantised to doubles (fp16/bf16 -> double is
- * exact), and multiplied; the rotation is a dense 128x128 matrix-vector
+ * exact), and multiplied; the rotation is a dense n x n matrix-vector
  * product per block, not a fast transform. Threads split rows only; the
  * arithmetic for each output is a plain sequential sum over k.
  *
@@ -195,22 +197,24 @@ void orc_hadamard(int32_t n, int8_t* h) {
       h[(int64_t)i * n + j] = (int8_t)((popcount32((uint32_t)(i & j)) & 1) ? -1 : 1);
 }
 
-/* xr[m][k] = sum_j H[i][j] * sign[b*128+j] * x[m][b*128+j] / sqrt(128), k = b*128 + i */
-void orc_rotate_f64(const double* x, const int8_t* sign, int64_t m, int64_t k, double* xr) {
-  int8_t h[128 * 128];
-  orc_hadamard(128, h);
-  const double norm = sqrt(128.0);
+/* xr[m][k] = sum_j H[i][j] * sign[b*n+j] * x[m][b*n+j] / sqrt(n), k = b*n + i, for blocks of
+   n = 128 or 1024 (k a multiple of n): a dense n x n product per block */
+void orc_rotate_f64(const double* x, const int8_t* sign, int64_t m, int64_t k, int64_t n, double* xr) {
+  int8_t* h = (int8_t*)malloc((size_t)(n * n));
+  orc_hadamard((int32_t)n, h);
+  const double norm = sqrt((double)n);
   for (int64_t r = 0; r < m; ++r) {
-    for (int64_t b = 0; b < k / 128; ++b) {
-      const double* xb = x + r * k + b * 128;
-      const int8_t* sb = sign + b * 128;
-      for (int i = 0; i < 128; ++i) {
+    for (int64_t b = 0; b < k / n; ++b) {
+      const double* xb = x + r * k + b * n;
+      const int8_t* sb = sign + b * n;
+      for (int64_t i = 0; i < n; ++i) {
         double acc = 0.0;
-        for (int j = 0; j < 128; ++j) acc += (double)h[i * 128 + j] * ((double)sb[j] * xb[j]);
-        xr[r * k + b * 128 + i] = acc / norm;
+        for (int64_t j = 0; j < n; ++j) acc += (double)h[i * n + j] * ((double)sb[j] * xb[j]);
+        xr[r * k + b * n + i] = acc / norm;
       }
     }
   }
+  free(h);
 }
 
 /* activation bits -> doubles */
@@ -234,9 +238,11 @@ int orc_load_x(const uint16_t* x, int32_t x_dtype, int64_t count, double* out) {
 int orc_matmul_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
                    const uint16_t* scales, int64_t n, int64_t k,
                    const uint16_t* x, int32_t x_dtype, int64_t m,
-                   const int8_t* sign, const int64_t* rows, int64_t n_sel,
+                   const int8_t* sign, int64_t block, const int64_t* rows, int64_t n_sel,
                    double* y, double* bound) {
   if (k <= 0 || k % 128 != 0 || m < 1 || n < 0) return ORC_BAD_SHAPE;
+  if (sign && (block != 128 && block != 1024)) return ORC_BAD_SHAPE;
+  if (sign && k % block != 0) return ORC_BAD_SHAPE;
   if (orc_row_bytes(layout, k) == 0) return ORC_BAD_LAYOUT;
   if (row_stride < orc_row_bytes(layout, k)) return ORC_BAD_SHAPE;
   if (rows == NULL && n_sel != n) return ORC_BAD_SHAPE;
@@ -246,7 +252,7 @@ int orc_matmul_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
   if (!xd || !xr) { free(xd); free(xr); return ORC_BAD_SHAPE; }
   int rc = orc_load_x(x, x_dtype, m * k, xd);
   if (rc == ORC_OK) {
-    if (sign) orc_rotate_f64(xd, sign, m, k, xr);
+    if (sign) orc_rotate_f64(xd, sign, m, k, block, xr);
     else memcpy(xr, xd, sizeof(double) * (size_t)(m * k));
   }
   free(xd);

@@ -21,13 +21,14 @@ MUTANTS = {
     "base3_pad_value": ("int digit = 1; /* trit 0", "int digit = 0; /* trit 0"),
     "scale_group_index": ("scales[r * (k / 128) + c / 128]", "scales[r * (k / 128) + (c / 128 + 1) % (k / 128)]"),
     "rotation_sign_side": ("((double)sb[j] * xb[j])", "((double)sb[i] * xb[j])"),
-    "rotation_norm": ("xr[r * k + b * 128 + i] = acc / norm;", "xr[r * k + b * 128 + i] = acc / 128.0;"),
-    "rotation_hadamard_index": ("(double)h[i * 128 + j]", "(double)h[i * 128 + ((j + 1) & 127)]"),
+    "rotation_norm": ("xr[r * k + b * n + i] = acc / norm;", "xr[r * k + b * n + i] = acc / (double)n;"),
+    "rotation_hadamard_index": ("(double)h[i * n + j]", "(double)h[i * n + ((j + 1) & (n - 1))]"),
     "dropped_last_term": ("for (int64_t c = 0; c < k; ++c) {\n          double p", "for (int64_t c = 0; c + 1 < k; ++c) {\n          double p"),
     "bound_without_abs": ("mag += fabs(p);", "mag += p;"),
     "f16_exponent_bias": ("v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
     "f16_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     "bf16_mantissa_width": ("v = ldexp((double)(128 + m), e - 134);", "v = ldexp((double)(256 + m), e - 135);"),
+    "rotation_block_ignored": ("orc_rotate_f64(xd, sign, m, k, block, xr);", "orc_rotate_f64(xd, sign, m, k, 128, xr);"),
     "flips_dropped_last_trit": ("for (int64_t i = 0; i < k; ++i) c += ta[i] != tb[i];",
                                 "for (int64_t i = 0; i + 1 < k; ++i) c += ta[i] != tb[i];"),
     "flips_row_stride": ("unpack_row(layout, b + r * row_stride_b, k, tb)", "unpack_row(layout, b + r * row_stride_a, k, tb)"),

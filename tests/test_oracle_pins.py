@@ -219,7 +219,7 @@ def test_published_file_sizes_fit_34_bytes_per_group():
 # ---------------------------------------------------------------- Hadamard and rotation (P3 "Block-wise Hadamard rotation")
 
 def test_hadamard_is_sylvester():
-    for n in (1, 2, 4, 8, 16, 32, 64, 128):
+    for n in (1, 2, 4, 8, 16, 32, 64, 128, 1024):
         h = oracle.hadamard(n).astype(np.int64)
         assert (h == scipy.linalg.hadamard(n)).all()
         assert (h @ h.T == n * np.eye(n, dtype=np.int64)).all()
@@ -229,43 +229,57 @@ def test_hadamard_is_sylvester():
             assert (h == np.block([[half, half], [half, -half]])).all()
 
 
-def _dense_rotation(signs):
+def _dense_rotation(signs, block=128):
     k = signs.size
-    h = scipy.linalg.hadamard(128).astype(np.float64) / math.sqrt(128)
+    h = scipy.linalg.hadamard(block).astype(np.float64) / math.sqrt(block)
     r = np.zeros((k, k))
-    for b in range(k // 128):
-        sl = slice(b * 128, (b + 1) * 128)
+    for b in range(k // block):
+        sl = slice(b * block, (b + 1) * block)
         r[sl, sl] = h * signs[sl].astype(np.float64)[None, :]  # H S: sign on the input side
     return r
 
 
-def test_rotation_matches_dense_block_matrix():
-    k = 512
+@pytest.mark.parametrize("block,k", [(128, 512), (1024, 2048)])
+def test_rotation_matches_dense_block_matrix(block, k):
     sg = synth.signs(0, 1, k)
     x = synth.normal(0, 2, (3, k))
-    got = oracle.rotate(x, sg)
-    ref = x @ _dense_rotation(sg).T
-    assert np.abs(got - ref).max() < 1e-13
+    got = oracle.rotate(x, sg, block)
+    ref = x @ _dense_rotation(sg, block).T
+    assert np.abs(got - ref).max() < 1e-12
 
 
-def test_rotation_is_orthogonal():
-    k = 256
+@pytest.mark.parametrize("block,k", [(128, 256), (1024, 1024)])
+def test_rotation_is_orthogonal(block, k):
     sg = synth.signs(5, 1, k)
-    rcols = oracle.rotate(np.eye(k), sg)  # row i = R e_i = column i of R
+    rcols = oracle.rotate(np.eye(k), sg, block)  # row i = R e_i = column i of R
     r = rcols.T
-    assert np.abs(r.T @ r - np.eye(k)).max() < 1e-14
+    assert np.abs(r.T @ r - np.eye(k)).max() < 1e-13
     x = synth.normal(1, 3, (4, k))
-    assert np.allclose(np.linalg.norm(oracle.rotate(x, sg), axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    assert np.allclose(np.linalg.norm(oracle.rotate(x, sg, block), axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
 
 
-def test_rotation_of_one_hot():
-    k = 128
+@pytest.mark.parametrize("block", [128, 1024])
+def test_rotation_of_one_hot(block):
+    k = block
     sg = synth.signs(7, 1, k)
-    h = scipy.linalg.hadamard(128)
-    for j in (0, 1, 77, 127):
+    h = scipy.linalg.hadamard(block)
+    for j in (0, 1, 77, block - 1):
         e = np.zeros(k)
         e[j] = 1.0
-        assert np.allclose(oracle.rotate(e, sg), sg[j] * h[:, j] / math.sqrt(128), atol=1e-15)
+        assert np.allclose(oracle.rotate(e, sg, block), sg[j] * h[:, j] / math.sqrt(block), atol=1e-15)
+
+
+def test_1024_block_is_the_kronecker_product_of_8_and_128():
+    # natural-order Sylvester: H_1024 = H_8 (x) H_128, so one 1024-block rotation equals the
+    # 128-block rotations of its 8 groups followed by an 8-point transform across the groups
+    k = 2048
+    sg = synth.signs(9, 2, k)
+    x = synth.normal(9, 3, (2, k))
+    small = oracle.rotate(x, sg, 128).reshape(2, k // 1024, 8, 128) * math.sqrt(128)
+    h8 = scipy.linalg.hadamard(8).astype(np.float64)
+    mixed = np.einsum("ij,rbjc->rbic", h8, small).reshape(2, k) / math.sqrt(1024)
+    assert np.abs(mixed - oracle.rotate(x, sg, 1024)).max() < 1e-12
+    assert np.abs(mixed - oracle.rotate(x, sg, 128)).max() > 1e-3  # and the two block sizes differ
 
 
 def test_rotation_identities():
@@ -345,14 +359,16 @@ def test_bf16_activations():
 
 
 @pytest.mark.parametrize("layout", [oracle.SLOT2, oracle.BASE3])
-def test_rotated_product_brute_force(layout):
-    k, m = 256, 2
+@pytest.mark.parametrize("block,k", [(128, 256), (1024, 1024)])
+def test_rotated_product_brute_force(layout, block, k):
+    m = 2
     t = synth.trits(8, 1, (3, k), 0.5)
-    s = synth.scales_f16(8, 2, (3, 2))
+    s = synth.scales_f16(8, 2, (3, k // 128))
     x16 = synth.x_f16(8, 3, (m, k))
     sg = synth.signs(8, 4, k)
-    y, bound = oracle.matmul(layout, oracle.pack(layout, t), s, k, x16.view(np.uint16), oracle.X_F16, signs=sg)
-    xr = x16.astype(np.float64) @ _dense_rotation(sg).T
+    y, bound = oracle.matmul(layout, oracle.pack(layout, t), s, k, x16.view(np.uint16), oracle.X_F16, signs=sg,
+                             block=block)
+    xr = x16.astype(np.float64) @ _dense_rotation(sg, block).T
     terms = xr[:, None, :] * _dense_weights(t, s)[None, :, :]
     assert np.allclose(y, terms.sum(axis=2), rtol=1e-12, atol=1e-15)
     assert np.allclose(bound, 1e-3 * np.abs(terms).sum(axis=2) + 1e-6, rtol=1e-12)
