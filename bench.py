@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--mode", default="layer", choices=["layer", "fused-layer", "set"],
                     help="launch grouping for the 8B set: same-input groups (144 launches), one launch per "
                          "layer (36), or the whole set in as few launches as possible")
+    ap.add_argument("--rot-block", type=int, default=128, choices=[128, 1024],
+                    help="rotation block of the rotated 27B-class set (128: one block per scale group)")
     ap.add_argument("--one-mode", action="store_true", help="time only --mode (the others are reported by default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -278,16 +280,17 @@ def cpu_baseline_8b(torch, host, xs, ys, layout, seconds, gpu_ms, layer_bytes, l
 def bench_rotated(args, torch, tgs, synth):
     """27B-class rotated-basis GEMV, base-3: gate/up 17408x5120 and down 5120x17408 per layer."""
     layers = args.layers or 64
+    block = args.rot_block
     shapes = [("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408)]
     res = []
     for m in (1, 8):
-        log(f"[bench] rotated base-3 set, {layers} layers, m={m}")
+        log(f"[bench] rotated base-3 set, {layers} layers, m={m}, rotation block {block}")
         mats, xs, ys, sg = [], [], [], {}
         for k in (5120, 17408):
             sg[k] = torch.from_numpy(synth.signs(0, synth.stream_id("rot/signs", k), k)).cuda()
         for L in range(layers):
             for name, n, k in shapes:
-                w, _, _ = build_matrix(torch, tgs, synth, 2, 0, f"rot/L{L}/{name}", n, k, 0.5, rotated=True)
+                w, _, _ = build_matrix(torch, tgs, synth, 2, 0, f"rot/L{L}/{name}", n, k, 0.5, rotated=block)
                 mats.append(w)
                 ys.append(torch.empty((m, n), dtype=torch.float32, device="cuda"))
             xg = x_f16_dev(torch, synth, 0, f"rot/L{L}/in{m}", m, 5120)[0]
@@ -311,7 +314,8 @@ def bench_rotated(args, torch, tgs, synth):
         log(f"[bench] rotated m={m}: step {ms * 1e3:.1f} us -> {nb / ms / 1e6:.0f} GB/s")
         res.append({"metric": "rotated ternary GEMV achieved GB/s, 27B-class set", "value": round(nb / ms / 1e6, 1),
                     "unit": "GB/s", "m": m, "ms_per_step": round(ms, 4), "launches_per_step": len(launches),
-                    "config": {"workload": f"27B-class rotated GEMV set, base-3, {layers} layers, M={m}",
+                    "config": {"workload": f"27B-class rotated GEMV set, base-3, {layers} layers, M={m}, "
+                                           f"rotation block {block}",
                                "bytes_per_step": int(nb)}})
         del mats, xs, ys
         torch.cuda.empty_cache()

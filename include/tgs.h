@@ -78,11 +78,13 @@ typedef enum { TGS_F16 = 1, TGS_BF16 = 2, TGS_F32 = 3 } tgs_dtype;
  * A packed weight matrix W [n][k] (n output features, k input features).
  *   magic, version  TGS_MAGIC, TGS_VERSION (tgs_matrix_init fills them)
  *   layout          a tgs_layout
- *   rotated         0: plain basis. 1: the codes are weights of the rotated basis, so the layer
- *                   computes y = W (R x), R = blockdiag_128((1/sqrt(128)) H_128 S) with H_128 the
+ *   rotated         0: plain basis. 1 or 1024: the codes are weights of the rotated basis, so the
+ *                   layer computes y = W (R x), R = blockdiag_n((1/sqrt(n)) H_n S) with H_n the
  *                   natural-order Sylvester Hadamard matrix and S = diag(signs) ([P3] section
- *                   "Block-wise Hadamard rotation": R = H_n S / sqrt(n), f(x) = W(Rx); here n = 128,
- *                   one rotation block per scale group). The packed model declares its basis and
+ *                   "Block-wise Hadamard rotation": R = H_n S / sqrt(n), f(x) = W(Rx)). 1 means
+ *                   n = 128, one rotation block per scale group; 1024 means n = 1024, the size that
+ *                   section names (a block spans 8 scale groups; k % 1024 == 0). tgs_matrix_init
+ *                   also accepts 128 and stores it as 1. The packed model declares its basis and
  *                   the runtime must either apply the transform or refuse ([P3], same section):
  *                   calls on rotated weights require signs, calls on plain weights reject them.
  *   n, k            n >= 1, k >= 128, k % 128 == 0
@@ -134,11 +136,12 @@ tgs_status unpack_ternary(const tgs_matrix* w, int8_t* trits_out, uint16_t* scal
 
 /*
  * ternary_gemv (device): y[i][j] = sum_k s[j][k/128] * t[j][k] * xr[i][k] for i < m, j < n,
- * with xr = x, or xr = R x when w->rotated (the rotation is computed inside the kernel).
+ * with xr = x, or xr = R x when w->rotated (the rotation, with the descriptor's block size, is
+ * computed inside the kernel).
  *   w       descriptor (host memory) of device-resident codes and scales
  *   x       device [m][k] activations of x_dtype; only TGS_F16 is accepted; 16-byte aligned
  *   m       1 .. TGS_MAX_M_GEMV (decode, or a small verify batch)
- *   signs   device [k] int8 in {-1, +1} when w->rotated, else NULL. Values are not checked on
+ *   signs   device [k] int8 in {-1, +1}, 16-byte aligned, when w->rotated, else NULL. Values are not checked on
  *           the device: any other value gives an unspecified result.
  *   y       device [m][n] fp32, 4-byte aligned
  *   stream  hipStream_t or NULL
@@ -214,6 +217,14 @@ tgs_status ternary_code_flips(const tgs_matrix* a, const tgs_matrix* b, uint32_t
  */
 tgs_status ternary_code_flips_batched(const tgs_matrix* as, const tgs_matrix* bs, int32_t count,
                                       uint32_t* const* row_counts, uint64_t* const* totals, void* stream);
+
+/*
+ * hadamard_rotate (device): the same rotation for blocks of `block` elements, 128 or 1024 (k a
+ * multiple of block; [P3] "Block-wise Hadamard rotation" names n = 1024). Same arguments and
+ * rules as hadamard_rotate_g128, which is this call with block = 128.
+ */
+tgs_status hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block,
+                           const int8_t* signs, void* y, int32_t y_dtype, void* stream);
 
 /* Static text for a status code. */
 const char* tgs_status_string(tgs_status status);

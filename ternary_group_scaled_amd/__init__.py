@@ -59,11 +59,13 @@ _lib.ternary_gemv_batched.argtypes = [ctypes.POINTER(Matrix), _i32, ctypes.POINT
                                       ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]
 _lib.ternary_gemm.argtypes = [ctypes.POINTER(Matrix), _vp, _i32, _i64, _vp, _vp, _vp]
 _lib.hadamard_rotate_g128.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]
+_lib.hadamard_rotate.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i32, _vp]
 _lib.ternary_code_flips.argtypes = [ctypes.POINTER(Matrix), ctypes.POINTER(Matrix), _vp, _vp, _vp]
 _lib.ternary_code_flips_batched.argtypes = [ctypes.POINTER(Matrix), ctypes.POINTER(Matrix), _i32,
                                             ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]
 for _name in ("tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv", "ternary_gemv_batched",
-              "ternary_gemm", "hadamard_rotate_g128", "ternary_code_flips", "ternary_code_flips_batched"):
+              "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
+              "ternary_code_flips_batched"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.tgs_status_string.argtypes = [ctypes.c_int]
 _lib.tgs_status_string.restype = ctypes.c_char_p
@@ -71,7 +73,7 @@ _lib.tgs_last_error.argtypes = []
 _lib.tgs_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("tgs_code_row_bytes", "tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv",
-           "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "ternary_code_flips",
+           "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
            "ternary_code_flips_batched", "tgs_status_string", "tgs_last_error")
 
 
@@ -146,7 +148,8 @@ def _stream_handle(stream) -> int | None:
 class PackedMatrix:
     """Packed ternary weights resident on the GPU: codes [n][stride] uint8, scales [n][k/128] fp16."""
 
-    def __init__(self, layout: int, codes, scales, k: int, rotated: bool = False):
+    def __init__(self, layout: int, codes, scales, k: int, rotated=False):
+        """rotated: False/0 (plain basis), True/1/128 (128-element rotation blocks) or 1024."""
         self.layout = layout
         self.codes = codes
         self.scales = scales
@@ -156,6 +159,7 @@ class PackedMatrix:
         self.desc = Matrix()
         _check(_lib.tgs_matrix_init(ctypes.byref(self.desc), layout, int(rotated), self.n, self.k,
                                     codes.data_ptr(), scales.data_ptr()))
+        self.block = 1024 if self.desc.rotated == 1024 else (128 if self.rotated else 0)
         self.desc.code_row_stride = int(codes.stride(0))
 
     @classmethod
@@ -204,6 +208,19 @@ def ternary_gemm(w: PackedMatrix, x, y=None, stream=None):
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
     _check(_lib.ternary_gemm(ctypes.byref(w.desc), x2.data_ptr(), BF16, m, None, y.data_ptr(), _stream_handle(stream)))
+    return y
+
+
+def hadamard_rotate(x, signs, block=128, y=None, out_dtype=None, stream=None):
+    """Block-wise signed Walsh-Hadamard rotation (128 or 1024 per block) of x [m][k]; fp16/fp32 output."""
+    torch = _torch()
+    dt = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    k = x.shape[-1]
+    x2 = x.reshape(-1, k)
+    if y is None:
+        y = torch.empty(x2.shape, dtype=out_dtype or torch.float32, device=x.device)
+    _check(_lib.hadamard_rotate(x2.data_ptr(), dt[x2.dtype], x2.shape[0], k, block, signs.data_ptr(), y.data_ptr(),
+                                dt[y.dtype], _stream_handle(stream)))
     return y
 
 

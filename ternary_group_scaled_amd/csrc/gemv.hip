@@ -38,6 +38,8 @@
 //
 // Scales are applied in fp32 per chunk; partial sums are reduced across the S lanes of a row in
 // a fixed order: results are identical run to run.
+#include <type_traits>
+
 #include "lane_ops.h"
 #include "tgs_internal.h"
 
@@ -116,10 +118,66 @@ __device__ __forceinline__ float chunk_dot_slot2(const uint4& cw, const uint32_t
 // Rotated basis: each wave rotates whole 128-blocks into lds_x (fp16):
 // x -> (1/sqrt(128)) H_128 diag(sign) x, H in natural Sylvester order, computed in fp32 with an
 // in-register butterfly (lane l holds elements l and l + 64), then rounded once to fp16.
-template <int MT, int WAVES>
+template <int MT, int WAVES, int BLOCK>
 __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint16_t* x, const int8_t* sign,
                                               int k, int m, int m0, int k_begin) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if constexpr (BLOCK == 1024) {
+    // 1024-element blocks (k and the slice are multiples of 1024): lane l holds elements
+    // 16 l .. 16 l + 15; four butterfly stages inside the lane, six with lane l ^ s
+    const int blocks = len / 1024;
+    for (int idx = wave; idx < MT * blocks; idx += WAVES) {
+      const int t = idx / blocks, b = idx - t * blocks;
+      const int kb = k_begin + 1024 * b + 16 * lane;
+      float v[16];
+      uint4 q[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+      uint4 sg = make_uint4(0, 0, 0, 0);
+      if (m0 + t < m && kb < k) {
+        const uint4* xb = reinterpret_cast<const uint4*>(x + (int64_t)(m0 + t) * k + kb);
+        q[0] = xb[0];
+        q[1] = xb[1];
+        sg = *reinterpret_cast<const uint4*>(sign + kb);
+      }
+      const uint32_t xw[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+      const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float xv = f16_to_f32((uint16_t)(xw[i / 2] >> (16 * (i & 1))));
+        v[i] = xv * (float)(int8_t)(sw[i / 4] >> (8 * (i & 3)));
+      }
+#pragma unroll
+      for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((i & h) == 0) {
+            const float a = v[i], c = v[i + h];
+            v[i] = a + c;
+            v[i + h] = a - c;
+          }
+      auto cross = [&](auto s_tag) {
+        constexpr int S = decltype(s_tag)::value;
+        const float sgn = (lane & S) ? -1.f : 1.f;  // the upper lane of a pair keeps partner - own
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = fmaf(v[i], sgn, xor_lane<S>(v[i], lane));
+      };
+      cross(std::integral_constant<int, 1>{});
+      cross(std::integral_constant<int, 2>{});
+      cross(std::integral_constant<int, 4>{});
+      cross(std::integral_constant<int, 8>{});
+      cross(std::integral_constant<int, 16>{});
+      cross(std::integral_constant<int, 32>{});
+      uint32_t out[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const _Float16 lo = (_Float16)(v[2 * i] * 0.03125f), hi = (_Float16)(v[2 * i + 1] * 0.03125f);  // 1/sqrt(1024)
+        out[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(lds + t * len + 1024 * b + 16 * lane);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    }
+    return;
+  }
   const int blocks = len / 128;
   for (int idx = wave; idx < MT * blocks; idx += WAVES) {
     const int t = idx / blocks, b = idx - t * blocks;
@@ -151,12 +209,13 @@ __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint
 
 // Single-token kernels must keep four waves per SIMD resident (at most 128 VGPRs; three for the
 // rotated variant) to have enough loads in flight; the build fails if that ever forces a spill.
-template <int MT, bool ROT>
+template <int MT, int ROT>
 constexpr int min_waves_per_eu() {
   return MT == 1 ? (ROT ? 3 : 4) : 1;
 }
 
-template <int S, int MT, int ITER, bool ROT>
+// ROT: 0 for the plain basis, else the rotation block (128 or 1024)
+template <int S, int MT, int ITER, int ROT>
 __global__ __launch_bounds__(64 * waves_for<ITER>())
 __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_kernel(const GemvArgs args) {
   constexpr int kWaves = waves_for<ITER>();
@@ -236,7 +295,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
       // ---- stage: pairs and all-zero-row products of the slice's chunks, once per workgroup
       __syncthreads();  // the previous slice's pairs are no longer read
       if constexpr (ROT) {
-        stage_rotated<MT, kWaves>(lds_x, kSliceElems, job.x, job.signs, k, m, m0, k_begin);
+        stage_rotated<MT, kWaves, ROT>(lds_x, kSliceElems, job.x, job.signs, k, m, m0, k_begin);
         __syncthreads();
       }
       for (int u = tid; u < MT * S; u += kThreads) {
@@ -528,28 +587,34 @@ hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices
   return hipGetLastError();
 }
 
-template <int S, int MT, int ITER, bool ROT>
+template <int S, int MT, int ITER, int ROT>
 hipError_t launch_one(GemvArgs& args, int blocks, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_kernel<S, MT, ITER, ROT>), dim3(blocks), dim3(64 * waves_for<ITER>()), 0, stream, args);
   return hipGetLastError();
 }
 
+template <int S, int MT, int ITER>
+hipError_t launch_block(int rot, GemvArgs& args, int blocks, hipStream_t stream) {
+  if (rot == 1024) return launch_one<S, MT, ITER, 1024>(args, blocks, stream);
+  if (rot) return launch_one<S, MT, ITER, 128>(args, blocks, stream);
+  return launch_one<S, MT, ITER, 0>(args, blocks, stream);
+}
+
 // rows per lane slot: 8 for large single-token launches (more work per workgroup), else 4;
-// fewer when several tokens share the registers
+// fewer when several tokens share the registers. rot: 0, 128 or 1024 (the rotation block)
 template <int S, int MT>
-hipError_t launch_rot(bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
+hipError_t launch_rot(int rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   if constexpr (MT == 1) {
-    if (iter == 8)
-      return rot ? launch_one<S, MT, 8, true>(args, blocks, stream) : launch_one<S, MT, 8, false>(args, blocks, stream);
-    return rot ? launch_one<S, MT, 4, true>(args, blocks, stream) : launch_one<S, MT, 4, false>(args, blocks, stream);
+    if (iter == 8) return launch_block<S, MT, 8>(rot, args, blocks, stream);
+    return launch_block<S, MT, 4>(rot, args, blocks, stream);
   } else {
     constexpr int it = MT == 2 ? 2 : 1;
-    return rot ? launch_one<S, MT, it, true>(args, blocks, stream) : launch_one<S, MT, it, false>(args, blocks, stream);
+    return launch_block<S, MT, it>(rot, args, blocks, stream);
   }
 }
 
 template <int S>
-hipError_t launch_mt(int mt, bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
+hipError_t launch_mt(int mt, int rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   switch (mt) {
     case 1: return launch_rot<S, 1>(rot, iter, args, blocks, stream);
     case 2: return launch_rot<S, 2>(rot, iter, args, blocks, stream);
@@ -557,7 +622,7 @@ hipError_t launch_mt(int mt, bool rot, int iter, GemvArgs& args, int blocks, hip
   }
 }
 
-hipError_t launch_s(int s, int mt, bool rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
+hipError_t launch_s(int s, int mt, int rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   switch (s) {
     case 16: return launch_mt<16>(mt, rot, iter, args, blocks, stream);
     case 32: return launch_mt<32>(mt, rot, iter, args, blocks, stream);
@@ -638,7 +703,7 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
 }
 
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream) {
-  if (plan.mfma) return gemv_b3_mfma_launch(args, blocks, plan.m, plan.rotated != 0, stream);
+  if (plan.mfma) return gemv_b3_mfma_launch(args, blocks, plan.m, (int)rotation_block(plan.rotated), stream);
   if (plan.stream) {
     switch (plan.lanes) {
       case 16: return launch_wave<16>(args, blocks, plan.iter, plan.slices, stream);
@@ -646,7 +711,8 @@ hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hip
       default: return launch_wave<64>(args, blocks, plan.iter, plan.slices, stream);
     }
   }
-  return launch_s(plan.lanes, tokens_per_pass(plan.m), plan.rotated != 0, plan.iter, args, blocks, stream);
+  return launch_s(plan.lanes, tokens_per_pass(plan.m), (int)rotation_block(plan.rotated), plan.iter, args, blocks,
+                  stream);
 }
 
 }  // namespace tgs

@@ -1,9 +1,9 @@
 // Base-3 GEMV (1..8 tokens) on the matrix cores.
 //
 // y[i][j] = sum_k s[j][k/128] * t[j][k] * xr[i][k], with xr = x or, for weights stored in the
-// rotated basis, xr = R x, R = blockdiag((1/sqrt(128)) H_128 S) ("Ternary Bonsai 2 27B, 5.93GB ...
-// (feat. PrismML)" (discuss.pytorch.kr), subsections "Group-scaled ternary format" and
-// "Block-wise Hadamard rotation"). A dot2 decode would repeat the whole base-3 digit extraction
+// rotated basis, xr = R x, R = blockdiag((1/sqrt(n)) H_n S) with n = 128 or 1024 ("Ternary Bonsai 2
+// 27B, 5.93GB ... (feat. PrismML)" (discuss.pytorch.kr), subsections "Group-scaled ternary format"
+// and "Block-wise Hadamard rotation"). A dot2 decode would repeat the whole base-3 digit extraction
 // for every token; here the codes are decoded once into fp16 weights t in {-1, 0, +1} and
 // v_mfma_f32_16x16x32_f16 multiplies them by all tokens at once (tokens are the 16 rows of the A
 // operand, padded with zeros). Even for one token this measured faster than the dot2 decode: the
@@ -24,6 +24,11 @@
 //     so each MFMA step reads its A fragment with one 16-byte load. The 32 slots of the 160-trit
 //     window that lie outside the group hold zeros: the trits there (neighbouring groups, or
 //     bytes past the row) multiply zero, and every MFMA step stays within one scale group.
+//   - 1024-element rotation blocks span eight groups, so they are rotated once per workgroup: wave
+//     w < MT rotates token w's block b + 1 into one half of a double-buffered LDS array (16 elements
+//     per lane: 4 butterfly stages in the lane, 6 across lanes) while every wave multiplies its group
+//     8 b + w of block b from the other half; one barrier per block. The waves thus take the groups
+//     of K round robin instead of in contiguous slices.
 //   - Each group's 16 x 16 partial is scaled by its fp16 scale in fp32 and added to the running
 //     sum; at the end the 8 waves' sums are added through LDS in wave order (deterministic).
 #include <type_traits>
@@ -69,13 +74,16 @@ __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both 
   return d;
 }
 
-template <int MT, int kFB, bool ROT>
+template <int MT, int kFB, int ROT>
 __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
+  static_assert(ROT == 0 || ROT == 128 || ROT == 1024, "rotation block is 0 (none), 128 or 1024");
   __shared__ __attribute__((aligned(16))) _Float16 tiles[kWaves][16 * kRowPitch];
   // byte offsets of tile slots for each start digit off0 (0..4): the group's 128 activations in
   // K order, then the 32 window positions outside the group
   __shared__ __attribute__((aligned(16))) uint16_t slot_tab[5][128];
   __shared__ __attribute__((aligned(16))) uint16_t zero_tab[5][32];
+  // rotated 1024-blocks of the MT tokens, double-buffered: [buffer][token][1024]
+  __shared__ __attribute__((aligned(16))) _Float16 blk[ROT == 1024 ? 2 * MT * 1024 : 8];
 
   const GemvJob job = gemv_job_of_block(args);
   const int n = job.n, k = job.k, m = args.m;
@@ -85,6 +93,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   const int fr = lane & 15, kq = lane >> 4;
   const int n_base = ((int)blockIdx.x - job.block0) * 16 * kFB;
   const int g_begin = wave * groups / kWaves, g_end = (wave + 1) * groups / kWaves;
+  const int blocks = k / 1024;  // used with 1024-element rotation blocks only (k % 1024 == 0)
 
   // activations: kL lanes per token, each with kE consecutive elements of the group
   constexpr int kL = 64 / MT, kE = 2 * MT;
@@ -124,11 +133,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   struct Stage {
     uint32_t c[kFB][3];          // three aligned dwords of codes per row block
     uint32_t s[kFB];             // raw fp16 scale bits
-    uint32_t x[MT];              // this lane's kE fp16 activations, in pairs
+    uint32_t x[MT];              // this lane's kE fp16 activations of the group, in pairs
     uint32_t sg[(kE + 3) / 4];   // their sign bytes
+    uint32_t bx[ROT == 1024 ? 8 : 1];  // 1024-blocks: 16 fp16 activations of the next block
+    uint32_t bs[ROT == 1024 ? 4 : 1];  // and their sign bytes
   };
-  auto load = [&](Stage& st, int g) {
-    const bool live = g < g_end;
+  auto load_codes = [&](Stage& st, int g, bool live) {
     const uint32_t byte0 = (uint32_t)((128 * g) / 5 + 8 * kq);
 #pragma unroll
     for (int fb = 0; fb < kFB; ++fb) {
@@ -140,6 +150,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       st.s[fb] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, live ? (int)(scale_row[fb] + 2u * g) : kOobOffset,
                                                      0, 0);
     }
+  };
+  // group g of the contiguous split: codes, scales and this lane's activations (and signs)
+  auto load = [&](Stage& st, int g) {
+    const bool live = g < g_end;
+    load_codes(st, g, live);
     const int xo = live ? (tok * k + 128 * g + kE * p) * 2 : kOobOffset;
     if constexpr (MT == 8) {
       const auto a = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo, 0, 0);
@@ -160,7 +175,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     } else {
       st.x[0] = __builtin_amdgcn_raw_buffer_load_b32(x_rsrc, xo, 0, 0);
     }
-    if constexpr (ROT) {
+    if constexpr (ROT == 128) {
       const int so = live ? 128 * g + kE * p : kOobOffset;
       if constexpr (MT == 8) {
         const auto a = __builtin_amdgcn_raw_buffer_load_b128(sign_rsrc, so, 0, 0);
@@ -177,13 +192,73 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       }
     }
   };
+  // 1024-blocks: token `wave`'s 16 activations 1024 bb + 16 lane .. and their signs (waves < MT)
+  auto load_block = [&](Stage& st, int bb) {
+    const bool live = bb < blocks && wave < MT;
+    const int e0 = 1024 * bb + 16 * lane;
+    const int xo = live ? (wave * k + e0) * 2 : kOobOffset;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo, 0, 0);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, live ? xo + 16 : kOobOffset, 0, 0);
+    const auto sv = __builtin_amdgcn_raw_buffer_load_b128(sign_rsrc, live ? e0 : kOobOffset, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st.bx[i] = a[i];
+      st.bx[4 + i] = b[i];
+      st.bs[i] = sv[i];
+    }
+  };
+  // 1024-blocks: signs, the natural-order Sylvester butterfly over the block in fp32 (strides 1..8
+  // inside the lane, 16..512 across lanes), 1/sqrt(1024), one rounding to fp16, into buffer `buf`
+  auto rotate_block = [&](const Stage& st, int buf) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t sel = (i & 1) ? 0x030C020Cu : 0x010C000Cu;  // sign bytes 2i, 2i + 1 -> bits 15, 31
+      const uint32_t xd = st.bx[i] ^ (__builtin_amdgcn_perm(0u, st.bs[i >> 1], sel) & 0x80008000u);
+      v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)xd);
+      v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(xd >> 16));
+    }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i & h) == 0) {
+          const float a = v[i], b = v[i + h];
+          v[i] = a + b;
+          v[i + h] = a - b;
+        }
+    auto cross = [&](auto s_tag) {
+      constexpr int S = decltype(s_tag)::value;
+      const float sgn = (lane & S) ? -1.f : 1.f;  // the upper lane of a pair keeps partner - own
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = fmaf(v[i], sgn, xor_lane<S>(v[i], lane));
+    };
+    cross(std::integral_constant<int, 1>{});
+    cross(std::integral_constant<int, 2>{});
+    cross(std::integral_constant<int, 4>{});
+    cross(std::integral_constant<int, 8>{});
+    cross(std::integral_constant<int, 16>{});
+    cross(std::integral_constant<int, 32>{});
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(v[2 * i] * 0.03125f));
+      const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(v[2 * i + 1] * 0.03125f));
+      w[i] = lo | (hi << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(blk + (buf * MT + wave) * 1024 + 16 * lane);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  };
 
   f32x4 acc[kFB];
 #pragma unroll
   for (int fb = 0; fb < kFB; ++fb) acc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   char* row_bytes = reinterpret_cast<char*>(tile + tok * kRowPitch);
-  auto compute = [&](const Stage& st, int g) {
+  // group g: activations into the tile, decode, 5 MFMA steps, scale; `buf` is the LDS buffer that
+  // holds g's rotated 1024-block
+  auto compute = [&](const Stage& st, int g, int buf) {
     const int off0 = 128 * g - 5 * ((128 * g) / 5);  // digit of byte B0 where the group starts
     const uint32_t sh = (uint32_t)(((128 * g) / 5 + 8 * kq) & 3);
     // this lane's slots: kE consecutive entries of the table row for off0
@@ -213,49 +288,79 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
         slot[1] = (uint16_t)(q >> 16);
       }
     }
-    // activations of this group -> tile row tok, in the weight operand's slot order; for rotated
-    // weights: sign flip (on the fp16 sign bits), the natural-order Sylvester butterfly over the
-    // 128-block in fp32 (strides below kE inside the lane, the rest across lanes), 1/sqrt(128),
-    // one rounding to fp16
-    float v[kE];
+    // activations of this group -> tile row tok, in the weight operand's slot order
+    _Float16 hv[kE];
+    if constexpr (ROT == 1024) {
+      // already rotated: kE consecutive fp16 values of token tok's block, at the group's place in it
+      const _Float16* src = blk + (buf * MT + tok) * 1024 + 128 * (g & 7) + kE * p;
+      uint32_t w[MT];
+      if constexpr (MT >= 4) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      uint32_t xd = st.x[i];
-      if constexpr (ROT) {
-        // sign bytes of elements 2i and 2i + 1 -> bits 15 and 31
-        const uint32_t sel = (i & 1) ? 0x030C020Cu : 0x010C000Cu;
-        xd ^= __builtin_amdgcn_perm(0u, st.sg[i >> 1], sel) & 0x80008000u;
+        for (int h = 0; h < MT / 4; ++h) {
+          const uint4 q = reinterpret_cast<const uint4*>(src)[h];
+          w[4 * h] = q.x;
+          w[4 * h + 1] = q.y;
+          w[4 * h + 2] = q.z;
+          w[4 * h + 3] = q.w;
+        }
+      } else if constexpr (MT == 2) {
+        const uint2 q = *reinterpret_cast<const uint2*>(src);
+        w[0] = q.x;
+        w[1] = q.y;
+      } else {
+        w[0] = *reinterpret_cast<const uint32_t*>(src);
       }
-      v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)xd);
-      v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(xd >> 16));
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        hv[2 * i] = __builtin_bit_cast(_Float16, (uint16_t)w[i]);
+        hv[2 * i + 1] = __builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+      }
+    } else {
+      // 128-blocks: sign flip (on the fp16 sign bits), the natural-order Sylvester butterfly over
+      // the group in fp32 (strides below kE inside the lane, the rest across lanes), 1/sqrt(128),
+      // one rounding to fp16
+      float v[kE];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        uint32_t xd = st.x[i];
+        if constexpr (ROT == 128) {
+          // sign bytes of elements 2i and 2i + 1 -> bits 15 and 31
+          const uint32_t sel = (i & 1) ? 0x030C020Cu : 0x010C000Cu;
+          xd ^= __builtin_amdgcn_perm(0u, st.sg[i >> 1], sel) & 0x80008000u;
+        }
+        v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)xd);
+        v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(xd >> 16));
+      }
+      if constexpr (ROT == 128) {
+#pragma unroll
+        for (int h = 1; h < kE; h <<= 1)
+#pragma unroll
+          for (int i = 0; i < kE; ++i)
+            if ((i & h) == 0) {
+              const float a = v[i], b = v[i + h];
+              v[i] = a + b;
+              v[i + h] = a - b;
+            }
+        auto cross = [&](auto s_tag) {
+          constexpr int S = decltype(s_tag)::value;
+          const float sgn = (p & S) ? -1.f : 1.f;  // the upper lane of a pair keeps partner - own
+#pragma unroll
+          for (int i = 0; i < kE; ++i) v[i] = fmaf(v[i], sgn, xor_lane<S>(v[i], lane));
+        };
+        if constexpr (kL > 1) cross(std::integral_constant<int, 1>{});
+        if constexpr (kL > 2) cross(std::integral_constant<int, 2>{});
+        if constexpr (kL > 4) cross(std::integral_constant<int, 4>{});
+        if constexpr (kL > 8) cross(std::integral_constant<int, 8>{});
+        if constexpr (kL > 16) cross(std::integral_constant<int, 16>{});
+        if constexpr (kL > 32) cross(std::integral_constant<int, 32>{});
+#pragma unroll
+        for (int i = 0; i < kE; ++i) v[i] *= 0.08838834764831845f;  // 1/sqrt(128)
+      }
+#pragma unroll
+      for (int i = 0; i < kE; ++i) hv[i] = (_Float16)v[i];
     }
-    if constexpr (ROT) {
 #pragma unroll
-      for (int h = 1; h < kE; h <<= 1)
-#pragma unroll
-        for (int i = 0; i < kE; ++i)
-          if ((i & h) == 0) {
-            const float a = v[i], b = v[i + h];
-            v[i] = a + b;
-            v[i + h] = a - b;
-          }
-      auto cross = [&](auto s_tag) {
-        constexpr int S = decltype(s_tag)::value;
-        const float sgn = (p & S) ? -1.f : 1.f;  // the upper lane of a pair keeps partner - own
-#pragma unroll
-        for (int i = 0; i < kE; ++i) v[i] = fmaf(v[i], sgn, xor_lane<S>(v[i], lane));
-      };
-      if constexpr (kL > 1) cross(std::integral_constant<int, 1>{});
-      if constexpr (kL > 2) cross(std::integral_constant<int, 2>{});
-      if constexpr (kL > 4) cross(std::integral_constant<int, 4>{});
-      if constexpr (kL > 8) cross(std::integral_constant<int, 8>{});
-      if constexpr (kL > 16) cross(std::integral_constant<int, 16>{});
-      if constexpr (kL > 32) cross(std::integral_constant<int, 32>{});
-#pragma unroll
-      for (int i = 0; i < kE; ++i) v[i] *= 0.08838834764831845f;  // 1/sqrt(128)
-    }
-#pragma unroll
-    for (int i = 0; i < kE; ++i) *reinterpret_cast<_Float16*>(row_bytes + slot[i]) = (_Float16)v[i];
+    for (int i = 0; i < kE; ++i) *reinterpret_cast<_Float16*>(row_bytes + slot[i]) = hv[i];
     // the 32 window slots outside the group meet zeros
     if constexpr (kL <= 32) {
       constexpr int kZ = 32 / kL;
@@ -304,15 +409,45 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     }
   };
 
-  // two groups of loads in flight; loads past the wave's last group are parked out of range
-  Stage st0, st1;
-  load(st0, g_begin);
-  for (int g = g_begin; g < g_end; g += 2) {
-    load(st1, g + 1);
-    compute(st0, g);
-    if (g + 1 >= g_end) break;
-    load(st0, g + 2);
-    compute(st1, g + 1);
+  if constexpr (ROT == 1024) {
+    // block b: waves < MT rotate block b + 1 into buffer (b + 1) & 1 while every wave multiplies
+    // group 8 b + wave from buffer b & 1; the barrier closing block b orders both against block
+    // b + 1 (every wave runs the same number of blocks, so all reach every barrier)
+    auto step = [&](const Stage& st, int b) {
+      if (wave < MT && b + 1 < blocks) rotate_block(st, (b + 1) & 1);
+      compute(st, 8 * b + wave, b & 1);
+      __syncthreads();
+    };
+    {
+      Stage st;
+      load_block(st, 0);
+      if (wave < MT) rotate_block(st, 0);
+    }
+    __syncthreads();
+    // stage b holds group 8 b + wave's codes and block b + 1's activations; two stages in flight
+    Stage st0, st1;
+    load_codes(st0, wave, 0 < blocks);
+    load_block(st0, 1);
+    for (int b = 0; b < blocks; b += 2) {
+      load_codes(st1, 8 * (b + 1) + wave, b + 1 < blocks);
+      load_block(st1, b + 2);
+      step(st0, b);
+      if (b + 1 >= blocks) break;
+      load_codes(st0, 8 * (b + 2) + wave, b + 2 < blocks);
+      load_block(st0, b + 3);
+      step(st1, b + 1);
+    }
+  } else {
+    // two groups of loads in flight; loads past the wave's last group are parked out of range
+    Stage st0, st1;
+    load(st0, g_begin);
+    for (int g = g_begin; g < g_end; g += 2) {
+      load(st1, g + 1);
+      compute(st0, g, 0);
+      if (g + 1 >= g_end) break;
+      load(st0, g + 2);
+      compute(st1, g + 1, 0);
+    }
   }
 
   // add the waves' sums in wave order
@@ -336,11 +471,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
 }
 
 template <int MT, int FB>
-hipError_t launch_mt(GemvArgs& args, int blocks, bool rotated, hipStream_t stream) {
-  if (rotated)
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, true>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+hipError_t launch_mt(GemvArgs& args, int blocks, int32_t block, hipStream_t stream) {
+  if (block == 1024)
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 1024>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+  else if (block)
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 128>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
   else
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, false>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 0>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -348,11 +485,11 @@ hipError_t launch_mt(GemvArgs& args, int blocks, bool rotated, hipStream_t strea
 
 int gemv_b3_mfma_rows(int32_t m) { return 16 * (m == 1 ? kMfmaFB1 : kMfmaFBMulti); }
 
-hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, bool rotated, hipStream_t stream) {
-  if (m <= 1) return launch_mt<1, kMfmaFB1>(args, blocks, rotated, stream);
-  if (m <= 2) return launch_mt<2, kMfmaFBMulti>(args, blocks, rotated, stream);
-  if (m <= 4) return launch_mt<4, kMfmaFBMulti>(args, blocks, rotated, stream);
-  return launch_mt<8, kMfmaFBMulti>(args, blocks, rotated, stream);
+hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, int32_t block, hipStream_t stream) {
+  if (m <= 1) return launch_mt<1, kMfmaFB1>(args, blocks, block, stream);
+  if (m <= 2) return launch_mt<2, kMfmaFBMulti>(args, blocks, block, stream);
+  if (m <= 4) return launch_mt<4, kMfmaFBMulti>(args, blocks, block, stream);
+  return launch_mt<8, kMfmaFBMulti>(args, blocks, block, stream);
 }
 
 }  // namespace tgs

@@ -1,12 +1,13 @@
-// Block-wise signed Walsh-Hadamard rotation of activations, 128 elements per block.
+// Block-wise signed Walsh-Hadamard rotation of activations, 128 or 1024 elements per block.
 //
-// y = R x with R = blockdiag((1/sqrt(128)) H_128 S): signs first, then the natural-order
-// Sylvester Hadamard transform, then the 1/sqrt(128) normalisation ("Ternary Bonsai 2 27B,
-// 5.93GB ... (feat. PrismML)" (discuss.pytorch.kr), subsection "Block-wise Hadamard rotation";
-// block size 128 here, one block per scale group). The sign flip is applied as the data is
-// loaded, so there is no separate pass over the activations (the page's Metal kernel does the
-// same), and the whole wave shares one block: lane l holds elements l and l + 64, the stride-64
-// stage runs inside the lane, the six others exchange values between lanes.
+// y = R x with R = blockdiag((1/sqrt(n)) H_n S): signs first, then the natural-order Sylvester
+// Hadamard transform, then the 1/sqrt(n) normalisation ("Ternary Bonsai 2 27B, 5.93GB ... (feat.
+// PrismML)" (discuss.pytorch.kr), subsection "Block-wise Hadamard rotation", which names
+// n = 1024; n = 128 makes one block per scale group). One wave owns one block of one row: lane l
+// holds the n/64 consecutive elements n/64 * l .., the butterfly stages of stride below n/64 run
+// inside the lane, and the six others exchange values with lane l ^ s (DPP quad permutes, masked
+// row rotations and the lane-half swaps; no LDS). The sign flip is applied as the data is loaded.
+#include "lane_ops.h"
 #include "tgs_internal.h"
 
 namespace tgs {
@@ -23,48 +24,65 @@ __device__ __forceinline__ float load_as_f32(const void* p, int32_t dtype, int64
   return reinterpret_cast<const float*>(p)[i];
 }
 
+template <int S, int E>
+__device__ __forceinline__ void cross_stage(float (&v)[E], int lane) {
+  const float sgn = (lane & S) ? -1.f : 1.f;  // the upper lane of a pair keeps partner - own
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] = fmaf(v[i], sgn, xor_lane<S>(v[i], lane));
+}
+
+template <int BLOCK>
 __global__ __launch_bounds__(kThreads) void hadamard_kernel(const void* __restrict__ x, int32_t x_dtype,
                                                             int64_t blocks_total, int64_t k,
                                                             const int8_t* __restrict__ sign, void* __restrict__ y,
                                                             int32_t y_dtype) {
+  constexpr int E = BLOCK / 64;
   const int lane = threadIdx.x & 63;
   const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (blk >= blocks_total) return;
-  const int64_t kb_per_row = k / 128;
-  const int64_t row = blk / kb_per_row, kb = (blk - row * kb_per_row) * 128;
-  const int64_t base = row * k + kb;
-  float v0 = load_as_f32(x, x_dtype, base + lane) * (float)sign[kb + lane];
-  float v1 = load_as_f32(x, x_dtype, base + lane + 64) * (float)sign[kb + lane + 64];
-  float a = v0 + v1, b = v0 - v1;
-  v0 = a;
-  v1 = b;
+  if (blk >= blocks_total) return;  // whole waves leave together
+  const int64_t kb_per_row = k / BLOCK;
+  const int64_t row = blk / kb_per_row, kb = (blk - row * kb_per_row) * BLOCK;
+  const int64_t base = row * k + kb + (int64_t)E * lane;
+  float v[E];
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) {
-    const float p0 = __shfl_xor(v0, s), p1 = __shfl_xor(v1, s);
-    const bool upper = (lane & s) != 0;
-    v0 = upper ? (p0 - v0) : (v0 + p0);
-    v1 = upper ? (p1 - v1) : (v1 + p1);
-  }
-  const float norm = 0.08838834764831845f;  // 1/sqrt(128)
-  v0 *= norm;
-  v1 *= norm;
-  if (y_dtype == TGS_F16) {
-    reinterpret_cast<_Float16*>(y)[base + lane] = (_Float16)v0;
-    reinterpret_cast<_Float16*>(y)[base + lane + 64] = (_Float16)v1;
-  } else {
-    reinterpret_cast<float*>(y)[base + lane] = v0;
-    reinterpret_cast<float*>(y)[base + lane + 64] = v1;
+  for (int i = 0; i < E; ++i) v[i] = load_as_f32(x, x_dtype, base + i) * (float)sign[kb + E * lane + i];
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  cross_stage<1>(v, lane);
+  cross_stage<2>(v, lane);
+  cross_stage<4>(v, lane);
+  cross_stage<8>(v, lane);
+  cross_stage<16>(v, lane);
+  cross_stage<32>(v, lane);
+  const float norm = BLOCK == 128 ? 0.08838834764831845f : 0.03125f;  // 1/sqrt(BLOCK)
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    if (y_dtype == TGS_F16)
+      reinterpret_cast<_Float16*>(y)[base + i] = (_Float16)(v[i] * norm);
+    else
+      reinterpret_cast<float*>(y)[base + i] = v[i] * norm;
   }
 }
 
 }  // namespace
 
-hipError_t hadamard_launch(const void* x, int32_t x_dtype, int64_t m, int64_t k, const int8_t* signs, void* y,
-                           int32_t y_dtype, hipStream_t stream) {
-  const int64_t blocks_total = m * (k / 128);
+hipError_t hadamard_launch(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block, const int8_t* signs,
+                           void* y, int32_t y_dtype, hipStream_t stream) {
+  const int64_t blocks_total = m * (k / block);
   const int64_t grid = (blocks_total + 3) / 4;
-  hipLaunchKernelGGL(hadamard_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, x_dtype, blocks_total, k,
-                     signs, y, y_dtype);
+  if (block == 1024)
+    hipLaunchKernelGGL(hadamard_kernel<1024>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, x_dtype,
+                       blocks_total, k, signs, y, y_dtype);
+  else
+    hipLaunchKernelGGL(hadamard_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, x_dtype,
+                       blocks_total, k, signs, y, y_dtype);
   return hipGetLastError();
 }
 

@@ -138,10 +138,13 @@ tgs_status check_matrix(const tgs_matrix* w, bool device) {
     return fail(TGS_E_LAYOUT, "bad descriptor magic/version (0x%08x, %u); use tgs_matrix_init", w->magic, w->version);
   if (w->layout != TGS_LAYOUT_SLOT2 && w->layout != TGS_LAYOUT_BASE3)
     return fail(TGS_E_LAYOUT, "unknown layout %d", w->layout);
-  if (w->rotated != 0 && w->rotated != 1) return fail(TGS_E_LAYOUT, "rotated flag must be 0 or 1, got %d", w->rotated);
+  if (w->rotated != 0 && w->rotated != 1 && w->rotated != 1024)
+    return fail(TGS_E_LAYOUT, "rotated must be 0, 1 (128-element blocks) or 1024, got %d", w->rotated);
   if (w->n < 1 || w->k < 128 || w->k % 128 != 0)
     return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128 (n=%lld, k=%lld)", (long long)w->n,
                 (long long)w->k);
+  if (w->rotated == 1024 && w->k % 1024 != 0)
+    return fail(TGS_E_SHAPE, "1024-element rotation blocks need k %% 1024 == 0 (k=%lld)", (long long)w->k);
   if (device && (w->n >= (1LL << 24) || w->k >= (1LL << 24) || w->code_row_stride >= (1LL << 24)))
     return fail(TGS_E_SHAPE, "n, k and the row stride must stay below 2^24 for the device kernels (n=%lld, k=%lld)",
                 (long long)w->n, (long long)w->k);
@@ -182,10 +185,14 @@ tgs_status tgs_matrix_init(tgs_matrix* w, int32_t layout, int32_t rotated, int64
   std::memset(w, 0, sizeof(*w));
   if (layout != TGS_LAYOUT_SLOT2 && layout != TGS_LAYOUT_BASE3) return fail(TGS_E_LAYOUT, "unknown layout %d", layout);
   if (n < 1 || k < 128 || k % 128 != 0) return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128");
+  if (rotated != 0 && rotated != 1 && rotated != 128 && rotated != 1024)
+    return fail(TGS_E_BASIS, "rotated must be 0, 1 (128-element blocks), 128 or 1024, got %d", rotated);
+  if (rotated == 1024 && k % 1024 != 0) return fail(TGS_E_SHAPE, "1024-element rotation blocks need k % 1024 == 0");
+  // the descriptor is written only once every check has passed: a failed call leaves it zeroed
   w->magic = TGS_MAGIC;
   w->version = TGS_VERSION;
   w->layout = layout;
-  w->rotated = rotated ? 1 : 0;
+  w->rotated = rotated == 0 ? 0 : (rotated == 1024 ? 1024 : 1);
   w->n = n;
   w->k = k;
   w->code_row_stride = (int64_t)row_bytes(layout, k);
@@ -258,6 +265,7 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
     if (!xs[i] || !ys[i]) return fail(TGS_E_NULL, "input or output %d is NULL", i);
     if (!aligned(xs[i], 16)) return fail(TGS_E_ALIGN, "x must be 16-byte aligned");
     if (!aligned(ys[i], 4)) return fail(TGS_E_ALIGN, "y must be 4-byte aligned");
+    if (signs && signs[i] && !aligned(signs[i], 16)) return fail(TGS_E_ALIGN, "signs must be 16-byte aligned");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   // one launch per distinct plan (layout, lanes per row, basis, kernel, K slices), in call order
@@ -385,22 +393,28 @@ tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int
   return ok();
 }
 
-tgs_status hadamard_rotate_g128(const void* x, int32_t x_dtype, int64_t m, int64_t k, const int8_t* signs, void* y,
-                                int32_t y_dtype, void* stream) {
+tgs_status hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block, const int8_t* signs,
+                           void* y, int32_t y_dtype, void* stream) {
   if (!x || !signs || !y) return fail(TGS_E_NULL, "x, signs or y is NULL");
   if (x_dtype != TGS_F16 && x_dtype != TGS_BF16 && x_dtype != TGS_F32)
     return fail(TGS_E_DTYPE, "x_dtype must be TGS_F16, TGS_BF16 or TGS_F32");
   if (y_dtype != TGS_F16 && y_dtype != TGS_F32) return fail(TGS_E_DTYPE, "y_dtype must be TGS_F16 or TGS_F32");
-  if (m < 1 || k < 128 || k % 128 != 0 || m * (k / 128) > (1LL << 40))
-    return fail(TGS_E_SHAPE, "need m >= 1 and k a positive multiple of 128");
+  if (block != 128 && block != 1024) return fail(TGS_E_SHAPE, "block must be 128 or 1024, got %lld", (long long)block);
+  if (m < 1 || k < block || k % block != 0 || m * (k / block) > (1LL << 40))
+    return fail(TGS_E_SHAPE, "need m >= 1 and k a positive multiple of the block (%lld)", (long long)block);
   if (!aligned(x, 16) || !aligned(y, 16)) return fail(TGS_E_ALIGN, "x and y must be 16-byte aligned");
   const size_t xe = x_dtype == TGS_F32 ? 4 : 2, ye = y_dtype == TGS_F32 ? 4 : 2;
   const char *xb = static_cast<const char*>(x), *yb = static_cast<const char*>(y);
   const size_t xn = (size_t)(m * k) * xe, yn = (size_t)(m * k) * ye;
   if (xb < yb + yn && yb < xb + xn) return fail(TGS_E_SHAPE, "x and y overlap");
-  hipError_t e = tgs::hadamard_launch(x, x_dtype, m, k, signs, y, y_dtype, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return device_error(e, "hadamard_rotate_g128 launch");
+  hipError_t e = tgs::hadamard_launch(x, x_dtype, m, k, block, signs, y, y_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "hadamard_rotate launch");
   return ok();
+}
+
+tgs_status hadamard_rotate_g128(const void* x, int32_t x_dtype, int64_t m, int64_t k, const int8_t* signs, void* y,
+                                int32_t y_dtype, void* stream) {
+  return hadamard_rotate(x, x_dtype, m, k, 128, signs, y, y_dtype, stream);
 }
 
 const char* tgs_status_string(tgs_status status) {

@@ -79,7 +79,7 @@ struct GemvPlan {
   int32_t layout;     // TGS_LAYOUT_*
   int32_t lanes;      // lanes per row (16, 32 or 64)
   int32_t m;          // activation rows
-  int32_t rotated;    // 0 or 1
+  int32_t rotated;    // 0 (plain), 1 (128-element rotation blocks) or 1024
   int32_t stream;     // 1: the single-token kernel (slot-2, plain basis, m = 1)
   int32_t slices;     // single-token kernel: K slices of 64 chunks = waves per workgroup
   int32_t mfma;       // 1: base-3, on the matrix cores (gemv_mfma.hip)
@@ -95,7 +95,8 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows);
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream);
 // base-3 on the matrix cores: rows of y per workgroup for m tokens
 int gemv_b3_mfma_rows(int32_t m);
-hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, bool rotated, hipStream_t stream);
+// block: 0 for plain-basis weights, else the rotation block (128 or 1024)
+hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, int32_t block, hipStream_t stream);
 
 // Code flips: one pair of matrices of a batched launch (device pointers).
 struct FlipJob {
@@ -123,7 +124,10 @@ hipError_t code_flip_launch(FlipArgs& args, int32_t blocks, hipStream_t stream);
 hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
                        const uint16_t* x_bf16, int64_t m, float* y, hipStream_t stream);
 
-hipError_t hadamard_launch(const void* x, int32_t x_dtype, int64_t m, int64_t k, const int8_t* signs, void* y,
-                           int32_t y_dtype, hipStream_t stream);
+hipError_t hadamard_launch(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block, const int8_t* signs,
+                           void* y, int32_t y_dtype, hipStream_t stream);
+
+// rotation block of a descriptor's `rotated` field: 0 (plain basis), 128 or 1024
+inline int64_t rotation_block(int32_t rotated) { return rotated == 0 ? 0 : (rotated == 1024 ? 1024 : 128); }
 
 }  // namespace tgs

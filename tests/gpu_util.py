@@ -25,9 +25,10 @@ def make_signs(seed, stream, k):
     return synth.signs(seed, synth.stream_id(stream, "signs"), k)
 
 
-def oracle_product(layout, trits, scales, x_bits, x_dtype, signs=None, rows=None):
+def oracle_product(layout, trits, scales, x_bits, x_dtype, signs=None, rows=None, block=128):
     codes = oracle.pack(layout, trits)
-    return oracle.matmul(layout, codes, scales, trits.shape[1], x_bits, x_dtype, signs=signs, rows=rows)
+    return oracle.matmul(layout, codes, scales, trits.shape[1], x_bits, x_dtype, signs=signs, rows=rows,
+                         block=block)
 
 
 def assert_within_bound(y_gpu, y_ref, bound, what=""):

@@ -29,8 +29,8 @@ def _x_dev(x16):
     return torch.from_numpy(x16.view(np.int16).copy()).to(DEV).view(torch.float16)
 
 
-def _gemv(layout, t, s, x16, signs=None):
-    w = _packed(layout, t, s, rotated=signs is not None)
+def _gemv(layout, t, s, x16, signs=None, block=128):
+    w = _packed(layout, t, s, rotated=block if signs is not None else 0)
     sg = torch.from_numpy(signs).to(DEV) if signs is not None else None
     y = tgs.ternary_gemv(w, _x_dev(x16), signs=sg)
     torch.cuda.synchronize()
@@ -79,6 +79,36 @@ def test_rotated_gemv_matches_oracle(layout, n, k, m):
     y = _gemv(layout, t, s, x16, signs=sg)
     y_ref, bound = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg)
     assert_within_bound(y, y_ref, bound, f"rotated {LNAME[layout]} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+@pytest.mark.parametrize("n,k", [(1, 1024), (33, 2048), (100, 5120), (20, 17408), (65, 4096), (300, 3072)])
+@pytest.mark.parametrize("m", [1, 2, 3, 8])
+def test_rotated_1024_gemv_matches_oracle(layout, n, k, m):
+    """1024-element rotation blocks (eight scale groups per block)."""
+    t, s = make_weights(n * 5 + k, f"rot1024{layout}", n, k, 0.5)
+    x16 = make_x_f16(m + 11, f"rot1024{n}x{k}", m, k)
+    sg = make_signs(k, "rot1024", k)
+    y = _gemv(layout, t, s, x16, signs=sg, block=1024)
+    y_ref, bound = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg, block=1024)
+    assert_within_bound(y, y_ref, bound, f"rotated-1024 {LNAME[layout]} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
+def test_rotation_block_changes_the_product(layout):
+    """The same weights and signs under 128- and 1024-element blocks give different products, each
+    matching its own oracle (a kernel that ignored the block size would fail one of the two)."""
+    n, k, m = 40, 2048, 2
+    t, s = make_weights(3, f"rotblk{layout}", n, k, 0.5)
+    x16 = make_x_f16(3, "rotblk", m, k)
+    sg = make_signs(3, "rotblk", k)
+    for block in (128, 1024):
+        y = _gemv(layout, t, s, x16, signs=sg, block=block)
+        y_ref, bound = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg, block=block)
+        assert_within_bound(y, y_ref, bound, f"block {block}")
+        other, _ = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg,
+                                  block=1152 - block)
+        assert (np.abs(y - other) > bound).any()
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
@@ -131,9 +161,10 @@ def test_batched_equals_single_calls(layout):
 
 
 def test_batched_mixed_layouts_and_bases():
-    k = 1280
+    k = 2048
     sg = make_signs(1, "mixed", k)
-    cases = [(tgs.SLOT2, False), (tgs.BASE3, True), (tgs.SLOT2, True), (tgs.BASE3, False)]
+    cases = [(tgs.SLOT2, 0), (tgs.BASE3, 128), (tgs.SLOT2, 1024), (tgs.SLOT2, 128), (tgs.BASE3, 1024),
+             (tgs.BASE3, 0)]
     ws, xs, ys, signs, refs = [], [], [], [], []
     for i, (layout, rot) in enumerate(cases):
         t, s = make_weights(i, "mixed", 50 + i, k, 0.5)
@@ -142,7 +173,8 @@ def test_batched_mixed_layouts_and_bases():
         xs.append(_x_dev(x16))
         ys.append(torch.empty((2, 50 + i), dtype=torch.float32, device=DEV))
         signs.append(torch.from_numpy(sg).to(DEV) if rot else None)
-        refs.append(oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg if rot else None))
+        refs.append(oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg if rot else None,
+                                   block=rot or 128))
     tgs.ternary_gemv_batched(ws, xs, ys, signs=signs)
     torch.cuda.synchronize()
     for y, (y_ref, bound) in zip(ys, refs):
@@ -187,6 +219,52 @@ def test_hadamard_rotate_matches_oracle(in_dtype, out_dtype):
         assert (np.abs(got - ref) <= 1e-6 * blk_l1 + 1e-30).all()
     else:
         assert (np.abs(got - ref) <= 2.0 ** -11 * np.abs(ref) + 1e-6 * blk_l1 + 2.0 ** -25).all()
+
+
+@pytest.mark.parametrize("in_dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("out_dtype", ["f32", "f16"])
+def test_hadamard_rotate_1024_matches_oracle(in_dtype, out_dtype):
+    m, k = 3, 3072
+    sg = make_signs(4, "had1024", k)
+    xd = synth.normal(4, 10, (m, k))
+    if in_dtype == "f16":
+        host = xd.astype(np.float16)
+        xt = torch.from_numpy(host.copy()).to(DEV)
+        xref = host.astype(np.float64)
+    elif in_dtype == "bf16":
+        bits = synth.bf16_bits(xd)
+        xt = torch.from_numpy(bits.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+        xref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        host = xd.astype(np.float32)
+        xt = torch.from_numpy(host.copy()).to(DEV)
+        xref = host.astype(np.float64)
+    od = torch.float32 if out_dtype == "f32" else torch.float16
+    y = tgs.hadamard_rotate(xt, torch.from_numpy(sg).to(DEV), block=1024, out_dtype=od)
+    torch.cuda.synchronize()
+    ref = oracle.rotate(xref, sg, block=1024)
+    got = y.float().cpu().numpy().astype(np.float64)
+    blk_l1 = np.repeat(np.abs(xref).reshape(m, -1, 1024).sum(axis=2), 1024, axis=1) / np.sqrt(1024)
+    if out_dtype == "f32":
+        assert (np.abs(got - ref) <= 1e-6 * blk_l1 + 1e-30).all()
+    else:
+        assert (np.abs(got - ref) <= 2.0 ** -11 * np.abs(ref) + 1e-6 * blk_l1 + 2.0 ** -25).all()
+    # the 128-block entry point is the general one at block 128
+    y128 = tgs.hadamard_rotate(xt, torch.from_numpy(sg).to(DEV), block=128, out_dtype=od)
+    y128b = tgs.hadamard_rotate_g128(xt, torch.from_numpy(sg).to(DEV), out_dtype=od)
+    torch.cuda.synchronize()
+    assert torch.equal(y128.view(torch.int16 if out_dtype == "f16" else torch.int32),
+                       y128b.view(torch.int16 if out_dtype == "f16" else torch.int32))
+
+
+def test_misaligned_signs_are_refused():
+    k = 2048
+    t, s = make_weights(1, "sgal", 8, k, 0.4)
+    w = _packed(tgs.BASE3, t, s, rotated=1024)
+    sg = torch.from_numpy(np.ones(k + 16, dtype=np.int8)).to(DEV)
+    with pytest.raises(tgs.TgsError) as info:
+        tgs.ternary_gemv(w, _x_dev(make_x_f16(1, "sgal", 1, k)), signs=sg[4:4 + k])
+    assert info.value.name == "TGS_E_ALIGN"
 
 
 # ------------------------------------------------------------------------------ GEMM

@@ -153,6 +153,20 @@ def test_device_call_argument_checks_happen_before_any_device_work():
     assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, 0x500000, 0x400000, tgs.BF16, None) == 8
     assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, None, 0x400000, tgs.F32, None) == 1
     assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, 0x500000, 0x300100, tgs.F32, None) == 2  # overlap
+    # hadamard_rotate: the block is 128 or 1024 and divides k
+    rot = lambda k, block, signs=0x500000: lib.hadamard_rotate(0x300000, tgs.F16, 2, k, block, signs, 0x400000,
+                                                                 tgs.F32, None)
+    assert rot(2048, 512) == 2
+    assert rot(1536, 1024) == 2
+    assert rot(512, 1024) == 2
+    assert rot(2048, 1024, signs=None) == 1
+    # rotated GEMV: signs 16-byte aligned; 1024-element blocks need k % 1024 == 0
+    assert _gemv(_fake_matrix(rotated=1), signs=0x500004) == 3
+    assert _gemv(_fake_matrix(rotated=1024, k=2048), signs=0x500008) == 3
+    bad = _fake_matrix(rotated=1024, k=2048)
+    bad.k = 1536
+    bad.code_row_stride = 384
+    assert _gemv(bad, signs=0x500000) == 2
     # batched
     ms = (tgs.Matrix * 2)(_fake_matrix(), _fake_matrix(rotated=1))
     xp = (ctypes.c_void_p * 2)(0x300000, 0x300000)
@@ -197,3 +211,12 @@ def test_matrix_init_rejects_bad_shapes():
     assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 0, 4, 129, 1, 1) == 2
     assert tgs.lib().tgs_matrix_init(ctypes.byref(m), 5, 0, 4, 128, 1, 1) == 5
     assert m.magic == 0
+    assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 1024, 4, 1536, 1, 1) == 2  # k % 1024 != 0
+    assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 512, 4, 2048, 1, 1) == 6   # no 512-blocks
+    assert m.magic == 0
+
+
+@pytest.mark.parametrize("rotated,stored", [(0, 0), (1, 1), (128, 1), (1024, 1024)])
+def test_matrix_init_records_the_rotation_block(rotated, stored):
+    m = _fake_matrix(rotated=rotated, k=2048)
+    assert m.rotated == stored
