@@ -23,6 +23,7 @@ _lib = None
 
 SLOT2 = 1
 BASE3 = 2
+BINARY = 3
 X_F16 = 1
 X_BF16 = 2
 
@@ -61,7 +62,8 @@ def _load():
         lib.orc_bf16_to_f64.restype = dbl
         lib.orc_row_bytes.argtypes = [i32, i64]
         lib.orc_row_bytes.restype = i64
-        for name in ("orc_pack_slot2", "orc_unpack_slot2", "orc_pack_base3", "orc_unpack_base3"):
+        for name in ("orc_pack_slot2", "orc_unpack_slot2", "orc_pack_base3", "orc_unpack_base3", "orc_pack_binary",
+                     "orc_unpack_binary"):
             f = getattr(lib, name)
             f.argtypes = [vp, i64, i64, vp]
             f.restype = ctypes.c_int
@@ -95,14 +97,14 @@ def row_bytes(layout: int, k: int) -> int:
 
 
 def pack(layout: int, trits: np.ndarray) -> np.ndarray:
-    """trits int8 [n][k] -> codes uint8 [n][row_bytes]."""
+    """trits int8 [n][k] -> codes uint8 [n][row_bytes] (binary: values must be -1 or +1)."""
     t = np.ascontiguousarray(trits, dtype=np.int8)
     n, k = t.shape
     rb = row_bytes(layout, k)
     if rb == 0:
         raise OracleError("bad layout or k")
     out = np.zeros((n, rb), dtype=np.uint8)
-    fn = _load().orc_pack_slot2 if layout == SLOT2 else _load().orc_pack_base3
+    fn = {SLOT2: _load().orc_pack_slot2, BASE3: _load().orc_pack_base3, BINARY: _load().orc_pack_binary}[layout]
     _check(fn(t.ctypes.data, n, k, out.ctypes.data), "pack")
     return out
 
@@ -114,7 +116,7 @@ def unpack(layout: int, codes: np.ndarray, k: int) -> np.ndarray:
     if c.shape[1] != row_bytes(layout, k):
         raise OracleError("codes row length does not match k")
     out = np.zeros((n, k), dtype=np.int8)
-    fn = _load().orc_unpack_slot2 if layout == SLOT2 else _load().orc_unpack_base3
+    fn = {SLOT2: _load().orc_unpack_slot2, BASE3: _load().orc_unpack_base3, BINARY: _load().orc_unpack_binary}[layout]
     _check(fn(c.ctypes.data, n, k, out.ctypes.data), "unpack")
     return out
 

@@ -9,7 +9,10 @@
  *
  *   y[m][n] = sum_k  s[n][k/128] * t[n][k] * xr[m][k]
  *
- * where t[n][k] in {-1, 0, +1} are the ternary codes, s[n][g] is the fp16
+ * where t[n][k] in {-1, 0, +1} are the ternary codes (in {-1, +1} for the
+ * binary sibling format, the two-level variant with the same group scale:
+ * "Bonsai 27B and how 1-bit survives" (velog.io), sections "What ternary and
+ * binary are" and "What the format is"), s[n][g] is the fp16
  * scale shared by the 128 weights of group g along K, and xr is the
  * activation x, or R x when the weights are stored in the rotated basis.
  *   - The weight definition w = s_g * t with one fp16 scale per 128 weights:
@@ -42,6 +45,11 @@
  *   base3: five trits per byte, byte b of a row = sum_{j<5} (t[5b+j]+1) * 3^j;
  *          trits past K are 0 (digit 1); a row holds ceil(K/5) such bytes,
  *          then pad bytes of value 121 (five zero trits) up to a multiple of 16.
+ *   binary: one bit per weight, element k of a row in bit k%8 of byte k/8, a
+ *          set bit meaning t = +1 and a clear bit t = -1 (t = 0 cannot be
+ *          stored); rows are K/8 bytes apart. With the fp16 scale that is 18
+ *          bytes per 128 weights, 1.125 bits per weight, the figure the velog.io
+ *          page gives for the binary format with group scales.
  *   scales: a separate fp16 array [n][K/128], row-major.
  */
 #include <math.h>
@@ -56,6 +64,7 @@
 
 #define ORC_SLOT2 1
 #define ORC_BASE3 2
+#define ORC_BINARY 3
 
 #define ORC_X_F16 1
 #define ORC_X_BF16 2
@@ -85,6 +94,7 @@ double orc_bf16_to_f64(uint16_t b) {
 int64_t orc_row_bytes(int32_t layout, int64_t k) {
   if (k <= 0 || k % 128 != 0) return 0;
   if (layout == ORC_SLOT2) return k / 4;
+  if (layout == ORC_BINARY) return k / 8;
   if (layout == ORC_BASE3) {
     int64_t used = (k + 4) / 5;
     return (used + 15) / 16 * 16;
@@ -174,11 +184,37 @@ int orc_unpack_base3(const uint8_t* codes, int64_t n, int64_t k, int8_t* t) {
   return ORC_OK;
 }
 
+/* ---- binary ---- */
+
+int orc_pack_binary(const int8_t* t, int64_t n, int64_t k, uint8_t* codes) {
+  if (k % 128 != 0 || n < 0) return ORC_BAD_SHAPE;
+  int64_t rb = k / 8;
+  memset(codes, 0, (size_t)(n * rb));
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t c = 0; c < k; ++c) {
+      int v = t[r * k + c];
+      if (v != -1 && v != 1) return ORC_BAD_CODE;  /* two levels only */
+      if (v == 1) codes[r * rb + c / 8] |= (uint8_t)(1u << (c % 8));
+    }
+  }
+  return ORC_OK;
+}
+
+int orc_unpack_binary(const uint8_t* codes, int64_t n, int64_t k, int8_t* t) {
+  if (k % 128 != 0 || n < 0) return ORC_BAD_SHAPE;
+  int64_t rb = k / 8;
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < k; ++c)
+      t[r * k + c] = ((codes[r * rb + c / 8] >> (c % 8)) & 1) ? 1 : -1;
+  return ORC_OK;
+}
+
 /* ---- one row of codes -> trits (used by the product; same loops as above) ---- */
 
 static int unpack_row(int32_t layout, const uint8_t* row, int64_t k, int8_t* t) {
   if (layout == ORC_SLOT2) return orc_unpack_slot2(row, 1, k, t);
   if (layout == ORC_BASE3) return orc_unpack_base3(row, 1, k, t);
+  if (layout == ORC_BINARY) return orc_unpack_binary(row, 1, k, t);
   return ORC_BAD_LAYOUT;
 }
 

@@ -31,6 +31,11 @@ MUTANTS = {
     "rotation_block_ignored": ("orc_rotate_f64(xd, sign, m, k, block, xr);", "orc_rotate_f64(xd, sign, m, k, 128, xr);"),
     "flips_dropped_last_trit": ("for (int64_t i = 0; i < k; ++i) c += ta[i] != tb[i];",
                                 "for (int64_t i = 0; i + 1 < k; ++i) c += ta[i] != tb[i];"),
+    "binary_bit_order": ("codes[r * rb + c / 8] |= (uint8_t)(1u << (c % 8));",
+                         "codes[r * rb + c / 8] |= (uint8_t)(1u << (7 - c % 8));"),
+    "binary_sign": ("t[r * k + c] = ((codes[r * rb + c / 8] >> (c % 8)) & 1) ? 1 : -1;",
+                    "t[r * k + c] = ((codes[r * rb + c / 8] >> (c % 8)) & 1) ? -1 : 1;"),
+    "binary_row_bytes": ("if (layout == ORC_BINARY) return k / 8;", "if (layout == ORC_BINARY) return k / 4;"),
     "flips_row_stride": ("unpack_row(layout, b + r * row_stride_b, k, tb)", "unpack_row(layout, b + r * row_stride_a, k, tb)"),
 }
 

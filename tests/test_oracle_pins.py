@@ -103,7 +103,7 @@ def test_slot2_random_round_trip_and_position():
 def test_pack_rejects_bad_trits():
     t = np.zeros((1, 128), dtype=np.int8)
     t[0, 5] = 2
-    for layout in (oracle.SLOT2, oracle.BASE3):
+    for layout in (oracle.SLOT2, oracle.BASE3, oracle.BINARY):
         with pytest.raises(oracle.OracleError):
             oracle.pack(layout, t)
 
@@ -292,6 +292,107 @@ def test_rotation_identities():
     sg = synth.signs(2, 3, k)
     rt = _dense_rotation(sg).T
     assert np.allclose((w @ rt) @ oracle.rotate(x, sg), w @ x, atol=1e-12)
+
+
+# ---------------------------------------------------------------- binary bits (P2, "What ternary and binary are")
+
+def _binary_row_with_prefix(prefix, k=128):
+    t = -np.ones((1, k), dtype=np.int8)
+    t[0, :len(prefix)] = prefix
+    return t
+
+
+def _signs(seed, stream, shape):
+    """Seeded weights in {-1, +1} (the binary format has no zero)."""
+    return synth.trits(seed, stream, shape, 0.0)
+
+
+@pytest.mark.parametrize("bits,hexbyte", _read_fixture("binary_bytes.txt"))
+def test_binary_hand_bytes(bits, hexbyte):
+    codes = oracle.pack(oracle.BINARY, _binary_row_with_prefix(bits))
+    assert codes.shape == (1, 16)
+    assert codes[0, 0] == int(hexbyte, 16)
+    assert (codes[0, 1:] == 0).all()  # -1 elsewhere: every bit clear
+
+
+def test_binary_every_byte_round_trips():
+    for b in range(256):
+        codes = np.zeros((1, 16), dtype=np.uint8)
+        codes[0, 0] = b
+        t = oracle.unpack(oracle.BINARY, codes, 128)
+        assert list(t[0, :8]) == [1 if (b >> i) & 1 else -1 for i in range(8)]
+        assert (t[0, 8:] == -1).all()
+        assert (oracle.pack(oracle.BINARY, t) == codes).all()
+
+
+def test_binary_random_round_trip_and_position():
+    t = _signs(0, 12, (5, 384))
+    codes = oracle.pack(oracle.BINARY, t)
+    assert codes.shape == (5, 48)
+    assert (oracle.unpack(oracle.BINARY, codes, 384) == t).all()
+    # element k lives in bit k%8 of byte k//8: numpy's little-endian bit unpacking
+    bits = np.unpackbits(codes, axis=1, bitorder="little")
+    assert (np.where(bits == 1, 1, -1) == t).all()
+
+
+def test_binary_rejects_zero_and_out_of_range():
+    for bad in (0, 2, -2):
+        t = np.ones((1, 128), dtype=np.int8)
+        t[0, 77] = bad
+        with pytest.raises(oracle.OracleError):
+            oracle.pack(oracle.BINARY, t)
+
+
+def test_binary_costs_one_and_an_eighth_bits_per_weight():
+    # P2 "What ternary and binary are": 1.125 bits per weight with the group scales
+    for k in (128, 1024, 4096, 5120, 12288, 17408):
+        total_bits = 8 * (oracle.row_bytes(oracle.BINARY, k) + 2 * (k // 128))
+        assert total_bits / k == 1.125
+
+
+@pytest.mark.parametrize("block", [None, 128, 1024])
+def test_binary_product_equals_the_slot2_product_of_the_same_signs(block):
+    # the same {-1, +1} weights stored in either layout define the same product, bit for bit
+    k = 1024
+    t = _signs(3, 4, (6, k))
+    s = synth.scales_f16(3, 5, (6, k // 128))
+    x16 = synth.x_f16(3, 6, (2, k))
+    sg = synth.signs(3, 7, k) if block else None
+    yb, bb = oracle.matmul(oracle.BINARY, oracle.pack(oracle.BINARY, t), s, k, x16.view(np.uint16), oracle.X_F16,
+                           signs=sg, block=block or 128)
+    ys, bs = oracle.matmul(oracle.SLOT2, oracle.pack(oracle.SLOT2, t), s, k, x16.view(np.uint16), oracle.X_F16,
+                           signs=sg, block=block or 128)
+    assert (yb == ys).all() and (bb == bs).all()
+
+
+def test_binary_closed_forms():
+    # all +1 gives s * sum x per group, all -1 gives -s * sum x; +1 on even positions and -1 on
+    # odd ones gives s * (sum of even - sum of odd)
+    k = 256
+    x16 = synth.x_f16(0, 2, (k,))
+    xs = x16.astype(np.float64)
+    t = np.ones((3, k), dtype=np.int8)
+    t[1] = -1
+    t[2, 1::2] = -1
+    s = np.array([[0.5, 3.0], [0.25, 2.0], [1.0, 4.0]], dtype=np.float16)
+    y, _ = oracle.matmul(oracle.BINARY, oracle.pack(oracle.BINARY, t), s, k, x16.view(np.uint16), oracle.X_F16)
+    assert y[0, 0] == pytest.approx(0.5 * xs[:128].sum() + 3.0 * xs[128:].sum(), rel=1e-15, abs=1e-15)
+    assert y[0, 1] == pytest.approx(-0.25 * xs[:128].sum() - 2.0 * xs[128:].sum(), rel=1e-15, abs=1e-15)
+    alt = xs[0::2] - xs[1::2]
+    assert y[0, 2] == pytest.approx(alt[:64].sum() + 4.0 * alt[64:].sum(), rel=1e-14, abs=1e-14)
+
+
+@pytest.mark.parametrize("k", [128, 384])
+@pytest.mark.parametrize("m", [1, 3])
+def test_binary_brute_force_tiny(k, m):
+    n = 5
+    t = _signs(k + m, 21, (n, k))
+    s = synth.scales_f16(k + m, 22, (n, k // 128))
+    x16 = synth.x_f16(k + m, 23, (m, k))
+    y, bound = oracle.matmul(oracle.BINARY, oracle.pack(oracle.BINARY, t), s, k, x16.view(np.uint16), oracle.X_F16)
+    terms = x16.astype(np.float64)[:, None, :] * _dense_weights(t, s)[None, :, :]
+    assert np.allclose(y, terms.sum(axis=2), rtol=1e-13, atol=1e-16)
+    assert np.allclose(bound, 1e-3 * np.abs(terms).sum(axis=2) + 1e-6, rtol=1e-13)
 
 
 # ---------------------------------------------------------------- the product (P3 "Group-scaled ternary format")
@@ -484,6 +585,23 @@ def test_code_flips_extremes_and_symmetry(layout):
     ab, ba = oracle.code_flips(layout, a, b, k)[0], oracle.code_flips(layout, b, a, k)[0]
     assert ab == ba
     assert oracle.code_flips(layout, a, c, k)[0] <= ab + oracle.code_flips(layout, b, c, k)[0]
+
+
+@pytest.mark.parametrize("k", [128, 1280])
+def test_binary_code_flips_count_the_planted_sign_changes(k):
+    n = 23
+    t = _signs(14, k, (n, k))
+    mask = np.random.default_rng(k).random((n, k)) < 0.05
+    u = np.where(mask, -t, t).astype(np.int8)
+    a, b = oracle.pack(oracle.BINARY, t), oracle.pack(oracle.BINARY, u)
+    total, rows = oracle.code_flips(oracle.BINARY, a, b, k)
+    assert total == int(mask.sum())
+    assert (rows == mask.sum(axis=1)).all()
+    assert oracle.code_flips(oracle.BINARY, a, a, k)[0] == 0
+    assert oracle.code_flips(oracle.BINARY, a, oracle.pack(oracle.BINARY, -t), k)[0] == n * k
+    # the same sign changes counted in the slot-2 layout give the same numbers
+    s_total, s_rows = oracle.code_flips(oracle.SLOT2, oracle.pack(oracle.SLOT2, t), oracle.pack(oracle.SLOT2, u), k)
+    assert s_total == total and (s_rows == rows).all()
 
 
 def test_code_flips_do_not_depend_on_the_layout_or_the_row_padding():
