@@ -52,12 +52,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8b", choices=["8b", "base3", "rotated", "gemm", "flips", "config1"])
+    ap.add_argument("--workload", default="8b", choices=["8b", "base3", "binary", "rotated", "gemm", "flips", "config1"])
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the set (default: 36 for the 8B-class sets, 64 for the rotated 27B-class set)")
     ap.add_argument("--mode", default="layer", choices=["layer", "fused-layer", "set"],
                     help="launch grouping for the 8B set: same-input groups (144 launches), one launch per "
                          "layer (36), or the whole set in as few launches as possible")
+    ap.add_argument("--gemm-layout", default="slot2", choices=["slot2", "binary"],
+                    help="code layout of the GEMM workload")
     ap.add_argument("--rot-block", type=int, default=128, choices=[128, 1024],
                     help="rotation block of the rotated 27B-class set (128: one block per scale group)")
     ap.add_argument("--one-mode", action="store_true", help="time only --mode (the others are reported by default)")
@@ -146,9 +148,12 @@ def measured_traffic(profile_name):
 
 # ----------------------------------------------------------------------------- 8B decode set
 
-def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_name=None):
+LAYOUT_NAME = {1: "slot2", 2: "base3", 3: "binary"}
+
+
+def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_name=None, metric=METRIC):
     layers = args.layers or 36
-    log(f"[bench] building {layers} layers x {len(LAYER_8B)} matrices ({'slot-2' if layout == 1 else 'base-3'})")
+    log(f"[bench] building {layers} layers x {len(LAYER_8B)} matrices ({LAYOUT_NAME[layout]})")
     t0 = time.time()
     mats, host = [], []
     for L in range(layers):
@@ -214,12 +219,12 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
     per_launch_bytes = total_bytes / n_launches
     per_launch_s = ms * 1e-3 / n_launches
     kernel_gbs = per_launch_bytes / per_launch_s / 1e9
-    kernel = "gemv_wave_kernel" if layout == 1 else "gemv_b3_mfma_kernel"
-    profile = f"{kernel}.8b_{'slot2' if layout == 1 else 'base3'}_m1_{args.mode}.pmc.txt"
+    kernel = "gemv_b3_mfma_kernel" if layout == 2 else "gemv_wave_kernel"
+    profile = f"{kernel}.8b_{LAYOUT_NAME[layout]}_m1_{args.mode}.pmc.txt"
     traffic = measured_traffic(profile)
 
     result = {
-        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": workload_name or "8B-class decode GEMV set, 2-bit-slot layout, M=1",
@@ -323,11 +328,13 @@ def bench_rotated(args, torch, tgs, synth):
 
 
 def bench_gemm(args, torch, tgs, synth):
-    """27B-class prefill GEMM, slot-2: gate/up 17408x5120 and down 5120x17408, M in {16, 128, 2048}."""
+    """27B-class prefill GEMM (slot-2, or binary codes): gate/up 17408x5120 and down 5120x17408, M in
+    {16, 128, 2048}."""
     res = []
     copies = 16
+    layout, p_zero = (3, 0.0) if args.gemm_layout == "binary" else (1, 0.4)
     for n, k in ((17408, 5120), (5120, 17408)):
-        ws = [build_matrix(torch, tgs, synth, 1, 0, f"gemm/{n}x{k}/{i}", n, k, 0.4)[0] for i in range(copies)]
+        ws = [build_matrix(torch, tgs, synth, layout, 0, f"gemm/{n}x{k}/{i}", n, k, p_zero)[0] for i in range(copies)]
         for m in (16, 128, 2048):
             xb = synth.x_bf16_bits(0, synth.stream_id("gemm/x", m, k), (m, k))
             x = torch.from_numpy(xb.view(np.int16).copy()).cuda().view(torch.bfloat16)
@@ -345,7 +352,7 @@ def bench_gemm(args, torch, tgs, synth):
             res.append({"metric": "ternary GEMM TFLOP/s", "value": round(flops / per / 1e9, 2), "unit": "TFLOP/s",
                         "pct_of_bf16_peak": round(100 * flops / per / 1e9 / BF16_MFMA_PEAK_TFLOPS, 2),
                         "gbs": round(nb / per / 1e6, 1), "us": round(per * 1e3, 2),
-                        "config": {"workload": f"27B-class prefill GEMM {n}x{k}, M={m}, slot-2"}})
+                        "config": {"workload": f"27B-class prefill GEMM {n}x{k}, M={m}, {LAYOUT_NAME[layout]}"}})
             log(f"[bench] gemm {n}x{k} m={m}: {per * 1e3:.1f} us, {flops / per / 1e9:.1f} TFLOP/s")
         del ws
         torch.cuda.empty_cache()
@@ -469,6 +476,10 @@ def main():
     elif args.workload == "base3":
         out = [bench_8b(args, torch, tgs, synth, layout=2, p_zero=0.5, tag="8b3",
                         workload_name="8B-class decode GEMV set, base-3 layout, M=1")]
+    elif args.workload == "binary":
+        out = [bench_8b(args, torch, tgs, synth, layout=3, p_zero=0.0, tag="8bb",
+                        workload_name="8B-class decode GEMV set, binary layout (t in {-1, +1}), M=1",
+                        metric="binary GEMV achieved HBM GB/s (% of peak), 8B-class set, M=1")]
     elif args.workload == "rotated":
         out = bench_rotated(args, torch, tgs, synth)
     elif args.workload == "gemm":

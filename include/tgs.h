@@ -65,11 +65,16 @@ typedef enum {
  *   ceil(K/5) bytes followed by pad bytes of value 121 (five zero trits) up to a multiple of
  *   16 bytes: minimum row length round_up(ceil(K/5), 16) bytes.
  *
- * Both layouts keep the scales in a separate fp16 array [N][K/128], row-major, one per group of
+ * TGS_LAYOUT_BINARY: the two-level sibling format, t in {-1, +1} ([P2] "What ternary and binary
+ *   are": two levels, 1.125 bits per weight with the group scales). One bit per weight: element
+ *   k of a row is bit k%8 of byte k/8, set for t = +1 and clear for t = -1 (t = 0 cannot be
+ *   stored). Minimum row length K/8 bytes; every byte is valid.
+ *
+ * All layouts keep the scales in a separate fp16 array [N][K/128], row-major, one per group of
  * 128 consecutive weights of a row ([P3] "Group-scaled ternary format": w_i = s_g * t_i with one
  * FP16 scale per 128 weights; [P2] "What the format is").
  */
-typedef enum { TGS_LAYOUT_SLOT2 = 1, TGS_LAYOUT_BASE3 = 2 } tgs_layout;
+typedef enum { TGS_LAYOUT_SLOT2 = 1, TGS_LAYOUT_BASE3 = 2, TGS_LAYOUT_BINARY = 3 } tgs_layout;
 
 /* Activation / output element types (IEEE binary16, bfloat16, binary32). */
 typedef enum { TGS_F16 = 1, TGS_BF16 = 2, TGS_F32 = 3 } tgs_dtype;
@@ -116,13 +121,14 @@ tgs_status tgs_matrix_init(tgs_matrix* w, int32_t layout, int32_t rotated, int64
 
 /*
  * pack_ternary (host): encode trits into the packed layout.
- *   trits      host [n][k] int8 in {-1, 0, +1}
+ *   trits      host [n][k] int8 in {-1, 0, +1} ({-1, +1} for TGS_LAYOUT_BINARY)
  *   scales     host [n][k/128] fp16 bits, copied to scales_out (both may be NULL to skip)
  *   codes_out  host buffer of codes_bytes >= n * tgs_code_row_bytes(layout, k); rows are
  *              written at the minimum stride
  * A native-ternary checkpoint is exactly scale x {-1, 0, +1}, so this re-encoding is lossless
  * ([P1] opening section on what these models are); unpack_ternary inverts it bit-exactly.
- * Returns TGS_E_CODE for a trit outside {-1, 0, +1}; codes_out may then be partly written.
+ * Returns TGS_E_CODE for a trit outside {-1, 0, +1} (or a 0 for the binary layout); codes_out may
+ * then be partly written.
  */
 tgs_status pack_ternary(int32_t layout, const int8_t* trits, const uint16_t* scales, int64_t n,
                         int64_t k, void* codes_out, size_t codes_bytes, uint16_t* scales_out);

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libtgs.so")
 
 SLOT2 = 1
 BASE3 = 2
+BINARY = 3
 F16 = 1
 BF16 = 2
 F32 = 3

@@ -9,6 +9,7 @@
 // and identical run to run, including the 64-bit atomic total.
 //   - Slot-2: a code word v = a ^ b is nonzero in a 2-bit field exactly where the codes differ,
 //     so the flips of 16 codes are popcount((v | v >> 1) & 0x55555555).
+//   - Binary: one bit per weight, so the flips of 32 codes are popcount(a ^ b).
 //   - Base-3: each byte is first rewritten as its five trits in 2-bit fields (peeling base-3
 //     digits with v = v * 171 >> 9 on packed 16-bit halves, as the GEMV kernels do), then the
 //     same XOR and popcount.
@@ -91,7 +92,14 @@ __global__ __launch_bounds__(kThreads) void code_flip_kernel(const FlipArgs args
       const uint32_t wa[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
       const uint32_t wb[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) count += LAYOUT == TGS_LAYOUT_SLOT2 ? flips_slot2(wa[i], wb[i]) : flips_base3(wa[i], wb[i]);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (LAYOUT == TGS_LAYOUT_SLOT2)
+          count += flips_slot2(wa[i], wb[i]);
+        else if constexpr (LAYOUT == TGS_LAYOUT_BINARY)
+          count += __builtin_popcount(wa[i] ^ wb[i]);
+        else
+          count += flips_base3(wa[i], wb[i]);
+      }
     }
   }
 
@@ -134,6 +142,8 @@ hipError_t code_flip_launch(FlipArgs& args, int32_t blocks, hipStream_t stream) 
   hipLaunchKernelGGL(zero_totals_kernel, dim3(1), dim3(64), 0, stream, args);
   if (args.layout == TGS_LAYOUT_SLOT2)
     hipLaunchKernelGGL(code_flip_kernel<TGS_LAYOUT_SLOT2>, dim3(blocks), dim3(kThreads), 0, stream, args);
+  else if (args.layout == TGS_LAYOUT_BINARY)
+    hipLaunchKernelGGL(code_flip_kernel<TGS_LAYOUT_BINARY>, dim3(blocks), dim3(kThreads), 0, stream, args);
   else
     hipLaunchKernelGGL(code_flip_kernel<TGS_LAYOUT_BASE3>, dim3(blocks), dim3(kThreads), 0, stream, args);
   return hipGetLastError();

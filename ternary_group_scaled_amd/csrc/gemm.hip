@@ -19,7 +19,8 @@
 //      v_perm table lookup makes two weights).
 // Within every 16 consecutive k, both tiles are stored in the order 0,8,1,9,...,7,15 (the order
 // the slot-2 decode produces pairs in); the contraction over k does not depend on that order.
-// Up to 32 activation rows take the skinny kernel further below instead.
+// Binary codes (t in {-1, +1}, one bit per weight) decode the same way into bf16 2t in {-2, +2}.
+// Up to 32 activation rows of slot-2 codes take the skinny kernel further below instead.
 #include <algorithm>
 
 #include "tgs_internal.h"
@@ -73,6 +74,15 @@ __device__ __forceinline__ void decode16_slot2(uint32_t u, uint32_t* out) {
   out[7] = __builtin_amdgcn_perm(0u, kTable, ((u >> 6) & 0x03000300u) | 0x000C000Cu);
 }
 
+// 16 binary codes (bits 0..15 of u, a set bit meaning t = +1) -> 8 words of bf16 pairs
+// (2 t_i, 2 t_{i+8}): the bit picks the high byte from the table {0xC0, 0x40} (bf16 -2, +2)
+__device__ __forceinline__ void decode16_binary(uint32_t u, uint32_t* out) {
+  constexpr uint32_t kTable = 0x000040C0u;
+  const uint32_t v = (u & 0xFFu) | ((u & 0xFF00u) << 8);  // bit i + 8 -> bit i + 16
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = __builtin_amdgcn_perm(0u, kTable, ((v << (8 - i)) & 0x01000100u) | 0x000C000Cu);
+}
+
 __device__ __forceinline__ uint16_t bf16_of_2t_digit(uint32_t digit) {
   // digit = t + 1 in {0, 1, 2} -> bf16(2t)
   return digit == 0 ? 0xC000u : (digit == 2 ? 0x4000u : 0u);
@@ -85,7 +95,7 @@ __device__ __forceinline__ uint16_t bf16_of_2t_digit(uint32_t digit) {
 // used when the tiles alone give too few workgroups.
 template <int LAYOUT, int BM, int BN, int KS>
 __global__ __launch_bounds__(kThreads * KS)
-__attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_SLOT2 ? 2 : 1, 8))) void gemm_tile_kernel(
+__attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void gemm_tile_kernel(
     const uint8_t* __restrict__ codes, int64_t stride, const uint16_t* __restrict__ scales, int n, int k,
     const uint16_t* __restrict__ x, int m, float* __restrict__ y) {
   constexpr int kWM = BM / 2, kWN = BN / 2;  // tile of one wave
@@ -130,6 +140,12 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_SLOT2 ? 2 : 1, 8))) void
       const uint32_t off = (uint32_t)(n_base + (tid >> 1)) * (uint32_t)stride + (uint32_t)(g * 32 + 16 * (tid & 1));
       cr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)off, 0, kStreamAux));
     }
+    if (LAYOUT == TGS_LAYOUT_BINARY && tid < kCodeThreads) {  // 64 codes are 8 bytes
+      const uint32_t off = (uint32_t)(n_base + (tid >> 1)) * (uint32_t)stride + (uint32_t)(g * 16 + 8 * (tid & 1));
+      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, (int)off, 0, kStreamAux));
+      cr.x = v.x;
+      cr.y = v.y;
+    }
   };
   auto store_stage = [&](int g) {
 #pragma unroll
@@ -149,6 +165,11 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_SLOT2 ? 2 : 1, 8))) void
         decode16_slot2(cr.y, out + 8);
         decode16_slot2(cr.z, out + 16);
         decode16_slot2(cr.w, out + 24);
+      } else if (LAYOUT == TGS_LAYOUT_BINARY) {
+        decode16_binary(cr.x, out + 0);
+        decode16_binary(cr.x >> 16, out + 8);
+        decode16_binary(cr.y, out + 16);
+        decode16_binary(cr.y >> 16, out + 24);
       } else {
         // base-3: digit by digit from the packed bytes (not on a measured path)
         const int row = n_base + r;
@@ -529,10 +550,12 @@ hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, con
   const int64_t max_rows = std::max<int64_t>(128, (kMaxDeviceCodeBytes / (2 * k)) / 128 * 128);
   for (int64_t r0 = 0; r0 < m; r0 += max_rows) {
     const int64_t mr = std::min(max_rows, m - r0);
+    const uint16_t* xr = x_bf16 + r0 * k;
+    float* yr = y + r0 * n;
     const hipError_t e =
-        layout == TGS_LAYOUT_SLOT2
-            ? launch_layout<TGS_LAYOUT_SLOT2>(codes, stride, scales, n, k, x_bf16 + r0 * k, mr, y + r0 * n, stream)
-            : launch_layout<TGS_LAYOUT_BASE3>(codes, stride, scales, n, k, x_bf16 + r0 * k, mr, y + r0 * n, stream);
+        layout == TGS_LAYOUT_SLOT2   ? launch_layout<TGS_LAYOUT_SLOT2>(codes, stride, scales, n, k, xr, mr, yr, stream)
+        : layout == TGS_LAYOUT_BASE3 ? launch_layout<TGS_LAYOUT_BASE3>(codes, stride, scales, n, k, xr, mr, yr, stream)
+                                     : launch_layout<TGS_LAYOUT_BINARY>(codes, stride, scales, n, k, xr, mr, yr, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -1,5 +1,5 @@
-// Ternary group-scaled GEMV (M <= 8 activation rows), slot-2 codes, for gfx950. (Base-3 codes
-// take the matrix-core kernel in gemv_mfma.hip.)
+// Ternary group-scaled GEMV (M <= 8 activation rows), slot-2 and binary codes, for gfx950.
+// (Base-3 codes take the matrix-core kernel in gemv_mfma.hip.)
 //
 // y[i][n] = sum_k s[n][k/128] * t[n][k] * xr[i][k], weights read once, in packed form.
 // The weight definition w = s_g * t with one fp16 scale per 128 weights is the one of
@@ -30,6 +30,17 @@
 // Since t = q - 1, sum_k t x = sum_k q x - sum_k x. The second sum is produced by running the
 // identical decode-and-dot sequence on the code word of an all-zero row (every slot q = 1): a
 // row whose codes are all zero then cancels bit for bit and gives exactly 0.
+//
+// Binary codes (t in {-1, +1}, one bit b = (t + 1) / 2 per weight; the two-level sibling format of
+// "Bonsai 27B and how 1-bit survives" (velog.io), section "What ternary and binary are") use the
+// same kernels with 8-byte chunks of 64 weights. A 32-bit word holds 32 weights, element j in bit
+// j, and dot2 pairs elements (j, j + 16): masking the word with 0x00010001 << p keeps the bits of
+// both in fp16 bit p of the two halves, exactly b * 2^(p-24) (a subnormal for p < 10, the
+// smallest normals for p = 10 and 11). Bits 4..11 are used in place and bits 0..3 and 12..15 are
+// moved there with one shift each (u << 4, u >> 4), so every position stays at bit 4 or above:
+// two shifts, sixteen ANDs and sixteen dot2 per 32 weights, into one accumulator per bit
+// position. Then sum_k t x = 2 sum_k b x - sum_k x, the second sum again from the identical
+// sequence on an all-ones word.
 //
 // Shared per-slice work. The activation pairs of a chunk and its all-zero-row product depend on
 // the chunk only, not on the wave, so one thread per chunk builds them once per workgroup and
@@ -111,6 +122,88 @@ __device__ __forceinline__ float chunk_dot_slot2(const uint4& cw, const uint32_t
     a4 = dot2(w & 0x03000300u, q[7], a4);  // j = 7
   }
   return fmaf(fmaf(a4, 0.25f, a3), 0.25f, a2);
+}
+
+// binary: p[16d + i] = (x_{32d+i}, x_{32d+i+16}) from the chunk's 64 fp16 activations (32 words)
+template <int I>
+__device__ __forceinline__ void pairs_binary_word(const uint32_t* w, uint32_t* p) {
+  if constexpr (I < 16) {
+    p[I] = xpair<I, I + 16>(w);
+    pairs_binary_word<I + 1>(w, p);
+  }
+}
+
+__device__ __forceinline__ void build_pairs_binary(const uint32_t* w, uint32_t* p) {
+  pairs_binary_word<0>(w, p);
+  pairs_binary_word<0>(w + 16, p + 16);
+}
+
+// binary: 2^-20 * sum_k b_k x_k over the 64 weights of a chunk
+__device__ __forceinline__ float chunk_dot_binary(const uint2& cw, const uint32_t* p) {
+  float a[8];  // a[j]: pairs whose bits sit at fp16 bit 4 + j, each term b * x * 2^(j - 20)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = 0.f;
+  const uint32_t words[2] = {cw.x, cw.y};
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const uint32_t u = words[d], lo = u << 4, hi = u >> 4;
+    const uint32_t* q = p + 16 * d;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = dot2(u & (0x00100010u << j), q[4 + j], a[j]);  // bits 4..11
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = dot2(lo & (0x00100010u << j), q[j], a[j]);  // bits 0..3
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[4 + j] = dot2(hi & (0x01000100u << j), q[12 + j], a[4 + j]);  // bits 12..15
+  }
+  float r = a[7];
+#pragma unroll
+  for (int j = 6; j >= 0; --j) r = fmaf(r, 0.5f, a[j]);
+  return r;
+}
+
+// ---- per-layout chunk operations (BIN: binary codes, else slot-2) --------------------------
+
+template <bool BIN>
+using ChunkCodes = typename std::conditional<BIN, uint2, uint4>::type;
+
+template <bool BIN>
+constexpr uint32_t chunk_bytes() {
+  return BIN ? 8u : 16u;
+}
+
+template <bool BIN>
+__device__ __forceinline__ ChunkCodes<BIN> load_chunk(__amdgpu_buffer_rsrc_t rsrc, int off) {
+  if constexpr (BIN)
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, kStreamAux));
+  else
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kStreamAux));
+}
+
+template <bool BIN>
+__device__ __forceinline__ void build_pairs(const uint32_t* w, uint32_t* p) {
+  if constexpr (BIN)
+    build_pairs_binary(w, p);
+  else
+    build_pairs_slot2(w, p);
+}
+
+// 2^-20 * sum_k x_k over the chunk, by the same instruction sequence as the rows (all-zero
+// slot-2 codes have q = 1 everywhere; all-ones binary codes have b = 1 everywhere)
+template <bool BIN>
+__device__ __forceinline__ float chunk_ref(const uint32_t* p) {
+  if constexpr (BIN)
+    return chunk_dot_binary(make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu), p);
+  else
+    return chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
+}
+
+// 2^-20 * sum_k t_k x_k over the chunk, given its reference sum
+template <bool BIN>
+__device__ __forceinline__ float chunk_value(const ChunkCodes<BIN>& cw, const uint32_t* p, float ref) {
+  if constexpr (BIN)
+    return fmaf(2.f, chunk_dot_binary(cw, p), -ref);
+  else
+    return chunk_dot_slot2(cw, p) - ref;
 }
 
 // ---- staging one slice of activations ----------------------------------------------------
@@ -214,8 +307,8 @@ constexpr int min_waves_per_eu() {
   return MT == 1 ? (ROT ? 3 : 4) : 1;
 }
 
-// ROT: 0 for the plain basis, else the rotation block (128 or 1024)
-template <int S, int MT, int ITER, int ROT>
+// ROT: 0 for the plain basis, else the rotation block (128 or 1024). BIN: binary codes.
+template <int S, int MT, int ITER, int ROT, bool BIN>
 __global__ __launch_bounds__(64 * waves_for<ITER>())
 __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_kernel(const GemvArgs args) {
   constexpr int kWaves = waves_for<ITER>();
@@ -246,7 +339,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
   constexpr int kBatches = kIter / kBatch;
   constexpr int kRing = kBatches >= 4 ? 4 : 3;
   struct Batch {
-    uint4 cw[kBatch];
+    ChunkCodes<BIN> cw[kBatch];
     uint32_t s0[kBatch];  // raw fp16 scale bits: converted only when used, so a prefetch never
                           // waits for its own loads
   };
@@ -266,9 +359,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
       // unsigned arithmetic: an offset past the buffer simply reads as zero. Rows, row strides
       // and group counts are below 2^24 (checked on the host), so the full-rate 24-bit multiply
       // gives the exact low 32 bits.
-      const uint32_t code_off = __umul24((uint32_t)row, (uint32_t)job.stride) + (uint32_t)c * 16u;
+      const uint32_t code_off = __umul24((uint32_t)row, (uint32_t)job.stride) + (uint32_t)c * chunk_bytes<BIN>();
       const uint32_t scale_off = (__umul24((uint32_t)row, (uint32_t)groups) + (uint32_t)g0) * 2u;
-      bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)code_off, 0, kStreamAux));
+      bt.cw[i] = load_chunk<BIN>(code_rsrc, (int)code_off);
       bt.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)scale_off, 0, 0);
     }
   };
@@ -317,8 +410,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
           w[4 * v + 3] = q.w;
         }
         uint32_t p[kChunkPairDw];
-        build_pairs_slot2(w, p);
-        lds_ref[t * S + bc] = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
+        build_pairs<BIN>(w, p);
+        lds_ref[t * S + bc] = chunk_ref<BIN>(p);
 #pragma unroll
         for (int g = 0; g < kGran; ++g)
           lds_pairs[(t * kGran + g) * S + bc] = make_uint4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
@@ -355,7 +448,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
           const float sc0 = chunk_ok ? f16_to_f32((uint16_t)cur.s0[i]) : 0.f;
 #pragma unroll
           for (int t = 0; t < MT; ++t)
-            part[it][t] = fmaf(sc0, chunk_dot_slot2(cur.cw[i], xp[t]) - ref0[t], part[it][t]);
+            part[it][t] = fmaf(sc0, chunk_value<BIN>(cur.cw[i], xp[t], ref0[t]), part[it][t]);
         }
       }
     }
@@ -464,7 +557,7 @@ __device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& 
   }
 }
 
-template <int S, int G>
+template <int S, int G, bool BIN>
 __global__ __launch_bounds__(1024)
 void gemv_wave_kernel(const GemvArgs args) {
   constexpr int kRowsPerInstr = 64 / S;
@@ -506,20 +599,19 @@ void gemv_wave_kernel(const GemvArgs args) {
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order
 
   struct Batch {
-    uint4 cw[2];
+    ChunkCodes<BIN> cw[2];
     uint32_t s[2];
   };
   // batch b -> rows row0 + (2b + i) * kRowsPerInstr. Rows past the matrix read as zero; a lane
   // past the row's last chunk parks its loads out of range (no traffic, zero data).
-  const uint32_t code_col = (uint32_t)c * 16u, scale_col = (uint32_t)(c >> 1) * 2u;
+  const uint32_t code_col = (uint32_t)c * chunk_bytes<BIN>(), scale_col = (uint32_t)(c >> 1) * 2u;
   auto load_batch = [&](Batch& bt, int b) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t row = (uint32_t)(row0 + (2 * b + i) * kRowsPerInstr);
       const uint32_t code_off = __umul24(row, (uint32_t)job.stride) + code_col;
       const uint32_t scale_off = __umul24(row, (uint32_t)groups) * 2u + scale_col;
-      bt.cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               code_rsrc, lane_live ? (int)code_off : kOobOffset, 0, kStreamAux));
+      bt.cw[i] = load_chunk<BIN>(code_rsrc, lane_live ? (int)code_off : kOobOffset);
       bt.s[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, lane_live ? (int)scale_off : kOobOffset, 0, 0);
     }
   };
@@ -530,14 +622,14 @@ void gemv_wave_kernel(const GemvArgs args) {
 
   // 2. dot2 pairs and the all-zero-row product of this lane's chunk
   uint32_t xp[32];
-  build_pairs_slot2(xw, xp);
-  const float ref = chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), xp);
+  build_pairs<BIN>(xw, xp);
+  const float ref = chunk_ref<BIN>(xp);
 
   constexpr int kSlotLanes = S == 64 ? 32 : (S == 32 ? 16 : 8);
   const bool writer = (lane & (kSlotLanes - 1)) == 0;
   auto consume = [&](const Batch& cur, int b) {
-    const float v0 = f16_to_f32((uint16_t)cur.s[0]) * (chunk_dot_slot2(cur.cw[0], xp) - ref);
-    const float v1 = f16_to_f32((uint16_t)cur.s[1]) * (chunk_dot_slot2(cur.cw[1], xp) - ref);
+    const float v0 = f16_to_f32((uint16_t)cur.s[0]) * chunk_value<BIN>(cur.cw[0], xp, ref);
+    const float v1 = f16_to_f32((uint16_t)cur.s[1]) * chunk_value<BIN>(cur.cw[1], xp, ref);
     int slot;
     const float sum = reduce_pair<S>(v0, v1, lane, slot);
     if (writer) {
@@ -574,59 +666,70 @@ void gemv_wave_kernel(const GemvArgs args) {
   }
 }
 
-template <int S>
+template <int S, bool BIN>
 hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
   const size_t lds = slices > 1 ? (size_t)slices * rows_per_wave * (64 / S) * sizeof(float) : 0;
   args.rows_per_wave = rows_per_wave;
   if (rows_per_wave >= 8)
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 4>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 4, BIN>), dim3(blocks), dim3(64 * slices), lds, stream, args);
   else if (rows_per_wave == 4)
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 2>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 2, BIN>), dim3(blocks), dim3(64 * slices), lds, stream, args);
   else
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 1>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 1, BIN>), dim3(blocks), dim3(64 * slices), lds, stream, args);
   return hipGetLastError();
 }
 
-template <int S, int MT, int ITER, int ROT>
+template <bool BIN>
+hipError_t launch_wave_s(int lanes, GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
+  switch (lanes) {
+    case 16: return launch_wave<16, BIN>(args, blocks, rows_per_wave, slices, stream);
+    case 32: return launch_wave<32, BIN>(args, blocks, rows_per_wave, slices, stream);
+    default: return launch_wave<64, BIN>(args, blocks, rows_per_wave, slices, stream);
+  }
+}
+
+template <int S, int MT, int ITER, int ROT, bool BIN>
 hipError_t launch_one(GemvArgs& args, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_kernel<S, MT, ITER, ROT>), dim3(blocks), dim3(64 * waves_for<ITER>()), 0, stream, args);
+  hipLaunchKernelGGL((gemv_kernel<S, MT, ITER, ROT, BIN>), dim3(blocks), dim3(64 * waves_for<ITER>()), 0, stream,
+                     args);
   return hipGetLastError();
 }
 
-template <int S, int MT, int ITER>
+template <int S, int MT, int ITER, bool BIN>
 hipError_t launch_block(int rot, GemvArgs& args, int blocks, hipStream_t stream) {
-  if (rot == 1024) return launch_one<S, MT, ITER, 1024>(args, blocks, stream);
-  if (rot) return launch_one<S, MT, ITER, 128>(args, blocks, stream);
-  return launch_one<S, MT, ITER, 0>(args, blocks, stream);
+  if (rot == 1024) return launch_one<S, MT, ITER, 1024, BIN>(args, blocks, stream);
+  if (rot) return launch_one<S, MT, ITER, 128, BIN>(args, blocks, stream);
+  return launch_one<S, MT, ITER, 0, BIN>(args, blocks, stream);
 }
 
 // rows per lane slot: 8 for large single-token launches (more work per workgroup), else 4;
 // fewer when several tokens share the registers. rot: 0, 128 or 1024 (the rotation block)
-template <int S, int MT>
+template <int S, int MT, bool BIN>
 hipError_t launch_rot(int rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   if constexpr (MT == 1) {
-    if (iter == 8) return launch_block<S, MT, 8>(rot, args, blocks, stream);
-    return launch_block<S, MT, 4>(rot, args, blocks, stream);
+    if (iter == 8) return launch_block<S, MT, 8, BIN>(rot, args, blocks, stream);
+    return launch_block<S, MT, 4, BIN>(rot, args, blocks, stream);
   } else {
     constexpr int it = MT == 2 ? 2 : 1;
-    return launch_block<S, MT, it>(rot, args, blocks, stream);
+    return launch_block<S, MT, it, BIN>(rot, args, blocks, stream);
   }
 }
 
-template <int S>
+template <int S, bool BIN>
 hipError_t launch_mt(int mt, int rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   switch (mt) {
-    case 1: return launch_rot<S, 1>(rot, iter, args, blocks, stream);
-    case 2: return launch_rot<S, 2>(rot, iter, args, blocks, stream);
-    default: return launch_rot<S, 4>(rot, iter, args, blocks, stream);
+    case 1: return launch_rot<S, 1, BIN>(rot, iter, args, blocks, stream);
+    case 2: return launch_rot<S, 2, BIN>(rot, iter, args, blocks, stream);
+    default: return launch_rot<S, 4, BIN>(rot, iter, args, blocks, stream);
   }
 }
 
+template <bool BIN>
 hipError_t launch_s(int s, int mt, int rot, int iter, GemvArgs& args, int blocks, hipStream_t stream) {
   switch (s) {
-    case 16: return launch_mt<16>(mt, rot, iter, args, blocks, stream);
-    case 32: return launch_mt<32>(mt, rot, iter, args, blocks, stream);
-    default: return launch_mt<64>(mt, rot, iter, args, blocks, stream);
+    case 16: return launch_mt<16, BIN>(mt, rot, iter, args, blocks, stream);
+    case 32: return launch_mt<32, BIN>(mt, rot, iter, args, blocks, stream);
+    default: return launch_mt<64, BIN>(mt, rot, iter, args, blocks, stream);
   }
 }
 
@@ -651,7 +754,7 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
     p.rows_per_block = gemv_b3_mfma_rows((int32_t)m);
     return p;
   }
-  // slot-2 from here on. The single-token kernel: one wave per K slice of 64 chunks, up to 16
+  // slot-2 and binary from here on (both in chunks of 64 weights). The single-token kernel: one wave per K slice of 64 chunks, up to 16
   // waves per workgroup
   const int chunks = (int)(k / kChunkElems);
   p.stream = (m == 1 && !rotated && k <= kMaxWaveKernelK) ? 1 : 0;
@@ -704,15 +807,13 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
 
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream) {
   if (plan.mfma) return gemv_b3_mfma_launch(args, blocks, plan.m, (int)rotation_block(plan.rotated), stream);
-  if (plan.stream) {
-    switch (plan.lanes) {
-      case 16: return launch_wave<16>(args, blocks, plan.iter, plan.slices, stream);
-      case 32: return launch_wave<32>(args, blocks, plan.iter, plan.slices, stream);
-      default: return launch_wave<64>(args, blocks, plan.iter, plan.slices, stream);
-    }
-  }
-  return launch_s(plan.lanes, tokens_per_pass(plan.m), (int)rotation_block(plan.rotated), plan.iter, args, blocks,
-                  stream);
+  const bool bin = plan.layout == TGS_LAYOUT_BINARY;
+  if (plan.stream)
+    return bin ? launch_wave_s<true>(plan.lanes, args, blocks, plan.iter, plan.slices, stream)
+               : launch_wave_s<false>(plan.lanes, args, blocks, plan.iter, plan.slices, stream);
+  const int rot = (int)rotation_block(plan.rotated), mt = tokens_per_pass(plan.m);
+  return bin ? launch_s<true>(plan.lanes, mt, rot, plan.iter, args, blocks, stream)
+             : launch_s<false>(plan.lanes, mt, rot, plan.iter, args, blocks, stream);
 }
 
 }  // namespace tgs

@@ -39,7 +39,12 @@ size_t row_bytes(int32_t layout, int64_t k) {
   if (k < 128 || k % 128 != 0) return 0;
   if (layout == TGS_LAYOUT_SLOT2) return (size_t)(k / 4);
   if (layout == TGS_LAYOUT_BASE3) return (size_t)(((k + 4) / 5 + 15) / 16 * 16);
+  if (layout == TGS_LAYOUT_BINARY) return (size_t)(k / 8);
   return 0;
+}
+
+bool valid_layout(int32_t layout) {
+  return layout == TGS_LAYOUT_SLOT2 || layout == TGS_LAYOUT_BASE3 || layout == TGS_LAYOUT_BINARY;
 }
 
 // Run fn(row_begin, row_end) over [0, n) on up to 16 host threads.
@@ -86,6 +91,25 @@ bool unpack_row_slot2(const uint8_t* in, int64_t k, int8_t* t) {
     for (int j = 0; j < 16; ++j) t[c + j] = (int8_t)((int)((word >> (2 * j)) & 3u) - 1);
   }
   return true;
+}
+
+// ---- binary: element j of a row in bit j%8 of byte j/8, set for +1 --------------------------
+
+bool pack_row_binary(const int8_t* t, int64_t k, uint8_t* out) {
+  for (int64_t c = 0; c < k; c += 8) {
+    uint32_t byte = 0;
+    for (int j = 0; j < 8; ++j) {
+      const int v = t[c + j];
+      if (v != 1 && v != -1) return false;
+      byte |= (uint32_t)(v == 1) << j;
+    }
+    out[c / 8] = (uint8_t)byte;
+  }
+  return true;
+}
+
+void unpack_row_binary(const uint8_t* in, int64_t k, int8_t* t) {
+  for (int64_t c = 0; c < k; ++c) t[c] = ((in[c / 8] >> (c % 8)) & 1) ? (int8_t)1 : (int8_t)-1;
 }
 
 // ---- base-3: byte b = sum_{j<5} (t[5b+j] + 1) * 3^j, pad bytes 121 -------------------------
@@ -136,8 +160,7 @@ tgs_status check_matrix(const tgs_matrix* w, bool device) {
   if (!w) return fail(TGS_E_NULL, "matrix descriptor is NULL");
   if (w->magic != TGS_MAGIC || w->version != TGS_VERSION)
     return fail(TGS_E_LAYOUT, "bad descriptor magic/version (0x%08x, %u); use tgs_matrix_init", w->magic, w->version);
-  if (w->layout != TGS_LAYOUT_SLOT2 && w->layout != TGS_LAYOUT_BASE3)
-    return fail(TGS_E_LAYOUT, "unknown layout %d", w->layout);
+  if (!valid_layout(w->layout)) return fail(TGS_E_LAYOUT, "unknown layout %d", w->layout);
   if (w->rotated != 0 && w->rotated != 1 && w->rotated != 1024)
     return fail(TGS_E_LAYOUT, "rotated must be 0, 1 (128-element blocks) or 1024, got %d", w->rotated);
   if (w->n < 1 || w->k < 128 || w->k % 128 != 0)
@@ -183,7 +206,7 @@ tgs_status tgs_matrix_init(tgs_matrix* w, int32_t layout, int32_t rotated, int64
                            const uint16_t* scales) {
   if (!w) return fail(TGS_E_NULL, "matrix descriptor is NULL");
   std::memset(w, 0, sizeof(*w));
-  if (layout != TGS_LAYOUT_SLOT2 && layout != TGS_LAYOUT_BASE3) return fail(TGS_E_LAYOUT, "unknown layout %d", layout);
+  if (!valid_layout(layout)) return fail(TGS_E_LAYOUT, "unknown layout %d", layout);
   if (n < 1 || k < 128 || k % 128 != 0) return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128");
   if (rotated != 0 && rotated != 1 && rotated != 128 && rotated != 1024)
     return fail(TGS_E_BASIS, "rotated must be 0, 1 (128-element blocks), 128 or 1024, got %d", rotated);
@@ -203,7 +226,7 @@ tgs_status tgs_matrix_init(tgs_matrix* w, int32_t layout, int32_t rotated, int64
 
 tgs_status pack_ternary(int32_t layout, const int8_t* trits, const uint16_t* scales, int64_t n, int64_t k,
                         void* codes_out, size_t codes_bytes, uint16_t* scales_out) {
-  if (layout != TGS_LAYOUT_SLOT2 && layout != TGS_LAYOUT_BASE3) return fail(TGS_E_LAYOUT, "unknown layout %d", layout);
+  if (!valid_layout(layout)) return fail(TGS_E_LAYOUT, "unknown layout %d", layout);
   if (n < 1 || k < 128 || k % 128 != 0) return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128");
   if (!trits || !codes_out) return fail(TGS_E_NULL, "trits or codes_out is NULL");
   if ((scales == nullptr) != (scales_out == nullptr))
@@ -217,12 +240,16 @@ tgs_status pack_ternary(int32_t layout, const int8_t* trits, const uint16_t* sca
     for (int64_t r = b; r < e; ++r) {
       const int8_t* t = trits + r * k;
       uint8_t* o = out + (size_t)r * rb;
-      bool good = layout == TGS_LAYOUT_SLOT2 ? pack_row_slot2(t, k, o) : pack_row_base3(t, k, rb, o);
+      bool good = layout == TGS_LAYOUT_SLOT2   ? pack_row_slot2(t, k, o)
+                  : layout == TGS_LAYOUT_BASE3 ? pack_row_base3(t, k, rb, o)
+                                               : pack_row_binary(t, k, o);
       if (!good) bad[(size_t)r] = 1;
     }
   });
   for (int64_t r = 0; r < n; ++r)
-    if (bad[(size_t)r]) return fail(TGS_E_CODE, "row %lld holds a trit outside {-1, 0, +1}", (long long)r);
+    if (bad[(size_t)r])
+      return fail(TGS_E_CODE, "row %lld holds a value outside %s", (long long)r,
+                  layout == TGS_LAYOUT_BINARY ? "{-1, +1}" : "{-1, 0, +1}");
   if (scales) std::memcpy(scales_out, scales, sizeof(uint16_t) * (size_t)n * (size_t)(k / 128));
   return ok();
 }
@@ -238,7 +265,13 @@ tgs_status unpack_ternary(const tgs_matrix* w, int8_t* trits_out, uint16_t* scal
     for (int64_t r = b; r < e; ++r) {
       const uint8_t* row = in + (size_t)r * (size_t)w->code_row_stride;
       int8_t* t = trits_out + r * w->k;
-      bool good = w->layout == TGS_LAYOUT_SLOT2 ? unpack_row_slot2(row, w->k, t) : unpack_row_base3(row, w->k, rb, t);
+      bool good = true;
+      if (w->layout == TGS_LAYOUT_SLOT2)
+        good = unpack_row_slot2(row, w->k, t);
+      else if (w->layout == TGS_LAYOUT_BASE3)
+        good = unpack_row_base3(row, w->k, rb, t);
+      else
+        unpack_row_binary(row, w->k, t);  // every byte is valid
       if (!good) bad[(size_t)r] = 1;
     }
   });

@@ -5,7 +5,8 @@ the tolerance is the oracle's per-element bound, |y - y_ref| <= 1e-3 * sum_k |s 
 Workloads (synthetic, seeded, the benchmark's shapes and value distributions):
   - 8B-class decode layer: q, k, v, o 4096 x 4096 / 1024 x 4096, gate and up 12288 x 4096, down
     4096 x 12288, M = 1, fp16 N(0, 1) activations, launched one layer at a time as q/k/v, o,
-    gate/up, down; both layouts (slot-2 with P(0) = 0.4, base-3 with P(0) = 0.5).
+    gate/up, down; all three layouts (slot-2 with P(0) = 0.4, base-3 with P(0) = 0.5, binary
+    with +1 and -1 equally likely).
   - 27B-class rotated-basis GEMV: base-3 gate 17408 x 5120 and down 5120 x 17408, M = 1 and 8,
     128- and 1024-element rotation blocks.
   - 27B-class prefill GEMM: slot-2 17408 x 5120 and 5120 x 17408, bf16 activations, M = 16, 128, 2048.
@@ -21,7 +22,7 @@ import ternary_group_scaled_amd as tgs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-LNAME = {tgs.SLOT2: "slot2", tgs.BASE3: "base3"}
+LNAME = {tgs.SLOT2: "slot2", tgs.BASE3: "base3", tgs.BINARY: "binary"}
 
 LAYER_8B = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
             ("gate", 12288, 4096), ("up", 12288, 4096), ("down", 4096, 12288)]
@@ -57,9 +58,9 @@ def _check_rows(layout, codes, scales, k, x_bits, x_dtype, y, rows, what, signs=
                           f"{float(np.nanmax(err / bound)):.3g}"
 
 
-@pytest.mark.parametrize("layout", [tgs.SLOT2, tgs.BASE3], ids=LNAME.get)
+@pytest.mark.parametrize("layout", [tgs.SLOT2, tgs.BASE3, tgs.BINARY], ids=LNAME.get)
 def test_8b_layer_as_launched_by_the_benchmark(layout):
-    p_zero = 0.4 if layout == tgs.SLOT2 else 0.5
+    p_zero = {tgs.SLOT2: 0.4, tgs.BASE3: 0.5, tgs.BINARY: 0.0}[layout]
     mats, host = {}, {}
     for name, n, k in LAYER_8B:
         w, codes, scales = _matrix(layout, f"full8b/{layout}/{name}", n, k, p_zero)

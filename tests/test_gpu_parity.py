@@ -416,3 +416,125 @@ def test_code_flips_full_size_matrix():
     ref_total, ref_rows = oracle.code_flips(tgs.SLOT2, ca, cb, 4096)
     assert int(total.item()) == ref_total
     assert (rows.cpu().numpy().astype(np.int64) == ref_rows).all()
+
+
+# ------------------------------------------------------------------------------ binary codes
+# The two-level sibling format: t in {-1, +1}, one bit per weight, the same fp16 group scales.
+
+
+def _binary_weights(seed, stream, n, k):
+    t = synth.trits(seed, synth.stream_id(stream, "codes"), (n, k), 0.0)  # {-1, +1}
+    s = synth.scales_f16(seed, synth.stream_id(stream, "scales"), (n, k // 128))
+    return t, s
+
+
+def test_binary_packing_on_the_device_path_round_trips():
+    t, s = _binary_weights(0, "binpack", 64, 1024)
+    codes, _ = tgs.pack_ternary(tgs.BINARY, t, s)
+    assert (codes == oracle.pack(tgs.BINARY, t)).all()
+    assert (tgs.unpack_ternary(tgs.BINARY, codes, s, 1024)[0] == t).all()
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 8])
+def test_binary_gemv_matches_oracle(n, k, m):
+    t, s = _binary_weights(n + k, "bingemv", n, k)
+    x16 = make_x_f16(m, f"bingemv{n}x{k}", m, k)
+    y = _gemv(tgs.BINARY, t, s, x16)
+    y_ref, bound = oracle_product(tgs.BINARY, t, s, x16.view(np.uint16), oracle.X_F16)
+    assert_within_bound(y, y_ref, bound, f"binary {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("block", [128, 1024])
+@pytest.mark.parametrize("n,k", [(33, 1024), (100, 5120), (20, 17408)])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_binary_rotated_gemv_matches_oracle(block, n, k, m):
+    t, s = _binary_weights(n + k + block, "binrot", n, k)
+    x16 = make_x_f16(m + 5, f"binrot{n}x{k}", m, k)
+    sg = make_signs(k, "binrot", k)
+    y = _gemv(tgs.BINARY, t, s, x16, signs=sg, block=block)
+    y_ref, bound = oracle_product(tgs.BINARY, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg, block=block)
+    assert_within_bound(y, y_ref, bound, f"binary rotated-{block} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 3])
+def test_binary_special_rows_and_integer_exactness(m):
+    # all +1 rows give s * sum x, all -1 rows -s * sum x; alternating signs and a single -1 among
+    # +1s too. Integer x in [-4, 4] with power-of-two scales: every partial sum is exact in fp32,
+    # so the GPU must equal the oracle bit for bit.
+    k = 4096
+    t = np.ones((6, k), dtype=np.int8)
+    t[1] = -1
+    t[2, 1::2] = -1
+    t[3, 2049] = -1
+    t[4, :] = synth.trits(7, 1, (k,), 0.0)
+    t[5, 64:] = -1
+    s = np.ldexp(1.0, synth.trits(7, 2, (6, k // 128), 0.0).astype(np.int64)).astype(np.float16)
+    xi = synth.trits(7, 3, (m, k), 0.2).astype(np.int64) * 4 + synth.trits(7, 4, (m, k), 0.3)
+    x16 = xi.astype(np.float16)
+    y = _gemv(tgs.BINARY, t, s, x16)
+    y_ref, _ = oracle_product(tgs.BINARY, t, s, x16.view(np.uint16), oracle.X_F16)
+    assert (y.astype(np.float64) == y_ref).all()
+
+
+def test_binary_batched_with_other_layouts():
+    k = 2048
+    sg = make_signs(2, "binmix", k)
+    cases = [(tgs.BINARY, 0), (tgs.SLOT2, 0), (tgs.BINARY, 128), (tgs.BASE3, 0), (tgs.BINARY, 1024)]
+    ws, xs, ys, signs, refs = [], [], [], [], []
+    for i, (layout, rot) in enumerate(cases):
+        if layout == tgs.BINARY:
+            t, s = _binary_weights(i, "binmix", 40 + i, k)
+        else:
+            t, s = make_weights(i, "binmix", 40 + i, k, 0.4)
+        x16 = make_x_f16(i, "binmix", 2, k)
+        ws.append(_packed(layout, t, s, rotated=rot))
+        xs.append(_x_dev(x16))
+        ys.append(torch.empty((2, 40 + i), dtype=torch.float32, device=DEV))
+        signs.append(torch.from_numpy(sg).to(DEV) if rot else None)
+        refs.append(oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg if rot else None,
+                                   block=rot or 128))
+    tgs.ternary_gemv_batched(ws, xs, ys, signs=signs)
+    torch.cuda.synchronize()
+    for y, (y_ref, bound) in zip(ys, refs):
+        assert_within_bound(y.cpu().numpy(), y_ref, bound, "binary mixed batch")
+
+
+@pytest.mark.parametrize("n,k", [(64, 256), (200, 2048), (130, 1280), (257, 640)])
+@pytest.mark.parametrize("m", [1, 16, 40, 128, 200])
+def test_binary_gemm_matches_oracle(n, k, m):
+    t, s = _binary_weights(n + m, "bingemm", n, k)
+    xb = make_x_bf16_bits(m, f"bingemm{n}", m, k)
+    y = _gemm(tgs.BINARY, t, s, xb)
+    y_ref, bound = oracle_product(tgs.BINARY, t, s, xb, oracle.X_BF16)
+    assert_within_bound(y, y_ref, bound, f"binary gemm {n}x{k} m={m}")
+
+
+def test_binary_gemm_integer_inputs_are_exact_and_match_gemv():
+    n, k, m = 160, 2048, 1
+    t, _ = _binary_weights(9, "bingemmexact", n, k)
+    s = np.ldexp(1.0, synth.trits(9, 5, (n, k // 128), 0.0).astype(np.int64)).astype(np.float16)
+    xi = (synth.trits(9, 6, (m, k), 0.2).astype(np.int64) * 3).astype(np.float32)
+    y_gemm = _gemm(tgs.BINARY, t, s, synth.bf16_bits(xi))
+    y_gemv = _gemv(tgs.BINARY, t, s, xi.astype(np.float16))
+    y_ref, _ = oracle_product(tgs.BINARY, t, s, xi.astype(np.float16).view(np.uint16), oracle.X_F16)
+    assert (y_gemm.astype(np.float64) == y_ref).all()
+    assert (y_gemm.view(np.uint32) == y_gemv.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("n,k,frac", [(1, 128, 0.5), (17, 384, 0.05), (300, 1280, 0.007), (129, 12288, 0.003)])
+def test_binary_code_flips_match_oracle(n, k, frac):
+    t, s = _binary_weights(n + k, "binflip", n, k)
+    mask = np.random.default_rng(n + k).random((n, k)) < frac
+    u = np.where(mask, -t, t).astype(np.int8)
+    ca, _ = tgs.pack_ternary(tgs.BINARY, t, s)
+    cb, _ = tgs.pack_ternary(tgs.BINARY, u, s)
+    sd = torch.from_numpy(s.view(np.int16)).to(DEV)
+    a = tgs.PackedMatrix(tgs.BINARY, torch.from_numpy(ca).to(DEV), sd, k)
+    b = tgs.PackedMatrix(tgs.BINARY, torch.from_numpy(cb).to(DEV), sd, k)
+    total, rows = tgs.ternary_code_flips(a, b)
+    torch.cuda.synchronize()
+    ref_total, ref_rows = oracle.code_flips(tgs.BINARY, ca, cb, k)
+    assert ref_total == int(mask.sum())
+    assert int(total.item()) == ref_total
+    assert (rows.cpu().numpy().astype(np.int64) == ref_rows).all()

@@ -36,7 +36,7 @@ def test_status_strings():
 
 @pytest.mark.parametrize("k", CONFIG_K)
 def test_row_bytes_match_oracle(k):
-    for layout in (tgs.SLOT2, tgs.BASE3):
+    for layout in (tgs.SLOT2, tgs.BASE3, tgs.BINARY):
         assert tgs.code_row_bytes(layout, k) == oracle.row_bytes(layout, k)
     assert tgs.code_row_bytes(tgs.SLOT2, 100) == 0
     assert tgs.code_row_bytes(7, 128) == 0
@@ -56,12 +56,31 @@ def test_pack_bit_exact_vs_oracle(layout, k):
     assert (s_back.view(np.uint16) == s.view(np.uint16)).all()
 
 
+@pytest.mark.parametrize("k", CONFIG_K)
+def test_binary_pack_bit_exact_vs_oracle(k):
+    n = 37
+    t = synth.trits(1, k * 10 + 3, (n, k), 0.0)  # {-1, +1}
+    s = synth.scales_f16(1, k, (n, k // 128))
+    codes, _ = tgs.pack_ternary(tgs.BINARY, t, s)
+    assert codes.shape == (n, k // 8)
+    assert (codes == oracle.pack(tgs.BINARY, t)).all()
+    back, _ = tgs.unpack_ternary(tgs.BINARY, codes, s, k)
+    assert (back == t).all()
+    # every byte value decodes (the binary layout has no invalid codes)
+    every = np.arange(n * k // 8, dtype=np.uint64).astype(np.uint8).reshape(n, k // 8)
+    back, _ = tgs.unpack_ternary(tgs.BINARY, every, s, k)
+    assert (back == oracle.unpack(tgs.BINARY, every, k)).all()
+
+
 def test_pack_large_parallel_path_is_exact():
     # big enough for the multi-threaded packer
     t = synth.trits(2, 3, (300, 12288), 0.4)
     for layout in (tgs.SLOT2, tgs.BASE3):
         codes, _ = tgs.pack_ternary(layout, t)
         assert (codes == oracle.pack(layout, t)).all()
+    t = synth.trits(2, 4, (300, 12288), 0.0)
+    codes, _ = tgs.pack_ternary(tgs.BINARY, t)
+    assert (codes == oracle.pack(tgs.BINARY, t)).all()
 
 
 def test_unpack_reads_the_oracle_bytes():
@@ -84,7 +103,9 @@ def test_pack_errors():
     _expect("TGS_E_CODE", tgs.pack_ternary, tgs.SLOT2, t)
     _expect("TGS_E_CODE", tgs.pack_ternary, tgs.BASE3, t)
     _expect("TGS_E_SHAPE", tgs.pack_ternary, tgs.SLOT2, np.zeros((2, 100), dtype=np.int8))
-    _expect("TGS_E_LAYOUT", tgs.pack_ternary, 3, np.zeros((2, 128), dtype=np.int8))
+    _expect("TGS_E_LAYOUT", tgs.pack_ternary, 4, np.zeros((2, 128), dtype=np.int8))
+    _expect("TGS_E_CODE", tgs.pack_ternary, tgs.BINARY, np.ones((2, 128), dtype=np.int8) - (t == 2))  # a zero
+    _expect("TGS_E_CODE", tgs.pack_ternary, tgs.BINARY, np.zeros((2, 128), dtype=np.int8))
     lib = tgs.lib()
     out = np.zeros(10, dtype=np.uint8)
     good = np.zeros((2, 128), dtype=np.int8)
