@@ -73,6 +73,13 @@ def _load():
         lib.orc_rotate_f64.restype = None
         lib.orc_matmul_f64.argtypes = [i32, vp, i64, vp, i64, i64, vp, i32, i64, vp, i64, vp, i64, vp, vp]
         lib.orc_matmul_f64.restype = ctypes.c_int
+        lib.orc_matmul_norm_f64.argtypes = [i32, vp, i64, vp, i64, i64, vp, i32, i64, vp, dbl, vp, i64, vp, i64, vp,
+                                            vp]
+        lib.orc_matmul_norm_f64.restype = ctypes.c_int
+        lib.orc_rmsnorm_f64.argtypes = [vp, vp, dbl, i64, i64, vp]
+        lib.orc_rmsnorm_f64.restype = ctypes.c_int
+        lib.orc_rmsnorm_rotate_f64.argtypes = [vp, i32, vp, dbl, vp, i64, i64, i64, vp]
+        lib.orc_rmsnorm_rotate_f64.restype = ctypes.c_int
         lib.orc_code_flips.argtypes = [i32, vp, i64, vp, i64, i64, i64, vp]
         lib.orc_code_flips.restype = i64
         _lib = lib
@@ -140,14 +147,43 @@ def rotate(x: np.ndarray, signs: np.ndarray, block: int = 128) -> np.ndarray:
     return out.reshape(shape)
 
 
+def rmsnorm(x: np.ndarray, gamma_bits: np.ndarray, eps: float) -> np.ndarray:
+    """x float64 [m][k] -> gamma * x / sqrt(mean(x^2) + eps) per row; gamma as bf16 bits [k]."""
+    xd = np.ascontiguousarray(x, dtype=np.float64)
+    shape = xd.shape
+    xd = xd.reshape(-1, shape[-1])
+    g = np.ascontiguousarray(gamma_bits).view(np.uint16)
+    assert g.shape == (xd.shape[1],)
+    out = np.zeros_like(xd)
+    _check(_load().orc_rmsnorm_f64(xd.ctypes.data, g.ctypes.data, float(eps), xd.shape[0], xd.shape[1],
+                                   out.ctypes.data), "rmsnorm")
+    return out.reshape(shape)
+
+
+def rmsnorm_rotate(x_bits: np.ndarray, x_dtype: int, gamma_bits: np.ndarray, eps: float,
+                   signs: np.ndarray | None, block: int = 128) -> np.ndarray:
+    """The fused operation R (RMSNorm x) (or RMSNorm x when signs is None), float64 [m][k]."""
+    xb = np.ascontiguousarray(x_bits).view(np.uint16)
+    xb = xb.reshape(-1, xb.shape[-1])
+    m, k = xb.shape
+    g = np.ascontiguousarray(gamma_bits).view(np.uint16)
+    sg = None if signs is None else np.ascontiguousarray(signs, dtype=np.int8)
+    out = np.zeros((m, k), dtype=np.float64)
+    _check(_load().orc_rmsnorm_rotate_f64(xb.ctypes.data, x_dtype, g.ctypes.data, float(eps),
+                                          sg.ctypes.data if sg is not None else None, m, k, block,
+                                          out.ctypes.data), "rmsnorm_rotate")
+    return out
+
+
 def matmul(layout: int, codes: np.ndarray, scales: np.ndarray, k: int, x_bits: np.ndarray,
-           x_dtype: int, signs: np.ndarray | None = None, rows: np.ndarray | None = None, block: int = 128):
+           x_dtype: int, signs: np.ndarray | None = None, rows: np.ndarray | None = None, block: int = 128,
+           gamma: np.ndarray | None = None, eps: float = 0.0):
     """Reference product. Returns (y, bound), both float64 [m][n_sel].
 
     codes uint8 [n][stride]; scales fp16 (float16 or uint16 bits) [n][k/128];
     x_bits uint16 bit patterns [m][k] (fp16 or bf16 per x_dtype); signs int8 [k] or None;
     rows: int64 row indices to evaluate, or None for all rows; block: rotation block (128 or
-    1024) when signs are given.
+    1024) when signs are given; gamma: bf16 bits [k] to RMS-normalise x first (with eps > 0).
     """
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     n, stride = c.shape
@@ -165,11 +201,16 @@ def matmul(layout: int, codes: np.ndarray, scales: np.ndarray, k: int, x_bits: n
     if signs is not None:
         sg = np.ascontiguousarray(signs, dtype=np.int8)
         assert sg.shape == (k,)
+    g = None
+    if gamma is not None:
+        g = np.ascontiguousarray(gamma).view(np.uint16)
+        assert g.shape == (k,)
     y = np.zeros((m, n_sel), dtype=np.float64)
     bound = np.zeros((m, n_sel), dtype=np.float64)
-    rc = _load().orc_matmul_f64(layout, c.ctypes.data, stride, s.ctypes.data, n, k, xb.ctypes.data,
-                                x_dtype, m, sg.ctypes.data if sg is not None else None, block, r_ptr, n_sel,
-                                y.ctypes.data, bound.ctypes.data)
+    rc = _load().orc_matmul_norm_f64(layout, c.ctypes.data, stride, s.ctypes.data, n, k, xb.ctypes.data,
+                                     x_dtype, m, g.ctypes.data if g is not None else None, float(eps),
+                                     sg.ctypes.data if sg is not None else None, block, r_ptr, n_sel,
+                                     y.ctypes.data, bound.ctypes.data)
     _check(rc, "matmul")
     return y, bound
 

@@ -29,6 +29,16 @@
  *     loader insists on (P3 page, section "Running in the browser with
  *     WebGPU").
  *
+ * Optionally the activation is first normalised with RMSNorm, x^ = gamma * x /
+ * sqrt(mean_k x^2 + eps) per row, and x^ takes the place of x above: the
+ * BlockHadamard operation of the P3 page's WebGPU runtime has a variant fused
+ * with RMSNorm (section "Running in the browser with WebGPU"), and the norm
+ * weights gamma stay in bf16, neither rotated nor quantised (section "The
+ * 0.0976% kept at high precision"). The pages do not write the norm out; this is
+ * the usual root-mean-square normalisation over the row (the mean of the squares
+ * over all K entries, eps added inside the square root), gamma applied
+ * elementwise after the division.
+ *
  * Every step is done the obvious way: each row is unpacked from its packed
  * bytes by a bit-by-bit loop, dequantised to doubles (fp16/bf16 -> double is
  * exact), and multiplied; the rotation is a dense n x n matrix-vector
@@ -263,6 +273,52 @@ int orc_load_x(const uint16_t* x, int32_t x_dtype, int64_t count, double* out) {
   return ORC_OK;
 }
 
+/* RMSNorm of each row of x [m][k] (doubles): out = gamma * x / sqrt(sum_c x^2 / k + eps), gamma
+ * given as bf16 bits [k]. eps must be > 0. */
+int orc_rmsnorm_f64(const double* x, const uint16_t* gamma, double eps, int64_t m, int64_t k, double* out) {
+  if (m < 1 || k < 1 || !(eps > 0.0)) return ORC_BAD_SHAPE;
+  for (int64_t r = 0; r < m; ++r) {
+    const double* xr = x + r * k;
+    double sq = 0.0;
+    for (int64_t c = 0; c < k; ++c) sq += xr[c] * xr[c];
+    double rms = sqrt(sq / (double)k + eps);
+    for (int64_t c = 0; c < k; ++c) out[r * k + c] = orc_bf16_to_f64(gamma[c]) * xr[c] / rms;
+  }
+  return ORC_OK;
+}
+
+/* The activation the product uses: x, optionally RMS-normalised (gamma != NULL), then
+ * optionally rotated (sign != NULL). out: [m][k] doubles. */
+static int prepare_x(const uint16_t* x, int32_t x_dtype, const uint16_t* gamma, double eps, const int8_t* sign,
+                     int64_t block, int64_t m, int64_t k, double* out) {
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(m * k));
+  if (!xd) return ORC_BAD_SHAPE;
+  int rc = orc_load_x(x, x_dtype, m * k, xd);
+  if (rc == ORC_OK && gamma) {
+    double* xn = (double*)malloc(sizeof(double) * (size_t)(m * k));
+    if (!xn) rc = ORC_BAD_SHAPE;
+    else {
+      rc = orc_rmsnorm_f64(xd, gamma, eps, m, k, xn);
+      free(xd);
+      xd = xn;
+    }
+  }
+  if (rc == ORC_OK) {
+    if (sign) orc_rotate_f64(xd, sign, m, k, block, out);
+    else memcpy(out, xd, sizeof(double) * (size_t)(m * k));
+  }
+  free(xd);
+  return rc;
+}
+
+/* The standalone fused operation: out = R (RMSNorm x), or RMSNorm x when sign is NULL. */
+int orc_rmsnorm_rotate_f64(const uint16_t* x, int32_t x_dtype, const uint16_t* gamma, double eps,
+                           const int8_t* sign, int64_t m, int64_t k, int64_t block, double* out) {
+  if (m < 1 || k <= 0 || !gamma) return ORC_BAD_SHAPE;
+  if (sign && ((block != 128 && block != 1024) || k % block != 0)) return ORC_BAD_SHAPE;
+  return prepare_x(x, x_dtype, gamma, eps, sign, block, m, k, out);
+}
+
 /*
  * y[m][j] and bound[m][j] for the selected rows n = rows[j] (all rows if rows == NULL,
  * then n_sel must equal n).
@@ -271,11 +327,12 @@ int orc_load_x(const uint16_t* x, int32_t x_dtype, int64_t count, double* out) {
  * codes: [n][row_stride] bytes, scales: [n][k/128] fp16 bits, x: [m][k] fp16/bf16 bits,
  * sign: [k] (+-1) or NULL for the unrotated basis.
  */
-int orc_matmul_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
-                   const uint16_t* scales, int64_t n, int64_t k,
-                   const uint16_t* x, int32_t x_dtype, int64_t m,
-                   const int8_t* sign, int64_t block, const int64_t* rows, int64_t n_sel,
-                   double* y, double* bound) {
+int orc_matmul_norm_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
+                        const uint16_t* scales, int64_t n, int64_t k,
+                        const uint16_t* x, int32_t x_dtype, int64_t m,
+                        const uint16_t* gamma, double eps,
+                        const int8_t* sign, int64_t block, const int64_t* rows, int64_t n_sel,
+                        double* y, double* bound) {
   if (k <= 0 || k % 128 != 0 || m < 1 || n < 0) return ORC_BAD_SHAPE;
   if (sign && (block != 128 && block != 1024)) return ORC_BAD_SHAPE;
   if (sign && k % block != 0) return ORC_BAD_SHAPE;
@@ -283,15 +340,9 @@ int orc_matmul_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
   if (row_stride < orc_row_bytes(layout, k)) return ORC_BAD_SHAPE;
   if (rows == NULL && n_sel != n) return ORC_BAD_SHAPE;
 
-  double* xd = (double*)malloc(sizeof(double) * (size_t)(m * k));
   double* xr = (double*)malloc(sizeof(double) * (size_t)(m * k));
-  if (!xd || !xr) { free(xd); free(xr); return ORC_BAD_SHAPE; }
-  int rc = orc_load_x(x, x_dtype, m * k, xd);
-  if (rc == ORC_OK) {
-    if (sign) orc_rotate_f64(xd, sign, m, k, block, xr);
-    else memcpy(xr, xd, sizeof(double) * (size_t)(m * k));
-  }
-  free(xd);
+  if (!xr) return ORC_BAD_SHAPE;
+  int rc = prepare_x(x, x_dtype, gamma, eps, sign, block, m, k, xr);
   if (rc != ORC_OK) { free(xr); return rc; }
 
   int status = ORC_OK;
@@ -321,6 +372,16 @@ int orc_matmul_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
   }
   free(xr);
   return status;
+}
+
+/* The product without the norm (gamma == NULL). */
+int orc_matmul_f64(int32_t layout, const uint8_t* codes, int64_t row_stride,
+                   const uint16_t* scales, int64_t n, int64_t k,
+                   const uint16_t* x, int32_t x_dtype, int64_t m,
+                   const int8_t* sign, int64_t block, const int64_t* rows, int64_t n_sel,
+                   double* y, double* bound) {
+  return orc_matmul_norm_f64(layout, codes, row_stride, scales, n, k, x, x_dtype, m, NULL, 0.0, sign, block, rows,
+                             n_sel, y, bound);
 }
 
 /* ---- code flips between two packed checkpoints ---- */

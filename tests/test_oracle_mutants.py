@@ -28,7 +28,11 @@ MUTANTS = {
     "f16_exponent_bias": ("v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
     "f16_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
     "bf16_mantissa_width": ("v = ldexp((double)(128 + m), e - 134);", "v = ldexp((double)(256 + m), e - 135);"),
-    "rotation_block_ignored": ("orc_rotate_f64(xd, sign, m, k, block, xr);", "orc_rotate_f64(xd, sign, m, k, 128, xr);"),
+    "rotation_block_ignored": ("orc_rotate_f64(xd, sign, m, k, block, out);", "orc_rotate_f64(xd, sign, m, k, 128, out);"),
+    "rmsnorm_mean_denominator": ("sqrt(sq / (double)k + eps)", "sqrt(sq / (double)(k - 1) + eps)"),
+    "rmsnorm_eps_outside_sqrt": ("sqrt(sq / (double)k + eps)", "(sqrt(sq / (double)k) + eps)"),
+    "rmsnorm_gamma_index": ("orc_bf16_to_f64(gamma[c]) * xr[c]", "orc_bf16_to_f64(gamma[k - 1 - c]) * xr[c]"),
+    "rmsnorm_skipped_in_product": ("if (rc == ORC_OK && gamma) {", "if (rc == ORC_OK && gamma && 0) {"),
     "flips_dropped_last_trit": ("for (int64_t i = 0; i < k; ++i) c += ta[i] != tb[i];",
                                 "for (int64_t i = 0; i + 1 < k; ++i) c += ta[i] != tb[i];"),
     "binary_bit_order": ("codes[r * rb + c / 8] |= (uint8_t)(1u << (c % 8));",

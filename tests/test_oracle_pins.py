@@ -542,6 +542,106 @@ def test_golden_small_product():
         assert (y[0] == expect).all()
 
 
+# ---------------------------------------------------------------- RMSNorm (P3, "Running in the browser with WebGPU")
+# The fused BlockHadamard + RMSNorm variant; norm weights gamma in bf16 (P3, "The 0.0976% kept at
+# high precision"). Reading: xhat = gamma * x / sqrt(mean(x^2) + eps) per row.
+
+def _bf16(values):
+    return synth.bf16_bits(np.asarray(values, dtype=np.float64))
+
+
+def _rmsnorm_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "rmsnorm_example.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, xs, eps, gs, outs = [part.strip() for part in line.split(";")]
+            cases.append((name, [float(v) for v in xs.split()], float(eps), [float(v) for v in gs.split()],
+                          [float(v) for v in outs.split()]))
+    return cases
+
+
+@pytest.mark.parametrize("name,x_prefix,eps,g_prefix,expect", _rmsnorm_cases())
+def test_rmsnorm_hand_examples(name, x_prefix, eps, g_prefix, expect):
+    k = 128
+    if name == "A":
+        x = np.zeros(k)
+        gamma = np.ones(k)
+    else:
+        x = np.ones(k)
+        gamma = np.where(np.arange(k) % 2 == 0, 1.0, -1.0)
+    x[:len(x_prefix)] = x_prefix
+    gamma[:len(g_prefix)] = g_prefix
+    out = oracle.rmsnorm(x[None, :], _bf16(gamma), eps)[0]
+    assert list(out[:len(expect)]) == expect
+    if name == "A":
+        assert (out[len(expect):] == 0).all()
+    else:
+        assert (np.abs(out) == 0.5).all()
+
+
+def test_rmsnorm_gives_unit_root_mean_square():
+    x = synth.normal(5, 1, (3, 1024)) * np.array([[0.01], [1.0], [300.0]])
+    out = oracle.rmsnorm(x, _bf16(np.ones(1024)), 1e-300)
+    assert np.allclose(np.sqrt((out ** 2).mean(axis=1)), 1.0, rtol=1e-14)
+
+
+def test_rmsnorm_is_invariant_to_power_of_two_scaling():
+    # gamma * (a x) / sqrt(mean((a x)^2) + a^2 eps) = gamma * x / sqrt(mean(x^2) + eps) exactly for a = 2^j
+    x = synth.normal(5, 2, (2, 640))
+    g = _bf16(synth.normal(5, 3, (640,)))
+    base = oracle.rmsnorm(x, g, 1e-3)
+    for j in (-3, 4):
+        a = 2.0 ** j
+        assert (oracle.rmsnorm(a * x, g, 1e-3 * a * a) == base).all()
+
+
+def test_rmsnorm_applies_gamma_per_element_and_rows_independently():
+    x = synth.normal(6, 1, (3, 384))
+    gvals = synth.normal(6, 2, (384,))
+    g = _bf16(gvals)
+    g_exact = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out = oracle.rmsnorm(x, g, 1e-5)
+    ones = oracle.rmsnorm(x, _bf16(np.ones(384)), 1e-5)
+    assert np.allclose(out, ones * g_exact[None, :], rtol=1e-15, atol=0)
+    for r in range(3):  # each row is normalised by its own root mean square
+        assert (oracle.rmsnorm(x[r:r + 1], g, 1e-5)[0] == out[r]).all()
+
+
+def test_rmsnorm_refuses_nonpositive_eps():
+    with pytest.raises(oracle.OracleError):
+        oracle.rmsnorm(np.ones((1, 128)), _bf16(np.ones(128)), 0.0)
+
+
+@pytest.mark.parametrize("layout", [oracle.SLOT2, oracle.BASE3, oracle.BINARY])
+@pytest.mark.parametrize("block", [None, 128, 1024])
+def test_rmsnorm_product_brute_force(layout, block):
+    k, n, m = 1024, 4, 2
+    t = synth.trits(9, layout, (n, k), 0.0 if layout == oracle.BINARY else 0.4)
+    s = synth.scales_f16(9, 2, (n, k // 128))
+    x16 = (synth.x_f16(9, 3, (m, k)).astype(np.float32) * 20).astype(np.float16)
+    gvals = synth.normal(9, 4, (k,))
+    g = _bf16(gvals)
+    sg = synth.signs(9, 5, k) if block else None
+    eps = 1e-6
+    y, bound = oracle.matmul(layout, oracle.pack(layout, t), s, k, x16.view(np.uint16), oracle.X_F16, signs=sg,
+                             block=block or 128, gamma=g, eps=eps)
+    xd = x16.astype(np.float64)
+    g_exact = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    xn = g_exact * xd / np.sqrt((xd ** 2).mean(axis=1, keepdims=True) + np.float64(np.float32(eps)))
+    if block:
+        xn = xn @ _dense_rotation(sg, block).T
+    terms = xn[:, None, :] * _dense_weights(t, s)[None, :, :]
+    assert np.allclose(y, terms.sum(axis=2), rtol=1e-12, atol=1e-13)
+    assert np.allclose(bound, 1e-3 * np.abs(terms).sum(axis=2) + 1e-6, rtol=1e-12)
+    # the standalone fused operation gives the same activation
+    if block:
+        fused = oracle.rmsnorm_rotate(x16.view(np.uint16), oracle.X_F16, g, eps, sg, block)
+        assert np.allclose(fused, xn, rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- code flips (P1, opening section)
 # A code flip is a weight whose code changed between two checkpoints. The pins plant flips at
 # positions the test chooses and compare with that known count, so a count of changed bytes or
