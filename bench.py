@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8b", choices=["8b", "base3", "binary", "rotated", "gemm", "flips", "config1"])
+    ap.add_argument("--workload", default="8b",
+                    choices=["8b", "base3", "binary", "rotated", "gemm", "flips", "rmsnorm", "config1"])
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the set (default: 36 for the 8B-class sets, 64 for the rotated 27B-class set)")
     ap.add_argument("--mode", default="layer", choices=["layer", "fused-layer", "set"],
@@ -114,6 +115,7 @@ def time_graph(torch, fn, steps, warmup):
 
 
 KERNEL_SOURCES = ["ternary_group_scaled_amd/csrc/gemv.hip", "ternary_group_scaled_amd/csrc/lane_ops.h",
+                  "ternary_group_scaled_amd/csrc/rms_norm.h",
                   "ternary_group_scaled_amd/csrc/tgs_internal.h", "ternary_group_scaled_amd/csrc/tgs_host.cpp"]
 
 
@@ -359,6 +361,54 @@ def bench_gemm(args, torch, tgs, synth):
     return res
 
 
+def bench_rmsnorm(args, torch, tgs, synth):
+    """The RMSNorm prologue on the launches that read a normalised input in an 8B-class layer
+    (q/k/v after the input norm, gate/up after the post-attention norm), 36 layers, M = 1, for
+    slot-2 and base-3 codes: the same launches timed with and without the fused norm."""
+    layers = args.layers or 36
+    res = []
+    for layout, p_zero, name in ((1, 0.4, "slot2"), (2, 0.5, "base3")):
+        log(f"[bench] rmsnorm prologue, {name}, {layers} layers")
+        groups = [("q", "k", "v"), ("gate", "up")]
+        shapes = {nm: (n, k) for nm, n, k in LAYER_8B}
+        plain, normed = [], []
+        nbytes = 0
+        keep = []
+        for L in range(layers):
+            for grp in groups:
+                k = shapes[grp[0]][1]
+                ws = [build_matrix(torch, tgs, synth, layout, 0, f"nrm/{name}/L{L}/{nm}", shapes[nm][0], k, p_zero)[0]
+                      for nm in grp]
+                x = (x_f16_dev(torch, synth, 0, f"nrm/L{L}/{grp[0]}", 1, k)[0].float() * 5.0).half()
+                g = torch.from_numpy(synth.bf16_bits(1.0 + 0.25 * synth.normal(0, synth.stream_id("nrm/g", L, grp[0]),
+                                                                               (k,))).view(np.int16)).cuda()
+                ys = [torch.empty((1, shapes[nm][0]), dtype=torch.float32, device="cuda") for nm in grp]
+                keep.append((ws, x, g, ys))
+                nbytes += sum(w.nbytes for w in ws) + 2 * k + 2 * k + sum(y.numel() * 4 for y in ys)
+                plain.append((lambda a, b, c: lambda: tgs.ternary_gemv_batched(a, b, c))(ws, [x] * len(ws), ys))
+                normed.append((lambda a, b, gg, c: lambda: tgs.ternary_gemv_rmsnorm_batched(a, b, gg, 1e-6, c))(
+                    ws, [x] * len(ws), [g] * len(ws), ys))
+        times = {}
+        for label, launches in (("plain", plain), ("rmsnorm", normed)):
+            def one_pass(launches=launches):
+                for fn in launches:
+                    fn()
+            ms, _ = time_graph(torch, one_pass, args.steps, args.warmup)
+            times[label] = ms
+            log(f"[bench] {name} {label}: step {ms * 1e3:.1f} us, {ms * 1e3 / len(launches):.2f} us per launch, "
+                f"{nbytes / ms / 1e6:.0f} GB/s")
+        res.append({"metric": "GEMV with fused RMSNorm prologue, achieved GB/s, 8B-class q/k/v + gate/up launches, M=1",
+                    "value": round(nbytes / times["rmsnorm"] / 1e6, 1), "unit": "GB/s",
+                    "ms_per_step": round(times["rmsnorm"], 5), "ms_per_step_without_norm": round(times["plain"], 5),
+                    "norm_overhead_pct": round(100 * (times["rmsnorm"] / times["plain"] - 1), 1),
+                    "launches_per_step": len(normed),
+                    "config": {"workload": f"8B-class q/k/v and gate/up launches with the RMSNorm prologue, {name}, "
+                                           f"{layers} layers, M=1", "bytes_per_step": int(nbytes)}})
+        del keep, plain, normed
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_flips(args, torch, tgs, synth):
     """Code flips between two checkpoints of the 8B-class set (every matrix of 36 layers), one line
     per layout: the second checkpoint is the first with 0.7% of its codes changed (the rate the
@@ -486,6 +536,8 @@ def main():
         out = bench_gemm(args, torch, tgs, synth)
     elif args.workload == "flips":
         out = bench_flips(args, torch, tgs, synth)
+    elif args.workload == "rmsnorm":
+        out = bench_rmsnorm(args, torch, tgs, synth)
     else:
         args.layers = 1
         out = [bench_8b(args, torch, tgs, synth)]

@@ -232,6 +232,46 @@ tgs_status ternary_code_flips_batched(const tgs_matrix* as, const tgs_matrix* bs
 tgs_status hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block,
                            const int8_t* signs, void* y, int32_t y_dtype, void* stream);
 
+/*
+ * ternary_gemv_rmsnorm (device): ternary_gemv of the RMS-normalised activation,
+ *   y[i][j] = sum_k s[j][k/128] * t[j][k] * xr[i][k],   xr = R xhat (rotated weights) or xhat,
+ *   xhat[i][k] = gamma[k] * x[i][k] / sqrt((1/K) sum_c x[i][c]^2 + eps).
+ * [P3] section "Running in the browser with WebGPU": the BlockHadamard operation has a variant
+ * fused with RMSNorm; section "The 0.0976% kept at high precision": the norm weights
+ * (input/post-attention layernorm) stay in bf16, neither rotated nor quantised. The pages do not
+ * write the norm out; this is the usual root-mean-square normalisation over each row.
+ *   gamma   device [k] bf16 bit patterns, 16-byte aligned
+ *   eps     > 0 and finite, else TGS_E_SHAPE
+ *   other arguments, rules and errors as ternary_gemv.
+ * Each workgroup computes the rows' sums of squares itself (fp32, fixed order, so results stay
+ * identical run to run); xhat (rotated or not) is rounded once to fp16.
+ */
+tgs_status ternary_gemv_rmsnorm(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m,
+                                const uint16_t* gamma, float eps, const int8_t* signs, float* y,
+                                void* stream);
+
+/*
+ * ternary_gemv_rmsnorm_batched (device): count ternary_gemv_rmsnorm calls sharing m, x_dtype and
+ * eps, as in ternary_gemv_batched; gammas is a host array of count device pointers (none NULL).
+ */
+tgs_status ternary_gemv_rmsnorm_batched(const tgs_matrix* ws, int32_t count, const void* const* xs,
+                                        int32_t x_dtype, int64_t m, const uint16_t* const* gammas,
+                                        float eps, const int8_t* const* signs, float* const* ys,
+                                        void* stream);
+
+/*
+ * rmsnorm_hadamard_rotate (device): y = R xhat with xhat the RMSNorm of each row of x as in
+ * ternary_gemv_rmsnorm and R the block rotation of hadamard_rotate: the BlockHadamard variant
+ * fused with RMSNorm of [P3] "Running in the browser with WebGPU".
+ *   gamma   device [k] bf16 bit patterns, 2-byte aligned
+ *   eps     > 0 and finite
+ *   k       a multiple of block below 2^24; m below 2^31
+ *   other arguments and rules as hadamard_rotate. One workgroup per row.
+ */
+tgs_status rmsnorm_hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block,
+                                   const uint16_t* gamma, float eps, const int8_t* signs, void* y,
+                                   int32_t y_dtype, void* stream);
+
 /* Static text for a status code. */
 const char* tgs_status_string(tgs_status status);
 

@@ -61,12 +61,18 @@ _lib.ternary_gemv_batched.argtypes = [ctypes.POINTER(Matrix), _i32, ctypes.POINT
 _lib.ternary_gemm.argtypes = [ctypes.POINTER(Matrix), _vp, _i32, _i64, _vp, _vp, _vp]
 _lib.hadamard_rotate_g128.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]
 _lib.hadamard_rotate.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i32, _vp]
+_lib.ternary_gemv_rmsnorm.argtypes = [ctypes.POINTER(Matrix), _vp, _i32, _i64, _vp, ctypes.c_float, _vp, _vp, _vp]
+_lib.ternary_gemv_rmsnorm_batched.argtypes = [ctypes.POINTER(Matrix), _i32, ctypes.POINTER(_vp), _i32, _i64,
+                                              ctypes.POINTER(_vp), ctypes.c_float, ctypes.POINTER(_vp),
+                                              ctypes.POINTER(_vp), _vp]
+_lib.rmsnorm_hadamard_rotate.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _i32, _vp]
 _lib.ternary_code_flips.argtypes = [ctypes.POINTER(Matrix), ctypes.POINTER(Matrix), _vp, _vp, _vp]
 _lib.ternary_code_flips_batched.argtypes = [ctypes.POINTER(Matrix), ctypes.POINTER(Matrix), _i32,
                                             ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]
 for _name in ("tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv", "ternary_gemv_batched",
               "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
-              "ternary_code_flips_batched"):
+              "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
+              "rmsnorm_hadamard_rotate"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.tgs_status_string.argtypes = [ctypes.c_int]
 _lib.tgs_status_string.restype = ctypes.c_char_p
@@ -75,7 +81,8 @@ _lib.tgs_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("tgs_code_row_bytes", "tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv",
            "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
-           "ternary_code_flips_batched", "tgs_status_string", "tgs_last_error")
+           "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
+           "rmsnorm_hadamard_rotate", "tgs_status_string", "tgs_last_error")
 
 
 def _check(status: int):
@@ -199,6 +206,48 @@ def ternary_gemv_batched(ws, xs, ys, signs=None, stream=None):
         sp = (_vp * count)(*[s.data_ptr() if s is not None else None for s in signs])
     _check(_lib.ternary_gemv_batched(descs, count, xp, F16, m, sp, yp, _stream_handle(stream)))
     return ys
+
+
+def ternary_gemv_rmsnorm(w: PackedMatrix, x, gamma, eps, signs=None, y=None, stream=None):
+    """y[m][n] (fp32) = W (R) RMSNorm(x) for fp16 x [m][k], m <= 8; gamma: bf16 [k]. Returns y."""
+    torch = _torch()
+    x2 = x.reshape(-1, w.k)
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
+    _check(_lib.ternary_gemv_rmsnorm(ctypes.byref(w.desc), x2.data_ptr(), F16, m, gamma.data_ptr(), float(eps),
+                                     signs.data_ptr() if signs is not None else None, y.data_ptr(),
+                                     _stream_handle(stream)))
+    return y
+
+
+def ternary_gemv_rmsnorm_batched(ws, xs, gammas, eps, ys, signs=None, stream=None):
+    """ternary_gemv_batched with the RMSNorm prologue (one bf16 gamma [k] per matrix)."""
+    count = len(ws)
+    descs = (Matrix * count)(*[w.desc for w in ws])
+    m = xs[0].reshape(-1, ws[0].k).shape[0]
+    xp = (_vp * count)(*[x.data_ptr() for x in xs])
+    gp = (_vp * count)(*[g.data_ptr() for g in gammas])
+    yp = (_vp * count)(*[y.data_ptr() for y in ys])
+    sp = None
+    if signs is not None:
+        sp = (_vp * count)(*[s.data_ptr() if s is not None else None for s in signs])
+    _check(_lib.ternary_gemv_rmsnorm_batched(descs, count, xp, F16, m, gp, float(eps), sp, yp, _stream_handle(stream)))
+    return ys
+
+
+def rmsnorm_hadamard_rotate(x, gamma, eps, signs, block=128, y=None, out_dtype=None, stream=None):
+    """R RMSNorm(x) per row of x [m][k] (fp16/bf16/fp32), gamma bf16 [k]; fp16/fp32 output."""
+    torch = _torch()
+    dt = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    k = x.shape[-1]
+    x2 = x.reshape(-1, k)
+    if y is None:
+        y = torch.empty(x2.shape, dtype=out_dtype or torch.float32, device=x.device)
+    _check(_lib.rmsnorm_hadamard_rotate(x2.data_ptr(), dt[x2.dtype], x2.shape[0], k, block, gamma.data_ptr(),
+                                        float(eps), signs.data_ptr(), y.data_ptr(), dt[y.dtype],
+                                        _stream_handle(stream)))
+    return y
 
 
 def ternary_gemm(w: PackedMatrix, x, y=None, stream=None):

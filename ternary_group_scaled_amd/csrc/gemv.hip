@@ -49,10 +49,17 @@
 //
 // Scales are applied in fp32 per chunk; partial sums are reduced across the S lanes of a row in
 // a fixed order: results are identical run to run.
+//
+// With the RMSNorm prologue (a runtime flag of the launch; the single-token kernel does not take
+// it), each pass of tokens first computes 1 / rms of its rows over all of K (rms_norm.h); the
+// staging step then multiplies every activation by gamma and that factor in fp32, before the
+// rotation (if any) and the one rounding to fp16.
 #include <type_traits>
 
 #include "lane_ops.h"
+#include "rms_norm.h"
 #include "tgs_internal.h"
+
 
 namespace tgs {
 namespace {
@@ -211,10 +218,14 @@ __device__ __forceinline__ float chunk_value(const ChunkCodes<BIN>& cw, const ui
 // Rotated basis: each wave rotates whole 128-blocks into lds_x (fp16):
 // x -> (1/sqrt(128)) H_128 diag(sign) x, H in natural Sylvester order, computed in fp32 with an
 // in-register butterfly (lane l holds elements l and l + 64), then rounded once to fp16.
+// With gamma set, each activation is first multiplied by gamma[k] and 1 / rms of its token
+// (RMSNorm), computed from the per-wave sums of squares norm_part[t * WAVES + w] (LDS).
 template <int MT, int WAVES, int BLOCK>
 __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint16_t* x, const int8_t* sign,
-                                              int k, int m, int m0, int k_begin) {
+                                              int k, int m, int m0, int k_begin, const uint16_t* gamma,
+                                              const float* norm_part, float eps) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto token_rinv = [&](int t) { return rms_inverse(norm_part, t, WAVES, k, eps); };
   if constexpr (BLOCK == 1024) {
     // 1024-element blocks (k and the slice are multiples of 1024): lane l holds elements
     // 16 l .. 16 l + 15; four butterfly stages inside the lane, six with lane l ^ s
@@ -237,6 +248,20 @@ __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint
       for (int i = 0; i < 16; ++i) {
         const float xv = f16_to_f32((uint16_t)(xw[i / 2] >> (16 * (i & 1))));
         v[i] = xv * (float)(int8_t)(sw[i / 4] >> (8 * (i & 3)));
+      }
+      if (gamma) {
+        const float r = token_rinv(t);
+        uint4 g[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+        if (kb < k) {
+          g[0] = reinterpret_cast<const uint4*>(gamma + kb)[0];
+          g[1] = reinterpret_cast<const uint4*>(gamma + kb)[1];
+        }
+        const uint32_t gw[8] = {g[0].x, g[0].y, g[0].z, g[0].w, g[1].x, g[1].y, g[1].z, g[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[2 * i] *= bf16_lo(gw[i]) * r;
+          v[2 * i + 1] *= bf16_hi(gw[i]) * r;
+        }
       }
 #pragma unroll
       for (int h = 1; h < 16; h <<= 1)
@@ -280,6 +305,11 @@ __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint
       const uint16_t* xb = x + (int64_t)(m0 + t) * k + kb;
       v0 = f16_to_f32(xb[lane]) * (float)sign[kb + lane];
       v1 = f16_to_f32(xb[lane + 64]) * (float)sign[kb + lane + 64];
+      if (gamma) {
+        const float r = token_rinv(t);
+        v0 *= __builtin_bit_cast(float, (uint32_t)gamma[kb + lane] << 16) * r;
+        v1 *= __builtin_bit_cast(float, (uint32_t)gamma[kb + lane + 64] << 16) * r;
+      }
     }
     float a = v0 + v1, c = v0 - v1;
     v0 = a;
@@ -323,6 +353,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
   __shared__ uint4 lds_pairs[MT * kGran * S];                                          // [t][granule][chunk]
   __shared__ float lds_ref[MT * S];                                                    // [t][chunk]
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[ROT ? MT * kSliceElems : 8];  // rotated staging
+  __shared__ float lds_norm[MT * kWaves];                                              // RMSNorm partial sums
 
   const GemvJob job = gemv_job_of_block(args);  // uniform
   const int n = job.n, k = job.k, m = args.m;
@@ -367,6 +398,12 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
   };
 
   for (int m0 = 0; m0 < m; m0 += MT) {
+    // RMSNorm: the sums of squares of this pass's rows, read by the staging steps below (the
+    // previous pass's last reads of lds_norm came before its last barrier)
+    if (args.norm) {
+      rms_partials<MT>(job.x, k, m, m0, lds_norm, kThreads);
+      __syncthreads();
+    }
     float part[kIter][MT];
 #pragma unroll
     for (int it = 0; it < kIter; ++it)
@@ -388,7 +425,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
       // ---- stage: pairs and all-zero-row products of the slice's chunks, once per workgroup
       __syncthreads();  // the previous slice's pairs are no longer read
       if constexpr (ROT) {
-        stage_rotated<MT, kWaves, ROT>(lds_x, kSliceElems, job.x, job.signs, k, m, m0, k_begin);
+        stage_rotated<MT, kWaves, ROT>(lds_x, kSliceElems, job.x, job.signs, k, m, m0, k_begin,
+                                       args.norm ? job.gamma : nullptr, lds_norm, args.eps);
         __syncthreads();
       }
       for (int u = tid; u < MT * S; u += kThreads) {
@@ -402,7 +440,15 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
           if constexpr (ROT) {
             q = *reinterpret_cast<const uint4*>(lds_x + t * kSliceElems + bc * kChunkElems + 8 * v);
           } else {
-            if (m0 + t < m && kk < k) q = *reinterpret_cast<const uint4*>(job.x + (int64_t)(m0 + t) * k + kk);
+            if (m0 + t < m && kk < k) {
+              q = *reinterpret_cast<const uint4*>(job.x + (int64_t)(m0 + t) * k + kk);
+              if (args.norm) {
+                const float r = rms_inverse(lds_norm, t, kWaves, k, args.eps);
+                const uint4 g = *reinterpret_cast<const uint4*>(job.gamma + kk);
+                q = make_uint4(norm_word(q.x, g.x, r), norm_word(q.y, g.y, r), norm_word(q.z, g.z, r),
+                               norm_word(q.w, g.w, r));
+              }
+            }
           }
           w[4 * v + 0] = q.x;
           w[4 * v + 1] = q.y;
@@ -557,12 +603,17 @@ __device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& 
   }
 }
 
-template <int S, int G, bool BIN>
-__global__ __launch_bounds__(1024)
+// NORM: the RMSNorm prologue. The lane's 64 activations are in its registers, so the sum of
+// squares costs a few FMAs per lane; the waves' sums meet in LDS after one barrier (by then every
+// wave's first weight loads are in flight), and each lane scales its activations by gamma and
+// 1 / rms before building its dot2 pairs. At most 8 waves (K <= 32768) in this variant.
+template <int S, int G, bool BIN, bool NORM>
+__global__ __launch_bounds__(NORM ? 512 : 1024)
 void gemv_wave_kernel(const GemvArgs args) {
   constexpr int kRowsPerInstr = 64 / S;
   constexpr int kRing = G;  // batches per group: 4, or 1-2 for waves of 2-4 rows
   extern __shared__ float lds_acc[];  // [slices][rows of the workgroup], only when slices > 1
+  __shared__ float norm_part[NORM ? 8 : 1];  // RMSNorm: sum of squares of each wave's K slice
 
   const GemvJob job = gemv_job_of_block(args);  // a copy: the fields stay in scalar registers
   const int n = job.n, k = job.k;
@@ -586,7 +637,7 @@ void gemv_wave_kernel(const GemvArgs args) {
   const __amdgpu_buffer_rsrc_t scale_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)job.scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
 
-  // 1. activations of this lane's chunk (reads past K return zero)
+  // 1. activations of this lane's chunk (reads past K return zero), and their norm weights
   uint32_t xw[32];
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
@@ -595,6 +646,18 @@ void gemv_wave_kernel(const GemvArgs args) {
     xw[4 * v + 1] = q.y;
     xw[4 * v + 2] = q.z;
     xw[4 * v + 3] = q.w;
+  }
+  uint32_t gw[NORM ? 32 : 1];
+  if constexpr (NORM) {
+    const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)job.gamma, 0, k * 2, kRsrcWord3);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(g_rsrc, c * 128 + 16 * v, 0, 0));
+      gw[4 * v + 0] = q.x;
+      gw[4 * v + 1] = q.y;
+      gw[4 * v + 2] = q.z;
+      gw[4 * v + 3] = q.w;
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order
 
@@ -619,6 +682,21 @@ void gemv_wave_kernel(const GemvArgs args) {
 #pragma unroll
   for (int u = 0; u < kRing; ++u) load_batch(ring[u], u);
   __builtin_amdgcn_sched_barrier(0);  // every load is out before anything waits
+
+  if constexpr (NORM) {
+    // the row's sum of squares: each chunk once (lanes of row slot 0), wave by wave in LDS
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sq = add_squares(xw[i], sq);
+    sq = wave_sum(rslot == 0 ? sq : 0.f, lane);
+    if (lane == 0) norm_part[ks] = sq;
+    __syncthreads();
+    float total = 0.f;
+    for (int q = 0; q < slices; ++q) total += norm_part[q];
+    const float r = 1.0f / sqrtf(total / (float)k + args.eps);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xw[i] = norm_word(xw[i], gw[i], r);
+  }
 
   // 2. dot2 pairs and the all-zero-row product of this lane's chunk
   uint32_t xp[32];
@@ -666,25 +744,27 @@ void gemv_wave_kernel(const GemvArgs args) {
   }
 }
 
-template <int S, bool BIN>
+template <int S, bool BIN, bool NORM>
 hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
   const size_t lds = slices > 1 ? (size_t)slices * rows_per_wave * (64 / S) * sizeof(float) : 0;
   args.rows_per_wave = rows_per_wave;
-  if (rows_per_wave >= 8)
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 4, BIN>), dim3(blocks), dim3(64 * slices), lds, stream, args);
-  else if (rows_per_wave == 4)
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 2, BIN>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+  // with the norm's 32 extra registers the 4-batch ring would cost a wave per SIMD (148 registers);
+  // the 2-batch ring keeps 4 and measured the same
+  if (rows_per_wave >= 8 && !NORM)
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 4, BIN, NORM>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+  else if (rows_per_wave >= 4)
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 2, BIN, NORM>), dim3(blocks), dim3(64 * slices), lds, stream, args);
   else
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 1, BIN>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 1, BIN, NORM>), dim3(blocks), dim3(64 * slices), lds, stream, args);
   return hipGetLastError();
 }
 
-template <bool BIN>
+template <bool BIN, bool NORM>
 hipError_t launch_wave_s(int lanes, GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
   switch (lanes) {
-    case 16: return launch_wave<16, BIN>(args, blocks, rows_per_wave, slices, stream);
-    case 32: return launch_wave<32, BIN>(args, blocks, rows_per_wave, slices, stream);
-    default: return launch_wave<64, BIN>(args, blocks, rows_per_wave, slices, stream);
+    case 16: return launch_wave<16, BIN, NORM>(args, blocks, rows_per_wave, slices, stream);
+    case 32: return launch_wave<32, BIN, NORM>(args, blocks, rows_per_wave, slices, stream);
+    default: return launch_wave<64, BIN, NORM>(args, blocks, rows_per_wave, slices, stream);
   }
 }
 
@@ -738,11 +818,12 @@ hipError_t launch_s(int s, int mt, int rot, int iter, GemvArgs& args, int blocks
 // Tokens per pass (compile-time width of the activation registers); larger m loops over passes.
 static int tokens_per_pass(int64_t m) { return m >= 4 ? 4 : (m >= 2 ? 2 : 1); }
 
-GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
+GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated, bool norm) {
   GemvPlan p;
   p.layout = layout;
   p.m = (int32_t)m;
   p.rotated = rotated;
+  p.norm = norm ? 1 : 0;
   p.slices = 0;
   p.mfma = 0;
   // base-3: decode once, multiply all tokens on the matrix cores
@@ -757,7 +838,8 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated) {
   // slot-2 and binary from here on (both in chunks of 64 weights). The single-token kernel: one wave per K slice of 64 chunks, up to 16
   // waves per workgroup
   const int chunks = (int)(k / kChunkElems);
-  p.stream = (m == 1 && !rotated && k <= kMaxWaveKernelK) ? 1 : 0;
+  // (with the RMSNorm prologue: at most 8 waves per workgroup, K <= 32768)
+  p.stream = (m == 1 && !rotated && k <= (norm ? kMaxWaveKernelK / 2 : kMaxWaveKernelK)) ? 1 : 0;
   if (p.stream) {
     // rows shorter than one full slice: 32 or 16 lanes per row, several rows per instruction
     p.lanes = chunks > 32 ? 64 : (chunks > 16 ? 32 : 16);
@@ -806,11 +888,16 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
 }
 
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream) {
-  if (plan.mfma) return gemv_b3_mfma_launch(args, blocks, plan.m, (int)rotation_block(plan.rotated), stream);
+  if (plan.mfma)
+    return gemv_b3_mfma_launch(args, blocks, plan.m, (int)rotation_block(plan.rotated), plan.norm != 0, stream);
   const bool bin = plan.layout == TGS_LAYOUT_BINARY;
-  if (plan.stream)
-    return bin ? launch_wave_s<true>(plan.lanes, args, blocks, plan.iter, plan.slices, stream)
-               : launch_wave_s<false>(plan.lanes, args, blocks, plan.iter, plan.slices, stream);
+  if (plan.stream) {
+    if (plan.norm)
+      return bin ? launch_wave_s<true, true>(plan.lanes, args, blocks, plan.iter, plan.slices, stream)
+                 : launch_wave_s<false, true>(plan.lanes, args, blocks, plan.iter, plan.slices, stream);
+    return bin ? launch_wave_s<true, false>(plan.lanes, args, blocks, plan.iter, plan.slices, stream)
+               : launch_wave_s<false, false>(plan.lanes, args, blocks, plan.iter, plan.slices, stream);
+  }
   const int rot = (int)rotation_block(plan.rotated), mt = tokens_per_pass(plan.m);
   return bin ? launch_s<true>(plan.lanes, mt, rot, plan.iter, args, blocks, stream)
              : launch_s<false>(plan.lanes, mt, rot, plan.iter, args, blocks, stream);

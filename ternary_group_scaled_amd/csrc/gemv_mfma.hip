@@ -29,11 +29,16 @@
 //     per lane: 4 butterfly stages in the lane, 6 across lanes) while every wave multiplies its group
 //     8 b + w of block b from the other half; one barrier per block. The waves thus take the groups
 //     of K round robin instead of in contiguous slices.
+//   - RMSNorm prologue (NORM): the workgroup first computes 1 / rms of each token over all of K
+//     (rms_norm.h; its loads are issued before the first weights are needed), and every
+//     activation is multiplied by gamma[k] and that factor in fp32 before the sign flip, the
+//     butterfly and the one rounding to fp16.
 //   - Each group's 16 x 16 partial is scaled by its fp16 scale in fp32 and added to the running
 //     sum; at the end the 8 waves' sums are added through LDS in wave order (deterministic).
 #include <type_traits>
 
 #include "lane_ops.h"
+#include "rms_norm.h"
 #include "tgs_internal.h"
 
 namespace tgs {
@@ -74,7 +79,7 @@ __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both 
   return d;
 }
 
-template <int MT, int kFB, int ROT>
+template <int MT, int kFB, int ROT, bool NORM>
 __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
   static_assert(ROT == 0 || ROT == 128 || ROT == 1024, "rotation block is 0 (none), 128 or 1024");
   __shared__ __attribute__((aligned(16))) _Float16 tiles[kWaves][16 * kRowPitch];
@@ -84,6 +89,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   __shared__ __attribute__((aligned(16))) uint16_t zero_tab[5][32];
   // rotated 1024-blocks of the MT tokens, double-buffered: [buffer][token][1024]
   __shared__ __attribute__((aligned(16))) _Float16 blk[ROT == 1024 ? 2 * MT * 1024 : 8];
+  __shared__ float norm_part[NORM ? MT * kWaves : 1];  // RMSNorm: per-wave sums of squares
 
   const GemvJob job = gemv_job_of_block(args);
   const int n = job.n, k = job.k, m = args.m;
@@ -109,7 +115,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     else  // rel in [0, o) and [o + 128, 160)
       zero_tab[o][e - 128] = (uint16_t)(2 * tile_slot(e - 128 < o ? e - 128 : e));
   }
+  if constexpr (NORM) rms_partials<MT>(job.x, k, m, 0, norm_part, kWaves * 64);
   __syncthreads();
+  // RMSNorm factors: of this lane's token (group staging) and of token `wave` (block staging)
+  float rinv_tok = 1.f, rinv_wave = 1.f;
+  if constexpr (NORM) {
+    rinv_tok = rms_inverse(norm_part, tok, kWaves, k, args.eps);
+    rinv_wave = rms_inverse(norm_part, wave < MT ? wave : 0, kWaves, k, args.eps);
+  }
 
   // reads past each buffer return zero: rows >= n, tokens >= m (their outputs are not stored)
   const __amdgpu_buffer_rsrc_t code_rsrc =
@@ -120,6 +133,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       __builtin_amdgcn_make_buffer_rsrc((void*)job.x, 0, (int)((int64_t)m * k * 2), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t sign_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)job.signs, 0, ROT ? k : 0, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t gamma_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)job.gamma, 0, NORM ? k * 2 : 0, kRsrcWord3);
 
   // offsets are unsigned: n * stride < 2^31 and 64 rows more add less than 2^31
   uint32_t row_off[kFB], scale_row[kFB];
@@ -137,6 +152,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     uint32_t sg[(kE + 3) / 4];   // their sign bytes
     uint32_t bx[ROT == 1024 ? 8 : 1];  // 1024-blocks: 16 fp16 activations of the next block
     uint32_t bs[ROT == 1024 ? 4 : 1];  // and their sign bytes
+    uint32_t gm[NORM && ROT != 1024 ? MT : 1];  // RMSNorm weights (bf16 pairs) of x's elements
+    uint32_t bg[NORM && ROT == 1024 ? 8 : 1];   // and of bx's
   };
   auto load_codes = [&](Stage& st, int g, bool live) {
     const uint32_t byte0 = (uint32_t)((128 * g) / 5 + 8 * kq);
@@ -175,6 +192,28 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     } else {
       st.x[0] = __builtin_amdgcn_raw_buffer_load_b32(x_rsrc, xo, 0, 0);
     }
+    if constexpr (NORM) {
+      const int go = live ? (128 * g + kE * p) * 2 : kOobOffset;
+      if constexpr (MT == 8) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(gamma_rsrc, go, 0, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(gamma_rsrc, live ? go + 16 : kOobOffset, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          st.gm[i] = a[i];
+          st.gm[4 + i] = b[i];
+        }
+      } else if constexpr (MT == 4) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(gamma_rsrc, go, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.gm[i] = a[i];
+      } else if constexpr (MT == 2) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b64(gamma_rsrc, go, 0, 0);
+        st.gm[0] = a[0];
+        st.gm[1] = a[1];
+      } else {
+        st.gm[0] = __builtin_amdgcn_raw_buffer_load_b32(gamma_rsrc, go, 0, 0);
+      }
+    }
     if constexpr (ROT == 128) {
       const int so = live ? 128 * g + kE * p : kOobOffset;
       if constexpr (MT == 8) {
@@ -206,6 +245,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       st.bx[4 + i] = b[i];
       st.bs[i] = sv[i];
     }
+    if constexpr (NORM) {
+      const auto ga = __builtin_amdgcn_raw_buffer_load_b128(gamma_rsrc, live ? 2 * e0 : kOobOffset, 0, 0);
+      const auto gb = __builtin_amdgcn_raw_buffer_load_b128(gamma_rsrc, live ? 2 * e0 + 16 : kOobOffset, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st.bg[i] = ga[i];
+        st.bg[4 + i] = gb[i];
+      }
+    }
   };
   // 1024-blocks: signs, the natural-order Sylvester butterfly over the block in fp32 (strides 1..8
   // inside the lane, 16..512 across lanes), 1/sqrt(1024), one rounding to fp16, into buffer `buf`
@@ -217,6 +265,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       const uint32_t xd = st.bx[i] ^ (__builtin_amdgcn_perm(0u, st.bs[i >> 1], sel) & 0x80008000u);
       v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)xd);
       v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(xd >> 16));
+      if constexpr (NORM) {
+        v[2 * i] *= bf16_lo(st.bg[i]) * rinv_wave;
+        v[2 * i + 1] *= bf16_hi(st.bg[i]) * rinv_wave;
+      }
     }
 #pragma unroll
     for (int h = 1; h < 16; h <<= 1)
@@ -330,6 +382,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
         }
         v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)xd);
         v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(xd >> 16));
+        if constexpr (NORM) {
+          v[2 * i] *= bf16_lo(st.gm[i]) * rinv_tok;
+          v[2 * i + 1] *= bf16_hi(st.gm[i]) * rinv_tok;
+        }
       }
       if constexpr (ROT == 128) {
 #pragma unroll
@@ -470,26 +526,33 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   }
 }
 
-template <int MT, int FB>
-hipError_t launch_mt(GemvArgs& args, int blocks, int32_t block, hipStream_t stream) {
+template <int MT, int FB, bool NORM>
+hipError_t launch_rot(GemvArgs& args, int blocks, int32_t block, hipStream_t stream) {
   if (block == 1024)
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 1024>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 1024, NORM>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
   else if (block)
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 128>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 128, NORM>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
   else
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 0>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 0, NORM>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
   return hipGetLastError();
+}
+
+template <int MT, int FB>
+hipError_t launch_mt(GemvArgs& args, int blocks, int32_t block, bool norm, hipStream_t stream) {
+  return norm ? launch_rot<MT, FB, true>(args, blocks, block, stream)
+              : launch_rot<MT, FB, false>(args, blocks, block, stream);
 }
 
 }  // namespace
 
 int gemv_b3_mfma_rows(int32_t m) { return 16 * (m == 1 ? kMfmaFB1 : kMfmaFBMulti); }
 
-hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, int32_t block, hipStream_t stream) {
-  if (m <= 1) return launch_mt<1, kMfmaFB1>(args, blocks, block, stream);
-  if (m <= 2) return launch_mt<2, kMfmaFBMulti>(args, blocks, block, stream);
-  if (m <= 4) return launch_mt<4, kMfmaFBMulti>(args, blocks, block, stream);
-  return launch_mt<8, kMfmaFBMulti>(args, blocks, block, stream);
+hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, int32_t block, bool norm,
+                               hipStream_t stream) {
+  if (m <= 1) return launch_mt<1, kMfmaFB1>(args, blocks, block, norm, stream);
+  if (m <= 2) return launch_mt<2, kMfmaFBMulti>(args, blocks, block, norm, stream);
+  if (m <= 4) return launch_mt<4, kMfmaFBMulti>(args, blocks, block, norm, stream);
+  return launch_mt<8, kMfmaFBMulti>(args, blocks, block, norm, stream);
 }
 
 }  // namespace tgs

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <string>
 #include <thread>
@@ -284,8 +285,12 @@ tgs_status unpack_ternary(const tgs_matrix* w, int8_t* trits_out, uint16_t* scal
   return ok();
 }
 
-tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void* const* xs, int32_t x_dtype,
-                                int64_t m, const int8_t* const* signs, float* const* ys, void* stream) {
+namespace {
+
+// The batched GEMV, with the RMSNorm prologue when gammas is set (one norm weight vector per matrix).
+tgs_status gemv_batched(const tgs_matrix* ws, int32_t count, const void* const* xs, int32_t x_dtype, int64_t m,
+                        const uint16_t* const* gammas, float eps, const int8_t* const* signs, float* const* ys,
+                        void* stream) {
   if (!ws || !xs || !ys) return fail(TGS_E_NULL, "descriptor, input or output array is NULL");
   if (count < 1 || count > TGS_MAX_BATCH) return fail(TGS_E_SHAPE, "count must be 1..%d, got %d", TGS_MAX_BATCH, count);
   if (x_dtype != TGS_F16) return fail(TGS_E_DTYPE, "ternary_gemv takes fp16 activations (TGS_F16)");
@@ -299,19 +304,24 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
     if (!aligned(xs[i], 16)) return fail(TGS_E_ALIGN, "x must be 16-byte aligned");
     if (!aligned(ys[i], 4)) return fail(TGS_E_ALIGN, "y must be 4-byte aligned");
     if (signs && signs[i] && !aligned(signs[i], 16)) return fail(TGS_E_ALIGN, "signs must be 16-byte aligned");
+    if (gammas) {
+      if (!gammas[i]) return fail(TGS_E_NULL, "gamma %d is NULL", i);
+      if (!aligned(gammas[i], 16)) return fail(TGS_E_ALIGN, "gamma must be 16-byte aligned");
+    }
   }
+  if (gammas && !(eps > 0.f && eps < INFINITY)) return fail(TGS_E_SHAPE, "eps must be positive and finite");
   hipStream_t s = static_cast<hipStream_t>(stream);
   // one launch per distinct plan (layout, lanes per row, basis, kernel, K slices), in call order
   std::vector<char> done((size_t)count, 0);
   for (int32_t i = 0; i < count; ++i) {
     if (done[(size_t)i]) continue;
-    tgs::GemvPlan plan = tgs::gemv_plan(ws[i].layout, ws[i].k, m, ws[i].rotated);
+    tgs::GemvPlan plan = tgs::gemv_plan(ws[i].layout, ws[i].k, m, ws[i].rotated, gammas != nullptr);
     // the jobs of this launch: every remaining matrix with the same plan, in call order
     std::vector<int32_t> members;
     int64_t total_rows = 0;
     for (int32_t j = i; j < count; ++j) {
       if (done[(size_t)j]) continue;
-      const tgs::GemvPlan pj = tgs::gemv_plan(ws[j].layout, ws[j].k, m, ws[j].rotated);
+      const tgs::GemvPlan pj = tgs::gemv_plan(ws[j].layout, ws[j].k, m, ws[j].rotated, gammas != nullptr);
       if (pj.layout != plan.layout || pj.lanes != plan.lanes || pj.rotated != plan.rotated ||
           pj.stream != plan.stream || pj.slices != plan.slices || pj.mfma != plan.mfma)
         continue;
@@ -323,6 +333,8 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
     tgs::GemvArgs args;
     std::memset(&args, 0, sizeof(args));
     args.m = (int32_t)m;
+    args.norm = gammas ? 1 : 0;
+    args.eps = eps;
     for (int32_t i = 0; i < tgs::kMaxJobs; ++i) args.start[i] = INT32_MAX;
     int32_t blocks = 0;
     for (int32_t j : members) {
@@ -331,6 +343,7 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
       job.scales = ws[j].scales;
       job.x = static_cast<const uint16_t*>(xs[j]);
       job.signs = signs ? signs[j] : nullptr;
+      job.gamma = gammas ? gammas[j] : nullptr;
       job.y = ys[j];
       job.stride = ws[j].code_row_stride;
       job.n = (int32_t)ws[j].n;
@@ -344,6 +357,30 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
     if (e != hipSuccess) return device_error(e, "ternary_gemv launch");
   }
   return ok();
+}
+
+}  // namespace
+
+tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void* const* xs, int32_t x_dtype,
+                                int64_t m, const int8_t* const* signs, float* const* ys, void* stream) {
+  return gemv_batched(ws, count, xs, x_dtype, m, nullptr, 0.f, signs, ys, stream);
+}
+
+tgs_status ternary_gemv_rmsnorm_batched(const tgs_matrix* ws, int32_t count, const void* const* xs, int32_t x_dtype,
+                                        int64_t m, const uint16_t* const* gammas, float eps,
+                                        const int8_t* const* signs, float* const* ys, void* stream) {
+  if (!gammas) return fail(TGS_E_NULL, "gammas is NULL");
+  return gemv_batched(ws, count, xs, x_dtype, m, gammas, eps, signs, ys, stream);
+}
+
+tgs_status ternary_gemv_rmsnorm(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m, const uint16_t* gamma,
+                                float eps, const int8_t* signs, float* y, void* stream) {
+  if (!w) return fail(TGS_E_NULL, "matrix descriptor is NULL");
+  const void* xs[1] = {x};
+  const uint16_t* gs[1] = {gamma};
+  const int8_t* ss[1] = {signs};
+  float* ys[1] = {y};
+  return ternary_gemv_rmsnorm_batched(w, 1, xs, x_dtype, m, gs, eps, ss, ys, stream);
 }
 
 tgs_status ternary_code_flips_batched(const tgs_matrix* as, const tgs_matrix* bs, int32_t count,
@@ -442,6 +479,29 @@ tgs_status hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, int64_t k,
   if (xb < yb + yn && yb < xb + xn) return fail(TGS_E_SHAPE, "x and y overlap");
   hipError_t e = tgs::hadamard_launch(x, x_dtype, m, k, block, signs, y, y_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "hadamard_rotate launch");
+  return ok();
+}
+
+tgs_status rmsnorm_hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block,
+                                   const uint16_t* gamma, float eps, const int8_t* signs, void* y, int32_t y_dtype,
+                                   void* stream) {
+  if (!x || !gamma || !signs || !y) return fail(TGS_E_NULL, "x, gamma, signs or y is NULL");
+  if (x_dtype != TGS_F16 && x_dtype != TGS_BF16 && x_dtype != TGS_F32)
+    return fail(TGS_E_DTYPE, "x_dtype must be TGS_F16, TGS_BF16 or TGS_F32");
+  if (y_dtype != TGS_F16 && y_dtype != TGS_F32) return fail(TGS_E_DTYPE, "y_dtype must be TGS_F16 or TGS_F32");
+  if (block != 128 && block != 1024) return fail(TGS_E_SHAPE, "block must be 128 or 1024, got %lld", (long long)block);
+  if (m < 1 || m >= (1LL << 31) || k < block || k % block != 0 || k >= (1LL << 24))
+    return fail(TGS_E_SHAPE, "need 1 <= m < 2^31 and k a multiple of the block (%lld) below 2^24", (long long)block);
+  if (!(eps > 0.f && eps < INFINITY)) return fail(TGS_E_SHAPE, "eps must be positive and finite");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(TGS_E_ALIGN, "x and y must be 16-byte aligned");
+  if (!aligned(gamma, 2)) return fail(TGS_E_ALIGN, "gamma must be 2-byte aligned");
+  const size_t xe = x_dtype == TGS_F32 ? 4 : 2, ye = y_dtype == TGS_F32 ? 4 : 2;
+  const char *xb = static_cast<const char*>(x), *yb = static_cast<const char*>(y);
+  const size_t xn = (size_t)(m * k) * xe, yn = (size_t)(m * k) * ye;
+  if (xb < yb + yn && yb < xb + xn) return fail(TGS_E_SHAPE, "x and y overlap");
+  hipError_t e = tgs::rmsnorm_hadamard_launch(x, x_dtype, m, k, block, gamma, eps, signs, y, y_dtype,
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "rmsnorm_hadamard_rotate launch");
   return ok();
 }
 

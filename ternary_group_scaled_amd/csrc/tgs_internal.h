@@ -29,6 +29,7 @@ struct GemvJob {
   const uint16_t* scales;  // [n][k/128] fp16 bits
   const uint16_t* x;       // [m][k] fp16 bits
   const int8_t* signs;     // [k] or nullptr (plain basis)
+  const uint16_t* gamma;   // [k] bf16 bits of the RMSNorm weight, or nullptr (no norm)
   float* y;                // [m][n]
   int64_t stride;          // bytes between rows of codes
   int32_t n;
@@ -44,6 +45,8 @@ struct GemvArgs {
   int32_t count;
   int32_t m;
   int32_t rows_per_wave;     // single-token kernel only
+  int32_t norm;              // 1: RMS-normalise x with each job's gamma first (the jobs' gammas are set)
+  float eps;                 // the norm's epsilon
   int32_t reserved;
   int32_t start[kMaxJobs];   // == job[i].block0 for i < count; INT32_MAX past the last job
   GemvJob job[kMaxJobs];
@@ -85,18 +88,20 @@ struct GemvPlan {
   int32_t mfma;       // 1: base-3, on the matrix cores (gemv_mfma.hip)
   int32_t iter;       // rows per lane slot
   int32_t rows_per_block;
+  int32_t norm;       // 1: RMSNorm prologue
 };
 
 // Launch helpers implemented in the .hip files. They only queue work; all argument checks
 // happen in tgs_host.cpp before they are called.
-GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated);
+GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated, bool norm = false);
 // after the jobs of a launch are known: pick rows per workgroup from their total row count
 void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows);
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream);
 // base-3 on the matrix cores: rows of y per workgroup for m tokens
 int gemv_b3_mfma_rows(int32_t m);
 // block: 0 for plain-basis weights, else the rotation block (128 or 1024)
-hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, int32_t block, hipStream_t stream);
+hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, int32_t block, bool norm,
+                               hipStream_t stream);
 
 // Code flips: one pair of matrices of a batched launch (device pointers).
 struct FlipJob {
@@ -126,6 +131,10 @@ hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, con
 
 hipError_t hadamard_launch(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block, const int8_t* signs,
                            void* y, int32_t y_dtype, hipStream_t stream);
+// the same rotation after RMSNorm of each row (gamma: bf16 bits [k]); one workgroup per row
+hipError_t rmsnorm_hadamard_launch(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block,
+                                   const uint16_t* gamma, float eps, const int8_t* signs, void* y, int32_t y_dtype,
+                                   hipStream_t stream);
 
 // rotation block of a descriptor's `rotated` field: 0 (plain basis), 128 or 1024
 inline int64_t rotation_block(int32_t rotated) { return rotated == 0 ? 0 : (rotated == 1024 ? 1024 : 128); }

@@ -10,6 +10,8 @@ Workloads (synthetic, seeded, the benchmark's shapes and value distributions):
   - 27B-class rotated-basis GEMV: base-3 gate 17408 x 5120 and down 5120 x 17408, M = 1 and 8,
     128- and 1024-element rotation blocks.
   - 27B-class prefill GEMM: slot-2 17408 x 5120 and 5120 x 17408, bf16 activations, M = 16, 128, 2048.
+  - The RMSNorm prologue: q/k/v of the 8B layer in one batched call, and the 27B gate projection with
+    1024-element rotation blocks at M = 8.
 """
 import numpy as np
 import pytest
@@ -100,6 +102,40 @@ def test_27b_rotated_gemv(block, m):
         torch.cuda.synchronize()
         _check_rows(tgs.BASE3, codes, scales, k, xh.view(np.uint16), oracle.X_F16, y.cpu().numpy(),
                     _sample_rows(n, 40, 10 + i), f"27B rotated {name} m={m} block={block}", signs=sg, block=block)
+
+
+def test_8b_attention_inputs_with_the_rmsnorm_prologue():
+    """q, k, v of the 8B-class layer in one batched call with the RMSNorm prologue (slot-2, M = 1),
+    and the 27B gate projection, base-3 with 1024-element rotation blocks, M = 8."""
+    x, xh = _x_f16("full8bn/x", 1, 4096)
+    x = (x.float() * 7.0).half()
+    xh = (xh.astype(np.float32) * 7.0).astype(np.float16)
+    gamma = synth.bf16_bits(1.0 + 0.25 * synth.normal(0, 77, (4096,)))
+    gd = torch.from_numpy(gamma.view(np.int16).copy()).to(DEV)
+    mats, ys = [], []
+    for name, n, k in LAYER_8B[:3]:
+        w, codes, scales = _matrix(tgs.SLOT2, f"full8bn/{name}", n, k, 0.4)
+        mats.append((w, codes, scales, n))
+        ys.append(torch.empty((1, n), dtype=torch.float32, device=DEV))
+    tgs.ternary_gemv_rmsnorm_batched([w for w, _, _, _ in mats], [x] * 3, [gd] * 3, 1e-6, ys)
+    torch.cuda.synchronize()
+    for i, ((w, codes, scales, n), y) in enumerate(zip(mats, ys)):
+        rows = _sample_rows(n, 40, 30 + i)
+        y_ref, bound = oracle.matmul(tgs.SLOT2, codes, scales, 4096, xh.view(np.uint16), oracle.X_F16, rows=rows,
+                                     gamma=gamma, eps=float(np.float32(1e-6)))
+        assert (np.abs(y.cpu().numpy()[:, rows] - y_ref) <= bound).all(), LAYER_8B[i][0]
+    n, k, m = 17408, 5120, 8
+    w, codes, scales = _matrix(tgs.BASE3, "full27n/gate", n, k, 0.5, rotated=1024)
+    sg = synth.signs(0, synth.stream_id("full27n/signs", k), k)
+    xd, xh = _x_f16("full27n/x", m, k)
+    gamma = synth.bf16_bits(1.0 + 0.25 * synth.normal(0, 78, (k,)))
+    y = tgs.ternary_gemv_rmsnorm(w, xd, torch.from_numpy(gamma.view(np.int16).copy()).to(DEV), 1e-6,
+                                 signs=torch.from_numpy(sg).to(DEV))
+    torch.cuda.synchronize()
+    rows = _sample_rows(n, 40, 40)
+    y_ref, bound = oracle.matmul(tgs.BASE3, codes, scales, k, xh.view(np.uint16), oracle.X_F16, signs=sg, block=1024,
+                                 rows=rows, gamma=gamma, eps=float(np.float32(1e-6)))
+    assert (np.abs(y.cpu().numpy()[:, rows] - y_ref) <= bound).all()
 
 
 @pytest.mark.parametrize("m", [16, 128, 2048])

@@ -538,3 +538,115 @@ def test_binary_code_flips_match_oracle(n, k, frac):
     assert ref_total == int(mask.sum())
     assert int(total.item()) == ref_total
     assert (rows.cpu().numpy().astype(np.int64) == ref_rows).all()
+
+
+# ------------------------------------------------------------------------------ RMSNorm prologue
+# xhat = gamma * x / sqrt(mean(x^2) + eps), gamma in bf16, then the rotation (if any) and the product.
+
+
+def _norm_inputs(seed, m, k):
+    """Activations with a different scale per row (hidden states, not unit normals) and bf16 gamma."""
+    scale = np.array([0.05, 3.0, 40.0, 0.7, 11.0, 0.2, 6.0, 1.5])[:m, None]
+    x16 = (synth.normal(seed, 1, (m, k)) * scale).astype(np.float16)
+    gamma = synth.bf16_bits(1.0 + 0.25 * synth.normal(seed, 2, (k,)))
+    return x16, gamma
+
+
+def _gamma_dev(gamma):
+    return torch.from_numpy(gamma.view(np.int16).copy()).to(DEV)
+
+
+NORM_LAYOUT_BLOCKS = [(tgs.SLOT2, 0), (tgs.SLOT2, 128), (tgs.SLOT2, 1024), (tgs.BASE3, 0), (tgs.BASE3, 128),
+                      (tgs.BASE3, 1024), (tgs.BINARY, 0), (tgs.BINARY, 1024)]
+
+
+@pytest.mark.parametrize("layout,block", NORM_LAYOUT_BLOCKS, ids=lambda v: str(v))
+@pytest.mark.parametrize("n,k", [(33, 1024), (100, 5120), (70, 2048), (20, 40960)])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_rmsnorm_gemv_matches_oracle(layout, block, n, k, m):
+    """Every kernel path takes the prologue: the single-token kernel (plain slot-2/binary, m = 1,
+    K <= 32768), the general slot-2/binary kernel (the rest: K = 40960 for m = 1) and the base-3
+    matrix-core kernel, each plain and with both rotation blocks."""
+    if block == 1024 and k % 1024:
+        pytest.skip("k is not a multiple of the rotation block")
+    if layout == tgs.BINARY:
+        t, s = _binary_weights(n + k, "norm", n, k)
+    else:
+        t, s = make_weights(n + k, f"norm{layout}", n, k, 0.4)
+    x16, gamma = _norm_inputs(m + k, m, k)
+    sg = make_signs(k, "norm", k) if block else None
+    w = _packed(layout, t, s, rotated=block)
+    eps = 1e-6
+    y = tgs.ternary_gemv_rmsnorm(w, _x_dev(x16), _gamma_dev(gamma), eps,
+                                 signs=torch.from_numpy(sg).to(DEV) if block else None)
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul(layout, oracle.pack(layout, t), s, k, x16.view(np.uint16), oracle.X_F16, signs=sg,
+                                 block=block or 128, gamma=gamma, eps=float(np.float32(eps)))
+    assert_within_bound(y.cpu().numpy(), y_ref, bound, f"rmsnorm {LNAME.get(layout, 'binary')} b{block} {n}x{k} m={m}")
+
+
+def test_rmsnorm_gemv_zero_rows_and_batched():
+    # an all-zero activation row normalises to zero (eps keeps the factor finite): y is exactly 0;
+    # the batched call equals single calls bit for bit, gammas may differ per matrix
+    k, m = 2048, 3
+    sg = make_signs(5, "normb", k)
+    x16, gamma = _norm_inputs(5, m, k)
+    x16[1] = 0
+    cases = [(tgs.SLOT2, 0), (tgs.BASE3, 128), (tgs.SLOT2, 1024), (tgs.BINARY, 128)]
+    ws, gs, ys, signs, singles = [], [], [], [], []
+    for i, (layout, rot) in enumerate(cases):
+        if layout == tgs.BINARY:
+            t, s = _binary_weights(i, "normb", 40 + i, k)
+        else:
+            t, s = make_weights(i, "normb", 40 + i, k, 0.4)
+        w = _packed(layout, t, s, rotated=rot)
+        g = _gamma_dev(synth.bf16_bits(1.0 + 0.1 * i + 0.2 * synth.normal(i, 7, (k,))))
+        sgd = torch.from_numpy(sg).to(DEV) if rot else None
+        ws.append(w)
+        gs.append(g)
+        signs.append(sgd)
+        ys.append(torch.empty((m, 40 + i), dtype=torch.float32, device=DEV))
+        singles.append(tgs.ternary_gemv_rmsnorm(w, _x_dev(x16), g, 1e-5, signs=sgd))
+    tgs.ternary_gemv_rmsnorm_batched(ws, [_x_dev(x16)] * len(ws), gs, 1e-5, ys, signs=signs)
+    torch.cuda.synchronize()
+    for y, single in zip(ys, singles):
+        assert torch.equal(y.view(torch.int32), single.view(torch.int32))
+        assert (y[1] == 0).all()
+
+
+@pytest.mark.parametrize("in_dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("block", [128, 1024])
+def test_rmsnorm_hadamard_rotate_matches_oracle(in_dtype, block):
+    m, k = 3, 3072
+    sg = make_signs(6, "nrot", k)
+    xd = synth.normal(6, 9, (m, k)) * np.array([[0.1], [5.0], [60.0]])
+    gamma = synth.bf16_bits(1.0 + 0.3 * synth.normal(6, 10, (k,)))
+    if in_dtype == "f16":
+        host = xd.astype(np.float16)
+        xt = torch.from_numpy(host.copy()).to(DEV)
+        bits, xdt = host.view(np.uint16), oracle.X_F16
+        xref = host.astype(np.float64)
+    elif in_dtype == "bf16":
+        bits = synth.bf16_bits(xd)
+        xt = torch.from_numpy(bits.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+        xdt = oracle.X_BF16
+        xref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        host = xd.astype(np.float32)
+        xt = torch.from_numpy(host.copy()).to(DEV)
+        bits, xdt = None, None
+        xref = host.astype(np.float64)
+    eps = 1e-6
+    xhat = oracle.rmsnorm(xref, gamma, float(np.float32(eps)))
+    blk_l1 = np.repeat(np.abs(xhat).reshape(m, -1, block).sum(axis=2), block, axis=1) / np.sqrt(block)
+    for od in (torch.float32, torch.float16):
+        y = tgs.rmsnorm_hadamard_rotate(xt, _gamma_dev(gamma), eps, torch.from_numpy(sg).to(DEV), block=block,
+                                        out_dtype=od)
+        torch.cuda.synchronize()
+        got = y.float().cpu().numpy().astype(np.float64)
+        if bits is not None:
+            ref = oracle.rmsnorm_rotate(bits, xdt, gamma, float(np.float32(eps)), sg, block)
+        else:  # fp32 input: the oracle's rotation of its own RMSNorm of the fp32 values
+            ref = oracle.rotate(xhat, sg, block)
+        tol = 2e-6 * blk_l1 + 1e-30 if od == torch.float32 else 2.0 ** -11 * np.abs(ref) + 2e-6 * blk_l1 + 2.0 ** -25
+        assert (np.abs(got - ref) <= tol).all(), f"{in_dtype} block {block} {od}"

@@ -188,6 +188,31 @@ def test_device_call_argument_checks_happen_before_any_device_work():
     bad.k = 1536
     bad.code_row_stride = 384
     assert _gemv(bad, signs=0x500000) == 2
+    # RMSNorm prologue: gamma required and 16-byte aligned, eps positive and finite
+    norm = lambda m, gamma=0x600000, eps=1e-6, signs=None: lib.ternary_gemv_rmsnorm(
+        ctypes.byref(m), 0x300000, tgs.F16, 1, gamma, eps, signs, 0x400000, None)
+    assert norm(_fake_matrix(), gamma=None) == 1
+    assert norm(_fake_matrix(), gamma=0x600008) == 3
+    assert norm(_fake_matrix(), eps=0.0) == 2
+    assert norm(_fake_matrix(), eps=-1e-6) == 2
+    assert norm(_fake_matrix(), eps=float("inf")) == 2
+    assert norm(_fake_matrix(), eps=float("nan")) == 2
+    assert norm(_fake_matrix(rotated=1)) == 6                    # rotated weights still need signs
+    assert norm(_fake_matrix(rotated=0), signs=0x500000) == 6
+    gp = (ctypes.c_void_p * 1)(None)
+    assert lib.ternary_gemv_rmsnorm_batched((tgs.Matrix * 1)(_fake_matrix()), 1, (ctypes.c_void_p * 1)(0x300000),
+                                            tgs.F16, 1, gp, 1e-6, None, (ctypes.c_void_p * 1)(0x400000), None) == 1
+    assert lib.ternary_gemv_rmsnorm_batched((tgs.Matrix * 1)(_fake_matrix()), 1, (ctypes.c_void_p * 1)(0x300000),
+                                            tgs.F16, 1, None, 1e-6, None, (ctypes.c_void_p * 1)(0x400000), None) == 1
+    # the fused standalone norm + rotation
+    nrot = lambda k=2048, block=1024, gamma=0x600000, eps=1e-6, y=0x400000: lib.rmsnorm_hadamard_rotate(
+        0x300000, tgs.F16, 2, k, block, gamma, eps, 0x500000, y, tgs.F32, None)
+    assert nrot(block=512) == 2
+    assert nrot(k=1536) == 2
+    assert nrot(gamma=None) == 1
+    assert nrot(eps=0.0) == 2
+    assert nrot(y=0x300100) == 2                                  # overlaps x
+    assert nrot(k=1 << 24, block=128) == 2                        # k below 2^24
     # batched
     ms = (tgs.Matrix * 2)(_fake_matrix(), _fake_matrix(rotated=1))
     xp = (ctypes.c_void_p * 2)(0x300000, 0x300000)
