@@ -867,11 +867,13 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated, bool n
 void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
   if (p.mfma) return;
   if (p.stream) {
-    // rows per wave: as many (8..64) as still give kWaveKernelTargetWaves waves in all. Small
-    // launches get 8 rows per wave, which puts every load of a wave in flight at once.
+    // rows per wave: as many (4..64) as still give kWaveKernelTargetWaves waves in all. Small
+    // launches get 4 or 8 rows per wave, which puts every load of a wave in flight at once.
+    // (Measured on the 8B set: a floor of 4 rows beat 8 by 1.5% in layer order and 3.7% as a set;
+    // 2 rows, or twice the target waves, lost 10-22%: every wave re-reads the activations.)
     const int64_t rows_per_instr = 64 / p.lanes;
     int r = 64;
-    while (r > 8 && (total_rows + r * rows_per_instr - 1) / (r * rows_per_instr) * p.slices < kWaveKernelTargetWaves)
+    while (r > 4 && (total_rows + r * rows_per_instr - 1) / (r * rows_per_instr) * p.slices < kWaveKernelTargetWaves)
       r /= 2;
     p.iter = r;
     p.rows_per_block = (int32_t)(r * rows_per_instr);

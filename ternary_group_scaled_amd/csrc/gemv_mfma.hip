@@ -24,11 +24,14 @@
 //     so each MFMA step reads its A fragment with one 16-byte load. The 32 slots of the 160-trit
 //     window that lie outside the group hold zeros: the trits there (neighbouring groups, or
 //     bytes past the row) multiply zero, and every MFMA step stays within one scale group.
-//   - 1024-element rotation blocks span eight groups, so they are rotated once per workgroup: wave
-//     w < MT rotates token w's block b + 1 into one half of a double-buffered LDS array (16 elements
-//     per lane: 4 butterfly stages in the lane, 6 across lanes) while every wave multiplies its group
-//     8 b + w of block b from the other half; one barrier per block. The waves thus take the groups
-//     of K round robin instead of in contiguous slices.
+//   - 1024-element rotation blocks span eight groups, so they are rotated once per workgroup (16
+//     elements per lane: 4 butterfly stages in the lane, 6 across lanes). When the MT rotated rows
+//     fit in 48 KB of LDS (PRE), the workgroup rotates all of them before its weight stream, and the
+//     waves then walk contiguous group slices as in the plain basis. Otherwise wave w < MT rotates
+//     token w's block b + 1 into one half of a double-buffered LDS array while every wave
+//     multiplies its group 8 b + w of block b from the other half, with one barrier per block.
+//   - Only the MT live rows of each A tile are kept in LDS; lanes of the padding rows MT..15 hold
+//     zero fragments in registers.
 //   - RMSNorm prologue (NORM): the workgroup first computes 1 / rms of each token over all of K
 //     (rms_norm.h; its loads are issued before the first weights are needed), and every
 //     activation is multiplied by gamma[k] and that factor in fp32 before the sign flip, the
@@ -79,16 +82,21 @@ __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both 
   return d;
 }
 
-template <int MT, int kFB, int ROT, bool NORM>
+template <int MT, int kFB, int ROT, bool NORM, bool PRE>
 __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
   static_assert(ROT == 0 || ROT == 128 || ROT == 1024, "rotation block is 0 (none), 128 or 1024");
-  __shared__ __attribute__((aligned(16))) _Float16 tiles[kWaves][16 * kRowPitch];
+  static_assert(!PRE || ROT == 1024, "whole-row rotation is for 1024-element blocks");
+  // the waves' A tiles (MT rows each), and afterwards the waves' sums
+  constexpr int kTileBytes = kWaves * MT * kRowPitch * 2, kRedBytes = kWaves * kFB * 4 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
   // byte offsets of tile slots for each start digit off0 (0..4): the group's 128 activations in
   // K order, then the 32 window positions outside the group
   __shared__ __attribute__((aligned(16))) uint16_t slot_tab[5][128];
   __shared__ __attribute__((aligned(16))) uint16_t zero_tab[5][32];
   // rotated 1024-blocks of the MT tokens, double-buffered: [buffer][token][1024]
-  __shared__ __attribute__((aligned(16))) _Float16 blk[ROT == 1024 ? 2 * MT * 1024 : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 blk[ROT == 1024 && !PRE ? 2 * MT * 1024 : 8];
+  // PRE: the MT rows rotated, [MT][k] (dynamic LDS, MT * k * 2 bytes)
+  extern __shared__ __attribute__((aligned(16))) _Float16 xrot[];
   __shared__ float norm_part[NORM ? MT * kWaves : 1];  // RMSNorm: per-wave sums of squares
 
   const GemvJob job = gemv_job_of_block(args);
@@ -105,9 +113,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   constexpr int kL = 64 / MT, kE = 2 * MT;
   const int tok = lane / kL, p = lane % kL;
 
-  _Float16* tile = tiles[wave];
-  // rows MT..15 of the A operand stay zero; rows < MT are rewritten for every group
-  for (int i = lane; i < 16 * kRowPitch / 8; i += 64) reinterpret_cast<uint4*>(tile)[i] = make_uint4(0, 0, 0, 0);
+  // rows < MT of this wave's A tile, rewritten for every group
+  _Float16* tile = reinterpret_cast<_Float16*>(smem) + wave * MT * kRowPitch;
   for (int i = threadIdx.x; i < 5 * 160; i += kWaves * 64) {
     const int o = i / 160, e = i - 160 * o;
     if (e < 128)
@@ -231,11 +238,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       }
     }
   };
-  // 1024-blocks: token `wave`'s 16 activations 1024 bb + 16 lane .. and their signs (waves < MT)
-  auto load_block = [&](Stage& st, int bb) {
-    const bool live = bb < blocks && wave < MT;
+  // 1024-blocks: token t's 16 activations 1024 bb + 16 lane .. and their signs (t < MT)
+  auto load_block = [&](Stage& st, int bb, int t) {
+    const bool live = bb < blocks && t < MT;
     const int e0 = 1024 * bb + 16 * lane;
-    const int xo = live ? (wave * k + e0) * 2 : kOobOffset;
+    const int xo = live ? (t * k + e0) * 2 : kOobOffset;
     const auto a = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo, 0, 0);
     const auto b = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, live ? xo + 16 : kOobOffset, 0, 0);
     const auto sv = __builtin_amdgcn_raw_buffer_load_b128(sign_rsrc, live ? e0 : kOobOffset, 0, 0);
@@ -256,8 +263,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     }
   };
   // 1024-blocks: signs, the natural-order Sylvester butterfly over the block in fp32 (strides 1..8
-  // inside the lane, 16..512 across lanes), 1/sqrt(1024), one rounding to fp16, into buffer `buf`
-  auto rotate_block = [&](const Stage& st, int buf) {
+  // inside the lane, 16..512 across lanes), 1/sqrt(1024), one rounding to fp16, into dst[0 .. 1024);
+  // rn: the token's RMSNorm factor
+  auto rotate_block = [&](const Stage& st, _Float16* dst_block, float rn) {
     float v[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -266,8 +274,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)xd);
       v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(xd >> 16));
       if constexpr (NORM) {
-        v[2 * i] *= bf16_lo(st.bg[i]) * rinv_wave;
-        v[2 * i + 1] *= bf16_hi(st.bg[i]) * rinv_wave;
+        v[2 * i] *= bf16_lo(st.bg[i]) * rn;
+        v[2 * i + 1] *= bf16_hi(st.bg[i]) * rn;
       }
     }
 #pragma unroll
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(v[2 * i + 1] * 0.03125f));
       w[i] = lo | (hi << 16);
     }
-    uint4* dst = reinterpret_cast<uint4*>(blk + (buf * MT + wave) * 1024 + 16 * lane);
+    uint4* dst = reinterpret_cast<uint4*>(dst_block + 16 * lane);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   };
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     _Float16 hv[kE];
     if constexpr (ROT == 1024) {
       // already rotated: kE consecutive fp16 values of token tok's block, at the group's place in it
-      const _Float16* src = blk + (buf * MT + tok) * 1024 + 128 * (g & 7) + kE * p;
+      const _Float16* src = PRE ? xrot + tok * k + 128 * g + kE * p : blk + (buf * MT + tok) * 1024 + 128 * (g & 7) + kE * p;
       uint32_t w[MT];
       if constexpr (MT >= 4) {
 #pragma unroll
@@ -443,7 +451,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     for (int fb = 0; fb < kFB; ++fb) part[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
-      const half8 a = *reinterpret_cast<const half8*>(tile + fr * kRowPitch + (kq * 5 + j) * 8);
+      half8 a = {};  // the padding rows MT..15 of the A operand are zero
+      if (fr < MT) a = *reinterpret_cast<const half8*>(tile + fr * kRowPitch + (kq * 5 + j) * 8);
 #pragma unroll
       for (int fb = 0; fb < kFB; ++fb) {
         const u16x2 de0 = j < 4 ? peel(ve0[fb]) : ve0[fb];
@@ -465,32 +474,52 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     }
   };
 
-  if constexpr (ROT == 1024) {
+  if constexpr (PRE) {
+    // every block of every token rotated once (round robin over the waves), then contiguous group
+    // slices per wave, as in the plain basis
+    for (int idx = wave; idx < MT * blocks; idx += kWaves) {
+      const int t = idx / blocks, bb = idx - t * blocks;
+      Stage st;
+      load_block(st, bb, t);
+      const float rn = NORM ? rms_inverse(norm_part, t, kWaves, k, args.eps) : 1.f;
+      rotate_block(st, xrot + t * k + 1024 * bb, rn);
+    }
+    __syncthreads();
+    Stage st0, st1;
+    load_codes(st0, g_begin, g_begin < g_end);
+    for (int g = g_begin; g < g_end; g += 2) {
+      load_codes(st1, g + 1, g + 1 < g_end);
+      compute(st0, g, 0);
+      if (g + 1 >= g_end) break;
+      load_codes(st0, g + 2, g + 2 < g_end);
+      compute(st1, g + 1, 0);
+    }
+  } else if constexpr (ROT == 1024) {
     // block b: waves < MT rotate block b + 1 into buffer (b + 1) & 1 while every wave multiplies
     // group 8 b + wave from buffer b & 1; the barrier closing block b orders both against block
     // b + 1 (every wave runs the same number of blocks, so all reach every barrier)
     auto step = [&](const Stage& st, int b) {
-      if (wave < MT && b + 1 < blocks) rotate_block(st, (b + 1) & 1);
+      if (wave < MT && b + 1 < blocks) rotate_block(st, blk + (((b + 1) & 1) * MT + wave) * 1024, rinv_wave);
       compute(st, 8 * b + wave, b & 1);
       __syncthreads();
     };
     {
       Stage st;
-      load_block(st, 0);
-      if (wave < MT) rotate_block(st, 0);
+      load_block(st, 0, wave);
+      if (wave < MT) rotate_block(st, blk + wave * 1024, rinv_wave);
     }
     __syncthreads();
     // stage b holds group 8 b + wave's codes and block b + 1's activations; two stages in flight
     Stage st0, st1;
     load_codes(st0, wave, 0 < blocks);
-    load_block(st0, 1);
+    load_block(st0, 1, wave);
     for (int b = 0; b < blocks; b += 2) {
       load_codes(st1, 8 * (b + 1) + wave, b + 1 < blocks);
-      load_block(st1, b + 2);
+      load_block(st1, b + 2, wave);
       step(st0, b);
       if (b + 1 >= blocks) break;
       load_codes(st0, 8 * (b + 2) + wave, b + 2 < blocks);
-      load_block(st0, b + 3);
+      load_block(st0, b + 3, wave);
       step(st1, b + 1);
     }
   } else {
@@ -508,8 +537,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
 
   // add the waves' sums in wave order
   __syncthreads();
-  float* red = reinterpret_cast<float*>(&tiles[0][0]);  // [wave][fb * 4 + r][lane]
-  static_assert(kWaves * kFB * 4 * 64 * sizeof(float) <= sizeof(tiles), "the wave sums fit in the tiles");
+  float* red = reinterpret_cast<float*>(smem);  // [wave][fb * 4 + r][lane]
+  static_assert(kRedBytes <= sizeof(smem), "the wave sums fit in the tile memory");
 #pragma unroll
   for (int fb = 0; fb < kFB; ++fb)
 #pragma unroll
@@ -526,14 +555,26 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   }
 }
 
+// the whole rotated activation rows of a launch fit this much dynamic LDS
+constexpr int kPreRotBytes = 48 * 1024;
+
 template <int MT, int FB, bool NORM>
 hipError_t launch_rot(GemvArgs& args, int blocks, int32_t block, hipStream_t stream) {
-  if (block == 1024)
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 1024, NORM>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+  int max_k = 0;
+  for (int i = 0; i < args.count; ++i) max_k = args.job[i].k > max_k ? args.job[i].k : max_k;
+  const size_t pre_bytes = (size_t)MT * (size_t)max_k * 2;
+  if (block == 1024 && pre_bytes <= (size_t)kPreRotBytes)
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 1024, NORM, true>), dim3(blocks), dim3(kWaves * 64), pre_bytes,
+                       stream, args);
+  else if (block == 1024)
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 1024, NORM, false>), dim3(blocks), dim3(kWaves * 64), 0, stream,
+                       args);
   else if (block)
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 128, NORM>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 128, NORM, false>), dim3(blocks), dim3(kWaves * 64), 0, stream,
+                       args);
   else
-    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 0, NORM>), dim3(blocks), dim3(kWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL((gemv_b3_mfma_kernel<MT, FB, 0, NORM, false>), dim3(blocks), dim3(kWaves * 64), 0, stream,
+                       args);
   return hipGetLastError();
 }
 
