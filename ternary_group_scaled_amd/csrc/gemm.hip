@@ -20,7 +20,7 @@
 // Within every 16 consecutive k, both tiles are stored in the order 0,8,1,9,...,7,15 (the order
 // the slot-2 decode produces pairs in); the contraction over k does not depend on that order.
 // Binary codes (t in {-1, +1}, one bit per weight) decode the same way into bf16 2t in {-2, +2}.
-// Up to 32 activation rows of slot-2 codes take the skinny kernel further below instead.
+// Up to 32 activation rows of slot-2 or binary codes take the skinny kernel further below instead.
 #include <algorithm>
 
 #include "tgs_internal.h"
@@ -291,7 +291,7 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
     }
 }
 
-// ---- skinny product: up to 32 activation rows, slot-2 codes ----------------------------------
+// ---- skinny product: up to 32 activation rows, slot-2 or binary codes -----------------------
 //
 // With few activation rows the tile kernel above has too few workgroups (n / 128) to fill the
 // chip, and its LDS round trips sit on the critical path. Here a workgroup of W waves owns
@@ -301,6 +301,7 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
 // per group. Within each 16 consecutive k, both operands use the order 0,8,1,9,...,7,15 of the
 // slot-2 decode, so the contraction is unchanged. Each group's partial is scaled in fp32; the W
 // per-wave results are added through LDS in wave order (deterministic, no atomics).
+// Binary codes (BIN) take 4 bytes (32 weights) per lane per group and decode to the same pair order.
 // Every workgroup reads all of x for its outputs, so x traffic from L2 falls as FB grows. The
 // host picks FB so that a launch is about one workgroup per CU (one round of workgroups) rather
 // than shrinking FB to get more workgroups.
@@ -319,6 +320,20 @@ __device__ __forceinline__ uint4 decode4_slot2(uint32_t u) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// pairs 4H..4H+3 of decode16_binary(u): bf16(2t_i) low, bf16(2t_{i+8}) high, from bits 0..15 of u
+template <int H>
+__device__ __forceinline__ uint4 decode4_binary(uint32_t u) {
+  constexpr uint32_t kTable = 0x000040C0u;
+  const uint32_t v = (u & 0xFFu) | ((u & 0xFF00u) << 8);  // bit i + 8 -> bit i + 16
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * H + j;
+    o[j] = __builtin_amdgcn_perm(0u, kTable, ((v << (8 - i)) & 0x01000100u) | 0x000C000Cu);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // pairs 4H..4H+3 of interleave16 over 16 consecutive bf16 values in w[0..7]
 template <int H>
 __device__ __forceinline__ uint4 interleave4(const uint32_t* w) {
@@ -328,7 +343,7 @@ __device__ __forceinline__ uint4 interleave4(const uint32_t* w) {
     return make_uint4(pair16<4, 12>(w), pair16<5, 13>(w), pair16<6, 14>(w), pair16<7, 15>(w));
 }
 
-template <int TB, int kFB, int kWaves, int kStages>
+template <int TB, int kFB, int kWaves, int kStages, bool BIN>
 __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t* __restrict__ codes, int64_t stride,
                                                           const uint16_t* __restrict__ scales, int n, int k,
                                                           const uint16_t* __restrict__ x, int m,
@@ -360,7 +375,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
 #pragma unroll
   for (int fb = 0; fb < kFB; ++fb) {
     const uint32_t row = (uint32_t)(n_base + 16 * fb + fr);
-    code_off[fb] = row * (uint32_t)stride + 8u * (uint32_t)kq;
+    code_off[fb] = row * (uint32_t)stride + (BIN ? 4u : 8u) * (uint32_t)kq;
     scale_off[fb] = row * (uint32_t)groups * 2u;
   }
 #pragma unroll
@@ -385,10 +400,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
     if (g >= g_end) g -= count;
 #pragma unroll
     for (int fb = 0; fb < kFB; ++fb) {
-      const int off = live ? (int)(code_off[fb] + 32u * (uint32_t)g) : kOobOffset;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, off, 0, 0);
-      st.cw[fb][0] = v[0];
-      st.cw[fb][1] = v[1];
+      if constexpr (BIN) {  // 16 bytes of codes per group
+        const int off = live ? (int)(code_off[fb] + 16u * (uint32_t)g) : kOobOffset;
+        st.cw[fb][0] = __builtin_amdgcn_raw_buffer_load_b32(code_rsrc, off, 0, 0);
+        st.cw[fb][1] = 0;
+      } else {  // 32 bytes of codes per group
+        const int off = live ? (int)(code_off[fb] + 32u * (uint32_t)g) : kOobOffset;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, off, 0, 0);
+        st.cw[fb][0] = v[0];
+        st.cw[fb][1] = v[1];
+      }
       st.sc[fb] = __builtin_amdgcn_raw_buffer_load_b16(
           scale_rsrc, live ? (int)(scale_off[fb] + 2u * (uint32_t)g) : kOobOffset, 0, 0);
     }
@@ -425,9 +446,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
         a[tb] = __builtin_bit_cast(bf16x8, (s & 1) ? interleave4<1>(st.xv[tb] + 8 * (s >> 1))
                                                    : interleave4<0>(st.xv[tb] + 8 * (s >> 1)));
 #pragma unroll
-      for (int fb = 0; fb < kFB; ++fb)
-        b[fb] = __builtin_bit_cast(bf16x8, (s & 1) ? decode4_slot2<1>(st.cw[fb][s >> 1])
-                                                   : decode4_slot2<0>(st.cw[fb][s >> 1]));
+      for (int fb = 0; fb < kFB; ++fb) {
+        if constexpr (BIN)  // step s: bits 16 (s >> 1) .. + 15 of the lane's word
+          b[fb] = __builtin_bit_cast(bf16x8, (s & 1) ? decode4_binary<1>(st.cw[fb][0] >> (16 * (s >> 1)))
+                                                     : decode4_binary<0>(st.cw[fb][0] >> (16 * (s >> 1))));
+        else
+          b[fb] = __builtin_bit_cast(bf16x8, (s & 1) ? decode4_slot2<1>(st.cw[fb][s >> 1])
+                                                     : decode4_slot2<0>(st.cw[fb][s >> 1]));
+      }
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -480,7 +506,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
 template <int LAYOUT>
 hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
                          const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
-  if (LAYOUT == TGS_LAYOUT_SLOT2 && m <= 32) {
+  constexpr bool kBin = LAYOUT == TGS_LAYOUT_BINARY;
+  if ((LAYOUT == TGS_LAYOUT_SLOT2 || kBin) && m <= 32) {
     const int ni = (int)n, ki = (int)k, mi = (int)m;
     if (m <= 16) {
       // 16 * FB outputs per workgroup of 8 waves, FB = n / 4096 rounded up, within 2..6: about one
@@ -490,8 +517,8 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
       const int64_t fb = std::min<int64_t>(6, std::max<int64_t>(2, (n + 4095) / 4096));
       const dim3 grid((unsigned)((n + 16 * fb - 1) / (16 * fb)));
 #define TGS_SKINNY(FB_)                                                                                          \
-  hipLaunchKernelGGL((gemm_skinny_kernel<1, FB_, 8, 2>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki, \
-                     x, mi, y)
+  hipLaunchKernelGGL((gemm_skinny_kernel<1, FB_, 8, 2, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, \
+                     ki, x, mi, y)
       switch (fb) {
         case 2: TGS_SKINNY(2); break;
         case 3: TGS_SKINNY(3); break;
@@ -505,13 +532,13 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
       const int64_t fb = (n + 63) / 64 >= 512 ? 4 : ((n + 31) / 32 >= 512 ? 2 : 1);
       const dim3 grid((unsigned)((n + 16 * fb - 1) / (16 * fb)), (unsigned)((m + 31) / 32));
       if (fb == 4)
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 8, 3>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 8, 3, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
                            x, mi, y);
       else if (fb == 2)
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, 2, 8, 3>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, 2, 8, 3, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
                            x, mi, y);
       else
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, 1, 8, 3>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, 1, 8, 3, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
                            x, mi, y);
     }
     return hipGetLastError();
