@@ -75,12 +75,13 @@ def parse():
 # ----------------------------------------------------------------------------- inputs
 
 def build_matrix(torch, tgs, synth, layout, seed, tag, n, k, p_zero, rotated=False):
+    """The device matrix, plus its trits and fp16 scales (the oracle packs the trits itself)."""
     t = synth.trits(seed, synth.stream_id(tag, "codes"), (n, k), p_zero)
     s = synth.scales_f16(seed, synth.stream_id(tag, "scales"), (n, k // 128))
     codes, scales = tgs.pack_ternary(layout, t, s)
     w = tgs.PackedMatrix(layout, torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda(), k,
                          rotated=rotated)
-    return w, codes, scales
+    return w, t, s
 
 
 def x_f16_dev(torch, synth, seed, tag, m, k):
@@ -161,10 +162,10 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
     for L in range(layers):
         d = {}
         for name, n, k in LAYER_8B:
-            w, codes, scales = build_matrix(torch, tgs, synth, layout, 0, f"{tag}/L{L}/{name}", n, k, p_zero)
+            w, trits, scales = build_matrix(torch, tgs, synth, layout, 0, f"{tag}/L{L}/{name}", n, k, p_zero)
             d[name] = w
             if L == 0:
-                host.append((name, codes, scales, n, k))
+                host.append((name, trits, scales, n, k))
         mats.append(d)
     inputs, outputs = [], []
     for L in range(layers):
@@ -253,9 +254,10 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
 def cpu_baseline_8b(torch, host, xs, ys, layout, seconds, gpu_ms, layer_bytes, layers):
     """The fp64 oracle on the host cores over layer 0's 7 matrices, with the inputs the GPU pass
     used, repeated for ~`seconds`. Its first pass is also compared with the GPU's layer-0 outputs
-    (every row, within the tolerance bound)."""
+    (every row, within the tolerance bound). The oracle packs layer 0's trits itself (untimed)."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    host = [(name, oracle.pack(layout, trits), scales, n, k) for name, trits, scales, n, k in host]
     torch.cuda.synchronize()
     y_gpu = {name: ys[name].cpu().numpy().astype(np.float64) for name, _, _, _, _ in host}
     x_of = {name: xs[[g for g in GROUPS_8B if name in g][0]][1] for name, _, _, _, _ in host}
@@ -435,7 +437,7 @@ def bench_flips(args, torch, tgs, synth):
                 b = tgs.PackedMatrix(layout, torch.from_numpy(cb).cuda(), sd, k)
                 pairs.append((a, b))
                 if L == 0:
-                    host0.append((nm, ca, cb, k))
+                    host0.append((nm, t, u, k))
         totals = [torch.zeros(1, dtype=torch.int64, device="cuda") for _ in pairs]
         rows = [torch.empty(a.n, dtype=torch.int32, device="cuda") for a, _ in pairs]
         torch.cuda.synchronize()
@@ -481,9 +483,11 @@ def bench_flips(args, torch, tgs, synth):
 
 def cpu_baseline_flips(torch, host0, rows0, layout, seconds, gpu_ms, n_pairs):
     """The oracle's code-flip count over layer 0's 7 pairs, repeated for ~`seconds`; its first pass
-    is also compared with the GPU's per-row counts of those pairs."""
+    is also compared with the GPU's per-row counts of those pairs. The oracle packs the two
+    checkpoints' trits itself (untimed)."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    host0 = [(nm, oracle.pack(layout, t), oracle.pack(layout, u), k) for nm, t, u, k in host0]
     gpu_rows = [r.cpu().numpy().astype(np.int64) for r in rows0]
     t0 = time.time()
     passes, nbytes = 0, sum(ca.nbytes + cb.nbytes for _, ca, cb, _ in host0)

@@ -38,12 +38,16 @@ def _sample_rows(n, count, seed):
 
 
 def _matrix(layout, tag, n, k, p_zero, rotated=0):
+    """The device matrix (packed by the library) and the oracle's own packing of the same trits,
+    which must be identical; the oracle is only ever given its own bytes."""
     t = synth.trits(0, synth.stream_id(tag, "codes"), (n, k), p_zero)
     s = synth.scales_f16(0, synth.stream_id(tag, "scales"), (n, k // 128))
     codes, scales = tgs.pack_ternary(layout, t, s)
+    ref_codes = oracle.pack(layout, t)
+    assert np.array_equal(codes, ref_codes)
     w = tgs.PackedMatrix(layout, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales.view(np.int16)).to(DEV),
                          k, rotated=rotated)
-    return w, codes, scales
+    return w, ref_codes, s
 
 
 def _x_f16(tag, m, k):
@@ -149,3 +153,39 @@ def test_27b_prefill_gemm(m):
         torch.cuda.synchronize()
         _check_rows(tgs.SLOT2, codes, scales, k, xb, oracle.X_BF16, y.cpu().numpy(),
                     _sample_rows(n, 24 if m == 2048 else 40, 20 + i), f"27B GEMM {name} m={m}")
+
+
+@pytest.mark.parametrize("layout", [tgs.SLOT2, tgs.BINARY, tgs.BASE3], ids=LNAME.get)
+@pytest.mark.parametrize("k", [65536, 65536 + 128, 32768, 32768 + 1024])
+def test_gemv_at_the_single_token_kernel_limits(layout, k):
+    """K at and just past the largest K of the single-token kernel (65536 plain, 32768 with the
+    RMSNorm prologue): either kernel must give the oracle's rows, with and without the norm."""
+    n = 96
+    p_zero = {tgs.SLOT2: 0.4, tgs.BASE3: 0.5, tgs.BINARY: 0.0}[layout]
+    w, codes, scales = _matrix(layout, f"limk/{layout}/{k}", n, k, p_zero)
+    xd, xh = _x_f16(f"limk/{k}", 1, k)
+    y = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    tgs.ternary_gemv_batched([w], [xd], [y])
+    gamma = synth.bf16_bits(1.0 + 0.25 * synth.normal(1, k, (k,)))
+    yn = tgs.ternary_gemv_rmsnorm(w, xd, torch.from_numpy(gamma.view(np.int16).copy()).to(DEV), 1e-6)
+    torch.cuda.synchronize()
+    rows = _sample_rows(n, 32, k)
+    _check_rows(layout, codes, scales, k, xh.view(np.uint16), oracle.X_F16, y.cpu().numpy(), rows, f"k={k}")
+    y_ref, bound = oracle.matmul(layout, codes, scales, k, xh.view(np.uint16), oracle.X_F16, rows=rows,
+                                 gamma=gamma, eps=float(np.float32(1e-6)))
+    assert (np.abs(yn.cpu().numpy()[:, rows] - y_ref) <= bound).all(), f"rmsnorm k={k}"
+
+
+@pytest.mark.parametrize("layout", [tgs.SLOT2, tgs.BINARY, tgs.BASE3], ids=LNAME.get)
+def test_gemv_with_a_million_rows(layout):
+    """n = 2^20 rows of K = 256: tens of thousands of workgroups, first and last rows included."""
+    n, k = 1 << 20, 256
+    p_zero = {tgs.SLOT2: 0.4, tgs.BASE3: 0.5, tgs.BINARY: 0.0}[layout]
+    w, codes, scales = _matrix(layout, f"mrows/{layout}", n, k, p_zero)
+    for m in (1, 8):
+        xd, xh = _x_f16(f"mrows/{m}", m, k)
+        y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+        tgs.ternary_gemv_batched([w], [xd], [y])
+        torch.cuda.synchronize()
+        _check_rows(layout, codes, scales, k, xh.view(np.uint16), oracle.X_F16, y.cpu().numpy(),
+                    _sample_rows(n, 64, m), f"{n}x{k} m={m}")

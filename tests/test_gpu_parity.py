@@ -342,7 +342,8 @@ def test_gemm_integer_inputs_are_exact_and_match_gemv():
 
 def _flip_pair(layout, n, k, frac, seed, pad=0):
     """Two packed checkpoints: t and t with a seeded fraction of trits changed. Returns
-    (PackedMatrix a, PackedMatrix b, codes_a, codes_b)."""
+    (PackedMatrix a, PackedMatrix b, codes_a, codes_b) where codes_a and codes_b are the oracle's
+    own packing (the library's bytes must equal them; the padded stride copies the oracle's)."""
     t = synth.trits(seed, n * 7 + k, (n, k), 0.4)
     rng = np.random.default_rng(seed)
     mask = rng.random((n, k)) < frac
@@ -352,6 +353,8 @@ def _flip_pair(layout, n, k, frac, seed, pad=0):
     s = synth.scales_f16(seed, 5, (n, k // 128))
     ca, _ = tgs.pack_ternary(layout, t, s)
     cb, _ = tgs.pack_ternary(layout, u, s)
+    assert np.array_equal(ca, oracle.pack(layout, t)) and np.array_equal(cb, oracle.pack(layout, u))
+    ca, cb = oracle.pack(layout, t), oracle.pack(layout, u)
     if pad:  # a wider row stride for the first matrix, with garbage past its codes
         wide = np.full((n, ca.shape[1] + pad), 0xEE, dtype=np.uint8)
         wide[:, :ca.shape[1]] = ca
@@ -529,6 +532,8 @@ def test_binary_code_flips_match_oracle(n, k, frac):
     u = np.where(mask, -t, t).astype(np.int8)
     ca, _ = tgs.pack_ternary(tgs.BINARY, t, s)
     cb, _ = tgs.pack_ternary(tgs.BINARY, u, s)
+    assert np.array_equal(ca, oracle.pack(tgs.BINARY, t)) and np.array_equal(cb, oracle.pack(tgs.BINARY, u))
+    ca, cb = oracle.pack(tgs.BINARY, t), oracle.pack(tgs.BINARY, u)
     sd = torch.from_numpy(s.view(np.int16)).to(DEV)
     a = tgs.PackedMatrix(tgs.BINARY, torch.from_numpy(ca).to(DEV), sd, k)
     b = tgs.PackedMatrix(tgs.BINARY, torch.from_numpy(cb).to(DEV), sd, k)
