@@ -610,14 +610,18 @@ __device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& 
 // Only the wave itself uses its region and one wave's LDS accesses complete in order, so no
 // barrier is needed. Unit U is stored at slot U ^ ((U >> 3) & 7) of 16-byte slots: in every group
 // of 8 lanes, both the writes and the reads then touch 8 different slots of a 128-byte row.
+// W row waves (W = 4, for launches whose rows span one K slice) share the slice's activations:
+// the workgroup holds W waves, each with its own rows; they load the 8 KB together (2 loads per
+// lane) and meet at one barrier before reading their lanes' bytes, so x is read once per W waves.
 // NORM: the RMSNorm prologue. The lane's 64 activations are in its registers, so the sum of
 // squares costs a few FMAs per lane; the waves' sums meet in LDS after one barrier (by then every
 // wave's first weight loads are in flight), and each lane scales its activations by gamma and
 // 1 / rms before building its dot2 pairs. At most 8 waves (K <= 32768) in this variant.
-template <int S, int G, bool BIN, bool NORM, bool XS>
+template <int S, int G, bool BIN, bool NORM, bool XS, int W>
 __global__ __launch_bounds__(NORM ? 512 : 1024)
 void gemv_wave_kernel(const GemvArgs args) {
   static_assert(!XS || (S == 64 && !NORM), "activation staging is for 64 lanes per row");
+  static_assert(W == 1 || (XS && W == kWaveKernelRowWaves), "row waves share activations through LDS only");
   constexpr int kRowsPerInstr = 64 / S;
   constexpr int kRing = G;  // batches per group: 4, or 1-2 for waves of 2-4 rows
   // dynamic LDS: XS: [slices][512] 16-byte units of activations; then [slices][rows of the
@@ -629,17 +633,19 @@ void gemv_wave_kernel(const GemvArgs args) {
   const int n = job.n, k = job.k;
   const int groups = k / 128;
   const int chunks = k / 64;
-  const int slices = (chunks + S - 1) / S;  // == waves per workgroup
+  const int slices = (chunks + S - 1) / S;  // waves per workgroup: slices * W
   const int R = args.rows_per_wave;         // row slots per wave: 2 * G * (number of groups)
   const int batches = R / 2;
-  const int rows_wg = R * kRowsPerInstr;
+  const int rows_wave = R * kRowsPerInstr;
+  const int rows_wg = W * rows_wave;
 
-  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;  // wave index == K slice
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % slices, rw = wave / slices;  // K slice and row wave
   const int cl = lane % S, rslot = lane / S;
   const int c = ks * S + cl;  // this lane's chunk
   const bool lane_live = c < chunks;
   const int block_row0 = ((int)blockIdx.x - job.block0) * rows_wg;
-  const int row0 = block_row0 + rslot;
+  const int row0 = block_row0 + rw * rows_wave + rslot;
   uint4* lds_x = reinterpret_cast<uint4*>(lds_dyn);
   float* lds_acc = reinterpret_cast<float*>(lds_dyn + (XS ? slices * 8192 : 0));
 
@@ -650,15 +656,17 @@ void gemv_wave_kernel(const GemvArgs args) {
       __builtin_amdgcn_make_buffer_rsrc((void*)job.scales, 0, (int)((int64_t)n * groups * 2), kRsrcWord3);
 
   // 1. activations of this lane's chunk (reads past K return zero), and their norm weights
+  // (XS: this wave's share of the slice's coalesced loads, units 64 v + lane for v = rw, rw + W, ..)
   uint32_t xw[32];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
+  for (int i = 0; i < 8 / W; ++i) {
+    const int v = XS ? rw + W * i : i;
     const int xoff = XS ? ks * 8192 + 1024 * v + 16 * lane : c * 128 + 16 * v;
     const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xoff, 0, 0));
-    xw[4 * v + 0] = q.x;
-    xw[4 * v + 1] = q.y;
-    xw[4 * v + 2] = q.z;
-    xw[4 * v + 3] = q.w;
+    xw[4 * i + 0] = q.x;
+    xw[4 * i + 1] = q.y;
+    xw[4 * i + 2] = q.z;
+    xw[4 * i + 3] = q.w;
   }
   uint32_t gw[NORM ? 32 : 1];
   if constexpr (NORM) {
@@ -699,10 +707,11 @@ void gemv_wave_kernel(const GemvArgs args) {
   if constexpr (XS) {
     uint4* region = lds_x + ks * 512;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int u = 64 * v + lane;
-      region[u ^ ((u >> 3) & 7)] = make_uint4(xw[4 * v], xw[4 * v + 1], xw[4 * v + 2], xw[4 * v + 3]);
+    for (int i = 0; i < 8 / W; ++i) {
+      const int u = 64 * (rw + W * i) + lane;
+      region[u ^ ((u >> 3) & 7)] = make_uint4(xw[4 * i], xw[4 * i + 1], xw[4 * i + 2], xw[4 * i + 3]);
     }
+    if constexpr (W > 1) __syncthreads();  // the slice's other units come from the other row waves
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int u = 8 * lane + j;
@@ -741,7 +750,7 @@ void gemv_wave_kernel(const GemvArgs args) {
     int slot;
     const float sum = reduce_pair<S>(v0, v1, lane, slot);
     if (writer) {
-      const int local = (2 * b + slot) * kRowsPerInstr + rslot;  // one writer per (row, slice)
+      const int local = rw * rows_wave + (2 * b + slot) * kRowsPerInstr + rslot;  // one writer per (row, slice)
       if (slices == 1) {
         const int row = block_row0 + local;
         if (row < n) job.y[row] = sum * 1048576.0f;
@@ -774,37 +783,42 @@ void gemv_wave_kernel(const GemvArgs args) {
   }
 }
 
-template <int S, bool BIN, bool NORM, bool XS>
+template <int S, bool BIN, bool NORM, bool XS, int W>
 hipError_t launch_wave_xs(GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
-  const size_t lds = (slices > 1 ? (size_t)slices * rows_per_wave * (64 / S) * sizeof(float) : 0) +
+  const size_t lds = (slices > 1 ? (size_t)slices * W * rows_per_wave * (64 / S) * sizeof(float) : 0) +
                      (XS ? (size_t)slices * 8192 : 0);
   args.rows_per_wave = rows_per_wave;
+  const dim3 block(64 * slices * W);
   // with the norm's 32 extra registers the 4-batch ring would cost a wave per SIMD (148 registers);
   // the 2-batch ring keeps 4 and measured the same
   if (rows_per_wave >= 8 && !NORM)
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 4, BIN, NORM, XS>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 4, BIN, NORM, XS, W>), dim3(blocks), block, lds, stream, args);
   else if (rows_per_wave >= 4)
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 2, BIN, NORM, XS>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 2, BIN, NORM, XS, W>), dim3(blocks), block, lds, stream, args);
   else
-    hipLaunchKernelGGL((gemv_wave_kernel<S, 1, BIN, NORM, XS>), dim3(blocks), dim3(64 * slices), lds, stream, args);
+    hipLaunchKernelGGL((gemv_wave_kernel<S, 1, BIN, NORM, XS, W>), dim3(blocks), block, lds, stream, args);
   return hipGetLastError();
 }
 
-// activations staged through LDS (XS) with 64 lanes per row and at most 4 K slices (32 KB)
+// activations staged through LDS (XS) with 64 lanes per row and at most 4 K slices (32 KB), shared
+// by row_waves waves per slice
 template <int S, bool BIN, bool NORM>
-hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
+hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices, int row_waves,
+                       hipStream_t stream) {
   if constexpr (S == 64 && !NORM) {
-    if (slices <= 4) return launch_wave_xs<S, BIN, NORM, true>(args, blocks, rows_per_wave, slices, stream);
+    if (slices == 1 && row_waves == kWaveKernelRowWaves)
+      return launch_wave_xs<S, BIN, NORM, true, kWaveKernelRowWaves>(args, blocks, rows_per_wave, slices, stream);
+    if (slices <= 4) return launch_wave_xs<S, BIN, NORM, true, 1>(args, blocks, rows_per_wave, slices, stream);
   }
-  return launch_wave_xs<S, BIN, NORM, false>(args, blocks, rows_per_wave, slices, stream);
+  return launch_wave_xs<S, BIN, NORM, false, 1>(args, blocks, rows_per_wave, slices, stream);
 }
 
 template <bool BIN, bool NORM>
-hipError_t launch_wave_s(int lanes, GemvArgs& args, int blocks, int rows_per_wave, int slices, hipStream_t stream) {
-  switch (lanes) {
-    case 16: return launch_wave<16, BIN, NORM>(args, blocks, rows_per_wave, slices, stream);
-    case 32: return launch_wave<32, BIN, NORM>(args, blocks, rows_per_wave, slices, stream);
-    default: return launch_wave<64, BIN, NORM>(args, blocks, rows_per_wave, slices, stream);
+hipError_t launch_wave_s(const GemvPlan& plan, GemvArgs& args, int blocks, hipStream_t stream) {
+  switch (plan.lanes) {
+    case 16: return launch_wave<16, BIN, NORM>(args, blocks, plan.iter, plan.slices, 1, stream);
+    case 32: return launch_wave<32, BIN, NORM>(args, blocks, plan.iter, plan.slices, 1, stream);
+    default: return launch_wave<64, BIN, NORM>(args, blocks, plan.iter, plan.slices, plan.row_waves, stream);
   }
 }
 
@@ -864,6 +878,7 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated, bool n
   p.m = (int32_t)m;
   p.rotated = rotated;
   p.norm = norm ? 1 : 0;
+  p.row_waves = 1;
   p.slices = 0;
   p.mfma = 0;
   // base-3: decode once, multiply all tokens on the matrix cores
@@ -916,7 +931,13 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
     while (r > 4 && (total_rows + r * rows_per_instr - 1) / (r * rows_per_instr) * p.slices < kWaveKernelTargetWaves)
       r /= 2;
     p.iter = r;
-    p.rows_per_block = (int32_t)(r * rows_per_instr);
+    // row waves sharing the activations (64 lanes per row, one K slice, no norm), for launches of
+    // up to kWaveKernelShareRows rows. Measured on the 8B set: 4 row waves +9% in layer order;
+    // 8 row waves, or sharing in the 3-slice launches, or in launches of a whole set, were slower.
+    p.row_waves = 1;
+    if (p.lanes == 64 && p.slices == 1 && !p.norm && total_rows <= kWaveKernelShareRows)
+      p.row_waves = kWaveKernelRowWaves;
+    p.rows_per_block = (int32_t)(r * rows_per_instr * p.row_waves);
     return;
   }
   // single-token slot-2 launches with plenty of rows: twice the rows per workgroup (8 rows per lane
@@ -935,10 +956,10 @@ hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hip
   const bool bin = plan.layout == TGS_LAYOUT_BINARY;
   if (plan.stream) {
     if (plan.norm)
-      return bin ? launch_wave_s<true, true>(plan.lanes, args, blocks, plan.iter, plan.slices, stream)
-                 : launch_wave_s<false, true>(plan.lanes, args, blocks, plan.iter, plan.slices, stream);
-    return bin ? launch_wave_s<true, false>(plan.lanes, args, blocks, plan.iter, plan.slices, stream)
-               : launch_wave_s<false, false>(plan.lanes, args, blocks, plan.iter, plan.slices, stream);
+      return bin ? launch_wave_s<true, true>(plan, args, blocks, stream)
+                 : launch_wave_s<false, true>(plan, args, blocks, stream);
+    return bin ? launch_wave_s<true, false>(plan, args, blocks, stream)
+               : launch_wave_s<false, false>(plan, args, blocks, stream);
   }
   const int rot = (int)rotation_block(plan.rotated), mt = tokens_per_pass(plan.m);
   return bin ? launch_s<true>(plan.lanes, mt, rot, plan.iter, args, blocks, stream)

@@ -22,6 +22,10 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kMaxWaveKernelK = 16 * 4096;
 // and aims for at least this many waves per launch when choosing rows per wave
 constexpr int kWaveKernelTargetWaves = 4096;
+// and, with 64 lanes per row and one K slice, this many row waves share the activations, in
+// launches of up to kWaveKernelShareRows rows
+constexpr int kWaveKernelRowWaves = 4;
+constexpr int64_t kWaveKernelShareRows = 65536;
 
 // One matrix of a batched GEMV launch. All pointers are device pointers.
 struct GemvJob {
@@ -89,6 +93,7 @@ struct GemvPlan {
   int32_t iter;       // rows per lane slot
   int32_t rows_per_block;
   int32_t norm;       // 1: RMSNorm prologue
+  int32_t row_waves;  // single-token kernel: waves per K slice sharing the activations
 };
 
 // Launch helpers implemented in the .hip files. They only queue work; all argument checks

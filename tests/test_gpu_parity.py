@@ -55,7 +55,7 @@ def test_config1_slot2_gemv():
 
 
 SHAPES = [(1, 128), (17, 256), (300, 1024), (129, 4096), (64, 5120), (33, 12288), (40, 17408), (70, 640),
-          (9, 30720), (130, 2048)]
+          (9, 30720), (130, 2048), (257, 2560), (1000, 3968)]
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
