@@ -618,16 +618,17 @@ __device__ __forceinline__ float reduce_pair(float v0, float v1, int lane, int& 
 // wave's first weight loads are in flight), and each lane scales its activations by gamma and
 // 1 / rms before building its dot2 pairs. At most 8 waves (K <= 32768) in this variant.
 template <int S, int G, bool BIN, bool NORM, bool XS, int W>
-__global__ __launch_bounds__(NORM ? 512 : 1024)
+__global__ __launch_bounds__(1024)  // (also with NORM, whose workgroups are smaller: 128 registers
+                                    // keep 4 waves per SIMD)
 void gemv_wave_kernel(const GemvArgs args) {
-  static_assert(!XS || (S == 64 && !NORM), "activation staging is for 64 lanes per row");
+  static_assert(!XS || S == 64, "activation staging is for 64 lanes per row");
   static_assert(W == 1 || (XS && W == kWaveKernelRowWaves), "row waves share activations through LDS only");
   constexpr int kRowsPerInstr = 64 / S;
   constexpr int kRing = G;  // batches per group: 4, or 1-2 for waves of 2-4 rows
-  // dynamic LDS: XS: [slices][512] 16-byte units of activations; then [slices][rows of the
-  // workgroup] slice sums, when slices > 1
+  // dynamic LDS: XS: [slices][512] 16-byte units of activations (normalised, with NORM); then
+  // [slices][rows of the workgroup] slice sums, when slices > 1
   extern __shared__ __attribute__((aligned(16))) char lds_dyn[];
-  __shared__ float norm_part[NORM ? 8 : 1];  // RMSNorm: sum of squares of each wave's K slice
+  __shared__ float norm_part[NORM ? 8 : 1];  // RMSNorm: each wave's sum of squares
 
   const GemvJob job = gemv_job_of_block(args);  // a copy: the fields stay in scalar registers
   const int n = job.n, k = job.k;
@@ -672,12 +673,14 @@ void gemv_wave_kernel(const GemvArgs args) {
   if constexpr (NORM) {
     const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)job.gamma, 0, k * 2, kRsrcWord3);
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(g_rsrc, c * 128 + 16 * v, 0, 0));
-      gw[4 * v + 0] = q.x;
-      gw[4 * v + 1] = q.y;
-      gw[4 * v + 2] = q.z;
-      gw[4 * v + 3] = q.w;
+    for (int i = 0; i < 8 / W; ++i) {
+      const int v = XS ? rw + W * i : i;
+      const int goff = XS ? ks * 8192 + 1024 * v + 16 * lane : c * 128 + 16 * v;
+      const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(g_rsrc, goff, 0, 0));
+      gw[4 * i + 0] = q.x;
+      gw[4 * i + 1] = q.y;
+      gw[4 * i + 2] = q.z;
+      gw[4 * i + 3] = q.w;
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order
@@ -705,6 +708,23 @@ void gemv_wave_kernel(const GemvArgs args) {
   __builtin_amdgcn_sched_barrier(0);  // every load is out before anything waits
 
   if constexpr (XS) {
+    if constexpr (NORM) {
+      // RMSNorm while staging: every unit of x is held by exactly one thread of the workgroup, so
+      // each thread adds the squares of its own units, the waves' sums meet in LDS, and each
+      // thread scales its units by gamma / rms before storing them (once per workgroup, not once
+      // per wave)
+      float sq = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4 * (8 / W); ++i) sq = add_squares(xw[i], sq);
+      sq = wave_sum(sq, lane);
+      if (lane == 0) norm_part[wave] = sq;
+      __syncthreads();
+      float total = 0.f;
+      for (int q = 0; q < slices * W; ++q) total += norm_part[q];
+      const float r = 1.0f / sqrtf(total / (float)k + args.eps);
+#pragma unroll
+      for (int i = 0; i < 4 * (8 / W); ++i) xw[i] = norm_word(xw[i], gw[i], r);
+    }
     uint4* region = lds_x + ks * 512;
 #pragma unroll
     for (int i = 0; i < 8 / W; ++i) {
@@ -722,7 +742,7 @@ void gemv_wave_kernel(const GemvArgs args) {
       xw[4 * j + 3] = q.w;
     }
   }
-  if constexpr (NORM) {
+  if constexpr (NORM && !XS) {
     // the row's sum of squares: each chunk once (lanes of row slot 0), wave by wave in LDS
     float sq = 0.f;
 #pragma unroll
@@ -789,9 +809,7 @@ hipError_t launch_wave_xs(GemvArgs& args, int blocks, int rows_per_wave, int sli
                      (XS ? (size_t)slices * 8192 : 0);
   args.rows_per_wave = rows_per_wave;
   const dim3 block(64 * slices * W);
-  // with the norm's 32 extra registers the 4-batch ring would cost a wave per SIMD (148 registers);
-  // the 2-batch ring keeps 4 and measured the same
-  if (rows_per_wave >= 8 && !NORM)
+  if (rows_per_wave >= 8)
     hipLaunchKernelGGL((gemv_wave_kernel<S, 4, BIN, NORM, XS, W>), dim3(blocks), block, lds, stream, args);
   else if (rows_per_wave >= 4)
     hipLaunchKernelGGL((gemv_wave_kernel<S, 2, BIN, NORM, XS, W>), dim3(blocks), block, lds, stream, args);
@@ -805,7 +823,7 @@ hipError_t launch_wave_xs(GemvArgs& args, int blocks, int rows_per_wave, int sli
 template <int S, bool BIN, bool NORM>
 hipError_t launch_wave(GemvArgs& args, int blocks, int rows_per_wave, int slices, int row_waves,
                        hipStream_t stream) {
-  if constexpr (S == 64 && !NORM) {
+  if constexpr (S == 64) {
     if (slices == 1 && row_waves == kWaveKernelRowWaves)
       return launch_wave_xs<S, BIN, NORM, true, kWaveKernelRowWaves>(args, blocks, rows_per_wave, slices, stream);
     if (slices <= 4) return launch_wave_xs<S, BIN, NORM, true, 1>(args, blocks, rows_per_wave, slices, stream);
@@ -931,11 +949,11 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
     while (r > 4 && (total_rows + r * rows_per_instr - 1) / (r * rows_per_instr) * p.slices < kWaveKernelTargetWaves)
       r /= 2;
     p.iter = r;
-    // row waves sharing the activations (64 lanes per row, one K slice, no norm), for launches of
+    // row waves sharing the activations (64 lanes per row, one K slice), for launches of
     // up to kWaveKernelShareRows rows. Measured on the 8B set: 4 row waves +9% in layer order;
     // 8 row waves, or sharing in the 3-slice launches, or in launches of a whole set, were slower.
     p.row_waves = 1;
-    if (p.lanes == 64 && p.slices == 1 && !p.norm && total_rows <= kWaveKernelShareRows)
+    if (p.lanes == 64 && p.slices == 1 && total_rows <= kWaveKernelShareRows)
       p.row_waves = kWaveKernelRowWaves;
     p.rows_per_block = (int32_t)(r * rows_per_instr * p.row_waves);
     return;
