@@ -321,12 +321,38 @@ def bench_rotated(args, torch, tgs, synth):
 
         ms, _ = time_graph(torch, one_pass, args.steps, args.warmup)
         log(f"[bench] rotated m={m}: step {ms * 1e3:.1f} us -> {nb / ms / 1e6:.0f} GB/s")
+
+        # the same products in two passes: hadamard_rotate of each input once (fp16 out), then the
+        # plain-basis GEMV on descriptors of the same code buffers (the rotation is not repeated by
+        # every workgroup that reads a group)
+        plain = [tgs.PackedMatrix(2, w.codes, w.scales, w.k, rotated=0) for w in mats]
+        xr = [torch.empty_like(x) for x in xs]
+        two = []
+        for L in range(layers):
+            i = 3 * L
+            two.append((lambda a, b, s, bl: lambda: tgs.hadamard_rotate(a, s, block=bl, y=b))(xs[i], xr[i], sg[5120],
+                                                                                              block))
+            two.append((lambda a, b, c: lambda: tgs.ternary_gemv_batched(a, b, c))(plain[i:i + 2], [xr[i]] * 2,
+                                                                                  ys[i:i + 2]))
+            two.append((lambda a, b, s, bl: lambda: tgs.hadamard_rotate(a, s, block=bl, y=b))(xs[i + 2], xr[i + 2],
+                                                                                              sg[17408], block))
+            two.append((lambda a, b, c: lambda: tgs.ternary_gemv_batched(a, b, c))(plain[i + 2:i + 3], [xr[i + 2]],
+                                                                                  ys[i + 2:i + 3]))
+
+        def two_pass():
+            for fn in two:
+                fn()
+
+        ms2, _ = time_graph(torch, two_pass, args.steps, args.warmup)
+        log(f"[bench] rotated m={m}, two passes: step {ms2 * 1e3:.1f} us -> {nb / ms2 / 1e6:.0f} GB/s")
         res.append({"metric": "rotated ternary GEMV achieved GB/s, 27B-class set", "value": round(nb / ms / 1e6, 1),
                     "unit": "GB/s", "m": m, "ms_per_step": round(ms, 4), "launches_per_step": len(launches),
+                    "two_pass": {"gbs": round(nb / ms2 / 1e6, 1), "ms_per_step": round(ms2, 4),
+                                 "launches_per_step": len(two)},
                     "config": {"workload": f"27B-class rotated GEMV set, base-3, {layers} layers, M={m}, "
                                            f"rotation block {block}",
                                "bytes_per_step": int(nb)}})
-        del mats, xs, ys
+        del mats, xs, ys, plain, xr
         torch.cuda.empty_cache()
     return res
 

@@ -154,6 +154,10 @@ tgs_status unpack_ternary(const tgs_matrix* w, int8_t* trits_out, uint16_t* scal
  * Arithmetic: codes are decoded in registers; each 128-group is accumulated in fp32 and scaled
  * by its fp16 scale in fp32. Rotated activations are rounded once to fp16 after the transform,
  * so |R x| must stay below 65504. Results are deterministic run to run (no float atomics).
+ * Rotated weights: the rotation is fused, and every workgroup that reads a group of K rotates it
+ * again. A caller with a buffer for R x can instead rotate once with hadamard_rotate (fp16
+ * output, the same rounding) and multiply with a plain-basis descriptor (rotated = 0) of the same
+ * codes and scales; for several tokens that is the faster schedule.
  * Device limits (all device calls): n, k and the row stride below 2^24, and n * row stride at
  * most 2^31 - 2^20 bytes; larger matrices give TGS_E_SHAPE.
  */
