@@ -61,6 +61,9 @@ def parse():
                          "layer (36), or the whole set in as few launches as possible")
     ap.add_argument("--gemm-layout", default="slot2", choices=["slot2", "binary"],
                     help="code layout of the GEMM workload")
+    ap.add_argument("--gemm-rot-block", type=int, default=0, choices=[0, 128, 1024],
+                    help="GEMM workload with rotated weights: each product first rotates its fp16 activations "
+                         "into a bf16 buffer with this block (0: plain basis)")
     ap.add_argument("--rot-block", type=int, default=128, choices=[128, 1024],
                     help="rotation block of the rotated 27B-class set (128: one block per scale group)")
     ap.add_argument("--one-mode", action="store_true", help="time only --mode (the others are reported by default)")
@@ -359,17 +362,29 @@ def bench_rotated(args, torch, tgs, synth):
 
 def bench_gemm(args, torch, tgs, synth):
     """27B-class prefill GEMM (slot-2, or binary codes): gate/up 17408x5120 and down 5120x17408, M in
-    {16, 128, 2048}."""
+    {16, 128, 2048}. With --gemm-rot-block the weights are in the rotated basis: every product first
+    rotates its fp16 activations into a bf16 buffer (hadamard_rotate), then multiplies that buffer
+    with a plain-basis descriptor of the same codes; the line reports both launches together and
+    the rotation alone."""
     res = []
     copies = 16
+    rot = args.gemm_rot_block
     layout, p_zero = (3, 0.0) if args.gemm_layout == "binary" else (1, 0.4)
     for n, k in ((17408, 5120), (5120, 17408)):
         ws = [build_matrix(torch, tgs, synth, layout, 0, f"gemm/{n}x{k}/{i}", n, k, p_zero)[0] for i in range(copies)]
         for m in (16, 128, 2048):
-            xb = synth.x_bf16_bits(0, synth.stream_id("gemm/x", m, k), (m, k))
-            x = torch.from_numpy(xb.view(np.int16).copy()).cuda().view(torch.bfloat16)
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-            launches = [(lambda w: lambda: tgs.ternary_gemm(w, x, y))(w) for w in ws]
+            if rot:
+                x16 = synth.x_f16(0, synth.stream_id("gemm/x16", m, k), (m, k))
+                xh = torch.from_numpy(x16.view(np.int16).copy()).cuda().view(torch.float16)
+                sg = torch.from_numpy(synth.signs(0, synth.stream_id("gemm/signs", k), k)).cuda()
+                x = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+                rotate = lambda: tgs.hadamard_rotate(xh, sg, block=rot, y=x)
+                launches = [(lambda w: lambda: (rotate(), tgs.ternary_gemm(w, x, y)))(w) for w in ws]
+            else:
+                xb = synth.x_bf16_bits(0, synth.stream_id("gemm/x", m, k), (m, k))
+                x = torch.from_numpy(xb.view(np.int16).copy()).cuda().view(torch.bfloat16)
+                launches = [(lambda w: lambda: tgs.ternary_gemm(w, x, y))(w) for w in ws]
 
             def one_pass():
                 for fn in launches:
@@ -379,11 +394,21 @@ def bench_gemm(args, torch, tgs, synth):
             per = ms / copies
             flops = 2.0 * m * n * k
             nb = ws[0].nbytes + m * k * 2 + m * n * 4
-            res.append({"metric": "ternary GEMM TFLOP/s", "value": round(flops / per / 1e9, 2), "unit": "TFLOP/s",
-                        "pct_of_bf16_peak": round(100 * flops / per / 1e9 / BF16_MFMA_PEAK_TFLOPS, 2),
-                        "gbs": round(nb / per / 1e6, 1), "us": round(per * 1e3, 2),
-                        "config": {"workload": f"27B-class prefill GEMM {n}x{k}, M={m}, {LAYOUT_NAME[layout]}"}})
-            log(f"[bench] gemm {n}x{k} m={m}: {per * 1e3:.1f} us, {flops / per / 1e9:.1f} TFLOP/s")
+            line = {"metric": "ternary GEMM TFLOP/s", "value": round(flops / per / 1e9, 2), "unit": "TFLOP/s",
+                    "pct_of_bf16_peak": round(100 * flops / per / 1e9 / BF16_MFMA_PEAK_TFLOPS, 2),
+                    "gbs": round(nb / per / 1e6, 1), "us": round(per * 1e3, 2),
+                    "config": {"workload": f"27B-class prefill GEMM {n}x{k}, M={m}, {LAYOUT_NAME[layout]}"
+                                           + (f", rotated basis ({rot}-blocks, rotation + GEMM)" if rot else "")}}
+            if rot:
+                def rotations():
+                    for _ in range(copies):
+                        rotate()
+
+                rms, _ = time_graph(torch, rotations, max(2, args.steps // 4), 1)
+                line["rotate_us"] = round(rms / copies * 1e3, 2)
+            res.append(line)
+            log(f"[bench] gemm {n}x{k} m={m}{' rot ' + str(rot) if rot else ''}: {per * 1e3:.1f} us, "
+                f"{flops / per / 1e9:.1f} TFLOP/s" + (f" (rotation {line['rotate_us']} us)" if rot else ""))
         del ws
         torch.cuda.empty_cache()
     return res

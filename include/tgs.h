@@ -184,6 +184,9 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
  *   signs   must be NULL: this product is provided for plain-basis weights only, and rotated
  *           weights are refused with TGS_E_BASIS rather than multiplied in the wrong basis
  *   y       device [m][n] fp32, 4-byte aligned
+ * Rotated weights (prefill): rotate the activations once with hadamard_rotate or
+ * rmsnorm_hadamard_rotate into a bf16 buffer (y_dtype TGS_BF16) and multiply that buffer with a
+ * plain-basis descriptor (rotated = 0) of the same codes and scales.
  */
 tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m,
                         const int8_t* signs, float* y, void* stream);
@@ -194,9 +197,11 @@ tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int
  * Hadamard rotation" with n = 128 and H the natural-order Sylvester matrix, signs applied first.
  *   x        device [m][k], x_dtype TGS_F16, TGS_BF16 or TGS_F32; 16-byte aligned
  *   k        multiple of 128
- *   signs    device [k] int8 in {-1, +1}
- *   y        device [m][k], y_dtype TGS_F16 or TGS_F32; 16-byte aligned; must not overlap x
- * Computed in fp32 with a fast Walsh-Hadamard butterfly; fp16 output is rounded once.
+ *   signs    device [k] int8 in {-1, +1}, 16-byte aligned
+ *   y        device [m][k], y_dtype TGS_F16, TGS_BF16 or TGS_F32; 16-byte aligned; must not
+ *            overlap x
+ * Computed in fp32 with a fast Walsh-Hadamard butterfly; fp16 and bf16 output is rounded once
+ * from fp32, to nearest with ties to even.
  */
 tgs_status hadamard_rotate_g128(const void* x, int32_t x_dtype, int64_t m, int64_t k,
                                 const int8_t* signs, void* y, int32_t y_dtype, void* stream);
@@ -267,7 +272,7 @@ tgs_status ternary_gemv_rmsnorm_batched(const tgs_matrix* ws, int32_t count, con
  * rmsnorm_hadamard_rotate (device): y = R xhat with xhat the RMSNorm of each row of x as in
  * ternary_gemv_rmsnorm and R the block rotation of hadamard_rotate: the BlockHadamard variant
  * fused with RMSNorm of [P3] "Running in the browser with WebGPU".
- *   gamma   device [k] bf16 bit patterns, 2-byte aligned
+ *   gamma   device [k] bf16 bit patterns, 16-byte aligned
  *   eps     > 0 and finite
  *   k       a multiple of block below 2^24; m below 2^31
  *   other arguments and rules as hadamard_rotate. One workgroup per row.

@@ -237,7 +237,7 @@ def ternary_gemv_rmsnorm_batched(ws, xs, gammas, eps, ys, signs=None, stream=Non
 
 
 def rmsnorm_hadamard_rotate(x, gamma, eps, signs, block=128, y=None, out_dtype=None, stream=None):
-    """R RMSNorm(x) per row of x [m][k] (fp16/bf16/fp32), gamma bf16 [k]; fp16/fp32 output."""
+    """R RMSNorm(x) per row of x [m][k] (fp16/bf16/fp32), gamma bf16 [k]; fp16/bf16/fp32 output."""
     torch = _torch()
     dt = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
     k = x.shape[-1]
@@ -262,7 +262,8 @@ def ternary_gemm(w: PackedMatrix, x, y=None, stream=None):
 
 
 def hadamard_rotate(x, signs, block=128, y=None, out_dtype=None, stream=None):
-    """Block-wise signed Walsh-Hadamard rotation (128 or 1024 per block) of x [m][k]; fp16/fp32 output."""
+    """Block-wise signed Walsh-Hadamard rotation (128 or 1024 per block) of x [m][k]; fp16/bf16/fp32
+    output."""
     torch = _torch()
     dt = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
     k = x.shape[-1]
@@ -275,7 +276,7 @@ def hadamard_rotate(x, signs, block=128, y=None, out_dtype=None, stream=None):
 
 
 def hadamard_rotate_g128(x, signs, y=None, out_dtype=None, stream=None):
-    """Block-wise signed Walsh-Hadamard rotation (128 per block) of x [m][k]; fp16/fp32 output."""
+    """Block-wise signed Walsh-Hadamard rotation (128 per block) of x [m][k]; fp16/bf16/fp32 output."""
     torch = _torch()
     dt = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
     k = x.shape[-1]

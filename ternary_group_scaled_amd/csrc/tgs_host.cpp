@@ -468,11 +468,13 @@ tgs_status hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, int64_t k,
   if (!x || !signs || !y) return fail(TGS_E_NULL, "x, signs or y is NULL");
   if (x_dtype != TGS_F16 && x_dtype != TGS_BF16 && x_dtype != TGS_F32)
     return fail(TGS_E_DTYPE, "x_dtype must be TGS_F16, TGS_BF16 or TGS_F32");
-  if (y_dtype != TGS_F16 && y_dtype != TGS_F32) return fail(TGS_E_DTYPE, "y_dtype must be TGS_F16 or TGS_F32");
+  if (y_dtype != TGS_F16 && y_dtype != TGS_BF16 && y_dtype != TGS_F32)
+    return fail(TGS_E_DTYPE, "y_dtype must be TGS_F16, TGS_BF16 or TGS_F32");
   if (block != 128 && block != 1024) return fail(TGS_E_SHAPE, "block must be 128 or 1024, got %lld", (long long)block);
   if (m < 1 || k < block || k % block != 0 || m * (k / block) > (1LL << 40))
     return fail(TGS_E_SHAPE, "need m >= 1 and k a positive multiple of the block (%lld)", (long long)block);
   if (!aligned(x, 16) || !aligned(y, 16)) return fail(TGS_E_ALIGN, "x and y must be 16-byte aligned");
+  if (!aligned(signs, 16)) return fail(TGS_E_ALIGN, "signs must be 16-byte aligned");
   const size_t xe = x_dtype == TGS_F32 ? 4 : 2, ye = y_dtype == TGS_F32 ? 4 : 2;
   const char *xb = static_cast<const char*>(x), *yb = static_cast<const char*>(y);
   const size_t xn = (size_t)(m * k) * xe, yn = (size_t)(m * k) * ye;
@@ -488,13 +490,15 @@ tgs_status rmsnorm_hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, in
   if (!x || !gamma || !signs || !y) return fail(TGS_E_NULL, "x, gamma, signs or y is NULL");
   if (x_dtype != TGS_F16 && x_dtype != TGS_BF16 && x_dtype != TGS_F32)
     return fail(TGS_E_DTYPE, "x_dtype must be TGS_F16, TGS_BF16 or TGS_F32");
-  if (y_dtype != TGS_F16 && y_dtype != TGS_F32) return fail(TGS_E_DTYPE, "y_dtype must be TGS_F16 or TGS_F32");
+  if (y_dtype != TGS_F16 && y_dtype != TGS_BF16 && y_dtype != TGS_F32)
+    return fail(TGS_E_DTYPE, "y_dtype must be TGS_F16, TGS_BF16 or TGS_F32");
   if (block != 128 && block != 1024) return fail(TGS_E_SHAPE, "block must be 128 or 1024, got %lld", (long long)block);
   if (m < 1 || m >= (1LL << 31) || k < block || k % block != 0 || k >= (1LL << 24))
     return fail(TGS_E_SHAPE, "need 1 <= m < 2^31 and k a multiple of the block (%lld) below 2^24", (long long)block);
   if (!(eps > 0.f && eps < INFINITY)) return fail(TGS_E_SHAPE, "eps must be positive and finite");
   if (!aligned(x, 16) || !aligned(y, 16)) return fail(TGS_E_ALIGN, "x and y must be 16-byte aligned");
-  if (!aligned(gamma, 2)) return fail(TGS_E_ALIGN, "gamma must be 2-byte aligned");
+  if (!aligned(signs, 16)) return fail(TGS_E_ALIGN, "signs must be 16-byte aligned");
+  if (!aligned(gamma, 16)) return fail(TGS_E_ALIGN, "gamma must be 16-byte aligned");
   const size_t xe = x_dtype == TGS_F32 ? 4 : 2, ye = y_dtype == TGS_F32 ? 4 : 2;
   const char *xb = static_cast<const char*>(x), *yb = static_cast<const char*>(y);
   const size_t xn = (size_t)(m * k) * xe, yn = (size_t)(m * k) * ye;

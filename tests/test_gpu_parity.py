@@ -257,6 +257,90 @@ def test_hadamard_rotate_1024_matches_oracle(in_dtype, out_dtype):
                        y128b.view(torch.int16 if out_dtype == "f16" else torch.int32))
 
 
+@pytest.mark.parametrize("block,k", [(128, 128), (128, 384), (128, 640), (1024, 1024), (1024, 5120)])
+@pytest.mark.parametrize("m", [1, 5, 13])
+def test_hadamard_rotate_ragged_tiles(block, k, m):
+    """A wave rotates 512 consecutive elements (four 128-blocks) or one 1024-block of the
+    flattened rows: tiles that span rows, and a last tile with only some 128-blocks in it."""
+    sg = make_signs(m + k, "hadrag", k)
+    x16 = make_x_f16(m + k, f"hadrag{block}", m, k)
+    y = tgs.hadamard_rotate(_x_dev(x16), torch.from_numpy(sg).to(DEV), block=block)
+    gamma = synth.bf16_bits(1.0 + 0.3 * synth.normal(m + k, 13, (k,)))
+    yn = tgs.rmsnorm_hadamard_rotate(_x_dev(x16), _gamma_dev(gamma), 1e-6, torch.from_numpy(sg).to(DEV),
+                                     block=block)
+    torch.cuda.synchronize()
+    xref = x16.astype(np.float64)
+    ref = oracle.rotate(xref, sg, block)
+    blk_l1 = np.repeat(np.abs(xref).reshape(m, -1, block).sum(axis=2), block, axis=1) / np.sqrt(block)
+    assert (np.abs(y.cpu().numpy() - ref) <= 1e-6 * blk_l1 + 1e-30).all()
+    xhat = oracle.rmsnorm(xref, gamma, float(np.float32(1e-6)))
+    refn = oracle.rmsnorm_rotate(x16.view(np.uint16), oracle.X_F16, gamma, float(np.float32(1e-6)), sg, block)
+    blk_n = np.repeat(np.abs(xhat).reshape(m, -1, block).sum(axis=2), block, axis=1) / np.sqrt(block)
+    assert (np.abs(yn.cpu().numpy() - refn) <= 2e-6 * blk_n + 1e-30).all()
+
+
+def _bf16_rne(f32):
+    """fp32 values -> bf16 bits, round to nearest with ties to even (finite inputs)."""
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("block", [128, 1024])
+@pytest.mark.parametrize("norm", [False, True])
+def test_rotation_bf16_output_is_the_rounded_fp32_output(block, norm):
+    """bf16 output is the fp32 output rounded once to nearest-even, and within bf16's unit
+    roundoff (2^-8) of the oracle's rotation."""
+    m, k = 5, 3072
+    sg = torch.from_numpy(make_signs(8, "rotbf16", k)).to(DEV)
+    xd = synth.normal(8, 11, (m, k)) * np.array([[1e-3], [0.5], [3.0], [40.0], [900.0]])
+    host = xd.astype(np.float16)
+    xt = torch.from_numpy(host.copy()).to(DEV)
+    xref = host.astype(np.float64)
+    if norm:
+        gamma = synth.bf16_bits(1.0 + 0.3 * synth.normal(8, 12, (k,)))
+        rot = lambda od: tgs.rmsnorm_hadamard_rotate(xt, _gamma_dev(gamma), 1e-6, sg, block=block, out_dtype=od)
+        ref = oracle.rmsnorm_rotate(host.view(np.uint16), oracle.X_F16, gamma, float(np.float32(1e-6)),
+                                    make_signs(8, "rotbf16", k), block)
+        src = oracle.rmsnorm(xref, gamma, float(np.float32(1e-6)))
+    else:
+        rot = lambda od: tgs.hadamard_rotate(xt, sg, block=block, out_dtype=od)
+        ref = oracle.rotate(xref, make_signs(8, "rotbf16", k), block)
+        src = xref
+    y32, y16 = rot(torch.float32), rot(torch.bfloat16)
+    torch.cuda.synchronize()
+    got32 = y32.cpu().numpy()
+    got16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert (got16 == _bf16_rne(got32)).all()
+    got = (got16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    blk_l1 = np.repeat(np.abs(src).reshape(m, -1, block).sum(axis=2), block, axis=1) / np.sqrt(block)
+    assert (np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 2e-6 * blk_l1 + 1e-38).all()
+
+
+ROT_LAYOUTS = [tgs.SLOT2, tgs.BASE3, tgs.BINARY]
+
+
+@pytest.mark.parametrize("layout", ROT_LAYOUTS, ids=["slot2", "base3", "binary"])
+@pytest.mark.parametrize("block", [128, 1024])
+@pytest.mark.parametrize("m", [1, 24, 130])
+def test_rotated_prefill_two_pass_matches_oracle(layout, block, m):
+    """Prefill with rotated weights: rotate the activations once into bf16, then ternary_gemm
+    with a plain-basis descriptor of the same codes. The reference is the oracle's rotation,
+    rounded to bf16 (via fp32, as the kernel rounds), multiplied by the oracle."""
+    n, k = 200, 3072
+    if layout == tgs.BINARY:
+        t, s = _binary_weights(m, f"rotpre{block}", n, k)
+    else:
+        t, s = make_weights(m, f"rotpre{layout}{block}", n, k, 0.4)
+    sg = make_signs(m, f"rotpre{block}", k)
+    x16 = make_x_f16(m, f"rotpre{block}", m, k)
+    xr = tgs.hadamard_rotate(_x_dev(x16), torch.from_numpy(sg).to(DEV), block=block, out_dtype=torch.bfloat16)
+    y = tgs.ternary_gemm(_packed(layout, t, s), xr)
+    torch.cuda.synchronize()
+    xr_bits = synth.bf16_bits(oracle.rotate(x16.astype(np.float64), sg, block))
+    y_ref, bound = oracle_product(layout, t, s, xr_bits, oracle.X_BF16)
+    assert_within_bound(y.cpu().numpy(), y_ref, bound, f"rotated prefill {layout} block {block} m={m}")
+
+
 def test_misaligned_signs_are_refused():
     k = 2048
     t, s = make_weights(1, "sgal", 8, k, 0.4)

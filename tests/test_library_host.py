@@ -171,7 +171,7 @@ def test_device_call_argument_checks_happen_before_any_device_work():
     assert lib.ternary_gemm(ctypes.byref(m), 0x300000, tgs.BF16, 0, None, 0x400000, None) == 2
     # hadamard_rotate_g128
     assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 200, 0x500000, 0x400000, tgs.F32, None) == 2
-    assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, 0x500000, 0x400000, tgs.BF16, None) == 8
+    assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, 0x500000, 0x400000, 99, None) == 8  # no such dtype
     assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, None, 0x400000, tgs.F32, None) == 1
     assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, 0x500000, 0x300100, tgs.F32, None) == 2  # overlap
     # hadamard_rotate: the block is 128 or 1024 and divides k
@@ -181,6 +181,8 @@ def test_device_call_argument_checks_happen_before_any_device_work():
     assert rot(1536, 1024) == 2
     assert rot(512, 1024) == 2
     assert rot(2048, 1024, signs=None) == 1
+    assert rot(2048, 1024, signs=0x500008) == 3                   # signs 16-byte aligned
+    assert rot(2048, 128, signs=0x500001) == 3
     # rotated GEMV: signs 16-byte aligned; 1024-element blocks need k % 1024 == 0
     assert _gemv(_fake_matrix(rotated=1), signs=0x500004) == 3
     assert _gemv(_fake_matrix(rotated=1024, k=2048), signs=0x500008) == 3
@@ -205,8 +207,10 @@ def test_device_call_argument_checks_happen_before_any_device_work():
     assert lib.ternary_gemv_rmsnorm_batched((tgs.Matrix * 1)(_fake_matrix()), 1, (ctypes.c_void_p * 1)(0x300000),
                                             tgs.F16, 1, None, 1e-6, None, (ctypes.c_void_p * 1)(0x400000), None) == 1
     # the fused standalone norm + rotation
-    nrot = lambda k=2048, block=1024, gamma=0x600000, eps=1e-6, y=0x400000: lib.rmsnorm_hadamard_rotate(
-        0x300000, tgs.F16, 2, k, block, gamma, eps, 0x500000, y, tgs.F32, None)
+    nrot = lambda k=2048, block=1024, gamma=0x600000, eps=1e-6, y=0x400000, signs=0x500000: \
+        lib.rmsnorm_hadamard_rotate(0x300000, tgs.F16, 2, k, block, gamma, eps, signs, y, tgs.F32, None)
+    assert nrot(gamma=0x600002) == 3                              # gamma 16-byte aligned
+    assert nrot(signs=0x500004) == 3                              # signs 16-byte aligned
     assert nrot(block=512) == 2
     assert nrot(k=1536) == 2
     assert nrot(gamma=None) == 1
