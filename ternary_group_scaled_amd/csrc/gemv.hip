@@ -721,7 +721,7 @@ void gemv_wave_kernel(const GemvArgs args) {
       __syncthreads();
       float total = 0.f;
       for (int q = 0; q < slices * W; ++q) total += norm_part[q];
-      const float r = 1.0f / sqrtf(total / (float)k + args.eps);
+      const float r = rms_scale(total, k, args.eps);
 #pragma unroll
       for (int i = 0; i < 4 * (8 / W); ++i) xw[i] = norm_word(xw[i], gw[i], r);
     }
@@ -752,7 +752,7 @@ void gemv_wave_kernel(const GemvArgs args) {
     __syncthreads();
     float total = 0.f;
     for (int q = 0; q < slices; ++q) total += norm_part[q];
-    const float r = 1.0f / sqrtf(total / (float)k + args.eps);
+    const float r = rms_scale(total, k, args.eps);
 #pragma unroll
     for (int i = 0; i < 32; ++i) xw[i] = norm_word(xw[i], gw[i], r);
   }

@@ -77,11 +77,20 @@ __device__ __forceinline__ void rms_partials(const uint16_t* x, int k, int m, in
   }
 }
 
+// 1 / sqrt(sum / k + eps) with the hardware reciprocal and reciprocal square root (each within
+// about one ulp in fp32); sub-normal arguments, which those may flush, take the exact route.
+// The value is the same for every lane that calls it with the same sum.
+__device__ __forceinline__ float rms_scale(float sum, int k, float eps) {
+  const float v = sum * __builtin_amdgcn_rcpf((float)k) + eps;
+  if (v < 1.17549435e-38f) return 1.0f / sqrtf(v);
+  return __builtin_amdgcn_rsqf(v);
+}
+
 // 1 / sqrt(sum_k x^2 / k + eps) of row t from the partial sums (after a barrier)
 __device__ __forceinline__ float rms_inverse(const float* part, int t, int waves, int k, float eps) {
   float s = 0.f;
   for (int w = 0; w < waves; ++w) s += part[t * waves + w];
-  return 1.0f / sqrtf(s / (float)k + eps);
+  return rms_scale(s, k, eps);
 }
 
 }  // namespace tgs
