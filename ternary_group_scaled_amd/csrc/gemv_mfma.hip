@@ -82,6 +82,12 @@ __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both 
   return d;
 }
 
+// pipeline depth of the group loop (plain and 128-block bases): stages of loads per wave. Two
+// measured best: on the 8B base-3 set with one token, 3, 4 and 6 stages ran at 838, 815 and
+// 748 GB/s in layer order against 860 (1362, 1289, 1127 against 1429 as a set), and 3 stages with
+// 8 tokens at 505 against 602 GB/s on the 27B rotated set.
+constexpr int kStagesOneToken = 2, kStagesTokens = 2;
+
 template <int MT, int kFB, int ROT, bool NORM, bool PRE>
 __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
   static_assert(ROT == 0 || ROT == 128 || ROT == 1024, "rotation block is 0 (none), 128 or 1024");
@@ -523,15 +529,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       step(st1, b + 1);
     }
   } else {
-    // two groups of loads in flight; loads past the wave's last group are parked out of range
-    Stage st0, st1;
-    load(st0, g_begin);
-    for (int g = g_begin; g < g_end; g += 2) {
-      load(st1, g + 1);
-      compute(st0, g, 0);
-      if (g + 1 >= g_end) break;
-      load(st0, g + 2);
-      compute(st1, g + 1, 0);
+    // kS - 1 groups of loads in flight ahead of the one being multiplied (a ring of kS stages);
+    // loads past the wave's last group are parked out of range
+    constexpr int kS = MT == 1 ? kStagesOneToken : kStagesTokens;
+    Stage st[kS];
+#pragma unroll
+    for (int i = 0; i < kS - 1; ++i) load(st[i], g_begin + i);
+    for (int g = g_begin; g < g_end; g += kS) {
+#pragma unroll
+      for (int u = 0; u < kS; ++u) {
+        if (g + u >= g_end) break;
+        load(st[(u + kS - 1) % kS], g + u + kS - 1);
+        compute(st[u], g + u, 0);
+      }
     }
   }
 
