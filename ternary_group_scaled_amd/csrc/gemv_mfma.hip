@@ -115,9 +115,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   const int g_begin = wave * groups / kWaves, g_end = (wave + 1) * groups / kWaves;
   const int blocks = k / 1024;  // used with 1024-element rotation blocks only (k % 1024 == 0)
 
-  // activations: kL lanes per token, each with kE consecutive elements of the group
+  // activations: kL lanes per token, each with kE consecutive elements of the group. With eight
+  // tokens a token's lanes are those with equal lane bits 2, 4 and 5 (p from bits 0, 1 and 3), so
+  // the rotation's three cross-lane butterfly stages pair lanes 1, 2 and 8 apart: each a single
+  // DPP move (lanes 4 apart would take two masked moves and a copy)
   constexpr int kL = 64 / MT, kE = 2 * MT;
-  const int tok = lane / kL, p = lane % kL;
+  const int tok = MT == 8 ? ((lane >> 2) & 1) | ((lane >> 3) & 6) : lane / kL;
+  const int p = MT == 8 ? (lane & 3) | ((lane >> 1) & 4) : lane % kL;
 
   // rows < MT of this wave's A tile, rewritten for every group
   _Float16* tile = reinterpret_cast<_Float16*>(smem) + wave * MT * kRowPitch;
@@ -412,10 +416,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
               v[i + h] = a - b;
             }
         auto cross = [&](auto s_tag) {
-          constexpr int S = decltype(s_tag)::value;
+          constexpr int S = decltype(s_tag)::value;       // stride in p
+          constexpr int LS = (MT == 8 && S == 4) ? 8 : S;  // the same stride in lanes
           const float sgn = (p & S) ? -1.f : 1.f;  // the upper lane of a pair keeps partner - own
 #pragma unroll
-          for (int i = 0; i < kE; ++i) v[i] = fmaf(v[i], sgn, xor_lane<S>(v[i], lane));
+          for (int i = 0; i < kE; ++i) v[i] = fmaf(v[i], sgn, xor_lane<LS>(v[i], lane));
         };
         if constexpr (kL > 1) cross(std::integral_constant<int, 1>{});
         if constexpr (kL > 2) cross(std::integral_constant<int, 2>{});
