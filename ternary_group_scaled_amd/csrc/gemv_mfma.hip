@@ -82,6 +82,18 @@ __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both 
   return d;
 }
 
+// Element of the group that entry e = kE p + i of a lane's slot list holds after the rotation:
+// e itself, except for one token in 128-element blocks. There the two lane-half butterfly stages
+// pair the lane's own two elements (a swap of one register's half with the other's, then a sum
+// and a difference), which leaves element bit 0 on lane bit 4, bits 1..4 on lane bits 0..3,
+// bit 5 on lane bit 5 and bit 6 on the register.
+template <int MT, int ROT>
+__host__ __device__ constexpr int rotated_element(int e) {
+  if (MT != 1 || ROT != 128) return e;
+  const int p = e >> 1, reg = e & 1;
+  return ((p >> 4) & 1) | ((p & 15) << 1) | (((p >> 5) & 1) << 5) | (reg << 6);
+}
+
 // pipeline depth of the group loop (plain and 128-block bases): stages of loads per wave. Two
 // measured best: on the 8B base-3 set with one token, 3, 4 and 6 stages ran at 838, 815 and
 // 748 GB/s in layer order against 860 (1362, 1289, 1127 against 1429 as a set), and 3 stages with
@@ -128,7 +140,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   for (int i = threadIdx.x; i < 5 * 160; i += kWaves * 64) {
     const int o = i / 160, e = i - 160 * o;
     if (e < 128)
-      slot_tab[o][e] = (uint16_t)(2 * tile_slot(o + e));
+      slot_tab[o][e] = (uint16_t)(2 * tile_slot(o + rotated_element<MT, ROT>(e)));
     else  // rel in [0, o) and [o + 128, 160)
       zero_tab[o][e - 128] = (uint16_t)(2 * tile_slot(e - 128 < o ? e - 128 : e));
   }
@@ -426,8 +438,23 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
         if constexpr (kL > 2) cross(std::integral_constant<int, 2>{});
         if constexpr (kL > 4) cross(std::integral_constant<int, 4>{});
         if constexpr (kL > 8) cross(std::integral_constant<int, 8>{});
-        if constexpr (kL > 16) cross(std::integral_constant<int, 16>{});
-        if constexpr (kL > 32) cross(std::integral_constant<int, 32>{});
+        if constexpr (MT == 1) {
+          // lane strides 16 and 32 (element bits 5 and 6): after each swap a lane holds both
+          // partners of one of its elements, so a sum and a difference finish the stage (the slot
+          // table follows the new places, rotated_element)
+          swap_rows16(v[0], v[1]);
+          float a = v[0], b = v[1];
+          v[0] = a + b;
+          v[1] = a - b;
+          swap_halves32(v[0], v[1]);
+          a = v[0];
+          b = v[1];
+          v[0] = a + b;
+          v[1] = a - b;
+        } else {
+          if constexpr (kL > 16) cross(std::integral_constant<int, 16>{});
+          if constexpr (kL > 32) cross(std::integral_constant<int, 32>{});
+        }
 #pragma unroll
         for (int i = 0; i < kE; ++i) v[i] *= 0.08838834764831845f;  // 1/sqrt(128)
       }
