@@ -30,8 +30,8 @@
 //     waves then walk contiguous group slices as in the plain basis. Otherwise wave w < MT rotates
 //     token w's block b + 1 into one half of a double-buffered LDS array while every wave
 //     multiplies its group 8 b + w of block b from the other half, with one barrier per block.
-//   - Only the MT live rows of each A tile are kept in LDS; lanes of the padding rows MT..15 hold
-//     zero fragments in registers.
+//   - Only the MT live rows of each A tile are kept in LDS; lanes of the padding rows MT..15 read
+//     their fragments from one shared zero row, so every lane issues the same unconditional read.
 //   - RMSNorm prologue (NORM): the workgroup first computes 1 / rms of each token over all of K
 //     (rms_norm.h; its loads are issued before the first weights are needed), and every
 //     activation is multiplied by gamma[k] and that factor in fp32 before the sign flip, the
@@ -111,6 +111,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   // K order, then the 32 window positions outside the group
   __shared__ __attribute__((aligned(16))) uint16_t slot_tab[5][128];
   __shared__ __attribute__((aligned(16))) uint16_t zero_tab[5][32];
+  // the A operand's padding rows MT..15: every lane reads a fragment, those lanes from this zero
+  // row (one address per k quarter, so the reads broadcast)
+  __shared__ __attribute__((aligned(16))) _Float16 zero_row[160];
   // rotated 1024-blocks of the MT tokens, double-buffered: [buffer][token][1024]
   __shared__ __attribute__((aligned(16))) _Float16 blk[ROT == 1024 && !PRE ? 2 * MT * 1024 : 8];
   // PRE: the MT rows rotated, [MT][k] (dynamic LDS, MT * k * 2 bytes)
@@ -137,6 +140,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
 
   // rows < MT of this wave's A tile, rewritten for every group
   _Float16* tile = reinterpret_cast<_Float16*>(smem) + wave * MT * kRowPitch;
+  const _Float16* a_row = fr < MT ? tile + fr * kRowPitch : zero_row;
+  for (int i = threadIdx.x; i < 160; i += kWaves * 64) zero_row[i] = (_Float16)0.f;
   for (int i = threadIdx.x; i < 5 * 160; i += kWaves * 64) {
     const int o = i / 160, e = i - 160 * o;
     if (e < 128)
@@ -489,8 +494,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     for (int fb = 0; fb < kFB; ++fb) part[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
-      half8 a = {};  // the padding rows MT..15 of the A operand are zero
-      if (fr < MT) a = *reinterpret_cast<const half8*>(tile + fr * kRowPitch + (kq * 5 + j) * 8);
+      const half8 a = *reinterpret_cast<const half8*>(a_row + (kq * 5 + j) * 8);
 #pragma unroll
       for (int fb = 0; fb < kFB; ++fb) {
         const u16x2 de0 = j < 4 ? peel(ve0[fb]) : ve0[fb];
