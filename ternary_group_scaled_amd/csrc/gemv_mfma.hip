@@ -124,7 +124,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   const int n = job.n, k = job.k, m = args.m;
   const int groups = k / 128;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is the same in every lane; read it as such so that each wave's group range,
+  // loop counters and load offsets stay in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int fr = lane & 15, kq = lane >> 4;
   const int n_base = ((int)blockIdx.x - job.block0) * 16 * kFB;
   const int g_begin = wave * groups / kWaves, g_end = (wave + 1) * groups / kWaves;
