@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
   // of loads in flight per wave
   __shared__ float red[kWaves][TB * kFB * 4][64];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int fr = lane & 15, kq = lane >> 4;  // fragment row and k quarter
   const int n_base = blockIdx.x * 16 * kFB, m_base = blockIdx.y * 16 * TB;
   const int groups = k / 128;

@@ -224,7 +224,7 @@ template <int MT, int WAVES, int BLOCK>
 __device__ __forceinline__ void stage_rotated(uint16_t* lds, int len, const uint16_t* x, const int8_t* sign,
                                               int k, int m, int m0, int k_begin, const uint16_t* gamma,
                                               const float* norm_part, float eps) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   auto token_rinv = [&](int t) { return rms_inverse(norm_part, t, WAVES, k, eps); };
   if constexpr (BLOCK == 1024) {
     // 1024-element blocks (k and the slice are multiples of 1024): lane l holds elements
@@ -640,7 +640,7 @@ void gemv_wave_kernel(const GemvArgs args) {
   const int rows_wave = R * kRowsPerInstr;
   const int rows_wg = W * rows_wave;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int ks = wave % slices, rw = wave / slices;  // K slice and row wave
   const int cl = lane % S, rslot = lane / S;
   const int c = ks * S + cl;  // this lane's chunk
