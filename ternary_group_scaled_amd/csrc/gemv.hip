@@ -361,7 +361,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
   const int chunks = k / kChunkElems;
   const int slices = (chunks + S - 1) / S;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int cl = lane % S;     // chunk lane within a row
   const int rslot = lane / S;  // row slot within an instruction
   const int row0 = ((int)blockIdx.x - job.block0) * kRowsPerBlock + wave * kRowsPerWave + rslot;

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void hadamard_kernel(const void* __restri
   constexpr int E = kElems<BLOCK>, H = E / 8, TILE = 512 * H;
   constexpr float kNorm = BLOCK == 128 ? 0.08838834764831845f : 0.03125f;  // 1 / sqrt(BLOCK)
   const int lane = threadIdx.x & 63;
-  const int64_t wave0 = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t wave0 = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t stride = (int64_t)gridDim.x * kWaves * TILE;
   for (int64_t t0 = wave0 * TILE; t0 < total; t0 += stride) {
     float v[E];
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_hadamard_kernel(const void* 
   constexpr int E = kElems<BLOCK>, H = E / 8, TILE = 512 * H;
   constexpr float kNorm = BLOCK == 128 ? 0.08838834764831845f : 0.03125f;
   __shared__ float part[kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row0 = (int64_t)blockIdx.x * k;
   float acc = 0.f;
   for (int64_t c = 8 * (int64_t)threadIdx.x; c < k; c += 8 * kThreads) {
