@@ -4,9 +4,8 @@
 // rotated basis, xr = R x, R = blockdiag((1/sqrt(n)) H_n S) with n = 128 or 1024 ("Ternary Bonsai 2
 // 27B, 5.93GB ... (feat. PrismML)" (discuss.pytorch.kr), subsections "Group-scaled ternary format"
 // and "Block-wise Hadamard rotation"). A dot2 decode would repeat the whole base-3 digit extraction
-// for every token; here the codes are decoded once into fp16 weights t in {-1, 0, +1} and
-// v_mfma_f32_16x16x32_f16 multiplies them by all tokens at once (tokens are the 16 rows of the A
-// operand, padded with zeros). Even for one token this measured faster than the dot2 decode: the
+// for every token; here the codes are decoded once and v_mfma_f32_16x16x32_f16 multiplies them by
+// all tokens at once (tokens are the 16 rows of the A operand, padded with zeros). Even for one token this measured faster than the dot2 decode: the
 // matrix cores take the multiply-adds and the decode is a few packed integer ops per digit.
 //
 // Work split. A workgroup of 8 waves owns 16 * FB output rows and splits the scale
@@ -16,8 +15,14 @@
 //     reads bytes B0 + 8q .. B0 + 8q + 7 of row r (three aligned dwords and a funnel shift) and
 //     peels their digits with packed 16-bit integer ops (q = v * 171 >> 9 equals v / 3 for
 //     v < 256; digit = v - 3q), five per byte, as the dot2 kernels do. MFMA step j (0..4) takes
-//     digit j of all eight bytes, paired (byte 0, byte 2), (1, 3), (4, 6), (5, 7); one v_perm table
-//     lookup turns a digit pair into two fp16 weights (t = digit - 1, exact).
+//     digit j of all eight bytes, paired (byte 0, byte 2), (1, 3), (4, 6), (5, 7). Shifted left by
+//     8 bits, a digit d in a 16-bit half is the bit pattern of the fp16 sub-normal d * 2^-16, so
+//     one shift per register makes the weight operand. With t = d - 1, sum x t = sum x d - sum x:
+//     a second chain of five MFMAs multiplies the same activations by the constant 2^-16 (the
+//     encoding of d = 1), its result is subtracted, and the outputs are scaled by 2^16 (exact)
+//     when they are stored. A row of zero weights runs the identical chain twice, so it gives
+//     exactly 0. (Digits used directly, as 2^-24 * d, lost precision on the matrix cores: a zero
+//     row came out at about 2^-16 of the activations' sum, not 0.)
 //   - Activations. The wave writes the group's activations (rotated when the weights are: sign
 //     flip, the natural-order Sylvester butterfly over the 128-block, 1/sqrt(128), one rounding to
 //     fp16) into a private LDS tile laid out [q][j][8] in exactly the order of the weight operand,
@@ -68,12 +73,8 @@ __device__ __forceinline__ int tile_slot(int rel) {
   return (q * 5 + j) * 8 + pos;
 }
 
-// two fp16 weights 2 digits -> (t_lo, t_hi): the digit picks byte d of the table {0xBC, 0, 0x3C, 0}
-// as the high byte of each half (fp16 -1, 0, +1; the fourth entry only ever meets a zero activation)
-__device__ __forceinline__ uint32_t weights_of_digits(u16x2 d) {
-  constexpr uint32_t kTable = 0x003C00BCu;
-  return __builtin_amdgcn_perm(0u, kTable, (__builtin_bit_cast(uint32_t, d) << 8) | 0x000C000Cu);
-}
+// 2^-16 in both fp16 halves of a word: the encoding of digit 1 (t = 0), which sums the activations
+constexpr uint32_t kUnitPair = 0x01000100u;
 
 __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both halves
   const u16x2 q = (v * (u16x2)171) >> (u16x2)9;
@@ -491,20 +492,24 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       ve1[fb] = __builtin_bit_cast(u16x2, w1 & 0x00FF00FFu);
       vo1[fb] = __builtin_bit_cast(u16x2, (w1 >> 8) & 0x00FF00FFu);
     }
+    // part: 2^-16 * sum x d per row block; ones: 2^-16 * sum x (the same for every output row)
     f32x4 part[kFB];
 #pragma unroll
     for (int fb = 0; fb < kFB; ++fb) part[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 ones = f32x4{0.f, 0.f, 0.f, 0.f};
+    const half8 unit = __builtin_bit_cast(half8, make_uint4(kUnitPair, kUnitPair, kUnitPair, kUnitPair));
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       const half8 a = *reinterpret_cast<const half8*>(a_row + (kq * 5 + j) * 8);
+      ones = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, unit, ones, 0, 0, 0);
 #pragma unroll
       for (int fb = 0; fb < kFB; ++fb) {
         const u16x2 de0 = j < 4 ? peel(ve0[fb]) : ve0[fb];
         const u16x2 do0 = j < 4 ? peel(vo0[fb]) : vo0[fb];
         const u16x2 de1 = j < 4 ? peel(ve1[fb]) : ve1[fb];
         const u16x2 do1 = j < 4 ? peel(vo1[fb]) : vo1[fb];
-        const uint4 b4 = make_uint4(weights_of_digits(de0), weights_of_digits(do0), weights_of_digits(de1),
-                                    weights_of_digits(do1));
+        const uint4 b4 = make_uint4(__builtin_bit_cast(uint32_t, de0) << 8, __builtin_bit_cast(uint32_t, do0) << 8,
+                                    __builtin_bit_cast(uint32_t, de1) << 8, __builtin_bit_cast(uint32_t, do1) << 8);
         part[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, b4), part[fb], 0, 0, 0);
       }
     }
@@ -514,7 +519,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     for (int fb = 0; fb < kFB; ++fb) {
       const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)st.s[fb]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[fb][r] = fmaf(sc, part[fb][r], acc[fb][r]);
+      for (int r = 0; r < 4; ++r) acc[fb][r] = fmaf(sc, part[fb][r] - ones[r], acc[fb][r]);
     }
   };
 
@@ -599,7 +604,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) sum += red[(w * kFB * 4 + idx) * 64 + ln];
     const int token = 4 * (ln >> 4) + r, row = n_base + 16 * fb + (ln & 15);
-    if (token < m && row < n) job.y[(int64_t)token * n + row] = sum;
+    if (token < m && row < n) job.y[(int64_t)token * n + row] = sum * 65536.0f;  // 2^16: the weights' scale
   }
 }
 
