@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     } else {
       st.x[0] = __builtin_amdgcn_raw_buffer_load_b32(x_rsrc, xo, 0, 0);
     }
-    if constexpr (NORM) {
+    if constexpr (NORM && ROT != 1024) {  // (1024-blocks load their norm weights with the block)
       const int go = live ? (128 * g + kE * p) * 2 : kOobOffset;
       if constexpr (MT == 8) {
         const auto a = __builtin_amdgcn_raw_buffer_load_b128(gamma_rsrc, go, 0, 0);
