@@ -152,14 +152,20 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     else  // rel in [0, o) and [o + 128, 160)
       zero_tab[o][e - 128] = (uint16_t)(2 * tile_slot(e - 128 < o ? e - 128 : e));
   }
-  if constexpr (NORM) rms_partials<MT>(job.x, k, m, 0, norm_part, kWaves * 64);
-  __syncthreads();
-  // RMSNorm factors: of this lane's token (group staging) and of token `wave` (block staging)
+  if constexpr (!NORM) __syncthreads();  // the tables (with the norm: at the barrier of norm_factors)
+  // RMSNorm factors: of this lane's token (group staging) and of token `wave` (block staging).
+  // Every thread calls norm_factors once, before its first multiply; its barrier also publishes
+  // the tables. The plain-basis loop calls it after its first loads are issued, so the rows'
+  // extra read overlaps the first weights.
   float rinv_tok = 1.f, rinv_wave = 1.f;
-  if constexpr (NORM) {
-    rinv_tok = rms_inverse(norm_part, tok, kWaves, k, args.eps);
-    rinv_wave = rms_inverse(norm_part, wave < MT ? wave : 0, kWaves, k, args.eps);
-  }
+  auto norm_factors = [&]() {
+    if constexpr (NORM) {
+      rms_partials<MT>(job.x, k, m, 0, norm_part, kWaves * 64);
+      __syncthreads();
+      rinv_tok = rms_inverse(norm_part, tok, kWaves, k, args.eps);
+      rinv_wave = rms_inverse(norm_part, wave < MT ? wave : 0, kWaves, k, args.eps);
+    }
+  };
 
   // reads past each buffer return zero: rows >= n, tokens >= m (their outputs are not stored)
   const __amdgpu_buffer_rsrc_t code_rsrc =
@@ -526,6 +532,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   if constexpr (PRE) {
     // every block of every token rotated once (round robin over the waves), then contiguous group
     // slices per wave, as in the plain basis
+    norm_factors();
     for (int idx = wave; idx < MT * blocks; idx += kWaves) {
       const int t = idx / blocks, bb = idx - t * blocks;
       Stage st;
@@ -552,6 +559,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       compute(st, 8 * b + wave, b & 1);
       __syncthreads();
     };
+    norm_factors();
     {
       Stage st;
       load_block(st, 0, wave);
@@ -578,6 +586,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     Stage st[kS];
 #pragma unroll
     for (int i = 0; i < kS - 1; ++i) load(st[i], g_begin + i);
+    norm_factors();
     for (int g = g_begin; g < g_end; g += kS) {
 #pragma unroll
       for (int u = 0; u < kS; ++u) {
