@@ -333,18 +333,38 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     cross(std::integral_constant<int, 2>{});
     cross(std::integral_constant<int, 4>{});
     cross(std::integral_constant<int, 8>{});
-    cross(std::integral_constant<int, 16>{});
-    cross(std::integral_constant<int, 32>{});
-    uint32_t w[8];
+    // lane strides 16 and 32 (element bits 8 and 9): registers i and i + 8, then i and i + 4, are
+    // paired by a lane-half swap, after which a lane holds both partners of one of them and a sum
+    // and a difference finish the stage. Element bits 8 and 9 end on register bits 3 and 2, and
+    // register bits 3 and 2 (element bits 3 and 2) on lane bits 4 and 5.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(v[2 * i] * 0.03125f));
-      const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(v[2 * i + 1] * 0.03125f));
-      w[i] = lo | (hi << 16);
+      swap_rows16(v[i], v[i + 8]);
+      const float a = v[i], b = v[i + 8];
+      v[i] = a + b;
+      v[i + 8] = a - b;
     }
-    uint4* dst = reinterpret_cast<uint4*>(dst_block + 16 * lane);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+      if ((i & 4) == 0) {
+        swap_halves32(v[i], v[i + 4]);
+        const float a = v[i], b = v[i + 4];
+        v[i] = a + b;
+        v[i + 4] = a - b;
+      }
+    // registers 4q .. 4q + 3 hold four consecutive elements: q's bits are element bits 9 and 8
+    const int e0 = (((lane >> 5) & 1) << 2) | (((lane >> 4) & 1) << 3) | ((lane & 15) << 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(v[4 * q + 2 * h] * 0.03125f));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(v[4 * q + 2 * h + 1] * 0.03125f));
+        w[h] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint2*>(dst_block + e0 + 512 * (q & 1) + 256 * (q >> 1)) = make_uint2(w[0], w[1]);
+    }
   };
 
   f32x4 acc[kFB];
