@@ -353,8 +353,18 @@ int orc_matmul_norm_f64(int32_t layout, const uint8_t* codes, int64_t row_stride
 #pragma omp for schedule(dynamic, 16)
     for (int64_t j = 0; j < n_sel; ++j) {
       int64_t r = rows ? rows[j] : j;
-      if (r < 0 || r >= n) { status = ORC_BAD_SHAPE; continue; }
-      if (unpack_row(layout, codes + r * row_stride, k, t) != ORC_OK) { status = ORC_BAD_CODE; continue; }
+      /* several threads may report a failure: each store is atomic, and any one failing status is
+         the result */
+      if (r < 0 || r >= n) {
+#pragma omp atomic write
+        status = ORC_BAD_SHAPE;
+        continue;
+      }
+      if (unpack_row(layout, codes + r * row_stride, k, t) != ORC_OK) {
+#pragma omp atomic write
+        status = ORC_BAD_CODE;
+        continue;
+      }
       for (int64_t c = 0; c < k; ++c) w[c] = orc_f16_to_f64(scales[r * (k / 128) + c / 128]) * (double)t[c];
       for (int64_t i = 0; i < m; ++i) {
         double acc = 0.0, mag = 0.0;
@@ -413,6 +423,7 @@ int64_t orc_code_flips(int32_t layout, const uint8_t* a, int64_t row_stride_a, c
     for (int64_t r = 0; r < n; ++r) {
       if (unpack_row(layout, a + r * row_stride_a, k, ta) != ORC_OK ||
           unpack_row(layout, b + r * row_stride_b, k, tb) != ORC_OK) {
+#pragma omp atomic write
         status = ORC_BAD_CODE;
         continue;
       }

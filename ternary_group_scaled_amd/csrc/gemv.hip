@@ -16,20 +16,19 @@
 // zero), issued before the activation slice is staged and pipelined in a ring of register sets.
 //
 // Decode without unpacking (slot-2). Codes q = t + 1 sit in 2-bit slots; a 32-bit word holds 16
-// of them, element j in bits 2j..2j+1. Masking the word (or the word shifted by 4 or 6 bits)
-// with 0x00300030, 0x00C000C0 or 0x03000300 keeps the codes of elements j and j+8 in mantissa
-// bits 4..9 of the two fp16 halves: with a zero exponent field those halves are the fp16
-// subnormals q * 2^(p-24), p in {4, 6, 8}, exactly. v_dot2_f32_f16 multiplies them by the
-// activation pair (x_j, x_{j+8}) and adds into an fp32 accumulator, one accumulator per bit
-// position p. Three shifted copies cover all 16 codes: two shifts, eight ANDs and eight dot2 per
-// 16 weights. (Positions below bit 4 are avoided: measured on gfx950, dot2 with an fp16
-// subnormal operand whose value is q * 2^-24 loses about 7 bits, while at bit 4 and above the
-// error stays below 4e-7 of the sum.) The accumulators are combined with exact power-of-two
-// factors into 2^-20 * sum_k q x.
+// of them, element j in bits 2j..2j+1. dot2 pairs elements (j, j+8): masking the word (or the
+// word shifted right by 6 bits) with 3 << p in both 16-bit halves, p in {0, 2, 4, 6, 8}, keeps the
+// codes of elements j and j+8 in mantissa bits p..p+1 of the two halves, and OR-ing in the bits of
+// 1.0 makes each half the fp16 number 1 + q * 2^(p-10), exactly. One packed fp16 add of
+// -(1 + 2^(p-10)) then leaves (q - 1) * 2^(p-10) = t * 2^(p-10) in each half, again exactly (both
+// operands and the difference are representable). v_dot2_f32_f16 multiplies the pair by the
+// activation pair (x_j, x_{j+8}) and adds into an fp32 accumulator, one accumulator per position p.
+// Per 16 weights: one shift, eight AND-ORs, eight packed adds and eight dot2. The accumulators are
+// combined with exact power-of-two factors into 2^-20 * sum_k t x.
 //
-// Since t = q - 1, sum_k t x = sum_k q x - sum_k x. The second sum is produced by running the
-// identical decode-and-dot sequence on the code word of an all-zero row (every slot q = 1): a
-// row whose codes are all zero then cancels bit for bit and gives exactly 0.
+// Every product is t * x itself (times a power of two): a zero code contributes exactly nothing,
+// so the partial sums, and with them the rounding, are those of the nonzero terms only; a row with
+// one nonzero code gives s * t * x_k exactly.
 //
 // Binary codes (t in {-1, +1}, one bit b = (t + 1) / 2 per weight; the two-level sibling format of
 // "Bonsai 27B and how 1-bit survives" (velog.io), section "What ternary and binary are") use the
@@ -42,9 +41,9 @@
 // position. Then sum_k t x = 2 sum_k b x - sum_k x, the second sum again from the identical
 // sequence on an all-ones word.
 //
-// Shared per-slice work. The activation pairs of a chunk and its all-zero-row product depend on
-// the chunk only, not on the wave, so one thread per chunk builds them once per workgroup and
-// stores them in LDS, laid out [16-byte granule][chunk] so that the waves' reads are
+// Shared per-slice work. The activation pairs of a chunk (and, for binary codes, its all-ones-row
+// product) depend on the chunk only, not on the wave, so one thread per chunk builds them once per
+// workgroup and stores them in LDS, laid out [16-byte granule][chunk] so that the waves' reads are
 // conflict-free 16-byte accesses by consecutive lanes.
 //
 // Scales are applied in fp32 per chunk; partial sums are reduced across the S lanes of a row in
@@ -110,25 +109,47 @@ __device__ __forceinline__ void build_pairs_slot2(const uint32_t* w, uint32_t* p
 
 // ---- chunk products -------------------------------------------------------------------------
 
-// slot-2: 2^-20 * sum_k q_k x_k over the 64 weights of a chunk
+// The bits of fp16 1.0 in both halves, held in a vector register: with the mask in a scalar
+// register, each pair then takes one v_and_or_b32 (with both operands as literal constants the
+// compiler splits it into an AND and an OR, since these three-operand forms take no literals)
+__device__ __forceinline__ uint32_t one_pair_bits() {
+  uint32_t r;
+  asm("v_mov_b32 %0, 0x3c003c00" : "=v"(r));
+  return r;
+}
+
+// Two slot-2 codes as signed fp16 operands: the codes of elements j and j+8 sit in bits p..p+1 of
+// the two 16-bit halves of `word`; returns t * 2^(p-10) in each half (see the file comment).
+// `one` = one_pair_bits().
+template <int P>
+__device__ __forceinline__ uint32_t slot2_signed_pair(uint32_t word, uint32_t one) {
+  constexpr uint32_t kMask = 0x00030003u << P;
+  constexpr uint32_t kNegBias = (0xBC00u | (1u << P)) * 0x00010001u;  // -(1 + 2^(P-10)) in both halves
+  const half2_t h = __builtin_bit_cast(half2_t, (word & kMask) | one);
+  return __builtin_bit_cast(uint32_t, h + __builtin_bit_cast(half2_t, kNegBias));
+}
+
+// slot-2: 2^-20 * sum_k t_k x_k over the 64 weights of a chunk
 __device__ __forceinline__ float chunk_dot_slot2(const uint4& cw, const uint32_t* p) {
-  float a2 = 0.f, a3 = 0.f, a4 = 0.f;
+  const uint32_t one = one_pair_bits();
+  float a0 = 0.f, a2 = 0.f, a4 = 0.f, a6 = 0.f, a8 = 0.f;  // a_p: pairs at bit p, terms t x 2^(p-10)
   const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t u = words[d], v = u << 4, w = u >> 6;
+    const uint32_t u = words[d], w = u >> 6;
     const uint32_t* q = p + 8 * d;
-    // codes of elements (j, j+8) at fp16 mantissa bits 4-5 (a2), 6-7 (a3) or 8-9 (a4)
-    a2 = dot2(u & 0x00300030u, q[2], a2);  // j = 2
-    a3 = dot2(u & 0x00C000C0u, q[3], a3);  // j = 3
-    a4 = dot2(u & 0x03000300u, q[4], a4);  // j = 4
-    a2 = dot2(v & 0x00300030u, q[0], a2);  // j = 0
-    a3 = dot2(v & 0x00C000C0u, q[1], a3);  // j = 1
-    a2 = dot2(w & 0x00300030u, q[5], a2);  // j = 5
-    a3 = dot2(w & 0x00C000C0u, q[6], a3);  // j = 6
-    a4 = dot2(w & 0x03000300u, q[7], a4);  // j = 7
+    a0 = dot2(slot2_signed_pair<0>(u, one), q[0], a0);  // j = 0
+    a2 = dot2(slot2_signed_pair<2>(u, one), q[1], a2);  // j = 1
+    a4 = dot2(slot2_signed_pair<4>(u, one), q[2], a4);  // j = 2
+    a6 = dot2(slot2_signed_pair<6>(u, one), q[3], a6);  // j = 3
+    a8 = dot2(slot2_signed_pair<8>(u, one), q[4], a8);  // j = 4
+    a4 = dot2(slot2_signed_pair<4>(w, one), q[5], a4);  // j = 5
+    a6 = dot2(slot2_signed_pair<6>(w, one), q[6], a6);  // j = 6
+    a8 = dot2(slot2_signed_pair<8>(w, one), q[7], a8);  // j = 7
   }
-  return fmaf(fmaf(a4, 0.25f, a3), 0.25f, a2);
+  // sum t x = 2^10 a0 + 2^8 a2 + 2^6 a4 + 2^4 a6 + 2^2 a8 = 4 r
+  const float r = fmaf(fmaf(fmaf(fmaf(a0, 4.f, a2), 4.f, a4), 4.f, a6), 4.f, a8);
+  return r * 0x1p-18f;
 }
 
 // binary: p[16d + i] = (x_{32d+i}, x_{32d+i+16}) from the chunk's 64 fp16 activations (32 words)
@@ -194,23 +215,24 @@ __device__ __forceinline__ void build_pairs(const uint32_t* w, uint32_t* p) {
     build_pairs_slot2(w, p);
 }
 
-// 2^-20 * sum_k x_k over the chunk, by the same instruction sequence as the rows (all-zero
-// slot-2 codes have q = 1 everywhere; all-ones binary codes have b = 1 everywhere)
+// Binary codes: 2^-20 * sum_k x_k over the chunk, by the same instruction sequence as the rows
+// (all-ones codes have b = 1 everywhere). Slot-2 codes decode to signed operands and need none.
 template <bool BIN>
 __device__ __forceinline__ float chunk_ref(const uint32_t* p) {
   if constexpr (BIN)
     return chunk_dot_binary(make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu), p);
   else
-    return chunk_dot_slot2(make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u), p);
+    return 0.f;
 }
 
-// 2^-20 * sum_k t_k x_k over the chunk, given its reference sum
+// 2^-20 * sum_k t_k x_k over the chunk (binary: given its reference sum; every binary weight is
+// nonzero, so sum |x| over the chunk is also sum |t x|)
 template <bool BIN>
 __device__ __forceinline__ float chunk_value(const ChunkCodes<BIN>& cw, const uint32_t* p, float ref) {
   if constexpr (BIN)
     return fmaf(2.f, chunk_dot_binary(cw, p), -ref);
   else
-    return chunk_dot_slot2(cw, p) - ref;
+    return chunk_dot_slot2(cw, p);
 }
 
 // ---- staging one slice of activations ----------------------------------------------------
@@ -422,7 +444,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
 #pragma unroll
       for (int b = 0; b < kRing - 1 && b < kBatches; ++b) load_batch(ring[b], b, c, g0);
 
-      // ---- stage: pairs and all-zero-row products of the slice's chunks, once per workgroup
+      // ---- stage: pairs (and binary reference products) of the slice's chunks, once per workgroup
       __syncthreads();  // the previous slice's pairs are no longer read
       if constexpr (ROT) {
         stage_rotated<MT, kWaves, ROT>(lds_x, kSliceElems, job.x, job.signs, k, m, m0, k_begin,
@@ -457,7 +479,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
         }
         uint32_t p[kChunkPairDw];
         build_pairs<BIN>(w, p);
-        lds_ref[t * S + bc] = chunk_ref<BIN>(p);
+        if constexpr (BIN) lds_ref[t * S + bc] = chunk_ref<BIN>(p);
 #pragma unroll
         for (int g = 0; g < kGran; ++g)
           lds_pairs[(t * kGran + g) * S + bc] = make_uint4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
@@ -477,7 +499,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
           xp[t][4 * g + 2] = q.z;
           xp[t][4 * g + 3] = q.w;
         }
-        ref0[t] = lds_ref[t * S + cl];
+        ref0[t] = BIN ? lds_ref[t * S + cl] : 0.f;
       }
 
       // rows in batches; kRing - 1 batches are in flight while one is computed (a ring of register
@@ -547,8 +569,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
 //
 // The decode case that carries most of the traffic. A workgroup owns a block of rows and has one
 // wave per K slice of S chunks (64 weights each). Each lane owns one chunk of every row of its
-// wave, so the lane that turns its 64 activations into dot2 pairs (and their all-zero-row
-// product) is the only one that ever uses them: they stay in registers, with no LDS staging and
+// wave, so the lane that turns its 64 activations into dot2 pairs (and, for binary codes, their
+// all-ones-row product) is the only one that ever uses them: they stay in registers, with no LDS staging and
 // no barrier before the weight stream. Per wave:
 //   1. its activation loads (8 x 16 B per lane) go out first, then the first four 2-row batches
 //      of codes and scales, so for small matrices all of a wave's loads are in flight at once;
@@ -757,7 +779,7 @@ void gemv_wave_kernel(const GemvArgs args) {
     for (int i = 0; i < 32; ++i) xw[i] = norm_word(xw[i], gw[i], r);
   }
 
-  // 2. dot2 pairs and the all-zero-row product of this lane's chunk
+  // 2. dot2 pairs (and, for binary codes, the all-ones-row product) of this lane's chunk
   uint32_t xp[32];
   build_pairs<BIN>(xw, xp);
   const float ref = chunk_ref<BIN>(xp);
@@ -908,6 +930,16 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated, bool n
     p.rows_per_block = gemv_b3_mfma_rows((int32_t)m);
     return p;
   }
+  // single-token slot-2 in the plain basis: on the matrix cores when K fits
+  if (layout == TGS_LAYOUT_SLOT2 && m == 1 && !rotated && gemv_s2_mfma_fits(k)) {
+    p.mfma = 2;
+    p.stream = 1;
+    p.lanes = 64;
+    p.iter = 1;
+    p.slices = gemv_s2_mfma_waves(k);
+    p.rows_per_block = 16;
+    return p;
+  }
   // slot-2 and binary from here on (both in chunks of 64 weights). The single-token kernel: one wave per K slice of 64 chunks, up to 16
   // waves per workgroup
   const int chunks = (int)(k / kChunkElems);
@@ -969,6 +1001,11 @@ void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows) {
 }
 
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream) {
+  if (plan.mfma == 2) {
+    int64_t max_k = 0;
+    for (int i = 0; i < args.count; ++i) max_k = args.job[i].k > max_k ? args.job[i].k : max_k;
+    return gemv_s2_mfma_launch(args, blocks, max_k, plan.norm != 0, stream);
+  }
   if (plan.mfma)
     return gemv_b3_mfma_launch(args, blocks, plan.m, (int)rotation_block(plan.rotated), plan.norm != 0, stream);
   const bool bin = plan.layout == TGS_LAYOUT_BINARY;

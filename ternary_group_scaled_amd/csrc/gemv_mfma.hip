@@ -14,15 +14,14 @@
 //     and end within the 32 bytes from B0. Lane (r, q) of a row block (r = lane % 16, q = lane / 16)
 //     reads bytes B0 + 8q .. B0 + 8q + 7 of row r (three aligned dwords and a funnel shift) and
 //     peels their digits with packed 16-bit integer ops (q = v * 171 >> 9 equals v / 3 for
-//     v < 256; digit = v - 3q), five per byte, as the dot2 kernels do. MFMA step j (0..4) takes
-//     digit j of all eight bytes, paired (byte 0, byte 2), (1, 3), (4, 6), (5, 7). Shifted left by
-//     8 bits, a digit d in a 16-bit half is the bit pattern of the fp16 sub-normal d * 2^-16, so
-//     one shift per register makes the weight operand. With t = d - 1, sum x t = sum x d - sum x:
-//     a second chain of five MFMAs multiplies the same activations by the constant 2^-16 (the
-//     encoding of d = 1), its result is subtracted, and the outputs are scaled by 2^16 (exact)
-//     when they are stored. A row of zero weights runs the identical chain twice, so it gives
-//     exactly 0. (Digits used directly, as 2^-24 * d, lost precision on the matrix cores: a zero
-//     row came out at about 2^-16 of the activations' sum, not 0.)
+//     v < 256; digit = v - 3q), five per byte. MFMA step j (0..4) takes
+//     digit j of all eight bytes, paired (byte 0, byte 2), (1, 3), (4, 6), (5, 7). A digit d in
+//     the low byte of a 16-bit half becomes the fp16 weight t = d - 1 (-1.0, 0 or +1.0) with one
+//     byte lookup (v_perm): the digit, shifted into the high byte of the selector, picks the high
+//     byte of the fp16 value from the table {0xBC, 0x00, 0x3C}, and the low byte is a constant
+//     zero. So every product is t * x exactly, and a zero weight adds nothing: the partial sums
+//     and their rounding are those of the nonzero terms, and a row with a single nonzero weight
+//     gives s * t * x exactly.
 //   - Activations. The wave writes the group's activations (rotated when the weights are: sign
 //     flip, the natural-order Sylvester butterfly over the 128-block, 1/sqrt(128), one rounding to
 //     fp16) into a private LDS tile laid out [q][j][8] in exactly the order of the weight operand,
@@ -73,8 +72,13 @@ __device__ __forceinline__ int tile_slot(int rel) {
   return (q * 5 + j) * 8 + pos;
 }
 
-// 2^-16 in both fp16 halves of a word: the encoding of digit 1 (t = 0), which sums the activations
-constexpr uint32_t kUnitPair = 0x01000100u;
+// Weight operand of two digits: d (0..2) in the low byte of each 16-bit half -> fp16 t = d - 1 in
+// each half. The selector holds the digits in bytes 1 and 3 and 0x0C (constant zero) in bytes 0
+// and 2; the table's bytes 0..2 are the high bytes of fp16 -1.0, 0 and +1.0.
+__device__ __forceinline__ uint32_t digits_to_weights(u16x2 d) {
+  constexpr uint32_t kTable = 0x003C00BCu;
+  return __builtin_amdgcn_perm(0u, kTable, (__builtin_bit_cast(uint32_t, d) << 8) | 0x000C000Cu);
+}
 
 __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both halves
   const u16x2 q = (v * (u16x2)171) >> (u16x2)9;
@@ -518,24 +522,21 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
       ve1[fb] = __builtin_bit_cast(u16x2, w1 & 0x00FF00FFu);
       vo1[fb] = __builtin_bit_cast(u16x2, (w1 >> 8) & 0x00FF00FFu);
     }
-    // part: 2^-16 * sum x d per row block; ones: 2^-16 * sum x (the same for every output row)
+    // part: sum x t per row block
     f32x4 part[kFB];
 #pragma unroll
     for (int fb = 0; fb < kFB; ++fb) part[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 ones = f32x4{0.f, 0.f, 0.f, 0.f};
-    const half8 unit = __builtin_bit_cast(half8, make_uint4(kUnitPair, kUnitPair, kUnitPair, kUnitPair));
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       const half8 a = *reinterpret_cast<const half8*>(a_row + (kq * 5 + j) * 8);
-      ones = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, unit, ones, 0, 0, 0);
 #pragma unroll
       for (int fb = 0; fb < kFB; ++fb) {
         const u16x2 de0 = j < 4 ? peel(ve0[fb]) : ve0[fb];
         const u16x2 do0 = j < 4 ? peel(vo0[fb]) : vo0[fb];
         const u16x2 de1 = j < 4 ? peel(ve1[fb]) : ve1[fb];
         const u16x2 do1 = j < 4 ? peel(vo1[fb]) : vo1[fb];
-        const uint4 b4 = make_uint4(__builtin_bit_cast(uint32_t, de0) << 8, __builtin_bit_cast(uint32_t, do0) << 8,
-                                    __builtin_bit_cast(uint32_t, de1) << 8, __builtin_bit_cast(uint32_t, do1) << 8);
+        const uint4 b4 = make_uint4(digits_to_weights(de0), digits_to_weights(do0), digits_to_weights(de1),
+                                    digits_to_weights(do1));
         part[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, b4), part[fb], 0, 0, 0);
       }
     }
@@ -545,7 +546,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     for (int fb = 0; fb < kFB; ++fb) {
       const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)st.s[fb]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[fb][r] = fmaf(sc, part[fb][r] - ones[r], acc[fb][r]);
+      for (int r = 0; r < 4; ++r) acc[fb][r] = fmaf(sc, part[fb][r], acc[fb][r]);
     }
   };
 
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) sum += red[(w * kFB * 4 + idx) * 64 + ln];
     const int token = 4 * (ln >> 4) + r, row = n_base + 16 * fb + (ln & 15);
-    if (token < m && row < n) job.y[(int64_t)token * n + row] = sum * 65536.0f;  // 2^16: the weights' scale
+    if (token < m && row < n) job.y[(int64_t)token * n + row] = sum;
   }
 }
 

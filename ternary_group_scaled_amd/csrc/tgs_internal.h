@@ -89,7 +89,8 @@ struct GemvPlan {
   int32_t rotated;    // 0 (plain), 1 (128-element rotation blocks) or 1024
   int32_t stream;     // 1: the single-token kernel (slot-2, plain basis, m = 1)
   int32_t slices;     // single-token kernel: K slices of 64 chunks = waves per workgroup
-  int32_t mfma;       // 1: base-3, on the matrix cores (gemv_mfma.hip)
+  int32_t mfma;       // 1: base-3, on the matrix cores (gemv_mfma.hip); 2: single-token slot-2 on the
+                      // matrix cores (gemv_s2_mfma.hip)
   int32_t iter;       // rows per lane slot
   int32_t rows_per_block;
   int32_t norm;       // 1: RMSNorm prologue
@@ -102,6 +103,11 @@ GemvPlan gemv_plan(int32_t layout, int64_t k, int64_t m, int32_t rotated, bool n
 // after the jobs of a launch are known: pick rows per workgroup from their total row count
 void gemv_plan_set_rows(GemvPlan& p, int64_t total_rows);
 hipError_t gemv_launch(const GemvPlan& plan, GemvArgs& args, int32_t blocks, hipStream_t stream);
+// single-token slot-2 on the matrix cores: whether K fits (a multiple of 512, at most 16384), waves
+// per workgroup for K, and the launch (16 rows per workgroup; LDS sized for the largest K of the jobs)
+bool gemv_s2_mfma_fits(int64_t k);
+int gemv_s2_mfma_waves(int64_t k);
+hipError_t gemv_s2_mfma_launch(GemvArgs& args, int32_t blocks, int64_t max_k, bool norm, hipStream_t stream);
 // base-3 on the matrix cores: rows of y per workgroup for m tokens
 int gemv_b3_mfma_rows(int32_t m);
 // block: 0 for plain-basis weights, else the rotation block (128 or 1024)
