@@ -44,8 +44,8 @@ typedef enum {
   TGS_E_SHAPE = 2,    /* K % 128 != 0, N < 1, M out of range, row stride too small ... */
   TGS_E_ALIGN = 3,    /* a buffer is not aligned as documented */
   TGS_E_CODE = 4,     /* invalid code: trit outside {-1,0,1}, slot value 3, base-3 byte > 242,
-                         non-canonical padding, sign outside {-1,+1} */
-  TGS_E_LAYOUT = 5,   /* bad descriptor magic/version or unknown layout */
+                         non-canonical padding (host arrays only: device signs are not read) */
+  TGS_E_LAYOUT = 5,   /* bad descriptor magic/version, unknown layout or rotation block */
   TGS_E_BASIS = 6,    /* weights in the rotated basis without signs, or signs for plain weights */
   TGS_E_SIZE = 7,     /* an output buffer is too small */
   TGS_E_DTYPE = 8,    /* unsupported activation/output dtype for this call */
@@ -114,8 +114,10 @@ typedef struct tgs_matrix {
 /* Minimum bytes per row of codes for the layout, or 0 if layout/k is invalid. */
 size_t tgs_code_row_bytes(int32_t layout, int64_t k);
 
-/* Fill a descriptor with magic/version and the minimum row stride. Returns TGS_E_SHAPE or
- * TGS_E_LAYOUT for invalid shapes/layouts (the descriptor is then left zeroed). */
+/* Fill a descriptor with magic/version and the minimum row stride. Returns TGS_E_SHAPE for an
+ * invalid shape and TGS_E_LAYOUT for an unknown layout or a `rotated` value other than 0, 1, 128
+ * and 1024, the same status every device call returns for such a descriptor (the descriptor is
+ * then left zeroed). */
 tgs_status tgs_matrix_init(tgs_matrix* w, int32_t layout, int32_t rotated, int64_t n, int64_t k,
                            const void* codes, const uint16_t* scales);
 
@@ -135,20 +137,28 @@ tgs_status pack_ternary(int32_t layout, const int8_t* trits, const uint16_t* sca
 
 /*
  * unpack_ternary (host): decode a host-resident packed matrix back to trits (and copy its
- * scales). Every byte is checked: slot value 3, base-3 bytes above 242, nonzero trits past K and
- * pad bytes other than 121 give TGS_E_CODE. trits_out is [n][k] int8; scales_out may be NULL.
+ * scales): the exact inverse of pack_ternary for either packing of [P3] "Two packings: PTQ1_0 and
+ * PQ2_0" (and the binary layout), so a native-ternary checkpoint survives the round trip bit for
+ * bit ([P1] opening section: re-encoding such a checkpoint is lossless). Every byte is checked:
+ * slot value 3, base-3 bytes above 242, nonzero trits past K and pad bytes other than 121 give
+ * TGS_E_CODE. trits_out is [n][k] int8; scales_out may be NULL.
  */
 tgs_status unpack_ternary(const tgs_matrix* w, int8_t* trits_out, uint16_t* scales_out);
 
 /*
  * ternary_gemv (device): y[i][j] = sum_k s[j][k/128] * t[j][k] * xr[i][k] for i < m, j < n,
  * with xr = x, or xr = R x when w->rotated (the rotation, with the descriptor's block size, is
- * computed inside the kernel).
+ * computed inside the kernel). The weight of row j, column k is w = s_g * t with one fp16 scale
+ * per 128-weight group ([P3] "Group-scaled ternary format"; [P2] "What the format is"); rotated
+ * codes are weights of the basis R x ([P3] "Block-wise Hadamard rotation": the layer computes
+ * W (R x)). The packed codes are read as they are, never expanded in memory ([P3] "Low-bit
+ * kernels for hybrid attention": the kernels consume the packed weights directly).
  *   w       descriptor (host memory) of device-resident codes and scales
  *   x       device [m][k] activations of x_dtype; only TGS_F16 is accepted; 16-byte aligned
  *   m       1 .. TGS_MAX_M_GEMV (decode, or a small verify batch)
- *   signs   device [k] int8 in {-1, +1}, 16-byte aligned, when w->rotated, else NULL. Values are not checked on
- *           the device: any other value gives an unspecified result.
+ *   signs   device [k] int8 in {-1, +1}, 16-byte aligned, when w->rotated, else NULL. The values
+ *           live in device memory and are not read by the host (checking them would take a
+ *           synchronous copy on every call); another value v multiplies its activation by v.
  *   y       device [m][n] fp32, 4-byte aligned
  *   stream  hipStream_t or NULL
  * Arithmetic: codes are decoded in registers; each 128-group is accumulated in fp32 and scaled
@@ -180,7 +190,8 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
  * are decoded tile by tile into LDS as bf16 and multiplied on the matrix cores (MFMA) with fp32
  * accumulation; each 128-group's partial product is scaled by its fp16 scale in fp32 ([P3]
  * section "Low-bit kernels for hybrid attention": unpack and group scale fused into the GEMM).
- *   x       device [m][k], TGS_BF16 only, 16-byte aligned
+ *   x       device [m][k], TGS_BF16 only, 16-byte aligned; k at most 8384512 (the kernels address
+ *           128 activation rows with 32-bit byte offsets), else TGS_E_SHAPE
  *   signs   must be NULL: this product is provided for plain-basis weights only, and rotated
  *           weights are refused with TGS_E_BASIS rather than multiplied in the wrong basis
  *   y       device [m][n] fp32, 4-byte aligned

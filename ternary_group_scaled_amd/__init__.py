@@ -140,6 +140,14 @@ def unpack_ternary(layout: int, codes: np.ndarray, scales: np.ndarray, k: int):
 
 
 # ------------------------------------------------------------------------------ device calls
+#
+# The C ABI sees raw pointers only, so it cannot know a buffer's size, type or device: the wrappers
+# below check every tensor before the call (dtype, element count, contiguity, then device), and
+# raise TgsError with the status the library uses for that kind of error. A rejected call queues
+# nothing.
+
+_CODE = {name: code for code, name in STATUS.items()}
+
 
 def _torch():
     import torch  # imported lazily: host packing works without it
@@ -153,11 +161,54 @@ def _stream_handle(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _raise(name: str, message: str):
+    raise TgsError(_CODE[name], message)
+
+
+def _need(t, what: str, dtypes, numel: int | None = None, min_numel: int | None = None):
+    """Check one tensor argument of a device call: dtype, element count, contiguity."""
+    if t is None:
+        _raise("TGS_E_NULL", f"{what} is None")
+    if t.dtype not in dtypes:
+        _raise("TGS_E_DTYPE", f"{what} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        _raise("TGS_E_SHAPE", f"{what} holds {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        _raise("TGS_E_SIZE", f"{what} holds {t.numel()} elements, needs at least {min_numel}")
+    if not t.is_contiguous():
+        _raise("TGS_E_SHAPE", f"{what} must be contiguous")
+
+
+def _on_device(device, **tensors):
+    """Every tensor argument must be device memory of the call's device (checked last, so that a
+    call with host tensors still reports its other argument errors first)."""
+    for what, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != device):
+            _raise("TGS_E_DEVICE", f"{what} is on {t.device}; the call runs on {device} (device memory only)")
+
+
+def _signs_ok(signs, k: int):
+    if signs is not None:
+        _need(signs, "signs", (_torch().int8,), numel=k)
+
+
+def _gamma_ok(gamma, k: int):
+    torch = _torch()
+    _need(gamma, "gamma", (torch.bfloat16, torch.int16), numel=k)
+
+
 class PackedMatrix:
     """Packed ternary weights resident on the GPU: codes [n][stride] uint8, scales [n][k/128] fp16."""
 
     def __init__(self, layout: int, codes, scales, k: int, rotated=False):
         """rotated: False/0 (plain basis), True/1/128 (128-element rotation blocks) or 1024."""
+        torch = _torch()
+        if codes.dtype != torch.uint8 or codes.dim() != 2 or codes.stride(1) != 1:
+            _raise("TGS_E_SHAPE", "codes must be a uint8 [n][stride] tensor with contiguous rows")
+        if scales.dtype not in (torch.float16, torch.int16) or not scales.is_contiguous():
+            _raise("TGS_E_DTYPE", "scales must be a contiguous fp16 (or int16 bit-pattern) tensor")
+        if scales.numel() != codes.shape[0] * (int(k) // 128) or scales.device != codes.device:
+            _raise("TGS_E_SHAPE", "scales must hold n * k / 128 values on the codes' device")
         self.layout = layout
         self.codes = codes
         self.scales = scales
@@ -178,32 +229,79 @@ class PackedMatrix:
                    trits.shape[1], rotated)
 
     @property
+    def device(self):
+        return self.codes.device
+
+    @property
     def nbytes(self) -> int:
         return int(self.codes.numel() + 2 * self.scales.numel())
+
+
+def _rows_of(x, k: int, what: str = "x") -> int:
+    if x is None:
+        _raise("TGS_E_NULL", f"{what} is None")
+    if k <= 0 or x.numel() % k != 0 or x.numel() == 0:
+        _raise("TGS_E_SHAPE", f"{what} holds {x.numel()} elements, not a positive multiple of k = {k}")
+    return x.numel() // k
+
+
+def _out(y, m: int, n: int, device):
+    """The fp32 output [m][n]: allocated on the call's device when y is None, else checked."""
+    torch = _torch()
+    if y is None:
+        return torch.empty((m, n), dtype=torch.float32, device=device)
+    _need(y, "y", (torch.float32,), min_numel=m * n)
+    return y
 
 
 def ternary_gemv(w: PackedMatrix, x, signs=None, y=None, stream=None):
     """y[m][n] (fp32) = W (R) x for fp16 x [m][k], m <= 8. Returns y."""
     torch = _torch()
-    x2 = x.reshape(-1, w.k)
-    m = x2.shape[0]
-    if y is None:
-        y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
-    _check(_lib.ternary_gemv(ctypes.byref(w.desc), x2.data_ptr(), F16, m,
+    m = _rows_of(x, w.k)
+    _need(x, "x", (torch.float16,))
+    _signs_ok(signs, w.k)
+    y = _out(y, m, w.n, w.device)
+    _on_device(w.device, codes=w.codes, scales=w.scales, x=x, signs=signs, y=y)
+    _check(_lib.ternary_gemv(ctypes.byref(w.desc), x.data_ptr(), F16, m,
                              signs.data_ptr() if signs is not None else None, y.data_ptr(), _stream_handle(stream)))
     return y
 
 
-def ternary_gemv_batched(ws, xs, ys, signs=None, stream=None):
-    """Independent GEMVs sharing m (fp16 inputs, fp32 outputs), issued as few launches as possible."""
+def _batched_ptrs(ws, xs, ys, signs, gammas=None):
+    """Checks and pointer arrays of a batched call: m is taken from xs[0], and every x must then
+    hold m * k_i fp16 values, every y at least m * n_i fp32 values."""
+    torch = _torch()
     count = len(ws)
+    if count == 0 or len(xs) != count or len(ys) != count:
+        _raise("TGS_E_SHAPE", "ws, xs and ys must be non-empty lists of one length")
+    if signs is not None and len(signs) != count:
+        _raise("TGS_E_SHAPE", "signs must have one entry per matrix")
+    m = _rows_of(xs[0], ws[0].k, "xs[0]")
+    for i, (w, x, y) in enumerate(zip(ws, xs, ys)):
+        _need(x, f"xs[{i}]", (torch.float16,), numel=m * w.k)
+        _need(y, f"ys[{i}]", (torch.float32,), min_numel=m * w.n)
+        if signs is not None:
+            _signs_ok(signs[i], w.k)
+        if gammas is not None:
+            _gamma_ok(gammas[i], w.k)
+    for i, (w, x, y) in enumerate(zip(ws, xs, ys)):
+        _on_device(ws[0].device, codes=w.codes, scales=w.scales, x=x, y=y,
+                   signs=signs[i] if signs is not None else None, gamma=gammas[i] if gammas is not None else None)
     descs = (Matrix * count)(*[w.desc for w in ws])
-    m = xs[0].reshape(-1, ws[0].k).shape[0]
     xp = (_vp * count)(*[x.data_ptr() for x in xs])
     yp = (_vp * count)(*[y.data_ptr() for y in ys])
     sp = None
     if signs is not None:
         sp = (_vp * count)(*[s.data_ptr() if s is not None else None for s in signs])
+    gp = None
+    if gammas is not None:
+        gp = (_vp * count)(*[g.data_ptr() for g in gammas])
+    return count, m, descs, xp, yp, sp, gp
+
+
+def ternary_gemv_batched(ws, xs, ys, signs=None, stream=None):
+    """Independent GEMVs sharing m (fp16 inputs, fp32 outputs), issued as few launches as possible."""
+    count, m, descs, xp, yp, sp, _ = _batched_ptrs(ws, xs, ys, signs)
     _check(_lib.ternary_gemv_batched(descs, count, xp, F16, m, sp, yp, _stream_handle(stream)))
     return ys
 
@@ -211,11 +309,13 @@ def ternary_gemv_batched(ws, xs, ys, signs=None, stream=None):
 def ternary_gemv_rmsnorm(w: PackedMatrix, x, gamma, eps, signs=None, y=None, stream=None):
     """y[m][n] (fp32) = W (R) RMSNorm(x) for fp16 x [m][k], m <= 8; gamma: bf16 [k]. Returns y."""
     torch = _torch()
-    x2 = x.reshape(-1, w.k)
-    m = x2.shape[0]
-    if y is None:
-        y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
-    _check(_lib.ternary_gemv_rmsnorm(ctypes.byref(w.desc), x2.data_ptr(), F16, m, gamma.data_ptr(), float(eps),
+    m = _rows_of(x, w.k)
+    _need(x, "x", (torch.float16,))
+    _gamma_ok(gamma, w.k)
+    _signs_ok(signs, w.k)
+    y = _out(y, m, w.n, w.device)
+    _on_device(w.device, codes=w.codes, scales=w.scales, x=x, gamma=gamma, signs=signs, y=y)
+    _check(_lib.ternary_gemv_rmsnorm(ctypes.byref(w.desc), x.data_ptr(), F16, m, gamma.data_ptr(), float(eps),
                                      signs.data_ptr() if signs is not None else None, y.data_ptr(),
                                      _stream_handle(stream)))
     return y
@@ -223,67 +323,74 @@ def ternary_gemv_rmsnorm(w: PackedMatrix, x, gamma, eps, signs=None, y=None, str
 
 def ternary_gemv_rmsnorm_batched(ws, xs, gammas, eps, ys, signs=None, stream=None):
     """ternary_gemv_batched with the RMSNorm prologue (one bf16 gamma [k] per matrix)."""
-    count = len(ws)
-    descs = (Matrix * count)(*[w.desc for w in ws])
-    m = xs[0].reshape(-1, ws[0].k).shape[0]
-    xp = (_vp * count)(*[x.data_ptr() for x in xs])
-    gp = (_vp * count)(*[g.data_ptr() for g in gammas])
-    yp = (_vp * count)(*[y.data_ptr() for y in ys])
-    sp = None
-    if signs is not None:
-        sp = (_vp * count)(*[s.data_ptr() if s is not None else None for s in signs])
+    if gammas is None or len(gammas) != len(ws):
+        _raise("TGS_E_NULL", "one gamma per matrix is required")
+    count, m, descs, xp, yp, sp, gp = _batched_ptrs(ws, xs, ys, signs, gammas)
     _check(_lib.ternary_gemv_rmsnorm_batched(descs, count, xp, F16, m, gp, float(eps), sp, yp, _stream_handle(stream)))
     return ys
 
 
+def _float_dtypes():
+    torch = _torch()
+    return {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+
+
+def _rotation_args(x, signs, y, out_dtype, gamma=None):
+    dt = _float_dtypes()
+    if x is None:
+        _raise("TGS_E_NULL", "x is None")
+    if x.dim() < 1:
+        _raise("TGS_E_SHAPE", "x must have a last dimension k")
+    k = x.shape[-1]
+    m = _rows_of(x, k)
+    _need(x, "x", tuple(dt))
+    if signs is None:
+        _raise("TGS_E_NULL", "signs are required")
+    _signs_ok(signs, k)
+    if gamma is not None:
+        _gamma_ok(gamma, k)
+    if y is None:
+        y = _torch().empty((m, k), dtype=out_dtype or _torch().float32, device=x.device)
+    else:
+        _need(y, "y", tuple(dt), min_numel=m * k)
+    _on_device(x.device, x=x, signs=signs, gamma=gamma, y=y)
+    return dt, k, m, y
+
+
 def rmsnorm_hadamard_rotate(x, gamma, eps, signs, block=128, y=None, out_dtype=None, stream=None):
     """R RMSNorm(x) per row of x [m][k] (fp16/bf16/fp32), gamma bf16 [k]; fp16/bf16/fp32 output."""
-    torch = _torch()
-    dt = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
-    k = x.shape[-1]
-    x2 = x.reshape(-1, k)
-    if y is None:
-        y = torch.empty(x2.shape, dtype=out_dtype or torch.float32, device=x.device)
-    _check(_lib.rmsnorm_hadamard_rotate(x2.data_ptr(), dt[x2.dtype], x2.shape[0], k, block, gamma.data_ptr(),
-                                        float(eps), signs.data_ptr(), y.data_ptr(), dt[y.dtype],
-                                        _stream_handle(stream)))
+    if gamma is None:
+        _raise("TGS_E_NULL", "gamma is None")
+    dt, k, m, y = _rotation_args(x, signs, y, out_dtype, gamma)
+    _check(_lib.rmsnorm_hadamard_rotate(x.data_ptr(), dt[x.dtype], m, k, block, gamma.data_ptr(), float(eps),
+                                        signs.data_ptr(), y.data_ptr(), dt[y.dtype], _stream_handle(stream)))
     return y
 
 
 def ternary_gemm(w: PackedMatrix, x, y=None, stream=None):
     """y[m][n] (fp32) = W x for bf16 x [m][k]. Returns y."""
     torch = _torch()
-    x2 = x.reshape(-1, w.k)
-    m = x2.shape[0]
-    if y is None:
-        y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
-    _check(_lib.ternary_gemm(ctypes.byref(w.desc), x2.data_ptr(), BF16, m, None, y.data_ptr(), _stream_handle(stream)))
+    m = _rows_of(x, w.k)
+    _need(x, "x", (torch.bfloat16,))
+    y = _out(y, m, w.n, w.device)
+    _on_device(w.device, codes=w.codes, scales=w.scales, x=x, y=y)
+    _check(_lib.ternary_gemm(ctypes.byref(w.desc), x.data_ptr(), BF16, m, None, y.data_ptr(), _stream_handle(stream)))
     return y
 
 
 def hadamard_rotate(x, signs, block=128, y=None, out_dtype=None, stream=None):
     """Block-wise signed Walsh-Hadamard rotation (128 or 1024 per block) of x [m][k]; fp16/bf16/fp32
     output."""
-    torch = _torch()
-    dt = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
-    k = x.shape[-1]
-    x2 = x.reshape(-1, k)
-    if y is None:
-        y = torch.empty(x2.shape, dtype=out_dtype or torch.float32, device=x.device)
-    _check(_lib.hadamard_rotate(x2.data_ptr(), dt[x2.dtype], x2.shape[0], k, block, signs.data_ptr(), y.data_ptr(),
+    dt, k, m, y = _rotation_args(x, signs, y, out_dtype)
+    _check(_lib.hadamard_rotate(x.data_ptr(), dt[x.dtype], m, k, block, signs.data_ptr(), y.data_ptr(),
                                 dt[y.dtype], _stream_handle(stream)))
     return y
 
 
 def hadamard_rotate_g128(x, signs, y=None, out_dtype=None, stream=None):
     """Block-wise signed Walsh-Hadamard rotation (128 per block) of x [m][k]; fp16/bf16/fp32 output."""
-    torch = _torch()
-    dt = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
-    k = x.shape[-1]
-    x2 = x.reshape(-1, k)
-    if y is None:
-        y = torch.empty(x2.shape, dtype=out_dtype or torch.float32, device=x.device)
-    _check(_lib.hadamard_rotate_g128(x2.data_ptr(), dt[x2.dtype], x2.shape[0], k, signs.data_ptr(), y.data_ptr(),
+    dt, k, m, y = _rotation_args(x, signs, y, out_dtype)
+    _check(_lib.hadamard_rotate_g128(x.data_ptr(), dt[x.dtype], m, k, signs.data_ptr(), y.data_ptr(),
                                      dt[y.dtype], _stream_handle(stream)))
     return y
 
@@ -292,7 +399,8 @@ def ternary_code_flips(a: PackedMatrix, b: PackedMatrix, rows=True, total=True, 
     """Code flips between two packed matrices on the GPU: (total uint64 [1] or None,
     per-row counts int32 [n] holding uint32 values, or None)."""
     torch = _torch()
-    dev = a.codes.device
+    dev = a.device
+    _on_device(dev, a_codes=a.codes, b_codes=b.codes)
     r = torch.empty(a.n, dtype=torch.int32, device=dev) if rows else None
     t = torch.empty(1, dtype=torch.int64, device=dev) if total else None
     _check(_lib.ternary_code_flips(ctypes.byref(a.desc), ctypes.byref(b.desc), r.data_ptr() if r is not None else None,
@@ -303,7 +411,18 @@ def ternary_code_flips(a: PackedMatrix, b: PackedMatrix, rows=True, total=True, 
 def ternary_code_flips_batched(pairs, totals, rows=None, stream=None):
     """Code flips of several pairs (a, b) of one layout in one launch. totals: int64 [1] tensors
     (or None entries); rows: int32 [n] tensors (or None entries), or None."""
+    torch = _torch()
     count = len(pairs)
+    if count == 0 or len(totals) != count or (rows is not None and len(rows) != count):
+        _raise("TGS_E_SHAPE", "pairs, totals (and rows) must be non-empty lists of one length")
+    for i, (a, b) in enumerate(pairs):
+        if totals[i] is not None:
+            _need(totals[i], f"totals[{i}]", (torch.int64,), min_numel=1)
+        if rows is not None and rows[i] is not None:
+            _need(rows[i], f"rows[{i}]", (torch.int32,), min_numel=a.n)
+    for i, (a, b) in enumerate(pairs):
+        _on_device(pairs[0][0].device, a_codes=a.codes, b_codes=b.codes, total=totals[i],
+                   rows=rows[i] if rows is not None else None)
     da = (Matrix * count)(*[a.desc for a, _ in pairs])
     db = (Matrix * count)(*[b.desc for _, b in pairs])
     tp = (_vp * count)(*[t.data_ptr() if t is not None else None for t in totals])

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     const int xo = live ? (tok * k + 128 * g + kE * p) * 2 : kOobOffset;
     if constexpr (MT == 8) {
       const auto a = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo, 0, 0);
-      const auto b = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo + 16, 0, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, live ? xo + 16 : kOobOffset, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         st.x[i] = a[i];

@@ -210,7 +210,7 @@ tgs_status tgs_matrix_init(tgs_matrix* w, int32_t layout, int32_t rotated, int64
   if (!valid_layout(layout)) return fail(TGS_E_LAYOUT, "unknown layout %d", layout);
   if (n < 1 || k < 128 || k % 128 != 0) return fail(TGS_E_SHAPE, "need n >= 1 and k a positive multiple of 128");
   if (rotated != 0 && rotated != 1 && rotated != 128 && rotated != 1024)
-    return fail(TGS_E_BASIS, "rotated must be 0, 1 (128-element blocks), 128 or 1024, got %d", rotated);
+    return fail(TGS_E_LAYOUT, "rotated must be 0, 1 (128-element blocks), 128 or 1024, got %d", rotated);
   if (rotated == 1024 && k % 1024 != 0) return fail(TGS_E_SHAPE, "1024-element rotation blocks need k % 1024 == 0");
   // the descriptor is written only once every check has passed: a failed call leaves it zeroed
   w->magic = TGS_MAGIC;
@@ -454,6 +454,10 @@ tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int
   if (signs) return fail(TGS_E_BASIS, "signs given for weights in the plain basis");
   if (x_dtype != TGS_BF16) return fail(TGS_E_DTYPE, "ternary_gemm takes bf16 activations (TGS_BF16)");
   if (m < 1 || m > (1LL << 30)) return fail(TGS_E_SHAPE, "m must be >= 1, got %lld", (long long)m);
+  // the kernels address a launch's activation rows (at least 128 of them) with 32-bit offsets
+  if (w->k > tgs::kMaxDeviceCodeBytes / (128 * 2))
+    return fail(TGS_E_SHAPE, "ternary_gemm needs k <= %lld (got %lld)", (long long)(tgs::kMaxDeviceCodeBytes / 256),
+                (long long)w->k);
   if (!x || !y) return fail(TGS_E_NULL, "x or y is NULL");
   if (!aligned(x, 16)) return fail(TGS_E_ALIGN, "x must be 16-byte aligned");
   if (!aligned(y, 4)) return fail(TGS_E_ALIGN, "y must be 4-byte aligned");

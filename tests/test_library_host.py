@@ -169,6 +169,8 @@ def test_device_call_argument_checks_happen_before_any_device_work():
     assert lib.ternary_gemm(ctypes.byref(_fake_matrix(rotated=1)), 0x300000, tgs.BF16, 4, 0x500000, 0x400000,
                             None) == 6
     assert lib.ternary_gemm(ctypes.byref(m), 0x300000, tgs.BF16, 0, None, 0x400000, None) == 2
+    big = _fake_matrix(k=1 << 23)
+    assert lib.ternary_gemm(ctypes.byref(big), 0x300000, tgs.BF16, 4, None, 0x400000, None) == 2  # k <= 2^23 - 4096
     # hadamard_rotate_g128
     assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 200, 0x500000, 0x400000, tgs.F32, None) == 2
     assert lib.hadamard_rotate_g128(0x300000, tgs.F16, 2, 256, 0x500000, 0x400000, 99, None) == 8  # no such dtype
@@ -262,8 +264,22 @@ def test_matrix_init_rejects_bad_shapes():
     assert tgs.lib().tgs_matrix_init(ctypes.byref(m), 5, 0, 4, 128, 1, 1) == 5
     assert m.magic == 0
     assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 1024, 4, 1536, 1, 1) == 2  # k % 1024 != 0
-    assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 512, 4, 2048, 1, 1) == 6   # no 512-blocks
+    assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, 512, 4, 2048, 1, 1) == 5   # no 512-blocks
     assert m.magic == 0
+
+
+def test_bad_rotation_block_has_one_status_everywhere():
+    """An invalid `rotated` field is an invalid descriptor: TGS_E_LAYOUT from tgs_matrix_init and from
+    every call that checks a descriptor (the header documents the same status)."""
+    m = tgs.Matrix()
+    for rotated in (2, 512, -1, 2048):
+        assert tgs.lib().tgs_matrix_init(ctypes.byref(m), tgs.SLOT2, rotated, 4, 2048, 1, 1) == 5
+    bad = _fake_matrix(rotated=1, k=2048)
+    bad.rotated = 512
+    assert _gemv(bad, signs=0x500000) == 5
+    assert tgs.lib().ternary_gemm(ctypes.byref(bad), 0x300000, tgs.BF16, 4, None, 0x400000, None) == 5
+    codes = np.zeros((4, 512), dtype=np.uint8)
+    assert tgs.lib().unpack_ternary(ctypes.byref(bad), codes.ctypes.data, None) == 5
 
 
 @pytest.mark.parametrize("rotated,stored", [(0, 0), (1, 1), (128, 1), (1024, 1024)])
