@@ -1,24 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the ternary group-scaled GEMV/GEMM library on one MI355X.
 
-Default workload: the 8B-class decode GEMV set at M = 1 in the 2-bit-slot layout: 36 layers,
-each with q 4096x4096, k 1024x4096, v 1024x4096, o 4096x4096, gate 12288x4096, up 12288x4096 and
-down 4096x12288 (N x K), every matrix its own buffer (1.845 GB of packed weights, far more than
-the 256 MB last-level cache). One step = one pass over all 252 matrices in layer order, where
+Headline: the 8B-class decode GEMV set at M = 1 in the 2-bit-slot layout: 36 layers, each with
+q 4096x4096, k 1024x4096, v 1024x4096, o 4096x4096, gate 12288x4096, up 12288x4096 and down
+4096x12288 (N x K), every matrix its own buffer (1.845 GB of packed weights, far more than the
+256 MB last-level cache). One step = one pass over all 252 matrices in layer order, where
 matrices that read the same input share a launch (q/k/v, gate/up): 144 launches, captured once
 in a HIP graph and replayed. Inputs are seeded synthetic data already resident in HBM.
 
-Prints one JSON line (rank 0). `value` is achieved algorithmic GB/s for the whole pass:
-packed codes + fp16 scales + fp16 activations read + fp32 outputs written, divided by the
-wall time of a step (HIP events around the replays, on the stream they run on). `roofline`
-reports the GEMV kernel against the 8 TB/s HBM peak: algorithmic bytes per launch over the
-average launch duration (the timed region divided by the launches in it; the launches run back
-to back). Its `traffic` is the HBM bytes per launch that rocprofv3 counters measured for the
-same command, read from profiles/ only while the kernel sources still match the ones profiled.
+The default run prints one JSON line (rank 0): `value` is the headline's achieved algorithmic
+GB/s (packed codes + fp16 scales + fp16 activations read + fp32 outputs written, over the wall
+time of a step: HIP events around the replays, on the stream they run on). `roofline` reports the
+GEMV kernel against the 8 TB/s HBM peak: algorithmic bytes per launch over the average launch
+duration (the timed region divided by the launches in it; the launches run back to back), and
+against the read bandwidth a plain streaming kernel reaches on the same device (`stream_read`,
+`frac_vs_measured`). Its `traffic` is the HBM bytes per launch that rocprofv3 counters measured for
+the same kernel, read from profiles/ only while the kernel sources still match the ones profiled.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
 
-Other workloads (`--workload base3|gemm|rotated|flips|config1`) print lines of their own; they are
-measurements for the design notes, not the headline.
+The same line carries the other measured configurations under `configs`, each with its own
+roofline and CPU baseline: the single 256 x 1024 GEMV (latency), the base-3 8B set, the 27B-class
+prefill GEMM at M in {16, 128, 2048} for both shapes, and the 27B-class rotated base-3 set at
+M in {1, 8} with the rotation fused and as two passes.
+
+`--workload` runs one workload alone (8b, config1, base3, gemm, rotated, binary, rmsnorm, flips,
+stream) and prints its lines.
 """
 from __future__ import annotations
 
@@ -52,8 +58,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8b",
-                    choices=["8b", "base3", "binary", "rotated", "gemm", "flips", "rmsnorm", "config1"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "8b", "base3", "binary", "rotated", "gemm", "flips", "rmsnorm", "config1",
+                             "stream"])
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the set (default: 36 for the 8B-class sets, 64 for the rotated 27B-class set)")
     ap.add_argument("--mode", default="layer", choices=["layer", "fused-layer", "set"],
@@ -67,12 +74,63 @@ def parse():
     ap.add_argument("--rot-block", type=int, default=128, choices=[128, 1024],
                     help="rotation block of the rotated 27B-class set (128: one block per scale group)")
     ap.add_argument("--one-mode", action="store_true", help="time only --mode (the others are reported by default)")
+    ap.add_argument("--no-eager", action="store_true",
+                    help="skip the eager pass before graph capture (with --warmup 0 every launch of the GEMV "
+                         "kernels is then a timed replay: the command for a kernel trace of the timed region)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="run one device-to-device copy of this many MiB first (a known-size kernel that calibrates "
-                         "the FETCH_SIZE/WRITE_SIZE counters in a profile of this command)")
+    ap.add_argument("--stream-gib", type=int, default=0,
+                    help="read a buffer of this many GiB once with the streaming-read probe first (a kernel of "
+                         "known traffic that calibrates the FETCH_SIZE counter in a profile of this command)")
     return ap.parse_args()
+
+
+def cpu_info():
+    """Host CPU model (from /proc/cpuinfo) and the threads the oracle's OpenMP loops use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return model, threads
+
+
+def roofline(bound, achieved, peak, unit, kernel, traffic=None, **extra):
+    line = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
+    line.update(extra)
+    return line
+
+
+def stream_read_ceiling(torch, tgs, gib=4, launches=8):
+    """Read bandwidth of the streaming-read probe over a cold buffer of `gib` GiB (16x the
+    last-level cache): the best of `launches` back-to-back reads, each timed with HIP events."""
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = tgs.stream_read(buf)  # first touch
+    torch.cuda.synchronize()
+    times = []
+    stream = torch.cuda.current_stream()
+    for _ in range(launches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        tgs.stream_read(buf, sink)
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del buf, sink
+    torch.cuda.empty_cache()
+    best = min(times)
+    log(f"[bench] streaming read of {gib} GiB: best {nbytes / best / 1e6:.0f} GB/s, median "
+        f"{nbytes / sorted(times)[len(times) // 2] / 1e6:.0f} GB/s")
+    return {"value": round(nbytes / best / 1e6, 1), "unit": "GB/s", "bytes": nbytes, "launches": launches,
+            "median_gbs": round(nbytes / sorted(times)[len(times) // 2] / 1e6, 1), "kernel": "stream_read_kernel",
+            "note": "plain cold read of the buffer, 16-byte non-temporal loads over the whole GPU"}
 
 
 # ----------------------------------------------------------------------------- inputs
@@ -94,12 +152,13 @@ def x_f16_dev(torch, synth, seed, tag, m, k):
 
 # ----------------------------------------------------------------------------- timing helpers
 
-def time_graph(torch, fn, steps, warmup):
+def time_graph(torch, fn, steps, warmup, eager=True):
     """Capture fn() once into a graph; replay warmup + steps times; ms per replay (event timing)."""
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        fn()  # eager run before capture
+    if eager:
+        with torch.cuda.stream(stream):
+            fn()  # eager run before capture
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
@@ -118,21 +177,27 @@ def time_graph(torch, fn, steps, warmup):
     return start.elapsed_time(stop) / steps, graph
 
 
-KERNEL_SOURCES = ["ternary_group_scaled_amd/csrc/gemv.hip", "ternary_group_scaled_amd/csrc/lane_ops.h",
-                  "ternary_group_scaled_amd/csrc/rms_norm.h",
-                  "ternary_group_scaled_amd/csrc/tgs_internal.h", "ternary_group_scaled_amd/csrc/tgs_host.cpp"]
+_CSRC = "ternary_group_scaled_amd/csrc/"
+_COMMON_SOURCES = [_CSRC + "tgs_internal.h", _CSRC + "tgs_host.cpp", _CSRC + "lane_ops.h", _CSRC + "rms_norm.h"]
+# the sources each kernel's code and launch configuration come from (gemv.hip holds the GEMV plan)
+KERNEL_SOURCES = {
+    "gemv_s2_mfma_kernel": [_CSRC + "gemv_s2_mfma.hip", _CSRC + "gemv.hip"] + _COMMON_SOURCES,
+    "gemv_b3_mfma_kernel": [_CSRC + "gemv_mfma.hip", _CSRC + "gemv.hip"] + _COMMON_SOURCES,
+    "gemv_wave_kernel": [_CSRC + "gemv.hip"] + _COMMON_SOURCES,
+    "gemm": [_CSRC + "gemm.hip"] + _COMMON_SOURCES,
+}
 
 
-def kernel_source_sha():
+def kernel_source_sha(kernel):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(profile_name):
+def measured_traffic(profile_name, kernel):
     """HBM bytes per launch from a committed counter summary (profiles/<name>), or None when the
     summary is missing or was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", profile_name)
@@ -144,7 +209,7 @@ def measured_traffic(profile_name):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
-    if fields.get("source_sha256") != kernel_source_sha():
+    if fields.get("source_sha256") != kernel_source_sha(kernel):
         return None
     try:
         return {"fetch": float(fields["fetch_bytes_per_launch"]), "write": float(fields["write_bytes_per_launch"])}
@@ -157,7 +222,8 @@ def measured_traffic(profile_name):
 LAYOUT_NAME = {1: "slot2", 2: "base3", 3: "binary"}
 
 
-def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_name=None, metric=METRIC):
+def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_name=None, metric=METRIC,
+             ceiling=None):
     layers = args.layers or 36
     log(f"[bench] building {layers} layers x {len(LAYER_8B)} matrices ({LAYOUT_NAME[layout]})")
     t0 = time.time()
@@ -215,7 +281,7 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
                 fn()
 
         log(f"[bench] timing {args.steps} graph replays of {len(launches)} launches ({mode})")
-        ms_m, _graph = time_graph(torch, one_pass, args.steps, args.warmup)
+        ms_m, _graph = time_graph(torch, one_pass, args.steps, args.warmup, eager=not args.no_eager)
         del _graph
         timings[mode] = (ms_m, len(launches))
         log(f"[bench]   {mode}: step {ms_m * 1e3:.1f} us -> {total_bytes / ms_m / 1e6:.0f} GB/s, "
@@ -225,9 +291,15 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
     per_launch_bytes = total_bytes / n_launches
     per_launch_s = ms * 1e-3 / n_launches
     kernel_gbs = per_launch_bytes / per_launch_s / 1e9
-    kernel = "gemv_b3_mfma_kernel" if layout == 2 else "gemv_wave_kernel"
+    kernel = {1: "gemv_s2_mfma_kernel", 2: "gemv_b3_mfma_kernel", 3: "gemv_wave_kernel"}[layout]
     profile = f"{kernel}.8b_{LAYOUT_NAME[layout]}_m1_{args.mode}.pmc.txt"
-    traffic = measured_traffic(profile)
+    traffic = measured_traffic(profile, kernel)
+    extra = {"avg_launch_us": round(per_launch_s * 1e6, 3), "bytes_per_launch_avg": int(per_launch_bytes),
+             "traffic_profile": profile if traffic is not None else None,
+             "duration": "timed region / launches (HIP events on the replay stream; back-to-back launches)"}
+    if ceiling:
+        extra["measured_read_ceiling_gbs"] = ceiling["value"]
+        extra["frac_vs_measured"] = round(kernel_gbs / ceiling["value"], 4)
 
     result = {
         "metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -241,12 +313,8 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
         "tokens_per_s": round(1e3 / ms, 1),
         "launch_modes": {m: {"launches": t[1], "ms_per_step": round(t[0], 5), "gbs": round(total_bytes / t[0] / 1e6, 1)}
                          for m, t in timings.items()},
-        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else int(traffic["fetch"] + traffic["write"]),
-                     "kernel": kernel, "avg_launch_us": round(per_launch_s * 1e6, 3),
-                     "bytes_per_launch_avg": int(per_launch_bytes),
-                     "traffic_profile": profile if traffic is not None else None},
+        "roofline": roofline("hbm", kernel_gbs, HBM_PEAK_GBS, "GB/s", kernel,
+                             None if traffic is None else int(traffic["fetch"] + traffic["write"]), **extra),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_8b(torch, host, inputs[0], outputs[0], layout, args.cpu_seconds, ms,
@@ -259,7 +327,7 @@ def cpu_baseline_8b(torch, host, xs, ys, layout, seconds, gpu_ms, layer_bytes, l
     used, repeated for ~`seconds`. Its first pass is also compared with the GPU's layer-0 outputs
     (every row, within the tolerance bound). The oracle packs layer 0's trits itself (untimed)."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    model, threads = cpu_info()
     host = [(name, oracle.pack(layout, trits), scales, n, k) for name, trits, scales, n, k in host]
     torch.cuda.synchronize()
     y_gpu = {name: ys[name].cpu().numpy().astype(np.float64) for name, _, _, _, _ in host}
@@ -281,33 +349,136 @@ def cpu_baseline_8b(torch, host, xs, ys, layout, seconds, gpu_ms, layer_bytes, l
     dt = (time.time() - t0) / passes
     log(f"[bench] layer-0 parity against the oracle ok (max err/bound {worst:.3g})")
     layer_gbs = layer_bytes / dt / 1e9
-    return {"value": round(layer_gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(layer_gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": model,
             "sample": f"layer 0 of the set (7 matrices, {int(layer_bytes)} algorithmic bytes), {passes} passes in "
                       f"{time.time() - t0:.1f}s; full-set equivalent {1.0 / (dt * layers):.3f} steps/s",
             "gpu_speedup": round((dt * layers) / (gpu_ms * 1e-3), 1)}
 
 
+# ----------------------------------------------------------------------------- single GEMV (latency)
+
+def bench_config1(args, torch, tgs, synth):
+    """The single ternary GEMV of 256 outputs x 1024 inputs, M = 1, codes P(0) = 0.4, scales
+    |N(0, 0.02)| + 1e-4, fp16 N(0, 1) activations, seed 0, 2-bit-slot layout: the pack/unpack round
+    trip, parity against the oracle on every output, and the time of one call in a stream of
+    back-to-back calls (72,704 bytes fit the cache, so this is a latency figure)."""
+    import oracle
+    n, k = 256, 1024
+    t = synth.trits(0, synth.stream_id("config1", "codes"), (n, k), 0.4)
+    s = synth.scales_f16(0, synth.stream_id("config1", "scales"), (n, k // 128))
+    codes, scales = tgs.pack_ternary(1, t, s)
+    back, _ = tgs.unpack_ternary(1, codes, scales, k)
+    ref_codes = oracle.pack(1, t)
+    if not ((back == t).all() and (codes == ref_codes).all()):
+        raise SystemExit("config1: pack/unpack round trip or packing parity failed")
+    w = tgs.PackedMatrix(1, torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda(), k)
+    x16 = synth.x_f16(0, synth.stream_id("config1", "x"), (1, k))
+    x = torch.from_numpy(x16.view(np.int16).copy()).cuda().view(torch.float16)
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    calls = 200
+
+    def run():
+        for _ in range(calls):
+            tgs.ternary_gemv(w, x, y=y)
+
+    ms, _ = time_graph(torch, run, max(3, args.steps // 4), 1, eager=not args.no_eager)
+    us = ms * 1e3 / calls
+    y_ref, bound = oracle.matmul(1, ref_codes, s, k, x16.view(np.uint16), oracle.X_F16)
+    ratio = float((np.abs(y.cpu().numpy().astype(np.float64) - y_ref) / bound).max())
+    if not ratio <= 1.0:
+        raise SystemExit(f"config1: parity check failed (max err/bound {ratio:.3g})")
+    nbytes = codes.nbytes + scales.nbytes + 2 * k + 4 * n
+    log(f"[bench] config1 256x1024 GEMV: {us:.2f} us per call, parity ok (max err/bound {ratio:.3g})")
+    line = {"metric": "single ternary GEMV latency, 256x1024, 2-bit-slot, M=1", "value": round(us, 3), "unit": "us",
+            "higher_is_better": False, "calls_per_replay": calls, "parity_max_err_over_bound": ratio,
+            "round_trip": "pack/unpack bit-exact",
+            "config": {"workload": "single GEMV, N=256 x K=1024, groups of 128 along K, M=1, codes P(0)=0.4, "
+                                   "seed 0", "algorithmic_bytes": int(nbytes)},
+            "roofline": roofline("hbm", nbytes / us / 1e3, HBM_PEAK_GBS, "GB/s", "gemv_s2_mfma_kernel",
+                                 note="72,704 bytes fit the cache: one launch's latency bounds the call, not HBM")}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_config1(ref_codes, s, x16, k, us)
+    return line
+
+
+_CONFIG1_ORACLE_SCRIPT = """
+import sys, time
+import numpy as np
+sys.path.insert(0, {root!r})
+import oracle, synth
+n, k = 256, 1024
+t = synth.trits(0, synth.stream_id("config1", "codes"), (n, k), 0.4)
+s = synth.scales_f16(0, synth.stream_id("config1", "scales"), (n, k // 128))
+x = synth.x_f16(0, synth.stream_id("config1", "x"), (1, k)).view(np.uint16)
+codes = oracle.pack(1, t)
+oracle.matmul(1, codes, s, k, x, oracle.X_F16)
+t0, calls = time.time(), 0
+while time.time() - t0 < {seconds}:
+    oracle.matmul(1, codes, s, k, x, oracle.X_F16)
+    calls += 1
+print((time.time() - t0) / calls * 1e6)
+"""
+
+
+def cpu_baseline_config1(codes, s, x16, k, gpu_us, seconds=2.0):
+    """The oracle on the whole config-1 GEMV, on all host threads and (in a child process with
+    OMP_NUM_THREADS=1) on one."""
+    import subprocess
+
+    import oracle
+    model, threads = cpu_info()
+    xb = x16.view(np.uint16)
+    oracle.matmul(1, codes, s, k, xb, oracle.X_F16)
+    t0, calls = time.time(), 0
+    while time.time() - t0 < seconds:
+        oracle.matmul(1, codes, s, k, xb, oracle.X_F16)
+        calls += 1
+    us = (time.time() - t0) / calls * 1e6
+    single = None
+    try:
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        out = subprocess.run([sys.executable, "-c", _CONFIG1_ORACLE_SCRIPT.format(root=ROOT, seconds=seconds)],
+                             env=env, capture_output=True, text=True, timeout=120)
+        single = round(float(out.stdout.strip().splitlines()[-1]), 2)
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        single = None
+    return {"value": round(us, 2), "unit": "us", "cores": threads, "kind": "oracle", "cpu": model,
+            "single_thread_us": single,
+            "sample": f"the whole config-1 GEMV, {calls} calls in {seconds:.0f}s on {threads} threads; one thread "
+                      f"in a child process",
+            "gpu_speedup": round(us / gpu_us, 1)}
+
+
 # ----------------------------------------------------------------------------- other workloads
 
 def bench_rotated(args, torch, tgs, synth):
-    """27B-class rotated-basis GEMV, base-3: gate/up 17408x5120 and down 5120x17408 per layer."""
+    """27B-class rotated-basis GEMV, base-3: gate/up 17408x5120 and down 5120x17408 per layer, 64
+    layers (3.69 GB), M in {1, 8}. Fused: the rotation runs inside the GEMV (two launches per layer,
+    gate/up sharing their input and signs). Two passes: hadamard_rotate of each input once (fp16),
+    then the plain-basis GEMV on descriptors of the same code buffers. Layer 0's gate and down outputs
+    are checked against the oracle on sampled rows."""
     layers = args.layers or 64
     block = args.rot_block
     shapes = [("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408)]
     res = []
     for m in (1, 8):
         log(f"[bench] rotated base-3 set, {layers} layers, m={m}, rotation block {block}")
-        mats, xs, ys, sg = [], [], [], {}
+        mats, xs, ys, sg, host = [], [], [], {}, {}
         for k in (5120, 17408):
             sg[k] = torch.from_numpy(synth.signs(0, synth.stream_id("rot/signs", k), k)).cuda()
         for L in range(layers):
             for name, n, k in shapes:
-                w, _, _ = build_matrix(torch, tgs, synth, 2, 0, f"rot/L{L}/{name}", n, k, 0.5, rotated=block)
+                w, t, s = build_matrix(torch, tgs, synth, 2, 0, f"rot/L{L}/{name}", n, k, 0.5, rotated=block)
                 mats.append(w)
                 ys.append(torch.empty((m, n), dtype=torch.float32, device="cuda"))
-            xg = x_f16_dev(torch, synth, 0, f"rot/L{L}/in{m}", m, 5120)[0]
-            xd = x_f16_dev(torch, synth, 0, f"rot/L{L}/mid{m}", m, 17408)[0]
+                if L == 0 and name in ("gate", "down"):
+                    host[name] = (t, s, n, k)
+            xg, xg16 = x_f16_dev(torch, synth, 0, f"rot/L{L}/in{m}", m, 5120)
+            xd, xd16 = x_f16_dev(torch, synth, 0, f"rot/L{L}/mid{m}", m, 17408)
             xs += [xg, xg, xd]
+            if L == 0:
+                host["gate"] += (xg16,)
+                host["down"] += (xd16,)
         nb = sum(w.nbytes for w in mats) + sum(x.numel() * 2 for x in xs[::3]) + sum(
             x.numel() * 2 for x in xs[2::3]) + sum(y.numel() * 4 for y in ys)
         launches = []
@@ -322,8 +493,9 @@ def bench_rotated(args, torch, tgs, synth):
             for fn in launches:
                 fn()
 
-        ms, _ = time_graph(torch, one_pass, args.steps, args.warmup)
+        ms, _ = time_graph(torch, one_pass, args.steps, args.warmup, eager=not args.no_eager)
         log(f"[bench] rotated m={m}: step {ms * 1e3:.1f} us -> {nb / ms / 1e6:.0f} GB/s")
+        y_gate, y_down = ys[0].cpu().numpy(), ys[2].cpu().numpy()
 
         # the same products in two passes: hadamard_rotate of each input once (fp16 out), then the
         # plain-basis GEMV on descriptors of the same code buffers (the rotation is not repeated by
@@ -346,32 +518,80 @@ def bench_rotated(args, torch, tgs, synth):
             for fn in two:
                 fn()
 
-        ms2, _ = time_graph(torch, two_pass, args.steps, args.warmup)
+        ms2, _ = time_graph(torch, two_pass, args.steps, args.warmup, eager=not args.no_eager)
         log(f"[bench] rotated m={m}, two passes: step {ms2 * 1e3:.1f} us -> {nb / ms2 / 1e6:.0f} GB/s")
-        res.append({"metric": "rotated ternary GEMV achieved GB/s, 27B-class set", "value": round(nb / ms / 1e6, 1),
-                    "unit": "GB/s", "m": m, "ms_per_step": round(ms, 4), "launches_per_step": len(launches),
-                    "two_pass": {"gbs": round(nb / ms2 / 1e6, 1), "ms_per_step": round(ms2, 4),
-                                 "launches_per_step": len(two)},
-                    "config": {"workload": f"27B-class rotated GEMV set, base-3, {layers} layers, M={m}, "
-                                           f"rotation block {block}",
-                               "bytes_per_step": int(nb)}})
+        gbs = nb / ms / 1e6
+        line = {"metric": "rotated ternary GEMV achieved GB/s, 27B-class set", "value": round(gbs, 1),
+                "unit": "GB/s", "m": m, "ms_per_step": round(ms, 4), "launches_per_step": len(launches),
+                "tokens_per_s": round(m * 1e3 / ms, 1), "dtype": "f16",
+                "two_pass": {"gbs": round(nb / ms2 / 1e6, 1), "ms_per_step": round(ms2, 4),
+                             "launches_per_step": len(two)},
+                "config": {"workload": f"27B-class rotated GEMV set, base-3, {layers} layers, M={m}, "
+                                       f"rotation block {block}",
+                           "bytes_per_step": int(nb)},
+                "roofline": roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", "gemv_b3_mfma_kernel",
+                                     avg_launch_us=round(ms * 1e3 / len(launches), 2),
+                                     note="fused path; the two-pass schedule is reported beside it")}
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_rotated(host, {"gate": y_gate, "down": y_down}, sg, block, m,
+                                                        gbs)
+        res.append(line)
         del mats, xs, ys, plain, xr
         torch.cuda.empty_cache()
     return res
 
 
+def cpu_baseline_rotated(host, y_gpu, sg, block, m, gpu_gbs, seconds=2.0):
+    """The oracle on sampled rows of layer 0's gate (K = 5120) and down (K = 17408) projections with
+    the rotation, repeated for about `seconds`; the GPU's outputs at those rows are checked against it."""
+    import oracle
+    model, threads = cpu_info()
+    jobs = []
+    for name in ("gate", "down"):
+        t, s, n, k, x16 = host[name]
+        rows = np.unique(np.linspace(0, n - 1, 256).astype(np.int64))
+        codes = oracle.pack(2, t)
+        signs = sg[k].cpu().numpy()
+        y_ref, bound = oracle.matmul(2, codes, s, k, x16.view(np.uint16), oracle.X_F16, signs=signs, rows=rows,
+                                     block=block)
+        ratio = float((np.abs(y_gpu[name][:, rows].astype(np.float64) - y_ref) / bound).max())
+        if not ratio <= 1.0:
+            raise SystemExit(f"rotated {name} m={m}: parity check failed on sampled rows (max err/bound {ratio:.3g})")
+        nbytes = rows.size * (oracle.row_bytes(2, k) + k // 64) + m * k * 2 + m * rows.size * 4
+        jobs.append((codes, s, k, x16, signs, rows, nbytes))
+    t0, passes = time.time(), 0
+    while True:
+        for codes, s, k, x16, signs, rows, _ in jobs:
+            oracle.matmul(2, codes, s, k, x16.view(np.uint16), oracle.X_F16, signs=signs, rows=rows, block=block)
+        passes += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = (time.time() - t0) / passes
+    nbytes = sum(j[6] for j in jobs)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": model,
+            "sample": f"256 sampled rows each of layer 0's gate and down projections, M={m}, rotation included, "
+                      f"{passes} passes in {time.time() - t0:.1f}s; the GPU's outputs at those rows within the bound",
+            "gpu_speedup": round(gpu_gbs / (nbytes / dt / 1e9), 1)}
+
+
 def bench_gemm(args, torch, tgs, synth):
     """27B-class prefill GEMM (slot-2, or binary codes): gate/up 17408x5120 and down 5120x17408, M in
-    {16, 128, 2048}. With --gemm-rot-block the weights are in the rotated basis: every product first
+    {16, 128, 2048}. 16 distinct weight copies per shape (379 MB, beyond the last-level cache) run
+    back to back. With --gemm-rot-block the weights are in the rotated basis: every product first
     rotates its fp16 activations into a bf16 buffer (hadamard_rotate), then multiplies that buffer
     with a plain-basis descriptor of the same codes; the line reports both launches together and
-    the rotation alone."""
+    the rotation alone. Each point is checked against the oracle on sampled output rows."""
+    import oracle
     res = []
     copies = 16
     rot = args.gemm_rot_block
     layout, p_zero = (3, 0.0) if args.gemm_layout == "binary" else (1, 0.4)
     for n, k in ((17408, 5120), (5120, 17408)):
-        ws = [build_matrix(torch, tgs, synth, layout, 0, f"gemm/{n}x{k}/{i}", n, k, p_zero)[0] for i in range(copies)]
+        w0, t0, s0 = build_matrix(torch, tgs, synth, layout, 0, f"gemm/{n}x{k}/0", n, k, p_zero)
+        ws = [w0] + [build_matrix(torch, tgs, synth, layout, 0, f"gemm/{n}x{k}/{i}", n, k, p_zero)[0]
+                     for i in range(1, copies)]
+        ref_codes = oracle.pack(layout, t0)
+        del t0
         for m in (16, 128, 2048):
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
             if rot:
@@ -390,28 +610,69 @@ def bench_gemm(args, torch, tgs, synth):
                 for fn in launches:
                     fn()
 
-            ms, _ = time_graph(torch, one_pass, max(2, args.steps // 4), 1)
+            ms, _ = time_graph(torch, one_pass, max(2, args.steps // 4), 1, eager=not args.no_eager)
             per = ms / copies
             flops = 2.0 * m * n * k
             nb = ws[0].nbytes + m * k * 2 + m * n * 4
-            line = {"metric": "ternary GEMM TFLOP/s", "value": round(flops / per / 1e9, 2), "unit": "TFLOP/s",
-                    "pct_of_bf16_peak": round(100 * flops / per / 1e9 / BF16_MFMA_PEAK_TFLOPS, 2),
-                    "gbs": round(nb / per / 1e6, 1), "us": round(per * 1e3, 2),
+            tflops = flops / per / 1e9
+            gbs = nb / per / 1e6
+            bound = "hbm" if m <= 16 else "mfma"
+            if bound == "hbm":
+                rl = roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", "gemm_skinny_kernel", avg_launch_us=round(per * 1e3, 2),
+                              note="about 114 flop per byte at M=16, below the bf16 ridge of about 312")
+            else:
+                rl = roofline("mfma", tflops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s", "gemm_tile_kernel",
+                              avg_launch_us=round(per * 1e3, 2), dtype_peak="bf16 dense MFMA")
+            line = {"metric": "ternary GEMM TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s",
+                    "pct_of_bf16_peak": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 2),
+                    "gbs": round(gbs, 1), "us": round(per * 1e3, 2), "dtype": "bf16",
                     "config": {"workload": f"27B-class prefill GEMM {n}x{k}, M={m}, {LAYOUT_NAME[layout]}"
-                                           + (f", rotated basis ({rot}-blocks, rotation + GEMM)" if rot else "")}}
+                                           + (f", rotated basis ({rot}-blocks, rotation + GEMM)" if rot else ""),
+                               "weight_copies": copies, "flops_per_launch": int(flops), "bytes_per_launch": int(nb)},
+                    "roofline": rl}
             if rot:
                 def rotations():
                     for _ in range(copies):
                         rotate()
 
-                rms, _ = time_graph(torch, rotations, max(2, args.steps // 4), 1)
+                rms, _ = time_graph(torch, rotations, max(2, args.steps // 4), 1, eager=not args.no_eager)
                 line["rotate_us"] = round(rms / copies * 1e3, 2)
+            elif not args.no_cpu_baseline:
+                # the last replay wrote y with copy 15; recompute copy 0's product for the parity sample
+                tgs.ternary_gemm(ws[0], x, y)
+                torch.cuda.synchronize()
+                line["cpu_baseline"] = cpu_baseline_gemm(layout, ref_codes, s0, k, xb, y.cpu().numpy(), m, n, tflops)
             res.append(line)
             log(f"[bench] gemm {n}x{k} m={m}{' rot ' + str(rot) if rot else ''}: {per * 1e3:.1f} us, "
-                f"{flops / per / 1e9:.1f} TFLOP/s" + (f" (rotation {line['rotate_us']} us)" if rot else ""))
+                f"{tflops:.1f} TFLOP/s" + (f" (rotation {line['rotate_us']} us)" if rot else ""))
         del ws
         torch.cuda.empty_cache()
     return res
+
+
+def cpu_baseline_gemm(layout, codes, s, k, xb, y_gpu, m, n, gpu_tflops, seconds=1.0):
+    """The oracle on a sample of output rows (first, last and evenly spaced ones), repeated for about
+    `seconds`; the GPU's outputs at those rows are checked against it."""
+    import oracle
+    model, threads = cpu_info()
+    count = max(2, min(n, int(4e8 / (m * k))))
+    rows = np.unique(np.linspace(0, n - 1, count).astype(np.int64))
+    y_ref, bound = oracle.matmul(layout, codes, s, k, xb.view(np.uint16), oracle.X_BF16, rows=rows)
+    ratio = float((np.abs(y_gpu[:, rows].astype(np.float64) - y_ref) / bound).max())
+    if not ratio <= 1.0:
+        raise SystemExit(f"gemm {n}x{k} m={m}: parity check failed on sampled rows (max err/bound {ratio:.3g})")
+    t0, calls = time.time(), 0
+    while True:
+        oracle.matmul(layout, codes, s, k, xb.view(np.uint16), oracle.X_BF16, rows=rows)
+        calls += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = (time.time() - t0) / calls
+    tflops = 2.0 * m * k * rows.size / dt / 1e12
+    return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu": model,
+            "sample": f"{rows.size} of {n} output rows at M={m}, {calls} passes in {time.time() - t0:.1f}s; "
+                      f"the GPU's outputs at those rows within the bound (max err/bound {ratio:.3g})",
+            "gpu_speedup": round(gpu_tflops / tflops, 1)}
 
 
 def bench_rmsnorm(args, torch, tgs, synth):
@@ -520,9 +781,7 @@ def bench_flips(args, torch, tgs, synth):
                            "layers": layers, "pairs": len(pairs), "launches_per_step": len(launches),
                            "bytes_per_step": int(code_bytes + out_bytes), "flips": counted},
                 "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-                "roofline": {"bound": "hbm" if layout == 1 else "alu", "achieved": round(gbs, 1),
-                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                             "kernel": "code_flip_kernel"}}
+                "roofline": roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", "code_flip_kernel")}
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_flips(torch, host0, rows[:len(host0)], layout, args.cpu_seconds,
                                                       ms, len(pairs))
@@ -557,6 +816,11 @@ def cpu_baseline_flips(torch, host0, rows0, layout, seconds, gpu_ms, n_pairs):
             "gpu_speedup": round((dt * n_pairs / len(host0)) / (gpu_ms * 1e-3), 1)}
 
 
+def nested(line):
+    """A workload's line as an entry of the combined line (without the run-wide fields)."""
+    return {k: v for k, v in line.items() if k not in ("n_gpus", "steps", "warmup", "scaling", "vs_baseline", "data")}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -570,17 +834,39 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    if args.copy_mib:
-        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+    if args.stream_gib:
+        buf = torch.empty(args.stream_gib << 30, dtype=torch.uint8, device="cuda")
+        tgs.stream_read(buf)
         torch.cuda.synchronize()
-        del src, dst
-    if args.workload == "8b":
+        del buf
+    if args.workload == "all":
+        t_start = time.time()
+        ceiling = stream_read_ceiling(torch, tgs)
+        head = bench_8b(args, torch, tgs, synth, ceiling=ceiling)
+        torch.cuda.empty_cache()
+        configs = {"config1_gemv_256x1024": nested(bench_config1(args, torch, tgs, synth))}
+        saved = args.cpu_seconds
+        args.cpu_seconds = min(saved, 5.0)
+        configs["config3_base3_set"] = nested(bench_8b(
+            args, torch, tgs, synth, layout=2, p_zero=0.5, tag="8b3",
+            workload_name="8B-class decode GEMV set, base-3 layout, M=1",
+            metric="base-3 ternary GEMV achieved HBM GB/s (% of peak), 8B-class set, M=1", ceiling=ceiling))
+        args.cpu_seconds = saved
+        torch.cuda.empty_cache()
+        configs["config4_gemm"] = [nested(x) for x in bench_gemm(args, torch, tgs, synth)]
+        configs["config5_rotated"] = [nested(x) for x in bench_rotated(args, torch, tgs, synth)]
+        head["stream_read"] = ceiling
+        head["configs"] = configs
+        head["wall_s"] = round(time.time() - t_start, 1)
+        out = [head]
+    elif args.workload == "8b":
         out = [bench_8b(args, torch, tgs, synth)]
+    elif args.workload == "config1":
+        out = [bench_config1(args, torch, tgs, synth)]
     elif args.workload == "base3":
         out = [bench_8b(args, torch, tgs, synth, layout=2, p_zero=0.5, tag="8b3",
-                        workload_name="8B-class decode GEMV set, base-3 layout, M=1")]
+                        workload_name="8B-class decode GEMV set, base-3 layout, M=1",
+                        metric="base-3 ternary GEMV achieved HBM GB/s (% of peak), 8B-class set, M=1")]
     elif args.workload == "binary":
         out = [bench_8b(args, torch, tgs, synth, layout=3, p_zero=0.0, tag="8bb",
                         workload_name="8B-class decode GEMV set, binary layout (t in {-1, +1}), M=1",
@@ -594,8 +880,7 @@ def main():
     elif args.workload == "rmsnorm":
         out = bench_rmsnorm(args, torch, tgs, synth)
     else:
-        args.layers = 1
-        out = [bench_8b(args, torch, tgs, synth)]
+        out = [stream_read_ceiling(torch, tgs)]
     for line in out:
         print(json.dumps(line), flush=True)
 

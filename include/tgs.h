@@ -292,6 +292,21 @@ tgs_status rmsnorm_hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, in
                                    const uint16_t* gamma, float eps, const int8_t* signs, void* y,
                                    int32_t y_dtype, void* stream);
 
+/*
+ * Measurement helpers (not part of the product; for measuring the rooflines the kernels are
+ * compared with).
+ *
+ * tgs_stream_read (device): read `bytes` of device memory once, as the plainest streaming kernel
+ * can (16-byte non-temporal loads over the whole GPU), folding the data into one word per thread,
+ * written to sink. Timing it on a buffer far larger than the last-level cache gives the read
+ * bandwidth a kernel can actually reach, next to the nominal HBM peak.
+ *   buf    device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink   device uint32 [tgs_stream_read_sink_words()], 4-byte aligned; its contents are not
+ *          meaningful
+ */
+size_t tgs_stream_read_sink_words(void);
+tgs_status tgs_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* tgs_status_string(tgs_status status);
 

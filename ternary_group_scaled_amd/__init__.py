@@ -74,6 +74,10 @@ for _name in ("tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv
               "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
               "rmsnorm_hadamard_rotate"):
     getattr(_lib, _name).restype = ctypes.c_int
+_lib.tgs_stream_read_sink_words.argtypes = []
+_lib.tgs_stream_read_sink_words.restype = _sz
+_lib.tgs_stream_read.argtypes = [_vp, _sz, _vp, _vp]
+_lib.tgs_stream_read.restype = ctypes.c_int
 _lib.tgs_status_string.argtypes = [ctypes.c_int]
 _lib.tgs_status_string.restype = ctypes.c_char_p
 _lib.tgs_last_error.argtypes = []
@@ -82,7 +86,8 @@ _lib.tgs_last_error.restype = ctypes.c_char_p
 EXPORTS = ("tgs_code_row_bytes", "tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv",
            "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
            "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
-           "rmsnorm_hadamard_rotate", "tgs_status_string", "tgs_last_error")
+           "rmsnorm_hadamard_rotate", "tgs_stream_read_sink_words", "tgs_stream_read", "tgs_status_string",
+           "tgs_last_error")
 
 
 def _check(status: int):
@@ -431,3 +436,18 @@ def ternary_code_flips_batched(pairs, totals, rows=None, stream=None):
         rp = (_vp * count)(*[r.data_ptr() if r is not None else None for r in rows])
     _check(_lib.ternary_code_flips_batched(da, db, count, rp, tp, _stream_handle(stream)))
     return totals, rows
+
+
+def stream_read(buf, sink=None, stream=None):
+    """Read the whole device tensor `buf` once (the streaming-read probe); returns the sink tensor."""
+    torch = _torch()
+    if buf is None or not buf.is_contiguous() or buf.numel() * buf.element_size() % 16 != 0:
+        _raise("TGS_E_SHAPE", "buf must be a contiguous tensor of a multiple of 16 bytes")
+    words = int(_lib.tgs_stream_read_sink_words())
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", (torch.int32,), min_numel=words)
+    _on_device(buf.device, buf=buf, sink=sink)
+    _check(_lib.tgs_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                _stream_handle(stream)))
+    return sink

@@ -518,6 +518,17 @@ tgs_status hadamard_rotate_g128(const void* x, int32_t x_dtype, int64_t m, int64
   return hadamard_rotate(x, x_dtype, m, k, 128, signs, y, y_dtype, stream);
 }
 
+size_t tgs_stream_read_sink_words(void) { return (size_t)tgs::stream_read_grid() * 256; }
+
+tgs_status tgs_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(TGS_E_NULL, "buf or sink is NULL");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(TGS_E_ALIGN, "buf must be 16-byte and sink 4-byte aligned");
+  if (bytes < 16 || bytes % 16 != 0) return fail(TGS_E_SHAPE, "bytes must be a positive multiple of 16");
+  hipError_t e = tgs::stream_read_launch(buf, (uint64_t)bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "tgs_stream_read launch");
+  return ok();
+}
+
 const char* tgs_status_string(tgs_status status) {
   switch (status) {
     case TGS_OK: return "ok";

@@ -147,6 +147,10 @@ hipError_t rmsnorm_hadamard_launch(const void* x, int32_t x_dtype, int64_t m, in
                                    const uint16_t* gamma, float eps, const int8_t* signs, void* y, int32_t y_dtype,
                                    hipStream_t stream);
 
+// streaming-read probe: workgroups of 256 threads in the launch, and the launch
+int stream_read_grid();
+hipError_t stream_read_launch(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // rotation block of a descriptor's `rotated` field: 0 (plain basis), 128 or 1024
 inline int64_t rotation_block(int32_t rotated) { return rotated == 0 ? 0 : (rotated == 1024 ? 1024 : 128); }
 
