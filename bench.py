@@ -63,9 +63,11 @@ def parse():
                              "stream"])
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the set (default: 36 for the 8B-class sets, 64 for the rotated 27B-class set)")
-    ap.add_argument("--mode", default="layer", choices=["layer", "fused-layer", "set"],
-                    help="launch grouping for the 8B set: same-input groups (144 launches), one launch per "
-                         "layer (36), or the whole set in as few launches as possible")
+    ap.add_argument("--mode", default="layer", choices=["chain", "layer", "fused-layer", "set"],
+                    help="launch grouping for the 8B set: the step chain in layer order (each step reads the "
+                         "previous step's output; 16 steps per launch, 9 launches; slot-2 only), same-input "
+                         "groups (144 launches), one launch per layer (36), or the whole set in as few launches "
+                         "as possible (independent matrices: the multi-matrix upper bound)")
     ap.add_argument("--gemm-layout", default="slot2", choices=["slot2", "binary"],
                     help="code layout of the GEMM workload")
     ap.add_argument("--gemm-rot-block", type=int, default=0, choices=[0, 128, 1024],
@@ -181,7 +183,8 @@ _CSRC = "ternary_group_scaled_amd/csrc/"
 _COMMON_SOURCES = [_CSRC + "tgs_internal.h", _CSRC + "tgs_host.cpp", _CSRC + "lane_ops.h", _CSRC + "rms_norm.h"]
 # the sources each kernel's code and launch configuration come from (gemv.hip holds the GEMV plan)
 KERNEL_SOURCES = {
-    "gemv_s2_mfma_kernel": [_CSRC + "gemv_s2_mfma.hip", _CSRC + "gemv.hip"] + _COMMON_SOURCES,
+    "gemv_s2_mfma_kernel": [_CSRC + "gemv_s2_mfma.hip", _CSRC + "s2_mfma.h", _CSRC + "gemv.hip"] + _COMMON_SOURCES,
+    "gemv_chain_kernel": [_CSRC + "gemv_chain.hip", _CSRC + "s2_mfma.h"] + _COMMON_SOURCES,
     "gemv_b3_mfma_kernel": [_CSRC + "gemv_mfma.hip", _CSRC + "gemv.hip"] + _COMMON_SOURCES,
     "gemv_wave_kernel": [_CSRC + "gemv.hip"] + _COMMON_SOURCES,
     "gemm": [_CSRC + "gemm.hip"] + _COMMON_SOURCES,
@@ -271,8 +274,17 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
     modes = {"layer": [group_launch(L, g) for L in range(layers) for g in GROUPS_8B],
              "fused-layer": batched_launches(len(LAYER_8B)),
              "set": batched_launches(tgs.MAX_BATCH)}
+    all_modes = ["layer", "fused-layer", "set"]
+    chain = None
+    if layout == 1:
+        chain = chain_steps_8b(torch, tgs, synth, mats, inputs, outputs, layers)
+        wsp = tgs.chain_workspace()
+        modes["chain"] = [(lambda part: lambda: tgs.ternary_gemv_chain(part, wsp))(chain[i:i + tgs.CHAIN_MAX_STEPS])
+                          for i in range(0, len(chain), tgs.CHAIN_MAX_STEPS)]
+        all_modes = ["chain"] + all_modes
+    mode = args.mode if args.mode in modes else "layer"
     timings = {}
-    timed_modes = [args.mode] + [m for m in ("layer", "fused-layer", "set") if m != args.mode and not args.one_mode]
+    timed_modes = [mode] + [m for m in all_modes if m != mode and not args.one_mode]
     for mode in timed_modes:
         launches = modes[mode]
 
@@ -286,13 +298,17 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
         timings[mode] = (ms_m, len(launches))
         log(f"[bench]   {mode}: step {ms_m * 1e3:.1f} us -> {total_bytes / ms_m / 1e6:.0f} GB/s, "
             f"{ms_m * 1e3 / len(launches):.2f} us per launch")
-    ms, n_launches = timings[args.mode]
+    ms, n_launches = timings[mode]
+    if mode == "chain":
+        chain_parity_check(tgs, torch, chain, wsp, host_chain_of(host, chain))
     gbs = total_bytes / (ms * 1e-3) / 1e9
     per_launch_bytes = total_bytes / n_launches
     per_launch_s = ms * 1e-3 / n_launches
     kernel_gbs = per_launch_bytes / per_launch_s / 1e9
     kernel = {1: "gemv_s2_mfma_kernel", 2: "gemv_b3_mfma_kernel", 3: "gemv_wave_kernel"}[layout]
-    profile = f"{kernel}.8b_{LAYOUT_NAME[layout]}_m1_{args.mode}.pmc.txt"
+    if mode == "chain":
+        kernel = "gemv_chain_kernel"
+    profile = f"{kernel}.8b_{LAYOUT_NAME[layout]}_m1_{mode}.pmc.txt"
     traffic = measured_traffic(profile, kernel)
     extra = {"avg_launch_us": round(per_launch_s * 1e6, 3), "bytes_per_launch_avg": int(per_launch_bytes),
              "traffic_profile": profile if traffic is not None else None,
@@ -307,7 +323,7 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": workload_name or "8B-class decode GEMV set, 2-bit-slot layout, M=1",
                    "layers": layers, "matrices": layers * len(LAYER_8B), "launches_per_step": n_launches,
-                   "launch_mode": args.mode, "p_zero": p_zero, "algorithmic_bytes_per_step": int(total_bytes),
+                   "launch_mode": mode, "p_zero": p_zero, "algorithmic_bytes_per_step": int(total_bytes),
                    "weight_bytes_per_step": int(w_bytes)},
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(1e3 / ms, 1),
@@ -317,9 +333,69 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
                              None if traffic is None else int(traffic["fetch"] + traffic["write"]), **extra),
     }
     if not args.no_cpu_baseline:
+        for fn in modes["layer"][:len(GROUPS_8B)]:  # layer 0 on its own inputs, for the oracle comparison
+            fn()
         result["cpu_baseline"] = cpu_baseline_8b(torch, host, inputs[0], outputs[0], layout, args.cpu_seconds, ms,
                                                  total_bytes / layers, layers)
     return result
+
+
+def chain_steps_8b(torch, tgs, synth, mats, inputs, outputs, layers):
+    """The 144 steps of a pass in layer order, each reading the output of the step before it: q/k/v
+    the RMS-normalised layer input (layer 0: the external fp16 input; later layers: the output of
+    the previous layer's down projection), o the output of q, gate/up the RMS-normalised output of o,
+    down the output of gate. Norm weights bf16 1 + N(0, 0.25^2), eps 1e-6."""
+    def gamma(tag):
+        g = synth.bf16_bits(1.0 + 0.25 * synth.normal(0, synth.stream_id("chain8b", tag), (4096,)))
+        return torch.from_numpy(g.view(np.int16).copy()).cuda()
+
+    g_in, g_post = gamma("input_norm"), gamma("post_norm")
+    flat = lambda L, nm: outputs[L][nm].view(-1)
+    steps = []
+    for L in range(layers):
+        x_in = inputs[0][("q", "k", "v")][0].view(-1) if L == 0 else flat(L - 1, "down")
+        steps.append({"ws": [mats[L][nm] for nm in ("q", "k", "v")], "x": x_in,
+                      "ys": [flat(L, nm) for nm in ("q", "k", "v")], "gamma": g_in, "eps": 1e-6})
+        steps.append({"ws": [mats[L]["o"]], "x": flat(L, "q"), "ys": [flat(L, "o")]})
+        steps.append({"ws": [mats[L]["gate"], mats[L]["up"]], "x": flat(L, "o"),
+                      "ys": [flat(L, "gate"), flat(L, "up")], "gamma": g_post, "eps": 1e-6})
+        steps.append({"ws": [mats[L]["down"]], "x": flat(L, "gate"), "ys": [flat(L, "down")]})
+    return steps
+
+
+def host_chain_of(host, chain):
+    """Layer 0's oracle inputs for the chain check: for each of its 4 steps, (codes, scales, k) of
+    each matrix, packed by the oracle from the trits."""
+    import oracle
+    by_name = {name: (oracle.pack(1, trits), scales, k) for name, trits, scales, n, k in host}
+    names = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    return [[by_name[nm] for nm in grp] for grp in names]
+
+
+def chain_parity_check(tgs, torch, chain, wsp, host_steps, rows_per_matrix=64):
+    """Run the chain once more and check layer 0's four steps against the oracle on sampled rows of
+    every matrix, each from the fp16 rounding of the input the GPU actually read (for o, gate/up and
+    down: the GPU's output of the step before)."""
+    import oracle
+    for i in range(0, len(chain), tgs.CHAIN_MAX_STEPS):
+        tgs.ternary_gemv_chain(chain[i:i + tgs.CHAIN_MAX_STEPS], wsp)
+    torch.cuda.synchronize()
+    if int(wsp[-1].item()) != 0:
+        raise SystemExit("chain: a wait between steps gave up (error word set)")
+    worst = 0.0
+    for i, grp in enumerate(host_steps):
+        st = chain[i]
+        x16 = st["x"].float().cpu().numpy().reshape(1, -1).astype(np.float16)
+        gbits = st["gamma"].cpu().numpy().view(np.uint16) if "gamma" in st else None
+        for (codes, scales, k), w, y in zip(grp, st["ws"], st["ys"]):
+            rows = np.unique(np.linspace(0, w.n - 1, rows_per_matrix).astype(np.int64))
+            y_ref, bound = oracle.matmul(1, codes, scales, k, x16.view(np.uint16), oracle.X_F16, rows=rows,
+                                         gamma=gbits, eps=st.get("eps", 0.0))
+            ratio = float((np.abs(y.cpu().numpy()[rows].astype(np.float64) - y_ref[0]) / bound[0]).max())
+            if not ratio <= 1.0:
+                raise SystemExit(f"chain step {i}: parity check failed (max err/bound {ratio:.3g})")
+            worst = max(worst, ratio)
+    log(f"[bench] chain: layer-0 steps against the oracle ok on sampled rows (max err/bound {worst:.3g})")
 
 
 def cpu_baseline_8b(torch, host, xs, ys, layout, seconds, gpu_ms, layer_bytes, layers):

@@ -293,6 +293,52 @@ tgs_status rmsnorm_hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, in
                                    int32_t y_dtype, void* stream);
 
 /*
+ * ternary_gemv_chain (device): up to TGS_CHAIN_MAX_STEPS single-token GEMV steps run in order by
+ * one launch. Step s computes, for each of its matrices i,
+ *   y_i[j] = sum_k s_i[j][k/128] * t_i[j][k] * xh[k],
+ * where xh is the step's input x in fp16 (an fp32 input is rounded to fp16, to nearest even),
+ * RMS-normalised first when norm is set (xh <- gamma * xh / sqrt(mean xh^2 + eps), as in
+ * ternary_gemv_rmsnorm): exactly what ternary_gemv (or ternary_gemv_rmsnorm) computes on that
+ * fp16 vector ([P3] "Group-scaled ternary format"). Step s multiplies only after step s - 1 is
+ * complete, so a step may read the output of any earlier step (an fp32 y, converted on the way in):
+ * the steps of a decode pass in layer order ([P3] "Throughput: the two packings swap order by
+ * hardware": batch-1 decode pays for every launch). The weights of step s are read while the
+ * launch waits for step s - 1.
+ *   steps      host array of count step descriptors (1 <= count <= TGS_CHAIN_MAX_STEPS)
+ *     .count   matrices sharing the step's input, 1..TGS_CHAIN_MAX_MATRICES
+ *     .x_dtype TGS_F16 or TGS_F32; .x device [k], 16-byte aligned
+ *     .norm    0 or 1; with 1, .gamma device [k] bf16 bits (16-byte aligned) and .eps > 0, finite
+ *     .w[i]    descriptors of device matrices: TGS_LAYOUT_SLOT2, plain basis, one k per step with
+ *              k % 512 == 0 and k <= 16384; at most 16 * 16 * (compute units) rows in a step
+ *     .y[i]    device [n_i] fp32, 4-byte aligned; must not overlap any step's input or weights
+ *   workspace  device uint32 [tgs_chain_workspace_bytes() / 4], 4-byte aligned, zero-filled by the
+ *              caller before its first use. A chain leaves it consistent for the next chain on the
+ *              same device (its words count completed steps); it must be zero-filled again after a
+ *              call whose error word (the last word) came back nonzero. Calls that use one
+ *              workspace must not run concurrently.
+ * The launch needs every compute unit (one workgroup each). Each wait between steps is bounded:
+ * if the workgroups cannot all run at once (another kernel holds compute units), the waits give
+ * up, the outputs are garbage and the workspace's last word becomes nonzero.
+ */
+#define TGS_CHAIN_MAX_STEPS 16
+#define TGS_CHAIN_MAX_MATRICES 3
+typedef struct tgs_chain_step {
+  int32_t count;
+  int32_t x_dtype;
+  int32_t norm;
+  float eps;
+  const void* x;
+  const uint16_t* gamma;
+  tgs_matrix w[TGS_CHAIN_MAX_MATRICES];
+  float* y[TGS_CHAIN_MAX_MATRICES];
+} tgs_chain_step;
+
+/* Bytes of the chain workspace on the current device (0 if no device is usable). */
+size_t tgs_chain_workspace_bytes(void);
+tgs_status ternary_gemv_chain(const tgs_chain_step* steps, int32_t count, uint32_t* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Measurement helpers (not part of the product; for measuring the rooflines the kernels are
  * compared with).
  *

@@ -44,6 +44,17 @@ class Matrix(ctypes.Structure):
                 ("code_row_stride", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
+CHAIN_MAX_STEPS = 16
+CHAIN_MAX_MATRICES = 3
+
+
+class ChainStep(ctypes.Structure):
+    """ctypes mirror of tgs_chain_step."""
+    _fields_ = [("count", ctypes.c_int32), ("x_dtype", ctypes.c_int32), ("norm", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("x", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("w", Matrix * CHAIN_MAX_MATRICES), ("y", ctypes.c_void_p * CHAIN_MAX_MATRICES)]
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python ternary_group_scaled_amd/build.py` "
                       "(or __graft_entry__.build()) first")
@@ -74,6 +85,10 @@ for _name in ("tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv
               "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
               "rmsnorm_hadamard_rotate"):
     getattr(_lib, _name).restype = ctypes.c_int
+_lib.tgs_chain_workspace_bytes.argtypes = []
+_lib.tgs_chain_workspace_bytes.restype = _sz
+_lib.ternary_gemv_chain.argtypes = [ctypes.POINTER(ChainStep), _i32, _vp, _sz, _vp]
+_lib.ternary_gemv_chain.restype = ctypes.c_int
 _lib.tgs_stream_read_sink_words.argtypes = []
 _lib.tgs_stream_read_sink_words.restype = _sz
 _lib.tgs_stream_read.argtypes = [_vp, _sz, _vp, _vp]
@@ -86,8 +101,8 @@ _lib.tgs_last_error.restype = ctypes.c_char_p
 EXPORTS = ("tgs_code_row_bytes", "tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv",
            "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
            "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
-           "rmsnorm_hadamard_rotate", "tgs_stream_read_sink_words", "tgs_stream_read", "tgs_status_string",
-           "tgs_last_error")
+           "rmsnorm_hadamard_rotate", "tgs_chain_workspace_bytes", "ternary_gemv_chain",
+           "tgs_stream_read_sink_words", "tgs_stream_read", "tgs_status_string", "tgs_last_error")
 
 
 def _check(status: int):
@@ -451,3 +466,54 @@ def stream_read(buf, sink=None, stream=None):
     _check(_lib.tgs_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
                                 _stream_handle(stream)))
     return sink
+
+
+def chain_workspace(device="cuda"):
+    """A zero-filled chain workspace for the current device (int32 words; see ternary_gemv_chain)."""
+    torch = _torch()
+    nbytes = int(_lib.tgs_chain_workspace_bytes())
+    if nbytes == 0:
+        _raise("TGS_E_DEVICE", "no usable device for the chain workspace")
+    return torch.zeros(nbytes // 4, dtype=torch.int32, device=device)
+
+
+def ternary_gemv_chain(steps, workspace, stream=None):
+    """Run up to CHAIN_MAX_STEPS single-token GEMV steps in order in one launch.
+
+    steps: a list of dicts with keys "ws" (1..3 slot-2 PackedMatrix of one k), "x" (fp16 or fp32
+    tensor of k elements: the step's input, which may be an earlier step's output), "ys" (fp32
+    tensors of n_i elements) and optionally "gamma" (bf16 [k], as bfloat16 or int16 bits) with
+    "eps" for the RMSNorm. workspace: from chain_workspace(), shared by consecutive chains.
+    """
+    torch = _torch()
+    count = len(steps)
+    if not 1 <= count <= CHAIN_MAX_STEPS:
+        _raise("TGS_E_SHAPE", f"1..{CHAIN_MAX_STEPS} steps per chain, got {count}")
+    arr = (ChainStep * count)()
+    dev = None
+    for i, st in enumerate(steps):
+        ws, x, ys, gamma = st["ws"], st["x"], st["ys"], st.get("gamma")
+        if not 1 <= len(ws) <= CHAIN_MAX_MATRICES or len(ys) != len(ws):
+            _raise("TGS_E_SHAPE", f"step {i}: 1..{CHAIN_MAX_MATRICES} matrices and one y each")
+        k = ws[0].k
+        dev = dev or ws[0].device
+        _need(x, f"steps[{i}].x", (torch.float16, torch.float32), numel=k)
+        for j, (w, y) in enumerate(zip(ws, ys)):
+            _need(y, f"steps[{i}].ys[{j}]", (torch.float32,), min_numel=w.n)
+        if gamma is not None:
+            _gamma_ok(gamma, k)
+        _on_device(dev, x=x, gamma=gamma, **{f"codes{j}": w.codes for j, w in enumerate(ws)},
+                   **{f"y{j}": y for j, y in enumerate(ys)})
+        a = arr[i]
+        a.count = len(ws)
+        a.x_dtype = F32 if x.dtype == torch.float32 else F16
+        a.norm = 1 if gamma is not None else 0
+        a.eps = float(st.get("eps", 0.0))
+        a.x = x.data_ptr()
+        a.gamma = gamma.data_ptr() if gamma is not None else None
+        for j, (w, y) in enumerate(zip(ws, ys)):
+            a.w[j] = w.desc
+            a.y[j] = y.data_ptr()
+    _need(workspace, "workspace", (torch.int32,), min_numel=int(_lib.tgs_chain_workspace_bytes()) // 4)
+    _on_device(dev, workspace=workspace)
+    _check(_lib.ternary_gemv_chain(arr, count, workspace.data_ptr(), workspace.numel() * 4, _stream_handle(stream)))

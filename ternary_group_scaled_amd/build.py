@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtgs.so")
 ARCH = "gfx950"
-SOURCES = ["tgs_host.cpp", "gemv.hip", "gemv_s2_mfma.hip", "gemv_mfma.hip", "gemm.hip", "hadamard.hip", "flips.hip", "probe.hip"]
+SOURCES = ["tgs_host.cpp", "gemv.hip", "gemv_s2_mfma.hip", "gemv_chain.hip", "gemv_mfma.hip", "gemm.hip", "hadamard.hip", "flips.hip", "probe.hip"]
 # No packed fp32 ops: the compiler may not form v_pk_{add,mul,fma}_f32 anywhere in this code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -2,86 +2,28 @@
 //
 // y[j] = sum_k s[j][k/128] * t[j][k] * x[k], with the weights w = s_g * t of "Ternary Bonsai 2 27B,
 // 5.93GB ... (feat. PrismML)" (discuss.pytorch.kr), subsection "Group-scaled ternary format": one
-// fp16 scale per 128 consecutive weights of a row. The codes are read once, in packed form.
-//
-// Decode. Codes q = t + 1 sit in 2-bit slots, element j of a little-endian 32-bit word in bits
-// 2j..2j+1. A pair (j, j+8) sits in bits p..p+1 of both 16-bit halves of the word, or of the word
-// shifted right by 6 (p in {0, 2, 4, 6, 8}). One v_and_or_b32 keeps those bits and sets the
-// exponent field 25 - p, which makes each half the fp16 number 2^(10-p) + q exactly; one packed
-// fp16 add of -(2^(10-p) + 1) leaves t = q - 1 (-1.0, 0 or +1.0) in each half, again exactly. Two
-// VALU operations per two weights, and no difference of sums: every product t * x is exact and a
-// zero code adds nothing, so a row with one nonzero code gives s * t * x_k exactly.
-//
-// Multiply. v_mfma_f32_16x16x32_f16 computes D[r][c] = sum over 32 k of A[r][k] B[k][c]. B holds
-// the weights: lane (c, q) (c = lane % 16, q = lane / 16) holds 8 weights of output row c. A window
-// is 512 weights of 16 rows: lane (c, q) owns group q of the window (32 bytes of row c, two 16-byte
-// loads; the four lanes of a row read its 128 contiguous bytes), and each of 16 MFMA steps takes
-// 8 of its 128 weights. The activations go in A, row r holding the window's group r: lane (r, q)
-// holds them only when r == q and zeros otherwise (rows 4..15 are all zero). So D[r][c] is the
-// partial sum of group r for output row c: lane c holds all four groups' partials in its four D
-// registers and scales each by its fp16 scale in fp32 (one 8-byte load of the four scales). The
-// K-reduction inside a window happens in the matrix core; no cross-lane reduction is needed.
-//
-// Activations. The workgroup stages x once as dot2-style pairs (x_j, x_{j+8}) of every 16
-// elements, in LDS, in the order of the weight operand: A fragment s of group g is 16 bytes at
-// word 68 g + 4 s (64 words per group plus 4 of padding, so the four groups a step reads fall in
-// different banks). Lanes whose A entries are zero read a 256-byte zero region instead, one shared
-// address per step (a broadcast). RMSNorm (NORM): the staging threads first add the squares of
-// their activations (fixed order: threads, waves in LDS), then scale by gamma / rms before the one
-// rounding to fp16.
+// fp16 scale per 128 consecutive weights of a row. The codes are read once, in packed form. The
+// window layout, the signed decode and the activation pairs are described in s2_mfma.h.
 //
 // Work split. A workgroup owns 16 rows and has one wave per SW windows of K. Each thread issues the
 // loads of its staging activations first, then every code and scale load of its wave, so the
 // staging waits only for the activations (vector-memory waits retire in issue order) and for the
 // small launches of a decode step every load is in flight at once. A wave's windows run as
 // independent MFMA chains, interleaved step by step. The waves' row sums meet in LDS and are added
-// in wave order (deterministic, no atomics).
+// in wave order (deterministic, no atomics). RMSNorm (NORM): the staging threads first add the
+// squares of their activations (fixed order: threads, waves in LDS), then scale by gamma / rms
+// before the one rounding to fp16.
 #include "lane_ops.h"
 #include "rms_norm.h"
+#include "s2_mfma.h"
 #include "tgs_internal.h"
 
 namespace tgs {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace s2;
 
-constexpr int kWinK = 512;           // weights of a row per window: four scale groups
-constexpr int kGroupPitch = 68;      // LDS words per group of activation pairs (64 + 4)
-constexpr int kZeroBytes = 16 * 16;  // one 16-byte zero fragment per MFMA step
-constexpr int kSW = 2;               // windows per wave
-
-// A 32-bit constant in a vector register: the three-operand AND-OR takes no literal, and its
-// other constant (the mask) goes in a scalar register.
-template <uint32_t V>
-__device__ __forceinline__ uint32_t vconst() {
-  uint32_t r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(V));
-  return r;
-}
-
-// exponent bits that give the code bits p..p+1 the weight 1: 2^(10-p) + q in each half
-template <int P>
-constexpr uint32_t kExpBits = ((uint32_t)(25 - P) << 10) * 0x00010001u;
-
-// t in both fp16 halves from the codes in bits P..P+1 of each half of `word`; exp_bits = vconst of
-// kExpBits<P>
-template <int P>
-__device__ __forceinline__ uint32_t signed_pair(uint32_t word, uint32_t exp_bits) {
-  constexpr uint32_t kMask = 0x00030003u << P;
-  // -(2^(10-P) + 1) in both halves, exactly representable (11 significant bits at most)
-  constexpr uint32_t kNeg = (0x8000u | ((uint32_t)(25 - P) << 10) | (1u << P)) * 0x00010001u;
-  const half2v h = __builtin_bit_cast(half2v, (word & kMask) | exp_bits);
-  return __builtin_bit_cast(uint32_t, h + __builtin_bit_cast(half2v, kNeg));
-}
-
-// Activation pair (element e1 in the low half, e2 in the high half) from fp16 words w[e/2].
-template <int E1, int E2>
-__device__ __forceinline__ uint32_t xpair(const uint32_t* w) {
-  constexpr uint32_t sel = ((E1 & 1) ? 0x0302u : 0x0100u) | (((E2 & 1) ? 0x0706u : 0x0504u) << 16);
-  return __builtin_amdgcn_perm(w[E2 / 2], w[E1 / 2], sel);
-}
+constexpr int kSW = 2;  // windows per wave
 
 template <int SW, bool NORM>
 __global__ __launch_bounds__(1024) void gemv_s2_mfma_kernel(const GemvArgs args) {
@@ -177,19 +119,14 @@ __global__ __launch_bounds__(1024) void gemv_s2_mfma_kernel(const GemvArgs args)
 #pragma unroll
   for (int i = 0; i < kMaxUnits; ++i) {
     const int u = (int)threadIdx.x + i * threads;
-    if (u < units) {
-      uint4* dst = reinterpret_cast<uint4*>(pairs + (u >> 3) * kGroupPitch + (u & 7) * 8);
-      dst[0] = make_uint4(xpair<0, 8>(xw[i]), xpair<1, 9>(xw[i]), xpair<2, 10>(xw[i]), xpair<3, 11>(xw[i]));
-      dst[1] = make_uint4(xpair<4, 12>(xw[i]), xpair<5, 13>(xw[i]), xpair<6, 14>(xw[i]), xpair<7, 15>(xw[i]));
-    }
+    if (u < units) store_unit_pairs(pairs, u, xw[i]);
   }
   if (threadIdx.x < 16) reinterpret_cast<uint4*>(lds + zero_off)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
   // 4. the wave's windows, their MFMA chains interleaved step by step (independent accumulators);
   // a window past K reads the zero region and its scales are zero
-  const uint32_t e0 = vconst<kExpBits<0>>(), e2 = vconst<kExpBits<2>>(), e4 = vconst<kExpBits<4>>(),
-                 e6 = vconst<kExpBits<6>>(), e8 = vconst<kExpBits<8>>();
+  const ExpBits e = exp_bits();
   const char* a_base[SW];
   f32x4 d[SW];
 #pragma unroll
@@ -198,32 +135,11 @@ __global__ __launch_bounds__(1024) void gemv_s2_mfma_kernel(const GemvArgs args)
     a_base[i] = (col == q && w < windows) ? lds + (4 * w + q) * kGroupPitch * 4 : lds + zero_off;
     d[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-#pragma unroll
-    for (int i = 0; i < SW; ++i) {
-      const half8 a = *reinterpret_cast<const half8*>(a_base[i] + 16 * s);
-      const uint4& c = cw[i][s >> 3];
-      const uint32_t u = (s & 6) == 0 ? c.x : ((s & 6) == 2 ? c.y : ((s & 6) == 4 ? c.z : c.w));
-      uint4 b;
-      if ((s & 1) == 0) {  // pairs j = 0..3: bits 0, 2, 4, 6 of u
-        b = make_uint4(signed_pair<0>(u, e0), signed_pair<2>(u, e2), signed_pair<4>(u, e4), signed_pair<6>(u, e6));
-      } else {  // pairs j = 4..7: bit 8 of u, bits 4, 6, 8 of u >> 6
-        const uint32_t v = u >> 6;
-        b = make_uint4(signed_pair<8>(u, e8), signed_pair<4>(v, e4), signed_pair<6>(v, e6), signed_pair<8>(v, e8));
-      }
-      d[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, b), d[i], 0, 0, 0);
-    }
-  }
+  mfma_windows<SW>(a_base, cw, d, e);
   // D[g][col] (group g of the window) is register g of lane col
   float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < SW; ++i) {
-    acc = fmaf(half_lo(sc[i].x), d[i][0], acc);
-    acc = fmaf(half_hi(sc[i].x), d[i][1], acc);
-    acc = fmaf(half_lo(sc[i].y), d[i][2], acc);
-    acc = fmaf(half_hi(sc[i].y), d[i][3], acc);
-  }
+  for (int i = 0; i < SW; ++i) acc = scale_window(acc, sc[i], d[i]);
 
   // 5. add the waves' sums in wave order
   if (lane < 16) red[wave * 16 + lane] = acc;
@@ -240,11 +156,11 @@ __global__ __launch_bounds__(1024) void gemv_s2_mfma_kernel(const GemvArgs args)
 
 int gemv_s2_mfma_waves(int64_t k) { return (int)((k / kWinK + kSW - 1) / kSW); }
 
-bool gemv_s2_mfma_fits(int64_t k) { return k % kWinK == 0 && k <= 16384; }
+bool gemv_s2_mfma_fits(int64_t k) { return k % kWinK == 0 && k <= kMaxK; }
 
 hipError_t gemv_s2_mfma_launch(GemvArgs& args, int32_t blocks, int64_t k, bool norm, hipStream_t stream) {
   const int waves = gemv_s2_mfma_waves(k);
-  const size_t lds = (size_t)(k / 128) * kGroupPitch * 4 + kZeroBytes + (size_t)waves * 16 * 4;
+  const size_t lds = (size_t)pair_bytes((int)k) + kZeroBytes + (size_t)waves * 16 * 4;
   if (norm)
     hipLaunchKernelGGL((gemv_s2_mfma_kernel<kSW, true>), dim3(blocks), dim3(64 * waves), lds, stream, args);
   else

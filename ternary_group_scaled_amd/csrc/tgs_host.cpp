@@ -518,6 +518,79 @@ tgs_status hadamard_rotate_g128(const void* x, int32_t x_dtype, int64_t m, int64
   return hadamard_rotate(x, x_dtype, m, k, 128, signs, y, y_dtype, stream);
 }
 
+size_t tgs_chain_workspace_bytes(void) {
+  const int grid = tgs::chain_grid();
+  return grid > 0 ? (size_t)(grid + 1) * sizeof(uint32_t) : 0;
+}
+
+tgs_status ternary_gemv_chain(const tgs_chain_step* steps, int32_t count, uint32_t* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!steps || !workspace) return fail(TGS_E_NULL, "steps or workspace is NULL");
+  if (count < 1 || count > TGS_CHAIN_MAX_STEPS)
+    return fail(TGS_E_SHAPE, "count must be 1..%d, got %d", TGS_CHAIN_MAX_STEPS, count);
+  if (!aligned(workspace, 4)) return fail(TGS_E_ALIGN, "workspace must be 4-byte aligned");
+  const int grid = tgs::chain_grid();
+  if (grid < 1) return fail(TGS_E_DEVICE, "no usable device for the chain launch");
+  if (workspace_bytes < (size_t)(grid + 1) * sizeof(uint32_t))
+    return fail(TGS_E_SIZE, "workspace holds %zu bytes, needs %zu", workspace_bytes,
+                (size_t)(grid + 1) * sizeof(uint32_t));
+  tgs::ChainArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.flags = workspace;
+  args.count = count;
+  for (int32_t s = 0; s < count; ++s) {
+    const tgs_chain_step& st = steps[s];
+    tgs::ChainStep& cs = args.step[s];
+    if (st.count < 1 || st.count > TGS_CHAIN_MAX_MATRICES)
+      return fail(TGS_E_SHAPE, "step %d: count must be 1..%d", s, TGS_CHAIN_MAX_MATRICES);
+    if (st.x_dtype != TGS_F16 && st.x_dtype != TGS_F32)
+      return fail(TGS_E_DTYPE, "step %d: x_dtype must be TGS_F16 or TGS_F32", s);
+    if (!st.x) return fail(TGS_E_NULL, "step %d: x is NULL", s);
+    if (!aligned(st.x, 16)) return fail(TGS_E_ALIGN, "step %d: x must be 16-byte aligned", s);
+    if (st.norm != 0 && st.norm != 1) return fail(TGS_E_SHAPE, "step %d: norm must be 0 or 1", s);
+    if (st.norm) {
+      if (!st.gamma) return fail(TGS_E_NULL, "step %d: gamma is NULL", s);
+      if (!aligned(st.gamma, 16)) return fail(TGS_E_ALIGN, "step %d: gamma must be 16-byte aligned", s);
+      if (!(st.eps > 0.f && st.eps < INFINITY)) return fail(TGS_E_SHAPE, "step %d: eps must be positive and finite", s);
+    }
+    int32_t rbs = 0;
+    for (int32_t i = 0; i < st.count; ++i) {
+      const tgs_matrix* w = &st.w[i];
+      tgs_status e = check_matrix(w, true);
+      if (e != TGS_OK) return e;
+      if (w->layout != TGS_LAYOUT_SLOT2) return fail(TGS_E_LAYOUT, "step %d: the chain takes slot-2 matrices", s);
+      if (w->rotated) return fail(TGS_E_BASIS, "step %d: the chain takes plain-basis matrices", s);
+      if (w->k != st.w[0].k) return fail(TGS_E_SHAPE, "step %d: the matrices of a step share k", s);
+      if (w->k % 512 != 0 || w->k > 16384)
+        return fail(TGS_E_SHAPE, "step %d: k must be a multiple of 512 up to 16384 (k=%lld)", s, (long long)w->k);
+      if (!st.y[i]) return fail(TGS_E_NULL, "step %d: y[%d] is NULL", s, i);
+      if (!aligned(st.y[i], 4)) return fail(TGS_E_ALIGN, "step %d: y must be 4-byte aligned", s);
+      tgs::ChainMat& cm = cs.mat[i];
+      cm.codes = static_cast<const uint8_t*>(w->codes);
+      cm.scales = w->scales;
+      cm.y = st.y[i];
+      cm.n = (int32_t)w->n;
+      cm.stride = (int32_t)w->code_row_stride;
+      cm.rb0 = rbs;
+      rbs += (int32_t)((w->n + 15) / 16);
+    }
+    if ((rbs + grid - 1) / grid > tgs::kChainMaxRbsPerWg)
+      return fail(TGS_E_SHAPE, "step %d: %d row blocks of 16 exceed %d per compute unit", s, rbs,
+                  tgs::kChainMaxRbsPerWg);
+    cs.x = st.x;
+    cs.gamma = st.norm ? st.gamma : nullptr;
+    cs.k = (int32_t)st.w[0].k;
+    cs.count = st.count;
+    cs.x_f32 = st.x_dtype == TGS_F32 ? 1 : 0;
+    cs.norm = st.norm;
+    cs.rbs = rbs;
+    cs.eps = st.eps;
+  }
+  hipError_t e = tgs::chain_launch(args, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "ternary_gemv_chain launch");
+  return ok();
+}
+
 size_t tgs_stream_read_sink_words(void) { return (size_t)tgs::stream_read_grid() * 256; }
 
 tgs_status tgs_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

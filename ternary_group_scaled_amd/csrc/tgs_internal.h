@@ -114,6 +114,42 @@ int gemv_b3_mfma_rows(int32_t m);
 hipError_t gemv_b3_mfma_launch(GemvArgs& args, int32_t blocks, int32_t m, int32_t block, bool norm,
                                hipStream_t stream);
 
+// GEMV step chain (gemv_chain.hip): up to kChainMaxSteps single-token slot-2 steps in one launch,
+// run in order with a wait between consecutive steps. Device pointers throughout.
+constexpr int kChainMaxSteps = 16;
+constexpr int kChainMaxMats = 3;
+struct ChainMat {
+  const uint8_t* codes;    // [n][stride]
+  const uint16_t* scales;  // [n][k/128] fp16 bits
+  float* y;                // [n]
+  int32_t n;
+  int32_t stride;
+  int32_t rb0;             // first 16-row block of this matrix in the step's numbering
+  int32_t reserved;
+};
+struct ChainStep {
+  const void* x;           // [k] fp16, or fp32 (x_f32) rounded to fp16 when staged
+  const uint16_t* gamma;   // [k] bf16 bits when norm
+  ChainMat mat[kChainMaxMats];
+  int32_t k;
+  int32_t count;           // matrices of the step
+  int32_t x_f32;
+  int32_t norm;
+  int32_t rbs;             // 16-row blocks of the step, all matrices
+  float eps;
+};
+struct ChainArgs {
+  uint32_t* flags;         // workspace: [grid] completed-step counts, then one error word
+  int32_t count;
+  int32_t reserved;
+  ChainStep step[kChainMaxSteps];
+};
+// workgroups of a chain launch on the current device (one per compute unit), or -1
+int chain_grid();
+// 16-row blocks one workgroup may own in a step
+constexpr int kChainMaxRbsPerWg = 16;
+hipError_t chain_launch(const ChainArgs& args, int32_t grid, hipStream_t stream);
+
 // Code flips: one pair of matrices of a batched launch (device pointers).
 struct FlipJob {
   const uint8_t* a;
