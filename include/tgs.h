@@ -339,6 +339,22 @@ tgs_status ternary_gemv_chain(const tgs_chain_step* steps, int32_t count, uint32
                               size_t workspace_bytes, void* stream);
 
 /*
+ * ternary_gemv_chain_static (device): ternary_gemv_chain without a workspace argument, for callers
+ * that cannot allocate device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation). It allocates and frees nothing. Its workspace is an array owned by the
+ * library, one per device (4 * 1025 bytes, held until the process ends); a device whose chain grid
+ * needs more than 1025 words (more than 1024 compute units) is refused with TGS_E_SIZE. Each call
+ * zero-fills that array on `stream` (a small fill kernel) before the chain, so no call depends on
+ * an earlier one. Calls that overlap on one device (on different streams, or from different
+ * threads) share the array and race: their results are undefined.
+ *   steps, count, stream   as for ternary_gemv_chain (same checks, same statuses)
+ *   error   NULL, or a device uint32, 4-byte aligned: after the chain, stream-ordered, it receives
+ *           the chain's error word (0: every wait between steps completed; nonzero: a wait gave
+ *           up and the outputs are garbage)
+ */
+tgs_status ternary_gemv_chain_static(const tgs_chain_step* steps, int32_t count, uint32_t* error, void* stream);
+
+/*
  * Measurement helpers (not part of the product; for measuring the rooflines the kernels are
  * compared with).
  *

@@ -89,6 +89,8 @@ _lib.tgs_chain_workspace_bytes.argtypes = []
 _lib.tgs_chain_workspace_bytes.restype = _sz
 _lib.ternary_gemv_chain.argtypes = [ctypes.POINTER(ChainStep), _i32, _vp, _sz, _vp]
 _lib.ternary_gemv_chain.restype = ctypes.c_int
+_lib.ternary_gemv_chain_static.argtypes = [ctypes.POINTER(ChainStep), _i32, _vp, _vp]
+_lib.ternary_gemv_chain_static.restype = ctypes.c_int
 _lib.tgs_stream_read_sink_words.argtypes = []
 _lib.tgs_stream_read_sink_words.restype = _sz
 _lib.tgs_stream_read.argtypes = [_vp, _sz, _vp, _vp]
@@ -101,7 +103,7 @@ _lib.tgs_last_error.restype = ctypes.c_char_p
 EXPORTS = ("tgs_code_row_bytes", "tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv",
            "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
            "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
-           "rmsnorm_hadamard_rotate", "tgs_chain_workspace_bytes", "ternary_gemv_chain",
+           "rmsnorm_hadamard_rotate", "tgs_chain_workspace_bytes", "ternary_gemv_chain", "ternary_gemv_chain_static",
            "tgs_stream_read_sink_words", "tgs_stream_read", "tgs_status_string", "tgs_last_error")
 
 
@@ -477,14 +479,8 @@ def chain_workspace(device="cuda"):
     return torch.zeros(nbytes // 4, dtype=torch.int32, device=device)
 
 
-def ternary_gemv_chain(steps, workspace, stream=None):
-    """Run up to CHAIN_MAX_STEPS single-token GEMV steps in order in one launch.
-
-    steps: a list of dicts with keys "ws" (1..3 slot-2 PackedMatrix of one k), "x" (fp16 or fp32
-    tensor of k elements: the step's input, which may be an earlier step's output), "ys" (fp32
-    tensors of n_i elements) and optionally "gamma" (bf16 [k], as bfloat16 or int16 bits) with
-    "eps" for the RMSNorm. workspace: from chain_workspace(), shared by consecutive chains.
-    """
+def _chain_steps(steps):
+    """The ctypes step array of a chain, its length and the device its tensors are on."""
     torch = _torch()
     count = len(steps)
     if not 1 <= count <= CHAIN_MAX_STEPS:
@@ -514,6 +510,34 @@ def ternary_gemv_chain(steps, workspace, stream=None):
         for j, (w, y) in enumerate(zip(ws, ys)):
             a.w[j] = w.desc
             a.y[j] = y.data_ptr()
+    return arr, count, dev
+
+
+def ternary_gemv_chain(steps, workspace, stream=None):
+    """Run up to CHAIN_MAX_STEPS single-token GEMV steps in order in one launch.
+
+    steps: a list of dicts with keys "ws" (1..3 slot-2 PackedMatrix of one k), "x" (fp16 or fp32
+    tensor of k elements: the step's input, which may be an earlier step's output), "ys" (fp32
+    tensors of n_i elements) and optionally "gamma" (bf16 [k], as bfloat16 or int16 bits) with
+    "eps" for the RMSNorm. workspace: from chain_workspace(), shared by consecutive chains.
+    """
+    torch = _torch()
+    arr, count, dev = _chain_steps(steps)
     _need(workspace, "workspace", (torch.int32,), min_numel=int(_lib.tgs_chain_workspace_bytes()) // 4)
     _on_device(dev, workspace=workspace)
     _check(_lib.ternary_gemv_chain(arr, count, workspace.data_ptr(), workspace.numel() * 4, _stream_handle(stream)))
+
+
+def ternary_gemv_chain_static(steps, error=None, stream=None):
+    """ternary_gemv_chain on the library's own per-device workspace: allocates nothing.
+
+    error: None, or an int32 device tensor of at least one element that receives the chain's
+    error word (0 when every wait between steps completed). Calls that overlap on one device race.
+    """
+    torch = _torch()
+    arr, count, dev = _chain_steps(steps)
+    if error is not None:
+        _need(error, "error", (torch.int32,), min_numel=1)
+        _on_device(dev, error=error)
+    _check(_lib.ternary_gemv_chain_static(arr, count, None if error is None else error.data_ptr(),
+                                          _stream_handle(stream)))

@@ -41,6 +41,8 @@
 // remaining waits, so a launch always ends (with garbage outputs and the error word set).
 //
 // Determinism: fixed item assignment, fixed reduction orders, no float atomics.
+#include <mutex>
+
 #include "lane_ops.h"
 #include "rms_norm.h"
 #include "s2_mfma.h"
@@ -348,7 +350,43 @@ __global__ __launch_bounds__(kThreads) void gemv_chain_kernel(const ChainArgs ar
     compute_role(args, sm, wave, wg, G, lane);
 }
 
+__global__ __launch_bounds__(256) void chain_clear_kernel(uint32_t* words, int32_t count) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < count) words[i] = 0u;
+}
+
+// The workspace of chains launched without one: one array per device, alive until the process
+// ends. In host code `scratch` names a host-side stand-in, never the device memory: the device
+// address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint32_t scratch[kChainStaticWords];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint32_t* g_scratch[kMaxDevices];
+
 }  // namespace
+
+hipError_t chain_static_workspace(uint32_t** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<uint32_t*>(p);
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
+}
+
+hipError_t chain_clear(uint32_t* words, int32_t count, hipStream_t stream) {
+  hipLaunchKernelGGL(chain_clear_kernel, dim3((count + 255) / 256), dim3(256), 0, stream, words, count);
+  return hipGetLastError();
+}
 
 int chain_grid() {
   int dev = 0, cus = 0;

@@ -523,20 +523,13 @@ size_t tgs_chain_workspace_bytes(void) {
   return grid > 0 ? (size_t)(grid + 1) * sizeof(uint32_t) : 0;
 }
 
-tgs_status ternary_gemv_chain(const tgs_chain_step* steps, int32_t count, uint32_t* workspace, size_t workspace_bytes,
-                              void* stream) {
-  if (!steps || !workspace) return fail(TGS_E_NULL, "steps or workspace is NULL");
+// The launch arguments of a chain from the caller's steps (everything but the workspace), or an
+// error status.
+static tgs_status chain_args(const tgs_chain_step* steps, int32_t count, int grid, tgs::ChainArgs& args) {
+  if (!steps) return fail(TGS_E_NULL, "steps is NULL");
   if (count < 1 || count > TGS_CHAIN_MAX_STEPS)
     return fail(TGS_E_SHAPE, "count must be 1..%d, got %d", TGS_CHAIN_MAX_STEPS, count);
-  if (!aligned(workspace, 4)) return fail(TGS_E_ALIGN, "workspace must be 4-byte aligned");
-  const int grid = tgs::chain_grid();
-  if (grid < 1) return fail(TGS_E_DEVICE, "no usable device for the chain launch");
-  if (workspace_bytes < (size_t)(grid + 1) * sizeof(uint32_t))
-    return fail(TGS_E_SIZE, "workspace holds %zu bytes, needs %zu", workspace_bytes,
-                (size_t)(grid + 1) * sizeof(uint32_t));
-  tgs::ChainArgs args;
   std::memset(&args, 0, sizeof(args));
-  args.flags = workspace;
   args.count = count;
   for (int32_t s = 0; s < count; ++s) {
     const tgs_chain_step& st = steps[s];
@@ -586,8 +579,51 @@ tgs_status ternary_gemv_chain(const tgs_chain_step* steps, int32_t count, uint32
     cs.rbs = rbs;
     cs.eps = st.eps;
   }
+  return ok();
+}
+
+tgs_status ternary_gemv_chain(const tgs_chain_step* steps, int32_t count, uint32_t* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!workspace) return fail(TGS_E_NULL, "workspace is NULL");
+  if (!aligned(workspace, 4)) return fail(TGS_E_ALIGN, "workspace must be 4-byte aligned");
+  const int grid = tgs::chain_grid();
+  if (grid < 1) return fail(TGS_E_DEVICE, "no usable device for the chain launch");
+  if (workspace_bytes < (size_t)(grid + 1) * sizeof(uint32_t))
+    return fail(TGS_E_SIZE, "workspace holds %zu bytes, needs %zu", workspace_bytes,
+                (size_t)(grid + 1) * sizeof(uint32_t));
+  tgs::ChainArgs args;
+  tgs_status st = chain_args(steps, count, grid, args);
+  if (st != TGS_OK) return st;
+  args.flags = workspace;
   hipError_t e = tgs::chain_launch(args, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "ternary_gemv_chain launch");
+  return ok();
+}
+
+tgs_status ternary_gemv_chain_static(const tgs_chain_step* steps, int32_t count, uint32_t* error, void* stream) {
+  if (error && !aligned(error, 4)) return fail(TGS_E_ALIGN, "error must be 4-byte aligned");
+  const int grid = tgs::chain_grid();
+  if (grid < 1) return fail(TGS_E_DEVICE, "no usable device for the chain launch");
+  if (grid + 1 > tgs::kChainStaticWords)
+    return fail(TGS_E_SIZE, "the library's chain workspace holds %d words; a chain on this device needs %d",
+                tgs::kChainStaticWords, grid + 1);
+  tgs::ChainArgs args;
+  tgs_status st = chain_args(steps, count, grid, args);
+  if (st != TGS_OK) return st;
+  uint32_t* words = nullptr;
+  hipError_t e = tgs::chain_static_workspace(&words);
+  if (e != hipSuccess) return device_error(e, "ternary_gemv_chain_static workspace lookup");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the counts start at zero on every call, and so does the error word
+  e = tgs::chain_clear(words, grid + 1, s);
+  if (e != hipSuccess) return device_error(e, "ternary_gemv_chain_static clear");
+  args.flags = words;
+  e = tgs::chain_launch(args, grid, s);
+  if (e != hipSuccess) return device_error(e, "ternary_gemv_chain_static launch");
+  if (error) {
+    e = hipMemcpyAsync(error, words + grid, sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return device_error(e, "ternary_gemv_chain_static error word copy");
+  }
   return ok();
 }
 

@@ -149,6 +149,12 @@ int chain_grid();
 // 16-row blocks one workgroup may own in a step
 constexpr int kChainMaxRbsPerWg = 16;
 hipError_t chain_launch(const ChainArgs& args, int32_t grid, hipStream_t stream);
+// The library-owned chain workspace of the current device (kChainStaticWords words, found once
+// per device), for the entry point that allocates nothing; chain_clear zero-fills words of it.
+constexpr int kChainStaticMaxGrid = 1024;
+constexpr int kChainStaticWords = kChainStaticMaxGrid + 1;
+hipError_t chain_static_workspace(uint32_t** ptr);
+hipError_t chain_clear(uint32_t* words, int32_t count, hipStream_t stream);
 
 // Code flips: one pair of matrices of a batched launch (device pointers).
 struct FlipJob {
