@@ -82,8 +82,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--stream-gib", type=int, default=0,
-                    help="read a buffer of this many GiB once with the streaming-read probe first (a kernel of "
-                         "known traffic that calibrates the FETCH_SIZE counter in a profile of this command)")
+                    help="read a buffer of this many GiB once with the streaming-read probe first, then copy "
+                         "256 MiB device to device (kernels of known traffic that calibrate the FETCH_SIZE and "
+                         "WRITE_SIZE counters in a profile of this command)")
     return ap.parse_args()
 
 
@@ -262,18 +263,26 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
         ys = [outputs[L][nm] for nm in grp]
         return lambda: tgs.ternary_gemv_batched(ws, xs, ys)
 
+    # kernel launches of one batched call: the library launches once per distinct kernel shape among
+    # its matrices (for slot-2 and binary, once per distinct K; every base-3 matrix of a call shares one)
+    def kernels_of(ws):
+        return 1 if layout == 2 else len({w.k for w in ws})
+
     def batched_launches(chunk):
         per = [(mats[L][nm], inputs[L][g][0], outputs[L][nm]) for L in range(layers) for g in GROUPS_8B for nm in g]
-        out = []
+        out, kernels = [], 0
         for i in range(0, len(per), chunk):
             part = per[i:i + chunk]
+            kernels += kernels_of([a for a, _, _ in part])
             out.append((lambda p: lambda: tgs.ternary_gemv_batched([a for a, _, _ in p], [b for _, b, _ in p],
                                                                    [c for _, _, c in p]))(part))
-        return out
+        return out, kernels
 
+    fused, fused_kernels = batched_launches(len(LAYER_8B))
+    whole, whole_kernels = batched_launches(tgs.MAX_BATCH)
     modes = {"layer": [group_launch(L, g) for L in range(layers) for g in GROUPS_8B],
-             "fused-layer": batched_launches(len(LAYER_8B)),
-             "set": batched_launches(tgs.MAX_BATCH)}
+             "fused-layer": fused, "set": whole}
+    kernels = {"layer": layers * len(GROUPS_8B), "fused-layer": fused_kernels, "set": whole_kernels}
     all_modes = ["layer", "fused-layer", "set"]
     chain = None
     if layout == 1:
@@ -281,6 +290,7 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
         wsp = tgs.chain_workspace()
         modes["chain"] = [(lambda part: lambda: tgs.ternary_gemv_chain(part, wsp))(chain[i:i + tgs.CHAIN_MAX_STEPS])
                           for i in range(0, len(chain), tgs.CHAIN_MAX_STEPS)]
+        kernels["chain"] = len(modes["chain"])
         all_modes = ["chain"] + all_modes
     mode = args.mode if args.mode in modes else "layer"
     timings = {}
@@ -295,10 +305,10 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
         log(f"[bench] timing {args.steps} graph replays of {len(launches)} launches ({mode})")
         ms_m, _graph = time_graph(torch, one_pass, args.steps, args.warmup, eager=not args.no_eager)
         del _graph
-        timings[mode] = (ms_m, len(launches))
+        timings[mode] = (ms_m, kernels[mode], len(launches))
         log(f"[bench]   {mode}: step {ms_m * 1e3:.1f} us -> {total_bytes / ms_m / 1e6:.0f} GB/s, "
-            f"{ms_m * 1e3 / len(launches):.2f} us per launch")
-    ms, n_launches = timings[mode]
+            f"{ms_m * 1e3 / kernels[mode]:.2f} us per kernel launch ({kernels[mode]} launches, {len(launches)} calls)")
+    ms, n_launches, n_calls = timings[mode]
     if mode == "chain":
         chain_parity_check(tgs, torch, chain, wsp, host_chain_of(host, chain))
     gbs = total_bytes / (ms * 1e-3) / 1e9
@@ -323,12 +333,13 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": workload_name or "8B-class decode GEMV set, 2-bit-slot layout, M=1",
                    "layers": layers, "matrices": layers * len(LAYER_8B), "launches_per_step": n_launches,
+                   "calls_per_step": n_calls,
                    "launch_mode": mode, "p_zero": p_zero, "algorithmic_bytes_per_step": int(total_bytes),
                    "weight_bytes_per_step": int(w_bytes)},
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(1e3 / ms, 1),
-        "launch_modes": {m: {"launches": t[1], "ms_per_step": round(t[0], 5), "gbs": round(total_bytes / t[0] / 1e6, 1)}
-                         for m, t in timings.items()},
+        "launch_modes": {m: {"launches": t[1], "calls": t[2], "ms_per_step": round(t[0], 5),
+                             "gbs": round(total_bytes / t[0] / 1e6, 1)} for m, t in timings.items()},
         "roofline": roofline("hbm", kernel_gbs, HBM_PEAK_GBS, "GB/s", kernel,
                              None if traffic is None else int(traffic["fetch"] + traffic["write"]), **extra),
     }
@@ -913,8 +924,11 @@ def main():
     if args.stream_gib:
         buf = torch.empty(args.stream_gib << 30, dtype=torch.uint8, device="cuda")
         tgs.stream_read(buf)
+        # a 256 MiB device-to-device copy: known writes (and reads) for the WRITE_SIZE counter
+        dst = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst.copy_(buf[:256 << 20])
         torch.cuda.synchronize()
-        del buf
+        del buf, dst
     if args.workload == "all":
         t_start = time.time()
         ceiling = stream_read_ceiling(torch, tgs)
