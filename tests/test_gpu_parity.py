@@ -385,6 +385,33 @@ def test_gemm_wide_matrices(n, m):
     assert_within_bound(y, y_ref, bound, f"gemm wide {n}x{k} m={m}")
 
 
+@pytest.mark.parametrize("n,k,m", [(16400, 1024, 16), (8200, 3072, 7), (1000, 2560, 16), (333, 512, 3),
+                                   (4096, 9216, 16), (17, 4608, 12), (8192, 512, 1), (300, 8192, 16),
+                                   (24000, 1024, 9)])
+def test_gemm_few_rows_shapes(n, k, m):
+    """Up to 16 activation rows over partial 16-output blocks, 1 to 16 rows, K from one to 18
+    windows of 512 and n from 17 to 24000 (2 to 6 output blocks per workgroup)."""
+    t, s = make_weights(n + k + 3 * m, "gemmfew", n, k, 0.4)
+    xb = make_x_bf16_bits(n + m, "gemmfewx", m, k)
+    y = _gemm(tgs.SLOT2, t, s, xb)
+    rows = None if n <= 4096 else np.unique(np.r_[0, n - 1, np.linspace(0, n - 1, 300).astype(np.int64)])
+    y_ref, bound = oracle_product(tgs.SLOT2, t, s, xb, oracle.X_BF16, rows=rows)
+    got = y if rows is None else y[:, rows]
+    assert_within_bound(got, y_ref, bound, f"gemm few rows {n}x{k} m={m}")
+
+
+def test_gemm_sixteen_rows_integer_inputs_are_exact():
+    """Integer activations and power-of-two scales with 16 rows and K = 4096: every partial is
+    exact in fp32, so the result equals the oracle bit for bit."""
+    n, k, m = 1040, 4096, 16
+    t, _ = make_weights(13, "gemmexact16", n, k, 0.4)
+    s = np.ldexp(1.0, synth.trits(13, 7, (n, k // 128), 0.0).astype(np.int64)).astype(np.float16)
+    xi = (synth.trits(13, 8, (m, k), 0.2).astype(np.int64) * 3).astype(np.float32)
+    y_gemm = _gemm(tgs.SLOT2, t, s, synth.bf16_bits(xi))
+    y_ref, _ = oracle_product(tgs.SLOT2, t, s, synth.bf16_bits(xi), oracle.X_BF16)
+    assert (y_gemm.astype(np.float64) == y_ref).all()
+
+
 def test_gemm_large_tiles_sampled():
     """Many rows and columns take 128 x 128 tiles; checked on sampled output columns."""
     n, k, m = 8192, 256, 1040
