@@ -8,8 +8,9 @@
 // Work split. A workgroup owns 16 rows and has one wave per SW windows of K. Each thread issues the
 // loads of its staging activations first, then every code and scale load of its wave, so the
 // staging waits only for the activations (vector-memory waits retire in issue order) and for the
-// small launches of a decode step every load is in flight at once. A wave's windows run as
-// independent MFMA chains, interleaved step by step. The waves' row sums meet in LDS and are added
+// small launches of a decode step every load is in flight at once. A wave multiplies its windows
+// one after the other, in the order their loads were issued, so each window's MFMAs start as soon
+// as its own codes have arrived. The waves' row sums meet in LDS and are added
 // in wave order (deterministic, no atomics). RMSNorm (NORM): the staging threads first add the
 // squares of their activations (fixed order: threads, waves in LDS), then scale by gamma / rms
 // before the one rounding to fp16.
@@ -124,8 +125,9 @@ __global__ __launch_bounds__(1024) void gemv_s2_mfma_kernel(const GemvArgs args)
   if (threadIdx.x < 16) reinterpret_cast<uint4*>(lds + zero_off)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
-  // 4. the wave's windows, their MFMA chains interleaved step by step (independent accumulators);
-  // a window past K reads the zero region and its scales are zero
+  // 4. the wave's windows, one MFMA chain after the other (a window's chain waits only for its own
+  // codes: measured +2% in layer order and +4% as a set against interleaving the chains step by
+  // step); a window past K reads the zero region and its scales are zero
   const ExpBits e = exp_bits();
   const char* a_base[SW];
   f32x4 d[SW];
@@ -135,7 +137,8 @@ __global__ __launch_bounds__(1024) void gemv_s2_mfma_kernel(const GemvArgs args)
     a_base[i] = (col == q && w < windows) ? lds + (4 * w + q) * kGroupPitch * 4 : lds + zero_off;
     d[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  mfma_windows<SW>(a_base, cw, d, e);
+#pragma unroll
+  for (int i = 0; i < SW; ++i) mfma_windows<1>(a_base + i, cw + i, d + i, e);
   // D[g][col] (group g of the window) is register g of lane col
   float acc = 0.f;
 #pragma unroll
