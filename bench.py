@@ -216,9 +216,14 @@ def measured_traffic(profile_name, kernel):
     if fields.get("source_sha256") != kernel_source_sha(kernel):
         return None
     try:
-        return {"fetch": float(fields["fetch_bytes_per_launch"]), "write": float(fields["write_bytes_per_launch"])}
+        out = {"fetch": float(fields["fetch_bytes_per_launch"]), "write": float(fields["write_bytes_per_launch"])}
     except (KeyError, ValueError):
         return None
+    try:  # the profiler's average launch duration, when the summary records it
+        out["trace_avg_launch_us"] = float(fields["trace_avg_launch_us"].split()[0])
+    except (KeyError, ValueError, IndexError):
+        pass
+    return out
 
 
 # ----------------------------------------------------------------------------- 8B decode set
@@ -323,6 +328,11 @@ def bench_8b(args, torch, tgs, synth, layout=1, p_zero=0.4, tag="8b", workload_n
     extra = {"avg_launch_us": round(per_launch_s * 1e6, 3), "bytes_per_launch_avg": int(per_launch_bytes),
              "traffic_profile": profile if traffic is not None else None,
              "duration": "timed region / launches (HIP events on the replay stream; back-to-back launches)"}
+    if traffic is not None and "trace_avg_launch_us" in traffic:
+        # the kernel-side figure: the same kernel sources under rocprofv3 --kernel-trace (each dispatch
+        # signals the profiler, so traced launches run somewhat longer than untraced ones)
+        extra["trace_avg_launch_us"] = traffic["trace_avg_launch_us"]
+        extra["trace_gbs"] = round(per_launch_bytes / (traffic["trace_avg_launch_us"] * 1e-6) / 1e9, 1)
     if ceiling:
         extra["measured_read_ceiling_gbs"] = ceiling["value"]
         extra["frac_vs_measured"] = round(kernel_gbs / ceiling["value"], 4)
