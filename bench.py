@@ -23,7 +23,7 @@ roofline and CPU baseline: the single 256 x 1024 GEMV (latency), the base-3 8B s
 prefill GEMM at M in {16, 128, 2048} for both shapes, and the 27B-class rotated base-3 set at
 M in {1, 8} with the rotation fused and as two passes.
 
-`--workload` runs one workload alone (8b, config1, base3, gemm, rotated, binary, rmsnorm, flips,
+`--workload` runs one workload alone (8b, gemv256, base3, gemm, rotated, binary, rmsnorm, flips,
 stream) and prints its lines.
 """
 from __future__ import annotations
@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "8b", "base3", "binary", "rotated", "gemm", "flips", "rmsnorm", "config1",
+                    choices=["all", "8b", "base3", "binary", "rotated", "gemm", "flips", "rmsnorm", "gemv256",
                              "stream"])
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the set (default: 36 for the 8B-class sets, 64 for the rotated 27B-class set)")
@@ -456,21 +456,21 @@ def cpu_baseline_8b(torch, host, xs, ys, layout, seconds, gpu_ms, layer_bytes, l
 
 # ----------------------------------------------------------------------------- single GEMV (latency)
 
-def bench_config1(args, torch, tgs, synth):
+def bench_gemv256(args, torch, tgs, synth):
     """The single ternary GEMV of 256 outputs x 1024 inputs, M = 1, codes P(0) = 0.4, scales
     |N(0, 0.02)| + 1e-4, fp16 N(0, 1) activations, seed 0, 2-bit-slot layout: the pack/unpack round
     trip, and the time of one call in a stream of back-to-back calls (72,704 bytes fit the cache, so
     this is a latency figure). The CPU-baseline leg also checks the packing and every output against
     the oracle."""
     n, k = 256, 1024
-    t = synth.trits(0, synth.stream_id("config1", "codes"), (n, k), 0.4)
-    s = synth.scales_f16(0, synth.stream_id("config1", "scales"), (n, k // 128))
+    t = synth.trits(0, synth.stream_id("gemv256x1024", "codes"), (n, k), 0.4)
+    s = synth.scales_f16(0, synth.stream_id("gemv256x1024", "scales"), (n, k // 128))
     codes, scales = tgs.pack_ternary(1, t, s)
     back, _ = tgs.unpack_ternary(1, codes, scales, k)
     if not (back == t).all():
-        raise SystemExit("config1: pack/unpack round trip failed")
+        raise SystemExit("256x1024 GEMV: pack/unpack round trip failed")
     w = tgs.PackedMatrix(1, torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda(), k)
-    x16 = synth.x_f16(0, synth.stream_id("config1", "x"), (1, k))
+    x16 = synth.x_f16(0, synth.stream_id("gemv256x1024", "x"), (1, k))
     x = torch.from_numpy(x16.view(np.int16).copy()).cuda().view(torch.float16)
     y = torch.empty((1, n), dtype=torch.float32, device="cuda")
     calls = 200
@@ -482,7 +482,7 @@ def bench_config1(args, torch, tgs, synth):
     ms, _ = time_graph(torch, run, max(3, args.steps // 4), 1, eager=not args.no_eager)
     us = ms * 1e3 / calls
     nbytes = codes.nbytes + scales.nbytes + 2 * k + 4 * n
-    log(f"[bench] config1 256x1024 GEMV: {us:.2f} us per call")
+    log(f"[bench] single 256x1024 GEMV: {us:.2f} us per call")
     line = {"metric": "single ternary GEMV latency, 256x1024, 2-bit-slot, M=1", "value": round(us, 3), "unit": "us",
             "higher_is_better": False, "calls_per_replay": calls, "round_trip": "pack/unpack bit-exact",
             "config": {"workload": "single GEMV, N=256 x K=1024, groups of 128 along K, M=1, codes P(0)=0.4, "
@@ -493,13 +493,13 @@ def bench_config1(args, torch, tgs, synth):
         import oracle
         ref_codes = oracle.pack(1, t)
         if not (codes == ref_codes).all():
-            raise SystemExit("config1: packing differs from the oracle's")
+            raise SystemExit("256x1024 GEMV: packing differs from the oracle's")
         y_ref, bound = oracle.matmul(1, ref_codes, s, k, x16.view(np.uint16), oracle.X_F16)
         ratio = float((np.abs(y.cpu().numpy().astype(np.float64) - y_ref) / bound).max())
         if not ratio <= 1.0:
-            raise SystemExit(f"config1: parity check failed (max err/bound {ratio:.3g})")
-        log(f"[bench] config1: packing and every output match the oracle (max err/bound {ratio:.3g})")
-        line["cpu_baseline"] = cpu_baseline_config1(ref_codes, s, x16, k, us)
+            raise SystemExit(f"256x1024 GEMV: parity check failed (max err/bound {ratio:.3g})")
+        log(f"[bench] 256x1024 GEMV: packing and every output match the oracle (max err/bound {ratio:.3g})")
+        line["cpu_baseline"] = cpu_baseline_gemv256(ref_codes, s, x16, k, us)
         line["cpu_baseline"]["parity_max_err_over_bound"] = ratio
     return line
 
@@ -510,9 +510,9 @@ import numpy as np
 sys.path.insert(0, {root!r})
 import oracle, synth
 n, k = 256, 1024
-t = synth.trits(0, synth.stream_id("config1", "codes"), (n, k), 0.4)
-s = synth.scales_f16(0, synth.stream_id("config1", "scales"), (n, k // 128))
-x = synth.x_f16(0, synth.stream_id("config1", "x"), (1, k)).view(np.uint16)
+t = synth.trits(0, synth.stream_id("gemv256x1024", "codes"), (n, k), 0.4)
+s = synth.scales_f16(0, synth.stream_id("gemv256x1024", "scales"), (n, k // 128))
+x = synth.x_f16(0, synth.stream_id("gemv256x1024", "x"), (1, k)).view(np.uint16)
 codes = oracle.pack(1, t)
 oracle.matmul(1, codes, s, k, x, oracle.X_F16)
 t0, calls = time.time(), 0
@@ -523,7 +523,7 @@ print((time.time() - t0) / calls * 1e6)
 """
 
 
-def cpu_baseline_config1(codes, s, x16, k, gpu_us, seconds=2.0):
+def cpu_baseline_gemv256(codes, s, x16, k, gpu_us, seconds=2.0):
     """The oracle on the whole config-1 GEMV, on all host threads and (in a child process with
     OMP_NUM_THREADS=1) on one."""
     import subprocess
@@ -952,25 +952,25 @@ def main():
         ceiling = stream_read_ceiling(torch, tgs)
         head = bench_8b(args, torch, tgs, synth, ceiling=ceiling)
         torch.cuda.empty_cache()
-        configs = {"config1_gemv_256x1024": nested(bench_config1(args, torch, tgs, synth))}
+        configs = {"gemv_256x1024": nested(bench_gemv256(args, torch, tgs, synth))}
         saved = args.cpu_seconds
         args.cpu_seconds = min(saved, 5.0)
-        configs["config3_base3_set"] = nested(bench_8b(
+        configs["base3_8b_set"] = nested(bench_8b(
             args, torch, tgs, synth, layout=2, p_zero=0.5, tag="8b3",
             workload_name="8B-class decode GEMV set, base-3 layout, M=1",
             metric="base-3 ternary GEMV achieved HBM GB/s (% of peak), 8B-class set, M=1", ceiling=ceiling))
         args.cpu_seconds = saved
         torch.cuda.empty_cache()
-        configs["config4_gemm"] = [nested(x) for x in bench_gemm(args, torch, tgs, synth)]
-        configs["config5_rotated"] = [nested(x) for x in bench_rotated(args, torch, tgs, synth)]
+        configs["gemm_27b"] = [nested(x) for x in bench_gemm(args, torch, tgs, synth)]
+        configs["rotated_base3_27b_set"] = [nested(x) for x in bench_rotated(args, torch, tgs, synth)]
         head["stream_read"] = ceiling
         head["configs"] = configs
         head["wall_s"] = round(time.time() - t_start, 1)
         out = [head]
     elif args.workload == "8b":
         out = [bench_8b(args, torch, tgs, synth)]
-    elif args.workload == "config1":
-        out = [bench_config1(args, torch, tgs, synth)]
+    elif args.workload == "gemv256":
+        out = [bench_gemv256(args, torch, tgs, synth)]
     elif args.workload == "base3":
         out = [bench_8b(args, torch, tgs, synth, layout=2, p_zero=0.5, tag="8b3",
                         workload_name="8B-class decode GEMV set, base-3 layout, M=1",

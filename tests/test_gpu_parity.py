@@ -39,17 +39,17 @@ def _gemv(layout, t, s, x16, signs=None, block=128):
 
 # ------------------------------------------------------------------------------ small configuration
 
-def test_config1_slot2_gemv():
+def test_single_gemv_256x1024_slot2():
     """256 x 1024 GEMV, codes P(0)=0.4, scales |N(0,0.02)|+1e-4, x fp16 N(0,1), seed 0."""
-    t, s = make_weights(0, "config1", 256, 1024, 0.4)
-    x16 = make_x_f16(0, "config1", 1, 1024)
+    t, s = make_weights(0, "gemv256x1024", 256, 1024, 0.4)
+    x16 = make_x_f16(0, "gemv256x1024", 1, 1024)
     codes, _ = tgs.pack_ternary(tgs.SLOT2, t, s)
     assert (codes == oracle.pack(tgs.SLOT2, t)).all()
     back, _ = tgs.unpack_ternary(tgs.SLOT2, codes, s, 1024)
     assert (back == t).all()
     y = _gemv(tgs.SLOT2, t, s, x16)
     y_ref, bound = oracle_product(tgs.SLOT2, t, s, x16.view(np.uint16), oracle.X_F16)
-    assert_within_bound(y, y_ref, bound, "config1")
+    assert_within_bound(y, y_ref, bound, "256x1024 GEMV")
     y2 = _gemv(tgs.SLOT2, t, s, x16)
     assert (y2.view(np.uint32) == y.view(np.uint32)).all()  # run-to-run bitwise determinism
 

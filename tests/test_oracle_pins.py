@@ -196,7 +196,7 @@ def test_base3_density():
     assert oracle.row_bytes(oracle.BASE3, 17408) == 3488
 
 
-def test_config1_bytes():
+def test_single_gemv_256x1024_bytes():
     assert 256 * oracle.row_bytes(oracle.SLOT2, 1024) + 256 * 8 * 2 == 69632
 
 
