@@ -92,7 +92,7 @@ __device__ __forceinline__ uint16_t bf16_of_2t_digit(uint32_t digit) {
 // MFMAs run while the other waits on its loads (measured +40% at 2048 rows over one per CU).
 // KS = 2 splits K between two halves of the workgroup (4 waves each, groups taken alternately,
 // own LDS tiles); the second half's sums are added to the first's at the end, through LDS. It is
-// used when the tiles alone give too few workgroups.
+// used when the tiles alone give too few workgroups (KS parts of 4 waves, KS = 2 or 4).
 template <int LAYOUT, int BM, int BN, int KS>
 __global__ __launch_bounds__(kThreads * KS)
 __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void gemm_tile_kernel(
@@ -255,26 +255,35 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
       __syncthreads();
     }
   }
-  if constexpr (KS == 2) {
-    // the second half hands its sums to the first (fixed order: first + second)
-    float* red = reinterpret_cast<float*>(xs_all[1]);  // 4 waves x 64 lanes x kBlkM*kBlkN*4 floats
-    static_assert(kBlkM * kBlkN * 4 * 256 * 4 <= BM * kPitch * 2, "reduction buffer fits the tile");
-    if (kh == 1) {
+  if constexpr (KS > 1) {
+    // the other K parts hand their sums to the first, added in part order (deterministic). A part's
+    // sums go to its own tiles, now free: rows of 256 floats, first in its activation tile, then
+    // in its weight tile.
+    constexpr int kE = kBlkM * kBlkN * 4;
+    constexpr int kXsRows = BM * kPitch * 2 / 4 / 256, kWsRows = BN * kPitch * 2 / 4 / 256;
+    static_assert(kE <= kXsRows + kWsRows, "the sums fit a part's tiles");
+    auto slot = [&](int h, int e) -> float* {
+      return e < kXsRows ? reinterpret_cast<float*>(xs_all[h]) + e * 256 + tid
+                         : reinterpret_cast<float*>(ws_all[h]) + (e - kXsRows) * 256 + tid;
+    };
+    if (kh > 0) {
 #pragma unroll
       for (int a = 0; a < kBlkM; ++a)
 #pragma unroll
         for (int b = 0; b < kBlkN; ++b)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) red[((a * kBlkN + b) * 4 + r) * 256 + tid] = acc[a][b][r];
+          for (int r = 0; r < 4; ++r) *slot(kh, (a * kBlkN + b) * 4 + r) = acc[a][b][r];
     }
     __syncthreads();
-    if (kh == 1) return;
+    if (kh > 0) return;
 #pragma unroll
-    for (int a = 0; a < kBlkM; ++a)
+    for (int h = 1; h < KS; ++h)
 #pragma unroll
-      for (int b = 0; b < kBlkN; ++b)
+      for (int a = 0; a < kBlkM; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[a][b][r] += red[((a * kBlkN + b) * 4 + r) * 256 + tid];
+        for (int b = 0; b < kBlkN; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[a][b][r] += *slot(h, (a * kBlkN + b) * 4 + r);
   }
 
   // epilogue: D[i][j] of a 16x16 block sits in lane (i/4)*16 + j, register i%4
@@ -550,6 +559,9 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
   const int bn = (n + 127) / 128 * m_tiles >= 512 ? 128 : 64;
   const int64_t tiles = (n + bn - 1) / bn * m_tiles;
   const bool ks2 = tiles < 512 && k / 128 >= 16;
+  // four K parts for few 64 x 64 tiles over a long K: every part walks a quarter of the groups, and
+  // each group iteration waits out about one HBM latency
+  const bool ks4 = ks2 && bm == 64 && bn == 64 && tiles < 256 && k / 128 >= 64;
   const dim3 grid((unsigned)((n + bn - 1) / bn), (unsigned)m_tiles);
   const int ni = (int)n, ki = (int)k, mi = (int)m;
 #define TGS_TILE(BM_, BN_, KS_)                                                                           \
@@ -563,7 +575,7 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
   } else if (bn == 128) {
     TGS_TILE(64, 128, 1);
   } else {
-    if (ks2) TGS_TILE(64, 64, 2); else TGS_TILE(64, 64, 1);
+    if (ks4) TGS_TILE(64, 64, 4); else if (ks2) TGS_TILE(64, 64, 2); else TGS_TILE(64, 64, 1);
   }
 #undef TGS_TILE
   return hipGetLastError();
