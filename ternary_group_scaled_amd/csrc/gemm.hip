@@ -14,12 +14,11 @@
 //   2. meanwhile v_mfma_f32_16x16x32_bf16 runs over group g from LDS, and the group's partial is
 //      scaled by 0.5 * s[n][g] in fp32 and added to the running sum (the scale never enters a
 //      bf16 operand: rounding s to bf16 would cost 2^-9 relative);
-//   3. after a barrier the registers go to LDS: activations reordered, weights decoded to bf16
+//   3. after a barrier the registers go to LDS: activations as loaded, weights decoded to bf16
 //      2t in {-2, 0, +2} (exact; the factor 2 keeps the low byte of every bf16 zero, so one
 //      v_perm table lookup makes two weights).
-// Within every 16 consecutive k, both tiles are stored in the order 0,8,1,9,...,7,15 (the order
-// the slot-2 decode produces pairs in); the contraction over k does not depend on that order.
-// Binary codes (t in {-1, +1}, one bit per weight) decode the same way into bf16 2t in {-2, +2}.
+// Both tiles hold k in its natural order. Binary codes (t in {-1, +1}, one bit per weight) decode
+// the same way into bf16 2t in {-2, +2}.
 // Up to 32 activation rows of slot-2 or binary codes take the skinny kernel further below instead.
 #include <algorithm>
 
@@ -46,41 +45,52 @@ __device__ __forceinline__ uint32_t pair16(const uint32_t* w) {
   return __builtin_amdgcn_perm(w[E2 / 2], w[E1 / 2], sel);
 }
 
-// 16 consecutive k values (8 words) -> the 0,8,1,9,... order
-__device__ __forceinline__ void interleave16(const uint32_t* w, uint32_t* out) {
-  out[0] = pair16<0, 8>(w);
-  out[1] = pair16<1, 9>(w);
-  out[2] = pair16<2, 10>(w);
-  out[3] = pair16<3, 11>(w);
-  out[4] = pair16<4, 12>(w);
-  out[5] = pair16<5, 13>(w);
-  out[6] = pair16<6, 14>(w);
-  out[7] = pair16<7, 15>(w);
+// Codes to bf16 weight pairs in natural k order (2 t_{2j} in the low half, 2 t_{2j+1} in the
+// high half of word j). bf16(-2) = 0xC000, bf16(0) = 0, bf16(+2) = 0x4000: only the high byte
+// differs. The codes are first spread one per byte, each byte holding 4 + code; per output word
+// one v_perm gathers code 2j's byte into byte 1 and code 2j + 1's into byte 3 (zero in bytes 0
+// and 2), and a second v_perm uses that as a selector: 4 + code picks the high byte from a table
+// in the selector's upper source, 0 picks a zero byte of the lower one.
+// selector gathering byte I of `lo` (into byte 1) and byte I of `hi` (into byte 3)
+template <int I>
+__device__ __forceinline__ uint32_t gather_pair(uint32_t hi, uint32_t lo) {
+  constexpr uint32_t kSel = 0x0Cu | ((uint32_t)I << 8) | (0x0Cu << 16) | ((uint32_t)(4 + I) << 24);
+  return __builtin_amdgcn_perm(hi, lo, kSel);
 }
 
-// 16 slot-2 codes -> 8 words of bf16 pairs (2 t_i, 2 t_{i+8}).
-// bf16(-2) = 0xC000, bf16(0) = 0, bf16(+2) = 0x4000: only the high byte differs, so the
-// selector puts code q_i in byte 1 and q_{i+8} in byte 3 and 0x0C (a constant zero) in bytes
-// 0 and 2, and v_perm reads the high byte from the table {0xC0, 0x00, 0x40}.
+// 16 slot-2 codes (code i in bits 2i, 2i + 1 of u) -> 8 words of bf16 pairs
 __device__ __forceinline__ void decode16_slot2(uint32_t u, uint32_t* out) {
-  constexpr uint32_t kTable = 0x004000C0u;
-  out[0] = __builtin_amdgcn_perm(0u, kTable, ((u << 8) & 0x03000300u) | 0x000C000Cu);
-  out[1] = __builtin_amdgcn_perm(0u, kTable, ((u << 6) & 0x03000300u) | 0x000C000Cu);
-  out[2] = __builtin_amdgcn_perm(0u, kTable, ((u << 4) & 0x03000300u) | 0x000C000Cu);
-  out[3] = __builtin_amdgcn_perm(0u, kTable, ((u << 2) & 0x03000300u) | 0x000C000Cu);
-  out[4] = __builtin_amdgcn_perm(0u, kTable, (u & 0x03000300u) | 0x000C000Cu);
-  out[5] = __builtin_amdgcn_perm(0u, kTable, ((u >> 2) & 0x03000300u) | 0x000C000Cu);
-  out[6] = __builtin_amdgcn_perm(0u, kTable, ((u >> 4) & 0x03000300u) | 0x000C000Cu);
-  out[7] = __builtin_amdgcn_perm(0u, kTable, ((u >> 6) & 0x03000300u) | 0x000C000Cu);
+  constexpr uint32_t kTable = 0x004000C0u;  // codes 0, 1, 2: t = -1, 0, +1
+  uint32_t m[4];  // byte i of m[r]: 4 + code 4i + r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = ((u >> (2 * r)) & 0x03030303u) | 0x04040404u;
+  out[0] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<0>(m[1], m[0]));
+  out[1] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<0>(m[3], m[2]));
+  out[2] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<1>(m[1], m[0]));
+  out[3] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<1>(m[3], m[2]));
+  out[4] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<2>(m[1], m[0]));
+  out[5] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<2>(m[3], m[2]));
+  out[6] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<3>(m[1], m[0]));
+  out[7] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<3>(m[3], m[2]));
 }
 
-// 16 binary codes (bits 0..15 of u, a set bit meaning t = +1) -> 8 words of bf16 pairs
-// (2 t_i, 2 t_{i+8}): the bit picks the high byte from the table {0xC0, 0x40} (bf16 -2, +2)
-__device__ __forceinline__ void decode16_binary(uint32_t u, uint32_t* out) {
-  constexpr uint32_t kTable = 0x000040C0u;
-  const uint32_t v = (u & 0xFFu) | ((u & 0xFF00u) << 8);  // bit i + 8 -> bit i + 16
+// 32 binary codes (bit i of u, a set bit meaning t = +1) -> 16 words of bf16 pairs
+template <int I>
+__device__ __forceinline__ void decode8_binary(const uint32_t* m, uint32_t* out) {
+  constexpr uint32_t kTable = 0x000040C0u;  // bit 0, 1: t = -1, +1
+  out[0] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<I>(m[1], m[0]));
+  out[1] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<I>(m[3], m[2]));
+  out[2] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<I>(m[5], m[4]));
+  out[3] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<I>(m[7], m[6]));
+}
+__device__ __forceinline__ void decode32_binary(uint32_t u, uint32_t* out) {
+  uint32_t m[8];  // byte i of m[r]: 4 + bit 8i + r
 #pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = __builtin_amdgcn_perm(0u, kTable, ((v << (8 - i)) & 0x01000100u) | 0x000C000Cu);
+  for (int r = 0; r < 8; ++r) m[r] = ((u >> r) & 0x01010101u) | 0x04040404u;
+  decode8_binary<0>(m, out + 0);
+  decode8_binary<1>(m, out + 4);
+  decode8_binary<2>(m, out + 8);
+  decode8_binary<3>(m, out + 12);
 }
 
 __device__ __forceinline__ uint16_t bf16_of_2t_digit(uint32_t digit) {
@@ -151,11 +161,9 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
 #pragma unroll
     for (int u = 0; u < kXUnits; ++u) {
       const int unit = tid + u * kThreads, r = unit >> 3, c16 = (unit & 7) * 16;
-      uint32_t o[8];
-      interleave16(xr[u], o);
       uint4* dst = reinterpret_cast<uint4*>(xs + r * kPitch + c16);
-      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      dst[0] = make_uint4(xr[u][0], xr[u][1], xr[u][2], xr[u][3]);
+      dst[1] = make_uint4(xr[u][4], xr[u][5], xr[u][6], xr[u][7]);
     }
     if (tid < kCodeThreads) {
       const int r = tid >> 1, h = tid & 1;
@@ -166,14 +174,11 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
         decode16_slot2(cr.z, out + 16);
         decode16_slot2(cr.w, out + 24);
       } else if (LAYOUT == TGS_LAYOUT_BINARY) {
-        decode16_binary(cr.x, out + 0);
-        decode16_binary(cr.x >> 16, out + 8);
-        decode16_binary(cr.y, out + 16);
-        decode16_binary(cr.y >> 16, out + 24);
+        decode32_binary(cr.x, out + 0);
+        decode32_binary(cr.y, out + 16);
       } else {
         // base-3: digit by digit from the packed bytes (not on a measured path)
         const int row = n_base + r;
-        uint32_t w[32];
         const int kk0 = g * 128 + 64 * h;
         for (int e = 0; e < 64; e += 2) {
           uint32_t lo = 0, hi = 0;
@@ -185,9 +190,8 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
             lo = bf16_of_2t_digit(d0 % 3);
             hi = bf16_of_2t_digit(d1 % 3);
           }
-          w[e / 2] = lo | (hi << 16);
+          out[e / 2] = lo | (hi << 16);
         }
-        for (int q = 0; q < 4; ++q) interleave16(w + 8 * q, out + 8 * q);
       }
       uint4* dst = reinterpret_cast<uint4*>(ws + r * kPitch + 64 * h);
 #pragma unroll
@@ -315,7 +319,9 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
 // host picks FB so that a launch is about one workgroup per CU (one round of workgroups) rather
 // than shrinking FB to get more workgroups.
 
-// pairs 4H..4H+3 of decode16_slot2(u): bf16(2t_i) in the low half, bf16(2t_{i+8}) in the high half
+// pairs 4H..4H+3 of the 16 slot-2 codes in u, in the order 0,8,1,9,...: bf16(2t_i) in the low
+// half, bf16(2t_{i+8}) in the high half (the selector puts code i in byte 1 and code i + 8 in
+// byte 3, 0x0C, a constant zero, in bytes 0 and 2; v_perm reads the high byte from the table)
 template <int H>
 __device__ __forceinline__ uint4 decode4_slot2(uint32_t u) {
   constexpr uint32_t kTable = 0x004000C0u;
@@ -329,7 +335,7 @@ __device__ __forceinline__ uint4 decode4_slot2(uint32_t u) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// pairs 4H..4H+3 of decode16_binary(u): bf16(2t_i) low, bf16(2t_{i+8}) high, from bits 0..15 of u
+// the same pairs for 16 binary codes, bits 0..15 of u: bf16(2t_i) low, bf16(2t_{i+8}) high
 template <int H>
 __device__ __forceinline__ uint4 decode4_binary(uint32_t u) {
   constexpr uint32_t kTable = 0x000040C0u;
@@ -343,7 +349,7 @@ __device__ __forceinline__ uint4 decode4_binary(uint32_t u) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// pairs 4H..4H+3 of interleave16 over 16 consecutive bf16 values in w[0..7]
+// pairs 4H..4H+3 in the order 0,8,1,9,... of 16 consecutive bf16 values in w[0..7]
 template <int H>
 __device__ __forceinline__ uint4 interleave4(const uint32_t* w) {
   if constexpr (H == 0)
