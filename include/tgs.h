@@ -203,6 +203,32 @@ tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int
                         const int8_t* signs, float* y, void* stream);
 
 /*
+ * ternary_gemm_ws (device): ternary_gemm with a workspace, which lets a launch that would leave
+ * compute units idle (few output tiles over a long K: e.g. the 5120 x 17408 down projection at
+ * m <= 128) split K across workgroups: part p of P walks the 128-groups [p G / P, (p+1) G / P),
+ * part 0 writes y, every other part writes its own [m][n] fp32 slice of the workspace, and a
+ * second kernel on `stream` adds the parts into y in part order (deterministic: fixed order, no
+ * atomics; the sum differs from ternary_gemm's only by fp32 rounding order). Nothing is allocated.
+ *   w, x, x_dtype, m, signs, y, stream   as for ternary_gemm (same checks, same statuses)
+ *   workspace        device memory, 4-byte aligned, not overlapping x or y, or NULL: then this is
+ *                    ternary_gemm
+ *   workspace_bytes  its size; below ternary_gemm_workspace_size(w, m) (and workspace not NULL):
+ *                    TGS_E_SIZE
+ * The workspace holds no state between calls; calls that overlap in time (different streams)
+ * need workspaces of their own.
+ */
+tgs_status ternary_gemm_ws(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m,
+                           const int8_t* signs, float* y, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * ternary_gemm_workspace_size (host): the bytes of workspace ternary_gemm_ws uses for this matrix
+ * and m (0: that product is not split and needs none). Depends on w's layout, n and k and on m
+ * only. Returns 0 for a descriptor that ternary_gemm would refuse, or m < 1.
+ */
+size_t ternary_gemm_workspace_size(const tgs_matrix* w, int64_t m);
+
+/*
  * hadamard_rotate_g128 (device): y[i][b*128 + r] = (1/sqrt(128)) * sum_c H[r][c] * signs[b*128+c]
  * * x[i][b*128+c] for every row i < m and 128-block b: the block rotation R of [P3] "Block-wise
  * Hadamard rotation" with n = 128 and H the natural-order Sylvester matrix, signs applied first.

@@ -70,6 +70,9 @@ _lib.ternary_gemv.argtypes = [ctypes.POINTER(Matrix), _vp, _i32, _i64, _vp, _vp,
 _lib.ternary_gemv_batched.argtypes = [ctypes.POINTER(Matrix), _i32, ctypes.POINTER(_vp), _i32, _i64,
                                       ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]
 _lib.ternary_gemm.argtypes = [ctypes.POINTER(Matrix), _vp, _i32, _i64, _vp, _vp, _vp]
+_lib.ternary_gemm_ws.argtypes = [ctypes.POINTER(Matrix), _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp]
+_lib.ternary_gemm_workspace_size.argtypes = [ctypes.POINTER(Matrix), _i64]
+_lib.ternary_gemm_workspace_size.restype = _sz
 _lib.hadamard_rotate_g128.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp]
 _lib.hadamard_rotate.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i32, _vp]
 _lib.ternary_gemv_rmsnorm.argtypes = [ctypes.POINTER(Matrix), _vp, _i32, _i64, _vp, ctypes.c_float, _vp, _vp, _vp]
@@ -81,7 +84,7 @@ _lib.ternary_code_flips.argtypes = [ctypes.POINTER(Matrix), ctypes.POINTER(Matri
 _lib.ternary_code_flips_batched.argtypes = [ctypes.POINTER(Matrix), ctypes.POINTER(Matrix), _i32,
                                             ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]
 for _name in ("tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv", "ternary_gemv_batched",
-              "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
+              "ternary_gemm", "ternary_gemm_ws", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
               "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
               "rmsnorm_hadamard_rotate"):
     getattr(_lib, _name).restype = ctypes.c_int
@@ -101,7 +104,8 @@ _lib.tgs_last_error.argtypes = []
 _lib.tgs_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("tgs_code_row_bytes", "tgs_matrix_init", "pack_ternary", "unpack_ternary", "ternary_gemv",
-           "ternary_gemv_batched", "ternary_gemm", "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
+           "ternary_gemv_batched", "ternary_gemm", "ternary_gemm_ws", "ternary_gemm_workspace_size",
+           "hadamard_rotate_g128", "hadamard_rotate", "ternary_code_flips",
            "ternary_code_flips_batched", "ternary_gemv_rmsnorm", "ternary_gemv_rmsnorm_batched",
            "rmsnorm_hadamard_rotate", "tgs_chain_workspace_bytes", "ternary_gemv_chain", "ternary_gemv_chain_static",
            "tgs_stream_read_sink_words", "tgs_stream_read", "tgs_status_string", "tgs_last_error")
@@ -389,14 +393,39 @@ def rmsnorm_hadamard_rotate(x, gamma, eps, signs, block=128, y=None, out_dtype=N
     return y
 
 
-def ternary_gemm(w: PackedMatrix, x, y=None, stream=None):
-    """y[m][n] (fp32) = W x for bf16 x [m][k]. Returns y."""
+def gemm_workspace_bytes(w: PackedMatrix, m: int) -> int:
+    """Bytes of workspace the split product (ternary_gemm_ws) uses for W and m rows; 0: not split."""
+    return int(_lib.ternary_gemm_workspace_size(ctypes.byref(w.desc), int(m)))
+
+
+def ternary_gemm(w: PackedMatrix, x, y=None, stream=None, workspace=None, split=True):
+    """y[m][n] (fp32) = W x for bf16 x [m][k]. Returns y.
+
+    split: a product that would leave compute units idle splits K across workgroups, with the
+    parts' sums in a workspace: `workspace` (a device tensor of at least gemm_workspace_bytes(w, m)
+    bytes, used by no other call at the same time) or, when None, a temporary from torch's
+    allocator on the call's stream. split=False: the single-launch product (ternary_gemm).
+    """
     torch = _torch()
     m = _rows_of(x, w.k)
     _need(x, "x", (torch.bfloat16,))
     y = _out(y, m, w.n, w.device)
     _on_device(w.device, codes=w.codes, scales=w.scales, x=x, y=y)
-    _check(_lib.ternary_gemm(ctypes.byref(w.desc), x.data_ptr(), BF16, m, None, y.data_ptr(), _stream_handle(stream)))
+    handle = _stream_handle(stream)
+    need = gemm_workspace_bytes(w, m) if split else 0
+    if need == 0:
+        _check(_lib.ternary_gemm(ctypes.byref(w.desc), x.data_ptr(), BF16, m, None, y.data_ptr(), handle))
+        return y
+    if workspace is None:
+        on = stream if isinstance(stream, torch.cuda.Stream) else (
+            torch.cuda.current_stream(w.device) if stream is None else torch.cuda.ExternalStream(handle, device=w.device))
+        with torch.cuda.stream(on):
+            workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=w.device)
+    elif workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+        _raise("TGS_E_SIZE", f"workspace must be a contiguous tensor of at least {need} bytes")
+    _on_device(w.device, workspace=workspace)
+    _check(_lib.ternary_gemm_ws(ctypes.byref(w.desc), x.data_ptr(), BF16, m, None, y.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), handle))
     return y
 
 

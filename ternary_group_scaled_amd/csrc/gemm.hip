@@ -20,6 +20,12 @@
 // Both tiles hold k in its natural order. Binary codes (t in {-1, +1}, one bit per weight) decode
 // the same way into bf16 2t in {-2, +2}.
 // Up to 32 activation rows of slot-2 or binary codes take the skinny kernel further below instead.
+//
+// K split across workgroups (both kernels). When a launch would leave CUs idle, the grid gets a
+// third dimension of P parts: part p walks the scale groups [p G / P, (p + 1) G / P). Part 0
+// writes y, part p > 0 writes its own [m][n] fp32 slice of a caller-supplied workspace, and a
+// second kernel adds the parts into y in part order: y = ((y_0 + y_1) + y_2) + ... The sum is
+// deterministic (fixed order, no atomics) and nothing is allocated.
 #include <algorithm>
 
 #include "tgs_internal.h"
@@ -33,6 +39,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kBK = 128;
 constexpr int kPitch = kBK + 16;  // LDS row pitch in bf16 elements (32 bytes of padding: measured best of 132..168)
+// K split across workgroups: the workgroups a launch aims for (skinny: one 8-wave workgroup per
+// CU fits; tiled 64 x 64: 4 waves each)
+constexpr int64_t kSkinnyTarget = 384;
+constexpr int64_t kTileTarget = 640;
+// ... and the fewest 128-groups a part keeps: with fewer, a wave has too few groups to stream
+// (measured: 17408 x 5120, 40 groups, is slower in two parts at 16 and 128 rows)
+constexpr int64_t kMinPartGroups = 32;
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
@@ -107,7 +120,7 @@ template <int LAYOUT, int BM, int BN, int KS>
 __global__ __launch_bounds__(kThreads * KS)
 __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void gemm_tile_kernel(
     const uint8_t* __restrict__ codes, int64_t stride, const uint16_t* __restrict__ scales, int n, int k,
-    const uint16_t* __restrict__ x, int m, float* __restrict__ y) {
+    const uint16_t* __restrict__ x, int m, float* __restrict__ y, float* __restrict__ part_sums) {
   constexpr int kWM = BM / 2, kWN = BN / 2;  // tile of one wave
   constexpr int kBlkM = kWM / 16, kBlkN = kWN / 16;
   constexpr int kXUnits = BM * 8 / kThreads;  // 16-value activation units per thread and group
@@ -123,6 +136,10 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
   uint16_t* ws = ws_all[kh];
   const int n_base = blockIdx.x * BN, m_base = blockIdx.y * BM;
   const int groups = k / 128;
+  // this workgroup's part of K, and where its sums go
+  const int part = (int)blockIdx.z, parts = (int)gridDim.z;
+  const int pg0 = part * groups / parts, pg1 = (part + 1) * groups / parts;
+  float* __restrict__ out = part == 0 ? y : part_sums + (int64_t)(part - 1) * m * n;
 
   // Rows past m (activations) and past n (codes, scales) land beyond their buffers and read as
   // zero; they only feed outputs that are never stored. Offsets are unsigned: the host keeps
@@ -206,14 +223,15 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
     for (int b = 0; b < kBlkN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  // this half takes groups kh, kh + KS, ...; both halves run the same number of iterations (the
-  // barriers are shared), and a group index past the end is loaded harmlessly but not multiplied
-  const int iters = (groups + KS - 1) / KS;
-  load_stage(kh);
-  store_stage(kh);
+  // K part kh takes groups pg0 + kh, pg0 + kh + KS, ...; all KS parts run the same number of
+  // iterations (the barriers are shared), and a group index past pg1 is loaded harmlessly (in
+  // range, or beyond the buffer and read as zero) but not multiplied
+  const int iters = (pg1 - pg0 + KS - 1) / KS;
+  load_stage(pg0 + kh);
+  store_stage(pg0 + kh);
   __syncthreads();
   for (int i = 0; i < iters; ++i) {
-    const int g = i * KS + kh;
+    const int g = pg0 + i * KS + kh;
     const bool more = i + 1 < iters;
     if (more) load_stage(g + KS);
     // this lane's output columns: their scales, loaded ahead of the MFMAs
@@ -243,7 +261,7 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
         for (int b = 0; b < kBlkN; ++b)
           part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], part[a][b], 0, 0, 0);
     }
-    if (KS == 1 || g < groups) {
+    if (KS == 1 || g < pg1) {
 #pragma unroll
       for (int b = 0; b < kBlkN; ++b) {
         const float sc = 0.5f * f16_to_f32((uint16_t)sraw[b]);  // the weights were decoded as 2t
@@ -299,7 +317,7 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m_base + wm * kWM + 16 * a + 4 * (lane >> 4) + r;
-        if (row < m && col < n) y[(int64_t)row * n + col] = acc[a][b][r];
+        if (row < m && col < n) out[(int64_t)row * n + col] = acc[a][b][r];
       }
     }
 }
@@ -362,7 +380,7 @@ template <int TB, int kFB, int kWaves, int kStages, bool BIN>
 __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t* __restrict__ codes, int64_t stride,
                                                           const uint16_t* __restrict__ scales, int n, int k,
                                                           const uint16_t* __restrict__ x, int m,
-                                                          float* __restrict__ y) {
+                                                          float* __restrict__ y, float* __restrict__ part_sums) {
   // kFB: 16-output blocks per workgroup; kWaves: K slices (waves) per workgroup; kStages: groups
   // of loads in flight per wave
   __shared__ float red[kWaves][TB * kFB * 4][64];
@@ -371,7 +389,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
   const int fr = lane & 15, kq = lane >> 4;  // fragment row and k quarter
   const int n_base = blockIdx.x * 16 * kFB, m_base = blockIdx.y * 16 * TB;
   const int groups = k / 128;
-  const int g_begin = wave * groups / kWaves, g_end = (wave + 1) * groups / kWaves;
+  // this workgroup's part of K: groups [pg0, pg0 + pgn); wave w takes pg0 + w, pg0 + w + W, ...,
+  // so that the waves of a workgroup read every row front to back together
+  const int part = (int)blockIdx.z, parts = (int)gridDim.z;
+  const int pg0 = part * groups / parts, pgn = (part + 1) * groups / parts - pg0;
+  float* __restrict__ out = part == 0 ? y : part_sums + (int64_t)(part - 1) * m * n;
 
   // reads past each buffer (rows >= n, activation rows >= m) return zero
   const __amdgpu_buffer_rsrc_t code_rsrc =
@@ -406,13 +428,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
   };
   // Every workgroup reads the same activations; if all started at the same group, hundreds of CUs
   // would request the same few L2 lines at once. Each workgroup walks its waves' groups in a
-  // rotated order instead: its i-th group is g_begin + (i + rot) mod count.
-  const int count = g_end - g_begin;
+  // rotated order instead: a wave's i-th group is its ((i + rot) mod count)-th.
+  const int count = (pgn - wave + kWaves - 1) / kWaves;
   const int rot = count > 0 ? (int)(blockIdx.x % (unsigned)count) : 0;
   auto load = [&](Stage& st, int i) {
     const bool live = i < count;
-    int g = g_begin + i + rot;
-    if (g >= g_end) g -= count;
+    int j = i + rot;
+    if (j >= count) j -= count;
+    const int g = pg0 + wave + kWaves * j;
 #pragma unroll
     for (int fb = 0; fb < kFB; ++fb) {
       if constexpr (BIN) {  // 16 bytes of codes per group
@@ -514,27 +537,96 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) sum += red[w][idx][ln];
     const int row = m_base + 16 * tb + 4 * (ln >> 4) + r, col = n_base + 16 * fb + (ln & 15);
-    if (row < m && col < n) y[(int64_t)row * n + col] = sum;
+    if (row < m && col < n) out[(int64_t)row * n + col] = sum;
   }
 }
 
-template <int LAYOUT>
-hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
-                         const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
-  constexpr bool kBin = LAYOUT == TGS_LAYOUT_BINARY;
-  if ((LAYOUT == TGS_LAYOUT_SLOT2 || kBin) && m <= 32) {
-    const int ni = (int)n, ki = (int)k, mi = (int)m;
+// How one launch (at most a chunk of activation rows) is laid out.
+struct GemmPlan {
+  int kind;    // 0: skinny, up to 16 rows; 1: skinny, 17..32 rows; 2: tiled
+  int fb;      // skinny: 16-output blocks per workgroup
+  int bm, bn;  // tiled: tile shape
+  int ks;      // tiled: K parts inside a workgroup
+  int parts;   // K parts across workgroups (the grid's third dimension)
+  int64_t wgs; // workgroups of one part
+};
+
+GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
+  GemmPlan p{};
+  const int64_t groups = k / 128;
+  // parts for a launch of `wgs` workgroups: enough to give the CUs about `target` workgroups,
+  // each part keeping at least `min_groups` scale groups
+  auto parts_for = [&](int64_t wgs, int64_t target, int64_t max_parts, int64_t min_groups) {
+    if (!split) return 1;
+    int64_t q = (target + wgs - 1) / wgs;
+    q = std::min(q, max_parts);
+    q = std::min(q, groups / min_groups);
+    return (int)std::max<int64_t>(1, q);
+  };
+  if ((layout == TGS_LAYOUT_SLOT2 || layout == TGS_LAYOUT_BINARY) && m <= 32) {
     if (m <= 16) {
       // 16 * FB outputs per workgroup of 8 waves, FB = n / 4096 rounded up, within 2..6: about one
       // workgroup per CU (the kernel's registers allow one), and every workgroup reads all of x,
       // so its L2 traffic falls as FB grows. (Measured on 17408 x 5120 and 5120 x 17408: FB = 5
       // and 2 beat both neighbours and the 16-wave variants.)
-      const int64_t fb = std::min<int64_t>(6, std::max<int64_t>(2, (n + 4095) / 4096));
-      const dim3 grid((unsigned)((n + 16 * fb - 1) / (16 * fb)));
+      p.kind = 0;
+      p.fb = (int)std::min<int64_t>(6, std::max<int64_t>(2, (n + 4095) / 4096));
+      p.wgs = (n + 16 * p.fb - 1) / (16 * p.fb);
+      p.parts = parts_for(p.wgs, kSkinnyTarget, 4, kMinPartGroups);
+    } else {
+      // 16 outputs per block: the most (4, 2, 1) that still gives 512 workgroups
+      p.kind = 1;
+      p.fb = (n + 63) / 64 >= 512 ? 4 : ((n + 31) / 32 >= 512 ? 2 : 1);
+      p.wgs = (n + 16 * p.fb - 1) / (16 * p.fb) * ((m + 31) / 32);
+      p.parts = 1;
+    }
+    return p;
+  }
+  // tiles: 128 x 128 for many activation rows, else 64 rows; 64 columns when 128 gives too few
+  // tiles. With too few tiles even then, K is split: across workgroups when a workspace is given
+  // (each part is a workgroup of its own, so the parts spread over all CUs), else inside the
+  // workgroup (two or four parts of 4 waves, added through LDS).
+  p.kind = 2;
+  p.bm = m > 128 ? 128 : 64;
+  const int64_t m_tiles = (m + p.bm - 1) / p.bm;
+  p.bn = (n + 127) / 128 * m_tiles >= 512 ? 128 : 64;
+  const int64_t tiles = (n + p.bn - 1) / p.bn * m_tiles;
+  p.wgs = tiles;
+  p.parts = p.bm == 64 && p.bn == 64 ? parts_for(tiles, kTileTarget, 4, kMinPartGroups) : 1;
+  p.ks = 1;
+  if (p.parts == 1) {
+    const bool ks2 = tiles < 512 && groups >= 16;
+    // four K parts for few 64 x 64 tiles over a long K: every part walks a quarter of the groups,
+    // and each group iteration waits out about one HBM latency
+    const bool ks4 = ks2 && p.bm == 64 && p.bn == 64 && tiles < 256 && groups >= 64;
+    p.ks = ks4 ? 4 : (ks2 && p.bn == 64 ? 2 : 1);  // (128-column tiles come with >= 512 tiles)
+  }
+  return p;
+}
+
+// y[i] += ws[0][i] + ws[1][i] + ... (parts 1, 2, ... of a split launch), added in part order
+__global__ __launch_bounds__(256) void gemm_parts_add_kernel(float* __restrict__ y, const float* __restrict__ ws,
+                                                             int64_t count, int extra) {
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += step) {
+    float v = y[i];
+    for (int q = 0; q < extra; ++q) v += ws[q * count + i];
+    y[i] = v;
+  }
+}
+
+template <int LAYOUT>
+hipError_t launch_layout(const GemmPlan& p, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n,
+                         int64_t k, const uint16_t* x, int64_t m, float* y, float* ws, hipStream_t stream) {
+  constexpr bool kBin = LAYOUT == TGS_LAYOUT_BINARY;
+  const int ni = (int)n, ki = (int)k, mi = (int)m;
+  if (p.kind == 0) {
+    if constexpr (LAYOUT == TGS_LAYOUT_SLOT2 || kBin) {
+      const dim3 grid((unsigned)p.wgs, 1, (unsigned)p.parts);
 #define TGS_SKINNY(FB_)                                                                                          \
   hipLaunchKernelGGL((gemm_skinny_kernel<1, FB_, 8, 2, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, \
-                     ki, x, mi, y)
-      switch (fb) {
+                     ki, x, mi, y, ws)
+      switch (p.fb) {
         case 2: TGS_SKINNY(2); break;
         case 3: TGS_SKINNY(3); break;
         case 4: TGS_SKINNY(4); break;
@@ -542,65 +634,69 @@ hipError_t launch_layout(const uint8_t* codes, int64_t stride, const uint16_t* s
         default: TGS_SKINNY(6); break;
       }
 #undef TGS_SKINNY
-    } else {
-      // 16 outputs per block: the most (4, 2, 1) that still gives 512 workgroups
-      const int64_t fb = (n + 63) / 64 >= 512 ? 4 : ((n + 31) / 32 >= 512 ? 2 : 1);
-      const dim3 grid((unsigned)((n + 16 * fb - 1) / (16 * fb)), (unsigned)((m + 31) / 32));
-      if (fb == 4)
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, 4, 8, 3, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
-                           x, mi, y);
-      else if (fb == 2)
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, 2, 8, 3, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
-                           x, mi, y);
-      else
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, 1, 8, 3, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, ki,
-                           x, mi, y);
     }
-    return hipGetLastError();
-  }
-  // tiles: 128 x 128 for many activation rows, else 64 rows; 64 columns when 128 gives too few tiles;
-  // K split in two inside the workgroup when even then there are fewer than 512 tiles
-  const int bm = m > 128 ? 128 : 64;
-  const int64_t m_tiles = (m + bm - 1) / bm;
-  const int bn = (n + 127) / 128 * m_tiles >= 512 ? 128 : 64;
-  const int64_t tiles = (n + bn - 1) / bn * m_tiles;
-  const bool ks2 = tiles < 512 && k / 128 >= 16;
-  // four K parts for few 64 x 64 tiles over a long K: every part walks a quarter of the groups, and
-  // each group iteration waits out about one HBM latency
-  const bool ks4 = ks2 && bm == 64 && bn == 64 && tiles < 256 && k / 128 >= 64;
-  const dim3 grid((unsigned)((n + bn - 1) / bn), (unsigned)m_tiles);
-  const int ni = (int)n, ki = (int)k, mi = (int)m;
+  } else if (p.kind == 1) {
+    if constexpr (LAYOUT == TGS_LAYOUT_SLOT2 || kBin) {
+      const dim3 grid((unsigned)((n + 16 * p.fb - 1) / (16 * p.fb)), (unsigned)((m + 31) / 32), (unsigned)p.parts);
+#define TGS_SKINNY2(FB_)                                                                                          \
+  hipLaunchKernelGGL((gemm_skinny_kernel<2, FB_, 8, 3, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, \
+                     ki, x, mi, y, ws)
+      if (p.fb == 4) TGS_SKINNY2(4); else if (p.fb == 2) TGS_SKINNY2(2); else TGS_SKINNY2(1);
+#undef TGS_SKINNY2
+    }
+  } else {
+    const dim3 grid((unsigned)((n + p.bn - 1) / p.bn), (unsigned)((m + p.bm - 1) / p.bm), (unsigned)p.parts);
 #define TGS_TILE(BM_, BN_, KS_)                                                                           \
   hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, BM_, BN_, KS_>), grid, dim3(kThreads * KS_), 0, stream, codes, \
-                     stride, scales, ni, ki, x, mi, y)
-  // (128-column tiles are only chosen with >= 512 tiles, so never with the K split)
-  if (bm == 128 && bn == 128) {
-    TGS_TILE(128, 128, 1);
-  } else if (bm == 128) {
-    if (ks2) TGS_TILE(128, 64, 2); else TGS_TILE(128, 64, 1);
-  } else if (bn == 128) {
-    TGS_TILE(64, 128, 1);
-  } else {
-    if (ks4) TGS_TILE(64, 64, 4); else if (ks2) TGS_TILE(64, 64, 2); else TGS_TILE(64, 64, 1);
-  }
+                     stride, scales, ni, ki, x, mi, y, ws)
+    if (p.bm == 128 && p.bn == 128) {
+      TGS_TILE(128, 128, 1);
+    } else if (p.bm == 128) {
+      if (p.ks == 2) TGS_TILE(128, 64, 2); else TGS_TILE(128, 64, 1);
+    } else if (p.bn == 128) {
+      TGS_TILE(64, 128, 1);
+    } else {
+      if (p.ks == 4) TGS_TILE(64, 64, 4); else if (p.ks == 2) TGS_TILE(64, 64, 2); else TGS_TILE(64, 64, 1);
+    }
 #undef TGS_TILE
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.parts == 1) return e;
+  const int64_t count = m * n;
+  const int64_t blocks = std::min<int64_t>(2048, (count + 255) / 256);
+  hipLaunchKernelGGL(gemm_parts_add_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, ws, count, p.parts - 1);
   return hipGetLastError();
 }
 
+// activation rows per launch: the kernels address x with 32-bit offsets (m * k * 2 < 2^31)
+int64_t rows_per_launch(int64_t k) { return std::max<int64_t>(128, (kMaxDeviceCodeBytes / (2 * k)) / 128 * 128); }
+
 }  // namespace
 
+size_t gemm_workspace_bytes(int32_t layout, int64_t n, int64_t k, int64_t m) {
+  const int64_t rows = rows_per_launch(k);
+  size_t bytes = 0;
+  // the full chunks and the last one (the only launch shapes)
+  for (const int64_t mr : {std::min(rows, m), m % rows}) {
+    if (mr <= 0) continue;
+    const GemmPlan p = plan_of(layout, n, k, mr, true);
+    bytes = std::max(bytes, (size_t)(p.parts - 1) * (size_t)mr * (size_t)n * sizeof(float));
+  }
+  return bytes;
+}
+
 hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n,
-                       int64_t k, const uint16_t* x_bf16, int64_t m, float* y, hipStream_t stream) {
-  // activation rows per launch: the kernels address x with 32-bit offsets (m * k * 2 < 2^31)
-  const int64_t max_rows = std::max<int64_t>(128, (kMaxDeviceCodeBytes / (2 * k)) / 128 * 128);
+                       int64_t k, const uint16_t* x_bf16, int64_t m, float* y, float* ws, hipStream_t stream) {
+  const int64_t max_rows = rows_per_launch(k);
   for (int64_t r0 = 0; r0 < m; r0 += max_rows) {
     const int64_t mr = std::min(max_rows, m - r0);
     const uint16_t* xr = x_bf16 + r0 * k;
     float* yr = y + r0 * n;
+    const GemmPlan p = plan_of(layout, n, k, mr, ws != nullptr);
     const hipError_t e =
-        layout == TGS_LAYOUT_SLOT2   ? launch_layout<TGS_LAYOUT_SLOT2>(codes, stride, scales, n, k, xr, mr, yr, stream)
-        : layout == TGS_LAYOUT_BASE3 ? launch_layout<TGS_LAYOUT_BASE3>(codes, stride, scales, n, k, xr, mr, yr, stream)
-                                     : launch_layout<TGS_LAYOUT_BINARY>(codes, stride, scales, n, k, xr, mr, yr, stream);
+        layout == TGS_LAYOUT_SLOT2   ? launch_layout<TGS_LAYOUT_SLOT2>(p, codes, stride, scales, n, k, xr, mr, yr, ws, stream)
+        : layout == TGS_LAYOUT_BASE3 ? launch_layout<TGS_LAYOUT_BASE3>(p, codes, stride, scales, n, k, xr, mr, yr, ws, stream)
+                                     : launch_layout<TGS_LAYOUT_BINARY>(p, codes, stride, scales, n, k, xr, mr, yr, ws, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

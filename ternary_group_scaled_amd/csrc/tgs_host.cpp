@@ -447,6 +447,11 @@ tgs_status ternary_gemv(const tgs_matrix* w, const void* x, int32_t x_dtype, int
 
 tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m, const int8_t* signs, float* y,
                         void* stream) {
+  return ternary_gemm_ws(w, x, x_dtype, m, signs, y, nullptr, 0, stream);
+}
+
+tgs_status ternary_gemm_ws(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m, const int8_t* signs,
+                           float* y, void* workspace, size_t workspace_bytes, void* stream) {
   tgs_status st = check_matrix(w, true);
   if (st != TGS_OK) return st;
   if (w->rotated)
@@ -461,10 +466,26 @@ tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int
   if (!x || !y) return fail(TGS_E_NULL, "x or y is NULL");
   if (!aligned(x, 16)) return fail(TGS_E_ALIGN, "x must be 16-byte aligned");
   if (!aligned(y, 4)) return fail(TGS_E_ALIGN, "y must be 4-byte aligned");
+  float* ws = static_cast<float*>(workspace);
+  if (ws) {
+    if (!aligned(ws, 4)) return fail(TGS_E_ALIGN, "workspace must be 4-byte aligned");
+    const size_t need = tgs::gemm_workspace_bytes(w->layout, w->n, w->k, m);
+    if (workspace_bytes < need)
+      return fail(TGS_E_SIZE, "workspace of %zu bytes, this product needs %zu", workspace_bytes, need);
+    if (need == 0) ws = nullptr;  // not split
+  }
   hipError_t e = tgs::gemm_launch(w->layout, static_cast<const uint8_t*>(w->codes), w->code_row_stride, w->scales,
-                                  w->n, w->k, static_cast<const uint16_t*>(x), m, y, static_cast<hipStream_t>(stream));
+                                  w->n, w->k, static_cast<const uint16_t*>(x), m, y, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "ternary_gemm launch");
   return ok();
+}
+
+size_t ternary_gemm_workspace_size(const tgs_matrix* w, int64_t m) {
+  if (check_matrix(w, true) != TGS_OK || w->rotated || m < 1 || m > (1LL << 30) ||
+      w->k > tgs::kMaxDeviceCodeBytes / (128 * 2))
+    return 0;
+  ok();
+  return tgs::gemm_workspace_bytes(w->layout, w->n, w->k, m);
 }
 
 tgs_status hadamard_rotate(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block, const int8_t* signs,

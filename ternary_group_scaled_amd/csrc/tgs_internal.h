@@ -179,8 +179,10 @@ struct FlipArgs {
 int code_flip_rows_per_block();
 hipError_t code_flip_launch(FlipArgs& args, int32_t blocks, hipStream_t stream);
 
+// ws: NULL (no K split across workgroups), or gemm_workspace_bytes of device memory
 hipError_t gemm_launch(int32_t layout, const uint8_t* codes, int64_t stride, const uint16_t* scales, int64_t n, int64_t k,
-                       const uint16_t* x_bf16, int64_t m, float* y, hipStream_t stream);
+                       const uint16_t* x_bf16, int64_t m, float* y, float* ws, hipStream_t stream);
+size_t gemm_workspace_bytes(int32_t layout, int64_t n, int64_t k, int64_t m);
 
 hipError_t hadamard_launch(const void* x, int32_t x_dtype, int64_t m, int64_t k, int64_t block, const int8_t* signs,
                            void* y, int32_t y_dtype, hipStream_t stream);

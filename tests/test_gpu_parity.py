@@ -4,6 +4,8 @@ Tolerance per element: |y - y_ref| <= 1e-3 * sum_k |s t xr| + 1e-6 (the oracle's
 rotated activation for rotated weights. Packing must be bit-exact. Exact equalities hold where every
 partial sum is exactly representable in fp32 (integer activations, power-of-two scales).
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -353,10 +355,10 @@ def test_misaligned_signs_are_refused():
 
 # ------------------------------------------------------------------------------ GEMM
 
-def _gemm(layout, t, s, xbits):
+def _gemm(layout, t, s, xbits, split=True):
     w = _packed(layout, t, s)
     xt = torch.from_numpy(xbits.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
-    y = tgs.ternary_gemm(w, xt)
+    y = tgs.ternary_gemm(w, xt, split=split)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -412,17 +414,83 @@ def test_gemm_sixteen_rows_integer_inputs_are_exact():
     assert (y_gemm.astype(np.float64) == y_ref).all()
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["in_workgroup", "across_workgroups"])
 @pytest.mark.parametrize("layout", ROT_LAYOUTS, ids=["slot2", "base3", "binary"])
 @pytest.mark.parametrize("n,k,m", [(300, 8192, 100), (200, 8448, 40), (1000, 16384, 128)])
-def test_gemm_four_k_parts(layout, n, k, m):
-    """Few 64 x 64 tiles over a long K (at least 64 groups) split K in four parts inside the
-    workgroup; 8448 = 66 groups leaves the last parts' final group past the end (loaded, not
-    multiplied). The parts' sums are added in part order."""
+def test_gemm_four_k_parts(layout, n, k, m, split):
+    """Few 64 x 64 tiles over a long K (at least 64 groups) split K in four parts: inside the
+    workgroup without a workspace (8448 = 66 groups leaves the last parts' final group past the
+    end: loaded, not multiplied), or across workgroups with one. Either way the parts' sums are
+    added in part order."""
     t, s = make_weights(n + k + m, f"gemm4k{layout}", n, k, 0.0 if layout == tgs.BINARY else 0.4)
     xb = make_x_bf16_bits(n + m, "gemm4kx", m, k)
-    y = _gemm(layout, t, s, xb)
+    y = _gemm(layout, t, s, xb, split=split)
     y_ref, bound = oracle_product(layout, t, s, xb, oracle.X_BF16)
     assert_within_bound(y, y_ref, bound, f"gemm four K parts layout {layout} {n}x{k} m={m}")
+
+
+# (n, k, m, parts): K split across workgroups. Skinny kernel (m <= 16): 16 * FB outputs per
+# workgroup, parts = min(ceil(384 / workgroups), 4, groups / 32). Tiled kernel (64 x 64 tiles,
+# 33 <= m <= 128): parts = min(ceil(640 / tiles), 4, groups / 32). Ragged n, parts that do not
+# divide the groups (130 / 4, 65 / 2, 66 / 2), one row, parts of exactly 32 groups, and a product
+# with too few groups to split.
+SPLIT_CASES = [(512, 16384, 1, 4), (1000, 16640, 16, 4), (70, 8320, 5, 2), (4100, 8192, 16, 2), (600, 16384, 100, 4),
+               (130, 8448, 64, 2), (64, 4096, 33, 1)]
+
+
+def _split_parts(n, k, m, layout):
+    w = _packed(layout, *make_weights(1, "splitshape", n, k, 0.4 if layout != tgs.BINARY else 0.0))
+    return tgs.gemm_workspace_bytes(w, m) // (4 * m * n) + 1
+
+
+@pytest.mark.parametrize("layout", ROT_LAYOUTS, ids=["slot2", "base3", "binary"])
+@pytest.mark.parametrize("n,k,m,parts", SPLIT_CASES)
+def test_gemm_split_across_workgroups(layout, n, k, m, parts):
+    """The K split across workgroups (ternary_gemm_ws): within the bound of the oracle, the
+    workspace size is (parts - 1) * m * n fp32, and repeated calls are bit-identical (the parts
+    are added in part order, no atomics). The single-launch product is within the bound too."""
+    if layout == tgs.BASE3 and m <= 32:
+        parts = _split_parts(n, k, m, layout)  # base-3 always takes the tiled kernel
+    t, s = make_weights(n + k + m, f"gemmsplit{layout}", n, k, 0.0 if layout == tgs.BINARY else 0.4)
+    xb = make_x_bf16_bits(n + m, "gemmsplitx", m, k)
+    w = _packed(layout, t, s)
+    assert tgs.gemm_workspace_bytes(w, m) == (parts - 1) * m * n * 4
+    xt = torch.from_numpy(xb.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    y1 = tgs.ternary_gemm(w, xt).cpu().numpy()
+    ws = torch.full((max(1, (parts - 1) * m * n),), float("nan"), device=DEV)  # no state between calls
+    y2 = tgs.ternary_gemm(w, xt, workspace=ws).cpu().numpy()
+    y0 = tgs.ternary_gemm(w, xt, split=False).cpu().numpy()
+    y_ref, bound = oracle_product(layout, t, s, xb, oracle.X_BF16)
+    assert_within_bound(y1, y_ref, bound, f"gemm split layout {layout} {n}x{k} m={m} parts={parts}")
+    assert_within_bound(y0, y_ref, bound, f"gemm unsplit layout {layout} {n}x{k} m={m}")
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+
+
+def test_gemm_split_workspace_checks():
+    """A workspace below the needed size is refused (binding and C entry point) before any launch;
+    a NULL workspace is the single-launch product; a product that is not split needs none."""
+    n, k, m = 512, 16384, 16
+    t, s = make_weights(5, "gemmsplitws", n, k, 0.4)
+    w = _packed(tgs.SLOT2, t, s)
+    need = tgs.gemm_workspace_bytes(w, m)
+    assert need == 3 * m * n * 4
+    xt = torch.from_numpy(make_x_bf16_bits(5, "gemmsplitwsx", m, k).view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    y = torch.zeros(m, n, device=DEV)
+    with pytest.raises(tgs.TgsError) as e:
+        tgs.ternary_gemm(w, xt, y, workspace=torch.empty(need // 4 - 1, device=DEV))
+    assert e.value.status == 7
+    small = torch.empty(need // 4 - 1, device=DEV)
+    st = tgs.lib().ternary_gemm_ws(ctypes.byref(w.desc), xt.data_ptr(), tgs.BF16, m, None, y.data_ptr(),
+                                   small.data_ptr(), need - 4, None)
+    assert st == 7 and not y.any()
+    st = tgs.lib().ternary_gemm_ws(ctypes.byref(w.desc), xt.data_ptr(), tgs.BF16, m, None, y.data_ptr(), None, 0,
+                                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    y0 = tgs.ternary_gemm(w, xt, split=False)
+    assert torch.equal(y, y0)
+    w_short = _packed(tgs.SLOT2, *make_weights(6, "gemmsplitws2", 512, 5120, 0.4))
+    assert tgs.gemm_workspace_bytes(w_short, m) == 0  # 40 groups: too few to split
 
 
 def test_gemm_large_tiles_sampled():
