@@ -21,11 +21,13 @@
 // the same way into bf16 2t in {-2, +2}.
 // Up to 32 activation rows of slot-2 or binary codes take the skinny kernel further below instead.
 //
-// K split across workgroups (both kernels). When a launch would leave CUs idle, the grid gets a
-// third dimension of P parts: part p walks the scale groups [p G / P, (p + 1) G / P). Part 0
-// writes y, part p > 0 writes its own [m][n] fp32 slice of a caller-supplied workspace, and a
-// second kernel adds the parts into y in part order: y = ((y_0 + y_1) + y_2) + ... The sum is
-// deterministic (fixed order, no atomics) and nothing is allocated.
+// K split across workgroups (both kernels). When a launch would leave CUs idle, some outputs are
+// computed in P parts: part p walks the scale groups [p G / P, (p + 1) G / P). Part 0 writes y,
+// part p > 0 writes its sums to a caller-supplied workspace, and a second kernel adds the parts
+// into y in part order: y = ((y_0 + y_1) + y_2) + ... The sum is deterministic (fixed order, no
+// atomics) and nothing is allocated. The skinny kernel splits every output ([m][n] workspace slice
+// per part); the tiled kernel takes whole tiles first, for as many full rounds of workgroups as
+// the tiles fill, and splits only the tiles left over for the last round ([tile][BM][BN] slices).
 #include <algorithm>
 
 #include "tgs_internal.h"
@@ -46,6 +48,10 @@ constexpr int64_t kTileTarget = 640;
 // ... and the fewest 128-groups a part keeps: with fewer, a wave has too few groups to stream
 // (measured: 17408 x 5120, 40 groups, is slower in two parts at 16 and 128 rows)
 constexpr int64_t kMinPartGroups = 32;
+// 128 x 128 tiles: workgroups resident at once (two per CU), and the fewest groups a part of a
+// tail tile keeps
+constexpr int64_t kTileSlots = 512;
+constexpr int64_t kMinTailGroups = 8;
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
@@ -120,7 +126,8 @@ template <int LAYOUT, int BM, int BN, int KS>
 __global__ __launch_bounds__(kThreads * KS)
 __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void gemm_tile_kernel(
     const uint8_t* __restrict__ codes, int64_t stride, const uint16_t* __restrict__ scales, int n, int k,
-    const uint16_t* __restrict__ x, int m, float* __restrict__ y, float* __restrict__ part_sums) {
+    const uint16_t* __restrict__ x, int m, float* __restrict__ y, float* __restrict__ part_sums, int n_tiles,
+    int whole, int parts) {
   constexpr int kWM = BM / 2, kWN = BN / 2;  // tile of one wave
   constexpr int kBlkM = kWM / 16, kBlkN = kWN / 16;
   constexpr int kXUnits = BM * 8 / kThreads;  // 16-value activation units per thread and group
@@ -134,12 +141,18 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
   const int wm = wave >> 1, wn = wave & 1;
   uint16_t* xs = xs_all[kh];
   uint16_t* ws = ws_all[kh];
-  const int n_base = blockIdx.x * BN, m_base = blockIdx.y * BM;
+  // Workgroups [0, whole) take tiles 0.. whole; workgroup whole + j * parts + p takes part p of
+  // tile whole + j. Tile t is column tile t % n_tiles of row tile t / n_tiles.
+  const int id = (int)blockIdx.x;
+  const int j = id < whole ? 0 : (id - whole) / parts;
+  const int tile = id < whole ? id : whole + j;
+  const int part = id < whole ? 0 : id - whole - j * parts, nparts = id < whole ? 1 : parts;
+  const int n_base = (tile % n_tiles) * BN, m_base = (tile / n_tiles) * BM;
   const int groups = k / 128;
-  // this workgroup's part of K, and where its sums go
-  const int part = (int)blockIdx.z, parts = (int)gridDim.z;
-  const int pg0 = part * groups / parts, pg1 = (part + 1) * groups / parts;
-  float* __restrict__ out = part == 0 ? y : part_sums + (int64_t)(part - 1) * m * n;
+  const int pg0 = part * groups / nparts, pg1 = (part + 1) * groups / nparts;
+  // where the sums go: y, or this part's [BM][BN] slice for the tile in the workspace
+  const int tail = (int)((gridDim.x - (unsigned)whole) / (unsigned)parts);
+  float* __restrict__ slice = part > 0 ? part_sums + ((int64_t)(part - 1) * tail + j) * (BM * BN) : nullptr;
 
   // Rows past m (activations) and past n (codes, scales) land beyond their buffers and read as
   // zero; they only feed outputs that are never stored. Offsets are unsigned: the host keeps
@@ -317,7 +330,12 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m_base + wm * kWM + 16 * a + 4 * (lane >> 4) + r;
-        if (row < m && col < n) out[(int64_t)row * n + col] = acc[a][b][r];
+        if (row < m && col < n) {
+          if (part == 0)
+            y[(int64_t)row * n + col] = acc[a][b][r];
+          else
+            slice[(row - m_base) * BN + (col - n_base)] = acc[a][b][r];
+        }
       }
     }
 }
@@ -547,8 +565,10 @@ struct GemmPlan {
   int fb;      // skinny: 16-output blocks per workgroup
   int bm, bn;  // tiled: tile shape
   int ks;      // tiled: K parts inside a workgroup
-  int parts;   // K parts across workgroups (the grid's third dimension)
-  int64_t wgs; // workgroups of one part
+  int parts;   // K parts across workgroups (skinny: of every output; tiled: of the tail tiles)
+  int64_t wgs; // workgroups of one part (skinny), tiles (tiled)
+  int64_t whole, tail;  // tiled: tiles taken whole, then tiles split in `parts`
+  int64_t n_tiles;      // tiled: column tiles
 };
 
 GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
@@ -590,9 +610,23 @@ GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
   p.bm = m > 128 ? 128 : 64;
   const int64_t m_tiles = (m + p.bm - 1) / p.bm;
   p.bn = (n + 127) / 128 * m_tiles >= 512 ? 128 : 64;
-  const int64_t tiles = (n + p.bn - 1) / p.bn * m_tiles;
+  p.n_tiles = (n + p.bn - 1) / p.bn;
+  const int64_t tiles = p.n_tiles * m_tiles;
   p.wgs = tiles;
-  p.parts = p.bm == 64 && p.bn == 64 ? parts_for(tiles, kTileTarget, 4, kMinPartGroups) : 1;
+  p.parts = 1;
+  p.whole = tiles;
+  p.tail = 0;
+  if (p.bm == 64 && p.bn == 64) {
+    // few small tiles over a long K: every tile in parts
+    p.parts = parts_for(tiles, kTileTarget, 4, kMinPartGroups);
+    if (p.parts > 1) p.whole = 0, p.tail = tiles;
+  } else if (p.bm == 128 && p.bn == 128 && split) {
+    // 128 x 128 tiles run two workgroups per CU (kTileSlots at a time): whole tiles for the full
+    // rounds, and the tiles left over for a last, partly empty round in up to 4 parts that fill it
+    const int64_t rem = tiles % kTileSlots;
+    const int64_t q = rem > 0 ? std::min<int64_t>({4, kTileSlots / rem, groups / kMinTailGroups}) : 1;
+    if (q > 1) p.parts = (int)q, p.whole = tiles - rem, p.tail = rem;
+  }
   p.ks = 1;
   if (p.parts == 1) {
     const bool ks2 = tiles < 512 && groups >= 16;
@@ -612,6 +646,24 @@ __global__ __launch_bounds__(256) void gemm_parts_add_kernel(float* __restrict__
     float v = y[i];
     for (int q = 0; q < extra; ++q) v += ws[q * count + i];
     y[i] = v;
+  }
+}
+
+// the same for the split tiles of the tiled kernel: y over tail tile j += its slices of parts
+// 1, 2, ... ([part - 1][j][BM][BN] in ws), in part order
+__global__ __launch_bounds__(256) void gemm_tile_parts_add_kernel(float* __restrict__ y, const float* __restrict__ ws,
+                                                                  int m, int n, int n_tiles, int whole, int tail,
+                                                                  int extra, int bm, int bn) {
+  const int64_t per = (int64_t)bm * bn, count = (int64_t)tail * per;
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count; e += step) {
+    const int j = (int)(e / per), l = (int)(e - (int64_t)j * per);
+    const int tile = whole + j;
+    const int row = (tile / n_tiles) * bm + l / bn, col = (tile % n_tiles) * bn + l % bn;
+    if (row >= m || col >= n) continue;
+    float v = y[(int64_t)row * n + col];
+    for (int q = 0; q < extra; ++q) v += ws[((int64_t)q * tail + j) * per + l];
+    y[(int64_t)row * n + col] = v;
   }
 }
 
@@ -645,10 +697,10 @@ hipError_t launch_layout(const GemmPlan& p, const uint8_t* codes, int64_t stride
 #undef TGS_SKINNY2
     }
   } else {
-    const dim3 grid((unsigned)((n + p.bn - 1) / p.bn), (unsigned)((m + p.bm - 1) / p.bm), (unsigned)p.parts);
+    const dim3 grid((unsigned)(p.whole + p.tail * p.parts));
 #define TGS_TILE(BM_, BN_, KS_)                                                                           \
   hipLaunchKernelGGL((gemm_tile_kernel<LAYOUT, BM_, BN_, KS_>), grid, dim3(kThreads * KS_), 0, stream, codes, \
-                     stride, scales, ni, ki, x, mi, y, ws)
+                     stride, scales, ni, ki, x, mi, y, ws, (int)p.n_tiles, (int)p.whole, p.parts)
     if (p.bm == 128 && p.bn == 128) {
       TGS_TILE(128, 128, 1);
     } else if (p.bm == 128) {
@@ -662,9 +714,16 @@ hipError_t launch_layout(const GemmPlan& p, const uint8_t* codes, int64_t stride
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.parts == 1) return e;
-  const int64_t count = m * n;
-  const int64_t blocks = std::min<int64_t>(2048, (count + 255) / 256);
-  hipLaunchKernelGGL(gemm_parts_add_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, ws, count, p.parts - 1);
+  if (p.kind == 2) {
+    const int64_t count = p.tail * p.bm * p.bn;
+    const int64_t blocks = std::min<int64_t>(4096, (count + 255) / 256);
+    hipLaunchKernelGGL(gemm_tile_parts_add_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, ws, mi, ni,
+                       (int)p.n_tiles, (int)p.whole, (int)p.tail, p.parts - 1, p.bm, p.bn);
+  } else {
+    const int64_t count = m * n;
+    const int64_t blocks = std::min<int64_t>(2048, (count + 255) / 256);
+    hipLaunchKernelGGL(gemm_parts_add_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, ws, count, p.parts - 1);
+  }
   return hipGetLastError();
 }
 
@@ -680,7 +739,8 @@ size_t gemm_workspace_bytes(int32_t layout, int64_t n, int64_t k, int64_t m) {
   for (const int64_t mr : {std::min(rows, m), m % rows}) {
     if (mr <= 0) continue;
     const GemmPlan p = plan_of(layout, n, k, mr, true);
-    bytes = std::max(bytes, (size_t)(p.parts - 1) * (size_t)mr * (size_t)n * sizeof(float));
+    const size_t per_part = p.kind == 2 ? (size_t)p.tail * p.bm * p.bn : (size_t)mr * (size_t)n;
+    bytes = std::max(bytes, (size_t)(p.parts - 1) * per_part * sizeof(float));
   }
   return bytes;
 }

@@ -438,9 +438,17 @@ SPLIT_CASES = [(512, 16384, 1, 4), (1000, 16640, 16, 4), (70, 8320, 5, 2), (4100
                (130, 8448, 64, 2), (64, 4096, 33, 1)]
 
 
-def _split_parts(n, k, m, layout):
-    w = _packed(layout, *make_weights(1, "splitshape", n, k, 0.4 if layout != tgs.BINARY else 0.0))
-    return tgs.gemm_workspace_bytes(w, m) // (4 * m * n) + 1
+def _split_bytes(n, m, parts, skinny):
+    """Workspace of a split product: an [m][n] fp32 slice per extra part (skinny kernel), or one
+    [64][64] slice per tile and extra part (tiled kernel, every 64 x 64 tile split)."""
+    per = m * n if skinny else -(-n // 64) * -(-m // 64) * 64 * 64
+    return (parts - 1) * per * 4
+
+
+def _tile_parts(n, k, m):
+    """Parts of the tiled kernel's split for 64 x 64 tiles: min(ceil(640 / tiles), 4, groups / 32)."""
+    tiles = -(-n // 64) * -(-m // 64)
+    return max(1, min(-(-640 // tiles), 4, (k // 128) // 32))
 
 
 @pytest.mark.parametrize("layout", ROT_LAYOUTS, ids=["slot2", "base3", "binary"])
@@ -449,15 +457,16 @@ def test_gemm_split_across_workgroups(layout, n, k, m, parts):
     """The K split across workgroups (ternary_gemm_ws): within the bound of the oracle, the
     workspace size is (parts - 1) * m * n fp32, and repeated calls are bit-identical (the parts
     are added in part order, no atomics). The single-launch product is within the bound too."""
+    skinny = m <= 16 and layout != tgs.BASE3  # base-3 always takes the tiled kernel
     if layout == tgs.BASE3 and m <= 32:
-        parts = _split_parts(n, k, m, layout)  # base-3 always takes the tiled kernel
+        parts = _tile_parts(n, k, m)
     t, s = make_weights(n + k + m, f"gemmsplit{layout}", n, k, 0.0 if layout == tgs.BINARY else 0.4)
     xb = make_x_bf16_bits(n + m, "gemmsplitx", m, k)
     w = _packed(layout, t, s)
-    assert tgs.gemm_workspace_bytes(w, m) == (parts - 1) * m * n * 4
+    assert tgs.gemm_workspace_bytes(w, m) == _split_bytes(n, m, parts, skinny)
     xt = torch.from_numpy(xb.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
     y1 = tgs.ternary_gemm(w, xt).cpu().numpy()
-    ws = torch.full((max(1, (parts - 1) * m * n),), float("nan"), device=DEV)  # no state between calls
+    ws = torch.full((max(1, _split_bytes(n, m, parts, skinny) // 4),), float("nan"), device=DEV)  # no state kept
     y2 = tgs.ternary_gemm(w, xt, workspace=ws).cpu().numpy()
     y0 = tgs.ternary_gemm(w, xt, split=False).cpu().numpy()
     y_ref, bound = oracle_product(layout, t, s, xb, oracle.X_BF16)
@@ -491,6 +500,23 @@ def test_gemm_split_workspace_checks():
     assert torch.equal(y, y0)
     w_short = _packed(tgs.SLOT2, *make_weights(6, "gemmsplitws2", 512, 5120, 0.4))
     assert tgs.gemm_workspace_bytes(w_short, m) == 0  # 40 groups: too few to split
+
+
+def test_gemm_split_large_tiles_sampled():
+    """540 tiles of 128 x 128 (9 x 60) over 64 groups: 512 tiles (one full round of two
+    workgroups per CU) taken whole, the last 28 in four parts across workgroups; checked on
+    sampled output columns, with the workspace size (3 extra parts x 28 tiles x 128 x 128)."""
+    n, k, m = 7680, 8192, 1040
+    t, s = make_weights(37, "gemmsplitbig", n, k, 0.4)
+    xb = make_x_bf16_bits(37, "gemmsplitbigx", m, k)
+    w = _packed(tgs.SLOT2, t, s)
+    assert tgs.gemm_workspace_bytes(w, m) == 3 * 28 * 128 * 128 * 4
+    xt = torch.from_numpy(xb.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    y = tgs.ternary_gemm(w, xt).cpu().numpy()
+    cols = np.sort(np.random.default_rng(5).choice(n, size=64, replace=False))
+    cols[0], cols[-1] = 0, n - 1
+    y_ref, bound = oracle_product(tgs.SLOT2, t, s, xb, oracle.X_BF16, rows=cols)
+    assert_within_bound(y[:, cols], y_ref, bound, f"gemm split {n}x{k} m={m} sampled")
 
 
 def test_gemm_large_tiles_sampled():
