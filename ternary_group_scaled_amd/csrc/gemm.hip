@@ -41,9 +41,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kBK = 128;
 constexpr int kPitch = kBK + 16;  // LDS row pitch in bf16 elements (32 bytes of padding: measured best of 132..168)
-// K split across workgroups: the workgroups a launch aims for (skinny: one 8-wave workgroup per
-// CU fits; tiled 64 x 64: 4 waves each)
-constexpr int64_t kSkinnyTarget = 384;
+// K split across workgroups: the workgroups a launch of 64 x 64 tiles (4 waves each) aims for
 constexpr int64_t kTileTarget = 640;
 // ... and the fewest 128-groups a part keeps: with fewer, a wave has too few groups to stream
 // (measured: 17408 x 5120, 40 groups, is slower in two parts at 16 and 128 rows)
@@ -571,11 +569,20 @@ struct GemmPlan {
   int64_t n_tiles;      // tiled: column tiles
 };
 
+// compute units of the current device (256 on MI355X; 256 if the query fails)
+int64_t device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return 256;
+  return cus;
+}
+
 GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
   GemmPlan p{};
   const int64_t groups = k / 128;
-  // parts for a launch of `wgs` workgroups: enough to give the CUs about `target` workgroups,
-  // each part keeping at least `min_groups` scale groups
+  // parts for a launch of `wgs` tiles: enough to give the CUs about `target` workgroups, each part
+  // keeping at least `min_groups` scale groups
   auto parts_for = [&](int64_t wgs, int64_t target, int64_t max_parts, int64_t min_groups) {
     if (!split) return 1;
     int64_t q = (target + wgs - 1) / wgs;
@@ -585,14 +592,24 @@ GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
   };
   if ((layout == TGS_LAYOUT_SLOT2 || layout == TGS_LAYOUT_BINARY) && m <= 32) {
     if (m <= 16) {
-      // 16 * FB outputs per workgroup of 8 waves, FB = n / 4096 rounded up, within 2..6: about one
-      // workgroup per CU (the kernel's registers allow one), and every workgroup reads all of x,
-      // so its L2 traffic falls as FB grows. (Measured on 17408 x 5120 and 5120 x 17408: FB = 5
-      // and 2 beat both neighbours and the 16-wave variants.)
+      // 16 * FB outputs per workgroup of 8 waves (FB in 2..6), in P parts of K (P in 1..4, each at
+      // least kMinPartGroups groups; P = 1 without a workspace): the most workgroups that still
+      // give no CU a second one, ties to the larger FB. A CU streams this kernel's loads at a
+      // rate of its own, so a CU with two workgroups doubles the launch (17408 x 5120: FB = 4,
+      // 272 workgroups, 30.9 us against 20.6 us for FB = 5, 218); and every workgroup reads x for
+      // its part of K, so x's L2 traffic falls as FB grows. 5120 x 17408: FB = 5 in four parts
+      // (256 workgroups) 22.0 us, FB = 6 in four (216) 24.3 us, FB = 2 in three (480) 27.5 us.
       p.kind = 0;
-      p.fb = (int)std::min<int64_t>(6, std::max<int64_t>(2, (n + 4095) / 4096));
+      const int64_t cus = device_cus();
+      const int64_t max_parts = split ? std::min<int64_t>(4, std::max<int64_t>(1, groups / kMinPartGroups)) : 1;
+      p.fb = 6, p.parts = 1;
+      int64_t best = 0;
+      for (int fb = 6; fb >= 2; --fb)
+        for (int64_t q = 1; q <= max_parts; ++q) {
+          const int64_t w = (n + 16 * fb - 1) / (16 * fb) * q;
+          if (w <= cus && w > best) best = w, p.fb = fb, p.parts = (int)q;
+        }
       p.wgs = (n + 16 * p.fb - 1) / (16 * p.fb);
-      p.parts = parts_for(p.wgs, kSkinnyTarget, 4, kMinPartGroups);
     } else {
       // 16 outputs per block: the most (4, 2, 1) that still gives 512 workgroups
       p.kind = 1;

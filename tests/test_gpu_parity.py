@@ -429,8 +429,9 @@ def test_gemm_four_k_parts(layout, n, k, m, split):
     assert_within_bound(y, y_ref, bound, f"gemm four K parts layout {layout} {n}x{k} m={m}")
 
 
-# (n, k, m, parts): K split across workgroups. Skinny kernel (m <= 16): 16 * FB outputs per
-# workgroup, parts = min(ceil(384 / workgroups), 4, groups / 32). Tiled kernel (64 x 64 tiles,
+# (n, k, m, parts): K split across workgroups. Skinny kernel (m <= 16): FB in 2..6 and parts in
+# 1..min(4, groups / 32), the most workgroups ceil(n / 16 FB) * parts that fit one per CU (256),
+# ties to the larger FB (4100 x 8192: FB = 3 in two parts). Tiled kernel (64 x 64 tiles,
 # 33 <= m <= 128): parts = min(ceil(640 / tiles), 4, groups / 32). Ragged n, parts that do not
 # divide the groups (130 / 4, 65 / 2, 66 / 2), one row, parts of exactly 32 groups, and a product
 # with too few groups to split.
