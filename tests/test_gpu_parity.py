@@ -520,16 +520,18 @@ def test_gemm_split_large_tiles_sampled():
     assert_within_bound(y[:, cols], y_ref, bound, f"gemm split {n}x{k} m={m} sampled")
 
 
-def test_gemm_large_tiles_sampled():
-    """Many rows and columns take 128 x 128 tiles; checked on sampled output columns."""
-    n, k, m = 8192, 256, 1040
-    t, s = make_weights(31, "gemmbig", n, k, 0.4)
+@pytest.mark.parametrize("layout", [tgs.SLOT2, tgs.BINARY], ids=["slot2", "binary"])
+@pytest.mark.parametrize("n,k,m", [(8192, 256, 1040), (8190, 384, 1100), (4200, 128, 2100)])
+def test_gemm_large_tiles_sampled(layout, n, k, m):
+    """Many rows and columns take 128 x 128 tiles: slot-2 and binary codes, ragged m and n, one to
+    three groups; checked on sampled output columns."""
+    t, s = make_weights(31, "gemmbig", n, k, 0.0 if layout == tgs.BINARY else 0.4)
     xb = make_x_bf16_bits(31, "gemmbigx", m, k)
-    y = _gemm(tgs.SLOT2, t, s, xb)
+    y = _gemm(layout, t, s, xb)
     cols = np.sort(np.random.default_rng(3).choice(n, size=96, replace=False))
     cols[0], cols[-1] = 0, n - 1
-    y_ref, bound = oracle_product(tgs.SLOT2, t, s, xb, oracle.X_BF16, rows=cols)
-    assert_within_bound(y[:, cols], y_ref, bound, f"gemm {n}x{k} m={m} sampled")
+    y_ref, bound = oracle_product(layout, t, s, xb, oracle.X_BF16, rows=cols)
+    assert_within_bound(y[:, cols], y_ref, bound, f"gemm layout {layout} {n}x{k} m={m} sampled")
 
 
 @pytest.mark.parametrize("m", [1, 20, 40])
