@@ -624,6 +624,7 @@ GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
   // (each part is a workgroup of its own, so the parts spread over all CUs), else inside the
   // workgroup (two or four parts of 4 waves, added through LDS).
   p.kind = 2;
+  const int64_t cus = device_cus();
   p.bm = m > 128 ? 128 : 64;
   const int64_t m_tiles = (m + p.bm - 1) / p.bm;
   p.bn = (n + 127) / 128 * m_tiles >= 512 ? 128 : 64;
@@ -636,7 +637,16 @@ GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
   if (p.bm == 64 && p.bn == 64) {
     // few small tiles over a long K: every tile in parts
     p.parts = parts_for(tiles, kTileTarget, 4, kMinPartGroups);
-    if (p.parts > 1) p.whole = 0, p.tail = tiles;
+    if (p.parts > 1) {
+      p.whole = 0, p.tail = tiles;
+    } else if (split && tiles > 2 * cus) {
+      // otherwise two whole tiles per CU, and the tiles left over in up to 4 parts, so that no CU
+      // takes a third whole tile (a CU's throughput is shared by its workgroups: 17408 x 5120 at
+      // 128 rows, 544 tiles, 66.5 -> 62.5 us with 512 whole and 32 in four parts)
+      const int64_t rem = tiles % (2 * cus);
+      const int64_t q = rem > 0 ? std::min<int64_t>({4, 2 * cus / rem, groups / kMinTailGroups}) : 1;
+      if (q > 1) p.parts = (int)q, p.whole = tiles - rem, p.tail = rem;
+    }
   } else if (p.bm == 128 && p.bn == 128 && split) {
     // 128 x 128 tiles run two workgroups per CU (kTileSlots at a time): whole tiles for the full
     // rounds, and the tiles left over for a last, partly empty round in up to 4 parts that fill it

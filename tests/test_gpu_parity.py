@@ -520,6 +520,24 @@ def test_gemm_split_large_tiles_sampled():
     assert_within_bound(y[:, cols], y_ref, bound, f"gemm split {n}x{k} m={m} sampled")
 
 
+def test_gemm_split_balance_sampled():
+    """532 tiles of 64 x 64 (2 x 266) over 16 groups: 512 taken whole (two per CU) and the last 20
+    (row tile 1, columns 15744..16999) in two K parts; checked on sampled columns that include
+    all of the split tiles' last 64 and some of the rest."""
+    n, k, m = 17000, 2048, 100
+    t, s = make_weights(41, "gemmbal", n, k, 0.4)
+    xb = make_x_bf16_bits(41, "gemmbalx", m, k)
+    w = _packed(tgs.SLOT2, t, s)
+    assert tgs.gemm_workspace_bytes(w, m) == 20 * 64 * 64 * 4
+    xt = torch.from_numpy(xb.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    y = tgs.ternary_gemm(w, xt).cpu().numpy()
+    rng = np.random.default_rng(7)
+    cols = np.unique(np.r_[np.arange(n - 64, n), rng.choice(15744, 48, replace=False),
+                           15744 + rng.choice(n - 64 - 15744, 48, replace=False), 0])
+    y_ref, bound = oracle_product(tgs.SLOT2, t, s, xb, oracle.X_BF16, rows=cols)
+    assert_within_bound(y[:, cols], y_ref, bound, f"gemm balanced split {n}x{k} m={m} sampled")
+
+
 @pytest.mark.parametrize("layout", [tgs.SLOT2, tgs.BINARY], ids=["slot2", "binary"])
 @pytest.mark.parametrize("n,k,m", [(8192, 256, 1040), (8190, 384, 1100), (4200, 128, 2100)])
 def test_gemm_large_tiles_sampled(layout, n, k, m):
