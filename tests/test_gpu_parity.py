@@ -520,6 +520,31 @@ def test_gemm_split_large_tiles_sampled():
     assert_within_bound(y[:, cols], y_ref, bound, f"gemm split {n}x{k} m={m} sampled")
 
 
+def test_gemm_split_on_a_side_stream():
+    """A split product on a stream of its own (its temporary workspace allocated on that stream),
+    twice in a row with the stream's own work between: bit-identical to the product on the
+    current stream."""
+    n, k, m = 512, 16384, 16
+    t, s = make_weights(43, "gemmsplitstream", n, k, 0.4)
+    w = _packed(tgs.SLOT2, t, s)
+    assert tgs.gemm_workspace_bytes(w, m) > 0
+    xt = torch.from_numpy(make_x_bf16_bits(43, "gemmsplitstreamx", m, k).view(np.int16).copy()).to(DEV)
+    xt = xt.view(torch.bfloat16)
+    ref = tgs.ternary_gemm(w, xt)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            y = tgs.ternary_gemm(w, xt, stream=side)
+            outs.append(y.clone())
+            y.zero_()
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y, ref)
+
+
 def test_gemm_split_balance_sampled():
     """532 tiles of 64 x 64 (2 x 266) over 16 groups: 512 taken whole (two per CU) and the last 20
     (row tile 1, columns 15744..16999) in two K parts; checked on sampled columns that include
