@@ -164,23 +164,31 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
 
   uint32_t xr[kXUnits][8];
   uint4 cr = make_uint4(0, 0, 0, 0);
-  auto load_stage = [&](int g) {
+  // With 128-row tiles every thread issues the same loads whether or not it needs them (live
+  // false, or a thread without a weight row: parked out of range), so that the compiler's wait
+  // counts stay exact (see the group loop).
+  auto load_stage = [&](int g, bool live) {
 #pragma unroll
     for (int u = 0; u < kXUnits; ++u) {
       const int unit = tid + u * kThreads, r = unit >> 3, c16 = (unit & 7) * 16;
       const uint32_t off = ((uint32_t)(m_base + r) * (uint32_t)k + (uint32_t)(g * 128 + c16)) * 2u;
-      const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (int)off, 0, 0));
-      const uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (int)(off + 16u), 0, 0));
+      const uint4 a = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, live ? (int)off : kOobOffset, 0, 0));
+      const uint4 b = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, live ? (int)(off + 16u) : kOobOffset, 0, 0));
       xr[u][0] = a.x; xr[u][1] = a.y; xr[u][2] = a.z; xr[u][3] = a.w;
       xr[u][4] = b.x; xr[u][5] = b.y; xr[u][6] = b.z; xr[u][7] = b.w;
     }
-    if (LAYOUT == TGS_LAYOUT_SLOT2 && tid < kCodeThreads) {
+    const bool code_live = live && tid < kCodeThreads;
+    if (LAYOUT == TGS_LAYOUT_SLOT2 && (BM == 128 || tid < kCodeThreads)) {
       const uint32_t off = (uint32_t)(n_base + (tid >> 1)) * (uint32_t)stride + (uint32_t)(g * 32 + 16 * (tid & 1));
-      cr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)off, 0, kStreamAux));
+      cr = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, code_live ? (int)off : kOobOffset, 0, kStreamAux));
     }
-    if (LAYOUT == TGS_LAYOUT_BINARY && tid < kCodeThreads) {  // 64 codes are 8 bytes
+    if (LAYOUT == TGS_LAYOUT_BINARY && (BM == 128 || tid < kCodeThreads)) {  // 64 codes are 8 bytes
       const uint32_t off = (uint32_t)(n_base + (tid >> 1)) * (uint32_t)stride + (uint32_t)(g * 16 + 8 * (tid & 1));
-      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, (int)off, 0, kStreamAux));
+      const uint2 v = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, code_live ? (int)off : kOobOffset, 0, kStreamAux));
       cr.x = v.x;
       cr.y = v.y;
     }
@@ -238,25 +246,21 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
   // iterations (the barriers are shared), and a group index past pg1 is loaded harmlessly (in
   // range, or beyond the buffer and read as zero) but not multiplied
   const int iters = (pg1 - pg0 + KS - 1) / KS;
-  load_stage(pg0 + kh);
-  store_stage(pg0 + kh);
-  __syncthreads();
-  for (int i = 0; i < iters; ++i) {
-    const int g = pg0 + i * KS + kh;
-    const bool more = i + 1 < iters;
-    if (more) load_stage(g + KS);
-    // this lane's output columns: their scales, loaded ahead of the MFMAs
-    uint32_t sraw[kBlkN];
+  // (128-row tiles) a group's sums before its scale, and this lane's output columns' scales
+  f32x4 gsum[kBlkM][kBlkN];
+  uint32_t sraw[kBlkN];
+  auto load_scales = [&](int g) {
 #pragma unroll
     for (int b = 0; b < kBlkN; ++b) {
       const uint32_t col = (uint32_t)(n_base + wn * kWN + 16 * b + fr);
       sraw[b] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)((col * (uint32_t)groups + (uint32_t)g) * 2u), 0, 0);
     }
-    f32x4 part[kBlkM][kBlkN];
+  };
+  auto multiply = [&]() {
 #pragma unroll
     for (int a = 0; a < kBlkM; ++a)
 #pragma unroll
-      for (int b = 0; b < kBlkN; ++b) part[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < kBlkN; ++b) gsum[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 af[kBlkM], bfr[kBlkN];
@@ -270,22 +274,93 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
       for (int a = 0; a < kBlkM; ++a)
 #pragma unroll
         for (int b = 0; b < kBlkN; ++b)
-          part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], part[a][b], 0, 0, 0);
+          gsum[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], gsum[a][b], 0, 0, 0);
     }
-    if (KS == 1 || g < pg1) {
+  };
+  auto scale_add = [&]() {
 #pragma unroll
-      for (int b = 0; b < kBlkN; ++b) {
-        const float sc = 0.5f * f16_to_f32((uint16_t)sraw[b]);  // the weights were decoded as 2t
+    for (int b = 0; b < kBlkN; ++b) {
+      const float sc = 0.5f * f16_to_f32((uint16_t)sraw[b]);  // the weights were decoded as 2t
 #pragma unroll
-        for (int a = 0; a < kBlkM; ++a)
+      for (int a = 0; a < kBlkM; ++a)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[a][b][r] = fmaf(sc, part[a][b][r], acc[a][b][r]);
+        for (int r = 0; r < 4; ++r) acc[a][b][r] = fmaf(sc, gsum[a][b][r], acc[a][b][r]);
+    }
+  };
+  load_stage(pg0 + kh, true);
+  store_stage(pg0 + kh);
+  __syncthreads();
+  if constexpr (BM == 128) {
+    // Each iteration first issues the next stage's loads, then scales the previous group's sums
+    // by its scales (loaded an iteration earlier), then loads this group's scales; the MFMAs
+    // follow. The scheduling barrier keeps the compiler from sinking the scale loads below the
+    // MFMAs, which leaves their latency in front of the next iteration's loads, and every stage
+    // load is issued (parked past the end) so that the waits stay exact. (5120 x 17408 at 2048
+    // rows: 477 -> 457 us on one box; with 64-row tiles this order was 2-7% slower.)
+    bool prev_live = false;
+    for (int i = 0; i < iters; ++i) {
+      const int g = pg0 + i * KS + kh;
+      const bool more = i + 1 < iters;
+      load_stage(g + KS, more);
+      if (prev_live) scale_add();
+      load_scales(g);
+      prev_live = KS == 1 || g < pg1;
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();
+      __syncthreads();
+      if (more) {
+        store_stage(g + KS);
+        __syncthreads();
       }
     }
-    __syncthreads();
-    if (more) {
-      store_stage(g + KS);
+    if (prev_live) scale_add();
+  } else {
+    for (int i = 0; i < iters; ++i) {
+      const int g = pg0 + i * KS + kh;
+      const bool more = i + 1 < iters;
+      if (more) load_stage(g + KS, true);
+      // this lane's output columns: their scales, loaded ahead of the MFMAs
+      uint32_t sr[kBlkN];
+  #pragma unroll
+      for (int b = 0; b < kBlkN; ++b) {
+        const uint32_t col = (uint32_t)(n_base + wn * kWN + 16 * b + fr);
+        sr[b] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, (int)((col * (uint32_t)groups + (uint32_t)g) * 2u), 0, 0);
+      }
+      f32x4 part[kBlkM][kBlkN];
+  #pragma unroll
+      for (int a = 0; a < kBlkM; ++a)
+  #pragma unroll
+        for (int b = 0; b < kBlkN; ++b) part[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 af[kBlkM], bfr[kBlkN];
+  #pragma unroll
+        for (int a = 0; a < kBlkM; ++a)
+          af[a] = *reinterpret_cast<const bf16x8*>(xs + (wm * kWM + 16 * a + fr) * kPitch + 32 * s + fk);
+  #pragma unroll
+        for (int b = 0; b < kBlkN; ++b)
+          bfr[b] = *reinterpret_cast<const bf16x8*>(ws + (wn * kWN + 16 * b + fr) * kPitch + 32 * s + fk);
+  #pragma unroll
+        for (int a = 0; a < kBlkM; ++a)
+  #pragma unroll
+          for (int b = 0; b < kBlkN; ++b)
+            part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], part[a][b], 0, 0, 0);
+      }
+      if (KS == 1 || g < pg1) {
+  #pragma unroll
+        for (int b = 0; b < kBlkN; ++b) {
+          const float sc = 0.5f * f16_to_f32((uint16_t)sr[b]);  // the weights were decoded as 2t
+  #pragma unroll
+          for (int a = 0; a < kBlkM; ++a)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) acc[a][b][r] = fmaf(sc, part[a][b][r], acc[a][b][r]);
+        }
+      }
       __syncthreads();
+      if (more) {
+        store_stage(g + KS);
+        __syncthreads();
+      }
     }
   }
   if constexpr (KS > 1) {
