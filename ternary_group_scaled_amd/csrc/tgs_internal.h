@@ -60,9 +60,12 @@ struct GemvArgs {
 __device__ __forceinline__ GemvJob gemv_job_of_block(const GemvArgs& a) {
   const int b = (int)blockIdx.x;
   GemvJob job = a.job[0];
-  // job 0 is read with the start table, before the search (not as a select of two addresses)
-  __asm__ volatile("" ::"s"(job.codes), "s"(job.scales), "s"(job.x), "s"(job.signs), "s"(job.y), "s"(job.stride),
-                   "s"(job.n), "s"(job.k), "s"(job.block0));
+  // job 0 and the job count in one batch of scalar loads (job 0 not as a select of two
+  // addresses); a launch of one job, as every launch in layer order is, needs nothing else
+  const int32_t count = a.count;
+  __asm__ volatile("" ::"s"(count), "s"(job.codes), "s"(job.scales), "s"(job.x), "s"(job.signs), "s"(job.y),
+                   "s"(job.stride), "s"(job.n), "s"(job.k), "s"(job.block0));
+  if (count == 1) return job;
   // starts increase and are >= 1 past job 0: start - 1 - b is negative exactly when b >= start
   int32_t st[kMaxJobs];
 #pragma unroll
