@@ -377,8 +377,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<MT, ROT>(), 8))) void gemv_k
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[ROT ? MT * kSliceElems : 8];  // rotated staging
   __shared__ float lds_norm[MT * kWaves];                                              // RMSNorm partial sums
 
-  const GemvJob job = gemv_job_of_block(args);  // uniform
-  const int n = job.n, k = job.k, m = args.m;
+  int m = 0;
+  const GemvJob job = gemv_job_of_block(args, &m);  // uniform; m read with the job
+  const int n = job.n, k = job.k;
   const int groups = k / 128;
   const int chunks = k / kChunkElems;
   const int slices = (chunks + S - 1) / S;
@@ -652,12 +653,12 @@ void gemv_wave_kernel(const GemvArgs args) {
   extern __shared__ __attribute__((aligned(16))) char lds_dyn[];
   __shared__ float norm_part[NORM ? 8 : 1];  // RMSNorm: each wave's sum of squares
 
-  const GemvJob job = gemv_job_of_block(args);  // a copy: the fields stay in scalar registers
+  int R = 0;  // row slots per wave: 2 * G * (number of groups), read with the job
+  const GemvJob job = gemv_job_of_block(args, nullptr, &R);  // a copy: the fields stay in scalar registers
   const int n = job.n, k = job.k;
   const int groups = k / 128;
   const int chunks = k / 64;
   const int slices = (chunks + S - 1) / S;  // waves per workgroup: slices * W
-  const int R = args.rows_per_wave;         // row slots per wave: 2 * G * (number of groups)
   const int batches = R / 2;
   const int rows_wave = R * kRowsPerInstr;
   const int rows_wg = W * rows_wave;

@@ -125,8 +125,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   extern __shared__ __attribute__((aligned(16))) _Float16 xrot[];
   __shared__ float norm_part[NORM ? MT * kWaves : 1];  // RMSNorm: per-wave sums of squares
 
-  const GemvJob job = gemv_job_of_block(args);
-  const int n = job.n, k = job.k, m = args.m;
+  int m = 0;
+  const GemvJob job = gemv_job_of_block(args, &m);  // m read with the job, kept in a register
+  const int n = job.n, k = job.k;
   const int groups = k / 128;
 
   // the wave index is the same in every lane; read it as such so that each wave's group range,
@@ -148,15 +149,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   // rows < MT of this wave's A tile, rewritten for every group
   _Float16* tile = reinterpret_cast<_Float16*>(smem) + wave * MT * kRowPitch;
   const _Float16* a_row = fr < MT ? tile + fr * kRowPitch : zero_row;
-  for (int i = threadIdx.x; i < 160; i += kWaves * 64) zero_row[i] = (_Float16)0.f;
-  for (int i = threadIdx.x; i < 5 * 160; i += kWaves * 64) {
-    const int o = i / 160, e = i - 160 * o;
-    if (e < 128)
-      slot_tab[o][e] = (uint16_t)(2 * tile_slot(o + rotated_element<MT, ROT>(e)));
-    else  // rel in [0, o) and [o + 128, 160)
-      zero_tab[o][e - 128] = (uint16_t)(2 * tile_slot(e - 128 < o ? e - 128 : e));
-  }
-  if constexpr (!NORM) __syncthreads();  // the tables (with the norm: at the barrier of norm_factors)
+  // the zero row and the slot tables; the plain basis writes them after its first loads are issued
+  auto init_tables = [&]() {
+    for (int i = threadIdx.x; i < 160; i += kWaves * 64) zero_row[i] = (_Float16)0.f;
+    for (int i = threadIdx.x; i < 5 * 160; i += kWaves * 64) {
+      const int o = i / 160, e = i - 160 * o;
+      if (e < 128)
+        slot_tab[o][e] = (uint16_t)(2 * tile_slot(o + rotated_element<MT, ROT>(e)));
+      else  // rel in [0, o) and [o + 128, 160)
+        zero_tab[o][e - 128] = (uint16_t)(2 * tile_slot(e - 128 < o ? e - 128 : e));
+    }
+    if constexpr (!NORM) __syncthreads();  // the tables (with the norm: at the barrier of norm_factors)
+  };
+  if constexpr (PRE || ROT == 1024) init_tables();
   // RMSNorm factors: of this lane's token (group staging) and of token `wave` (block staging).
   // Every thread calls norm_factors once, before its first multiply; its barrier also publishes
   // the tables. The plain-basis loop calls it after its first loads are issued, so the rows'
@@ -607,6 +612,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     Stage st[kS];
 #pragma unroll
     for (int i = 0; i < kS - 1; ++i) load(st[i], g_begin + i);
+    init_tables();
     norm_factors();
     for (int g = g_begin; g < g_end; g += kS) {
 #pragma unroll

@@ -57,14 +57,19 @@ struct GemvArgs {
 };
 
 // The job of this workgroup: the last one whose first workgroup is at or before blockIdx.x.
-__device__ __forceinline__ GemvJob gemv_job_of_block(const GemvArgs& a) {
+// m_out, rpw_out (optional): the header's m and rows_per_wave, taken from the same batch (asm
+// outputs, so that the compiler keeps them in registers rather than loading them again later)
+__device__ __forceinline__ GemvJob gemv_job_of_block(const GemvArgs& a, int* m_out = nullptr, int* rpw_out = nullptr) {
   const int b = (int)blockIdx.x;
   GemvJob job = a.job[0];
-  // job 0 and the job count in one batch of scalar loads (job 0 not as a select of two
-  // addresses); a launch of one job, as every launch in layer order is, needs nothing else
+  // job 0, the job count and the header in one batch of scalar loads (job 0 not as a select of
+  // two addresses); a launch of one job, as every launch in layer order is, needs nothing else
   const int32_t count = a.count;
-  __asm__ volatile("" ::"s"(count), "s"(job.codes), "s"(job.scales), "s"(job.x), "s"(job.signs), "s"(job.y),
-                   "s"(job.stride), "s"(job.n), "s"(job.k), "s"(job.block0));
+  int32_t m = a.m, rpw = a.rows_per_wave;
+  __asm__ volatile("" : "+s"(m), "+s"(rpw) : "s"(count), "s"(job.codes), "s"(job.scales), "s"(job.x), "s"(job.signs),
+                   "s"(job.y), "s"(job.stride), "s"(job.n), "s"(job.k), "s"(job.block0));
+  if (m_out) *m_out = m;
+  if (rpw_out) *rpw_out = rpw;
   if (count == 1) return job;
   // starts increase and are >= 1 past job 0: start - 1 - b is negative exactly when b >= start
   int32_t st[kMaxJobs];
