@@ -88,15 +88,74 @@ __device__ __forceinline__ u16x2 peel(u16x2& v) {  // next base-3 digit of both 
 }
 
 // Element of the group that entry e = kE p + i of a lane's slot list holds after the rotation:
-// e itself, except for one token in 128-element blocks. There the two lane-half butterfly stages
-// pair the lane's own two elements (a swap of one register's half with the other's, then a sum
-// and a difference), which leaves element bit 0 on lane bit 4, bits 1..4 on lane bits 0..3,
-// bit 5 on lane bit 5 and bit 6 on the register.
-template <int MT, int ROT>
+// e itself, except in 128-element blocks for one token and for eight on the matrix cores (MROT).
+// One token: the two lane-half butterfly stages pair the lane's own two elements (a swap of one
+// register's half with the other's, then a sum and a difference), which leaves element bit 0 on
+// lane bit 4, bits 1..4 on lane bits 0..3, bit 5 on lane bit 5 and bit 6 on the register.
+// Eight tokens (MROT): entry j = 8 h + 4 i + r of p = cb + 2 eq is element 4 eq + r of 16-element
+// chunk 4 h + 2 i + cb (the layout the rotation's products leave, below).
+template <int MT, int ROT, bool MROT>
 __host__ __device__ constexpr int rotated_element(int e) {
+  if (MROT) {
+    const int p = e >> 4, j = e & 15;
+    return 64 * (j >> 3) + 32 * ((j >> 2) & 1) + 16 * (p & 1) + 4 * (p >> 1) + (j & 3);
+  }
   if (MT != 1 || ROT != 128) return e;
   const int p = e >> 1, reg = e & 1;
   return ((p >> 4) & 1) | ((p & 15) << 1) | (((p >> 5) & 1) << 5) | (reg << 6);
+}
+
+// Rotation of eight tokens' 128-element groups on the matrix cores. Sylvester's H_128 is
+// H_8 (x) H_16 over the 16-element chunks c of the group: y[16 c' + e] = sum_c H_8[c'][c]
+// (H_16 x_c)[e]. One v_mfma_f32_16x16x32_f16 takes H_16 on both halves of its A operand (rows e)
+// and, as the B operand's 16 columns, eight tokens times two chunk parities cb: column
+// tok + 8 cb holds chunk pp = 2 i + cb in its k rows 0..15 and chunk pp + 4 in rows 16..31. With
+// [H_16 | H_16] it yields H_16 (x_pp + x_pp+4), with [H_16 | -H_16] H_16 (x_pp - x_pp+4): the
+// product and the H_8 stage on chunk bit 2. The stage on chunk bit 1 (i) is a sum and a difference
+// in the lane, the one on bit 0 (cb, lane bit 3) one DPP exchange with the lane 8 apart. Products
+// of +-1 and fp16 values are exact and the sums are fp32, as in the butterfly; the one rounding to
+// fp16 follows 1/sqrt(128).
+// v[j] += v[j] of lane (lane ^ 8) * sp for the 16 values, each one v_fmac_f32 reading the partner
+// through DPP (row_ror:8 is lane ^ 8 within a 16-lane row). The compiler emits a separate DPP move
+// for this form, so it is written out; the s_nop gives the two wait states a DPP read needs after
+// a VALU write of its source (every later source was written before the first), and each
+// instruction reads its partner's value before any lane's result is written.
+__device__ __forceinline__ void fmac_partner8x16(float (&v)[16], float sp) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %8, %8, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %9, %9, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %10, %10, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %11, %11, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %12, %12, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %13, %13, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %14, %14, %16 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %15, %15, %16 row_ror:8 row_mask:0xf bank_mask:0xf"
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+        "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+      : "v"(sp));
+}
+
+// A operand of lane (e = lane % 16, k rows 8 (lane / 16) ..): H_16[e][k mod 16], negated in rows
+// k >= 16 when `minus`
+__device__ __forceinline__ half8 hadamard16_operand(int lane, bool minus) {
+  const int e = lane & 15, k0 = 8 * ((lane >> 4) & 1);
+  const bool neg = minus && (lane >> 5);
+  half8 h;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const bool odd = (__builtin_popcount((unsigned)(e & (k0 + t))) & 1) != 0;
+    h[t] = (odd != neg) ? (_Float16)-1.f : (_Float16)1.f;
+  }
+  return h;
 }
 
 // pipeline depth of the group loop (plain and 128-block bases): stages of loads per wave. Two
@@ -109,6 +168,9 @@ template <int MT, int kFB, int ROT, bool NORM, bool PRE>
 __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArgs args) {
   static_assert(ROT == 0 || ROT == 128 || ROT == 1024, "rotation block is 0 (none), 128 or 1024");
   static_assert(!PRE || ROT == 1024, "whole-row rotation is for 1024-element blocks");
+  // eight tokens' 128-element groups rotate on the matrix cores (rotated_element); with the RMSNorm
+  // prologue the normalized activations are fp32, which that product's fp16 operand would round
+  constexpr bool MROT = MT == 8 && ROT == 128 && !NORM;
   // the waves' A tiles (MT rows each), and afterwards the waves' sums
   constexpr int kTileBytes = kWaves * MT * kRowPitch * 2, kRedBytes = kWaves * kFB * 4 * 64 * 4;
   __shared__ __attribute__((aligned(16))) char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
@@ -142,9 +204,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   // tokens a token's lanes are those with equal lane bits 2, 4 and 5 (p from bits 0, 1 and 3), so
   // the rotation's three cross-lane butterfly stages pair lanes 1, 2 and 8 apart: each a single
   // DPP move (lanes 4 apart would take two masked moves and a copy)
+  // MROT: token lane % 8, p = cb + 2 eq from lane bits 3 and 4..5 (rotated_element)
   constexpr int kL = 64 / MT, kE = 2 * MT;
-  const int tok = MT == 8 ? ((lane >> 2) & 1) | ((lane >> 3) & 6) : lane / kL;
-  const int p = MT == 8 ? (lane & 3) | ((lane >> 1) & 4) : lane % kL;
+  const int tok = MROT ? lane & 7 : MT == 8 ? ((lane >> 2) & 1) | ((lane >> 3) & 6) : lane / kL;
+  const int p = MROT ? ((lane >> 3) & 1) | ((lane >> 4) << 1) : MT == 8 ? (lane & 3) | ((lane >> 1) & 4) : lane % kL;
+  // MROT: the lane's B operand elements of the group, for i = 0 (+ 32 for i = 1): chunk
+  // cb + 4 (k quarter >> 1), half (k quarter & 1); and the two A operands
+  const int mrot_e = 16 * ((lane >> 3) & 1) + 64 * (lane >> 5) + 8 * ((lane >> 4) & 1);
+  const half8 h_plus = MROT ? hadamard16_operand(lane, false) : half8{};
+  const half8 h_minus = MROT ? hadamard16_operand(lane, true) : half8{};
 
   // rows < MT of this wave's A tile, rewritten for every group
   _Float16* tile = reinterpret_cast<_Float16*>(smem) + wave * MT * kRowPitch;
@@ -155,7 +223,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
     for (int i = threadIdx.x; i < 5 * 160; i += kWaves * 64) {
       const int o = i / 160, e = i - 160 * o;
       if (e < 128)
-        slot_tab[o][e] = (uint16_t)(2 * tile_slot(o + rotated_element<MT, ROT>(e)));
+        slot_tab[o][e] = (uint16_t)(2 * tile_slot(o + rotated_element<MT, ROT, MROT>(e)));
       else  // rel in [0, o) and [o + 128, 160)
         zero_tab[o][e - 128] = (uint16_t)(2 * tile_slot(e - 128 < o ? e - 128 : e));
     }
@@ -224,6 +292,25 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
   auto load = [&](Stage& st, int g) {
     const bool live = g < g_end;
     load_codes(st, g, live);
+    if constexpr (MROT) {
+      // x[0..3] and sg[0..1]: the lane's B operand of product i = 0, x[4..7] and sg[2..3]: of i = 1
+      const int xo = live ? (tok * k + 128 * g + mrot_e) * 2 : kOobOffset;
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo, 0, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, live ? xo + 64 : kOobOffset, 0, 0);
+      const int so = live ? 128 * g + mrot_e : kOobOffset;
+      const auto sa = __builtin_amdgcn_raw_buffer_load_b64(sign_rsrc, so, 0, 0);
+      const auto sb = __builtin_amdgcn_raw_buffer_load_b64(sign_rsrc, live ? so + 32 : kOobOffset, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st.x[i] = a[i];
+        st.x[4 + i] = b[i];
+      }
+      st.sg[0] = sa[0];
+      st.sg[1] = sa[1];
+      st.sg[2] = sb[0];
+      st.sg[3] = sb[1];
+      return;
+    }
     const int xo = live ? (tok * k + 128 * g + kE * p) * 2 : kOobOffset;
     if constexpr (MT == 8) {
       const auto a = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo, 0, 0);
@@ -440,6 +527,39 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_b3_mfma_kernel(const GemvArg
         hv[2 * i] = __builtin_bit_cast(_Float16, (uint16_t)w[i]);
         hv[2 * i + 1] = __builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
       }
+    } else if constexpr (MROT) {
+      // sign flip on the fp16 sign bits, then the rotation's products (rotated_element's layout)
+      // (the columns of odd chunks, lane bit 3, are negated as well: see the last stage)
+      const uint32_t odd_neg = (lane & 8) ? 0x80808080u : 0u;
+      uint32_t xs[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = (i & 1) ? 0x030C020Cu : 0x010C000Cu;  // sign bytes 2i, 2i + 1 -> bits 15, 31
+        xs[i] = st.x[i] ^ (__builtin_amdgcn_perm(0u, st.sg[i >> 1] ^ odd_neg, sel) & 0x80008000u);
+      }
+      f32x4 d[2][2];  // [chunk bit 2 of the output][i]
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const half8 b = __builtin_bit_cast(half8, make_uint4(xs[4 * i], xs[4 * i + 1], xs[4 * i + 2], xs[4 * i + 3]));
+        d[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_plus, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        d[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_minus, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+      float v[16];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = d[h][0][r], b = d[h][1][r];
+          v[8 * h + r] = a + b;      // chunk bit 1 clear
+          v[8 * h + 4 + r] = a - b;  // chunk bit 1 set
+        }
+      // chunk bit 0: the even lane holds a, the odd one -b (its column was negated), so
+      // own + partner * (-1 even, +1 odd) gives a + b and a - b: one multiply-add that takes the
+      // partner through DPP
+      const float sp = (lane & 8) ? 1.f : -1.f;
+      fmac_partner8x16(v, sp);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) hv[j] = (_Float16)(v[j] * 0.08838834764831845f);  // 1/sqrt(128)
     } else {
       // 128-blocks: sign flip (on the fp16 sign bits), the natural-order Sylvester butterfly over
       // the group in fp32 (strides below kE inside the lane, the rest across lanes), 1/sqrt(128),

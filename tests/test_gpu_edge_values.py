@@ -34,8 +34,8 @@ DEV = "cuda"
 # GEMV kernel paths: (layout, m, rotation block). slot-2 m = 1 plain is the single-token kernel;
 # m = 2 and 8 (and rotated) the general slot-2/binary kernel; every base-3 case the matrix-core kernel.
 GEMV_PATHS = [(tgs.SLOT2, 1, 0), (tgs.SLOT2, 2, 0), (tgs.SLOT2, 8, 0), (tgs.BASE3, 1, 0), (tgs.BASE3, 8, 0)]
-GEMV_PATHS_ALL = GEMV_PATHS + [(tgs.SLOT2, 1, 128), (tgs.BASE3, 1, 128), (tgs.BASE3, 8, 1024),
-                               (tgs.BINARY, 1, 0), (tgs.BINARY, 8, 0)]
+GEMV_PATHS_ALL = GEMV_PATHS + [(tgs.SLOT2, 1, 128), (tgs.BASE3, 1, 128), (tgs.BASE3, 8, 128),
+                               (tgs.BASE3, 8, 1024), (tgs.BINARY, 1, 0), (tgs.BINARY, 8, 0)]
 LNAME = {tgs.SLOT2: "slot2", tgs.BASE3: "base3", tgs.BINARY: "binary"}
 
 

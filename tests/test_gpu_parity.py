@@ -73,7 +73,7 @@ def test_gemv_matches_oracle(layout, n, k, m):
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LNAME.get)
 @pytest.mark.parametrize("n,k", [(1, 128), (33, 640), (100, 5120), (20, 17408), (65, 4096)])
-@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("m", [1, 3, 5, 8])
 def test_rotated_gemv_matches_oracle(layout, n, k, m):
     t, s = make_weights(n * 3 + k, f"rot{layout}", n, k, 0.5)
     x16 = make_x_f16(m + 7, f"rot{n}x{k}", m, k)
