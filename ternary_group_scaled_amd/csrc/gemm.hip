@@ -55,59 +55,82 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// word holding (e1 in the low half, e2 in the high half) from 16-bit elements packed in w
-template <int E1, int E2>
-__device__ __forceinline__ uint32_t pair16(const uint32_t* w) {
-  constexpr uint32_t sel = ((E1 & 1) ? 0x0302u : 0x0100u) | (((E2 & 1) ? 0x0706u : 0x0504u) << 16);
-  return __builtin_amdgcn_perm(w[E2 / 2], w[E1 / 2], sel);
-}
-
 // Codes to bf16 weight pairs in natural k order (2 t_{2j} in the low half, 2 t_{2j+1} in the
 // high half of word j). bf16(-2) = 0xC000, bf16(0) = 0, bf16(+2) = 0x4000: only the high byte
-// differs. The codes are first spread one per byte, each byte holding 4 + code; per output word
-// one v_perm gathers code 2j's byte into byte 1 and code 2j + 1's into byte 3 (zero in bytes 0
-// and 2), and a second v_perm uses that as a selector: 4 + code picks the high byte from a table
-// in the selector's upper source, 0 picks a zero byte of the lower one.
-// selector gathering byte I of `lo` (into byte 1) and byte I of `hi` (into byte 3)
+// differs. Two levels of v_perm, 19 VALU operations per 16 slot-2 codes:
+//   1. spread: a shift and a mask put one code per byte (byte j of selector r: code 4j + r of a
+//      slot-2 word, bit 8j + r of a binary word), and one v_perm per selector reads each byte's
+//      high byte from a table; code 3, never written by the packer, reads as 0;
+//   2. pair: one v_perm with a constant selector takes byte J of two spread words into bytes 1
+//      and 3 of a word, with 0x0C (a constant zero) in bytes 0 and 2.
+// word holding byte I of `lo` (in byte 1) and byte I of `hi` (in byte 3), zero low bytes
 template <int I>
 __device__ __forceinline__ uint32_t gather_pair(uint32_t hi, uint32_t lo) {
   constexpr uint32_t kSel = 0x0Cu | ((uint32_t)I << 8) | (0x0Cu << 16) | ((uint32_t)(4 + I) << 24);
   return __builtin_amdgcn_perm(hi, lo, kSel);
 }
 
-// 16 slot-2 codes (code i in bits 2i, 2i + 1 of u) -> 8 words of bf16 pairs
-__device__ __forceinline__ void decode16_slot2(uint32_t u, uint32_t* out) {
-  constexpr uint32_t kTable = 0x004000C0u;  // codes 0, 1, 2: t = -1, 0, +1
-  uint32_t m[4];  // byte i of m[r]: 4 + code 4i + r
-#pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = ((u >> (2 * r)) & 0x03030303u) | 0x04040404u;
-  out[0] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<0>(m[1], m[0]));
-  out[1] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<0>(m[3], m[2]));
-  out[2] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<1>(m[1], m[0]));
-  out[3] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<1>(m[3], m[2]));
-  out[4] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<2>(m[1], m[0]));
-  out[5] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<2>(m[3], m[2]));
-  out[6] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<3>(m[1], m[0]));
-  out[7] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<3>(m[3], m[2]));
+// byte j of d[r]: the bf16 high byte of code 4j + r of the 16 slot-2 codes in u (code i in
+// bits 2i, 2i + 1)
+// The table is a scalar register: v_perm may read one, and the compiler would otherwise keep
+// the constant in a vector register, which the 128 x 128 tile kernel (at its 256-register limit)
+// does not have to spare.
+__device__ __forceinline__ uint32_t scalar_const(uint32_t v) {
+  uint32_t r;
+  __asm__("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+  return r;
 }
 
-// 32 binary codes (bit i of u, a set bit meaning t = +1) -> 16 words of bf16 pairs
-template <int I>
-__device__ __forceinline__ void decode8_binary(const uint32_t* m, uint32_t* out) {
-  constexpr uint32_t kTable = 0x000040C0u;  // bit 0, 1: t = -1, +1
-  out[0] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<I>(m[1], m[0]));
-  out[1] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<I>(m[3], m[2]));
-  out[2] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<I>(m[5], m[4]));
-  out[3] = __builtin_amdgcn_perm(kTable, 0u, gather_pair<I>(m[7], m[6]));
-}
-__device__ __forceinline__ void decode32_binary(uint32_t u, uint32_t* out) {
-  uint32_t m[8];  // byte i of m[r]: 4 + bit 8i + r
+__device__ __forceinline__ void spread_slot2(uint32_t u, uint32_t* d) {
+  const uint32_t table = scalar_const(0x004000C0u);  // codes 0, 1, 2: t = -1, 0, +1
 #pragma unroll
-  for (int r = 0; r < 8; ++r) m[r] = ((u >> r) & 0x01010101u) | 0x04040404u;
-  decode8_binary<0>(m, out + 0);
-  decode8_binary<1>(m, out + 4);
-  decode8_binary<2>(m, out + 8);
-  decode8_binary<3>(m, out + 12);
+  for (int r = 0; r < 4; ++r) d[r] = __builtin_amdgcn_perm(0u, table, (u >> (2 * r)) & 0x03030303u);
+}
+
+// byte j of d[r]: the bf16 high byte of bit 8j + r of u (a set bit meaning t = +1)
+__device__ __forceinline__ void spread_binary(uint32_t u, uint32_t* d) {
+  const uint32_t table = scalar_const(0x000040C0u);  // bit 0, 1: t = -1, +1
+#pragma unroll
+  for (int r = 0; r < 8; ++r) d[r] = __builtin_amdgcn_perm(0u, table, (u >> r) & 0x01010101u);
+}
+
+// words 4H..4H+3 (codes 8H..8H+7) of a spread slot-2 word: word j pairs codes 2j and 2j + 1
+template <int H>
+__device__ __forceinline__ uint4 pairs4_slot2(const uint32_t* d) {
+  return make_uint4(gather_pair<2 * H>(d[1], d[0]), gather_pair<2 * H>(d[3], d[2]),
+                    gather_pair<2 * H + 1>(d[1], d[0]), gather_pair<2 * H + 1>(d[3], d[2]));
+}
+
+// words 4S..4S+3 (bits 8S..8S+7) of a spread binary word
+template <int S>
+__device__ __forceinline__ uint4 pairs4_binary(const uint32_t* d) {
+  return make_uint4(gather_pair<S>(d[1], d[0]), gather_pair<S>(d[3], d[2]), gather_pair<S>(d[5], d[4]),
+                    gather_pair<S>(d[7], d[6]));
+}
+
+__device__ __forceinline__ void put4(uint32_t* out, uint4 v) {
+  out[0] = v.x;
+  out[1] = v.y;
+  out[2] = v.z;
+  out[3] = v.w;
+}
+
+// 16 slot-2 codes -> 8 words of bf16 pairs
+__device__ __forceinline__ void decode16_slot2(uint32_t u, uint32_t* out) {
+  uint32_t d[4];
+  spread_slot2(u, d);
+  put4(out, pairs4_slot2<0>(d));
+  put4(out + 4, pairs4_slot2<1>(d));
+}
+
+// 32 binary codes -> 16 words of bf16 pairs
+__device__ __forceinline__ void decode32_binary(uint32_t u, uint32_t* out) {
+  uint32_t d[8];
+  spread_binary(u, d);
+  put4(out, pairs4_binary<0>(d));
+  put4(out + 4, pairs4_binary<1>(d));
+  put4(out + 8, pairs4_binary<2>(d));
+  put4(out + 12, pairs4_binary<3>(d));
 }
 
 __device__ __forceinline__ uint16_t bf16_of_2t_digit(uint32_t digit) {
@@ -203,16 +226,30 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
     }
     if (tid < kCodeThreads) {
       const int r = tid >> 1, h = tid & 1;
-      uint32_t out[32];
-      if (LAYOUT == TGS_LAYOUT_SLOT2) {
-        decode16_slot2(cr.x, out + 0);
-        decode16_slot2(cr.y, out + 8);
-        decode16_slot2(cr.z, out + 16);
-        decode16_slot2(cr.w, out + 24);
-      } else if (LAYOUT == TGS_LAYOUT_BINARY) {
-        decode32_binary(cr.x, out + 0);
-        decode32_binary(cr.y, out + 16);
+      // decoded a 16-code word (slot-2) or a 32-code word (binary) at a time, each stored as
+      // soon as it is made, so that few decoded words are live at once
+      uint4* dst = reinterpret_cast<uint4*>(ws + r * kPitch + 64 * h);
+      const uint32_t cw[4] = {cr.x, cr.y, cr.z, cr.w};
+      if constexpr (LAYOUT == TGS_LAYOUT_SLOT2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t d[4];
+          spread_slot2(cw[q], d);
+          dst[2 * q] = pairs4_slot2<0>(d);
+          dst[2 * q + 1] = pairs4_slot2<1>(d);
+        }
+      } else if constexpr (LAYOUT == TGS_LAYOUT_BINARY) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint32_t d[8];
+          spread_binary(cw[q], d);
+          dst[4 * q] = pairs4_binary<0>(d);
+          dst[4 * q + 1] = pairs4_binary<1>(d);
+          dst[4 * q + 2] = pairs4_binary<2>(d);
+          dst[4 * q + 3] = pairs4_binary<3>(d);
+        }
       } else {
+        uint32_t out[32];
         // base-3: digit by digit from the packed bytes (not on a measured path)
         const int row = n_base + r;
         const int kk0 = g * 128 + 64 * h;
@@ -228,10 +265,9 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
           }
           out[e / 2] = lo | (hi << 16);
         }
-      }
-      uint4* dst = reinterpret_cast<uint4*>(ws + r * kPitch + 64 * h);
 #pragma unroll
-      for (int v = 0; v < 8; ++v) dst[v] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
+        for (int v = 0; v < 8; ++v) dst[v] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
+      }
     }
   };
 
@@ -420,52 +456,13 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
 // 16 * FB outputs and 16 * TB activation rows, and splits K across its waves: wave w takes
 // scale groups [w * G / W, (w + 1) * G / W). Every wave builds its MFMA operands in
 // registers: x fragments straight from memory, weights decoded from 8 bytes of codes per lane
-// per group. Within each 16 consecutive k, both operands use the order 0,8,1,9,...,7,15 of the
-// slot-2 decode, so the contraction is unchanged. Each group's partial is scaled in fp32; the W
-// per-wave results are added through LDS in wave order (deterministic, no atomics).
-// Binary codes (BIN) take 4 bytes (32 weights) per lane per group and decode to the same pair order.
+// per group. Both operands keep k in its natural order (the pair decode above), so the x
+// fragments go to the MFMA as loaded. Each group's partial is scaled in fp32; the W per-wave
+// results are added through LDS in wave order (deterministic, no atomics).
+// Binary codes (BIN) take 4 bytes (32 weights) per lane per group and decode the same way.
 // Every workgroup reads all of x for its outputs, so x traffic from L2 falls as FB grows. The
 // host picks FB so that a launch is about one workgroup per CU (one round of workgroups) rather
 // than shrinking FB to get more workgroups.
-
-// pairs 4H..4H+3 of the 16 slot-2 codes in u, in the order 0,8,1,9,...: bf16(2t_i) in the low
-// half, bf16(2t_{i+8}) in the high half (the selector puts code i in byte 1 and code i + 8 in
-// byte 3, 0x0C, a constant zero, in bytes 0 and 2; v_perm reads the high byte from the table)
-template <int H>
-__device__ __forceinline__ uint4 decode4_slot2(uint32_t u) {
-  constexpr uint32_t kTable = 0x004000C0u;
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * H + j;  // shift left by 8 - 2i (negative: right)
-    const uint32_t v = i <= 4 ? (u << (8 - 2 * i)) : (u >> (2 * i - 8));
-    o[j] = __builtin_amdgcn_perm(0u, kTable, (v & 0x03000300u) | 0x000C000Cu);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-// the same pairs for 16 binary codes, bits 0..15 of u: bf16(2t_i) low, bf16(2t_{i+8}) high
-template <int H>
-__device__ __forceinline__ uint4 decode4_binary(uint32_t u) {
-  constexpr uint32_t kTable = 0x000040C0u;
-  const uint32_t v = (u & 0xFFu) | ((u & 0xFF00u) << 8);  // bit i + 8 -> bit i + 16
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * H + j;
-    o[j] = __builtin_amdgcn_perm(0u, kTable, ((v << (8 - i)) & 0x01000100u) | 0x000C000Cu);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-// pairs 4H..4H+3 in the order 0,8,1,9,... of 16 consecutive bf16 values in w[0..7]
-template <int H>
-__device__ __forceinline__ uint4 interleave4(const uint32_t* w) {
-  if constexpr (H == 0)
-    return make_uint4(pair16<0, 8>(w), pair16<1, 9>(w), pair16<2, 10>(w), pair16<3, 11>(w));
-  else
-    return make_uint4(pair16<4, 12>(w), pair16<5, 13>(w), pair16<6, 14>(w), pair16<7, 15>(w));
-}
 
 template <int TB, int kFB, int kWaves, int kStages, bool BIN>
 __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t* __restrict__ codes, int64_t stride,
@@ -567,21 +564,29 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int fb = 0; fb < kFB; ++fb) part[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Step s multiplies k = 32 kq + 8 s .. + 7 of the group (MFMA k slots 8 kq .. + 7), in natural
+    // order on both sides: the lane's x load s as loaded, and weights 8 s .. 8 s + 7 of its codes.
+    uint32_t d[kFB][8];  // spread codes (slot-2: one 16-code word at a time; binary: all 32)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // 32 k per step: this lane's k quarter holds 8 of them
+    for (int s = 0; s < 4; ++s) {
       bf16x8 a[TB], b[kFB];
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
-        a[tb] = __builtin_bit_cast(bf16x8, (s & 1) ? interleave4<1>(st.xv[tb] + 8 * (s >> 1))
-                                                   : interleave4<0>(st.xv[tb] + 8 * (s >> 1)));
+        a[tb] = __builtin_bit_cast(
+            bf16x8, make_uint4(st.xv[tb][4 * s], st.xv[tb][4 * s + 1], st.xv[tb][4 * s + 2], st.xv[tb][4 * s + 3]));
 #pragma unroll
       for (int fb = 0; fb < kFB; ++fb) {
-        if constexpr (BIN)  // step s: bits 16 (s >> 1) .. + 15 of the lane's word
-          b[fb] = __builtin_bit_cast(bf16x8, (s & 1) ? decode4_binary<1>(st.cw[fb][0] >> (16 * (s >> 1)))
-                                                     : decode4_binary<0>(st.cw[fb][0] >> (16 * (s >> 1))));
-        else
-          b[fb] = __builtin_bit_cast(bf16x8, (s & 1) ? decode4_slot2<1>(st.cw[fb][s >> 1])
-                                                     : decode4_slot2<0>(st.cw[fb][s >> 1]));
+        if constexpr (BIN) {
+          if (s == 0) spread_binary(st.cw[fb][0], d[fb]);
+          const uint4 w = s == 0 ? pairs4_binary<0>(d[fb])
+                          : s == 1 ? pairs4_binary<1>(d[fb])
+                          : s == 2 ? pairs4_binary<2>(d[fb])
+                                   : pairs4_binary<3>(d[fb]);
+          b[fb] = __builtin_bit_cast(bf16x8, w);
+        } else {
+          if ((s & 1) == 0) spread_slot2(st.cw[fb][s >> 1], d[fb]);
+          b[fb] = __builtin_bit_cast(bf16x8, (s & 1) ? pairs4_slot2<1>(d[fb]) : pairs4_slot2<0>(d[fb]));
+        }
       }
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
