@@ -46,6 +46,9 @@ constexpr int64_t kTileTarget = 640;
 // ... and the fewest 128-groups a part keeps: with fewer, a wave has too few groups to stream
 // (measured: 17408 x 5120, 40 groups, is slower in two parts at 16 and 128 rows)
 constexpr int64_t kMinPartGroups = 32;
+// skinny kernel, scales staged in LDS: b16 loads per thread (512 threads), so at most
+// 512 * kSkinnyScaleLoads scales per workgroup take that path
+constexpr int kSkinnyScaleLoads = 8;
 // 128 x 128 tiles: workgroups resident at once (two per CU), and the fewest groups a part of a
 // tail tile keeps
 constexpr int64_t kTileSlots = 512;
@@ -464,14 +467,17 @@ __attribute__((amdgpu_waves_per_eu(LAYOUT == TGS_LAYOUT_BASE3 ? 1 : 2, 8))) void
 // host picks FB so that a launch is about one workgroup per CU (one round of workgroups) rather
 // than shrinking FB to get more workgroups.
 
-template <int TB, int kFB, int kWaves, int kStages, bool BIN>
+template <int TB, int kFB, int kWaves, int kStages, bool BIN, bool SL>
 __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t* __restrict__ codes, int64_t stride,
                                                           const uint16_t* __restrict__ scales, int n, int k,
                                                           const uint16_t* __restrict__ x, int m,
                                                           float* __restrict__ y, float* __restrict__ part_sums) {
   // kFB: 16-output blocks per workgroup; kWaves: K slices (waves) per workgroup; kStages: groups
-  // of loads in flight per wave
+  // of loads in flight per wave. SL: the scales of the workgroup's rows and K part go to LDS
+  // (dynamic, [16 kFB][part groups] fp16) before the weight stream starts; otherwise each wave
+  // loads its rows' scales with every group.
   __shared__ float red[kWaves][TB * kFB * 4][64];
+  extern __shared__ __attribute__((aligned(16))) uint16_t sc_lds[];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int fr = lane & 15, kq = lane >> 4;  // fragment row and k quarter
@@ -511,8 +517,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
 
   struct Stage {
     uint32_t cw[kFB][2];
-    uint32_t sc[kFB];
+    uint32_t sc[SL ? 1 : kFB];
     uint32_t xv[TB][16];
+    int g;  // its scale group
   };
   // Every workgroup reads the same activations; if all started at the same group, hundreds of CUs
   // would request the same few L2 lines at once. Each workgroup walks its waves' groups in a
@@ -524,6 +531,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
     int j = i + rot;
     if (j >= count) j -= count;
     const int g = pg0 + wave + kWaves * j;
+    st.g = g;
 #pragma unroll
     for (int fb = 0; fb < kFB; ++fb) {
       if constexpr (BIN) {  // 16 bytes of codes per group
@@ -536,8 +544,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
         st.cw[fb][0] = v[0];
         st.cw[fb][1] = v[1];
       }
-      st.sc[fb] = __builtin_amdgcn_raw_buffer_load_b16(
-          scale_rsrc, live ? (int)(scale_off[fb] + 2u * (uint32_t)g) : kOobOffset, 0, 0);
+      if constexpr (!SL)
+        st.sc[fb] = __builtin_amdgcn_raw_buffer_load_b16(
+            scale_rsrc, live ? (int)(scale_off[fb] + 2u * (uint32_t)g) : kOobOffset, 0, 0);
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
@@ -597,7 +606,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
     // D[i][j] (activation row i, output j) sits in lane 16 * (i / 4) + j, register i % 4
 #pragma unroll
     for (int fb = 0; fb < kFB; ++fb) {
-      const float sc = 0.5f * f16_to_f32((uint16_t)st.sc[fb]);  // the weights were decoded as 2t
+      const uint16_t sbits = SL ? sc_lds[(16 * fb + fr) * pgn + (st.g - pg0)] : (uint16_t)st.sc[SL ? 0 : fb];
+      const float sc = 0.5f * f16_to_f32(sbits);  // the weights were decoded as 2t
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -608,9 +618,42 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
   // kStages groups of loads in flight; a stage is reloaded as soon as it has been multiplied
   // (loads past the wave's last group are parked out of range, so every load is unconditional
   // and the compiler's wait counts stay exact)
+  // SL: the scales first, so that they do not wait behind the weight stream in the CU's memory
+  // pipeline. Scale i of the block [16 kFB rows][pgn groups] is row i / pgn, group pg0 + i % pgn:
+  // consecutive threads read consecutive scales of a row, so each load instruction touches one or
+  // two cache lines (in the group loop a scale load touches 16). Rows past n read as zero.
+  constexpr int kScaleLoads = SL ? kSkinnyScaleLoads : 1;
+  uint32_t sv[kScaleLoads];
+  const int sc_count = 16 * kFB * pgn;
+  if constexpr (SL) {
+    // (r, gl) of e = threadIdx.x + 512 i, advanced by 512 = q pgn + rem each step (no division per load)
+    const int q = kWaves * 64 / pgn, rem = kWaves * 64 - q * pgn;
+    int r = (int)threadIdx.x / pgn, gl = (int)threadIdx.x - r * pgn;
+#pragma unroll
+    for (int i = 0; i < kScaleLoads; ++i) {
+      const int e = (int)threadIdx.x + kWaves * 64 * i;
+      const int off = e < sc_count ? (int)(((uint32_t)(n_base + r) * (uint32_t)groups + (uint32_t)(pg0 + gl)) * 2u)
+                                   : kOobOffset;
+      sv[i] = __builtin_amdgcn_raw_buffer_load_b16(scale_rsrc, off, 0, 0);
+      r += q;
+      gl += rem;
+      if (gl >= pgn) {
+        gl -= pgn;
+        ++r;
+      }
+    }
+  }
   Stage st[kStages];
 #pragma unroll
   for (int u = 0; u < kStages; ++u) load(st[u], u);
+  if constexpr (SL) {
+#pragma unroll
+    for (int i = 0; i < kScaleLoads; ++i) {
+      const int e = (int)threadIdx.x + kWaves * 64 * i;
+      if (e < sc_count) sc_lds[e] = (uint16_t)sv[i];
+    }
+    __syncthreads();
+  }
   for (int base = 0; base < count; base += kStages) {
 #pragma unroll
     for (int u = 0; u < kStages; ++u) {
@@ -647,6 +690,8 @@ struct GemmPlan {
   int64_t wgs; // workgroups of one part (skinny), tiles (tiled)
   int64_t whole, tail;  // tiled: tiles taken whole, then tiles split in `parts`
   int64_t n_tiles;      // tiled: column tiles
+  bool sl;              // skinny: scales staged in LDS
+  int64_t lds;          // ... the dynamic LDS bytes that takes
 };
 
 // compute units of the current device (256 on MI355X; 256 if the query fails)
@@ -690,6 +735,10 @@ GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
           if (w <= cus && w > best) best = w, p.fb = fb, p.parts = (int)q;
         }
       p.wgs = (n + 16 * p.fb - 1) / (16 * p.fb);
+      // the scales of a workgroup's rows and (largest) part in LDS, when one batch of loads covers them
+      const int64_t sc = 16LL * p.fb * ((groups + p.parts - 1) / p.parts);
+      p.sl = sc <= 512LL * kSkinnyScaleLoads;
+      p.lds = p.sl ? sc * 2 : 0;
     } else {
       // 16 outputs per block: the most (4, 2, 1) that still gives 512 workgroups
       p.kind = 1;
@@ -782,9 +831,13 @@ hipError_t launch_layout(const GemmPlan& p, const uint8_t* codes, int64_t stride
   if (p.kind == 0) {
     if constexpr (LAYOUT == TGS_LAYOUT_SLOT2 || kBin) {
       const dim3 grid((unsigned)p.wgs, 1, (unsigned)p.parts);
-#define TGS_SKINNY(FB_)                                                                                          \
-  hipLaunchKernelGGL((gemm_skinny_kernel<1, FB_, 8, 2, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, \
-                     ki, x, mi, y, ws)
+#define TGS_SKINNY(FB_)                                                                                            \
+  if (p.sl)                                                                                                        \
+    hipLaunchKernelGGL((gemm_skinny_kernel<1, FB_, 8, 2, kBin, true>), grid, dim3(512), (size_t)p.lds, stream, codes, \
+                       stride, scales, ni, ki, x, mi, y, ws);                                                      \
+  else                                                                                                             \
+    hipLaunchKernelGGL((gemm_skinny_kernel<1, FB_, 8, 2, kBin, false>), grid, dim3(512), 0, stream, codes, stride,   \
+                       scales, ni, ki, x, mi, y, ws)
       switch (p.fb) {
         case 2: TGS_SKINNY(2); break;
         case 3: TGS_SKINNY(3); break;
@@ -798,7 +851,7 @@ hipError_t launch_layout(const GemmPlan& p, const uint8_t* codes, int64_t stride
     if constexpr (LAYOUT == TGS_LAYOUT_SLOT2 || kBin) {
       const dim3 grid((unsigned)((n + 16 * p.fb - 1) / (16 * p.fb)), (unsigned)((m + 31) / 32), (unsigned)p.parts);
 #define TGS_SKINNY2(FB_)                                                                                          \
-  hipLaunchKernelGGL((gemm_skinny_kernel<2, FB_, 8, 3, kBin>), grid, dim3(512), 0, stream, codes, stride, scales, ni, \
+  hipLaunchKernelGGL((gemm_skinny_kernel<2, FB_, 8, 3, kBin, false>), grid, dim3(512), 0, stream, codes, stride, scales, ni, \
                      ki, x, mi, y, ws)
       if (p.fb == 4) TGS_SKINNY2(4); else if (p.fb == 2) TGS_SKINNY2(2); else TGS_SKINNY2(1);
 #undef TGS_SKINNY2
