@@ -197,7 +197,10 @@ tgs_status ternary_gemv_batched(const tgs_matrix* ws, int32_t count, const void*
  *   y       device [m][n] fp32, 4-byte aligned
  * Rotated weights (prefill): rotate the activations once with hadamard_rotate or
  * rmsnorm_hadamard_rotate into a bf16 buffer (y_dtype TGS_BF16) and multiply that buffer with a
- * plain-basis descriptor (rotated = 0) of the same codes and scales.
+ * plain-basis descriptor (rotated = 0) of the same codes and scales. That is the product of
+ * bf16(R x): every rotated activation is rounded once to bf16 (unit roundoff 2^-8), so against
+ * the unrounded rotation the result holds |y - y_exact| <= (2^-8 + 1e-3 (1 + 2^-8)) B + 1e-6
+ * with B = sum |s t (R x)|, not the 1e-3 B + 1e-6 of the fused single-token route.
  */
 tgs_status ternary_gemm(const tgs_matrix* w, const void* x, int32_t x_dtype, int64_t m,
                         const int8_t* signs, float* y, void* stream);

@@ -326,8 +326,13 @@ ROT_LAYOUTS = [tgs.SLOT2, tgs.BASE3, tgs.BINARY]
 @pytest.mark.parametrize("m", [1, 24, 130])
 def test_rotated_prefill_two_pass_matches_oracle(layout, block, m):
     """Prefill with rotated weights: rotate the activations once into bf16, then ternary_gemm
-    with a plain-basis descriptor of the same codes. The reference is the oracle's rotation,
-    rounded to bf16 (via fp32, as the kernel rounds), multiplied by the oracle."""
+    with a plain-basis descriptor of the same codes. Two references:
+    - the oracle's rotation rounded to bf16 (via fp32, as the kernel rounds), multiplied by the
+      oracle: within the usual bound;
+    - the oracle's rotated product itself (no rounding of R x): within the bound derived for one
+      bf16 rounding of every rotated activation. With B = sum |s t (R x)| and bf16's unit roundoff
+      2^-8, |y - y_exact| <= 2^-8 B + 1e-3 (1 + 2^-8) B + 1e-6; the plain bound alone
+      (1e-3 B + 1e-6) does not hold on this route, and the header says so."""
     n, k = 200, 3072
     if layout == tgs.BINARY:
         t, s = _binary_weights(m, f"rotpre{block}", n, k)
@@ -341,6 +346,10 @@ def test_rotated_prefill_two_pass_matches_oracle(layout, block, m):
     xr_bits = synth.bf16_bits(oracle.rotate(x16.astype(np.float64), sg, block))
     y_ref, bound = oracle_product(layout, t, s, xr_bits, oracle.X_BF16)
     assert_within_bound(y.cpu().numpy(), y_ref, bound, f"rotated prefill {layout} block {block} m={m}")
+    y_exact, bound_exact = oracle_product(layout, t, s, x16.view(np.uint16), oracle.X_F16, signs=sg, block=block)
+    b = (bound_exact - 1e-6) / 1e-3  # sum |s t (R x)| per output
+    derived = (2.0 ** -8 + 1e-3 * (1 + 2.0 ** -8)) * b + 1e-6
+    assert_within_bound(y.cpu().numpy(), y_exact, derived, f"rotated prefill vs unrounded rotation {layout} {block} m={m}")
 
 
 def test_misaligned_signs_are_refused():
