@@ -682,7 +682,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_skinny_kernel(const uint8_t*
 
 // How one launch (at most a chunk of activation rows) is laid out.
 struct GemmPlan {
-  int kind;    // 0: skinny, up to 16 rows; 1: skinny, 17..32 rows; 2: tiled
+  int kind;    // 0: skinny, up to 16 rows; 1: skinny, 17..32 rows (two blocks of 16); 2: tiled
   int fb;      // skinny: 16-output blocks per workgroup
   int bm, bn;  // tiled: tile shape
   int ks;      // tiled: K parts inside a workgroup
@@ -716,36 +716,32 @@ GemmPlan plan_of(int32_t layout, int64_t n, int64_t k, int64_t m, bool split) {
     return (int)std::max<int64_t>(1, q);
   };
   if ((layout == TGS_LAYOUT_SLOT2 || layout == TGS_LAYOUT_BINARY) && m <= 32) {
-    if (m <= 16) {
-      // 16 * FB outputs per workgroup of 8 waves (FB in 2..6), in P parts of K (P in 1..4, each at
-      // least kMinPartGroups groups; P = 1 without a workspace): the most workgroups that still
-      // give no CU a second one, ties to the larger FB. A CU streams this kernel's loads at a
-      // rate of its own, so a CU with two workgroups doubles the launch (17408 x 5120: FB = 4,
-      // 272 workgroups, 30.9 us against 20.6 us for FB = 5, 218); and every workgroup reads x for
-      // its part of K, so x's L2 traffic falls as FB grows. 5120 x 17408: FB = 5 in four parts
-      // (256 workgroups) 22.0 us, FB = 6 in four (216) 24.3 us, FB = 2 in three (480) 27.5 us.
-      p.kind = 0;
-      const int64_t cus = device_cus();
-      const int64_t max_parts = split ? std::min<int64_t>(4, std::max<int64_t>(1, groups / kMinPartGroups)) : 1;
-      p.fb = 6, p.parts = 1;
-      int64_t best = 0;
-      for (int fb = 6; fb >= 2; --fb)
-        for (int64_t q = 1; q <= max_parts; ++q) {
-          const int64_t w = (n + 16 * fb - 1) / (16 * fb) * q;
-          if (w <= cus && w > best) best = w, p.fb = fb, p.parts = (int)q;
-        }
-      p.wgs = (n + 16 * p.fb - 1) / (16 * p.fb);
-      // the scales of a workgroup's rows and (largest) part in LDS, when one batch of loads covers them
-      const int64_t sc = 16LL * p.fb * ((groups + p.parts - 1) / p.parts);
-      p.sl = sc <= 512LL * kSkinnyScaleLoads;
-      p.lds = p.sl ? sc * 2 : 0;
-    } else {
-      // 16 outputs per block: the most (4, 2, 1) that still gives 512 workgroups
-      p.kind = 1;
-      p.fb = (n + 63) / 64 >= 512 ? 4 : ((n + 31) / 32 >= 512 ? 2 : 1);
-      p.wgs = (n + 16 * p.fb - 1) / (16 * p.fb) * ((m + 31) / 32);
-      p.parts = 1;
-    }
+    // 16 * FB outputs per workgroup of 8 waves (FB in 2..6) and one (m <= 16) or two blocks of 16
+    // activation rows, in P parts of K (P in 1..4, each at least kMinPartGroups groups; P = 1
+    // without a workspace): the most workgroups that still give no CU a second one, ties to the
+    // larger FB. A CU streams this kernel's loads at a rate of its own, so a CU with two
+    // workgroups doubles the launch (17408 x 5120: FB = 4, 272 workgroups, 30.9 us against 20.6 us
+    // for FB = 5, 218); and every workgroup reads x for its part of K, so x's L2 traffic falls as
+    // FB grows. 5120 x 17408: FB = 5 in four parts (256 workgroups) 22.0 us, FB = 6 in four (216)
+    // 24.3 us, FB = 2 in three (480) 27.5 us. (Up to 32 rows once took FB = 4/2/1 for at least 512
+    // workgroups: 50 / 78 us at 32 rows on these two shapes.)
+    p.kind = m <= 16 ? 0 : 1;
+    const int64_t cus = device_cus();
+    const int64_t max_parts = split ? std::min<int64_t>(4, std::max<int64_t>(1, groups / kMinPartGroups)) : 1;
+    // (two row blocks at FB = 6 spill with binary codes: FB <= 5 there)
+    const int fb_max = m <= 16 ? 6 : 5;
+    p.fb = fb_max, p.parts = 1;
+    int64_t best = 0;
+    for (int fb = fb_max; fb >= 2; --fb)
+      for (int64_t q = 1; q <= max_parts; ++q) {
+        const int64_t w = (n + 16 * fb - 1) / (16 * fb) * q;
+        if (w <= cus && w > best) best = w, p.fb = fb, p.parts = (int)q;
+      }
+    p.wgs = (n + 16 * p.fb - 1) / (16 * p.fb);
+    // the scales of a workgroup's rows and (largest) part in LDS, when one batch of loads covers them
+    const int64_t sc = 16LL * p.fb * ((groups + p.parts - 1) / p.parts);
+    p.sl = sc <= 512LL * kSkinnyScaleLoads;
+    p.lds = p.sl ? sc * 2 : 0;
     return p;
   }
   // tiles: 128 x 128 for many activation rows, else 64 rows; 64 columns when 128 gives too few
@@ -849,11 +845,20 @@ hipError_t launch_layout(const GemmPlan& p, const uint8_t* codes, int64_t stride
     }
   } else if (p.kind == 1) {
     if constexpr (LAYOUT == TGS_LAYOUT_SLOT2 || kBin) {
-      const dim3 grid((unsigned)((n + 16 * p.fb - 1) / (16 * p.fb)), (unsigned)((m + 31) / 32), (unsigned)p.parts);
-#define TGS_SKINNY2(FB_)                                                                                          \
-  hipLaunchKernelGGL((gemm_skinny_kernel<2, FB_, 8, 3, kBin, false>), grid, dim3(512), 0, stream, codes, stride, scales, ni, \
-                     ki, x, mi, y, ws)
-      if (p.fb == 4) TGS_SKINNY2(4); else if (p.fb == 2) TGS_SKINNY2(2); else TGS_SKINNY2(1);
+      const dim3 grid((unsigned)p.wgs, 1, (unsigned)p.parts);
+#define TGS_SKINNY2(FB_)                                                                                           \
+  if (p.sl)                                                                                                        \
+    hipLaunchKernelGGL((gemm_skinny_kernel<2, FB_, 8, 2, kBin, true>), grid, dim3(512), (size_t)p.lds, stream, codes, \
+                       stride, scales, ni, ki, x, mi, y, ws);                                                      \
+  else                                                                                                             \
+    hipLaunchKernelGGL((gemm_skinny_kernel<2, FB_, 8, 2, kBin, false>), grid, dim3(512), 0, stream, codes, stride,   \
+                       scales, ni, ki, x, mi, y, ws)
+      switch (p.fb) {
+        case 2: TGS_SKINNY2(2); break;
+        case 3: TGS_SKINNY2(3); break;
+        case 4: TGS_SKINNY2(4); break;
+        default: TGS_SKINNY2(5); break;
+      }
 #undef TGS_SKINNY2
     }
   } else {

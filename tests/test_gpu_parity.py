@@ -438,14 +438,15 @@ def test_gemm_four_k_parts(layout, n, k, m, split):
     assert_within_bound(y, y_ref, bound, f"gemm four K parts layout {layout} {n}x{k} m={m}")
 
 
-# (n, k, m, parts): K split across workgroups. Skinny kernel (m <= 16): FB in 2..6 and parts in
-# 1..min(4, groups / 32), the most workgroups ceil(n / 16 FB) * parts that fit one per CU (256),
-# ties to the larger FB (4100 x 8192: FB = 3 in two parts). Tiled kernel (64 x 64 tiles,
-# 33 <= m <= 128): parts = min(ceil(640 / tiles), 4, groups / 32). Ragged n, parts that do not
-# divide the groups (130 / 4, 65 / 2, 66 / 2), one row, parts of exactly 32 groups, and a product
+# (n, k, m, parts): K split across workgroups. Skinny kernel (m <= 32; one block of 16 rows, or
+# two above 16): FB in 2..6 (2..5 for two blocks) and parts in 1..min(4, groups / 32), the most
+# workgroups ceil(n / 16 FB) * parts that fit one per CU (256), ties to the larger FB
+# (4100 x 8192: FB = 3 in two parts). Tiled kernel (64 x 64 tiles, 33 <= m <= 128):
+# parts = min(ceil(640 / tiles), 4, groups / 32). Ragged n, parts that do not divide the groups
+# (130 / 4, 65 / 2, 66 / 2), one row, 17 to 32 rows, parts of exactly 32 groups, and a product
 # with too few groups to split.
 SPLIT_CASES = [(512, 16384, 1, 4), (1000, 16640, 16, 4), (70, 8320, 5, 2), (4100, 8192, 16, 2), (600, 16384, 100, 4),
-               (130, 8448, 64, 2), (64, 4096, 33, 1)]
+               (130, 8448, 64, 2), (64, 4096, 33, 1), (1000, 16640, 24, 4), (70, 8320, 32, 2), (4100, 8192, 17, 2)]
 
 
 def _split_bytes(n, m, parts, skinny):
@@ -467,7 +468,7 @@ def test_gemm_split_across_workgroups(layout, n, k, m, parts):
     """The K split across workgroups (ternary_gemm_ws): within the bound of the oracle, the
     workspace size is (parts - 1) * m * n fp32, and repeated calls are bit-identical (the parts
     are added in part order, no atomics). The single-launch product is within the bound too."""
-    skinny = m <= 16 and layout != tgs.BASE3  # base-3 always takes the tiled kernel
+    skinny = m <= 32 and layout != tgs.BASE3  # base-3 always takes the tiled kernel
     if layout == tgs.BASE3 and m <= 32:
         parts = _tile_parts(n, k, m)
     t, s = make_weights(n + k + m, f"gemmsplit{layout}", n, k, 0.0 if layout == tgs.BINARY else 0.4)
