@@ -226,8 +226,9 @@ tgs_status ternary_gemm_ws(const tgs_matrix* w, const void* x, int32_t x_dtype, 
 
 /*
  * ternary_gemm_workspace_size (host): the bytes of workspace ternary_gemm_ws uses for this matrix
- * and m (0: that product is not split and needs none). Depends on w's layout, n and k and on m
- * only. Returns 0 for a descriptor that ternary_gemm would refuse, or m < 1.
+ * and m (0: that product is not split and needs none). Depends on w's layout, n and k, on m, and
+ * on the current device's compute-unit count (256 when no device is visible), as the launch plan
+ * does. Returns 0 for a descriptor that ternary_gemm would refuse, or m < 1.
  */
 size_t ternary_gemm_workspace_size(const tgs_matrix* w, int64_t m);
 

@@ -286,3 +286,29 @@ def test_bad_rotation_block_has_one_status_everywhere():
 def test_matrix_init_records_the_rotation_block(rotated, stored):
     m = _fake_matrix(rotated=rotated, k=2048)
     assert m.rotated == stored
+
+
+# Workspace bytes of ternary_gemm_ws for the 27B prefill shapes, as the launch plan splits K on a
+# device of 256 compute units (MI355X; also the count the host assumes when no device is visible):
+# - 17408 x 5120 (40 groups): too few groups to split up to 32 rows (one block of 16 rows, or two
+#   above 16, per workgroup); 64 x 64 tiles at 128 rows (544 tiles: 512 whole, the 32 left over
+#   in four parts); 128 x 128 tiles at 2048 rows (2176 tiles: 128 left over, four parts);
+# - 5120 x 17408 (136 groups): FB = 5 and four K parts up to 32 rows, (4 - 1) m n fp32 values;
+#   every 64 x 64 tile in four parts at 33 and 128 rows (80 and 160 tiles); 128 left-over
+#   128 x 128 tiles in four parts at 2048 rows.
+GEMM_WORKSPACE_27B = [
+    (17408, 5120, 1, 0), (17408, 5120, 16, 0), (17408, 5120, 17, 0), (17408, 5120, 32, 0), (17408, 5120, 33, 0),
+    (17408, 5120, 128, 3 * 32 * 64 * 64 * 4), (17408, 5120, 2048, 3 * 128 * 128 * 128 * 4),
+    (5120, 17408, 1, 3 * 1 * 5120 * 4), (5120, 17408, 16, 3 * 16 * 5120 * 4), (5120, 17408, 17, 3 * 17 * 5120 * 4),
+    (5120, 17408, 32, 3 * 32 * 5120 * 4), (5120, 17408, 33, 3 * 80 * 64 * 64 * 4),
+    (5120, 17408, 128, 3 * 160 * 64 * 64 * 4), (5120, 17408, 2048, 3 * 128 * 128 * 128 * 4),
+]
+
+
+@pytest.mark.parametrize("n,k,m,expected", GEMM_WORKSPACE_27B)
+def test_gemm_workspace_follows_the_launch_plan(n, k, m, expected):
+    """The size query runs the same plan as the launch, so it pins how K is split (skinny kernel
+    up to 32 rows, tiled kernel above) without a device."""
+    w = _fake_matrix(n=n, k=k)
+    assert tgs.lib().ternary_gemm_workspace_size(ctypes.byref(w), m) == expected
+    assert tgs.lib().ternary_gemm_workspace_size(ctypes.byref(w), 0) == 0
