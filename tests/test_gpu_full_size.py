@@ -143,7 +143,7 @@ def test_8b_attention_inputs_with_the_rmsnorm_prologue():
     assert (np.abs(y.cpu().numpy()[:, rows] - y_ref) <= bound).all()
 
 
-@pytest.mark.parametrize("m", [16, 128, 2048])
+@pytest.mark.parametrize("m", [16, 32, 128, 2048])
 def test_27b_prefill_gemm(m):
     shapes = [("gate", 17408, 5120), ("down", 5120, 17408)]
     for i, (name, n, k) in enumerate(shapes):
